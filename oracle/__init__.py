@@ -1,0 +1,328 @@
+"""CPU oracle for 4-bit block-quantized weights (test infrastructure only).
+
+Plain, slow reference definitions of the MXFP4, NVFP4, Q4_K and Q4_0 decoders,
+of the GPTQ / AWQ / Q4_0 int4 layouts and of the dot products built on them.
+The arithmetic lives in ``qbn_oracle.c`` (plain C, gcc -O2, no SIMD
+intrinsics, no fast-math); this module only compiles it and marshals numpy
+arrays.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The library under ``bit_block_quantized_nibble_amd``
+never imports it and shares no code with it.
+
+Every function with an arithmetic definition is pinned by ``tests/test_oracle_*``
+against facts the source pages fix (printed worked values, closed forms,
+exhaustive enumeration against torch's float8 dtypes, brute force on tiny
+inputs). No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qbn_oracle.c")
+_BUILD = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD, "liboracle.so")
+
+MXFP4, NVFP4, Q4_K, Q4_0 = 1, 2, 3, 4
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into oracle/_build/liboracle.so with gcc -O2."""
+    os.makedirs(_BUILD, exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+               "-fvisibility=hidden", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.oracle_e2m1.argtypes = [ctypes.c_uint]
+        lib.oracle_e2m1.restype = ctypes.c_double
+        lib.oracle_e8m0.argtypes = [ctypes.c_uint]
+        lib.oracle_e8m0.restype = ctypes.c_double
+        lib.oracle_e4m3fn.argtypes = [ctypes.c_uint]
+        lib.oracle_e4m3fn.restype = ctypes.c_double
+        lib.oracle_f16.argtypes = [ctypes.c_uint]
+        lib.oracle_f16.restype = ctypes.c_double
+        lib.oracle_bf16_value.argtypes = [ctypes.c_uint]
+        lib.oracle_bf16_value.restype = ctypes.c_double
+        lib.oracle_bf16_rne.argtypes = [ctypes.c_float]
+        lib.oracle_bf16_rne.restype = ctypes.c_uint
+        lib.oracle_q4k_unpack_scales.argtypes = [P, P, P]
+        lib.oracle_q4k_pack_scales.argtypes = [P, P, P]
+        lib.oracle_pack_bits.argtypes = [P, I64, ctypes.c_int, P]
+        lib.oracle_unpack_bits.argtypes = [P, I64, ctypes.c_int, P]
+        for name in ("oracle_gptq_pack", "oracle_gptq_unpack", "oracle_awq_pack", "oracle_awq_unpack"):
+            getattr(lib, name).argtypes = [P, I64, I64, P]
+        lib.oracle_q4_0_pack.argtypes = [P, P, I64, I64, P]
+        lib.oracle_q4_0_unpack.argtypes = [P, I64, I64, P, P]
+        lib.oracle_affine_dequant.argtypes = [P, P, P, I64, I64, I64, P]
+        lib.oracle_dequant_rows.argtypes = [ctypes.c_int, P, P, ctypes.c_float, I64, P, I64, P]
+        lib.oracle_dequant_rows.restype = ctypes.c_int
+        lib.oracle_gemv_rows.argtypes = [ctypes.c_int, P, P, ctypes.c_float, I64, P, ctypes.c_int, P, I64,
+                                         P, P, P, P]
+        lib.oracle_gemv_rows.restype = ctypes.c_int
+        lib.oracle_gemm_entries.argtypes = [ctypes.c_int, P, P, ctypes.c_float, I64, P, I64, P, P, I64,
+                                            P, P, P, P]
+        lib.oracle_gemm_entries.restype = ctypes.c_int
+        lib.oracle_e2m1_nearest.argtypes = [ctypes.c_double, ctypes.c_double]
+        lib.oracle_e2m1_nearest.restype = ctypes.c_uint
+        lib.oracle_int4_sym_code.argtypes = [ctypes.c_double, ctypes.c_double]
+        lib.oracle_int4_sym_code.restype = ctypes.c_uint
+        lib.oracle_int4_sym_value.argtypes = [ctypes.c_uint]
+        lib.oracle_int4_sym_value.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+# ---------------------------------------------------------------- scalars
+
+def e2m1(code: int) -> float:
+    return _load().oracle_e2m1(code)
+
+
+def e8m0(byte: int) -> float:
+    return _load().oracle_e8m0(byte)
+
+
+def e4m3fn(byte: int) -> float:
+    return _load().oracle_e4m3fn(byte)
+
+
+def f16(bits: int) -> float:
+    return _load().oracle_f16(bits)
+
+
+def bf16_value(bits: int) -> float:
+    return _load().oracle_bf16_value(bits)
+
+
+def bf16_rne(values) -> np.ndarray:
+    """binary32 values -> bfloat16 bit patterns (uint16), round to nearest even."""
+    lib = _load()
+    v = np.ascontiguousarray(values, dtype=np.float32).ravel()
+    out = np.empty(v.shape, dtype=np.uint16)
+    for i, f in enumerate(v.tolist()):
+        out[i] = lib.oracle_bf16_rne(f)
+    return out.reshape(np.shape(values))
+
+
+def bf16_rne_array(values: np.ndarray) -> np.ndarray:
+    """Vector form of bf16_rne for large arrays; same rule, written with numpy
+    integer operations so that big outputs can be compared in seconds."""
+    u = np.ascontiguousarray(values, dtype=np.float32).view(np.uint32)
+    is_nan = ((u & 0x7F800000) == 0x7F800000) & ((u & 0x007FFFFF) != 0)
+    lsb = (u >> 16) & 1
+    r = ((u + np.uint32(0x7FFF) + lsb) >> 16).astype(np.uint16)
+    r = np.where(is_nan, ((u >> 16) | 0x40).astype(np.uint16), r)
+    return r.astype(np.uint16)
+
+
+def e2m1_nearest(w: float, s: float) -> int:
+    return _load().oracle_e2m1_nearest(w, s)
+
+
+def int4_sym_code(w: float, s: float) -> int:
+    return _load().oracle_int4_sym_code(w, s)
+
+
+def int4_sym_value(code: int) -> int:
+    return _load().oracle_int4_sym_value(code)
+
+
+# ---------------------------------------------------------------- Q4_K metadata
+
+def q4k_unpack_scales(B) -> tuple[list[int], list[int]]:
+    b = np.ascontiguousarray(np.asarray(B, dtype=np.uint8))
+    assert b.size == 12
+    s = np.zeros(8, dtype=np.uint32)
+    m = np.zeros(8, dtype=np.uint32)
+    _load().oracle_q4k_unpack_scales(_ptr(b), _ptr(s), _ptr(m))
+    return s.tolist(), m.tolist()
+
+
+def q4k_pack_scales(s, m) -> np.ndarray:
+    sa = np.ascontiguousarray(np.asarray(s, dtype=np.uint32))
+    ma = np.ascontiguousarray(np.asarray(m, dtype=np.uint32))
+    out = np.zeros(12, dtype=np.uint8)
+    _load().oracle_q4k_pack_scales(_ptr(sa), _ptr(ma), _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- bit streams and layouts
+
+def pack_bits(vals, bits: int) -> np.ndarray:
+    v = np.ascontiguousarray(np.asarray(vals, dtype=np.uint32))
+    words = np.zeros((v.size * bits + 31) // 32, dtype=np.uint32)
+    _load().oracle_pack_bits(_ptr(v), v.size, bits, _ptr(words))
+    return words
+
+
+def unpack_bits(words, bits: int, count: int) -> np.ndarray:
+    w = np.ascontiguousarray(np.asarray(words, dtype=np.uint32))
+    out = np.zeros(count, dtype=np.uint32)
+    _load().oracle_unpack_bits(_ptr(w), count, bits, _ptr(out))
+    return out
+
+
+def gptq_pack(q: np.ndarray) -> np.ndarray:
+    """q u8 [K][N] codes -> GPTQ qweight as uint32 [K/8][N]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    K, N = q.shape
+    out = np.zeros((K // 8, N), dtype=np.uint32)
+    _load().oracle_gptq_pack(_ptr(q), K, N, _ptr(out))
+    return out
+
+
+def gptq_unpack(qw: np.ndarray) -> np.ndarray:
+    qw = np.ascontiguousarray(qw).view(np.uint32)
+    K8, N = qw.shape
+    out = np.zeros((K8 * 8, N), dtype=np.uint8)
+    _load().oracle_gptq_unpack(_ptr(qw), K8 * 8, N, _ptr(out))
+    return out
+
+
+def awq_pack(q: np.ndarray) -> np.ndarray:
+    """q u8 [K][N] codes -> AWQ qweight as uint32 [K][N/8]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    K, N = q.shape
+    out = np.zeros((K, N // 8), dtype=np.uint32)
+    _load().oracle_awq_pack(_ptr(q), K, N, _ptr(out))
+    return out
+
+
+def awq_unpack(qw: np.ndarray) -> np.ndarray:
+    qw = np.ascontiguousarray(qw).view(np.uint32)
+    K, N8 = qw.shape
+    out = np.zeros((K, N8 * 8), dtype=np.uint8)
+    _load().oracle_awq_unpack(_ptr(qw), K, N8 * 8, _ptr(out))
+    return out
+
+
+def q4_0_pack(q: np.ndarray, d_bits: np.ndarray) -> np.ndarray:
+    """q u8 [K][N], d_bits u16 [N][K/32] -> Q4_0 blocks u8 [N][K/32][18]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    K, N = q.shape
+    d = np.ascontiguousarray(d_bits, dtype=np.uint16)
+    assert d.shape == (N, K // 32)
+    out = np.zeros((N, K // 32, 18), dtype=np.uint8)
+    _load().oracle_q4_0_pack(_ptr(q), _ptr(d), K, N, _ptr(out))
+    return out
+
+
+def q4_0_unpack(blocks: np.ndarray, K: int, N: int) -> tuple[np.ndarray, np.ndarray]:
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    assert b.size == N * (K // 32) * 18
+    q = np.zeros((K, N), dtype=np.uint8)
+    d = np.zeros((N, K // 32), dtype=np.uint16)
+    _load().oracle_q4_0_unpack(_ptr(b), K, N, _ptr(q), _ptr(d))
+    return q, d
+
+
+def affine_dequant(q: np.ndarray, scale_bits: np.ndarray, zeros: np.ndarray, group: int) -> np.ndarray:
+    """w[k][n] = s[k/g][n] * (q[k][n] - z[k/g][n]) as binary32, [K][N]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    K, N = q.shape
+    s = np.ascontiguousarray(scale_bits, dtype=np.uint16)
+    z = np.ascontiguousarray(zeros, dtype=np.uint8)
+    assert s.shape == (K // group, N) and z.shape == (K // group, N)
+    out = np.zeros((K, N), dtype=np.float32)
+    _load().oracle_affine_dequant(_ptr(q), _ptr(s), _ptr(z), K, N, group, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- dequant and dots
+
+def _scales_or_null(scales):
+    if scales is None:
+        return None, ctypes.c_void_p(0)
+    s = np.ascontiguousarray(scales, dtype=np.uint8)
+    return s, _ptr(s)
+
+
+def dequant_rows(fmt: int, data: np.ndarray, scales, scale2: float, k: int, rows) -> np.ndarray:
+    """Dequantized rows [len(rows)][k] (binary32) of an n x k weight."""
+    d = np.ascontiguousarray(data).view(np.uint8)
+    s_keep, s_ptr = _scales_or_null(scales)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.zeros((r.size, k), dtype=np.float32)
+    rc = _load().oracle_dequant_rows(fmt, _ptr(d), s_ptr, scale2, k, _ptr(r), r.size, _ptr(out))
+    if rc:
+        raise ValueError("oracle: unsupported format %r" % fmt)
+    return out
+
+
+def gemv_rows(fmt: int, data, scales, scale2: float, k: int, x: np.ndarray, rows):
+    """(y, S) in binary64 for the chosen rows: y = W_hat[rows] @ x and
+    S = |W_hat[rows]| @ |x|. x is float32 or bfloat16 bits (uint16)."""
+    d = np.ascontiguousarray(data).view(np.uint8)
+    s_keep, s_ptr = _scales_or_null(scales)
+    xa = np.ascontiguousarray(x)
+    if xa.dtype == np.float32:
+        xdt = 0
+    elif xa.dtype == np.uint16:
+        xdt = 1
+    else:
+        raise TypeError("x must be float32 or bfloat16 bits (uint16)")
+    assert xa.size == k
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    y = np.zeros(r.size, dtype=np.float64)
+    sa = np.zeros(r.size, dtype=np.float64)
+    wscr = np.zeros(k, dtype=np.float32)
+    xscr = np.zeros(k, dtype=np.float64)
+    rc = _load().oracle_gemv_rows(fmt, _ptr(d), s_ptr, scale2, k, _ptr(xa), xdt, _ptr(r), r.size,
+                                  _ptr(y), _ptr(sa), _ptr(wscr), _ptr(xscr))
+    if rc:
+        raise ValueError("oracle: unsupported format %r" % fmt)
+    return y, sa
+
+
+def gemm_entries(fmt: int, data, scales, scale2: float, k: int, X_bits: np.ndarray, ms, ns):
+    """(Y, S) in binary64 for entries (ms[i], ns[i]) of X @ W_hat^T, X bf16 bits [M][k]."""
+    d = np.ascontiguousarray(data).view(np.uint8)
+    s_keep, s_ptr = _scales_or_null(scales)
+    X = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    ms = np.asarray(ms, dtype=np.int64)
+    ns = np.asarray(ns, dtype=np.int64)
+    order = np.argsort(ns, kind="stable")
+    ms_o = np.ascontiguousarray(ms[order])
+    ns_o = np.ascontiguousarray(ns[order])
+    y = np.zeros(ms.size, dtype=np.float64)
+    sa = np.zeros(ms.size, dtype=np.float64)
+    wscr = np.zeros(k, dtype=np.float32)
+    xscr = np.zeros(k, dtype=np.float64)
+    rc = _load().oracle_gemm_entries(fmt, _ptr(d), s_ptr, scale2, k, _ptr(X), X.shape[1], _ptr(ms_o),
+                                     _ptr(ns_o), ms.size, _ptr(y), _ptr(sa), _ptr(wscr), _ptr(xscr))
+    if rc:
+        raise ValueError("oracle: unsupported format %r" % fmt)
+    y_out = np.empty_like(y)
+    s_out = np.empty_like(sa)
+    y_out[order] = y
+    s_out[order] = sa
+    return y_out, s_out

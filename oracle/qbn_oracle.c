@@ -1,0 +1,532 @@
+/*
+ * qbn oracle: plain, slow CPU definitions of what 4-bit block-quantized
+ * weights decode to, of the dot products built on them, and of the int4
+ * layout repacks.
+ *
+ * TEST INFRASTRUCTURE ONLY. The library's product path never links, loads
+ * or calls this file. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it. It shares no source with the HIP
+ * kernels: every decoder below is written from the formats' definitions,
+ * not from any table or helper used on the GPU.
+ *
+ * Build: gcc -O2 -std=c11 -fPIC -shared, no SIMD intrinsics, no fast-math.
+ *
+ * Sources (page title, section):
+ *  [FB]  "Four Bits, Three Contracts: an interactive guide to MXFP4, NVFP4
+ *        and Q4_K" (shivasnotes.com, blog 6006)
+ *  [WK]  "Why 4-Bit Quantization Is King: Understanding Q4_K, MXFP4, and
+ *        NVFP4" (shivasnotes.com, blog 5996)
+ *  [BP]  "Bit Packing Architecture" (aicassindra.com)
+ *  [NV]  "Chapter 7 - NVFP4: the native lane" (Muser book,
+ *        highperformanceailab.com)
+ *
+ * Every decoded weight is an IEEE binary32 value; products that the format
+ * definition makes exact are formed in binary64 and cast once, and the only
+ * inexact steps (NVFP4's multiply by scale2, Q4_K's gain-minus-offset) are
+ * rounded exactly once to binary32, as the formats prescribe.
+ * Dot products are formed in binary64 with Neumaier-compensated sums.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------ */
+/* Scalar decoders                                                     */
+/* ------------------------------------------------------------------ */
+
+/* E2M1 element code: 1 sign, 2 exponent, 1 fraction bit, exponent bias 1.
+ * Exponent field 0 holds zero and the single subnormal magnitude 0.5.
+ * Code 8 is negative zero. [FB] section 1; [NV] section 7.1, Figure 7.1. */
+ORACLE_API double oracle_e2m1(unsigned code)
+{
+    unsigned s = (code >> 3) & 1u;
+    unsigned e = (code >> 1) & 3u;
+    unsigned m = code & 1u;
+    double mag;
+    if (e == 0)
+        mag = 0.5 * (double)m;
+    else
+        mag = ldexp(1.0 + (double)m / 2.0, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+/* E8M0 shared scale: an unsigned biased exponent, value 2^(b-127); the byte
+ * 255 is reserved for NaN and there is no zero. [FB] section 3. */
+ORACLE_API double oracle_e8m0(unsigned b)
+{
+    b &= 0xFFu;
+    if (b == 255u)
+        return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* E4M3FN scale: sign, 4 exponent bits with bias 7, 3 fraction bits, no
+ * infinities; NaN only where exponent and fraction are all ones (0x7f, 0xff);
+ * exponent field 0 is subnormal with value fraction * 2^-9.
+ * [FB] section 4; [NV] sections 7.1, 7.2 and 7.8. */
+ORACLE_API double oracle_e4m3fn(unsigned b)
+{
+    b &= 0xFFu;
+    unsigned s = b >> 7;
+    unsigned e = (b >> 3) & 15u;
+    unsigned m = b & 7u;
+    double mag;
+    if (e == 15u && m == 7u)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -mag : mag;
+}
+
+/* IEEE binary16 from its bit pattern (the fp16 d, dmin, Q4_0 d and group
+ * scales are little-endian binary16). */
+ORACLE_API double oracle_f16(unsigned h)
+{
+    h &= 0xFFFFu;
+    unsigned s = h >> 15;
+    unsigned e = (h >> 10) & 31u;
+    unsigned f = h & 1023u;
+    double mag;
+    if (e == 31u)
+        mag = f ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)f, -24);
+    else
+        mag = ldexp(1.0 + (double)f / 1024.0, (int)e - 15);
+    return s ? -mag : mag;
+}
+
+/* bfloat16 bit pattern to its value (the upper half of a binary32). */
+ORACLE_API double oracle_bf16_value(unsigned bits)
+{
+    uint32_t u = (uint32_t)(bits & 0xFFFFu) << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* binary32 to bfloat16 with round-to-nearest-even on the dropped 16 bits.
+ * NaN stays NaN (quiet). */
+ORACLE_API unsigned oracle_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return ((u >> 16) | 0x40u) & 0xFFFFu;
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (u >> 16) & 0xFFFFu;
+}
+
+static unsigned rd_u16(const uint8_t *p) { return (unsigned)p[0] | ((unsigned)p[1] << 8); }
+static uint32_t rd_u32(const uint8_t *p)
+{
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+/* Logical element i of a row of two-codes-per-byte E2M1: the low nibble of
+ * byte i/2 holds the even element, the high nibble the odd one.
+ * [NV] Figure 7.2; the MXFP4 rows use the same order. */
+static unsigned nibble_lo_even(const uint8_t *row, int64_t i)
+{
+    uint8_t byte = row[i / 2];
+    return (i & 1) ? (byte >> 4) : (byte & 15u);
+}
+
+/* ------------------------------------------------------------------ */
+/* Q4_K super-block metadata                                          */
+/* ------------------------------------------------------------------ */
+
+/* Unpack the eight 6-bit (scale, min) pairs from the 12 metadata bytes B.
+ * Pairs 0..3 keep their six bits whole in B[j] and B[j+4]; pairs 4..7 put
+ * their low four bits in B[j+4] (scale low nibble, min high nibble) and their
+ * top two bits in the top of B[j-4] (scale) and B[j] (min).
+ * [FB] section 6. */
+ORACLE_API void oracle_q4k_unpack_scales(const uint8_t *B, unsigned *s, unsigned *m)
+{
+    for (int j = 0; j < 8; ++j) {
+        if (j < 4) {
+            s[j] = B[j] & 63u;
+            m[j] = B[j + 4] & 63u;
+        } else {
+            s[j] = (unsigned)(B[j + 4] & 15u) | ((unsigned)(B[j - 4] >> 6) << 4);
+            m[j] = (unsigned)(B[j + 4] >> 4) | ((unsigned)(B[j] >> 6) << 4);
+        }
+    }
+}
+
+/* Inverse of the above (encode side, used to build fixtures). */
+ORACLE_API void oracle_q4k_pack_scales(const unsigned *s, const unsigned *m, uint8_t *B)
+{
+    memset(B, 0, 12);
+    for (int j = 0; j < 4; ++j) {
+        B[j] = (uint8_t)((s[j] & 63u) | ((s[j + 4] >> 4) << 6));
+        B[j + 4] = (uint8_t)((m[j] & 63u) | ((m[j + 4] >> 4) << 6));
+        B[j + 8] = (uint8_t)((s[j + 4] & 15u) | ((m[j + 4] & 15u) << 4));
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Row dequantizers: decode row r of an n x k weight into out[0..k)    */
+/* ------------------------------------------------------------------ */
+
+/* MXFP4: codes u8 [n][k/2] (low nibble = even element), E8M0 scales u8
+ * [n][k/32] with groups running along k. w = E2M1(code) * 2^(b-127); the
+ * product is exact in binary32 or overflows to infinity. [FB] section 3. */
+static void mxfp4_row(const uint8_t *codes, const uint8_t *scales, int64_t k, int64_t r, float *out)
+{
+    const uint8_t *crow = codes + r * (k / 2);
+    const uint8_t *srow = scales + r * (k / 32);
+    for (int64_t i = 0; i < k; ++i)
+        out[i] = (float)(oracle_e2m1(nibble_lo_even(crow, i)) * oracle_e8m0(srow[i / 32]));
+}
+
+/* NVFP4: codes u8 [n][k/2], E4M3FN scales u8 [n][k/16], one binary32 scale2
+ * per tensor. Pinned order: (E2M1 * E4M3FN) first (exact), then times scale2
+ * with one rounding to binary32. [NV] sections 7.1 and 7.2; [FB] section 4. */
+static void nvfp4_row(const uint8_t *codes, const uint8_t *scales, float scale2, int64_t k, int64_t r,
+                      float *out)
+{
+    const uint8_t *crow = codes + r * (k / 2);
+    const uint8_t *srow = scales + r * (k / 16);
+    for (int64_t i = 0; i < k; ++i) {
+        float local = (float)(oracle_e2m1(nibble_lo_even(crow, i)) * oracle_e4m3fn(srow[i / 16]));
+        out[i] = (float)((double)local * (double)scale2);
+    }
+}
+
+/* Q4_K: 144-byte super-blocks of 256 weights, [n][k/256]. Byte layout:
+ * fp16 d at 0, fp16 dmin at 2, 12 metadata bytes at 4, 128 code bytes at 16.
+ * Code byte 32c+l (c = 0..3, l = 0..31) holds, in its low nibble, output
+ * 64c+l (sub-block 2c) and, in its high nibble, output 64c+32+l (sub-block
+ * 2c+1). w = (d*s_j)*q - dmin*m_j: the gain and offset are exact binary32
+ * products and the difference is rounded once.
+ * [FB] sections 5 and 6; [WK] sections 4 and 7b. */
+static void q4k_row(const uint8_t *blocks, int64_t k, int64_t r, float *out)
+{
+    int64_t nb = k / 256;
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t *blk = blocks + (r * nb + b) * 144;
+        double d = oracle_f16(rd_u16(blk + 0));
+        double dmin = oracle_f16(rd_u16(blk + 2));
+        unsigned s[8], m[8];
+        oracle_q4k_unpack_scales(blk + 4, s, m);
+        const uint8_t *qs = blk + 16;
+        for (int c = 0; c < 4; ++c) {
+            for (int l = 0; l < 32; ++l) {
+                uint8_t byte = qs[32 * c + l];
+                for (int half = 0; half < 2; ++half) {
+                    int j = 2 * c + half;
+                    unsigned q = half ? (byte >> 4) : (byte & 15u);
+                    float gain = (float)(d * (double)s[j]);
+                    float offset = (float)(dmin * (double)m[j]);
+                    out[b * 256 + 64 * c + 32 * half + l] = fmaf(gain, (float)q, -offset);
+                }
+            }
+        }
+    }
+}
+
+/* Q4_0: 18-byte blocks of 32 weights, [n][k/32]: fp16 d, then 16 bytes where
+ * byte j holds element j (low nibble) and element j+16 (high nibble).
+ * w = d * (q - 8), exact in binary32. [BP] "Real layouts compared". */
+static void q4_0_row(const uint8_t *blocks, int64_t k, int64_t r, float *out)
+{
+    int64_t nb = k / 32;
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t *blk = blocks + (r * nb + b) * 18;
+        double d = oracle_f16(rd_u16(blk));
+        for (int j = 0; j < 16; ++j) {
+            uint8_t byte = blk[2 + j];
+            out[b * 32 + j] = (float)(d * ((double)(byte & 15u) - 8.0));
+            out[b * 32 + j + 16] = (float)(d * ((double)(byte >> 4) - 8.0));
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* int4 layouts: GPTQ, AWQ, Q4_0 codes <-> logical u8 matrix q[K][N]   */
+/* ------------------------------------------------------------------ */
+
+/* Generic b-bit little-endian word stream: logical element i occupies bits
+ * [i*b, (i+1)*b) of a stream of 32-bit words; an element may straddle two
+ * words when b does not divide 32. [BP] "The packing arithmetic". */
+ORACLE_API void oracle_pack_bits(const uint32_t *vals, int64_t count, int bits, uint32_t *words)
+{
+    int64_t nwords = (count * bits + 31) / 32;
+    for (int64_t w = 0; w < nwords; ++w)
+        words[w] = 0;
+    uint64_t mask = (bits >= 32) ? 0xFFFFFFFFull : ((1ull << bits) - 1ull);
+    for (int64_t i = 0; i < count; ++i) {
+        uint64_t v = (uint64_t)vals[i] & mask;
+        int64_t pos = i * bits;
+        int64_t w = pos / 32;
+        int off = (int)(pos % 32);
+        words[w] |= (uint32_t)((v << off) & 0xFFFFFFFFull);
+        if (off + bits > 32)
+            words[w + 1] |= (uint32_t)(v >> (32 - off));
+    }
+}
+
+ORACLE_API void oracle_unpack_bits(const uint32_t *words, int64_t count, int bits, uint32_t *vals)
+{
+    uint64_t mask = (bits >= 32) ? 0xFFFFFFFFull : ((1ull << bits) - 1ull);
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t pos = i * bits;
+        int64_t w = pos / 32;
+        int off = (int)(pos % 32);
+        uint64_t v = (uint64_t)words[w] >> off;
+        if (off + bits > 32)
+            v |= (uint64_t)words[w + 1] << (32 - off);
+        vals[i] = (uint32_t)(v & mask);
+    }
+}
+
+/* AWQ slot order: slot t of a word holds logical column ORDER[t] of its
+ * group of eight. [BP] "Real layouts compared". */
+static const int AWQ_ORDER[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+
+/* GPTQ qweight: int32 [K/8][N], packed along K; each column is a 4-bit
+ * stream along K, so row 8r+j sits at bits 4j of word [r][n]. [BP]. */
+ORACLE_API void oracle_gptq_pack(const uint8_t *q, int64_t K, int64_t N, uint32_t *qw)
+{
+    uint32_t col[8], word;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t r = 0; r < K / 8; ++r) {
+            for (int j = 0; j < 8; ++j)
+                col[j] = q[(r * 8 + j) * N + n];
+            oracle_pack_bits(col, 8, 4, &word);
+            qw[r * N + n] = word;
+        }
+}
+
+ORACLE_API void oracle_gptq_unpack(const uint32_t *qw, int64_t K, int64_t N, uint8_t *q)
+{
+    uint32_t col[8];
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t r = 0; r < K / 8; ++r) {
+            oracle_unpack_bits(&qw[r * N + n], 8, 4, col);
+            for (int j = 0; j < 8; ++j)
+                q[(r * 8 + j) * N + n] = (uint8_t)col[j];
+        }
+}
+
+/* AWQ qweight: int32 [K][N/8], packed along N; within each group of eight
+ * columns the slots hold columns 0,2,4,6,1,3,5,7. [BP]. */
+ORACLE_API void oracle_awq_pack(const uint8_t *q, int64_t K, int64_t N, uint32_t *qw)
+{
+    uint32_t slots[8], word;
+    for (int64_t kk = 0; kk < K; ++kk)
+        for (int64_t g = 0; g < N / 8; ++g) {
+            for (int t = 0; t < 8; ++t)
+                slots[t] = q[kk * N + g * 8 + AWQ_ORDER[t]];
+            oracle_pack_bits(slots, 8, 4, &word);
+            qw[kk * (N / 8) + g] = word;
+        }
+}
+
+ORACLE_API void oracle_awq_unpack(const uint32_t *qw, int64_t K, int64_t N, uint8_t *q)
+{
+    uint32_t slots[8];
+    for (int64_t kk = 0; kk < K; ++kk)
+        for (int64_t g = 0; g < N / 8; ++g) {
+            oracle_unpack_bits(&qw[kk * (N / 8) + g], 8, 4, slots);
+            for (int t = 0; t < 8; ++t)
+                q[kk * N + g * 8 + AWQ_ORDER[t]] = (uint8_t)slots[t];
+        }
+}
+
+/* Q4_0 code layout for a K x N logical matrix: blocks run along K within
+ * each output column n and are stored [N][K/32] x 18 bytes; block (n, b)
+ * holds q[32b .. 32b+31][n], byte j = element j (low) | element j+16 (high).
+ * d_bits[(n*(K/32)) + b] is written as the fp16 d of each block. */
+ORACLE_API void oracle_q4_0_pack(const uint8_t *q, const uint16_t *d_bits, int64_t K, int64_t N,
+                                 uint8_t *blocks)
+{
+    int64_t nb = K / 32;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < nb; ++b) {
+            uint8_t *blk = blocks + (n * nb + b) * 18;
+            uint16_t d = d_bits[n * nb + b];
+            blk[0] = (uint8_t)(d & 0xFF);
+            blk[1] = (uint8_t)(d >> 8);
+            for (int j = 0; j < 16; ++j) {
+                unsigned lo = q[(32 * b + j) * N + n] & 15u;
+                unsigned hi = q[(32 * b + j + 16) * N + n] & 15u;
+                blk[2 + j] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+}
+
+ORACLE_API void oracle_q4_0_unpack(const uint8_t *blocks, int64_t K, int64_t N, uint8_t *q, uint16_t *d_bits)
+{
+    int64_t nb = K / 32;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = blocks + (n * nb + b) * 18;
+            if (d_bits)
+                d_bits[n * nb + b] = (uint16_t)rd_u16(blk);
+            for (int j = 0; j < 16; ++j) {
+                q[(32 * b + j) * N + n] = blk[2 + j] & 15u;
+                q[(32 * b + j + 16) * N + n] = blk[2 + j] >> 4;
+            }
+        }
+}
+
+/* Affine int4 dequantization of the logical matrix: w = s * (q - z) with
+ * fp16 s and integer zero point z per group of g rows along K; exact in
+ * binary32. [BP] "Repacking between formats", step 2. Output [K][N]. */
+ORACLE_API void oracle_affine_dequant(const uint8_t *q, const uint16_t *scale_bits, const uint8_t *zeros,
+                                      int64_t K, int64_t N, int64_t g, float *out)
+{
+    for (int64_t kk = 0; kk < K; ++kk)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = oracle_f16(scale_bits[(kk / g) * N + n]);
+            double z = (double)zeros[(kk / g) * N + n];
+            out[kk * N + n] = (float)(s * ((double)q[kk * N + n] - z));
+        }
+}
+
+/* ------------------------------------------------------------------ */
+/* Format dispatch: dequantize chosen rows of an n x k weight          */
+/* ------------------------------------------------------------------ */
+
+enum { OR_MXFP4 = 1, OR_NVFP4 = 2, OR_Q4_K = 3, OR_Q4_0 = 4 };
+
+static int row_dequant(int fmt, const uint8_t *data, const uint8_t *scales, float scale2, int64_t k,
+                       int64_t r, float *out)
+{
+    switch (fmt) {
+    case OR_MXFP4: mxfp4_row(data, scales, k, r, out); return 0;
+    case OR_NVFP4: nvfp4_row(data, scales, scale2, k, r, out); return 0;
+    case OR_Q4_K: q4k_row(data, k, r, out); return 0;
+    case OR_Q4_0: q4_0_row(data, k, r, out); return 0;
+    default: return -1;
+    }
+}
+
+/* out[i][0..k) = dequantized row rows[i]. Returns 0, or -1 on a bad format. */
+ORACLE_API int oracle_dequant_rows(int fmt, const uint8_t *data, const uint8_t *scales, float scale2, int64_t k,
+                                   const int64_t *rows, int64_t nrows, float *out)
+{
+    for (int64_t i = 0; i < nrows; ++i)
+        if (row_dequant(fmt, data, scales, scale2, k, rows[i], out + i * k))
+            return -1;
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dot products                                                        */
+/* ------------------------------------------------------------------ */
+
+/* Neumaier-compensated binary64 sum of w[i]*x[i] (each product exact in
+ * binary64 since both factors carry at most 24 significant bits), and the
+ * plain binary64 sum of |w[i]*x[i]|. */
+static void dot_f64(const float *w, const double *x, int64_t k, double *y, double *sabs)
+{
+    double sum = 0.0, comp = 0.0, a = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        double p = (double)w[i] * x[i];
+        double t = sum + p;
+        if (fabs(sum) >= fabs(p))
+            comp += (sum - t) + p;
+        else
+            comp += (p - t) + sum;
+        sum = t;
+        a += fabs(p);
+    }
+    *y = sum + comp;
+    *sabs = a;
+}
+
+/* Activation vector values: xdtype 0 = binary32, 1 = bfloat16 bits. */
+static void load_x(const void *x, int xdtype, int64_t k, double *xv)
+{
+    for (int64_t i = 0; i < k; ++i) {
+        if (xdtype == 1)
+            xv[i] = oracle_bf16_value(((const uint16_t *)x)[i]);
+        else
+            xv[i] = (double)((const float *)x)[i];
+    }
+}
+
+/* y[i] = sum_k w[rows[i]][k] * x[k] and s[i] = sum_k |w x| for the chosen
+ * rows. scratch must hold k floats + k doubles (caller-provided so the
+ * oracle itself never allocates). A fused kernel never materializes w;
+ * this definition does, one row at a time. [WK] sections 1 and 7b. */
+ORACLE_API int oracle_gemv_rows(int fmt, const uint8_t *data, const uint8_t *scales, float scale2, int64_t k,
+                                const void *x, int xdtype, const int64_t *rows, int64_t nrows, double *y,
+                                double *sabs, float *wscratch, double *xscratch)
+{
+    load_x(x, xdtype, k, xscratch);
+    for (int64_t i = 0; i < nrows; ++i) {
+        if (row_dequant(fmt, data, scales, scale2, k, rows[i], wscratch))
+            return -1;
+        dot_f64(wscratch, xscratch, k, &y[i], &sabs[i]);
+    }
+    return 0;
+}
+
+/* Sampled GEMM entries: Y[m][n] = sum_k X[m][k] * w[n][k] for the pairs
+ * (ms[i], ns[i]); X is bfloat16 bits [M][ldx]. Entries are grouped by the
+ * caller; each weight row is decoded once per call of this function for
+ * every pair (plain and slow by design). */
+ORACLE_API int oracle_gemm_entries(int fmt, const uint8_t *data, const uint8_t *scales, float scale2, int64_t k,
+                                   const uint16_t *X, int64_t ldx, const int64_t *ms, const int64_t *ns,
+                                   int64_t npairs, double *y, double *sabs, float *wscratch, double *xscratch)
+{
+    int64_t cur_n = -1;
+    for (int64_t i = 0; i < npairs; ++i) {
+        if (ns[i] != cur_n) {
+            if (row_dequant(fmt, data, scales, scale2, k, ns[i], wscratch))
+                return -1;
+            cur_n = ns[i];
+        }
+        load_x(X + ms[i] * ldx, 1, k, xscratch);
+        dot_f64(wscratch, xscratch, k, &y[i], &sabs[i]);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Encode-side helpers used only to reproduce the pages' worked facts  */
+/* ------------------------------------------------------------------ */
+
+/* Nearest scaled E2M1 code to w at scale s; on an exact tie the lowest
+ * unsigned code wins (the lab convention of [FB] section 2). */
+ORACLE_API unsigned oracle_e2m1_nearest(double w, double s)
+{
+    unsigned best = 0;
+    double best_err = INFINITY;
+    for (unsigned c = 0; c < 16; ++c) {
+        double err = fabs(oracle_e2m1(c) * s - w);
+        if (err < best_err) {
+            best_err = err;
+            best = c;
+        }
+    }
+    return best;
+}
+
+/* Symmetric signed int4: q = clip(round(w/s), -8, 7) with round half to even,
+ * stored as the 4-bit two's complement pattern. [WK] section 1. */
+ORACLE_API unsigned oracle_int4_sym_code(double w, double s)
+{
+    double q = nearbyint(w / s);
+    if (q < -8.0)
+        q = -8.0;
+    if (q > 7.0)
+        q = 7.0;
+    return (unsigned)((int)q & 15);
+}
+
+ORACLE_API int oracle_int4_sym_value(unsigned code)
+{
+    code &= 15u;
+    return (code & 8u) ? (int)code - 16 : (int)code;
+}
