@@ -1,0 +1,255 @@
+"""Python binding of libqbn: fused dequantize-and-dot over packed 4-bit
+block-quantized weights (MXFP4, NVFP4, Q4_K), bulk dequantization of six
+formats and bit-exact int4 layout repacks, on AMD MI355X (gfx950).
+
+This module only marshals arguments: it turns torch device tensors into raw
+pointers, passes torch's current HIP stream, and raises on a nonzero status.
+Every step of the computation runs in the HIP kernels of libqbn.so; there is
+no CPU or PyTorch fallback. The names mirror the C ABI in include/qbn.h
+(``qbn_quantized_gemv`` -> ``quantized_gemv`` and so on).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "QTensor", "QbnError", "quantized_gemv", "quantized_gemm", "dequantize", "repack", "validate", "nbytes",
+    "status_string", "lib_path", "FORMATS",
+]
+
+FORMATS = {"mxfp4": 1, "nvfp4": 2, "q4_k": 3, "q4_0": 4, "gptq4": 5, "awq4": 6}
+_F32, _BF16, _F16 = 0, 1, 2
+_DTYPES = {torch.float32: _F32, torch.bfloat16: _BF16, torch.float16: _F16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqbn.so")
+_lock = threading.Lock()
+_lib = None
+
+EXPORTED = (
+    "qbn_abi_version", "qbn_tensor_struct_size", "qbn_status_string", "qbn_last_hip_error", "qbn_bytes",
+    "qbn_quantized_gemv", "qbn_quantized_gemm", "qbn_dequantize", "qbn_repack", "qbn_validate",
+)
+
+
+class QbnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = _load().qbn_status_string(status).decode()
+        if status == 9:
+            detail += " (hipError %d)" % _load().qbn_last_hip_error()
+        super().__init__("%s: qbn status %d: %s" % (where, status, detail))
+
+
+class _CTensor(ctypes.Structure):
+    _fields_ = [
+        ("format", ctypes.c_int32), ("group", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
+        ("scale2", ctypes.c_float), ("reserved", ctypes.c_int32),
+    ]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libqbn.so is not built; run `python -m bit_block_quantized_nibble_amd.build` "
+                               "(or __graft_entry__.build()) first")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        T = ctypes.POINTER(_CTensor)
+        lib.qbn_abi_version.restype = I32
+        lib.qbn_tensor_struct_size.restype = ctypes.c_size_t
+        lib.qbn_status_string.argtypes = [I32]
+        lib.qbn_status_string.restype = ctypes.c_char_p
+        lib.qbn_last_hip_error.restype = I32
+        lib.qbn_bytes.argtypes = [I32, I64, I64, I32, I32]
+        lib.qbn_bytes.restype = I64
+        lib.qbn_quantized_gemv.argtypes = [T, P, I32, P, I32, P]
+        lib.qbn_quantized_gemv.restype = I32
+        lib.qbn_quantized_gemm.argtypes = [T, I64, P, I32, I64, P, I32, I64, P]
+        lib.qbn_quantized_gemm.restype = I32
+        lib.qbn_dequantize.argtypes = [T, P, I32, I32, P]
+        lib.qbn_dequantize.restype = I32
+        lib.qbn_repack.argtypes = [T, I32, I32, P, P, P, P]
+        lib.qbn_repack.restype = I32
+        lib.qbn_validate.argtypes = [T, P, P]
+        lib.qbn_validate.restype = I32
+        if lib.qbn_abi_version() != 1 or lib.qbn_tensor_struct_size() != ctypes.sizeof(_CTensor):
+            raise RuntimeError("libqbn ABI mismatch: rebuild the library")
+        _lib = lib
+        return lib
+
+
+def _ptr(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device (cuda) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+@dataclass
+class QTensor:
+    """A quantized weight W (n output rows x k inputs) in device memory.
+
+    Buffers follow include/qbn.h: MXFP4 / NVFP4 data u8 [n][k/2] with scale
+    bytes [n][k/32] / [n][k/16] (NVFP4 also takes scale2); Q4_K data u8
+    [n][k/256][144]; Q4_0 data u8 [n][k/32][18]; GPTQ4 data int32 [k/8][n],
+    AWQ4 data int32 [k][n/8], both with fp16 scales and u8 logical zero points
+    [k/group][n].
+    """
+    format: str
+    n: int
+    k: int
+    data: torch.Tensor
+    scales: Optional[torch.Tensor] = None
+    zeros: Optional[torch.Tensor] = None
+    scale2: float = 1.0
+    group: int = 0
+
+    def _c(self) -> _CTensor:
+        if self.format not in FORMATS:
+            raise ValueError("unknown format %r" % self.format)
+        c = _CTensor()
+        c.format = FORMATS[self.format]
+        c.group = int(self.group)
+        c.n = int(self.n)
+        c.k = int(self.k)
+        c.data = _ptr(self.data, "data")
+        c.scales = _ptr(self.scales, "scales")
+        c.zeros = _ptr(self.zeros, "zeros")
+        c.scale2 = float(self.scale2)
+        c.reserved = 0
+        return c
+
+    @property
+    def device(self) -> torch.device:
+        return self.data.device
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QbnError(status, where)
+
+
+def status_string(status: int) -> str:
+    return _load().qbn_status_string(status).decode()
+
+
+def nbytes(format: str, n: int, k: int, group: int = 0, part: int = 0) -> int:
+    """Bytes of part 0 (data), 1 (scales) or 2 (zeros); -1 if invalid."""
+    return int(_load().qbn_bytes(FORMATS[format], n, k, group, part))
+
+
+def quantized_gemv(w: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = W_hat @ x (float32 [n]) for x float32 or bfloat16 [k]."""
+    lib = _load()
+    if x.dtype not in _DTYPES:
+        raise TypeError("x dtype %s" % x.dtype)
+    if y is None:
+        y = torch.empty(w.n, dtype=torch.float32, device=w.device)
+    ct = w._c()
+    _check(lib.qbn_quantized_gemv(ctypes.byref(ct), _ptr(x, "x"), _DTYPES[x.dtype], _ptr(y, "y"),
+                                  _DTYPES.get(y.dtype, -1), _stream(w.device)), "qbn_quantized_gemv")
+    return y
+
+
+def quantized_gemm(w: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X @ W_hat^T, X bfloat16 [m][k] -> Y bfloat16 [m][n]."""
+    lib = _load()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [m][k]")
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.bfloat16, device=w.device)
+    ct = w._c()
+    ldx = x.stride(0) if x.shape[0] > 1 else x.shape[1]
+    ldy = y.stride(0) if y.shape[0] > 1 else y.shape[1]
+    if x.stride(1) != 1 or y.stride(1) != 1:
+        raise ValueError("rows of x and y must be contiguous")
+    _check(lib.qbn_quantized_gemm(ctypes.byref(ct), m, ctypes.c_void_p(x.data_ptr()), _DTYPES.get(x.dtype, -1), ldx,
+                                  ctypes.c_void_p(y.data_ptr()), _DTYPES.get(y.dtype, -1), ldy, _stream(w.device)),
+           "qbn_quantized_gemm")
+    return y
+
+
+def dequantize(w: QTensor, out: Optional[torch.Tensor] = None, dtype: torch.dtype = torch.float32,
+               layout: str = "nk") -> torch.Tensor:
+    """W_hat as float32 or bfloat16, layout "nk" ([n][k]) or "kn" ([k][n])."""
+    lib = _load()
+    lay = {"nk": 0, "kn": 1}[layout]
+    if out is None:
+        shape = (w.n, w.k) if lay == 0 else (w.k, w.n)
+        out = torch.empty(shape, dtype=dtype, device=w.device)
+    ct = w._c()
+    _check(lib.qbn_dequantize(ctypes.byref(ct), _ptr(out, "out"), _DTYPES.get(out.dtype, -1), lay,
+                              _stream(w.device)), "qbn_dequantize")
+    return out
+
+
+def repack(src: QTensor, dst_format: str, dst_group: Optional[int] = None, data: Optional[torch.Tensor] = None,
+           scales: Optional[torch.Tensor] = None, zeros: Optional[torch.Tensor] = None) -> QTensor:
+    """Repack int4 codes between GPTQ4, AWQ4 and Q4_0 (bit-exact)."""
+    lib = _load()
+    n, k, dev = src.n, src.k, src.device
+    fmt = FORMATS[dst_format]
+    if dst_group is None:
+        dst_group = src.group if dst_format != "q4_0" else 0
+    if data is None:
+        if dst_format == "gptq4":
+            data = torch.empty((k // 8, n), dtype=torch.int32, device=dev)
+        elif dst_format == "awq4":
+            data = torch.empty((k, n // 8), dtype=torch.int32, device=dev)
+        elif dst_format == "q4_0":
+            data = torch.empty((n, k // 32, 18), dtype=torch.uint8, device=dev)
+        else:
+            raise ValueError("repack target must be gptq4, awq4 or q4_0")
+    if dst_format in ("gptq4", "awq4"):
+        g = dst_group
+        if src.format == "q4_0":
+            if scales is None:
+                scales = torch.empty((k // g, n), dtype=torch.float16, device=dev)
+            if zeros is None:
+                zeros = torch.empty((k // g, n), dtype=torch.uint8, device=dev)
+        else:
+            if scales is None:
+                scales = src.scales
+            if zeros is None:
+                zeros = src.zeros
+    ct = src._c()
+    pass_scales = scales if (scales is not None and scales is not src.scales) else None
+    pass_zeros = zeros if (zeros is not None and zeros is not src.zeros) else None
+    _check(lib.qbn_repack(ctypes.byref(ct), fmt, int(dst_group), _ptr(data, "data"), _ptr(pass_scales, "scales"),
+                          _ptr(pass_zeros, "zeros"), _stream(dev)), "qbn_repack")
+    if dst_format == "q4_0":
+        return QTensor("q4_0", n, k, data)
+    return QTensor(dst_format, n, k, data, scales, zeros, group=dst_group)
+
+
+def validate(w: QTensor) -> int:
+    """Fail-closed load-time scan; returns the first bad index or -1.
+    Synchronizes the current stream to read the result."""
+    lib = _load()
+    first = torch.empty(1, dtype=torch.int64, device=w.device)
+    ct = w._c()
+    _check(lib.qbn_validate(ctypes.byref(ct), _ptr(first, "first_bad"), _stream(w.device)), "qbn_validate")
+    return int(first.item())

@@ -1,0 +1,528 @@
+// Decode GEMV, y = W_hat x at batch 1, for MXFP4, NVFP4 and Q4_K on gfx950.
+//
+// The weights are streamed once from HBM with 16-byte loads and decoded in
+// registers; W_hat is never written out ("Why 4-Bit Quantization Is King",
+// sections 1, 7 and 7d; "Four Bits, Three Contracts", section 8).
+//
+// Work split (wave64): a wave owns RPW row passes; in each pass its 64 lanes
+// cover SUB = 64/LPR rows with LPR lanes per row. Every lane sees the same k
+// positions for every row it touches, so its slice of x is loaded once into
+// registers and reused for all of the wave's rows. All weight loads of a
+// wave are issued before any activation load or arithmetic, so the HBM
+// requests of the whole grid are in flight as early as possible.
+//
+// Arithmetic: products accumulate in binary32. E2M1 formats factor the
+// block scale out of each 16/32-element group (group sum, then one FMA by
+// the scale, then scale2 once per row, as the Muser chapter 7 kernel does,
+// section 7.4.1). Q4_K forms each weight exactly as its dequantized value
+// (one rounding of d*s*q - dmin*m) before multiplying by x, so the error
+// bound holds even when gain and offset cancel. Each lane's chains are at
+// most 32 + 8 terms and the cross-lane sum is a fixed butterfly: the result
+// is deterministic and well inside |err| <= 1e-5 * sum|w x| + 1e-6.
+#include "qbn_device.h"
+#include "qbn_launch.h"
+
+namespace qbn {
+namespace {
+
+// ------------------------------------------------------------------ E2M1 helpers
+
+// 8 E2M1 codes of one dword times 8 binary32 activations, added to acc.
+__device__ __forceinline__ float dot8_f32(uint32_t w, f32x4 xa, f32x4 xb, float acc) {
+    f32x2 p0 = e2m1x2_f32<0>(w);
+    f32x2 p1 = e2m1x2_f32<1>(w);
+    f32x2 p2 = e2m1x2_f32<2>(w);
+    f32x2 p3 = e2m1x2_f32<3>(w);
+    acc = __builtin_fmaf(p0.x, xa.x, acc);
+    acc = __builtin_fmaf(p0.y, xa.y, acc);
+    acc = __builtin_fmaf(p1.x, xa.z, acc);
+    acc = __builtin_fmaf(p1.y, xa.w, acc);
+    acc = __builtin_fmaf(p2.x, xb.x, acc);
+    acc = __builtin_fmaf(p2.y, xb.y, acc);
+    acc = __builtin_fmaf(p3.x, xb.z, acc);
+    acc = __builtin_fmaf(p3.y, xb.w, acc);
+    return acc;
+}
+
+// 8 E2M1 codes of one dword times 8 bfloat16 activations (4 packed pairs):
+// each code pair converts to a bf16 pair (exact) and meets its activation
+// pair in one two-term dot with binary32 accumulation.
+// (Vector elements go through as_bf16x2's by-value parameter: bit-casting
+// an element expression such as xw.y directly reads the vector's first
+// element with this compiler.)
+__device__ __forceinline__ float dot8_bf16(uint32_t w, u32x4 xw, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<0>(w), as_bf16x2(xw.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<1>(w), as_bf16x2(xw.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<2>(w), as_bf16x2(xw.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<3>(w), as_bf16x2(xw.w), acc, false);
+    return acc;
+}
+
+// 32 activations starting at element e0 (e0 % 32 == 0), held in registers.
+template <typename XT>
+struct XChunk;
+template <>
+struct XChunk<float> {
+    f32x4 v[8];
+    __device__ __forceinline__ void load(const float *x, int64_t e0) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(x + e0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = p[i];
+    }
+    // dot of dword d (codes 8d..8d+7 of the chunk)
+    __device__ __forceinline__ float dot(int d, uint32_t w, float acc) const {
+        return dot8_f32(w, v[2 * d], v[2 * d + 1], acc);
+    }
+};
+template <>
+struct XChunk<__bf16> {
+    u32x4 v[4];
+    __device__ __forceinline__ void load(const __bf16 *x, int64_t e0) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(x + e0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = p[i];
+    }
+    __device__ __forceinline__ float dot(int d, uint32_t w, float acc) const { return dot8_bf16(w, v[d], acc); }
+};
+
+// 16 activations for the generic NVFP4 path (groups of 16).
+template <typename XT>
+__device__ __forceinline__ float dot16_generic(const uint8_t *cp, const XT *x, int64_t e0, float acc);
+template <>
+__device__ __forceinline__ float dot16_generic<float>(const uint8_t *cp, const float *x, int64_t e0, float acc) {
+    u32x2 w = ld8(cp);
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(x + e0);
+    acc = dot8_f32(w.x, p[0], p[1], acc);
+    acc = dot8_f32(w.y, p[2], p[3], acc);
+    return acc;
+}
+template <>
+__device__ __forceinline__ float dot16_generic<__bf16>(const uint8_t *cp, const __bf16 *x, int64_t e0, float acc) {
+    u32x2 w = ld8(cp);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(x + e0);
+    acc = dot8_bf16(w.x, p[0], acc);
+    acc = dot8_bf16(w.y, p[1], acc);
+    return acc;
+}
+
+// ------------------------------------------------------------------ E2M1 fast kernel
+// FMT: QBN_MXFP4 or QBN_NVFP4. A chunk is 16 code bytes = 32 elements
+// (one MXFP4 group, two NVFP4 groups). C = k/32 chunks per row; lane li of a
+// row covers chunks li + LPR*j, j < CPL. Requires C == LPR*CPL.
+template <int FMT, typename XT, int LPR, int CPL, int RPW>
+__global__ __launch_bounds__(256) void k_gemv_e2m1_fast(const uint8_t *__restrict__ codes,
+                                                        const uint8_t *__restrict__ scales, float scale2,
+                                                        const XT *__restrict__ x, float *__restrict__ y, int64_t n,
+                                                        int64_t k) {
+    constexpr int SUB = kWave / LPR;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int sub = lane / LPR;
+    const int li = lane % LPR;
+    const int64_t row0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + wave) * (int64_t)(RPW * SUB);
+    const int64_t row_bytes = k / 2;
+    const int64_t C = k / 32;
+    const int64_t spr = (FMT == QBN_MXFP4) ? C : 2 * C;  // scale bytes per row
+
+    u32x4 q[RPW][CPL];
+    uint32_t sb[RPW][CPL];
+#pragma unroll
+    for (int p = 0; p < RPW; ++p) {
+        const int64_t row = row0 + p * SUB + sub;
+        const bool ok = row < n;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int64_t ch = li + (int64_t)LPR * j;
+            if (ok) {
+                q[p][j] = ld16(codes + row * row_bytes + 16 * ch);
+            } else {
+                q[p][j] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < RPW; ++p) {
+        const int64_t row = row0 + p * SUB + sub;
+        const bool ok = row < n;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int64_t ch = li + (int64_t)LPR * j;
+            if (FMT == QBN_MXFP4) {
+                sb[p][j] = ok ? (uint32_t)scales[row * spr + ch] : 127u;
+            } else {
+                const uint8_t *sp = scales + row * spr + 2 * ch;
+                sb[p][j] = ok ? ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8)) : 0u;
+            }
+        }
+    }
+    XChunk<XT> xc[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) xc[j].load(x, 32 * (li + (int64_t)LPR * j));
+
+#pragma unroll
+    for (int p = 0; p < RPW; ++p) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const u32x4 w = q[p][j];
+            if (FMT == QBN_MXFP4) {
+                float g = 0.0f;
+                g = xc[j].dot(0, w.x, g);
+                g = xc[j].dot(1, w.y, g);
+                g = xc[j].dot(2, w.z, g);
+                g = xc[j].dot(3, w.w, g);
+                acc += __builtin_amdgcn_ldexpf(g, e8m0_exponent(sb[p][j]));
+            } else {
+                float g0 = 0.0f, g1 = 0.0f;
+                g0 = xc[j].dot(0, w.x, g0);
+                g0 = xc[j].dot(1, w.y, g0);
+                g1 = xc[j].dot(2, w.z, g1);
+                g1 = xc[j].dot(3, w.w, g1);
+                acc = __builtin_fmaf(g0, e4m3fn_f32_valid(sb[p][j] & 0xFFu), acc);
+                acc = __builtin_fmaf(g1, e4m3fn_f32_valid(sb[p][j] >> 8), acc);
+            }
+        }
+        acc = group_sum<LPR>(acc);
+        const int64_t row = row0 + p * SUB + sub;
+        if (li == 0 && row < n) y[row] = (FMT == QBN_NVFP4) ? acc * scale2 : acc;
+    }
+}
+
+// ------------------------------------------------------------------ E2M1 generic kernel
+// One wave per row; lanes stride over groups (G = 32 for MXFP4, 16 for
+// NVFP4). Two-level accumulation keeps every binary32 chain short for any k.
+template <int FMT, typename XT>
+__global__ __launch_bounds__(256) void k_gemv_e2m1_generic(const uint8_t *__restrict__ codes,
+                                                           const uint8_t *__restrict__ scales, float scale2,
+                                                           const XT *__restrict__ x, float *__restrict__ y,
+                                                           int64_t n, int64_t k) {
+    constexpr int G = (FMT == QBN_MXFP4) ? 32 : 16;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (row >= n) return;  // whole wave leaves together
+    const int64_t groups = k / G;
+    const uint8_t *crow = codes + row * (k / 2);
+    const uint8_t *srow = scales + row * groups;
+    float acc = 0.0f;
+    int64_t g = lane;
+    while (g < groups) {
+        float part = 0.0f;
+        for (int t = 0; t < 16 && g < groups; ++t, g += kWave) {
+            float gs;
+            if (FMT == QBN_MXFP4) {
+                gs = dot16_generic<XT>(crow + 16 * g, x, 32 * g, 0.0f);
+                gs = dot16_generic<XT>(crow + 16 * g + 8, x, 32 * g + 16, gs);
+                part += __builtin_amdgcn_ldexpf(gs, e8m0_exponent(srow[g]));
+            } else {
+                gs = dot16_generic<XT>(crow + 8 * g, x, 16 * g, 0.0f);
+                part = __builtin_fmaf(gs, e4m3fn_f32_valid(srow[g]), part);
+            }
+        }
+        acc += part;
+    }
+    acc = group_sum<kWave>(acc);
+    if (lane == 0) y[row] = (FMT == QBN_NVFP4) ? acc * scale2 : acc;
+}
+
+// ------------------------------------------------------------------ Q4_K
+// Lane layout inside a super-block: 8 lanes per block, lane c (0..7) owns
+// code bytes 16c..16c+15. In the page's lane map (byte 32c'+l -> outputs
+// 64c'+l and 64c'+32+l, "Four Bits, Three Contracts", section 5) those bytes
+// have c' = c/2 and l = 16(c%2) + t, so the lane's low nibbles are outputs
+// 64(c/2) + 16(c%2) + t of sub-block 2(c/2) and its high nibbles the same
+// plus 32, in sub-block 2(c/2)+1.
+//
+// Metadata: lane c decodes (scale, min) pair j = c of its block
+// ("Four Bits, Three Contracts", section 6) and the lanes of a quad swap the
+// two pairs each needs with DPP (pairs c&~1 and c|1).
+//
+// Codes become binary32 weights in one fused multiply-add each: a pair of
+// nibbles is masked into the two halves of a dword, read as two fp16
+// subnormals q * 2^-24 (or 16q * 2^-24 for high nibbles), and
+// fma(q * 2^-k, step * 2^k, -offset) gives RN(step*q - offset) exactly,
+// the dequantized value.
+
+template <typename XT>
+struct XQ4K;  // the 32 activations of one lane for one block
+template <>
+struct XQ4K<float> {
+    f32x4 lo[4], hi[4];
+    __device__ __forceinline__ void load(const float *x, int64_t base) {
+        const f32x4 *pl = reinterpret_cast<const f32x4 *>(x + base);
+        const f32x4 *ph = reinterpret_cast<const f32x4 *>(x + base + 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo[i] = pl[i];
+            hi[i] = ph[i];
+        }
+    }
+    __device__ __forceinline__ float xl(int i) const { return lo[i >> 2][i & 3]; }
+    __device__ __forceinline__ float xh(int i) const { return hi[i >> 2][i & 3]; }
+};
+template <>
+struct XQ4K<__bf16> {
+    u32x4 lo[2], hi[2];
+    __device__ __forceinline__ void load(const __bf16 *x, int64_t base) {
+        const u32x4 *pl = reinterpret_cast<const u32x4 *>(x + base);
+        const u32x4 *ph = reinterpret_cast<const u32x4 *>(x + base + 32);
+        lo[0] = pl[0];
+        lo[1] = pl[1];
+        hi[0] = ph[0];
+        hi[1] = ph[1];
+    }
+    __device__ __forceinline__ static float bf(const u32x4 *v, int i) {
+        uint32_t wd = v[i >> 3][(i >> 1) & 3];
+        return __uint_as_float((i & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+    }
+    __device__ __forceinline__ float xl(int i) const { return bf(lo, i); }
+    __device__ __forceinline__ float xh(int i) const { return bf(hi, i); }
+};
+
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// (step * 2^k, offset) of pair j = c of a block header; k = 24 for even j
+// (consumed as low nibbles), 20 for odd j (consumed as high nibbles * 16).
+struct Q4KLaneConsts {
+    uint32_t use_hi_src;  // j >= 4
+    uint32_t sh_s, w_s, sh_m, w_m, sh_top, w_top;
+    float pow2k;
+};
+
+__device__ __forceinline__ Q4KLaneConsts q4k_lane_consts(int c) {
+    Q4KLaneConsts L;
+    const int jj = c & 3;
+    L.use_hi_src = (c >= 4);
+    if (c < 4) {
+        L.sh_s = 8 * jj; L.w_s = 6; L.sh_m = 8 * jj; L.w_m = 6; L.sh_top = 0; L.w_top = 0;
+    } else {
+        L.sh_s = 8 * jj; L.w_s = 4; L.sh_m = 8 * jj + 4; L.w_m = 4; L.sh_top = 8 * jj + 6; L.w_top = 2;
+    }
+    L.pow2k = (c & 1) ? 0x1p20f : 0x1p24f;
+    return L;
+}
+
+__device__ __forceinline__ void q4k_pair(const u32x4 &h, const Q4KLaneConsts &L, float &step_k, float &off) {
+    // h.x: d | dmin << 16; h.y: B[0..3]; h.z: B[4..7]; h.w: B[8..11]
+    const uint32_t srcS = L.use_hi_src ? h.w : h.y;
+    const uint32_t srcM = L.use_hi_src ? h.w : h.z;
+    const uint32_t s = __builtin_amdgcn_ubfe(srcS, L.sh_s, L.w_s) | (__builtin_amdgcn_ubfe(h.y, L.sh_top, L.w_top) << 4);
+    const uint32_t m = __builtin_amdgcn_ubfe(srcM, L.sh_m, L.w_m) | (__builtin_amdgcn_ubfe(h.z, L.sh_top, L.w_top) << 4);
+    const float d = f16_bits_f32(h.x & 0xFFFFu);
+    const float dmin = f16_bits_f32(h.x >> 16);
+    step_k = (d * (float)s) * L.pow2k;  // both products exact
+    off = dmin * (float)m;              // exact
+}
+
+// 8 weights of code dword v (bytes t..t+3 of the lane's 16) times x.
+template <typename XT>
+__device__ __forceinline__ float q4k_dword(uint32_t v, int t, float sl, float ol, float sh, float oh,
+                                           const XQ4K<XT> &xq, float acc) {
+    const uint32_t wv = v >> 8;
+    const f16x2 p0 = __builtin_bit_cast(f16x2, v & 0x000F000Fu);   // lo nibbles of bytes 0, 2
+    const f16x2 p1 = __builtin_bit_cast(f16x2, wv & 0x000F000Fu);  // lo nibbles of bytes 1, 3
+    const f16x2 p2 = __builtin_bit_cast(f16x2, v & 0x00F000F0u);   // 16 * hi nibbles of bytes 0, 2
+    const f16x2 p3 = __builtin_bit_cast(f16x2, wv & 0x00F000F0u);  // 16 * hi nibbles of bytes 1, 3
+    const int i = 4 * t;
+    float w;
+    w = __builtin_fmaf((float)p0.x, sl, -ol); acc = __builtin_fmaf(w, xq.xl(i + 0), acc);
+    w = __builtin_fmaf((float)p1.x, sl, -ol); acc = __builtin_fmaf(w, xq.xl(i + 1), acc);
+    w = __builtin_fmaf((float)p0.y, sl, -ol); acc = __builtin_fmaf(w, xq.xl(i + 2), acc);
+    w = __builtin_fmaf((float)p1.y, sl, -ol); acc = __builtin_fmaf(w, xq.xl(i + 3), acc);
+    w = __builtin_fmaf((float)p2.x, sh, -oh); acc = __builtin_fmaf(w, xq.xh(i + 0), acc);
+    w = __builtin_fmaf((float)p3.x, sh, -oh); acc = __builtin_fmaf(w, xq.xh(i + 1), acc);
+    w = __builtin_fmaf((float)p2.y, sh, -oh); acc = __builtin_fmaf(w, xq.xh(i + 2), acc);
+    w = __builtin_fmaf((float)p3.y, sh, -oh); acc = __builtin_fmaf(w, xq.xh(i + 3), acc);
+    return acc;
+}
+
+// NB = blocks per row when NB < 8 (then SUB = 8/NB rows per pass, BPL = 1);
+// NB = 0 means k/256 = 8*BPL (SUB = 1).
+template <typename XT, int BPL, int SUB, int RPW>
+__global__ __launch_bounds__(256) void k_gemv_q4k_fast(const uint8_t *__restrict__ blocks,
+                                                       const XT *__restrict__ x, float *__restrict__ y, int64_t n,
+                                                       int64_t k) {
+    constexpr int LPR = kWave / SUB;  // lanes per row
+    constexpr int NBR = LPR / 8;      // blocks covered by one pass of a row's lanes
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int c = lane & 7;
+    const int slot = lane >> 3;
+    const int sub = slot / NBR;
+    const int bs = slot % NBR;
+    const int64_t nb = k / 256;
+    const int64_t row_bytes = 144 * nb;
+    const int64_t row0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + wave) * (int64_t)(RPW * SUB);
+
+    u32x4 hv[RPW][BPL], qv[RPW][BPL];
+#pragma unroll
+    for (int p = 0; p < RPW; ++p) {
+        const int64_t row = row0 + p * SUB + sub;
+        const bool ok = row < n;
+#pragma unroll
+        for (int j = 0; j < BPL; ++j) {
+            const uint8_t *blk = blocks + row * row_bytes + 144 * (int64_t)(bs + NBR * j);
+            if (ok) {
+                qv[p][j] = ld16(blk + 16 + 16 * c);
+                hv[p][j] = ld16(blk);
+            } else {
+                qv[p][j] = u32x4{0u, 0u, 0u, 0u};
+                hv[p][j] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    XQ4K<XT> xq[BPL];
+#pragma unroll
+    for (int j = 0; j < BPL; ++j)
+        xq[j].load(x, 256 * (int64_t)(bs + NBR * j) + 64 * (c >> 1) + 16 * (c & 1));
+    const Q4KLaneConsts L = q4k_lane_consts(c);
+
+#pragma unroll
+    for (int p = 0; p < RPW; ++p) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < BPL; ++j) {
+            float st, of;
+            q4k_pair(hv[p][j], L, st, of);
+            const float sl = quad_perm<0xA0>(st);  // pair c & ~1
+            const float ol = quad_perm<0xA0>(of);
+            const float sh = quad_perm<0xF5>(st);  // pair c | 1
+            const float oh = quad_perm<0xF5>(of);
+            const u32x4 v = qv[p][j];
+            acc = q4k_dword<XT>(v.x, 0, sl, ol, sh, oh, xq[j], acc);
+            acc = q4k_dword<XT>(v.y, 1, sl, ol, sh, oh, xq[j], acc);
+            acc = q4k_dword<XT>(v.z, 2, sl, ol, sh, oh, xq[j], acc);
+            acc = q4k_dword<XT>(v.w, 3, sl, ol, sh, oh, xq[j], acc);
+        }
+        acc = group_sum<LPR>(acc);
+        const int64_t row = row0 + p * SUB + sub;
+        if ((lane % LPR) == 0 && row < n) y[row] = acc;
+    }
+}
+
+// Generic Q4_K: one wave per row, 8 lanes per block as above, the wave's 8
+// block slots stride over the row's blocks; two-level accumulation.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_gemv_q4k_generic(const uint8_t *__restrict__ blocks,
+                                                          const XT *__restrict__ x, float *__restrict__ y,
+                                                          int64_t n, int64_t k) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (row >= n) return;
+    const int c = lane & 7;
+    const int slot = lane >> 3;
+    const int64_t nb = k / 256;
+    const uint8_t *rowp = blocks + row * 144 * nb;
+    const Q4KLaneConsts L = q4k_lane_consts(c);
+    float acc = 0.0f;
+    for (int64_t b0 = 0; b0 < nb; b0 += 8 * 16) {
+        float part = 0.0f;
+        for (int64_t b = b0 + slot; b < nb && b < b0 + 8 * 16; b += 8) {
+            // every lane of the quad takes the same branch (same block)
+            const uint8_t *blk = rowp + 144 * b;
+            const u32x4 qvv = ld16(blk + 16 + 16 * c);
+            const u32x4 h = ld16(blk);
+            XQ4K<XT> xq;
+            xq.load(x, 256 * b + 64 * (c >> 1) + 16 * (c & 1));
+            float st, of;
+            q4k_pair(h, L, st, of);
+            const float sl = quad_perm<0xA0>(st);
+            const float ol = quad_perm<0xA0>(of);
+            const float sh = quad_perm<0xF5>(st);
+            const float oh = quad_perm<0xF5>(of);
+            part = q4k_dword<XT>(qvv.x, 0, sl, ol, sh, oh, xq, part);
+            part = q4k_dword<XT>(qvv.y, 1, sl, ol, sh, oh, xq, part);
+            part = q4k_dword<XT>(qvv.z, 2, sl, ol, sh, oh, xq, part);
+            part = q4k_dword<XT>(qvv.w, 3, sl, ol, sh, oh, xq, part);
+        }
+        acc += part;
+    }
+    acc = group_sum<kWave>(acc);
+    if (lane == 0) y[row] = acc;
+}
+
+// ------------------------------------------------------------------ launchers
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+template <int FMT, typename XT, int LPR, int CPL, int RPW>
+hipError_t run_e2m1_fast(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+    constexpr int SUB = kWave / LPR;
+    const int64_t rows_per_block = (int64_t)kWavesPerBlock * RPW * SUB;
+    const int64_t grid = (w.n + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL((k_gemv_e2m1_fast<FMT, XT, LPR, CPL, RPW>), dim3((unsigned)grid), dim3(kBlock), 0, s,
+                       (const uint8_t *)w.data, (const uint8_t *)w.scales, w.scale2, x, y, w.n, w.k);
+    return hipGetLastError();
+}
+
+template <int FMT, typename XT>
+hipError_t run_e2m1(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+    const int64_t C = w.k / 32;
+    if (w.k % 32 == 0) {
+        switch (C) {
+        case 1: return run_e2m1_fast<FMT, XT, 1, 1, 1>(w, x, y, s);
+        case 2: return run_e2m1_fast<FMT, XT, 2, 1, 1>(w, x, y, s);
+        case 4: return run_e2m1_fast<FMT, XT, 4, 1, 1>(w, x, y, s);
+        case 8: return run_e2m1_fast<FMT, XT, 8, 1, 1>(w, x, y, s);
+        case 16: return run_e2m1_fast<FMT, XT, 16, 1, 2>(w, x, y, s);
+        case 32: return run_e2m1_fast<FMT, XT, 32, 1, 2>(w, x, y, s);
+        case 64: return run_e2m1_fast<FMT, XT, 64, 1, 4>(w, x, y, s);
+        case 128: return run_e2m1_fast<FMT, XT, 64, 2, 4>(w, x, y, s);
+        case 256: return run_e2m1_fast<FMT, XT, 64, 4, 2>(w, x, y, s);
+        default: break;
+        }
+    }
+    const int64_t grid = (w.n + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((k_gemv_e2m1_generic<FMT, XT>), dim3((unsigned)grid), dim3(kBlock), 0, s,
+                       (const uint8_t *)w.data, (const uint8_t *)w.scales, w.scale2, x, y, w.n, w.k);
+    return hipGetLastError();
+}
+
+template <typename XT, int BPL, int SUB, int RPW>
+hipError_t run_q4k_fast(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+    const int64_t rows_per_block = (int64_t)kWavesPerBlock * RPW * SUB;
+    const int64_t grid = (w.n + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL((k_gemv_q4k_fast<XT, BPL, SUB, RPW>), dim3((unsigned)grid), dim3(kBlock), 0, s,
+                       (const uint8_t *)w.data, x, y, w.n, w.k);
+    return hipGetLastError();
+}
+
+template <typename XT>
+hipError_t run_q4k(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+    switch (w.k / 256) {
+    case 1: return run_q4k_fast<XT, 1, 8, 1>(w, x, y, s);
+    case 2: return run_q4k_fast<XT, 1, 4, 1>(w, x, y, s);
+    case 4: return run_q4k_fast<XT, 1, 2, 2>(w, x, y, s);
+    case 8: return run_q4k_fast<XT, 1, 1, 4>(w, x, y, s);
+    case 16: return run_q4k_fast<XT, 2, 1, 2>(w, x, y, s);
+    case 32: return run_q4k_fast<XT, 4, 1, 1>(w, x, y, s);
+    default: break;
+    }
+    const int64_t grid = (w.n + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((k_gemv_q4k_generic<XT>), dim3((unsigned)grid), dim3(kBlock), 0, s, (const uint8_t *)w.data,
+                       x, y, w.n, w.k);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const qbn_tensor &w, const void *x, int x_dtype, float *y, hipStream_t s) {
+    const bool bf = (x_dtype == QBN_BF16);
+    switch (w.format) {
+    case QBN_MXFP4:
+        return bf ? run_e2m1<QBN_MXFP4, __bf16>(w, (const __bf16 *)x, y, s)
+                  : run_e2m1<QBN_MXFP4, float>(w, (const float *)x, y, s);
+    case QBN_NVFP4:
+        return bf ? run_e2m1<QBN_NVFP4, __bf16>(w, (const __bf16 *)x, y, s)
+                  : run_e2m1<QBN_NVFP4, float>(w, (const float *)x, y, s);
+    case QBN_Q4_K:
+        return bf ? run_q4k<__bf16>(w, (const __bf16 *)x, y, s) : run_q4k<float>(w, (const float *)x, y, s);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qbn

@@ -1,0 +1,244 @@
+// C-ABI entry points of libqbn: host-side argument checks, then dispatch to
+// the kernel launchers. Every check runs before anything is enqueued, so a
+// rejected call leaves the stream untouched ("Four Bits, Three Contracts",
+// sections 7 and 10: explicit rejection of unsupported cases; "Bit Packing
+// Architecture", 'Endianness, views and padding': dimensions must be
+// multiples of the pack and group sizes).
+#include <math.h>
+#include <stdint.h>
+
+#include "qbn_launch.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+// Largest element count a launch grid here can cover (256-thread blocks,
+// 32-bit grid dimension), with a wide margin.
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int32_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return QBN_OK;
+    g_last_hip_error = (int32_t)e;
+    return QBN_ERR_HIP;
+}
+
+bool known_format(int32_t f) { return f >= QBN_MXFP4 && f <= QBN_AWQ4; }
+
+// Shape, group and pointer rules of a tensor; `need_buffers` is false only
+// when the tensor is empty.
+int32_t check_tensor(const qbn_tensor *w) {
+    if (!w) return QBN_ERR_NULL;
+    if (!known_format(w->format)) return QBN_ERR_FORMAT;
+    if (w->reserved != 0) return QBN_ERR_FORMAT;
+    if (w->n < 0 || w->k < 0) return QBN_ERR_SHAPE;
+    if (w->n > kMaxElems || w->k > kMaxElems || (w->n > 0 && w->k > kMaxElems / w->n)) return QBN_ERR_SHAPE;
+    switch (w->format) {
+    case QBN_MXFP4:
+        if (w->k % 32) return QBN_ERR_SHAPE;
+        break;
+    case QBN_NVFP4:
+        if (w->k % 16) return QBN_ERR_SHAPE;
+        if (!(isfinite(w->scale2) && w->scale2 > 0.0f)) return QBN_ERR_SCALE2;
+        break;
+    case QBN_Q4_K:
+        if (w->k % 256) return QBN_ERR_SHAPE;
+        break;
+    case QBN_Q4_0:
+        if (w->k % 32) return QBN_ERR_SHAPE;
+        break;
+    case QBN_GPTQ4:
+    case QBN_AWQ4:
+        if (w->group <= 0 || w->group % 8) return QBN_ERR_GROUP;
+        if (w->k % 8 || w->k % w->group) return QBN_ERR_SHAPE;
+        if (w->format == QBN_AWQ4 && w->n % 8) return QBN_ERR_SHAPE;
+        break;
+    }
+    const bool empty = (w->n == 0 || w->k == 0);
+    if (empty) return QBN_OK;
+    if (!w->data) return QBN_ERR_NULL;
+    switch (w->format) {
+    case QBN_MXFP4:
+    case QBN_NVFP4:
+        if (!w->scales) return QBN_ERR_NULL;
+        if (!aligned(w->data, 16)) return QBN_ERR_ALIGN;
+        break;
+    case QBN_Q4_K:
+        if (!aligned(w->data, 16)) return QBN_ERR_ALIGN;
+        break;
+    case QBN_Q4_0:
+        if (!aligned(w->data, 2)) return QBN_ERR_ALIGN;
+        break;
+    case QBN_GPTQ4:
+    case QBN_AWQ4:
+        if (!w->scales || !w->zeros) return QBN_ERR_NULL;
+        if (!aligned(w->data, 4) || !aligned(w->scales, 2)) return QBN_ERR_ALIGN;
+        break;
+    }
+    return QBN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qbn_abi_version(void) { return QBN_ABI_VERSION; }
+
+size_t qbn_tensor_struct_size(void) { return sizeof(qbn_tensor); }
+
+int32_t qbn_last_hip_error(void) { return g_last_hip_error; }
+
+const char *qbn_status_string(int32_t status) {
+    switch (status) {
+    case QBN_OK: return "ok";
+    case QBN_ERR_NULL: return "a required pointer is NULL";
+    case QBN_ERR_FORMAT: return "unknown format or enum value";
+    case QBN_ERR_UNSUPPORTED: return "format not supported by this operation";
+    case QBN_ERR_SHAPE: return "shape is negative, too large, or not a multiple of the block/pack/group size";
+    case QBN_ERR_ALIGN: return "pointer or leading dimension is not aligned as required";
+    case QBN_ERR_SCALE2: return "NVFP4 scale2 must be finite and > 0";
+    case QBN_ERR_NAN_SCALE: return "a NaN scale encoding was found";
+    case QBN_ERR_DTYPE: return "unsupported activation or output dtype";
+    case QBN_ERR_HIP: return "HIP runtime error (see qbn_last_hip_error)";
+    case QBN_ERR_GROUP: return "invalid group size";
+    default: return "unknown status";
+    }
+}
+
+int64_t qbn_bytes(int32_t format, int64_t n, int64_t k, int32_t group, int32_t part) {
+    if (!known_format(format) || part < 0 || part > 2 || n < 0 || k < 0) return -1;
+    if (n > kMaxElems || k > kMaxElems || (n > 0 && k > kMaxElems / n)) return -1;
+    switch (format) {
+    case QBN_MXFP4:
+        if (k % 32) return -1;
+        return part == 0 ? n * k / 2 : part == 1 ? n * (k / 32) : 0;
+    case QBN_NVFP4:
+        if (k % 16) return -1;
+        return part == 0 ? n * k / 2 : part == 1 ? n * (k / 16) : 0;
+    case QBN_Q4_K:
+        if (k % 256) return -1;
+        return part == 0 ? n * (k / 256) * 144 : 0;
+    case QBN_Q4_0:
+        if (k % 32) return -1;
+        return part == 0 ? n * (k / 32) * 18 : 0;
+    case QBN_GPTQ4:
+    case QBN_AWQ4:
+        if (group <= 0 || group % 8 || k % 8 || k % group) return -1;
+        if (format == QBN_AWQ4 && n % 8) return -1;
+        return part == 0 ? n * k / 2 : part == 1 ? 2 * n * (k / group) : n * (k / group);
+    }
+    return -1;
+}
+
+int32_t qbn_quantized_gemv(const qbn_tensor *w, const void *x, int32_t x_dtype, void *y, int32_t y_dtype,
+                           void *stream) {
+    int32_t st = check_tensor(w);
+    if (st) return st;
+    if (w->format != QBN_MXFP4 && w->format != QBN_NVFP4 && w->format != QBN_Q4_K) return QBN_ERR_UNSUPPORTED;
+    if (x_dtype < QBN_F32 || x_dtype > QBN_F16 || y_dtype < QBN_F32 || y_dtype > QBN_F16) return QBN_ERR_FORMAT;
+    if ((x_dtype != QBN_F32 && x_dtype != QBN_BF16) || y_dtype != QBN_F32) return QBN_ERR_DTYPE;
+    if (w->n == 0) return QBN_OK;
+    if (!y) return QBN_ERR_NULL;
+    if (!aligned(y, 4)) return QBN_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (w->k == 0) return hip_status(qbn::launch_fill_zero(y, 4 * w->n, s));
+    if (!x) return QBN_ERR_NULL;
+    if (!aligned(x, 16)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_gemv(*w, x, x_dtype, (float *)y, s));
+}
+
+int32_t qbn_quantized_gemm(const qbn_tensor *w, int64_t m, const void *x, int32_t x_dtype, int64_t ldx, void *y,
+                           int32_t y_dtype, int64_t ldy, void *stream) {
+    int32_t st = check_tensor(w);
+    if (st) return st;
+    if (w->format != QBN_MXFP4) return QBN_ERR_UNSUPPORTED;
+    if (x_dtype < QBN_F32 || x_dtype > QBN_F16 || y_dtype < QBN_F32 || y_dtype > QBN_F16) return QBN_ERR_FORMAT;
+    if (x_dtype != QBN_BF16 || y_dtype != QBN_BF16) return QBN_ERR_DTYPE;
+    if (m < 0 || m > kMaxElems) return QBN_ERR_SHAPE;
+    if (m == 0 || w->n == 0) return QBN_OK;
+    if (ldy < w->n || ldy % 8) return ldy < w->n ? QBN_ERR_SHAPE : QBN_ERR_ALIGN;
+    if (ldy > kMaxElems / m) return QBN_ERR_SHAPE;
+    if (!y) return QBN_ERR_NULL;
+    if (!aligned(y, 16)) return QBN_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (w->k == 0) return hip_status(qbn::launch_fill_zero(y, 2 * ldy * m, s));
+    if (ldx < w->k || ldx % 8) return ldx < w->k ? QBN_ERR_SHAPE : QBN_ERR_ALIGN;
+    if (ldx > kMaxElems / m) return QBN_ERR_SHAPE;
+    if (!x) return QBN_ERR_NULL;
+    if (!aligned(x, 16)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_gemm(*w, m, x, ldx, y, ldy, s));
+}
+
+int32_t qbn_dequantize(const qbn_tensor *w, void *out, int32_t out_dtype, int32_t out_layout, void *stream) {
+    int32_t st = check_tensor(w);
+    if (st) return st;
+    if (out_dtype < QBN_F32 || out_dtype > QBN_F16 || out_layout < 0 || out_layout > 1) return QBN_ERR_FORMAT;
+    if (out_dtype != QBN_F32 && out_dtype != QBN_BF16) return QBN_ERR_DTYPE;
+    if (w->n == 0 || w->k == 0) return QBN_OK;
+    if (!out) return QBN_ERR_NULL;
+    if (!aligned(out, 16)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_dequant(*w, out, out_dtype, out_layout, (hipStream_t)stream));
+}
+
+int32_t qbn_repack(const qbn_tensor *src, int32_t dst_format, int32_t dst_group, void *dst_data, void *dst_scales,
+                   void *dst_zeros, void *stream) {
+    int32_t st = check_tensor(src);
+    if (st) return st;
+    if (!known_format(dst_format)) return QBN_ERR_FORMAT;
+    const bool src_int4 = src->format == QBN_GPTQ4 || src->format == QBN_AWQ4 || src->format == QBN_Q4_0;
+    const bool dst_int4 = dst_format == QBN_GPTQ4 || dst_format == QBN_AWQ4 || dst_format == QBN_Q4_0;
+    if (!src_int4 || !dst_int4 || src->format == dst_format) return QBN_ERR_UNSUPPORTED;
+    const int64_t n = src->n, k = src->k;
+    // destination shape rules
+    if (dst_format == QBN_Q4_0) {
+        if (k % 32) return QBN_ERR_SHAPE;
+        if (src->group % 32) return QBN_ERR_GROUP;  // Q4_0 blocks of 32 need whole groups
+    } else {
+        if (k % 8) return QBN_ERR_SHAPE;
+        if (dst_format == QBN_AWQ4 && n % 8) return QBN_ERR_SHAPE;
+        if (src->format == QBN_Q4_0) {
+            if (dst_group <= 0 || dst_group % 32 || k % dst_group) return QBN_ERR_GROUP;
+        } else if (dst_group != src->group && dst_group != 0) {
+            return QBN_ERR_GROUP;
+        }
+    }
+    if (n == 0 || k == 0) return QBN_OK;
+    if (!dst_data) return QBN_ERR_NULL;
+    if (dst_format == QBN_Q4_0) {
+        if (!aligned(dst_data, 2)) return QBN_ERR_ALIGN;
+    } else {
+        if (!aligned(dst_data, 4)) return QBN_ERR_ALIGN;
+        if (src->format == QBN_Q4_0) {
+            if (!dst_scales || !dst_zeros) return QBN_ERR_NULL;
+            if (!aligned(dst_scales, 2)) return QBN_ERR_ALIGN;
+        } else if (dst_scales && !aligned(dst_scales, 2)) {
+            return QBN_ERR_ALIGN;
+        }
+    }
+    return hip_status(qbn::launch_repack(*src, dst_format, dst_group, dst_data, dst_scales, dst_zeros,
+                                         (hipStream_t)stream));
+}
+
+int32_t qbn_validate(const qbn_tensor *w, int64_t *first_bad, void *stream) {
+    if (!w) return QBN_ERR_NULL;
+    if (w->format == QBN_Q4_0 && w->group != 0) {
+        if (w->group < 0 || w->group % 32) return QBN_ERR_GROUP;
+        if (w->k % w->group) return QBN_ERR_SHAPE;
+    }
+    int32_t st;
+    if (w->format == QBN_Q4_0) {
+        qbn_tensor t = *w;
+        t.group = 0;  // group here only selects the uniformity check
+        st = check_tensor(&t);
+    } else {
+        st = check_tensor(w);
+    }
+    if (st) return st;
+    if (!first_bad) return QBN_ERR_NULL;
+    if (!aligned(first_bad, 8)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_validate(*w, first_bad, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,21 @@
+// Internal launch entry points, one per kernel family. Arguments have been
+// validated by the C-ABI layer (qbn_api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qbn.h"
+
+namespace qbn {
+
+hipError_t launch_gemv(const qbn_tensor &w, const void *x, int x_dtype, float *y, hipStream_t s);
+hipError_t launch_gemm(const qbn_tensor &w, int64_t m, const void *x, int64_t ldx, void *y, int64_t ldy,
+                       hipStream_t s);
+hipError_t launch_dequant(const qbn_tensor &w, void *out, int out_dtype, int out_layout, hipStream_t s);
+hipError_t launch_repack(const qbn_tensor &src, int dst_format, int dst_group, void *dst_data, void *dst_scales,
+                         void *dst_zeros, hipStream_t s);
+hipError_t launch_validate(const qbn_tensor &w, int64_t *first_bad, hipStream_t s);
+hipError_t launch_fill_zero(void *out, int64_t bytes, hipStream_t s);
+
+}  // namespace qbn

@@ -1,0 +1,158 @@
+// Load-time fail-closed scan ("Chapter 7 - NVFP4: the native lane", section
+// 7.3: a NaN scale byte or an inconsistent companion refuses the load;
+// "Four Bits, Three Contracts", section 7: reject rather than misread).
+// The hot-path kernels trust validated scales and do not re-check them.
+//
+// The result is the smallest offending index, found with a 64-bit atomic
+// minimum (order-independent, so the answer is deterministic), then turned
+// into -1 when nothing was found. The three steps are kernels on the
+// caller's stream; no memset node is used.
+#include "qbn_device.h"
+#include "qbn_launch.h"
+
+namespace qbn {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr unsigned long long kNone = 0x7FFFFFFFFFFFFFFFull;
+
+__global__ void k_set(unsigned long long *p, unsigned long long v) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
+}
+
+__global__ void k_finish(unsigned long long *p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0 && *p == kNone) *p = ~0ull;  // -1 as int64
+}
+
+__device__ __forceinline__ bool f16_nonfinite(uint32_t h) { return ((h >> 10) & 31u) == 31u; }
+
+// kind 0: E8M0 scale bytes (0xFF is NaN); kind 1: E4M3FN (0x7F / 0xFF).
+template <int KIND>
+__global__ __launch_bounds__(kBlock) void k_scan_bytes(const uint8_t *__restrict__ p, int64_t count,
+                                                        unsigned long long *first) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        const uint32_t b = p[i];
+        const bool bad = (KIND == 0) ? (b == 0xFFu) : ((b & 0x7Fu) == 0x7Fu);
+        if (bad) atomicMin(first, (unsigned long long)i);
+    }
+}
+
+// Q4_K blocks: d or dmin not finite.
+__global__ __launch_bounds__(kBlock) void k_scan_q4k(const uint8_t *__restrict__ blocks, int64_t nblocks,
+                                                      unsigned long long *first) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nblocks; i += stride) {
+        const uint32_t h = ld4(blocks + 144 * i);
+        if (f16_nonfinite(h & 0xFFFFu) || f16_nonfinite(h >> 16)) atomicMin(first, (unsigned long long)i);
+    }
+}
+
+// Q4_0 blocks [n][k/32]: d not finite, or (bpg > 1) d differs from the first
+// block of its group of bpg blocks along k.
+__global__ __launch_bounds__(kBlock) void k_scan_q4_0(const uint8_t *__restrict__ blocks, int64_t nblocks,
+                                                       int64_t bpr, int64_t bpg, unsigned long long *first) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nblocks; i += stride) {
+        const uint32_t d = *reinterpret_cast<const uint16_t *>(blocks + 18 * i);
+        bool bad = f16_nonfinite(d);
+        if (bpg > 1) {
+            const int64_t b = i % bpr;
+            const int64_t lead = i - (b % bpg);
+            bad = bad || (*reinterpret_cast<const uint16_t *>(blocks + 18 * lead) != d);
+        }
+        if (bad) atomicMin(first, (unsigned long long)i);
+    }
+}
+
+// GPTQ / AWQ companions: scale not finite or logical zero point above 15.
+__global__ __launch_bounds__(kBlock) void k_scan_affine(const uint16_t *__restrict__ scales,
+                                                         const uint8_t *__restrict__ zeros, int64_t count,
+                                                         unsigned long long *first) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        if (f16_nonfinite(scales[i]) || zeros[i] > 15u) atomicMin(first, (unsigned long long)i);
+    }
+}
+
+int64_t scan_grid(int64_t count) {
+    int64_t g = (count + kBlock - 1) / kBlock;
+    if (g > 4096) g = 4096;
+    return g < 1 ? 1 : g;
+}
+
+__global__ void k_fill_zero(uint32_t *p, int64_t words) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride) p[i] = 0u;
+}
+
+__global__ void k_fill_zero_bytes(uint8_t *p, int64_t bytes) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < bytes; i += stride) p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_validate(const qbn_tensor &w, int64_t *first_bad, hipStream_t s) {
+    unsigned long long *f = reinterpret_cast<unsigned long long *>(first_bad);
+    hipLaunchKernelGGL(k_set, dim3(1), dim3(64), 0, s, f, kNone);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = w.n, k = w.k;
+    int64_t count = 0;
+    switch (w.format) {
+    case QBN_MXFP4:
+        count = n * (k / 32);
+        if (count > 0)
+            hipLaunchKernelGGL(k_scan_bytes<0>, dim3((unsigned)scan_grid(count)), dim3(kBlock), 0, s,
+                               (const uint8_t *)w.scales, count, f);
+        break;
+    case QBN_NVFP4:
+        count = n * (k / 16);
+        if (count > 0)
+            hipLaunchKernelGGL(k_scan_bytes<1>, dim3((unsigned)scan_grid(count)), dim3(kBlock), 0, s,
+                               (const uint8_t *)w.scales, count, f);
+        break;
+    case QBN_Q4_K:
+        count = n * (k / 256);
+        if (count > 0)
+            hipLaunchKernelGGL(k_scan_q4k, dim3((unsigned)scan_grid(count)), dim3(kBlock), 0, s,
+                               (const uint8_t *)w.data, count, f);
+        break;
+    case QBN_Q4_0: {
+        count = n * (k / 32);
+        const int64_t bpg = (w.group > 0) ? (int64_t)w.group / 32 : 1;
+        if (count > 0)
+            hipLaunchKernelGGL(k_scan_q4_0, dim3((unsigned)scan_grid(count)), dim3(kBlock), 0, s,
+                               (const uint8_t *)w.data, count, k / 32, bpg, f);
+        break;
+    }
+    case QBN_GPTQ4:
+    case QBN_AWQ4:
+        count = (k / w.group) * n;
+        if (count > 0)
+            hipLaunchKernelGGL(k_scan_affine, dim3((unsigned)scan_grid(count)), dim3(kBlock), 0, s,
+                               (const uint16_t *)w.scales, (const uint8_t *)w.zeros, count, f);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(64), 0, s, f);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void *out, int64_t bytes, hipStream_t s) {
+    if (bytes <= 0) return hipSuccess;
+    if (((uintptr_t)out % 4 == 0) && (bytes % 4 == 0)) {
+        const int64_t words = bytes / 4;
+        hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)scan_grid(words)), dim3(kBlock), 0, s, (uint32_t *)out, words);
+    } else {
+        hipLaunchKernelGGL(k_fill_zero_bytes, dim3((unsigned)scan_grid(bytes)), dim3(kBlock), 0, s, (uint8_t *)out,
+                           bytes);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qbn

@@ -1,0 +1,207 @@
+/*
+ * qbn.h - C ABI of the qbn library: fused dequantize-and-dot over packed
+ * 4-bit block-quantized weights, bulk dequantization and bit-exact int4
+ * layout repacks, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page title, section):
+ *  [FB] "Four Bits, Three Contracts: an interactive guide to MXFP4, NVFP4 and
+ *       Q4_K" (shivasnotes.com, blog 6006)
+ *  [WK] "Why 4-Bit Quantization Is King: Understanding Q4_K, MXFP4, and NVFP4"
+ *       (shivasnotes.com, blog 5996)
+ *  [BP] "Bit Packing Architecture" (aicassindra.com)
+ *  [NV] "Chapter 7 - NVFP4: the native lane" (Muser book,
+ *       highperformanceailab.com)
+ *
+ * Conventions shared by every call
+ *  - The logical weight W is n x k: n output features (rows), k input
+ *    features (the reduction dimension). W_hat is its dequantized value.
+ *  - Every buffer pointer is a DEVICE pointer owned by the caller; the
+ *    library never allocates, frees, retains or synchronizes on it.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL means the
+ *    default stream). A call returns after enqueueing its kernels.
+ *  - Every argument is checked on the host before anything is enqueued; a
+ *    rejected call returns a nonzero qbn_status and enqueues nothing. A
+ *    launch failure returns QBN_ERR_HIP; qbn_last_hip_error() gives the
+ *    hipError_t of the calling thread's last failure.
+ *  - All multi-byte fields are little-endian ([BP] "Endianness, views and
+ *    padding"). Dimensions must be multiples of the format's block or pack
+ *    size; callers pad and slice ([BP] same section).
+ *  - The library holds no state besides the per-thread last error and is
+ *    thread-safe.
+ *
+ * Formats (the `data` / `scales` / `zeros` buffers of a qbn_tensor)
+ *  QBN_MXFP4 [FB] section 3: data u8 [n][k/2], two E2M1 codes per byte, low
+ *            nibble = even element; scales u8 [n][k/32] E8M0 (2^(b-127)),
+ *            groups of 32 along k. k % 32 == 0.
+ *  QBN_NVFP4 [NV] sections 7.1-7.3, Figure 7.2: data u8 [n][k/2] as MXFP4;
+ *            scales u8 [n][k/16] E4M3FN; scale2 = per-tensor binary32, finite
+ *            and > 0. Dequantized value (e2m1 * e4m3fn) * scale2 in that
+ *            order. k % 16 == 0.
+ *  QBN_Q4_K  [FB] sections 5-6, [WK] section 4: data = [n][k/256] blocks of
+ *            144 bytes: fp16 d (offset 0), fp16 dmin (2), 12 bytes of packed
+ *            6-bit (scale, min) pairs (4), 128 code bytes (16); code byte
+ *            32c+l holds output 64c+l (low nibble, sub-block 2c) and
+ *            64c+32+l (high nibble, sub-block 2c+1);
+ *            w = d*s_j*q - dmin*m_j. k % 256 == 0.
+ *  QBN_Q4_0  [BP] "Real layouts compared": data = [n][k/32] blocks of 18
+ *            bytes: fp16 d, then byte j = element j (low) | element j+16
+ *            (high); w = d*(q-8). Blocks run along k inside each output row.
+ *            k % 32 == 0.
+ *  QBN_GPTQ4 [BP]: data int32 [k/8][n], packed along k, row 8r+j at bits 4j
+ *            of word [r][n]; scales fp16 [k/group][n]; zeros u8 [k/group][n]
+ *            holding LOGICAL zero points 0..15 (w = s*(q - z)).
+ *            k % 8 == 0, group % 8 == 0, k % group == 0.
+ *  QBN_AWQ4  [BP]: data int32 [k][n/8], packed along n, the word's slots hold
+ *            columns 0,2,4,6,1,3,5,7 of its group of eight; scales and zeros
+ *            as GPTQ4. n % 8 == 0, k % group == 0.
+ *
+ * Alignment: MXFP4 / NVFP4 / Q4_K data 16-byte aligned; Q4_0 data 2-byte;
+ * GPTQ4 / AWQ4 data 4-byte; fp16 scales 2-byte; GEMV x 16-byte and y 4-byte;
+ * GEMM X / Y and dequantize outputs 16-byte. Scale bytes of MXFP4 / NVFP4
+ * and zero points have no alignment requirement. A violation returns
+ * QBN_ERR_ALIGN.
+ */
+#ifndef QBN_H
+#define QBN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QBN_ABI_VERSION 1
+
+/* Exported from libqbn.so even when built with hidden default visibility. */
+#if defined(__GNUC__) || defined(__clang__)
+#define QBN_API __attribute__((visibility("default")))
+#else
+#define QBN_API
+#endif
+
+typedef enum qbn_status {
+    QBN_OK = 0,
+    QBN_ERR_NULL = 1,        /* a required pointer is NULL */
+    QBN_ERR_FORMAT = 2,      /* unknown format or dtype enum value */
+    QBN_ERR_UNSUPPORTED = 3, /* known format, but not for this operation */
+    QBN_ERR_SHAPE = 4,       /* negative size, or not a multiple of the block / pack / group size */
+    QBN_ERR_ALIGN = 5,       /* a pointer or leading dimension breaks the alignment rule */
+    QBN_ERR_SCALE2 = 6,      /* NVFP4 scale2 is not finite and > 0 */
+    QBN_ERR_NAN_SCALE = 7,   /* reserved for callers of qbn_validate: a NaN scale encoding was found */
+    QBN_ERR_DTYPE = 8,       /* unsupported activation / output dtype for this call */
+    QBN_ERR_HIP = 9,         /* the HIP runtime rejected a launch or copy */
+    QBN_ERR_GROUP = 10       /* group size invalid for the format or the repack */
+} qbn_status;
+
+typedef enum qbn_format {
+    QBN_MXFP4 = 1,
+    QBN_NVFP4 = 2,
+    QBN_Q4_K = 3,
+    QBN_Q4_0 = 4,
+    QBN_GPTQ4 = 5,
+    QBN_AWQ4 = 6
+} qbn_format;
+
+typedef enum qbn_dtype {
+    QBN_F32 = 0,  /* IEEE binary32 */
+    QBN_BF16 = 1, /* bfloat16 (upper half of a binary32) */
+    QBN_F16 = 2   /* IEEE binary16 (accepted by no call in this version) */
+} qbn_dtype;
+
+/* A quantized weight: plain sizes and caller-owned device pointers. */
+typedef struct qbn_tensor {
+    int32_t format;      /* qbn_format */
+    int32_t group;       /* GPTQ4 / AWQ4: group length along k; otherwise ignored */
+    int64_t n;           /* output features (rows of W) */
+    int64_t k;           /* input features (reduction length) */
+    const void *data;    /* packed codes / blocks, layout per format above */
+    const void *scales;  /* MXFP4 / NVFP4 scale bytes; GPTQ4 / AWQ4 fp16 scales; else NULL */
+    const void *zeros;   /* GPTQ4 / AWQ4 logical zero points u8 [k/group][n]; else NULL */
+    float scale2;        /* NVFP4 per-tensor scale; ignored by other formats */
+    int32_t reserved;    /* must be 0 */
+} qbn_tensor;
+
+/* Version of this ABI (QBN_ABI_VERSION) and sizeof(qbn_tensor), so that a
+ * binding can check that its struct mirror matches. */
+QBN_API int32_t qbn_abi_version(void);
+QBN_API size_t qbn_tensor_struct_size(void);
+
+/* Static text for a status code; never NULL. */
+QBN_API const char *qbn_status_string(int32_t status);
+
+/* hipError_t (as int) of the calling thread's last QBN_ERR_HIP, 0 if none. */
+QBN_API int32_t qbn_last_hip_error(void);
+
+/* Bytes of one part of a tensor of this format and shape:
+ * part 0 = data, 1 = scales, 2 = zeros. Returns -1 for an invalid format,
+ * part or shape, 0 for a part the format does not have. The per-weight
+ * storage cost follows [FB] sections 3-5 and [NV] section 7.1:
+ * MXFP4 17 bytes per 32 weights, NVFP4 9 per 16 (+4 per tensor for scale2,
+ * not counted here), Q4_K 144 per 256, Q4_0 18 per 32. */
+QBN_API int64_t qbn_bytes(int32_t format, int64_t n, int64_t k, int32_t group, int32_t part);
+
+/* y[r] = sum_i W_hat[r][i] * x[i] for r in 0..n  (decode GEMV, batch 1).
+ * Fused: W_hat is decoded in registers and never written to memory
+ * ([WK] sections 1, 7 and 7d; [FB] section 8).
+ * Formats: MXFP4, NVFP4, Q4_K. x: QBN_F32 or QBN_BF16 [k]; y: QBN_F32 [n].
+ * Accumulation is binary32 with a fixed, atomics-free reduction order, so
+ * repeated calls give bit-identical y. Each y[r] satisfies
+ * |y - y_exact| <= 1e-5 * sum_i |W_hat[r][i] x[i]| + 1e-6.
+ * Scale bytes are not re-checked here: run qbn_validate once at load time. */
+QBN_API int32_t qbn_quantized_gemv(const qbn_tensor *w, const void *x, int32_t x_dtype, void *y, int32_t y_dtype,
+                           void *stream);
+
+/* Y[i][r] = sum_j X[i][j] * W_hat[r][j] for i in 0..m, r in 0..n  (prefill
+ * GEMM with packed weights, [WK] sections 7 and 7d).
+ * Formats: MXFP4. X: QBN_BF16 [m][ldx] row-major, ldx >= k, ldx % 8 == 0;
+ * Y: QBN_BF16 [m][ldy], ldy >= n, ldy % 8 == 0. W_hat is expanded to bf16
+ * exactly (E2M1 x 2^e is exact in bf16), products run on bf16 matrix cores
+ * with binary32 accumulation, and Y is rounded to bf16 (nearest even). */
+QBN_API int32_t qbn_quantized_gemm(const qbn_tensor *w, int64_t m, const void *x, int32_t x_dtype, int64_t ldx, void *y,
+                           int32_t y_dtype, int64_t ldy, void *stream);
+
+/* Materialize W_hat. out_layout 0: out [n][k] row-major; 1: out [k][n].
+ * out_dtype QBN_F32: the exact binary32 value of each format's rule
+ * (NVFP4 rounded once after the multiply by scale2, Q4_K rounded once
+ * after the subtraction); QBN_BF16: that binary32 value rounded to bf16,
+ * nearest even. All six formats. Bit-exact with the definitions, including
+ * negative zero; a scale byte that qbn_validate rejects decodes to NaN. */
+QBN_API int32_t qbn_dequantize(const qbn_tensor *w, void *out, int32_t out_dtype, int32_t out_layout, void *stream);
+
+/* Bit-exact repack of the int4 codes through the logical matrix
+ * ([BP] "Repacking between formats"): src and destination share n and k.
+ * Directions: GPTQ4 <-> AWQ4, GPTQ4 <-> Q4_0, AWQ4 <-> Q4_0.
+ *  - GPTQ4 <-> AWQ4: dst_data receives the qweight; scales and zeros keep
+ *    their [k/group][n] layout and are copied to dst_scales / dst_zeros when
+ *    those are non-NULL. dst_group must equal src->group.
+ *  - GPTQ4 / AWQ4 -> Q4_0: dst_data receives [n][k/32] 18-byte blocks whose
+ *    fp16 d is a bit copy of the group scale s[(32b)/group][n]; requires
+ *    src->group % 32 == 0. Q4_0's zero point is fixed at 8, so the
+ *    dequantized values agree with the source exactly on groups whose zero
+ *    point is 8; the codes themselves always move bit-exactly.
+ *  - Q4_0 -> GPTQ4 / AWQ4: dst_group % 32 == 0 and k % dst_group == 0;
+ *    dst_scales (fp16 [k/dst_group][n]) receives the d of the first block of
+ *    each group (qbn_validate with format Q4_0 and group = dst_group checks
+ *    that all blocks of a group share d); dst_zeros (u8) is filled with 8. */
+QBN_API int32_t qbn_repack(const qbn_tensor *src, int32_t dst_format, int32_t dst_group, void *dst_data,
+                   void *dst_scales, void *dst_zeros, void *stream);
+
+/* Load-time fail-closed scan ([NV] section 7.3; [FB] section 7). Writes to
+ * *first_bad (a caller-owned DEVICE int64) the smallest index of an invalid
+ * element, or -1 if the tensor is clean:
+ *  MXFP4: scale byte 0xFF (E8M0 NaN), index into scales;
+ *  NVFP4: scale byte 0x7F or 0xFF (E4M3FN NaN), index into scales
+ *         (scale2 itself is checked on the host, QBN_ERR_SCALE2);
+ *  Q4_K:  d or dmin not finite, index = block;
+ *  Q4_0:  d not finite, or (group > 0) a block whose d differs from the
+ *         first block of its group of group/32 blocks, index = block;
+ *  GPTQ4 / AWQ4: scale not finite or zero point > 15, index into scales.
+ * Asynchronous like every other call: read *first_bad after the stream. */
+QBN_API int32_t qbn_validate(const qbn_tensor *w, int64_t *first_bad, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QBN_H */

@@ -1,0 +1,161 @@
+"""Host-side tests of the C ABI that need no GPU: the library loads, exports
+every entry point include/qbn.h declares, reports its sizes, and rejects bad
+arguments with the documented status codes before anything is launched
+(all pointers below are never dereferenced: every call fails its host checks
+or is an empty no-op)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_block_quantized_nibble_amd as qbn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, FORMAT, UNSUP, SHAPE, ALIGN, SCALE2, NANS, DTYPE, HIP, GROUP = range(11)
+MX, NV, QK, Q0, GP, AW = 1, 2, 3, 4, 5, 6
+F32, BF16 = 0, 1
+A = 0x10000  # an aligned fake address
+B = 0x20000
+C = 0x30000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return qbn._load()
+
+
+def T(fmt, n, k, data=A, scales=B, zeros=C, scale2=1.0, group=0, reserved=0):
+    t = qbn._CTensor()
+    t.format, t.group, t.n, t.k = fmt, group, n, k
+    t.data, t.scales, t.zeros = data, scales, zeros
+    t.scale2, t.reserved = scale2, reserved
+    return ctypes.byref(t)
+
+
+def test_exports_every_declared_symbol(lib):
+    header = open(os.path.join(ROOT, "include", "qbn.h")).read()
+    declared = re.findall(r"QBN_API\s+[\w\s\*]+?\b(qbn_\w+)\s*\(", header)
+    assert len(declared) == 10
+    assert set(declared) == set(qbn.EXPORTED)
+    so = ctypes.CDLL(qbn.lib_path())
+    for name in declared:
+        assert hasattr(so, name), name
+
+
+def test_abi_and_struct(lib):
+    assert lib.qbn_abi_version() == 1
+    assert lib.qbn_tensor_struct_size() == ctypes.sizeof(qbn._CTensor) == 56
+    for s in range(11):
+        assert lib.qbn_status_string(s)
+    assert lib.qbn_status_string(99) == b"unknown status"
+
+
+def test_bytes_match_page_bit_budgets(lib):
+    # Four Bits, Three Contracts sections 3-5; Chapter 7 section 7.1
+    n, k = 4096, 4096
+    mx = lib.qbn_bytes(MX, n, k, 0, 0) + lib.qbn_bytes(MX, n, k, 0, 1)
+    nv = lib.qbn_bytes(NV, n, k, 0, 0) + lib.qbn_bytes(NV, n, k, 0, 1)
+    qk = lib.qbn_bytes(QK, n, k, 0, 0)
+    q0 = lib.qbn_bytes(Q0, n, k, 0, 0)
+    assert mx * 8 / (n * k) == 4.25
+    assert nv * 8 / (n * k) == 4.5
+    assert qk * 8 / (n * k) == 4.5 and lib.qbn_bytes(QK, 1, 256, 0, 0) == 144
+    assert q0 * 8 / (n * k) == 4.5 and lib.qbn_bytes(Q0, 1, 32, 0, 0) == 18
+    assert lib.qbn_bytes(GP, 11008, 4096, 128, 0) == 22544384
+    assert lib.qbn_bytes(GP, 11008, 4096, 128, 1) == 2 * 32 * 11008
+    assert lib.qbn_bytes(AW, 11008, 4096, 128, 2) == 32 * 11008
+    assert lib.qbn_bytes(QK, 1, 255, 0, 0) == -1
+    assert lib.qbn_bytes(7, 1, 32, 0, 0) == -1
+    assert lib.qbn_bytes(MX, 1, 32, 0, 3) == -1
+    assert lib.qbn_bytes(QK, 1, 256, 0, 1) == 0
+
+
+def test_gemv_rejections(lib):
+    g = lib.qbn_quantized_gemv
+    assert g(None, A, F32, B, F32, None) == NULL
+    assert g(T(9, 4, 32), A, F32, B, F32, None) == FORMAT
+    assert g(T(MX, 4, 32, reserved=1), A, F32, B, F32, None) == FORMAT
+    assert g(T(MX, -1, 32), A, F32, B, F32, None) == SHAPE
+    assert g(T(MX, 4, 48), A, F32, B, F32, None) == SHAPE
+    assert g(T(NV, 4, 40), A, F32, B, F32, None) == SHAPE
+    assert g(T(QK, 4, 512 + 32), A, F32, B, F32, None) == SHAPE
+    assert g(T(Q0, 4, 64), A, F32, B, F32, None) == UNSUP
+    assert g(T(GP, 16, 64, group=32), A, F32, B, F32, None) == UNSUP
+    assert g(T(MX, 4, 64), A, 7, B, F32, None) == FORMAT
+    assert g(T(MX, 4, 64), A, 2, B, F32, None) == DTYPE
+    assert g(T(MX, 4, 64), A, F32, B, BF16, None) == DTYPE
+    assert g(T(MX, 4, 64, data=None), A, F32, B, F32, None) == NULL
+    assert g(T(MX, 4, 64, scales=None), A, F32, B, F32, None) == NULL
+    assert g(T(MX, 4, 64, data=A + 8), A, F32, B, F32, None) == ALIGN
+    assert g(T(MX, 4, 64), A + 4, F32, B, F32, None) == ALIGN
+    assert g(T(MX, 4, 64), A, F32, B + 2, F32, None) == ALIGN
+    assert g(T(MX, 4, 64), None, F32, B, F32, None) == NULL
+    assert g(T(MX, 4, 64), A, F32, None, F32, None) == NULL
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert g(T(NV, 4, 64, scale2=bad), A, F32, B, F32, None) == SCALE2
+    # empty: nothing to do, nothing launched
+    assert g(T(MX, 0, 64, data=None, scales=None), None, F32, None, F32, None) == OK
+
+
+def test_gemm_rejections(lib):
+    g = lib.qbn_quantized_gemm
+    assert g(T(NV, 8, 64), 4, A, BF16, 64, B, BF16, 8, None) == UNSUP
+    assert g(T(MX, 8, 64), 4, A, F32, 64, B, BF16, 8, None) == DTYPE
+    assert g(T(MX, 8, 64), 4, A, BF16, 64, B, F32, 8, None) == DTYPE
+    assert g(T(MX, 8, 64), -1, A, BF16, 64, B, BF16, 8, None) == SHAPE
+    assert g(T(MX, 8, 64), 4, A, BF16, 32, B, BF16, 8, None) == SHAPE
+    assert g(T(MX, 8, 64), 4, A, BF16, 68, B, BF16, 8, None) == ALIGN
+    assert g(T(MX, 8, 64), 4, A, BF16, 64, B, BF16, 4, None) == SHAPE
+    assert g(T(MX, 8, 64), 4, A, BF16, 64, B, BF16, 12, None) == ALIGN
+    assert g(T(MX, 8, 64), 4, A + 8, BF16, 64, B, BF16, 8, None) == ALIGN
+    assert g(T(MX, 8, 64), 0, None, BF16, 64, None, BF16, 8, None) == OK
+
+
+def test_dequant_rejections(lib):
+    d = lib.qbn_dequantize
+    assert d(T(MX, 4, 64), A, 2, 0, None) == DTYPE
+    assert d(T(MX, 4, 64), A, 5, 0, None) == FORMAT
+    assert d(T(MX, 4, 64), A, F32, 2, None) == FORMAT
+    assert d(T(MX, 4, 64), A + 4, F32, 0, None) == ALIGN
+    assert d(T(MX, 4, 64), None, F32, 0, None) == NULL
+    assert d(T(Q0, 4, 64, data=A + 1), B, F32, 0, None) == ALIGN
+    assert d(T(GP, 8, 64, group=0), B, F32, 0, None) == GROUP
+    assert d(T(GP, 8, 64, group=12), B, F32, 0, None) == GROUP
+    assert d(T(GP, 8, 64, group=48), B, F32, 0, None) == SHAPE
+    assert d(T(AW, 12, 64, group=32), B, F32, 0, None) == SHAPE
+    assert d(T(GP, 8, 64, group=32, zeros=None), B, F32, 0, None) == NULL
+    assert d(T(GP, 8, 64, group=32, scales=B + 1), B, F32, 0, None) == ALIGN
+
+
+def test_repack_rejections(lib):
+    r = lib.qbn_repack
+    assert r(T(MX, 8, 64), Q0, 0, A, None, None, None) == UNSUP
+    assert r(T(GP, 8, 64, group=32), GP, 32, A, None, None, None) == UNSUP
+    assert r(T(GP, 8, 64, group=32), 11, 32, A, None, None, None) == FORMAT
+    assert r(T(GP, 12, 64, group=32), AW, 32, A, None, None, None) == SHAPE
+    assert r(T(GP, 8, 64, group=32), AW, 64, A, None, None, None) == GROUP
+    assert r(T(GP, 8, 64, group=16), Q0, 0, A, None, None, None) == GROUP
+    assert r(T(Q0, 8, 64), GP, 16, A, B, C, None) == GROUP
+    assert r(T(Q0, 8, 64), GP, 96, A, B, C, None) == GROUP
+    assert r(T(Q0, 8, 64), GP, 32, A, None, C, None) == NULL
+    assert r(T(GP, 8, 64, group=32), AW, 32, None, None, None, None) == NULL
+    assert r(T(GP, 8, 64, group=32), AW, 32, A + 2, None, None, None) == ALIGN
+    assert r(T(GP, 8, 64, group=32), Q0, 0, A + 1, None, None, None) == ALIGN
+
+
+def test_validate_rejections(lib):
+    v = lib.qbn_validate
+    assert v(T(MX, 4, 64), None, None) == NULL
+    assert v(T(MX, 4, 64), A + 4, None) == ALIGN
+    assert v(T(NV, 4, 64, scale2=0.0), A, None) == SCALE2
+    assert v(T(Q0, 4, 64, group=48), A, None) == GROUP
+    assert v(T(Q0, 4, 96, group=64), A, None) == SHAPE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    w = qbn.QTensor("mxfp4", 2, 32, torch.zeros(2, 16, dtype=torch.uint8), torch.zeros(2, 1, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        qbn.quantized_gemv(w, torch.zeros(32), torch.zeros(2))
