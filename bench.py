@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Throughput of the 4-bit block-quantized hot path on one MI355X.
+
+Default workload (the headline one): NVFP4 decode GEMV, W 4096 x 4096 (E2M1
+codes, E4M3FN scale per 16, f32 scale2 = 0.01), x bf16, batch 1. A step is
+one fused dequantize-and-dot over one weight matrix. The other workloads
+(--workload) measure the remaining kernels of the path on their own shapes.
+
+Timing. Inputs are generated on the host once and copied to HBM before the
+timed region. Each step reads its own copy of the weights, cycling through R
+copies that together exceed 600 MB, so every launch streams its weights from
+HBM rather than from the 32 MB of L2 or the 256 MB MALL. The K timed steps
+are captured once into a HIP graph and replayed between two HIP events
+(launch overhead is then the GPU's, not Python's): ms_per_step and value
+come from that replay. The CPU baseline times the CPU oracle (single thread) on the
+same workload and reports it in the same unit.
+
+The per-launch duration used for the roofline is the event-timed replay
+divided by K: the graph issues the K launches back to back on one stream, so
+this is each kernel's average duration plus the (small) inter-kernel gap.
+Event pairs around individual launches are not used: each pair adds several
+microseconds of marker overhead, more than the kernels themselves take.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD published
+ROTATE_BYTES = 600e6
+
+# Algorithmic bytes / flops per step (read + write of every operand once).
+WORKLOADS = {
+    "nvfp4_gemv": dict(
+        cfg=2, kind="gemv", unit="GB/s",
+        desc="NVFP4 decode GEMV 4096x4096: E2M1 codes, E4M3FN scale per 16, f32 scale2=0.01, x bf16, y f32, batch 1",
+        bytes=4096 * 2048 + 4096 * 256 + 4 + 4096 * 2 + 4096 * 4),
+    "mxfp4_gemv": dict(
+        cfg=1, kind="gemv", unit="GB/s",
+        desc="MXFP4 dequant-GEMV 256x1024: E2M1 codes, E8M0 scale per 32, x f32, y f32, batch 1",
+        bytes=256 * 512 + 256 * 32 + 1024 * 4 + 256 * 4),
+    "q4k_gemv": dict(
+        cfg=3, kind="gemv", unit="GB/s",
+        desc="Q4_K decode GEMV 14336x4096: 144-byte super-blocks of 256, x f32, y f32, batch 1",
+        bytes=14336 * 16 * 144 + 4096 * 4 + 14336 * 4),
+    "mxfp4_gemm": dict(
+        cfg=4, kind="gemm", unit="TFLOP/s",
+        desc="MXFP4 prefill GEMM: W 8192x8192 (E2M1, E8M0 per 32) x X bf16 2048x8192 -> Y bf16, fp32 accumulate",
+        flops=2.0 * 2048 * 8192 * 8192, bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 * 2 * 2),
+    "gptq_to_awq": dict(
+        cfg=5, kind="repack", unit="GB/s", src="gptq4", dst="awq4",
+        desc="int4 repack GPTQ int32 [K/8][N] -> AWQ int32 [K][N/8], K x N = 4096 x 11008",
+        bytes=2 * 22544384),
+    "awq_to_q4_0": dict(
+        cfg=5, kind="repack", unit="GB/s", src="awq4", dst="q4_0",
+        desc="int4 repack AWQ int32 [K][N/8] + fp16 group-128 scales -> GGUF Q4_0 blocks, K x N = 4096 x 11008",
+        bytes=22544384 + 704512 + 25362432),
+    "gptq_dequant_bf16": dict(
+        cfg=5, kind="dequant", unit="GB/s",
+        desc="bulk dequant GPTQ (fp16 scales, u8 zeros, group 128) -> bf16 [K][N], K x N = 4096 x 11008",
+        bytes=22544384 + 704512 + 352256 + 90177536),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (default depends on the workload)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="nvfp4_gemv", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
+    return ap.parse_args()
+
+
+def host_to_device(a, dev):
+    import torch
+
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev)
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def build_steps(name, spec, dev):
+    """Return (list of prepared calls, one per weight copy, description of R)."""
+    import torch
+
+    import bit_block_quantized_nibble_amd as qbn
+    import workloads
+
+    inp = workloads.workload(spec["cfg"])
+    calls = []
+    if spec["kind"] == "gemv":
+        n, k = inp["n"], inp["k"]
+        wbytes = inp["data"].nbytes + (0 if inp["scales"] is None else inp["scales"].nbytes)
+        R = max(1, math.ceil(ROTATE_BYTES / wbytes))
+        d0 = host_to_device(inp["data"], dev)
+        s0 = None if inp["scales"] is None else host_to_device(inp["scales"], dev)
+        x = host_to_device(inp["x"], dev)
+        if inp["x"].dtype == np.uint16:
+            x = x.view(torch.bfloat16)
+        y = torch.empty(n, dtype=torch.float32, device=dev)
+        for _ in range(R):
+            w = qbn.QTensor(inp["fmt"], n, k, d0.clone(), None if s0 is None else s0.clone(), scale2=inp["scale2"])
+            calls.append(qbn.prepare_gemv(w, x, y))
+        return calls, R, inp
+    if spec["kind"] == "gemm":
+        n, k, m = inp["n"], inp["k"], inp["m"]
+        R = 2
+        d0 = host_to_device(inp["data"], dev)
+        s0 = host_to_device(inp["scales"], dev)
+        X = host_to_device(inp["X"], dev).view(torch.bfloat16)
+        Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        for _ in range(R):
+            w = qbn.QTensor("mxfp4", n, k, d0.clone(), s0.clone())
+            calls.append(qbn.prepare_gemm(w, X, Y))
+        return calls, R, inp
+    # cfg 5: repack / dequant from GPTQ (or from AWQ made by the library itself)
+    K, N, g = inp["K"], inp["N"], inp["group"]
+    qw = host_to_device(inp["qweight"], dev)
+    sc = host_to_device(inp["scales"].view(np.uint16), dev)
+    zr = host_to_device(inp["zeros"], dev)
+    per = spec["bytes"]
+    R = max(1, math.ceil(ROTATE_BYTES / per))
+    src_fmt = spec.get("src", "gptq4")
+    base = qbn.QTensor("gptq4", N, K, qw, sc, zr, group=g)
+    if src_fmt == "awq4":
+        base = qbn.repack(base, "awq4")
+        torch.cuda.synchronize()
+    for _ in range(R):
+        src = qbn.QTensor(src_fmt, N, K, base.data.clone(), sc.clone(), zr.clone(), group=g)
+        if spec["kind"] == "dequant":
+            out = torch.empty((K, N), dtype=torch.bfloat16, device=dev)
+            calls.append(qbn.prepare_dequantize(src, out, layout="kn"))
+        else:
+            if spec["dst"] == "awq4":
+                dst = qbn.QTensor("awq4", N, K, torch.empty((K, N // 8), dtype=torch.int32, device=dev), src.scales,
+                                  src.zeros, group=g)
+            else:
+                dst = qbn.QTensor("q4_0", N, K, torch.empty((N, K // 32, 18), dtype=torch.uint8, device=dev))
+            calls.append(qbn.prepare_repack(src, dst))
+    return calls, R, inp
+
+
+def cpu_baseline(name, spec, inp, budget_s):
+    """Time the CPU oracle (one thread) on the same workload."""
+    import oracle
+
+    cores = 1
+    reps = []
+    t_end = time.perf_counter() + budget_s
+    if spec["kind"] == "gemv":
+        fmt = {"mxfp4": oracle.MXFP4, "nvfp4": oracle.NVFP4, "q4_k": oracle.Q4_K}[inp["fmt"]]
+        n, k = inp["n"], inp["k"]
+        rows = np.arange(n)
+        while True:
+            t0 = time.perf_counter()
+            oracle.gemv_rows(fmt, inp["data"], inp["scales"], inp["scale2"], k, inp["x"], rows)
+            reps.append(time.perf_counter() - t0)
+            if time.perf_counter() > t_end and len(reps) >= 3:
+                break
+        t = float(np.median(reps))
+        return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                    sample="full %dx%d GEMV, median of %d runs (%.2f s each)" % (n, k, len(reps), t))
+    if spec["kind"] == "gemm":
+        n, k, m = inp["n"], inp["k"], inp["m"]
+        rng = np.random.default_rng(0)
+        ms_, ns_ = [], []
+        done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            mm = rng.integers(0, m, 16)
+            nn = np.full(16, rng.integers(0, n))
+            oracle.gemm_entries(oracle.MXFP4, inp["data"], inp["scales"], 1.0, k, inp["X"], mm, nn)
+            done += 16
+        t = time.perf_counter() - t0
+        return dict(value=2.0 * k * done / t / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                    sample="%d sampled output entries of the %dx%d output (2k flops each), %.1f s" % (done, m, n, t))
+    # repack / dequant through the oracle's logical matrix
+    K, N, g = inp["K"], inp["N"], inp["group"]
+    while True:
+        t0 = time.perf_counter()
+        q = oracle.gptq_unpack(inp["qweight"])
+        if spec["kind"] == "dequant":
+            w = oracle.affine_dequant(q, inp["scales"].view(np.uint16), inp["zeros"], g)
+            oracle.bf16_rne_array(w)
+        elif spec["dst"] == "awq4":
+            oracle.awq_pack(q)
+        else:
+            d = np.ascontiguousarray(np.repeat(inp["scales"].view(np.uint16).T, g // 32, axis=1))
+            oracle.q4_0_pack(q, d)
+        reps.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(reps) >= 5:
+            break
+    t = float(np.median(reps))
+    return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                sample="full %dx%d %s, median of %d runs (%.2f s each)" % (K, N, name, len(reps), t))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the GEMV would shard by output rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_block_quantized_nibble_amd as qbn
+
+    if not os.path.exists(qbn.lib_path()):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    spec = WORKLOADS[args.workload]
+    steps = args.steps or (2000 if spec["kind"] != "gemm" else 50)
+    dev = torch.device("cuda:0")
+    calls, R, inp = build_steps(args.workload, spec, dev)
+    torch.cuda.synchronize()
+
+    # warmup (untimed), then capture the K timed steps into one graph
+    for i in range(max(args.warmup, 1)):
+        calls[i % R]()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            calls[i % R]()
+    graph.replay()  # one untimed replay
+    torch.cuda.synchronize()
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / steps
+
+    # Further replays of the same graph give the spread of the per-launch
+    # duration (the first replay above is the reported measurement).
+    spread = []
+    for _ in range(4):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        spread.append(a.elapsed_time(b) / steps)
+    kernel_ms = ms_step
+
+    if spec["kind"] == "gemm":
+        value = spec["flops"] / (ms_step * 1e-3) / 1e12
+        achieved = spec["flops"] / (kernel_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), traffic=None)
+        metric = "FP4 GEMM TFLOP/s (% MFMA peak)"
+    else:
+        value = spec["bytes"] / (ms_step * 1e-3) / 1e9
+        achieved = spec["bytes"] / (kernel_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+        metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] == "gemv" else (
+            "int4 repack GB/s (% HBM peak)" if spec["kind"] == "repack" else "bulk dequant GB/s (% HBM peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, spec, inp, args.cpu_seconds)
+
+    line = {
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": spec["unit"],
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": spec["desc"],
+            "name": args.workload,
+            "seed": int(inp["seed"]),
+            "rotating_copies": R,
+            "step_bytes": spec["bytes"],
+            **({"step_flops": spec["flops"]} if "flops" in spec else {}),
+            "kernel_ms_per_launch": round(kernel_ms, 6),
+            "kernel_ms_other_replays": [round(v, 6) for v in spread],
+            "timed_wall_s": round(wall, 4),
+            "gpu": torch.cuda.get_device_name(0),
+            "host": platform.processor() or platform.machine(),
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -13,14 +13,15 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
-from dataclasses import dataclass, replace
+from dataclasses import dataclass
 from typing import Optional
 
 import torch
 
 __all__ = [
     "QTensor", "QbnError", "quantized_gemv", "quantized_gemm", "dequantize", "repack", "validate", "nbytes",
-    "status_string", "lib_path", "FORMATS",
+    "status_string", "lib_path", "FORMATS", "Prepared", "prepare_gemv", "prepare_gemm", "prepare_dequantize",
+    "prepare_repack",
 ]
 
 FORMATS = {"mxfp4": 1, "nvfp4": 2, "q4_k": 3, "q4_0": 4, "gptq4": 5, "awq4": 6}
@@ -181,6 +182,8 @@ def quantized_gemm(w: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None
     m = x.shape[0]
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.bfloat16, device=w.device)
+    if not (x.is_cuda and y.is_cuda):
+        raise ValueError("x and y must be device (cuda) tensors")
     ct = w._c()
     ldx = x.stride(0) if x.shape[0] > 1 else x.shape[1]
     ldy = y.stride(0) if y.shape[0] > 1 else y.shape[1]
@@ -253,3 +256,54 @@ def validate(w: QTensor) -> int:
     ct = w._c()
     _check(lib.qbn_validate(ctypes.byref(ct), _ptr(first, "first_bad"), _stream(w.device)), "qbn_validate")
     return int(first.item())
+
+
+class Prepared:
+    """A library call with its arguments marshalled once, for tight loops and
+    HIP-graph capture: calling it issues the C entry point on the current
+    stream of the tensors' device and raises on a nonzero status."""
+
+    def __init__(self, fn, args, where, device, keep):
+        self._fn, self._args, self._where, self._device = fn, args, where, device
+        self._keep = keep  # tensors and structs referenced by raw pointers
+
+    def __call__(self):
+        st = self._fn(*self._args, _stream(self._device))
+        if st != 0:
+            raise QbnError(st, self._where)
+
+
+def prepare_gemv(w: QTensor, x: torch.Tensor, y: torch.Tensor) -> Prepared:
+    lib = _load()
+    ct = w._c()
+    args = (ctypes.byref(ct), _ptr(x, "x"), _DTYPES[x.dtype], _ptr(y, "y"), _DTYPES.get(y.dtype, -1))
+    return Prepared(lib.qbn_quantized_gemv, args, "qbn_quantized_gemv", w.device, (w, x, y, ct))
+
+
+def prepare_gemm(w: QTensor, x: torch.Tensor, y: torch.Tensor) -> Prepared:
+    lib = _load()
+    if not (x.is_cuda and y.is_cuda) or x.stride(1) != 1 or y.stride(1) != 1:
+        raise ValueError("x and y must be device tensors with contiguous rows")
+    ct = w._c()
+    m = x.shape[0]
+    args = (ctypes.byref(ct), m, ctypes.c_void_p(x.data_ptr()), _DTYPES.get(x.dtype, -1), x.stride(0),
+            ctypes.c_void_p(y.data_ptr()), _DTYPES.get(y.dtype, -1), y.stride(0))
+    return Prepared(lib.qbn_quantized_gemm, args, "qbn_quantized_gemm", w.device, (w, x, y, ct))
+
+
+def prepare_dequantize(w: QTensor, out: torch.Tensor, layout: str = "nk") -> Prepared:
+    lib = _load()
+    ct = w._c()
+    args = (ctypes.byref(ct), _ptr(out, "out"), _DTYPES.get(out.dtype, -1), {"nk": 0, "kn": 1}[layout])
+    return Prepared(lib.qbn_dequantize, args, "qbn_dequantize", w.device, (w, out, ct))
+
+
+def prepare_repack(src: QTensor, dst: QTensor) -> Prepared:
+    """Repack src into the preallocated buffers of dst (same n, k)."""
+    lib = _load()
+    ct = src._c()
+    sc = dst.scales if (dst.scales is not None and dst.scales is not src.scales) else None
+    zr = dst.zeros if (dst.zeros is not None and dst.zeros is not src.zeros) else None
+    args = (ctypes.byref(ct), FORMATS[dst.format], int(dst.group), _ptr(dst.data, "data"), _ptr(sc, "scales"),
+            _ptr(zr, "zeros"))
+    return Prepared(lib.qbn_repack, args, "qbn_repack", src.device, (src, dst, ct))

@@ -18,10 +18,10 @@ namespace {
 
 constexpr int kBlock = 256;
 
-// AWQ slot order: slot t of a word holds column kAwqOrder[t] of its group of
-// eight ("Bit Packing Architecture", 'Real layouts compared'); column c sits
-// at bit 4 * kAwqSlot[c].
-__device__ __constant__ int kAwqSlot[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+// AWQ slot order: the slots of a word hold columns 0,2,4,6,1,3,5,7 of its
+// group of eight ("Bit Packing Architecture", 'Real layouts compared'), so
+// column c sits in slot awq_slot(c), at bit 4 * awq_slot(c).
+__device__ __forceinline__ constexpr int awq_slot(int c) { return (c & 1) ? 4 + (c >> 1) : (c >> 1); }
 
 template <bool BF16>
 struct Out;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kBlock) void k_dequant_awq(const uint32_t *__restri
         const int64_t col = 8 * g + c;
         const float s = f16_bits_f32(scales[gi * n + col]);
         const float z = (float)zeros[gi * n + col];
-        o[c] = s * ((float)((wd >> (4 * kAwqSlot[c])) & 15u) - z);
+        o[c] = s * ((float)((wd >> (4 * awq_slot(c))) & 15u) - z);
     }
     if (LAYOUT == 1) {
         Out<BF16>::put4(out, kk * n + 8 * g, o[0], o[1], o[2], o[3]);

@@ -105,86 +105,115 @@ __device__ __forceinline__ float dot16_generic<__bf16>(const uint8_t *cp, const 
     return acc;
 }
 
-// ------------------------------------------------------------------ E2M1 fast kernel
-// FMT: QBN_MXFP4 or QBN_NVFP4. A chunk is 16 code bytes = 32 elements
-// (one MXFP4 group, two NVFP4 groups). C = k/32 chunks per row; lane li of a
-// row covers chunks li + LPR*j, j < CPL. Requires C == LPR*CPL.
-template <int FMT, typename XT, int LPR, int CPL, int RPW>
-__global__ __launch_bounds__(256) void k_gemv_e2m1_fast(const uint8_t *__restrict__ codes,
-                                                        const uint8_t *__restrict__ scales, float scale2,
-                                                        const XT *__restrict__ x, float *__restrict__ y, int64_t n,
-                                                        int64_t k) {
-    constexpr int SUB = kWave / LPR;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int sub = lane / LPR;
-    const int li = lane % LPR;
-    const int64_t row0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + wave) * (int64_t)(RPW * SUB);
-    const int64_t row_bytes = k / 2;
-    const int64_t C = k / 32;
-    const int64_t spr = (FMT == QBN_MXFP4) ? C : 2 * C;  // scale bytes per row
+// ------------------------------------------------------------------ E2M1 row-loop kernel
+// FMT: QBN_MXFP4 or QBN_NVFP4. A chunk is 16 code bytes = 32 elements (one
+// MXFP4 group, two NVFP4 groups); C = k/32 chunks per row, C == LPR * CPL.
+// A pass is SUB = 64/LPR rows handled by one wave; lane li of a row covers
+// chunks li + LPR*j (j < CPL), so each 16-byte load instruction of a wave
+// reads 1 KiB of contiguous codes. Waves stride over passes; the next pass's
+// codes and scales are loaded into a second register set while the current
+// pass is computed, so HBM streaming overlaps the decode arithmetic.
+template <int CPL>
+struct E2M1Frag {
+    u32x4 q[CPL];
+    uint32_t sb[CPL];  // MXFP4: E8M0 byte; NVFP4: two E4M3FN bytes (low = first group)
+};
 
-    u32x4 q[RPW][CPL];
-    uint32_t sb[RPW][CPL];
+template <int FMT, int LPR, int CPL>
+__device__ __forceinline__ void e2m1_load(E2M1Frag<CPL> &f, const uint8_t *__restrict__ codes,
+                                          const uint8_t *__restrict__ scales, int64_t row, bool ok, int li,
+                                          int64_t row_bytes, int64_t spr) {
 #pragma unroll
-    for (int p = 0; p < RPW; ++p) {
-        const int64_t row = row0 + p * SUB + sub;
-        const bool ok = row < n;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int64_t ch = li + (int64_t)LPR * j;
-            if (ok) {
-                q[p][j] = ld16(codes + row * row_bytes + 16 * ch);
-            } else {
-                q[p][j] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
+    for (int j = 0; j < CPL; ++j) {
+        const int64_t ch = li + (int64_t)LPR * j;
+        f.q[j] = ok ? ld16(codes + row * row_bytes + 16 * ch) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int p = 0; p < RPW; ++p) {
-        const int64_t row = row0 + p * SUB + sub;
-        const bool ok = row < n;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int64_t ch = li + (int64_t)LPR * j;
-            if (FMT == QBN_MXFP4) {
-                sb[p][j] = ok ? (uint32_t)scales[row * spr + ch] : 127u;
-            } else {
-                const uint8_t *sp = scales + row * spr + 2 * ch;
-                sb[p][j] = ok ? ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8)) : 0u;
-            }
+    for (int j = 0; j < CPL; ++j) {
+        const int64_t ch = li + (int64_t)LPR * j;
+        if (FMT == QBN_MXFP4) {
+            f.sb[j] = ok ? (uint32_t)scales[row * spr + ch] : 127u;
+        } else {
+            const uint8_t *sp = scales + row * spr + 2 * ch;
+            f.sb[j] = ok ? ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8)) : 0u;
         }
+    }
+}
+
+template <int FMT, typename XT, int CPL>
+__device__ __forceinline__ float e2m1_compute(const E2M1Frag<CPL> &f, const XChunk<XT> *xc) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const u32x4 w = f.q[j];
+        if (FMT == QBN_MXFP4) {
+            float g = 0.0f;
+            g = xc[j].dot(0, w.x, g);
+            g = xc[j].dot(1, w.y, g);
+            g = xc[j].dot(2, w.z, g);
+            g = xc[j].dot(3, w.w, g);
+            acc += __builtin_amdgcn_ldexpf(g, e8m0_exponent(f.sb[j]));
+        } else {
+            float g0 = 0.0f, g1 = 0.0f;
+            g0 = xc[j].dot(0, w.x, g0);
+            g0 = xc[j].dot(1, w.y, g0);
+            g1 = xc[j].dot(2, w.z, g1);
+            g1 = xc[j].dot(3, w.w, g1);
+            acc = __builtin_fmaf(g0, e4m3fn_f32_valid(f.sb[j] & 0xFFu), acc);
+            acc = __builtin_fmaf(g1, e4m3fn_f32_valid(f.sb[j] >> 8), acc);
+        }
+    }
+    return acc;
+}
+
+template <int FMT, typename XT, int LPR, int CPL, int WPB>
+__global__ __launch_bounds__(WPB * 64) void k_gemv_e2m1_loop(const uint8_t *__restrict__ codes,
+                                                             const uint8_t *__restrict__ scales, float scale2,
+                                                             const XT *__restrict__ x, float *__restrict__ y,
+                                                             int64_t n, int64_t k) {
+    constexpr int SUB = kWave / LPR;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int sub = lane / LPR;
+    const int li = lane % LPR;
+    const int64_t passes = (n + SUB - 1) / SUB;
+    const int64_t stride = (int64_t)gridDim.x * WPB;
+    const int64_t row_bytes = k / 2;
+    const int64_t spr = (FMT == QBN_MXFP4) ? k / 32 : k / 16;  // scale bytes per row
+    int64_t p = (int64_t)blockIdx.x * WPB + threadIdx.x / kWave;
+
+    E2M1Frag<CPL> fa, fb;
+    if (p < passes) {
+        const int64_t row = p * SUB + sub;
+        e2m1_load<FMT, LPR, CPL>(fa, codes, scales, row, row < n, li, row_bytes, spr);
     }
     XChunk<XT> xc[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) xc[j].load(x, 32 * (li + (int64_t)LPR * j));
 
-#pragma unroll
-    for (int p = 0; p < RPW; ++p) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const u32x4 w = q[p][j];
-            if (FMT == QBN_MXFP4) {
-                float g = 0.0f;
-                g = xc[j].dot(0, w.x, g);
-                g = xc[j].dot(1, w.y, g);
-                g = xc[j].dot(2, w.z, g);
-                g = xc[j].dot(3, w.w, g);
-                acc += __builtin_amdgcn_ldexpf(g, e8m0_exponent(sb[p][j]));
-            } else {
-                float g0 = 0.0f, g1 = 0.0f;
-                g0 = xc[j].dot(0, w.x, g0);
-                g0 = xc[j].dot(1, w.y, g0);
-                g1 = xc[j].dot(2, w.z, g1);
-                g1 = xc[j].dot(3, w.w, g1);
-                acc = __builtin_fmaf(g0, e4m3fn_f32_valid(sb[p][j] & 0xFFu), acc);
-                acc = __builtin_fmaf(g1, e4m3fn_f32_valid(sb[p][j] >> 8), acc);
-            }
+    while (p < passes) {
+        int64_t pn = p + stride;
+        if (pn < passes) {
+            const int64_t row = pn * SUB + sub;
+            e2m1_load<FMT, LPR, CPL>(fb, codes, scales, row, row < n, li, row_bytes, spr);
         }
-        acc = group_sum<LPR>(acc);
-        const int64_t row = row0 + p * SUB + sub;
-        if (li == 0 && row < n) y[row] = (FMT == QBN_NVFP4) ? acc * scale2 : acc;
+        {
+            float acc = group_sum_last<LPR>(e2m1_compute<FMT, XT, CPL>(fa, xc));
+            const int64_t row = p * SUB + sub;
+            if (li == LPR - 1 && row < n) y[row] = (FMT == QBN_NVFP4) ? acc * scale2 : acc;
+        }
+        p = pn;
+        if (p >= passes) break;
+        pn = p + stride;
+        if (pn < passes) {
+            const int64_t row = pn * SUB + sub;
+            e2m1_load<FMT, LPR, CPL>(fa, codes, scales, row, row < n, li, row_bytes, spr);
+        }
+        {
+            float acc = group_sum_last<LPR>(e2m1_compute<FMT, XT, CPL>(fb, xc));
+            const int64_t row = p * SUB + sub;
+            if (li == LPR - 1 && row < n) y[row] = (FMT == QBN_NVFP4) ? acc * scale2 : acc;
+        }
+        p = pn;
     }
 }
 
@@ -220,8 +249,8 @@ __global__ __launch_bounds__(256) void k_gemv_e2m1_generic(const uint8_t *__rest
         }
         acc += part;
     }
-    acc = group_sum<kWave>(acc);
-    if (lane == 0) y[row] = (FMT == QBN_NVFP4) ? acc * scale2 : acc;
+    acc = group_sum_last<kWave>(acc);
+    if (lane == kWave - 1) y[row] = (FMT == QBN_NVFP4) ? acc * scale2 : acc;
 }
 
 // ------------------------------------------------------------------ Q4_K
@@ -338,40 +367,70 @@ __device__ __forceinline__ float q4k_dword(uint32_t v, int t, float sl, float ol
     return acc;
 }
 
-// NB = blocks per row when NB < 8 (then SUB = 8/NB rows per pass, BPL = 1);
-// NB = 0 means k/256 = 8*BPL (SUB = 1).
-template <typename XT, int BPL, int SUB, int RPW>
-__global__ __launch_bounds__(256) void k_gemv_q4k_fast(const uint8_t *__restrict__ blocks,
-                                                       const XT *__restrict__ x, float *__restrict__ y, int64_t n,
-                                                       int64_t k) {
+// Row-loop Q4_K kernel. A pass is SUB rows (SUB = 8/(k/256) when a row has
+// fewer than 8 blocks, else 1); within a row, the 8 block slots of a wave
+// (8 lanes each) cover blocks bs + 8j, j < BPL. Waves stride over passes
+// with the next pass's blocks prefetched into a second register set.
+template <int BPL>
+struct Q4KFrag {
+    u32x4 h[BPL], q[BPL];
+};
+
+template <int BPL, int NBR>
+__device__ __forceinline__ void q4k_load(Q4KFrag<BPL> &f, const uint8_t *__restrict__ blocks, int64_t row, bool ok,
+                                         int bs, int c, int64_t row_bytes) {
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+        const uint8_t *blk = blocks + row * row_bytes + 144 * (int64_t)(bs + NBR * j);
+        f.q[j] = ok ? ld16(blk + 16 + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+        const uint8_t *blk = blocks + row * row_bytes + 144 * (int64_t)(bs + NBR * j);
+        f.h[j] = ok ? ld16(blk) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <typename XT, int BPL>
+__device__ __forceinline__ float q4k_compute(const Q4KFrag<BPL> &f, const XQ4K<XT> *xq, const Q4KLaneConsts &L) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+        float st, of;
+        q4k_pair(f.h[j], L, st, of);
+        const float sl = quad_perm<0xA0>(st);  // pair c & ~1
+        const float ol = quad_perm<0xA0>(of);
+        const float sh = quad_perm<0xF5>(st);  // pair c | 1
+        const float oh = quad_perm<0xF5>(of);
+        const u32x4 v = f.q[j];
+        acc = q4k_dword<XT>(v.x, 0, sl, ol, sh, oh, xq[j], acc);
+        acc = q4k_dword<XT>(v.y, 1, sl, ol, sh, oh, xq[j], acc);
+        acc = q4k_dword<XT>(v.z, 2, sl, ol, sh, oh, xq[j], acc);
+        acc = q4k_dword<XT>(v.w, 3, sl, ol, sh, oh, xq[j], acc);
+    }
+    return acc;
+}
+
+template <typename XT, int BPL, int SUB, int WPB>
+__global__ __launch_bounds__(WPB * 64) void k_gemv_q4k_loop(const uint8_t *__restrict__ blocks,
+                                                            const XT *__restrict__ x, float *__restrict__ y,
+                                                            int64_t n, int64_t k) {
     constexpr int LPR = kWave / SUB;  // lanes per row
     constexpr int NBR = LPR / 8;      // blocks covered by one pass of a row's lanes
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
     const int c = lane & 7;
     const int slot = lane >> 3;
     const int sub = slot / NBR;
     const int bs = slot % NBR;
-    const int64_t nb = k / 256;
-    const int64_t row_bytes = 144 * nb;
-    const int64_t row0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + wave) * (int64_t)(RPW * SUB);
+    const int64_t row_bytes = 144 * (k / 256);
+    const int64_t passes = (n + SUB - 1) / SUB;
+    const int64_t stride = (int64_t)gridDim.x * WPB;
+    int64_t p = (int64_t)blockIdx.x * WPB + threadIdx.x / kWave;
 
-    u32x4 hv[RPW][BPL], qv[RPW][BPL];
-#pragma unroll
-    for (int p = 0; p < RPW; ++p) {
-        const int64_t row = row0 + p * SUB + sub;
-        const bool ok = row < n;
-#pragma unroll
-        for (int j = 0; j < BPL; ++j) {
-            const uint8_t *blk = blocks + row * row_bytes + 144 * (int64_t)(bs + NBR * j);
-            if (ok) {
-                qv[p][j] = ld16(blk + 16 + 16 * c);
-                hv[p][j] = ld16(blk);
-            } else {
-                qv[p][j] = u32x4{0u, 0u, 0u, 0u};
-                hv[p][j] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
+    Q4KFrag<BPL> fa, fb;
+    if (p < passes) {
+        const int64_t row = p * SUB + sub;
+        q4k_load<BPL, NBR>(fa, blocks, row, row < n, bs, c, row_bytes);
     }
     XQ4K<XT> xq[BPL];
 #pragma unroll
@@ -379,26 +438,30 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_fast(const uint8_t *__restrict
         xq[j].load(x, 256 * (int64_t)(bs + NBR * j) + 64 * (c >> 1) + 16 * (c & 1));
     const Q4KLaneConsts L = q4k_lane_consts(c);
 
-#pragma unroll
-    for (int p = 0; p < RPW; ++p) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < BPL; ++j) {
-            float st, of;
-            q4k_pair(hv[p][j], L, st, of);
-            const float sl = quad_perm<0xA0>(st);  // pair c & ~1
-            const float ol = quad_perm<0xA0>(of);
-            const float sh = quad_perm<0xF5>(st);  // pair c | 1
-            const float oh = quad_perm<0xF5>(of);
-            const u32x4 v = qv[p][j];
-            acc = q4k_dword<XT>(v.x, 0, sl, ol, sh, oh, xq[j], acc);
-            acc = q4k_dword<XT>(v.y, 1, sl, ol, sh, oh, xq[j], acc);
-            acc = q4k_dword<XT>(v.z, 2, sl, ol, sh, oh, xq[j], acc);
-            acc = q4k_dword<XT>(v.w, 3, sl, ol, sh, oh, xq[j], acc);
+    while (p < passes) {
+        int64_t pn = p + stride;
+        if (pn < passes) {
+            const int64_t row = pn * SUB + sub;
+            q4k_load<BPL, NBR>(fb, blocks, row, row < n, bs, c, row_bytes);
         }
-        acc = group_sum<LPR>(acc);
-        const int64_t row = row0 + p * SUB + sub;
-        if ((lane % LPR) == 0 && row < n) y[row] = acc;
+        {
+            const float acc = group_sum_last<LPR>(q4k_compute<XT, BPL>(fa, xq, L));
+            const int64_t row = p * SUB + sub;
+            if ((lane % LPR) == LPR - 1 && row < n) y[row] = acc;
+        }
+        p = pn;
+        if (p >= passes) break;
+        pn = p + stride;
+        if (pn < passes) {
+            const int64_t row = pn * SUB + sub;
+            q4k_load<BPL, NBR>(fa, blocks, row, row < n, bs, c, row_bytes);
+        }
+        {
+            const float acc = group_sum_last<LPR>(q4k_compute<XT, BPL>(fb, xq, L));
+            const int64_t row = p * SUB + sub;
+            if ((lane % LPR) == LPR - 1 && row < n) y[row] = acc;
+        }
+        p = pn;
     }
 }
 
@@ -439,8 +502,8 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_generic(const uint8_t *__restr
         }
         acc += part;
     }
-    acc = group_sum<kWave>(acc);
-    if (lane == 0) y[row] = acc;
+    acc = group_sum_last<kWave>(acc);
+    if (lane == kWave - 1) y[row] = acc;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -448,12 +511,34 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_generic(const uint8_t *__restr
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 
-template <int FMT, typename XT, int LPR, int CPL, int RPW>
-hipError_t run_e2m1_fast(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+// Compute units of the current device (cached per device ordinal).
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cache[dev] = v;
+    }
+    return cache[dev];
+}
+
+// Grid for a row-loop kernel: enough blocks for `passes` (one wave each)
+// but at most `per_cu` resident blocks per compute unit; the waves then
+// stride over the remaining passes.
+int64_t loop_grid(int64_t passes, int wpb, int per_cu) {
+    const int64_t want = (passes + wpb - 1) / wpb;
+    const int64_t cap = (int64_t)device_cus() * per_cu;
+    return want < cap ? want : cap;
+}
+
+template <int FMT, typename XT, int LPR, int CPL, int WPB, int PER_CU>
+hipError_t run_e2m1_loop(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     constexpr int SUB = kWave / LPR;
-    const int64_t rows_per_block = (int64_t)kWavesPerBlock * RPW * SUB;
-    const int64_t grid = (w.n + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((k_gemv_e2m1_fast<FMT, XT, LPR, CPL, RPW>), dim3((unsigned)grid), dim3(kBlock), 0, s,
+    const int64_t passes = (w.n + SUB - 1) / SUB;
+    const int64_t grid = loop_grid(passes, WPB, PER_CU);
+    hipLaunchKernelGGL((k_gemv_e2m1_loop<FMT, XT, LPR, CPL, WPB>), dim3((unsigned)grid), dim3(WPB * kWave), 0, s,
                        (const uint8_t *)w.data, (const uint8_t *)w.scales, w.scale2, x, y, w.n, w.k);
     return hipGetLastError();
 }
@@ -463,15 +548,15 @@ hipError_t run_e2m1(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     const int64_t C = w.k / 32;
     if (w.k % 32 == 0) {
         switch (C) {
-        case 1: return run_e2m1_fast<FMT, XT, 1, 1, 1>(w, x, y, s);
-        case 2: return run_e2m1_fast<FMT, XT, 2, 1, 1>(w, x, y, s);
-        case 4: return run_e2m1_fast<FMT, XT, 4, 1, 1>(w, x, y, s);
-        case 8: return run_e2m1_fast<FMT, XT, 8, 1, 1>(w, x, y, s);
-        case 16: return run_e2m1_fast<FMT, XT, 16, 1, 2>(w, x, y, s);
-        case 32: return run_e2m1_fast<FMT, XT, 32, 1, 2>(w, x, y, s);
-        case 64: return run_e2m1_fast<FMT, XT, 64, 1, 4>(w, x, y, s);
-        case 128: return run_e2m1_fast<FMT, XT, 64, 2, 4>(w, x, y, s);
-        case 256: return run_e2m1_fast<FMT, XT, 64, 4, 2>(w, x, y, s);
+        case 1: return run_e2m1_loop<FMT, XT, 1, 1, 4, 8>(w, x, y, s);
+        case 2: return run_e2m1_loop<FMT, XT, 2, 1, 4, 8>(w, x, y, s);
+        case 4: return run_e2m1_loop<FMT, XT, 4, 1, 4, 8>(w, x, y, s);
+        case 8: return run_e2m1_loop<FMT, XT, 8, 1, 4, 8>(w, x, y, s);
+        case 16: return run_e2m1_loop<FMT, XT, 16, 1, 4, 8>(w, x, y, s);
+        case 32: return run_e2m1_loop<FMT, XT, 32, 1, 4, 8>(w, x, y, s);
+        case 64: return run_e2m1_loop<FMT, XT, 64, 1, 4, 8>(w, x, y, s);
+        case 128: return run_e2m1_loop<FMT, XT, 64, 2, 4, 8>(w, x, y, s);
+        case 256: return run_e2m1_loop<FMT, XT, 64, 4, 4, 4>(w, x, y, s);
         default: break;
         }
     }
@@ -481,11 +566,11 @@ hipError_t run_e2m1(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename XT, int BPL, int SUB, int RPW>
-hipError_t run_q4k_fast(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
-    const int64_t rows_per_block = (int64_t)kWavesPerBlock * RPW * SUB;
-    const int64_t grid = (w.n + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((k_gemv_q4k_fast<XT, BPL, SUB, RPW>), dim3((unsigned)grid), dim3(kBlock), 0, s,
+template <typename XT, int BPL, int SUB, int WPB, int PER_CU>
+hipError_t run_q4k_loop(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+    const int64_t passes = (w.n + SUB - 1) / SUB;
+    const int64_t grid = loop_grid(passes, WPB, PER_CU);
+    hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB>), dim3((unsigned)grid), dim3(WPB * kWave), 0, s,
                        (const uint8_t *)w.data, x, y, w.n, w.k);
     return hipGetLastError();
 }
@@ -493,12 +578,12 @@ hipError_t run_q4k_fast(const qbn_tensor &w, const XT *x, float *y, hipStream_t 
 template <typename XT>
 hipError_t run_q4k(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     switch (w.k / 256) {
-    case 1: return run_q4k_fast<XT, 1, 8, 1>(w, x, y, s);
-    case 2: return run_q4k_fast<XT, 1, 4, 1>(w, x, y, s);
-    case 4: return run_q4k_fast<XT, 1, 2, 2>(w, x, y, s);
-    case 8: return run_q4k_fast<XT, 1, 1, 4>(w, x, y, s);
-    case 16: return run_q4k_fast<XT, 2, 1, 2>(w, x, y, s);
-    case 32: return run_q4k_fast<XT, 4, 1, 1>(w, x, y, s);
+    case 1: return run_q4k_loop<XT, 1, 8, 4, 8>(w, x, y, s);
+    case 2: return run_q4k_loop<XT, 1, 4, 4, 8>(w, x, y, s);
+    case 4: return run_q4k_loop<XT, 1, 2, 4, 8>(w, x, y, s);
+    case 8: return run_q4k_loop<XT, 1, 1, 4, 8>(w, x, y, s);
+    case 16: return run_q4k_loop<XT, 2, 1, 4, 4>(w, x, y, s);
+    case 32: return run_q4k_loop<XT, 4, 1, 4, 2>(w, x, y, s);
     default: break;
     }
     const int64_t grid = (w.n + kWavesPerBlock - 1) / kWavesPerBlock;

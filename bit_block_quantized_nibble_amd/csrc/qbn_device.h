@@ -86,6 +86,29 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
 __device__ __forceinline__ uint32_t ld4(const void *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
+// ---------------------------------------------------------------- DPP reductions
+// Cross-lane sums with data-parallel-primitive moves (no LDS traffic). The
+// disabled-row / out-of-range case reads the `old` operand, which is 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over groups of W consecutive lanes (W a power of two, 1..64). The
+// group's sum is valid in its LAST lane (lane % W == W - 1); for W <= 16 every
+// lane of the group holds it. Fixed order, hence deterministic.
+template <int W>
+__device__ __forceinline__ float group_sum_last(float v) {
+    if (W >= 2) v += dpp_f32<0xB1>(v);          // quad_perm [1,0,3,2]
+    if (W >= 4) v += dpp_f32<0x4E>(v);          // quad_perm [2,3,0,1]
+    if (W >= 8) v += dpp_f32<0x141>(v);         // row_half_mirror
+    if (W >= 16) v += dpp_f32<0x140>(v);        // row_mirror
+    if (W >= 32) v += dpp_f32<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    if (W >= 64) v += dpp_f32<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 // ---------------------------------------------------------------- reductions
 // Sum over groups of W consecutive lanes (W a power of two <= 64); every lane
 // of a group ends with the group's sum. Fixed butterfly order: deterministic.

@@ -1,0 +1,137 @@
+"""GPU parity: qbn_repack moves int4 codes between GPTQ, AWQ and Q4_0
+bit-exactly (compared with the oracle's pack(unpack(...)) through the
+logical matrix), on ragged tiles, on the verification probes and on the full
+4096 x 11008 workload, including the GPTQ -> AWQ -> Q4_0 -> AWQ -> GPTQ round
+trip."""
+import numpy as np
+import pytest
+import torch
+
+import bit_block_quantized_nibble_amd as qbn
+import oracle
+import workloads
+from gpu_util import DEV, dev, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _q4_0_d_from_scales(scales_u16, K, group):
+    """Q4_0 d bits [N][K/32] = bit copy of the group scale of each block."""
+    return np.ascontiguousarray(np.repeat(scales_u16.T, group // 32, axis=1))
+
+
+def _mk(fmt, q, scales, zeros, group):
+    K, N = q.shape
+    if fmt == "gptq4":
+        return qbn.QTensor("gptq4", N, K, dev(oracle.gptq_pack(q)), dev(scales), dev(zeros), group=group)
+    if fmt == "awq4":
+        return qbn.QTensor("awq4", N, K, dev(oracle.awq_pack(q)), dev(scales), dev(zeros), group=group)
+    d = _q4_0_d_from_scales(scales, K, group)
+    return qbn.QTensor("q4_0", N, K, dev(oracle.q4_0_pack(q, d)))
+
+
+def _expect(fmt, q, scales, group):
+    K, N = q.shape
+    if fmt == "gptq4":
+        return oracle.gptq_pack(q)
+    if fmt == "awq4":
+        return oracle.awq_pack(q)
+    return oracle.q4_0_pack(q, _q4_0_d_from_scales(scales, K, group))
+
+
+DIRS = [("gptq4", "awq4"), ("awq4", "gptq4"), ("gptq4", "q4_0"), ("awq4", "q4_0"), ("q4_0", "gptq4"),
+        ("q4_0", "awq4")]
+
+
+@pytest.mark.parametrize("src,dst", DIRS)
+@pytest.mark.parametrize("K,N,g", [(256, 64, 128), (512, 200, 128), (96, 8, 32), (1024, 136, 256), (4096, 72, 128)])
+def test_repack_random(src, dst, K, N, g):
+    if "awq4" in (src, dst) and N % 8:
+        pytest.skip("AWQ needs N % 8 == 0")
+    rng = np.random.default_rng(K * 7 + N + g)
+    q = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    scales = rng.uniform(-0.01, 0.01, (K // g, N)).astype(np.float16).view(np.uint16)
+    zeros = rng.integers(0, 16, (K // g, N)).astype(np.uint8)
+    if src == "q4_0":
+        zeros[:] = 8  # what Q4_0 implies; the scales round-trip as block d values
+    w = _mk(src, q, scales, zeros, g)
+    say("repack", src, "->", dst, K, N, g)
+    out = qbn.repack(w, dst, dst_group=g if dst != "q4_0" else None)
+    torch.cuda.synchronize()
+    want = _expect(dst, q, scales, g)
+    got = host_bits(out.data)
+    assert np.array_equal(got.reshape(want.shape).view(np.uint8), want.view(np.uint8))
+    if dst != "q4_0":
+        assert np.array_equal(host_bits(out.scales).view(np.uint16).reshape(scales.shape), scales)
+        assert np.array_equal(host_bits(out.zeros).reshape(zeros.shape), zeros)
+
+
+def test_repack_probes_all_directions():
+    K, N, g = 256, 256, 128
+    pat = ((np.arange(K)[:, None] * 7 + np.arange(N)[None, :] * 3) % 16).astype(np.uint8)
+    rng = np.random.default_rng(0)
+    rand = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    full = np.full((K, N), 15, np.uint8)
+    scales = np.full((K // g, N), 0x3C00, np.uint16)
+    zeros = np.full((K // g, N), 8, np.uint8)
+    for name, probe in (("patterned", pat), ("random", rand), ("all-15", full)):
+        for src, dst in DIRS:
+            say("repack probe", name, src, dst)
+            out = qbn.repack(_mk(src, probe, scales, zeros, g), dst, dst_group=g if dst != "q4_0" else None)
+            torch.cuda.synchronize()
+            want = _expect(dst, probe, scales, g)
+            assert np.array_equal(host_bits(out.data).reshape(want.shape).view(np.uint8), want.view(np.uint8)), \
+                (name, src, dst)
+
+
+def test_workload5_round_trip_and_dequant_identity():
+    inp = workloads.workload(5)
+    K, N, g = inp["K"], inp["N"], inp["group"]
+    scales = inp["scales"].view(np.uint16)
+    zeros = inp["zeros"]
+    qw = inp["qweight"]
+    gptq = qbn.QTensor("gptq4", N, K, dev(qw), dev(scales), dev(zeros), group=g)
+    say("workload 5: gptq -> awq")
+    awq = qbn.repack(gptq, "awq4")
+    say("workload 5: awq -> q4_0")
+    q40 = qbn.repack(awq, "q4_0")
+    say("workload 5: q4_0 -> awq")
+    awq2 = qbn.repack(q40, "awq4", dst_group=g)
+    say("workload 5: awq -> gptq")
+    gptq2 = qbn.repack(awq2, "gptq4")
+    torch.cuda.synchronize()
+    q = oracle.gptq_unpack(qw)
+    assert np.array_equal(host_bits(awq.data).view(np.uint32), oracle.awq_pack(q))
+    assert np.array_equal(host_bits(q40.data).reshape(N, K // 32, 18),
+                          oracle.q4_0_pack(q, _q4_0_d_from_scales(scales, K, g)))
+    # codes and scales round-trip bit for bit; Q4_0 carries no zero points, so
+    # they come back as 8
+    assert np.array_equal(host_bits(gptq2.data).view(np.uint32), qw)
+    assert np.array_equal(host_bits(gptq2.scales).view(np.uint16).reshape(scales.shape), scales)
+    assert (host_bits(gptq2.zeros) == 8).all()
+    # dequantized values: GPTQ and AWQ agree everywhere, Q4_0 agrees with them
+    # exactly where the group's zero point is 8
+    say("workload 5: dequant identities")
+    wg = host_bits(qbn.dequantize(gptq, dtype=torch.float32, layout="kn"))
+    wa = host_bits(qbn.dequantize(awq, dtype=torch.float32, layout="kn"))
+    w0 = host_bits(qbn.dequantize(q40, dtype=torch.float32, layout="kn"))
+    torch.cuda.synchronize()
+    assert np.array_equal(wg, wa)
+    z8 = np.repeat(zeros, g, axis=0) == 8
+    assert z8.any()
+    assert np.array_equal(w0.reshape(K, N)[z8], wg.reshape(K, N)[z8])
+
+
+def test_repack_validate_q4_0_group_scales():
+    # Q4_0 -> GPTQ takes each group's scale from its first block; the
+    # validator flags a group whose blocks disagree
+    K, N, g = 256, 16, 128
+    rng = np.random.default_rng(5)
+    q = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    scales = rng.uniform(0.001, 0.01, (K // g, N)).astype(np.float16).view(np.uint16)
+    blocks = oracle.q4_0_pack(q, _q4_0_d_from_scales(scales, K, g))
+    w = qbn.QTensor("q4_0", N, K, dev(blocks), group=g)
+    assert qbn.validate(w) == -1
+    blocks[3, 5, 0] ^= 0x10
+    w = qbn.QTensor("q4_0", N, K, dev(blocks), group=g)
+    assert qbn.validate(w) == 3 * (K // 32) + 5
