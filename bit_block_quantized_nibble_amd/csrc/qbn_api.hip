@@ -158,12 +158,12 @@ int32_t qbn_quantized_gemm(const qbn_tensor *w, int64_t m, const void *x, int32_
     if (x_dtype != QBN_BF16 || y_dtype != QBN_BF16) return QBN_ERR_DTYPE;
     if (m < 0 || m > kMaxElems) return QBN_ERR_SHAPE;
     if (m == 0 || w->n == 0) return QBN_OK;
-    if (ldy < w->n || ldy % 8) return ldy < w->n ? QBN_ERR_SHAPE : QBN_ERR_ALIGN;
+    if (ldy < w->n) return QBN_ERR_SHAPE;
     if (ldy > kMaxElems / m) return QBN_ERR_SHAPE;
     if (!y) return QBN_ERR_NULL;
-    if (!aligned(y, 16)) return QBN_ERR_ALIGN;
+    if (!aligned(y, 2)) return QBN_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    if (w->k == 0) return hip_status(qbn::launch_fill_zero(y, 2 * ldy * m, s));
+    if (w->k == 0) return hip_status(qbn::launch_fill_zero_2d_u16(y, m, w->n, ldy, s));
     if (ldx < w->k || ldx % 8) return ldx < w->k ? QBN_ERR_SHAPE : QBN_ERR_ALIGN;
     if (ldx > kMaxElems / m) return QBN_ERR_SHAPE;
     if (!x) return QBN_ERR_NULL;

@@ -17,5 +17,6 @@ hipError_t launch_repack(const qbn_tensor &src, int dst_format, int dst_group, v
                          void *dst_zeros, hipStream_t s);
 hipError_t launch_validate(const qbn_tensor &w, int64_t *first_bad, hipStream_t s);
 hipError_t launch_fill_zero(void *out, int64_t bytes, hipStream_t s);
+hipError_t launch_fill_zero_2d_u16(void *out, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
 
 }  // namespace qbn

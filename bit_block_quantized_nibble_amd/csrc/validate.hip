@@ -91,7 +91,25 @@ __global__ void k_fill_zero_bytes(uint8_t *p, int64_t bytes) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < bytes; i += stride) p[i] = 0u;
 }
 
+// Zero the logical [rows][cols] region of a 2-byte matrix with leading
+// dimension ld (padding columns are left untouched).
+__global__ void k_fill_zero_2d_u16(uint16_t *p, int64_t rows, int64_t cols, int64_t ld) {
+    const int64_t total = rows * cols;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / cols;
+        p[r * ld + (i - r * cols)] = 0;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_fill_zero_2d_u16(void *out, int64_t rows, int64_t cols, int64_t ld, hipStream_t s) {
+    if (rows <= 0 || cols <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_zero_2d_u16, dim3((unsigned)scan_grid(rows * cols)), dim3(kBlock), 0, s,
+                       (uint16_t *)out, rows, cols, ld);
+    return hipGetLastError();
+}
 
 hipError_t launch_validate(const qbn_tensor &w, int64_t *first_bad, hipStream_t s) {
     unsigned long long *f = reinterpret_cast<unsigned long long *>(first_bad);

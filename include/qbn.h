@@ -57,7 +57,7 @@
  *
  * Alignment: MXFP4 / NVFP4 / Q4_K data 16-byte aligned; Q4_0 data 2-byte;
  * GPTQ4 / AWQ4 data 4-byte; fp16 scales 2-byte; GEMV x 16-byte and y 4-byte;
- * GEMM X / Y and dequantize outputs 16-byte. Scale bytes of MXFP4 / NVFP4
+ * GEMM X 16-byte and Y 2-byte; dequantize outputs 16-byte. Scale bytes of MXFP4 / NVFP4
  * and zero points have no alignment requirement. A violation returns
  * QBN_ERR_ALIGN.
  */
@@ -154,8 +154,8 @@ QBN_API int32_t qbn_quantized_gemv(const qbn_tensor *w, const void *x, int32_t x
 
 /* Y[i][r] = sum_j X[i][j] * W_hat[r][j] for i in 0..m, r in 0..n  (prefill
  * GEMM with packed weights, [WK] sections 7 and 7d).
- * Formats: MXFP4. X: QBN_BF16 [m][ldx] row-major, ldx >= k, ldx % 8 == 0;
- * Y: QBN_BF16 [m][ldy], ldy >= n, ldy % 8 == 0. W_hat is expanded to bf16
+ * Formats: MXFP4. X: QBN_BF16 [m][ldx] row-major, ldx >= k, ldx % 8 == 0,
+ * X 16-byte aligned; Y: QBN_BF16 [m][ldy], ldy >= n, Y 2-byte aligned. W_hat is expanded to bf16
  * exactly (E2M1 x 2^e is exact in bf16), products run on bf16 matrix cores
  * with binary32 accumulation, and Y is rounded to bf16 (nearest even). */
 QBN_API int32_t qbn_quantized_gemm(const qbn_tensor *w, int64_t m, const void *x, int32_t x_dtype, int64_t ldx, void *y,

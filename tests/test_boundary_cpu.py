@@ -107,7 +107,7 @@ def test_gemm_rejections(lib):
     assert g(T(MX, 8, 64), 4, A, BF16, 32, B, BF16, 8, None) == SHAPE
     assert g(T(MX, 8, 64), 4, A, BF16, 68, B, BF16, 8, None) == ALIGN
     assert g(T(MX, 8, 64), 4, A, BF16, 64, B, BF16, 4, None) == SHAPE
-    assert g(T(MX, 8, 64), 4, A, BF16, 64, B, BF16, 12, None) == ALIGN
+    assert g(T(MX, 8, 64), 4, A, BF16, 64, B + 1, BF16, 12, None) == ALIGN
     assert g(T(MX, 8, 64), 4, A + 8, BF16, 64, B, BF16, 8, None) == ALIGN
     assert g(T(MX, 8, 64), 0, None, BF16, 64, None, BF16, 8, None) == OK
 

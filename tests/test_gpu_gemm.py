@@ -1,0 +1,111 @@
+"""GPU parity: qbn_quantized_gemm (MXFP4 weights, bf16 activations and
+output) against the oracle's binary64 entries. A bf16 output y passes when
+RNE_bf16(y_ref - T) <= y <= RNE_bf16(y_ref + T), T = 1e-5 * sum|w x| + 1e-6:
+rounding to nearest is monotone, so any binary32 result within T of the exact
+value rounds into this band. Inputs whose partial sums are all exact must
+match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import bit_block_quantized_nibble_amd as qbn
+import oracle
+import workloads
+from gpu_util import DEV, dev, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_value(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _band(y_ref, s_ref):
+    T = 1e-5 * s_ref + 1e-6
+    lo = oracle.bf16_rne_array((y_ref - T).astype(np.float32))
+    hi = oracle.bf16_rne_array((y_ref + T).astype(np.float32))
+    return _bf16_value(lo), _bf16_value(hi)
+
+
+def _run(inp, what):
+    n, k, m = inp["n"], inp["k"], inp["m"]
+    w = qbn.QTensor("mxfp4", n, k, dev(inp["data"]), dev(inp["scales"]))
+    X = dev(inp["X"]).view(torch.bfloat16)
+    say("gemm", what, m, n, k)
+    Y = qbn.quantized_gemm(w, X)
+    torch.cuda.synchronize()
+    return host_bits(Y).reshape(m, n)
+
+
+def _check_entries(inp, Ybits, ms, ns, what):
+    y_ref, s_ref = oracle.gemm_entries(oracle.MXFP4, inp["data"], inp["scales"], 1.0, inp["k"], inp["X"], ms, ns)
+    got = _bf16_value(Ybits[ms, ns])
+    lo, hi = _band(y_ref, s_ref)
+    bad = ~((lo <= got) & (got <= hi))
+    if bad.any():
+        i = int(np.argwhere(bad)[0][0])
+        raise AssertionError("%s: %d of %d entries outside the band; first (m=%d, n=%d): got %r, ref %r, band [%r, %r]"
+                             % (what, int(bad.sum()), bad.size, ms[i], ns[i], got[i], y_ref[i], lo[i], hi[i]))
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 128, 64), (37, 200, 512), (1, 64, 32), (130, 70, 96), (256, 384, 4096),
+                                   (64, 130, 1056)])
+def test_gemm_all_entries(m, n, k):
+    inp = workloads.workload(4, n=n, k=k, m=m, seed=m * 1000 + n + k)
+    Y = _run(inp, "all entries")
+    ms, ns = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+    _check_entries(inp, Y, ms.ravel(), ns.ravel(), "gemm %dx%dx%d" % (m, n, k))
+
+
+def test_gemm_dyadic_exact():
+    rng = np.random.default_rng(21)
+    m, n, k = 96, 160, 512
+    codes = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scales = (127 + rng.integers(-4, 3, (n, k // 32))).astype(np.uint8)
+    X = workloads.bf16_bits_from_f32(rng.integers(-8, 9, (m, k)).astype(np.float32))
+    inp = dict(n=n, k=k, m=m, data=codes, scales=scales, X=X)
+    Y = _run(inp, "dyadic")
+    ms, ns = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+    y_ref, _ = oracle.gemm_entries(oracle.MXFP4, codes, scales, 1.0, k, X, ms.ravel(), ns.ravel())
+    want = oracle.bf16_rne_array(y_ref.astype(np.float32))
+    assert np.array_equal(Y.ravel(), want)
+
+
+def test_gemm_workload_full_size_sampled():
+    inp = workloads.workload(4)
+    m, n = inp["m"], inp["n"]
+    Y = _run(inp, "full workload 4")
+    rng = np.random.default_rng(99)
+    ms = np.concatenate([rng.integers(0, m, 1500), np.full(64, m - 1), np.arange(64)])
+    ns = np.concatenate([rng.integers(0, n, 1500), np.arange(n - 64, n), np.full(64, 0)])
+    _check_entries(inp, Y, ms, ns, "workload 4 sampled")
+
+
+def test_gemm_deterministic_and_strided():
+    inp = workloads.workload(4, n=192, k=1024, m=80, seed=5)
+    w = qbn.QTensor("mxfp4", 192, 1024, dev(inp["data"]), dev(inp["scales"]))
+    X = dev(inp["X"]).view(torch.bfloat16)
+    a = qbn.quantized_gemm(w, X)
+    b = qbn.quantized_gemm(w, X)
+    # the same product through padded leading dimensions
+    Xp = torch.zeros((80, 1024 + 64), dtype=torch.bfloat16, device=DEV)
+    Xp[:, :1024] = X
+    Yp = torch.zeros((80, 192 + 8), dtype=torch.bfloat16, device=DEV)
+    say("gemm strided")
+    qbn.quantized_gemm(w, Xp[:, :1024], Yp[:, :192])
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(a), host_bits(b))
+    assert np.array_equal(host_bits(Yp[:, :192].contiguous()), host_bits(a))
+    assert (host_bits(Yp[:, 192:].contiguous()) == 0).all()
+
+
+def test_gemm_zero_k_fills_only_the_logical_output():
+    w = qbn.QTensor("mxfp4", 24, 0, torch.empty(24, 0, dtype=torch.uint8, device=DEV),
+                    torch.empty(24, 0, dtype=torch.uint8, device=DEV))
+    Yp = torch.full((5, 32), 3.0, dtype=torch.bfloat16, device=DEV)
+    X = torch.empty((5, 8), dtype=torch.bfloat16, device=DEV)
+    say("gemm k = 0")
+    qbn.quantized_gemm(w, X[:, :0], Yp[:, :24])
+    torch.cuda.synchronize()
+    assert (Yp[:, :24].float().cpu() == 0).all()
+    assert (Yp[:, 24:].float().cpu() == 3).all()
