@@ -49,6 +49,7 @@ def _check_entries(inp, Ybits, ms, ns, what):
 
 
 @pytest.mark.parametrize("m,n,k", [(128, 128, 64), (37, 200, 512), (1, 64, 32), (130, 70, 96), (256, 384, 4096),
+                                   (300, 520, 1056), (512, 256, 2048),
                                    (64, 130, 1056)])
 def test_gemm_all_entries(m, n, k):
     inp = workloads.workload(4, n=n, k=k, m=m, seed=m * 1000 + n + k)
