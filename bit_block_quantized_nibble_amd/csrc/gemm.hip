@@ -178,8 +178,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
 // Asynchronous 16-byte global -> LDS copy: lane i of the wave writes its 16
-// bytes at lds_base + 16 * i (lds_base must be the same for the whole wave).
-// It counts in vmcnt like any vector load.
+// bytes at lds_base + 16 * i (lds_base is the same for the whole wave). It
+// counts in vmcnt like any vector load.
 __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
     __builtin_amdgcn_global_load_lds((glb_void *)g, (lds_void *)lds_base, 16, 0, 0);
 }
@@ -190,168 +190,192 @@ __device__ __forceinline__ void dma2(const void *g, void *lds_base) {
     __builtin_amdgcn_global_load_lds((glb_void *)g, (lds_void *)lds_base, 2, 0, 0);
 }
 
-// Wait until at most n of this wave's vector-memory loads are outstanding
-// (n is wave-uniform). Loads complete in issue order.
-__device__ __forceinline__ void wait_vm(int n) {
-    switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0xF70 | 0); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0xF70 | 1); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0xF70 | 2); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0xF70 | 3); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0xF70 | 4); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0xF70 | 5); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0xF70 | 6); break;
-    default: __builtin_amdgcn_s_waitcnt(0xF70 | 7); break;
-    }
-}
-
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, not for its outstanding global loads (which __syncthreads'
 // fence would also drain). The memory clobber keeps the compiler from moving
 // LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// LDS layout of one k-tile (X: 256 rows x 128 bytes; W codes: 256 rows x 32
-// bytes; E8M0: one dword per row whose low 16 bits hold the row's two scale
-// bytes, first block in the low byte). X and W swizzle 16-byte chunks by row
-// so that the 32 rows a fragment read touches spread over the LDS banks:
-//   X chunk c of row r  -> row r, slot c ^ (r & 7)
-//   W half  h of row n  -> row n, slot h ^ ((n >> 3) & 1)
+// LDS layout of one k-tile.
+//  X (256 rows x 64 bf16): blocks of 8 rows; inside a block the 16-byte
+//    chunk c (k = 8c .. 8c + 7) of row r sits at c * 128 + (r % 8) * 16, and
+//    blocks are 1152 bytes apart (128 bytes of padding). A fragment read
+//    (32 consecutive rows, one chunk) is then contiguous within each group of
+//    8 lanes, and consecutive groups land 128 bytes apart modulo 256: no
+//    bank conflicts for 8- or 16-lane groups.
+//  W codes (256 rows x 32 bytes): blocks of 32 rows; half h of row n sits at
+//    (n / 32) * 1024 + h * 512 + (n % 32) * 16.
+//  E8M0: one dword per row whose low 16 bits hold the row's two scale bytes
+//    (first block in the low byte).
+// Every fragment address is affine in the MFMA indices, so the reads use one
+// base register and immediate offsets.
+constexpr int A_BLK = 1152;
+constexpr int A_STAGE = BM / 8 * A_BLK;
+constexpr int B_STAGE = BN * 32;
+constexpr int S_STAGE = BN * 4;
+
 struct Smem {
-    uint8_t a[STAGES][BM * 128];
-    uint8_t b[STAGES][BN * 32];
-    uint8_t s[STAGES][BN * 4];
+    uint8_t a[STAGES][A_STAGE];
+    uint8_t b[STAGES][B_STAGE];
+    uint8_t s[STAGES][S_STAGE];
 };
 
-__device__ __forceinline__ int a_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) * 16); }
-__device__ __forceinline__ int b_off(int n, int h) { return n * 32 + ((h ^ ((n >> 3) & 1)) * 16); }
+__device__ __forceinline__ int a_off(int r, int c) { return (r / 8) * A_BLK + c * 128 + (r % 8) * 16; }
+__device__ __forceinline__ int b_off(int n, int h) { return (n / 32) * 1024 + h * 512 + (n % 32) * 16; }
 
-template <int THREADS>
-struct Loader {
-    static constexpr int WAVES = THREADS / 64;
-    static constexpr int NA = BM * 8 / THREADS;  // X chunks per thread (register path)
-    static constexpr int NXW = BM / 8 / WAVES;   // X wave-copies per wave (direct path)
-    static_assert(BM * 8 % THREADS == 0 && NA >= 1 && (BM / 8) % WAVES == 0, "X tile split");
+// Copies of one k-tile for WAVES waves. Interior tiles (every row, column
+// and k of the tile exists, scales 2-byte aligned) are copied straight into
+// LDS; every wave issues the same number of copies, COPIES, per tile:
+//   X: 32 copies of 8 rows (1 KB), NXW per wave;
+//   W codes: 8 copies of 32 rows (1 KB);
+//   scale pairs: 8 half-wave copies of 32 rows.
+// With 16 waves, waves 0-7 take one W copy and waves 8-15 one scale copy;
+// with 8 waves every wave takes one of each.
+template <int WAVES>
+struct Copier {
+    static_assert(WAVES == 8 || WAVES == 16, "8 or 16 waves");
+    static constexpr int NXW = (BM / 8) / WAVES;
+    static constexpr int COPIES = NXW + (WAVES == 16 ? 1 : 2);
 
-    // Direct copies this wave issues per k-tile: X, then W codes (copies
-    // q < BN/32 go to wave q % WAVES), then scale pairs (copies q < BN/64 go
-    // to wave (BN/32 + q) % WAVES).
-    __device__ __forceinline__ static int direct_count(int wave) {
-        int c = NXW;
-        for (int q = 0; q < BN / 32; ++q) c += (q % WAVES == wave);
-        for (int q = 0; q < BN / 64; ++q) c += ((BN / 32 + q) % WAVES == wave);
-        return c;
-    }
+    const uint16_t *xg[NXW];  // per lane: X element of the lane's chunk at k = 0
+    const uint8_t *wg;        // per lane: code byte of the lane's half at k = 0
+    const uint8_t *sg;        // per lane: scale byte of the lane's row at k = 0
+    int xo[NXW];              // LDS offsets (wave-uniform) inside a stage
+    int wo, so;
+    bool has_w, has_s;
 
-    // Interior tiles (every row, column and k of the tile exists, scales
-    // 2-byte aligned): X, W codes and scale pairs go straight from global
-    // memory into LDS, no registers involved.
-    __device__ __forceinline__ static void direct(Smem &sm, int buf, const uint16_t *__restrict__ X, int64_t ldx,
-                                                  const uint8_t *__restrict__ codes,
-                                                  const uint8_t *__restrict__ scales, int64_t K, int64_t m0,
-                                                  int64_t n0, int64_t k0, int lane, int wave) {
-        // X: 32 KB = BM/8 wave-copies of 1 KB (8 rows of 128 bytes each)
+    __device__ __forceinline__ Copier(const uint16_t *X, int64_t ldx, const uint8_t *codes, const uint8_t *scales,
+                                      int64_t K, int64_t m0, int64_t n0, int lane, int wave) {
 #pragma unroll
         for (int q = 0; q < NXW; ++q) {
             const int blk = wave * NXW + q;
-            const int r = blk * 8 + lane / 8;
-            const int c = (lane % 8) ^ (r & 7);
-            dma16(X + (m0 + r) * ldx + k0 + 8 * c, &sm.a[buf][blk * 1024]);
+            const int r = blk * 8 + lane % 8, c = lane / 8;
+            xg[q] = X + (m0 + r) * ldx + 8 * c;
+            xo[q] = blk * A_BLK;
         }
-        // W codes: 8 KB = BN/32 wave-copies of 1 KB (32 rows of 32 bytes each)
-#pragma unroll
-        for (int q = 0; q < BN / 32; ++q) {
-            if (q % WAVES != wave) continue;
-            const int n = q * 32 + lane / 2;
-            const int h = (lane % 2) ^ ((n >> 3) & 1);
-            dma16(codes + (n0 + n) * (K / 2) + k0 / 2 + 16 * h, &sm.b[buf][q * 1024]);
-        }
-        // scale pairs: BN/64 wave-copies of 64 rows; lane l's 2 bytes land
-        // zero-extended in dword l
-#pragma unroll
-        for (int q = 0; q < BN / 64; ++q) {
-            if ((BN / 32 + q) % WAVES != wave) continue;
-            const int n = q * 64 + lane;
-            dma2(scales + (n0 + n) * (K / 32) + k0 / 32, &sm.s[buf][q * 256]);
-        }
+        const int qw = (WAVES == 16) ? wave : wave;          // W copy of this wave (if any)
+        const int qs = (WAVES == 16) ? wave - 8 : wave;      // scale copy of this wave (if any)
+        has_w = (WAVES == 16) ? (wave < 8) : true;
+        has_s = (WAVES == 16) ? (wave >= 8) : true;
+        const int nw = 32 * (has_w ? qw : 0) + lane % 32, hw = lane / 32;
+        wg = codes + (n0 + nw) * (K / 2) + 16 * hw;
+        wo = (has_w ? qw : 0) * 1024;
+        const int ns = 32 * (has_s ? qs : 0) + lane % 32;
+        sg = scales + (n0 + ns) * (K / 32);
+        so = (has_s ? qs : 0) * 128;
     }
 
-    // Edge tiles: through registers, zero-filling what lies outside.
-    __device__ __forceinline__ static void staged(Smem &sm, int buf, const uint16_t *__restrict__ X, int64_t ldx,
-                                                  const uint8_t *__restrict__ codes, int64_t M, int64_t N,
-                                                  int64_t K, int64_t m0, int64_t n0, int64_t k0) {
-        const int t = threadIdx.x;
+    __device__ __forceinline__ void issue(Smem &sm, int buf, int64_t k0, int lane) const {
 #pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int r = t / 8 + (THREADS / 8) * i;
-            const int c = t % 8;
-            const int64_t m = m0 + r, k = k0 + 8 * c;
-            const u32x4 v = (m < M && k < K) ? ld16(X + m * ldx + k) : u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4 *>(&sm.a[buf][a_off(r, c)]) = v;
-        }
-        for (int i = t; i < BN * 2; i += THREADS) {
-            const int n = i / 2, h = i % 2;
-            const int64_t nn = n0 + n, k = k0 + 32 * h;
-            const u32x4 v = (nn < N && k < K) ? ld16(codes + nn * (K / 2) + k / 2) : u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4 *>(&sm.b[buf][b_off(n, h)]) = v;
-        }
-    }
-
-    // Edge tiles: the two E8M0 bytes of row t (t < BN) of the k-tile at k0;
-    // missing rows or blocks read as 127 (scale 1, multiplying zero codes).
-    __device__ __forceinline__ static void scales_edge(Smem &sm, int buf, const uint8_t *__restrict__ scales,
-                                                       int64_t N, int64_t K, int64_t n0, int64_t k0) {
-        const int t = threadIdx.x;
-        if (t >= BN) return;
-        uint32_t b0 = 127u, b1 = 127u;
-        if (n0 + t < N) {
-            const uint8_t *sp = scales + (n0 + t) * (K / 32) + k0 / 32;
-            if (k0 < K) b0 = sp[0];
-            if (k0 + 32 < K) b1 = sp[1];
-        }
-        *reinterpret_cast<uint32_t *>(&sm.s[buf][4 * t]) = b0 | (b1 << 8);
+        for (int q = 0; q < NXW; ++q) dma16(xg[q] + k0, &sm.a[buf][xo[q]]);
+        if (has_w) dma16(wg + k0 / 2, &sm.b[buf][wo]);
+        if (has_s && lane < 32) dma2(sg + k0 / 32, &sm.s[buf][so]);
     }
 };
 
-// One k-tile of MFMA work for a wave owning TM x TN tiles of 32 x 32.
+// Edge tiles: through registers, zero-filling what lies outside; scale
+// bytes of missing rows or blocks read as 127 (scale 1, zero codes).
+template <int THREADS>
+__device__ __forceinline__ void stage_edge(Smem &sm, int buf, const uint16_t *__restrict__ X, int64_t ldx,
+                                           const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                           int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0, int64_t k0) {
+    const int t = threadIdx.x;
+    for (int i = t; i < BM * 8; i += THREADS) {
+        const int r = i / 8, c = i % 8;
+        const int64_t m = m0 + r, k = k0 + 8 * c;
+        const u32x4 v = (m < M && k < K) ? ld16(X + m * ldx + k) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(&sm.a[buf][a_off(r, c)]) = v;
+    }
+    for (int i = t; i < BN * 2; i += THREADS) {
+        const int n = i / 2, h = i % 2;
+        const int64_t nn = n0 + n, k = k0 + 32 * h;
+        const u32x4 v = (nn < N && k < K) ? ld16(codes + nn * (K / 2) + k / 2) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(&sm.b[buf][b_off(n, h)]) = v;
+    }
+    for (int n = t; n < BN; n += THREADS) {
+        uint32_t b0 = 127u, b1 = 127u;
+        if (n0 + n < N) {
+            const uint8_t *sp = scales + (n0 + n) * (K / 32) + k0 / 32;
+            if (k0 < K) b0 = sp[0];
+            if (k0 + 32 < K) b1 = sp[1];
+        }
+        *reinterpret_cast<uint32_t *>(&sm.s[buf][4 * n]) = b0 | (b1 << 8);
+    }
+}
+
+// MFMA work of one wave owning TM x TN tiles of 32 x 32.
+// The 64 k of a tile are dealt to the MFMA steps in a permuted order that
+// both operands share (the sum over k does not depend on it): at step ks the
+// lanes of half lh (k slots 8 lh .. 8 lh + 7 of the instruction) take k
+// = 8 (4 lh + ks) .. + 7. A lane's codes for the whole tile are then one
+// 16-byte chunk (half lh of its W row) under one scale (block lh).
 template <int TM, int TN>
-__device__ __forceinline__ void mma_ktile(const Smem &sm, int buf, int wm, int wn, int lr, int lh,
-                                          f32x16 (&acc)[TM][TN]) {
-    // this k-tile's scales of the lane's TN B rows, as 2^e
-    float sc[TN][2];
+struct Frags {
+    bf16x8 a[TM];  // X fragments of the next step
+    u32x4 bw[TN];     // the tile's codes
+    uint32_t sb[TN];  // the tile's scale pairs (converted at first use)
+};
+
+template <int TM, int TN>
+__device__ __forceinline__ void read_a(const uint8_t *a_lane, int ks, bf16x8 (&a)[TM]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(a_lane + 4 * A_BLK * i + 128 * ks);
+}
+
+// Codes, scales and step-0 X fragments of a tile.
+template <int TM, int TN>
+__device__ __forceinline__ void read_head(const uint8_t *a_lane, const uint8_t *b_lane, const uint8_t *s_lane,
+                                          Frags<TM, TN> &f) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        const int n = wn * (32 * TN) + 32 * j + lr;
-        const uint32_t b2 = *reinterpret_cast<const uint32_t *>(&sm.s[buf][4 * n]);
-        sc[j][0] = __builtin_amdgcn_ldexpf(1.0f, e8m0_exponent(b2 & 0xFFu));
-        sc[j][1] = __builtin_amdgcn_ldexpf(1.0f, e8m0_exponent((b2 >> 8) & 0xFFu));
+        f.sb[j] = *reinterpret_cast<const uint32_t *>(s_lane + 128 * j);
+        f.bw[j] = *reinterpret_cast<const u32x4 *>(b_lane + 1024 * j);
+    }
+    read_a<TM, TN>(a_lane, 0, f.a);
+}
+
+template <int TN>
+__device__ __forceinline__ void scales_of(const uint32_t (&sb)[TN], int lh, float (&sc)[TN]) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sc[j] = __builtin_amdgcn_ldexpf(1.0f, e8m0_exponent((sb[j] >> (8 * lh)) & 0xFFu));
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void mma_step(const bf16x8 (&a)[TM], const u32x4 (&bw)[TN], const float (&sc)[TN], int ks,
+                                         f32x16 (&acc)[TM][TN]) {
+    bf16x8 bfr[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const uint32_t w = bw[j][ks];
+        const float scale = sc[j];
+        const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+        const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+        const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+        const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+        bfr[j] = __builtin_bit_cast(bf16x8, u32x4{p0, p1, p2, p3});
     }
 #pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bfr[j], acc[i][j], 0, 0, 0);
+}
+
+// A whole tile from one LDS buffer (edge path).
+template <int TM, int TN>
+__device__ __forceinline__ void mma_ktile(const uint8_t *a_lane, const uint8_t *b_lane, const uint8_t *s_lane,
+                                          int lh, f32x16 (&acc)[TM][TN]) {
+    Frags<TM, TN> f;
+    read_head<TM, TN>(a_lane, b_lane, s_lane, f);
+    float sc[TN];
+    scales_of<TN>(f.sb, lh, sc);
+#pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8 af[TM], bfr[TN];
+        bf16x8 a[TM];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = wm * (32 * TM) + 32 * i + lr;
-            af[i] = *reinterpret_cast<const bf16x8 *>(&sm.a[buf][a_off(r, 2 * ks + lh)]);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = wn * (32 * TN) + 32 * j + lr;
-            // dword (2ks + lh) of row n: half ks / 2, dword (2ks + lh) % 4 within it
-            const uint32_t w =
-                *reinterpret_cast<const uint32_t *>(&sm.b[buf][b_off(n, ks / 2) + 4 * ((2 * ks + lh) % 4)]);
-            const float scale = sc[j][ks / 2];
-            const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-            const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-            const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-            const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
-            bfr[j] = __builtin_bit_cast(bf16x8, u32x4{p0, p1, p2, p3});
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < TM; ++i) a[i] = f.a[i];
+        if (ks + 1 < BK / 16) read_a<TM, TN>(a_lane, ks + 1, f.a);
+        mma_step<TM, TN>(a, f.bw, sc, ks, acc);
     }
 }
 
@@ -366,8 +390,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const uint16_t *__restr
                                                           uint16_t *__restrict__ Y, int64_t ldy, int64_t M,
                                                           int64_t N, int64_t K, int tiles_m, int tiles_n) {
     constexpr int THREADS = WGM * WGN * 64;
+    constexpr int WAVES = WGM * WGN;
     constexpr int TM = BM / WGM / 32, TN = BN / WGN / 32;
-    using L = Loader<THREADS>;
     __shared__ Smem sm;
     // XCD-aware order: consecutive workgroups go to different XCDs (round
     // robin), so give the workgroups of one XCD the same row panel of X.
@@ -395,6 +419,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const uint16_t *__restr
     const int lr = lane % 32, lh = lane / 32;
     const int nk = (int)((K + BK - 1) / BK);
 
+    // per-lane fragment bases inside a stage
+    const int r0 = wm * (32 * TM) + lr;
+    const int a_lane = a_off(r0, 4 * lh);
+    const int n0w = wn * (32 * TN) + lr;
+    const int b_lane = b_off(n0w, lh);
+    const int s_lane = 4 * n0w;
+
     f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -402,31 +433,65 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const uint16_t *__restr
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
     if (interior) {
-        // At the top of iteration kt only this wave's newest copies (those
-        // of tile kt + 1) may still be in flight.
-        const int ndirect = L::direct_count(wave);
-        L::direct(sm, 0, X, ldx, codes, scales, K, m0, n0, 0, lane, wave);
-        if (nk > 1) L::direct(sm, 1, X, ldx, codes, scales, K, m0, n0, BK, lane, wave);
+        // Ring of three buffers; tile t lives in buffer t % 3. The barrier of
+        // tile kt sits before its last MFMA step: by then every wave has read
+        // all of tile kt, so its buffer takes tile kt + 3, and the head of
+        // tile kt + 1 is read while the last step's MFMAs run.
+        using C = Copier<WAVES>;
+        const C cp(X, ldx, codes, scales, K, m0, n0, lane, wave);
+        cp.issue(sm, 0, 0, lane);
+        if (nk > 1) cp.issue(sm, 1, BK, lane);
+        if (nk > 2) cp.issue(sm, 2, 2 * BK, lane);
+        if (nk > 2) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * C::COPIES));
+        else if (nk > 1) __builtin_amdgcn_s_waitcnt(0xF70 | C::COPIES);
+        else __builtin_amdgcn_s_waitcnt(0xF70);
+        lds_barrier();
+        Frags<TM, TN> f;
+        read_head<TM, TN>(&sm.a[0][a_lane], &sm.b[0][b_lane], &sm.s[0][s_lane], f);
+        int rd = 0;
         for (int kt = 0; kt < nk; ++kt) {
-            wait_vm(kt + 1 < nk ? ndirect : 0);
-            lds_barrier();
-            if (kt + 2 < nk)
-                L::direct(sm, (kt + 2) % STAGES, X, ldx, codes, scales, K, m0, n0, (int64_t)(kt + 2) * BK, lane, wave);
-            mma_ktile<TM, TN>(sm, kt % STAGES, wm, wn, lr, lh, acc);
+            const int nx = (rd == STAGES - 1) ? 0 : rd + 1;
+            float sc[TN];
+            scales_of<TN>(f.sb, lh, sc);
+#pragma unroll
+            for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+                bf16x8 a[TM];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) a[i] = f.a[i];
+                read_a<TM, TN>(&sm.a[rd][a_lane], ks + 1, f.a);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_step<TM, TN>(a, f.bw, sc, ks, acc);
+            }
+            // last step of tile kt
+            bf16x8 a[TM];
+            u32x4 bw[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) a[i] = f.a[i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) bw[j] = f.bw[j];
+            if (kt + 1 < nk) {
+                // tile kt + 1 has landed once only tile kt + 2's copies remain
+                if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(0xF70 | C::COPIES);
+                else __builtin_amdgcn_s_waitcnt(0xF70);
+                lds_barrier();
+                if (kt + 3 < nk) cp.issue(sm, rd, (int64_t)(kt + 3) * BK, lane);
+                read_head<TM, TN>(&sm.a[nx][a_lane], &sm.b[nx][b_lane], &sm.s[nx][s_lane], f);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            mma_step<TM, TN>(a, bw, sc, BK / 16 - 1, acc);
+            rd = nx;
         }
     } else {
-        L::staged(sm, 0, X, ldx, codes, M, N, K, m0, n0, 0);
-        L::scales_edge(sm, 0, scales, N, K, n0, 0);
+        stage_edge<THREADS>(sm, 0, X, ldx, codes, scales, M, N, K, m0, n0, 0);
         __syncthreads();
+        int buf = 0;
         for (int kt = 0; kt < nk; ++kt) {
-            const int buf = kt % STAGES;
-            mma_ktile<TM, TN>(sm, buf, wm, wn, lr, lh, acc);
-            if (kt + 1 < nk) {
-                const int64_t k1 = (int64_t)(kt + 1) * BK;
-                L::staged(sm, (kt + 1) % STAGES, X, ldx, codes, M, N, K, m0, n0, k1);
-                L::scales_edge(sm, (kt + 1) % STAGES, scales, N, K, n0, k1);
-            }
+            const int nxt = (buf == STAGES - 1) ? 0 : buf + 1;
+            mma_ktile<TM, TN>(&sm.a[buf][a_lane], &sm.b[buf][b_lane], &sm.s[buf][s_lane], lh, acc);
+            if (kt + 1 < nk)
+                stage_edge<THREADS>(sm, nxt, X, ldx, codes, scales, M, N, K, m0, n0, (int64_t)(kt + 1) * BK);
             __syncthreads();
+            buf = nxt;
         }
     }
 
