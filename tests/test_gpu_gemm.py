@@ -48,8 +48,12 @@ def _check_entries(inp, Ybits, ms, ns, what):
                              % (what, int(bad.sum()), bad.size, ms[i], ns[i], got[i], y_ref[i], lo[i], hi[i]))
 
 
+# Shapes reach every path: the 128 x 128 kernel (m or n below 256), the
+# 256 x 256 kernel's edge tiles (ragged m / n, or k not a multiple of 64),
+# its per-k-tile interior path (k a multiple of 64 but not of 512) and its
+# chunked interior path (k a multiple of 512).
 @pytest.mark.parametrize("m,n,k", [(128, 128, 64), (37, 200, 512), (1, 64, 32), (130, 70, 96), (256, 384, 4096),
-                                   (300, 520, 1056), (512, 256, 2048),
+                                   (300, 520, 1056), (512, 256, 2048), (256, 256, 576), (512, 512, 1536),
                                    (64, 130, 1056)])
 def test_gemm_all_entries(m, n, k):
     inp = workloads.workload(4, n=n, k=k, m=m, seed=m * 1000 + n + k)
@@ -110,3 +114,22 @@ def test_gemm_zero_k_fills_only_the_logical_output():
     torch.cuda.synchronize()
     assert (Yp[:, :24].float().cpu() == 0).all()
     assert (Yp[:, 24:].float().cpu() == 3).all()
+
+
+@pytest.mark.parametrize("offset", [2, 1])
+def test_gemm_unaligned_scales(offset):
+    """Scale bytes at a 2-byte (per-k-tile interior path) or odd (edge path)
+    address must give the same product as aligned ones."""
+    m, n, k = 256, 256, 1024
+    inp = workloads.workload(4, n=n, k=k, m=m, seed=77 + offset)
+    base = dev(inp["data"])
+    sc = torch.zeros(inp["scales"].size + 16, dtype=torch.uint8, device=DEV)
+    sc[offset:offset + inp["scales"].size] = dev(inp["scales"]).reshape(-1)
+    w = qbn.QTensor("mxfp4", n, k, base, sc[offset:offset + inp["scales"].size].view(n, k // 32))
+    X = dev(inp["X"]).view(torch.bfloat16)
+    say("gemm scales offset", offset)
+    Y = host_bits(qbn.quantized_gemm(w, X)).reshape(m, n)
+    Y0 = _run(inp, "aligned scales")
+    assert np.array_equal(Y, Y0)
+    ms, ns = np.meshgrid(np.arange(0, m, 7), np.arange(0, n, 5), indexing="ij")
+    _check_entries(inp, Y, ms.ravel(), ns.ravel(), "unaligned scales")
