@@ -4,12 +4,18 @@
 // registers; W_hat is never written out ("Why 4-Bit Quantization Is King",
 // sections 1, 7 and 7d; "Four Bits, Three Contracts", section 8).
 //
-// Work split (wave64): a wave owns RPW row passes; in each pass its 64 lanes
-// cover SUB = 64/LPR rows with LPR lanes per row. Every lane sees the same k
-// positions for every row it touches, so its slice of x is loaded once into
-// registers and reused for all of the wave's rows. All weight loads of a
-// wave are issued before any activation load or arithmetic, so the HBM
-// requests of the whole grid are in flight as early as possible.
+// Work split (wave64): LPR lanes cover one row, so a wave covers SUB = 64/LPR
+// rows at a time. Every lane sees the same k positions for every row it
+// touches, so its slice of x is loaded once into registers and reused for
+// all of the wave's rows; x (bf16 or fp32) is several times the bytes of a
+// row's codes, so this reuse decides how much L1 traffic the GEMV makes.
+//  - E2M1: a wave owns R row groups and requests all of their codes and
+//    scales before it loads x or computes, so the whole grid's HBM requests
+//    are in flight at once.
+//  - Q4_K (the arithmetic is a larger share of the time): waves loop over row
+//    passes with the next pass prefetched into a second register set, and x
+//    is staged once per workgroup in LDS, from which each wave reads its
+//    slice, so its L1 path carries only the weight stream.
 //
 // Arithmetic: products accumulate in binary32. E2M1 formats factor the
 // block scale out of each 16/32-element group (group sum, then one FMA by
@@ -105,40 +111,16 @@ __device__ __forceinline__ float dot16_generic<__bf16>(const uint8_t *cp, const 
     return acc;
 }
 
-// ------------------------------------------------------------------ E2M1 row-loop kernel
+// ------------------------------------------------------------------ E2M1 fragments
 // FMT: QBN_MXFP4 or QBN_NVFP4. A chunk is 16 code bytes = 32 elements (one
 // MXFP4 group, two NVFP4 groups); C = k/32 chunks per row, C == LPR * CPL.
-// A pass is SUB = 64/LPR rows handled by one wave; lane li of a row covers
-// chunks li + LPR*j (j < CPL), so each 16-byte load instruction of a wave
-// reads 1 KiB of contiguous codes. Waves stride over passes; the next pass's
-// codes and scales are loaded into a second register set while the current
-// pass is computed, so HBM streaming overlaps the decode arithmetic.
+// Lane li of a row covers chunks li + LPR*j (j < CPL), so each 16-byte load
+// instruction of a wave reads 1 KiB of contiguous codes.
 template <int CPL>
 struct E2M1Frag {
     u32x4 q[CPL];
     uint32_t sb[CPL];  // MXFP4: E8M0 byte; NVFP4: two E4M3FN bytes (low = first group)
 };
-
-template <int FMT, int LPR, int CPL>
-__device__ __forceinline__ void e2m1_load(E2M1Frag<CPL> &f, const uint8_t *__restrict__ codes,
-                                          const uint8_t *__restrict__ scales, int64_t row, bool ok, int li,
-                                          int64_t row_bytes, int64_t spr) {
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int64_t ch = li + (int64_t)LPR * j;
-        f.q[j] = ok ? ld16(codes + row * row_bytes + 16 * ch) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int64_t ch = li + (int64_t)LPR * j;
-        if (FMT == QBN_MXFP4) {
-            f.sb[j] = ok ? (uint32_t)scales[row * spr + ch] : 127u;
-        } else {
-            const uint8_t *sp = scales + row * spr + 2 * ch;
-            f.sb[j] = ok ? ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8)) : 0u;
-        }
-    }
-}
 
 template <int FMT, typename XT, int CPL>
 __device__ __forceinline__ float e2m1_compute(const E2M1Frag<CPL> &f, const XChunk<XT> *xc) {
@@ -166,8 +148,12 @@ __device__ __forceinline__ float e2m1_compute(const E2M1Frag<CPL> &f, const XChu
     return acc;
 }
 
-template <int FMT, typename XT, int LPR, int CPL, int WPB>
-__global__ __launch_bounds__(WPB * 64) void k_gemv_e2m1_loop(const uint8_t *__restrict__ codes,
+// ------------------------------------------------------------------ E2M1 multi-row kernel
+// A wave owns R row groups of SUB rows: lane (sub, li) handles rows
+// row0 + r * SUB + sub (r < R), chunks li + LPR * j (j < CPL) of each. All
+// codes and scale bytes are requested first, then x once, then the R dots.
+template <int FMT, typename XT, int LPR, int CPL, int R, int WPB>
+__global__ __launch_bounds__(WPB * 64) void k_gemv_e2m1_rows(const uint8_t *__restrict__ codes,
                                                              const uint8_t *__restrict__ scales, float scale2,
                                                              const XT *__restrict__ x, float *__restrict__ y,
                                                              int64_t n, int64_t k) {
@@ -175,45 +161,43 @@ __global__ __launch_bounds__(WPB * 64) void k_gemv_e2m1_loop(const uint8_t *__re
     const int lane = threadIdx.x & (kWave - 1);
     const int sub = lane / LPR;
     const int li = lane % LPR;
-    const int64_t passes = (n + SUB - 1) / SUB;
-    const int64_t stride = (int64_t)gridDim.x * WPB;
+    const int64_t wave = (int64_t)blockIdx.x * WPB + threadIdx.x / kWave;
+    const int64_t row0 = wave * (R * SUB);
+    if (row0 >= n) return;  // whole wave leaves together
     const int64_t row_bytes = k / 2;
     const int64_t spr = (FMT == QBN_MXFP4) ? k / 32 : k / 16;  // scale bytes per row
-    int64_t p = (int64_t)blockIdx.x * WPB + threadIdx.x / kWave;
-
-    E2M1Frag<CPL> fa, fb;
-    if (p < passes) {
-        const int64_t row = p * SUB + sub;
-        e2m1_load<FMT, LPR, CPL>(fa, codes, scales, row, row < n, li, row_bytes, spr);
+    E2M1Frag<CPL> f[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = row0 + r * SUB + sub;
+        const int64_t rr = row < n ? row : row0;  // rows past n re-read row0 and are not stored
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) f[r].q[j] = ld16(codes + rr * row_bytes + 16 * (li + (int64_t)LPR * j));
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = row0 + r * SUB + sub;
+        const int64_t rr = row < n ? row : row0;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int64_t ch = li + (int64_t)LPR * j;
+            if (FMT == QBN_MXFP4) {
+                f[r].sb[j] = scales[rr * spr + ch];
+            } else {
+                uint16_t v;
+                __builtin_memcpy(&v, scales + rr * spr + 2 * ch, 2);
+                f[r].sb[j] = v;
+            }
+        }
     }
     XChunk<XT> xc[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) xc[j].load(x, 32 * (li + (int64_t)LPR * j));
-
-    while (p < passes) {
-        int64_t pn = p + stride;
-        if (pn < passes) {
-            const int64_t row = pn * SUB + sub;
-            e2m1_load<FMT, LPR, CPL>(fb, codes, scales, row, row < n, li, row_bytes, spr);
-        }
-        {
-            float acc = group_sum_last<LPR>(e2m1_compute<FMT, XT, CPL>(fa, xc));
-            const int64_t row = p * SUB + sub;
-            if (li == LPR - 1 && row < n) y[row] = (FMT == QBN_NVFP4) ? acc * scale2 : acc;
-        }
-        p = pn;
-        if (p >= passes) break;
-        pn = p + stride;
-        if (pn < passes) {
-            const int64_t row = pn * SUB + sub;
-            e2m1_load<FMT, LPR, CPL>(fa, codes, scales, row, row < n, li, row_bytes, spr);
-        }
-        {
-            float acc = group_sum_last<LPR>(e2m1_compute<FMT, XT, CPL>(fb, xc));
-            const int64_t row = p * SUB + sub;
-            if (li == LPR - 1 && row < n) y[row] = (FMT == QBN_NVFP4) ? acc * scale2 : acc;
-        }
-        p = pn;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float acc = group_sum_last<LPR>(e2m1_compute<FMT, XT, CPL>(f[r], xc));
+        const int64_t row = row0 + r * SUB + sub;
+        if (li == LPR - 1 && row < n) y[row] = (FMT == QBN_NVFP4) ? acc * scale2 : acc;
     }
 }
 
@@ -411,12 +395,56 @@ __device__ __forceinline__ float q4k_compute(const Q4KFrag<BPL> &f, const XQ4K<X
     return acc;
 }
 
-template <typename XT, int BPL, int SUB, int WPB>
+// x in LDS: 16-byte pieces; piece P sits at slot P ^ xswz(P), which permutes
+// the pieces inside each aligned group of 8 so that the 8 lanes of a block
+// reading piece i of their slices hit 8 different bank groups (for binary32
+// a lane's slice starts at piece 16 (c / 2) + 4 (c % 2) of the block, for
+// bfloat16 at 8 (c / 2) + 2 (c % 2)).
+template <typename XT>
+__device__ __forceinline__ int xswz(int P);
+template <>
+__device__ __forceinline__ int xswz<float>(int P) { return (P >> 4) & 3; }
+template <>
+__device__ __forceinline__ int xswz<__bf16>(int P) { return (((P >> 3) & 1) << 2) | ((P >> 4) & 1); }
+
+template <typename XT>
+__device__ __forceinline__ void xq4k_from_lds(XQ4K<XT> &xq, const u32x4 *xl, int e0);
+template <>
+__device__ __forceinline__ void xq4k_from_lds<float>(XQ4K<float> &xq, const u32x4 *xl, int e0) {
+    const int P0 = e0 / 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        xq.lo[i] = __builtin_bit_cast(f32x4, xl[(P0 + i) ^ xswz<float>(P0 + i)]);
+        xq.hi[i] = __builtin_bit_cast(f32x4, xl[(P0 + 8 + i) ^ xswz<float>(P0 + 8 + i)]);
+    }
+}
+template <>
+__device__ __forceinline__ void xq4k_from_lds<__bf16>(XQ4K<__bf16> &xq, const u32x4 *xl, int e0) {
+    const int P0 = e0 / 8;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        xq.lo[i] = xl[(P0 + i) ^ xswz<__bf16>(P0 + i)];
+        xq.hi[i] = xl[(P0 + 4 + i) ^ xswz<__bf16>(P0 + 4 + i)];
+    }
+}
+
+// XP: x pieces per thread (the launcher picks XP * 64 * WPB >= k pieces).
+template <typename XT, int BPL, int SUB, int WPB, int XP>
 __global__ __launch_bounds__(WPB * 64) void k_gemv_q4k_loop(const uint8_t *__restrict__ blocks,
                                                             const XT *__restrict__ x, float *__restrict__ y,
                                                             int64_t n, int64_t k) {
     constexpr int LPR = kWave / SUB;  // lanes per row
     constexpr int NBR = LPR / 8;      // blocks covered by one pass of a row's lanes
+    extern __shared__ u32x4 xl[];
+    const int npieces = (int)(k * (int64_t)sizeof(XT) / 16);
+    // x is requested first, so waiting for it below leaves the weight
+    // prefetch in flight
+    u32x4 xv[XP];
+#pragma unroll
+    for (int t = 0; t < XP; ++t) {
+        const int P = threadIdx.x + t * WPB * kWave;
+        if (P < npieces) xv[t] = reinterpret_cast<const u32x4 *>(x)[P];
+    }
     const int lane = threadIdx.x & (kWave - 1);
     const int c = lane & 7;
     const int slot = lane >> 3;
@@ -432,10 +460,15 @@ __global__ __launch_bounds__(WPB * 64) void k_gemv_q4k_loop(const uint8_t *__res
         const int64_t row = p * SUB + sub;
         q4k_load<BPL, NBR>(fa, blocks, row, row < n, bs, c, row_bytes);
     }
+#pragma unroll
+    for (int t = 0; t < XP; ++t) {
+        const int P = threadIdx.x + t * WPB * kWave;
+        if (P < npieces) xl[P ^ xswz<XT>(P)] = xv[t];
+    }
+    __syncthreads();
     XQ4K<XT> xq[BPL];
 #pragma unroll
-    for (int j = 0; j < BPL; ++j)
-        xq[j].load(x, 256 * (int64_t)(bs + NBR * j) + 64 * (c >> 1) + 16 * (c & 1));
+    for (int j = 0; j < BPL; ++j) xq4k_from_lds<XT>(xq[j], xl, 256 * (bs + NBR * j) + 64 * (c >> 1) + 16 * (c & 1));
     const Q4KLaneConsts L = q4k_lane_consts(c);
 
     while (p < passes) {
@@ -533,12 +566,12 @@ int64_t loop_grid(int64_t passes, int wpb, int per_cu) {
     return want < cap ? want : cap;
 }
 
-template <int FMT, typename XT, int LPR, int CPL, int WPB, int PER_CU>
-hipError_t run_e2m1_loop(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
-    constexpr int SUB = kWave / LPR;
-    const int64_t passes = (w.n + SUB - 1) / SUB;
-    const int64_t grid = loop_grid(passes, WPB, PER_CU);
-    hipLaunchKernelGGL((k_gemv_e2m1_loop<FMT, XT, LPR, CPL, WPB>), dim3((unsigned)grid), dim3(WPB * kWave), 0, s,
+template <int FMT, typename XT, int LPR, int CPL, int R, int WPB>
+hipError_t run_e2m1_rows(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+    constexpr int ROWS_PER_WAVE = R * (kWave / LPR);
+    const int64_t waves = (w.n + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
+    const int64_t grid = (waves + WPB - 1) / WPB;
+    hipLaunchKernelGGL((k_gemv_e2m1_rows<FMT, XT, LPR, CPL, R, WPB>), dim3((unsigned)grid), dim3(WPB * kWave), 0, s,
                        (const uint8_t *)w.data, (const uint8_t *)w.scales, w.scale2, x, y, w.n, w.k);
     return hipGetLastError();
 }
@@ -546,17 +579,17 @@ hipError_t run_e2m1_loop(const qbn_tensor &w, const XT *x, float *y, hipStream_t
 template <int FMT, typename XT>
 hipError_t run_e2m1(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     const int64_t C = w.k / 32;
-    if (w.k % 32 == 0) {
+    if (w.k % 32 == 0 && w.n < (int64_t)1 << 31) {
         switch (C) {
-        case 1: return run_e2m1_loop<FMT, XT, 1, 1, 4, 8>(w, x, y, s);
-        case 2: return run_e2m1_loop<FMT, XT, 2, 1, 4, 8>(w, x, y, s);
-        case 4: return run_e2m1_loop<FMT, XT, 4, 1, 4, 8>(w, x, y, s);
-        case 8: return run_e2m1_loop<FMT, XT, 8, 1, 4, 8>(w, x, y, s);
-        case 16: return run_e2m1_loop<FMT, XT, 16, 1, 4, 8>(w, x, y, s);
-        case 32: return run_e2m1_loop<FMT, XT, 32, 1, 4, 8>(w, x, y, s);
-        case 64: return run_e2m1_loop<FMT, XT, 64, 1, 4, 8>(w, x, y, s);
-        case 128: return run_e2m1_loop<FMT, XT, 64, 2, 4, 8>(w, x, y, s);
-        case 256: return run_e2m1_loop<FMT, XT, 64, 4, 4, 4>(w, x, y, s);
+        case 1: return run_e2m1_rows<FMT, XT, 1, 1, 2, 4>(w, x, y, s);
+        case 2: return run_e2m1_rows<FMT, XT, 2, 1, 2, 4>(w, x, y, s);
+        case 4: return run_e2m1_rows<FMT, XT, 4, 1, 2, 4>(w, x, y, s);
+        case 8: return run_e2m1_rows<FMT, XT, 8, 1, 2, 4>(w, x, y, s);
+        case 16: return run_e2m1_rows<FMT, XT, 16, 1, 2, 4>(w, x, y, s);
+        case 32: return run_e2m1_rows<FMT, XT, 32, 1, 2, 4>(w, x, y, s);
+        case 64: return run_e2m1_rows<FMT, XT, 64, 1, 2, 4>(w, x, y, s);
+        case 128: return run_e2m1_rows<FMT, XT, 64, 2, 2, 4>(w, x, y, s);
+        case 256: return run_e2m1_rows<FMT, XT, 64, 4, 2, 4>(w, x, y, s);
         default: break;
         }
     }
@@ -570,20 +603,32 @@ template <typename XT, int BPL, int SUB, int WPB, int PER_CU>
 hipError_t run_q4k_loop(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     const int64_t passes = (w.n + SUB - 1) / SUB;
     const int64_t grid = loop_grid(passes, WPB, PER_CU);
-    hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB>), dim3((unsigned)grid), dim3(WPB * kWave), 0, s,
-                       (const uint8_t *)w.data, x, y, w.n, w.k);
+    const int64_t pieces = w.k * (int64_t)sizeof(XT) / 16;  // k is a multiple of 256
+    constexpr int64_t T = WPB * kWave;
+    const size_t lds = (size_t)pieces * 16;
+    if (pieces <= T)
+        hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB, 1>), dim3((unsigned)grid), dim3(T), lds, s,
+                           (const uint8_t *)w.data, x, y, w.n, w.k);
+    else if (pieces <= 2 * T)
+        hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB, 2>), dim3((unsigned)grid), dim3(T), lds, s,
+                           (const uint8_t *)w.data, x, y, w.n, w.k);
+    else  // the shapes run_q4k admits have at most 4 * T pieces
+        hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB, 4>), dim3((unsigned)grid), dim3(T), lds, s,
+                           (const uint8_t *)w.data, x, y, w.n, w.k);
     return hipGetLastError();
 }
 
 template <typename XT>
 hipError_t run_q4k(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+    // the row-loop kernels stage x in LDS, at most 4 pieces per thread:
+    // k * sizeof(XT) / 16 <= 4 * WPB * 64 for every case below
     switch (w.k / 256) {
     case 1: return run_q4k_loop<XT, 1, 8, 4, 8>(w, x, y, s);
     case 2: return run_q4k_loop<XT, 1, 4, 4, 8>(w, x, y, s);
     case 4: return run_q4k_loop<XT, 1, 2, 4, 8>(w, x, y, s);
-    case 8: return run_q4k_loop<XT, 1, 1, 4, 8>(w, x, y, s);
-    case 16: return run_q4k_loop<XT, 2, 1, 4, 4>(w, x, y, s);
-    case 32: return run_q4k_loop<XT, 4, 1, 4, 2>(w, x, y, s);
+    case 8: return run_q4k_loop<XT, 1, 1, 8, 4>(w, x, y, s);
+    case 16: return run_q4k_loop<XT, 2, 1, 8, 2>(w, x, y, s);
+    case 32: return run_q4k_loop<XT, 4, 1, 8, 1>(w, x, y, s);
     default: break;
     }
     const int64_t grid = (w.n + kWavesPerBlock - 1) / kWavesPerBlock;
