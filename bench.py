@@ -79,7 +79,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0, help="timed steps (default depends on the workload)")
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default 200: long enough for the GEMM's clocks to settle)")
     ap.add_argument("--workload", default="nvfp4_gemv", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
@@ -217,7 +218,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the GEMV would shard by output rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
+              "(the GEMV would shard by output rows). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -229,12 +230,13 @@ def main():
         __graft_entry__.build()
     spec = WORKLOADS[args.workload]
     steps = args.steps or (2000 if spec["kind"] != "gemm" else 50)
+    warmup = args.warmup if args.warmup is not None else 200
     dev = torch.device("cuda:0")
     calls, R, inp = build_steps(args.workload, spec, dev)
     torch.cuda.synchronize()
 
     # warmup (untimed), then capture the K timed steps into one graph
-    for i in range(max(args.warmup, 1)):
+    for i in range(max(warmup, 1)):
         calls[i % R]()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -293,7 +295,7 @@ def main():
         "unit": spec["unit"],
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
         "scaling": "weak",

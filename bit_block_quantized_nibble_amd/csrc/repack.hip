@@ -4,10 +4,20 @@
 // goes through the logical matrix -- unpack the source codes to a plain
 // [K][N] u8 matrix with the source's axis, order and sign handling, then
 // pack with the target's axis and order -- and never reinterprets words.
-// Here the logical matrix exists one tile at a time, in LDS: a workgroup
-// unpacks a KT x NT tile of the source into LDS (u8 per code, [k][n]) with
-// loads that are contiguous across the workgroup, synchronizes, and packs
-// the tile into the target layout with stores that are contiguous as well.
+// GPTQ <-> AWQ: a thread holds the logical 8 x 8 block of codes (8 rows x 8
+// columns) that one group of 8 GPTQ words and one group of 8 AWQ words both
+// cover, as eight 32-bit words, and transposes it in registers (a three-
+// stage butterfly: 16-bit halves, bytes, nibbles), with AWQ's slot order
+// applied by renaming the words. Loads and stores are contiguous across
+// consecutive threads.
+// Q4_0 <-> GPTQ / AWQ: one Q4_0 block (32 consecutive k of one column) is
+// four GPTQ words of that column, or column slot s of 32 AWQ words after
+// four of the 8 x 8 transposes above; its 16 code bytes pair k = j with
+// k = j + 16, a nibble zip of those words. Q4_0 is column-major, so a
+// workgroup stages its tile's runs (8 consecutive blocks of each of its
+// columns) in LDS and moves each run with contiguous 4- or 2-byte accesses;
+// the GPTQ / AWQ side is read or written straight from registers, contiguous
+// across consecutive threads.
 //
 // Layouts ("Bit Packing Architecture", 'Real layouts compared'):
 //  GPTQ int32 [K/8][N]: row 8r+j of column n at bits 4j of word [r][n];
@@ -24,210 +34,333 @@
 namespace qbn {
 namespace {
 
-constexpr int KT = 256;            // tile rows (k)
-constexpr int NT = 64;             // tile columns (n)
-constexpr int LDP = NT + 4;        // LDS row pitch in bytes (breaks bank alignment of rows)
-constexpr int kThreads = 256;
-
 // AWQ slot s holds column awq_col(s) of its group of eight: 0,2,4,6,1,3,5,7.
 __device__ __forceinline__ constexpr int awq_col(int s) { return s < 4 ? 2 * s : 2 * (s - 4) + 1; }
 
-struct Tile {
-    uint8_t q[KT * LDP];
-};
-
-__device__ __forceinline__ uint32_t lds_dword(const Tile &t, int k, int c) {
-    return *reinterpret_cast<const uint32_t *>(&t.q[k * LDP + c]);
-}
-__device__ __forceinline__ void lds_put_dword(Tile &t, int k, int c, uint32_t v) {
-    *reinterpret_cast<uint32_t *>(&t.q[k * LDP + c]) = v;
-}
-
-// ------------------------------------------------------------------ unpack into LDS
-// GPTQ: thread -> column quad cq (4 columns), word rows r = t/16 + 16*i.
-__device__ void load_gptq(Tile &t, const uint32_t *__restrict__ qw, int64_t N, int64_t K, int64_t k0, int64_t n0) {
-    const int cq = threadIdx.x % (NT / 4);
-    const int rr = threadIdx.x / (NT / 4);
-    for (int r = rr; r < KT / 8; r += kThreads / (NT / 4)) {
-        const int64_t kr = k0 / 8 + r;
-        uint32_t w[4];
+// ------------------------------------------------------------------ 8 x 8 nibble transpose
+// x[s] nibble j -> x[j] nibble s (a three-stage butterfly).
+// __builtin_amdgcn_perm(a, b, sel): byte i of the result is byte sel_i of the
+// 8-byte value a:b (b = bytes 0..3, a = bytes 4..7).
+__device__ __forceinline__ void nib_transpose8(uint32_t *x) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int64_t n = n0 + 4 * cq + c;
-            w[c] = (8 * kr < K && n < N) ? qw[kr * N + n] : 0u;
+    for (int s = 0; s < 4; ++s) {  // 16-bit halves, distance 4
+        const uint32_t a = x[s], b = x[s + 4];
+        x[s] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+        x[s + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    }
+#pragma unroll
+    for (int g = 0; g < 8; g += 4)
+#pragma unroll
+        for (int s = g; s < g + 2; ++s) {  // bytes, distance 2
+            const uint32_t a = x[s], b = x[s + 2];
+            x[s] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+            x[s + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t v = 0;
+    for (int s = 0; s < 8; s += 2) {  // nibbles, distance 1
+        const uint32_t a = x[s], b = x[s + 1];
+        x[s] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+        x[s + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+    }
+}
+
+// ------------------------------------------------------------------ GPTQ <-> AWQ in registers
+// One thread per (GPTQ word row r, column group g of 8): GPTQ words
+// [r][8g .. 8g+7] <-> AWQ words [8r + j][g], j < 8. R = K/8, G = N/8.
+// VEC: the 8 GPTQ words are read / written as two 16-byte accesses.
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_gptq_to_awq(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst,
+                                                     int64_t R, int64_t G) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= R * G) return;
+    const int64_t r = i / G, g = i - r * G;
+    const uint32_t *sp = src + r * (8 * G) + 8 * g;
+    uint32_t a[8];
+    if (VEC) {
+        const u32x4 lo = reinterpret_cast<const u32x4 *>(sp)[0], hi = reinterpret_cast<const u32x4 *>(sp)[1];
+        a[0] = lo.x; a[1] = lo.y; a[2] = lo.z; a[3] = lo.w;
+        a[4] = hi.x; a[5] = hi.y; a[6] = hi.z; a[7] = hi.w;
+    } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) v |= ((w[c] >> (4 * j)) & 15u) << (8 * c);
-            lds_put_dword(t, 8 * r + j, 4 * cq, v);
+        for (int c = 0; c < 8; ++c) a[c] = sp[c];
+    }
+    // word s of the block = column awq_col(s); the transpose turns the
+    // columns' row nibbles into the rows' slot nibbles
+    uint32_t x[8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) x[s2] = a[awq_col(s2)];
+    nib_transpose8(x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[(8 * r + j) * G + g] = x[j];
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_awq_to_gptq(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst,
+                                                     int64_t R, int64_t G) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= R * G) return;
+    const int64_t r = i / G, g = i - r * G;
+    uint32_t x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = src[(8 * r + j) * G + g];
+    nib_transpose8(x);  // x[s] = column awq_col(s), nibble j = row 8r + j
+    uint32_t a[8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) a[awq_col(s2)] = x[s2];
+    uint32_t *dp = dst + r * (8 * G) + 8 * g;
+    if (VEC) {
+        reinterpret_cast<u32x4 *>(dp)[0] = u32x4{a[0], a[1], a[2], a[3]};
+        reinterpret_cast<u32x4 *>(dp)[1] = u32x4{a[4], a[5], a[6], a[7]};
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dp[c] = a[c];
+    }
+}
+
+// ------------------------------------------------------------------ Q4_0 blocks
+// A column's 32 codes of one block as four words T[q] (nibble j = k 8q + j,
+// the GPTQ word order) <-> the block's 16 code bytes as four words D[m]
+// (byte i of D[m] = code 4m + i | code 4m + i + 16 << 4).
+__device__ __forceinline__ uint32_t nib_spread(uint32_t x) {  // 4 nibbles -> low nibbles of 4 bytes
+    x &= 0xFFFFu;
+    x = (x | (x << 8)) & 0x00FF00FFu;
+    return (x | (x << 4)) & 0x0F0F0F0Fu;
+}
+__device__ __forceinline__ uint32_t nib_compress(uint32_t x) {  // low nibbles of 4 bytes -> 16 bits
+    x &= 0x0F0F0F0Fu;
+    x = (x | (x >> 4)) & 0x00FF00FFu;
+    return (x | (x >> 8)) & 0x0000FFFFu;
+}
+__device__ __forceinline__ void block_zip(const uint32_t *T, uint32_t *D) {
+    D[0] = nib_spread(T[0]) | (nib_spread(T[2]) << 4);
+    D[1] = nib_spread(T[0] >> 16) | (nib_spread(T[2] >> 16) << 4);
+    D[2] = nib_spread(T[1]) | (nib_spread(T[3]) << 4);
+    D[3] = nib_spread(T[1] >> 16) | (nib_spread(T[3] >> 16) << 4);
+}
+__device__ __forceinline__ void block_unzip(const uint32_t *D, uint32_t *T) {
+    T[0] = nib_compress(D[0]) | (nib_compress(D[1]) << 16);
+    T[2] = nib_compress(D[0] >> 4) | (nib_compress(D[1] >> 4) << 16);
+    T[1] = nib_compress(D[2]) | (nib_compress(D[3]) << 16);
+    T[3] = nib_compress(D[2] >> 4) | (nib_compress(D[3] >> 4) << 16);
+}
+
+// LDS staging of Q4_0 runs: run r (up to RB blocks of one column) at
+// r * RS bytes; RS is an odd number of words, so consecutive lanes writing
+// consecutive runs hit different banks.
+constexpr int RB = 8;
+constexpr int RS = RB * 18 + 4;
+
+__device__ __forceinline__ void put_block(uint8_t *run, int b, uint16_t d, const uint32_t *D) {
+    uint16_t *p = reinterpret_cast<uint16_t *>(run + 18 * b);
+    p[0] = d;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        p[1 + 2 * m] = (uint16_t)D[m];
+        p[2 + 2 * m] = (uint16_t)(D[m] >> 16);
+    }
+}
+__device__ __forceinline__ void get_block(const uint8_t *run, int b, uint32_t *D) {
+    const uint16_t *p = reinterpret_cast<const uint16_t *>(run + 18 * b);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) D[m] = (uint32_t)p[1 + 2 * m] | ((uint32_t)p[2 + 2 * m] << 16);
+}
+
+// Moves NR staged runs between LDS and global memory; run r belongs to
+// column col(r) (skipped when col(r) >= N) and holds blocks b0 .. b0+nb-1 of
+// it, contiguous at (col * nbr + b0) * 18. Wave w moves runs w, w + 4, ...,
+// BATCH runs at a time with all of a batch's loads issued before its stores.
+// WORDS: every run starts on a 4-byte boundary and has an even block count
+// (a run is then at most 36 words, one per lane); otherwise 2-byte units.
+template <bool TO_LDS, int NR, typename ColOf>
+__device__ __forceinline__ void move_runs(uint8_t *lds, uint8_t *__restrict__ blocks, ColOf col, int64_t N,
+                                          int64_t nbr, int64_t b0, int nb, bool words) {
+    constexpr int PER_WAVE = NR / 4;
+    constexpr int BATCH = PER_WAVE < 16 ? PER_WAVE : 16;
+    static_assert(NR % (4 * BATCH) == 0, "whole batches");
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    const int L = nb * 18;
+    for (int r0 = wave; r0 < NR; r0 += 4 * BATCH) {
+        if (words) {
+            uint32_t v[BATCH];
+            uint32_t *gp[BATCH];
+            bool ok[BATCH];
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                const int r = r0 + 4 * i;
+                const int64_t n = col(r);
+                ok[i] = n < N && lane < L / 4;
+                gp[i] = reinterpret_cast<uint32_t *>(blocks + (n * nbr + b0) * 18) + lane;
+                uint32_t *lp = reinterpret_cast<uint32_t *>(lds + r * RS) + lane;
+                v[i] = ok[i] ? (TO_LDS ? *gp[i] : *lp) : 0u;
+            }
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                uint32_t *lp = reinterpret_cast<uint32_t *>(lds + (r0 + 4 * i) * RS) + lane;
+                if (ok[i]) {
+                    if (TO_LDS) *lp = v[i];
+                    else *gp[i] = v[i];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {  // a run is at most 72 halfwords
+                const int u = lane + 64 * h;
+                uint16_t v[BATCH];
+                uint16_t *gp[BATCH];
+                bool ok[BATCH];
+#pragma unroll
+                for (int i = 0; i < BATCH; ++i) {
+                    const int r = r0 + 4 * i;
+                    const int64_t n = col(r);
+                    ok[i] = n < N && u < L / 2;
+                    gp[i] = reinterpret_cast<uint16_t *>(blocks + (n * nbr + b0) * 18) + u;
+                    uint16_t *lp = reinterpret_cast<uint16_t *>(lds + r * RS) + u;
+                    v[i] = ok[i] ? (TO_LDS ? *gp[i] : *lp) : (uint16_t)0;
+                }
+#pragma unroll
+                for (int i = 0; i < BATCH; ++i) {
+                    uint16_t *lp = reinterpret_cast<uint16_t *>(lds + (r0 + 4 * i) * RS) + u;
+                    if (ok[i]) {
+                        if (TO_LDS) *lp = v[i];
+                        else *gp[i] = v[i];
+                    }
+                }
+            }
         }
     }
 }
 
-// AWQ: thread -> word column g (8 codes), rows k = t/8 + 32*i.
-__device__ void load_awq(Tile &t, const uint32_t *__restrict__ qw, int64_t N, int64_t K, int64_t k0, int64_t n0) {
-    const int g = threadIdx.x % (NT / 8);
-    const int kk = threadIdx.x / (NT / 8);
-    const int64_t ng = N / 8;
-    for (int k = kk; k < KT; k += kThreads / (NT / 8)) {
-        const int64_t kg = k0 + k;
-        const int64_t gg = n0 / 8 + g;
-        const uint32_t w = (kg < K && gg < ng) ? qw[kg * ng + gg] : 0u;
-        uint32_t col[8];
+// Workgroup tiles: RB consecutive blocks (RB * 32 k) of 64 columns (GPTQ
+// side) or of 256 columns = 32 AWQ word columns (AWQ side); blockIdx.x runs
+// fastest along k so the runs of one column are completed together.
+// GPTQ tile: thread (c = t % 64, i = t / 64) handles blocks i and i + 4.
+__global__ __launch_bounds__(256) void k_gptq_to_q4_0(const uint32_t *__restrict__ src,
+                                                      const uint16_t *__restrict__ scales, int64_t group,
+                                                      uint8_t *__restrict__ dst, int64_t N, int64_t K, int words) {
+    __shared__ __attribute__((aligned(16))) uint8_t runs[64 * RS];
+    const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
+    const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, n0 = (int64_t)(blockIdx.x / nbt) * 64;
+    const int nb = (int)((nbr - b0) < RB ? (nbr - b0) : RB);
+    const int c = threadIdx.x % 64;
+    const int64_t n = n0 + c;
+    if (n < N) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) col[awq_col(s)] = (w >> (4 * s)) & 15u;
-        lds_put_dword(t, k, 8 * g, col[0] | (col[1] << 8) | (col[2] << 16) | (col[3] << 24));
-        lds_put_dword(t, k, 8 * g + 4, col[4] | (col[5] << 8) | (col[6] << 16) | (col[7] << 24));
-    }
-}
-
-// Q4_0: thread -> (column quad cq, block b); reads the 4 blocks (cq's columns, b).
-__device__ void load_q4_0(Tile &t, const uint8_t *__restrict__ blocks, int64_t N, int64_t K, int64_t k0,
-                          int64_t n0) {
-    const int cq = threadIdx.x % (NT / 4);
-    const int b = threadIdx.x / (NT / 4);
-    if (b >= KT / 32) return;
-    const int64_t nbr = K / 32;  // blocks per output column
-    const int64_t bg = k0 / 32 + b;
-    uint32_t codes[4][4];        // [column][code dword]
+        for (int h = 0; h < 2; ++h) {
+            const int b = threadIdx.x / 64 + 4 * h;
+            if (b >= nb) continue;
+            const int64_t bg = b0 + b;
+            uint32_t T[4], D[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int64_t n = n0 + 4 * cq + c;
-        const bool ok = (bg < nbr) && (n < N);
-        const uint16_t *bp = reinterpret_cast<const uint16_t *>(blocks + (n * nbr + bg) * 18);
-        uint16_t h[9];
-#pragma unroll
-        for (int i = 1; i < 9; ++i) h[i] = ok ? bp[i] : (uint16_t)0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) codes[c][i] = (uint32_t)h[1 + 2 * i] | ((uint32_t)h[2 + 2 * i] << 16);
-    }
-    // byte j of the 16 code bytes: element j (low), element j+16 (high)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t byte = (codes[c][j / 4] >> (8 * (j % 4))) & 0xFFu;
-            lo |= (byte & 15u) << (8 * c);
-            hi |= (byte >> 4) << (8 * c);
-        }
-        lds_put_dword(t, 32 * b + j, 4 * cq, lo);
-        lds_put_dword(t, 32 * b + j + 16, 4 * cq, hi);
-    }
-}
-
-// ------------------------------------------------------------------ pack from LDS
-__device__ void store_gptq(const Tile &t, uint32_t *__restrict__ qw, int64_t N, int64_t K, int64_t k0, int64_t n0) {
-    const int cq = threadIdx.x % (NT / 4);
-    const int rr = threadIdx.x / (NT / 4);
-    for (int r = rr; r < KT / 8; r += kThreads / (NT / 4)) {
-        const int64_t kr = k0 / 8 + r;
-        if (8 * kr >= K) break;
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t v = lds_dword(t, 8 * r + j, 4 * cq);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) w[c] |= ((v >> (8 * c)) & 15u) << (4 * j);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int64_t n = n0 + 4 * cq + c;
-            if (n < N) qw[kr * N + n] = w[c];
+            for (int q = 0; q < 4; ++q) T[q] = src[(4 * bg + q) * N + n];
+            block_zip(T, D);
+            put_block(runs + c * RS, b, scales[((32 * bg) / group) * N + n], D);
         }
     }
-}
-
-__device__ void store_awq(const Tile &t, uint32_t *__restrict__ qw, int64_t N, int64_t K, int64_t k0, int64_t n0) {
-    const int g = threadIdx.x % (NT / 8);
-    const int kk = threadIdx.x / (NT / 8);
-    const int64_t ng = N / 8;
-    for (int k = kk; k < KT; k += kThreads / (NT / 8)) {
-        const int64_t kg = k0 + k;
-        const int64_t gg = n0 / 8 + g;
-        if (kg >= K || gg >= ng) continue;
-        const uint32_t a = lds_dword(t, k, 8 * g), b = lds_dword(t, k, 8 * g + 4);
-        uint32_t col[8];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            col[c] = (a >> (8 * c)) & 15u;
-            col[4 + c] = (b >> (8 * c)) & 15u;
-        }
-        uint32_t w = 0;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) w |= col[awq_col(s)] << (4 * s);
-        qw[kg * ng + gg] = w;
-    }
-}
-
-// Q4_0 destination: d of block (n, b) = fp16 bits of scale[(32b)/group][n].
-__device__ void store_q4_0(const Tile &t, uint8_t *__restrict__ blocks, const uint16_t *__restrict__ scales,
-                           int64_t group, int64_t N, int64_t K, int64_t k0, int64_t n0) {
-    const int cq = threadIdx.x % (NT / 4);
-    const int b = threadIdx.x / (NT / 4);
-    if (b >= KT / 32) return;
-    const int64_t nbr = K / 32;
-    const int64_t bg = k0 / 32 + b;
-    if (bg >= nbr) return;
-    uint32_t lo[16], hi[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        lo[j] = lds_dword(t, 32 * b + j, 4 * cq);
-        hi[j] = lds_dword(t, 32 * b + j + 16, 4 * cq);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int64_t n = n0 + 4 * cq + c;
-        if (n >= N) break;
-        uint16_t *bp = reinterpret_cast<uint16_t *>(blocks + (n * nbr + bg) * 18);
-        bp[0] = scales[((32 * bg) / group) * N + n];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t b0 = ((lo[2 * i] >> (8 * c)) & 15u) | (((hi[2 * i] >> (8 * c)) & 15u) << 4);
-            const uint32_t b1 = ((lo[2 * i + 1] >> (8 * c)) & 15u) | (((hi[2 * i + 1] >> (8 * c)) & 15u) << 4);
-            bp[1 + i] = (uint16_t)(b0 | (b1 << 8));
-        }
-    }
-}
-
-template <int SRC, int DST>
-__global__ __launch_bounds__(kThreads) void k_repack(const void *__restrict__ src, const uint16_t *__restrict__ src_scales,
-                                                     int64_t group, void *__restrict__ dst, int64_t N, int64_t K) {
-    __shared__ Tile tile;
-    const int64_t ntiles_n = (N + NT - 1) / NT;
-    const int64_t k0 = (int64_t)(blockIdx.x / ntiles_n) * KT;
-    const int64_t n0 = (int64_t)(blockIdx.x % ntiles_n) * NT;
-    if (SRC == QBN_GPTQ4) load_gptq(tile, (const uint32_t *)src, N, K, k0, n0);
-    if (SRC == QBN_AWQ4) load_awq(tile, (const uint32_t *)src, N, K, k0, n0);
-    if (SRC == QBN_Q4_0) load_q4_0(tile, (const uint8_t *)src, N, K, k0, n0);
     __syncthreads();
-    if (DST == QBN_GPTQ4) store_gptq(tile, (uint32_t *)dst, N, K, k0, n0);
-    if (DST == QBN_AWQ4) store_awq(tile, (uint32_t *)dst, N, K, k0, n0);
-    if (DST == QBN_Q4_0) store_q4_0(tile, (uint8_t *)dst, src_scales, group, N, K, k0, n0);
+    move_runs<false, 64>(runs, dst, [&](int r) { return n0 + r; }, N, nbr, b0, nb, words != 0);
 }
 
-// Q4_0 -> GPTQ/AWQ companions: scale[gi][n] = d of block (n, gi*group/32), zero = 8.
-__global__ __launch_bounds__(256) void k_q4_0_group_scales(const uint8_t *__restrict__ blocks, int64_t N, int64_t K,
-                                                           int64_t group, uint16_t *__restrict__ scales,
-                                                           uint8_t *__restrict__ zeros) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t G = K / group;
-    if (i >= G * N) return;
-    const int64_t gi = i / N, n = i - gi * N;
-    const int64_t b = gi * (group / 32);
-    scales[i] = *reinterpret_cast<const uint16_t *>(blocks + (n * (K / 32) + b) * 18);
-    zeros[i] = 8;
+// Q4_0 -> GPTQ / AWQ also write the companions of the target: for every
+// group (group / 32 consecutive blocks of a column) the scale is the bit
+// pattern of its first block's d and the zero point is 8.
+__global__ __launch_bounds__(256) void k_q4_0_to_gptq(const uint8_t *__restrict__ src, uint32_t *__restrict__ dst,
+                                                      uint16_t *__restrict__ gscales, uint8_t *__restrict__ gzeros,
+                                                      int64_t group, int64_t N, int64_t K, int words) {
+    __shared__ __attribute__((aligned(16))) uint8_t runs[64 * RS];
+    const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
+    const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, n0 = (int64_t)(blockIdx.x / nbt) * 64;
+    const int nb = (int)((nbr - b0) < RB ? (nbr - b0) : RB);
+    move_runs<true, 64>(runs, const_cast<uint8_t *>(src), [&](int r) { return n0 + r; }, N, nbr, b0, nb,
+                        words != 0);
+    __syncthreads();
+    const int c = threadIdx.x % 64;
+    const int64_t n = n0 + c;
+    if (n >= N) return;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int b = threadIdx.x / 64 + 4 * h;
+        if (b >= nb) continue;
+        const int64_t bg = b0 + b;
+        uint32_t T[4], D[4];
+        get_block(runs + c * RS, b, D);
+        block_unzip(D, T);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[(4 * bg + q) * N + n] = T[q];
+        if ((32 * bg) % group == 0) {
+            const int64_t gi = (32 * bg) / group;
+            gscales[gi * N + n] = *reinterpret_cast<const uint16_t *>(runs + c * RS + 18 * b);
+            gzeros[gi * N + n] = 8;
+        }
+    }
 }
 
-template <int SRC, int DST>
-hipError_t run(const qbn_tensor &s, int64_t group, void *dst, hipStream_t st) {
-    const int64_t N = s.n, K = s.k;
-    const int64_t tiles = ((K + KT - 1) / KT) * ((N + NT - 1) / NT);
-    hipLaunchKernelGGL((k_repack<SRC, DST>), dim3((unsigned)tiles), dim3(kThreads), 0, st, s.data,
-                       (const uint16_t *)s.scales, group, dst, N, K);
-    return hipGetLastError();
+// AWQ tile: thread (g = t % 32, b = t / 32) reads the 32 AWQ words of block
+// b of word column g0 + g; run 32 s + g holds column 8 (g0 + g) + awq_col(s).
+__global__ __launch_bounds__(256) void k_awq_to_q4_0(const uint32_t *__restrict__ src,
+                                                     const uint16_t *__restrict__ scales, int64_t group,
+                                                     uint8_t *__restrict__ dst, int64_t N, int64_t K, int words) {
+    __shared__ __attribute__((aligned(16))) uint8_t runs[256 * RS];
+    const int64_t G = N / 8, nbr = K / 32, nbt = (nbr + RB - 1) / RB;
+    const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, g0 = (int64_t)(blockIdx.x / nbt) * 32;
+    const int nb = (int)((nbr - b0) < RB ? (nbr - b0) : RB);
+    const int g = threadIdx.x % 32, b = threadIdx.x / 32;
+    if (g0 + g < G && b < nb) {
+        const int64_t bg = b0 + b;
+        uint32_t x[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) x[j] = src[(32 * bg + j) * G + g0 + g];
+        // rows 8q .. 8q+7 -> T[q][s] = column awq_col(s), nibble j = row 8q + j
+#pragma unroll
+        for (int q = 0; q < 4; ++q) nib_transpose8(x + 8 * q);
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+            const int64_t n = 8 * (g0 + g) + awq_col(s2);
+            const uint32_t T[4] = {x[s2], x[8 + s2], x[16 + s2], x[24 + s2]};
+            uint32_t D[4];
+            block_zip(T, D);
+            put_block(runs + (32 * s2 + g) * RS, b, scales[((32 * bg) / group) * N + n], D);
+        }
+    }
+    __syncthreads();
+    move_runs<false, 256>(runs, dst, [&](int r) { return 8 * (g0 + r % 32) + awq_col(r / 32); }, N, nbr, b0, nb,
+                          words != 0);
+}
+
+__global__ __launch_bounds__(256) void k_q4_0_to_awq(const uint8_t *__restrict__ src, uint32_t *__restrict__ dst,
+                                                     uint16_t *__restrict__ gscales, uint8_t *__restrict__ gzeros,
+                                                     int64_t group, int64_t N, int64_t K, int words) {
+    __shared__ __attribute__((aligned(16))) uint8_t runs[256 * RS];
+    const int64_t G = N / 8, nbr = K / 32, nbt = (nbr + RB - 1) / RB;
+    const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, g0 = (int64_t)(blockIdx.x / nbt) * 32;
+    const int nb = (int)((nbr - b0) < RB ? (nbr - b0) : RB);
+    move_runs<true, 256>(runs, const_cast<uint8_t *>(src),
+                         [&](int r) { return 8 * (g0 + r % 32) + awq_col(r / 32); }, N, nbr, b0, nb, words != 0);
+    __syncthreads();
+    const int g = threadIdx.x % 32, b = threadIdx.x / 32;
+    if (g0 + g >= G || b >= nb) return;
+    const int64_t bg = b0 + b;
+    uint32_t x[32];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+        uint32_t D[4], T[4];
+        get_block(runs + (32 * s2 + g) * RS, b, D);
+        block_unzip(D, T);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[8 * q + s2] = T[q];
+    }
+    if ((32 * bg) % group == 0) {
+        const int64_t gi = (32 * bg) / group;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {  // column 8 (g0 + g) + c sits in slot awq_slot(c)
+            const int sl = (c % 2 == 0) ? c / 2 : 4 + c / 2;
+            gscales[gi * N + 8 * (g0 + g) + c] = *reinterpret_cast<const uint16_t *>(runs + (32 * sl + g) * RS + 18 * b);
+            gzeros[gi * N + 8 * (g0 + g) + c] = 8;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) nib_transpose8(x + 8 * q);  // x[8q + j] = AWQ word of row 8q + j
+#pragma unroll
+    for (int j = 0; j < 32; ++j) dst[(32 * bg + j) * G + g0 + g] = x[j];
 }
 
 }  // namespace
@@ -235,32 +368,66 @@ hipError_t run(const qbn_tensor &s, int64_t group, void *dst, hipStream_t st) {
 hipError_t launch_repack(const qbn_tensor &src, int dst_format, int dst_group, void *dst_data, void *dst_scales,
                          void *dst_zeros, hipStream_t s) {
     const int64_t N = src.n, K = src.k;
-    hipError_t e = hipErrorInvalidValue;
     const int sf = src.format;
-    if (sf == QBN_GPTQ4 && dst_format == QBN_AWQ4) e = run<QBN_GPTQ4, QBN_AWQ4>(src, src.group, dst_data, s);
-    else if (sf == QBN_AWQ4 && dst_format == QBN_GPTQ4) e = run<QBN_AWQ4, QBN_GPTQ4>(src, src.group, dst_data, s);
-    else if (sf == QBN_GPTQ4 && dst_format == QBN_Q4_0) e = run<QBN_GPTQ4, QBN_Q4_0>(src, src.group, dst_data, s);
-    else if (sf == QBN_AWQ4 && dst_format == QBN_Q4_0) e = run<QBN_AWQ4, QBN_Q4_0>(src, src.group, dst_data, s);
-    else if (sf == QBN_Q4_0 && dst_format == QBN_GPTQ4) e = run<QBN_Q4_0, QBN_GPTQ4>(src, dst_group, dst_data, s);
-    else if (sf == QBN_Q4_0 && dst_format == QBN_AWQ4) e = run<QBN_Q4_0, QBN_AWQ4>(src, dst_group, dst_data, s);
-    if (e != hipSuccess) return e;
-    if (sf == QBN_Q4_0) {
-        const int64_t cnt = (K / dst_group) * N;
+    const dim3 blk(256);
+    if ((sf == QBN_GPTQ4 && dst_format == QBN_AWQ4) || (sf == QBN_AWQ4 && dst_format == QBN_GPTQ4)) {
+        // one thread per 8 x 8 block of codes
+        const int64_t R = K / 8, G = N / 8, cnt = R * G;
         if (cnt > 0) {
-            hipLaunchKernelGGL(k_q4_0_group_scales, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s,
-                               (const uint8_t *)src.data, N, K, (int64_t)dst_group, (uint16_t *)dst_scales,
-                               (uint8_t *)dst_zeros);
-            e = hipGetLastError();
+            const void *gp = sf == QBN_GPTQ4 ? src.data : dst_data;  // the GPTQ side
+            const bool vec = (reinterpret_cast<uintptr_t>(gp) % 16) == 0;
+            const dim3 grid((unsigned)((cnt + 255) / 256));
+            const uint32_t *sp = (const uint32_t *)src.data;
+            uint32_t *dp = (uint32_t *)dst_data;
+            if (sf == QBN_GPTQ4) {
+                if (vec) hipLaunchKernelGGL(k_gptq_to_awq<true>, grid, blk, 0, s, sp, dp, R, G);
+                else hipLaunchKernelGGL(k_gptq_to_awq<false>, grid, blk, 0, s, sp, dp, R, G);
+            } else {
+                if (vec) hipLaunchKernelGGL(k_awq_to_gptq<true>, grid, blk, 0, s, sp, dp, R, G);
+                else hipLaunchKernelGGL(k_awq_to_gptq<false>, grid, blk, 0, s, sp, dp, R, G);
+            }
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
         }
-    } else if (dst_format != QBN_Q4_0) {
-        // GPTQ <-> AWQ: scales and zero points keep their [K/group][N] layout
-        const int64_t cnt = (K / src.group) * N;
-        if (dst_scales && dst_scales != src.scales && cnt > 0)
-            e = hipMemcpyAsync(dst_scales, src.scales, 2 * cnt, hipMemcpyDeviceToDevice, s);
-        if (e == hipSuccess && dst_zeros && dst_zeros != src.zeros && cnt > 0)
-            e = hipMemcpyAsync(dst_zeros, src.zeros, cnt, hipMemcpyDeviceToDevice, s);
+        // scales and zero points keep their [K/group][N] layout
+        const int64_t gcnt = (K / src.group) * N;
+        hipError_t e = hipSuccess;
+        if (dst_scales && dst_scales != src.scales && gcnt > 0)
+            e = hipMemcpyAsync(dst_scales, src.scales, 2 * gcnt, hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && dst_zeros && dst_zeros != src.zeros && gcnt > 0)
+            e = hipMemcpyAsync(dst_zeros, src.zeros, gcnt, hipMemcpyDeviceToDevice, s);
+        return e;
     }
-    return e;
+    const bool to_q4 = dst_format == QBN_Q4_0;
+    if (!(to_q4 ? (sf == QBN_GPTQ4 || sf == QBN_AWQ4) : (sf == QBN_Q4_0 && (dst_format == QBN_GPTQ4 ||
+                                                                              dst_format == QBN_AWQ4))))
+        return hipErrorInvalidValue;
+    const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
+    // Q4_0 runs move as 4-byte words when every run starts and ends on a
+    // word: an even block count per column (then every tile's count is even
+    // too) and a word-aligned base.
+    const void *q4 = to_q4 ? dst_data : src.data;
+    const int words = (nbr % 2 == 0) && (reinterpret_cast<uintptr_t>(q4) % 4 == 0);
+    const bool awq = (sf == QBN_AWQ4) || (dst_format == QBN_AWQ4);
+    const int64_t ntile = awq ? (N / 8 + 31) / 32 : (N + 63) / 64;
+    const int64_t tiles = nbt * ntile;
+    if (tiles > 0) {
+        const dim3 grid((unsigned)tiles);
+        if (sf == QBN_GPTQ4)
+            hipLaunchKernelGGL(k_gptq_to_q4_0, grid, blk, 0, s, (const uint32_t *)src.data,
+                               (const uint16_t *)src.scales, (int64_t)src.group, (uint8_t *)dst_data, N, K, words);
+        else if (sf == QBN_AWQ4)
+            hipLaunchKernelGGL(k_awq_to_q4_0, grid, blk, 0, s, (const uint32_t *)src.data,
+                               (const uint16_t *)src.scales, (int64_t)src.group, (uint8_t *)dst_data, N, K, words);
+        else if (dst_format == QBN_GPTQ4)
+            hipLaunchKernelGGL(k_q4_0_to_gptq, grid, blk, 0, s, (const uint8_t *)src.data, (uint32_t *)dst_data,
+                               (uint16_t *)dst_scales, (uint8_t *)dst_zeros, (int64_t)dst_group, N, K, words);
+        else
+            hipLaunchKernelGGL(k_q4_0_to_awq, grid, blk, 0, s, (const uint8_t *)src.data, (uint32_t *)dst_data,
+                               (uint16_t *)dst_scales, (uint8_t *)dst_zeros, (int64_t)dst_group, N, K, words);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 }  // namespace qbn
