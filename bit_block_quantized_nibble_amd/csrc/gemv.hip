@@ -428,8 +428,15 @@ __device__ __forceinline__ void xq4k_from_lds<__bf16>(XQ4K<__bf16> &xq, const u3
     }
 }
 
+// Workgroup barrier ordering LDS only: unlike __syncthreads it does not
+// wait for the wave's outstanding global loads (the weight prefetch).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // XP: x pieces per thread (the launcher picks XP * 64 * WPB >= k pieces).
-template <typename XT, int BPL, int SUB, int WPB, int XP>
+// D: passes in flight ahead of the one being computed (a ring of D + 1
+// register sets; the loop body is unrolled D + 1 times so set indices are
+// compile-time).
+template <typename XT, int BPL, int SUB, int WPB, int XP, int D>
 __global__ __launch_bounds__(WPB * 64) void k_gemv_q4k_loop(const uint8_t *__restrict__ blocks,
                                                             const XT *__restrict__ x, float *__restrict__ y,
                                                             int64_t n, int64_t k) {
@@ -453,48 +460,43 @@ __global__ __launch_bounds__(WPB * 64) void k_gemv_q4k_loop(const uint8_t *__res
     const int64_t row_bytes = 144 * (k / 256);
     const int64_t passes = (n + SUB - 1) / SUB;
     const int64_t stride = (int64_t)gridDim.x * WPB;
-    int64_t p = (int64_t)blockIdx.x * WPB + threadIdx.x / kWave;
+    const int64_t p0 = (int64_t)blockIdx.x * WPB + threadIdx.x / kWave;
 
-    Q4KFrag<BPL> fa, fb;
-    if (p < passes) {
-        const int64_t row = p * SUB + sub;
-        q4k_load<BPL, NBR>(fa, blocks, row, row < n, bs, c, row_bytes);
+    Q4KFrag<BPL> f[D + 1];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const int64_t pd = p0 + d * stride;
+        if (pd < passes) {
+            const int64_t row = pd * SUB + sub;
+            q4k_load<BPL, NBR>(f[d], blocks, row, row < n, bs, c, row_bytes);
+        }
     }
 #pragma unroll
     for (int t = 0; t < XP; ++t) {
         const int P = threadIdx.x + t * WPB * kWave;
         if (P < npieces) xl[P ^ xswz<XT>(P)] = xv[t];
     }
-    __syncthreads();
+    lds_barrier();
     XQ4K<XT> xq[BPL];
 #pragma unroll
     for (int j = 0; j < BPL; ++j) xq4k_from_lds<XT>(xq[j], xl, 256 * (bs + NBR * j) + 64 * (c >> 1) + 16 * (c & 1));
     const Q4KLaneConsts L = q4k_lane_consts(c);
 
+    int64_t p = p0;
     while (p < passes) {
-        int64_t pn = p + stride;
-        if (pn < passes) {
-            const int64_t row = pn * SUB + sub;
-            q4k_load<BPL, NBR>(fb, blocks, row, row < n, bs, c, row_bytes);
-        }
-        {
-            const float acc = group_sum_last<LPR>(q4k_compute<XT, BPL>(fa, xq, L));
+#pragma unroll
+        for (int u = 0; u < D + 1; ++u) {
+            if (p >= passes) break;
+            const int64_t pl = p + D * stride;  // into the set computed one step ago
+            if (pl < passes) {
+                const int64_t row = pl * SUB + sub;
+                q4k_load<BPL, NBR>(f[(u + D) % (D + 1)], blocks, row, row < n, bs, c, row_bytes);
+            }
+            const float acc = group_sum_last<LPR>(q4k_compute<XT, BPL>(f[u], xq, L));
             const int64_t row = p * SUB + sub;
             if ((lane % LPR) == LPR - 1 && row < n) y[row] = acc;
+            p += stride;
         }
-        p = pn;
-        if (p >= passes) break;
-        pn = p + stride;
-        if (pn < passes) {
-            const int64_t row = pn * SUB + sub;
-            q4k_load<BPL, NBR>(fa, blocks, row, row < n, bs, c, row_bytes);
-        }
-        {
-            const float acc = group_sum_last<LPR>(q4k_compute<XT, BPL>(fb, xq, L));
-            const int64_t row = p * SUB + sub;
-            if ((lane % LPR) == LPR - 1 && row < n) y[row] = acc;
-        }
-        p = pn;
     }
 }
 
@@ -599,7 +601,7 @@ hipError_t run_e2m1(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename XT, int BPL, int SUB, int WPB, int PER_CU>
+template <typename XT, int BPL, int SUB, int WPB, int PER_CU, int D>
 hipError_t run_q4k_loop(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     const int64_t passes = (w.n + SUB - 1) / SUB;
     const int64_t grid = loop_grid(passes, WPB, PER_CU);
@@ -607,13 +609,13 @@ hipError_t run_q4k_loop(const qbn_tensor &w, const XT *x, float *y, hipStream_t 
     constexpr int64_t T = WPB * kWave;
     const size_t lds = (size_t)pieces * 16;
     if (pieces <= T)
-        hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB, 1>), dim3((unsigned)grid), dim3(T), lds, s,
+        hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB, 1, D>), dim3((unsigned)grid), dim3(T), lds, s,
                            (const uint8_t *)w.data, x, y, w.n, w.k);
     else if (pieces <= 2 * T)
-        hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB, 2>), dim3((unsigned)grid), dim3(T), lds, s,
+        hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB, 2, D>), dim3((unsigned)grid), dim3(T), lds, s,
                            (const uint8_t *)w.data, x, y, w.n, w.k);
     else  // the shapes run_q4k admits have at most 4 * T pieces
-        hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB, 4>), dim3((unsigned)grid), dim3(T), lds, s,
+        hipLaunchKernelGGL((k_gemv_q4k_loop<XT, BPL, SUB, WPB, 4, D>), dim3((unsigned)grid), dim3(T), lds, s,
                            (const uint8_t *)w.data, x, y, w.n, w.k);
     return hipGetLastError();
 }
@@ -623,12 +625,12 @@ hipError_t run_q4k(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     // the row-loop kernels stage x in LDS, at most 4 pieces per thread:
     // k * sizeof(XT) / 16 <= 4 * WPB * 64 for every case below
     switch (w.k / 256) {
-    case 1: return run_q4k_loop<XT, 1, 8, 4, 8>(w, x, y, s);
-    case 2: return run_q4k_loop<XT, 1, 4, 4, 8>(w, x, y, s);
-    case 4: return run_q4k_loop<XT, 1, 2, 4, 8>(w, x, y, s);
-    case 8: return run_q4k_loop<XT, 1, 1, 8, 4>(w, x, y, s);
-    case 16: return run_q4k_loop<XT, 2, 1, 8, 2>(w, x, y, s);
-    case 32: return run_q4k_loop<XT, 4, 1, 8, 1>(w, x, y, s);
+    case 1: return run_q4k_loop<XT, 1, 8, 4, 8, 1>(w, x, y, s);
+    case 2: return run_q4k_loop<XT, 1, 4, 4, 8, 1>(w, x, y, s);
+    case 4: return run_q4k_loop<XT, 1, 2, 4, 8, 1>(w, x, y, s);
+    case 8: return run_q4k_loop<XT, 1, 1, 8, 4, 1>(w, x, y, s);
+    case 16: return run_q4k_loop<XT, 2, 1, 8, 2, 1>(w, x, y, s);
+    case 32: return run_q4k_loop<XT, 4, 1, 8, 1, 1>(w, x, y, s);
     default: break;
     }
     const int64_t grid = (w.n + kWavesPerBlock - 1) / kWavesPerBlock;
