@@ -21,6 +21,12 @@ this is each kernel's average duration plus the (small) inter-kernel gap.
 Event pairs around individual launches are not used: each pair adds several
 microseconds of marker overhead, more than the kernels themselves take.
 
+roofline.traffic is the HBM-side traffic per launch measured with rocprofv3
+(FETCH_SIZE and WRITE_SIZE in separate runs, scaled by the same counters on
+a device copy of known size), read from profiles/traffic.json. It is
+reported only while the kernel's source files hash to the value recorded
+with the measurement; after any change to them it is null.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
@@ -73,6 +79,28 @@ WORKLOADS = {
         desc="bulk dequant GPTQ (fp16 scales, u8 zeros, group 128) -> bf16 [K][N], K x N = 4096 x 11008",
         bytes=22544384 + 704512 + 352256 + 90177536),
 }
+
+
+def recorded_traffic(name):
+    """Bytes per launch from profiles/traffic.json if the kernel sources are unchanged, else None."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for rel in rec["source"]:
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        except OSError:
+            return None
+    return int(rec["traffic_bytes"]) if h.hexdigest() == rec["source_sha256"] else None
 
 
 def parse():
@@ -275,13 +303,13 @@ def main():
         value = spec["flops"] / (ms_step * 1e-3) / 1e12
         achieved = spec["flops"] / (kernel_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), traffic=None)
+                    frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), traffic=recorded_traffic(args.workload))
         metric = "FP4 GEMM TFLOP/s (% MFMA peak)"
     else:
         value = spec["bytes"] / (ms_step * 1e-3) / 1e9
         achieved = spec["bytes"] / (kernel_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=recorded_traffic(args.workload))
         metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] == "gemv" else (
             "int4 repack GB/s (% HBM peak)" if spec["kind"] == "repack" else "bulk dequant GB/s (% HBM peak)")
 
