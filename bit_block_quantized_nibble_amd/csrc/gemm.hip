@@ -450,22 +450,20 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const uint16_t *__restr
     using LT = LayoutTile;
     using LC = LayoutChunk;
     // XCD-aware order: consecutive workgroups go to different XCDs (round
-    // robin), so give the workgroups of one XCD the same row panel of X.
+    // robin), so workgroup bid is given position lin = xcd * per_xcd + local
+    // of a banded order: bands of GM tile rows, column-major inside a band.
+    // The workgroups of one XCD then cover a GM x (per_xcd / GM) block of
+    // tiles (4 x 8 for 2048 x 8192), sharing GM row panels of X and
+    // per_xcd / GM column panels of W in that XCD's L2.
     const int nwg = tiles_m * tiles_n;
     const int bid = blockIdx.x;
-    int tm, tn;
-    {
-        const int xcd = bid % 8, local = bid / 8;
-        const int per_xcd = (nwg + 7) / 8;
-        const int lin = xcd * per_xcd + local;  // position in an m-major order
-        if ((nwg % 8) == 0 && lin < nwg) {
-            tm = lin / tiles_n;
-            tn = lin % tiles_n;
-        } else {
-            tm = bid / tiles_n;
-            tn = bid % tiles_n;
-        }
-    }
+    int lin = bid;
+    if ((nwg % 8) == 0) lin = (bid % 8) * (nwg / 8) + bid / 8;
+    constexpr int GM = 4;
+    const int band = lin / (GM * tiles_n);
+    const int rows = (tiles_m - band * GM) < GM ? (tiles_m - band * GM) : GM;
+    const int rb = lin - band * (GM * tiles_n);
+    const int tm = band * GM + rb % rows, tn = rb / rows;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const bool inside = (m0 + BM <= M) && (n0 + BN <= N);
     const bool interior =
