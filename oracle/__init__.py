@@ -1,7 +1,8 @@
 """CPU oracle for 4-bit block-quantized weights (test infrastructure only).
 
 Plain, slow reference definitions of the MXFP4, NVFP4, Q4_K and Q4_0 decoders,
-of the GPTQ / AWQ / Q4_0 int4 layouts and of the dot products built on them.
+of the GPTQ / AWQ / Q4_0 int4 layouts, of the dot products built on them, and
+of the W4A8 route (int8 activation quantization, Q4_K x int8 dot).
 The arithmetic lives in ``qbn_oracle.c`` (plain C, gcc -O2, no SIMD
 intrinsics, no fast-math); this module only compiles it and marshals numpy
 arrays.
@@ -92,6 +93,13 @@ def _load():
         lib.oracle_int4_sym_code.restype = ctypes.c_uint
         lib.oracle_int4_sym_value.argtypes = [ctypes.c_uint]
         lib.oracle_int4_sym_value.restype = ctypes.c_int
+        lib.oracle_q8_code.argtypes = [ctypes.c_float, ctypes.c_float]
+        lib.oracle_q8_code.restype = ctypes.c_int
+        lib.oracle_q8_quantize.argtypes = [P, ctypes.c_int, I64, P, P, P]
+        lib.oracle_w4a8_term.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, P, P, ctypes.c_int,
+                                         ctypes.POINTER(I64), ctypes.POINTER(I64)]
+        lib.oracle_w4a8_term.restype = ctypes.c_double
+        lib.oracle_q4k_w4a8_rows.argtypes = [P, I64, P, P, P, I64, P, P]
         _lib = lib
         return lib
 
@@ -326,3 +334,54 @@ def gemm_entries(fmt: int, data, scales, scale2: float, k: int, X_bits: np.ndarr
     y_out[order] = y
     s_out[order] = sa
     return y_out, s_out
+
+
+# ---------------------------------------------------------------- W4A8 (Q4_K x int8 activations)
+
+def q8_code(x: float, inv: float) -> int:
+    """One int8 activation code: RNE(binary32(x * inv)) limited to [-127, 127]."""
+    return _load().oracle_q8_code(x, inv)
+
+
+def q8_quantize(x: np.ndarray):
+    """(q int8 [k], d float32 [k/256], bsums int32 [k/32]) of f32 or bf16-bit x."""
+    xa = np.ascontiguousarray(x)
+    if xa.dtype == np.float32:
+        xdt = 0
+    elif xa.dtype == np.uint16:
+        xdt = 1
+    else:
+        raise TypeError("x must be float32 or bfloat16 bits (uint16)")
+    k = xa.size
+    if k % 256:
+        raise ValueError("k must be a multiple of 256")
+    q = np.zeros(k, np.int8)
+    d = np.zeros(k // 256, np.float32)
+    bs = np.zeros(k // 32, np.int32)
+    _load().oracle_q8_quantize(_ptr(xa), xdt, k, _ptr(q), _ptr(d), _ptr(bs))
+    return q, d, bs
+
+
+def w4a8_term(step: float, offset: float, sx: float, qw, qx):
+    """(value, integer dot, code sum) of one sub-block in the W4A8 identity."""
+    a = np.ascontiguousarray(np.asarray(qw, dtype=np.int32))
+    b = np.ascontiguousarray(np.asarray(qx, dtype=np.int32))
+    assert a.size == b.size
+    idot = ctypes.c_int64()
+    csum = ctypes.c_int64()
+    v = _load().oracle_w4a8_term(step, offset, sx, _ptr(a), _ptr(b), a.size, ctypes.byref(idot), ctypes.byref(csum))
+    return v, idot.value, csum.value
+
+
+def q4k_w4a8_rows(blocks, k: int, q: np.ndarray, d: np.ndarray, rows):
+    """(y, S) in binary64 for the chosen rows of a Q4_K weight times the
+    int8-quantized activation d[i // 256] * q[i]."""
+    blk = np.ascontiguousarray(blocks).view(np.uint8)
+    qa = np.ascontiguousarray(q, dtype=np.int8)
+    da = np.ascontiguousarray(d, dtype=np.float32)
+    assert qa.size == k and da.size == k // 256
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    y = np.zeros(r.size, np.float64)
+    sa = np.zeros(r.size, np.float64)
+    _load().oracle_q4k_w4a8_rows(_ptr(blk), k, _ptr(qa), _ptr(da), _ptr(r), r.size, _ptr(y), _ptr(sa))
+    return y, sa

@@ -25,6 +25,12 @@
  * inexact steps (NVFP4's multiply by scale2, Q4_K's gain-minus-offset) are
  * rounded exactly once to binary32, as the formats prescribe.
  * Dot products are formed in binary64 with Neumaier-compensated sums.
+ *
+ * W4A8 ([WK] section 7): activations are quantized to int8 codes with one
+ * binary32 scale per 256 elements (a reading: the pages fix only the worked
+ * example's scale and codes); the Q4_K x int8 dot then uses each weight's
+ * exact value d*s_j*q - dmin*m_j, which is what the integer route
+ * (integer dot, code sums, scales applied afterwards) computes.
  */
 #include <math.h>
 #include <stddef.h>
@@ -491,6 +497,119 @@ ORACLE_API int oracle_gemm_entries(int fmt, const uint8_t *data, const uint8_t *
         dot_f64(wscratch, xscratch, k, &y[i], &sabs[i]);
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* W4A8: Q4_K weights times int8-quantized activations                 */
+/* ------------------------------------------------------------------ */
+
+/* One activation code: q = x * inv rounded to the nearest integer (ties to
+ * even) after the binary32 product, limited to [-127, 127]. [WK] section 7:
+ * activations quantized with a scale s_x to eight-bit codes. */
+ORACLE_API int oracle_q8_code(float x, float inv)
+{
+    float t = x * inv; /* binary32 product, rounded to nearest */
+    double r = nearbyint((double)t);
+    if (r > 127.0)
+        r = 127.0;
+    if (r < -127.0)
+        r = -127.0;
+    return (int)r;
+}
+
+/* Activation quantization, one scale per 256-element block (the Q4_K
+ * super-block): amax = max |x| (exact), inv = RN32(127 / amax),
+ * d = RN32(amax / 127), q = oracle_q8_code(x, inv); an all-zero block has
+ * d = 0 and q = 0. bsums[j] = sum of the 32 codes of sub-block j.
+ * x: binary32 (xdtype 0) or bfloat16 bits (1); k a multiple of 256. */
+ORACLE_API void oracle_q8_quantize(const void *x, int xdtype, int64_t k, int8_t *q, float *d, int32_t *bsums)
+{
+    for (int64_t b = 0; b < k / 256; ++b) {
+        float v[256];
+        float amax = 0.0f;
+        for (int i = 0; i < 256; ++i) {
+            int64_t e = 256 * b + i;
+            v[i] = xdtype == 1 ? (float)oracle_bf16_value(((const uint16_t *)x)[e]) : ((const float *)x)[e];
+            float a = fabsf(v[i]);
+            if (a > amax)
+                amax = a;
+        }
+        if (amax == 0.0f) {
+            d[b] = 0.0f;
+            for (int i = 0; i < 256; ++i)
+                q[256 * b + i] = 0;
+        } else {
+            float inv = 127.0f / amax;
+            d[b] = amax / 127.0f;
+            for (int i = 0; i < 256; ++i)
+                q[256 * b + i] = (int8_t)oracle_q8_code(v[i], inv);
+        }
+        for (int j = 0; j < 8; ++j) {
+            int32_t t = 0;
+            for (int i = 0; i < 32; ++i)
+                t += q[256 * b + 32 * j + i];
+            bsums[8 * b + j] = t;
+        }
+    }
+}
+
+/* The W4A8 contribution of one Q4_K sub-block, written as the integer dot
+ * and the activation-code sum: s_x * step * sum(q_w q_x) - s_x * offset *
+ * sum(q_x), in binary64. [WK] section 7 (the identity and its worked
+ * example), section 7b step 4 and section 7c. idot and csum return the two
+ * integer sums. */
+ORACLE_API double oracle_w4a8_term(double step, double offset, double sx, const int *qw, const int *qx, int n,
+                                   int64_t *idot, int64_t *csum)
+{
+    int64_t a = 0, c = 0;
+    for (int i = 0; i < n; ++i) {
+        a += (int64_t)qw[i] * qx[i];
+        c += qx[i];
+    }
+    *idot = a;
+    *csum = c;
+    return sx * step * (double)a - sx * offset * (double)c;
+}
+
+/* W4A8 Q4_K GEMV rows: y[i] = sum over the row's weights of w * x_hat,
+ * where w = (d*s_j)*q - dmin*m_j is the weight before any binary32 rounding
+ * (the value the integer route computes) and x_hat = d_b * q_x. Each product
+ * and the compensated sum are formed in binary64; s[i] = sum |w x_hat|. */
+ORACLE_API void oracle_q4k_w4a8_rows(const uint8_t *blocks, int64_t k, const int8_t *qx, const float *dx,
+                                     const int64_t *rows, int64_t nrows, double *y, double *sabs)
+{
+    int64_t nb = k / 256;
+    for (int64_t ri = 0; ri < nrows; ++ri) {
+        double sum = 0.0, comp = 0.0, sa = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = blocks + (rows[ri] * nb + b) * 144;
+            double d = oracle_f16(rd_u16(blk + 0));
+            double dmin = oracle_f16(rd_u16(blk + 2));
+            unsigned sc[8], mn[8];
+            oracle_q4k_unpack_scales(blk + 4, sc, mn);
+            const uint8_t *qs = blk + 16;
+            for (int c = 0; c < 4; ++c) {
+                for (int l = 0; l < 32; ++l) {
+                    for (int half = 0; half < 2; ++half) {
+                        int j = 2 * c + half;
+                        unsigned q = half ? (qs[32 * c + l] >> 4) : (qs[32 * c + l] & 15u);
+                        int64_t e = b * 256 + 64 * c + 32 * half + l;
+                        double w = d * (double)sc[j] * (double)q - dmin * (double)mn[j];
+                        double p = w * ((double)dx[b] * (double)qx[e]);
+                        double t = sum + p;
+                        if (fabs(sum) >= fabs(p))
+                            comp += (sum - t) + p;
+                        else
+                            comp += (p - t) + sum;
+                        sum = t;
+                        sa += fabs(p);
+                    }
+                }
+            }
+        }
+        y[ri] = sum + comp;
+        sabs[ri] = sa;
+    }
 }
 
 /* ------------------------------------------------------------------ */
