@@ -519,9 +519,12 @@ ORACLE_API int oracle_q8_code(float x, float inv)
 
 /* Activation quantization, one scale per 256-element block (the Q4_K
  * super-block): amax = max |x| (exact), inv = RN32(127 / amax),
- * d = RN32(amax / 127), q = oracle_q8_code(x, inv); an all-zero block has
- * d = 0 and q = 0. bsums[j] = sum of the 32 codes of sub-block j.
- * x: binary32 (xdtype 0) or bfloat16 bits (1); k a multiple of 256. */
+ * d = RN32(amax / 127), q = oracle_q8_code(x, inv). A block with
+ * amax < 2^-118 (all zeros included) has d = 0 and q = 0: below that,
+ * 127 / amax is no longer safely inside binary32's range (it overflows for
+ * amax < ~2^-121, where 0 * inf would leave the code undefined) and d would
+ * be subnormal. bsums[j] = sum of the 32 codes of sub-block j.
+ * x: finite binary32 (xdtype 0) or bfloat16 bits (1); k a multiple of 256. */
 ORACLE_API void oracle_q8_quantize(const void *x, int xdtype, int64_t k, int8_t *q, float *d, int32_t *bsums)
 {
     for (int64_t b = 0; b < k / 256; ++b) {
@@ -534,7 +537,7 @@ ORACLE_API void oracle_q8_quantize(const void *x, int xdtype, int64_t k, int8_t 
             if (a > amax)
                 amax = a;
         }
-        if (amax == 0.0f) {
+        if (amax < 0x1p-118f) {
             d[b] = 0.0f;
             for (int i = 0; i < 256; ++i)
                 q[256 * b + i] = 0;

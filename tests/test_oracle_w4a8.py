@@ -116,6 +116,12 @@ def test_q8_invariants(bf16):
     x[256 * 3: 256 * 4] = 0.0
     x[256 * 3 + 17] = -5e-30                  # a block with one tiny negative value
     x[256 * 4: 256 * 5] = 1e30                # a constant huge block
+    x[256 * 5: 256 * 6] *= 1e-39              # amax far below 2^-118 (subnormal values): treated as zero
+    x[256 * 6: 256 * 7] = 0.0
+    x[256 * 6 + 40] = 2.0 ** -118             # exactly at the threshold: quantized
+    x[256 * 6 + 41] = -2.0 ** -119
+    x[256 * 7: 256 * 8] = 0.0
+    x[256 * 7 + 3] = np.float32(2.0 ** -118) * np.float32(1 - 2.0 ** -24)  # just below it
     if bf16:
         from workloads import bf16_bits_from_f32
         xb = bf16_bits_from_f32(x)
@@ -131,7 +137,7 @@ def test_q8_invariants(bf16):
     assert np.array_equal(bs, Q.reshape(-1, 32).sum(1))
     for b in range(nb):
         amax = np.abs(X[b]).max()
-        if amax == 0:
+        if amax < 2.0 ** -118:
             assert d[b] == 0 and (Q[b] == 0).all()
             continue
         # d is amax / 127 to within half an ulp of binary32
@@ -146,6 +152,9 @@ def test_q8_invariants(bf16):
         o = np.argsort(X[b], kind="stable")
         assert (np.diff(Q[b][o]) >= 0).all()
     assert d[3] > 0 and Q[3, 17] == -127
+    if not bf16:
+        assert d[5] == 0 and d[7] == 0
+        assert Q[6, 40] == 127 and Q[6, 41] == -64  # -2^-119 * (127 / 2^-118) = -63.5, ties to even
 
 
 def test_w4a8_rows_exact_on_dyadic_blocks():
