@@ -36,6 +36,7 @@ _lib = None
 EXPORTED = (
     "qbn_abi_version", "qbn_tensor_struct_size", "qbn_status_string", "qbn_last_hip_error", "qbn_bytes",
     "qbn_quantized_gemv", "qbn_quantized_gemm", "qbn_dequantize", "qbn_repack", "qbn_validate",
+    "qbn_quantize_q8", "qbn_quantized_gemv_q8",
 )
 
 
@@ -88,6 +89,10 @@ def _load():
         lib.qbn_repack.restype = I32
         lib.qbn_validate.argtypes = [T, P, P]
         lib.qbn_validate.restype = I32
+        lib.qbn_quantize_q8.argtypes = [P, I32, I64, P, P, P, P]
+        lib.qbn_quantize_q8.restype = I32
+        lib.qbn_quantized_gemv_q8.argtypes = [T, P, P, P, P, I32, P]
+        lib.qbn_quantized_gemv_q8.restype = I32
         if lib.qbn_abi_version() != 1 or lib.qbn_tensor_struct_size() != ctypes.sizeof(_CTensor):
             raise RuntimeError("libqbn ABI mismatch: rebuild the library")
         _lib = lib
@@ -171,6 +176,38 @@ def quantized_gemv(w: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None
     ct = w._c()
     _check(lib.qbn_quantized_gemv(ctypes.byref(ct), _ptr(x, "x"), _DTYPES[x.dtype], _ptr(y, "y"),
                                   _DTYPES.get(y.dtype, -1), _stream(w.device)), "qbn_quantized_gemv")
+    return y
+
+
+def quantize_q8(x: torch.Tensor, q: Optional[torch.Tensor] = None, d: Optional[torch.Tensor] = None,
+                bsums: Optional[torch.Tensor] = None):
+    """int8 activation quantization of x (float32 or bfloat16 [k], k % 256 == 0):
+    returns (q int8 [k], d float32 [k/256], bsums int32 [k/32])."""
+    lib = _load()
+    if x.dtype not in _DTYPES:
+        raise TypeError("x dtype %s" % x.dtype)
+    k = x.numel()
+    if q is None:
+        q = torch.empty(k, dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty(k // 256, dtype=torch.float32, device=x.device)
+    if bsums is None:
+        bsums = torch.empty(k // 32, dtype=torch.int32, device=x.device)
+    _check(lib.qbn_quantize_q8(_ptr(x, "x"), _DTYPES[x.dtype], k, _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"),
+                               _stream(x.device)), "qbn_quantize_q8")
+    return q, d, bsums
+
+
+def quantized_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: torch.Tensor,
+                      y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = W_hat @ (d * q) (float32 [n]) for a Q4_K weight and activations from quantize_q8."""
+    lib = _load()
+    if y is None:
+        y = torch.empty(w.n, dtype=torch.float32, device=w.device)
+    ct = w._c()
+    _check(lib.qbn_quantized_gemv_q8(ctypes.byref(ct), _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"),
+                                     _ptr(y, "y"), _DTYPES.get(y.dtype, -1), _stream(w.device)),
+           "qbn_quantized_gemv_q8")
     return y
 
 
@@ -278,6 +315,20 @@ def prepare_gemv(w: QTensor, x: torch.Tensor, y: torch.Tensor) -> Prepared:
     ct = w._c()
     args = (ctypes.byref(ct), _ptr(x, "x"), _DTYPES[x.dtype], _ptr(y, "y"), _DTYPES.get(y.dtype, -1))
     return Prepared(lib.qbn_quantized_gemv, args, "qbn_quantized_gemv", w.device, (w, x, y, ct))
+
+
+def prepare_quantize_q8(x: torch.Tensor, q: torch.Tensor, d: torch.Tensor, bsums: torch.Tensor) -> Prepared:
+    lib = _load()
+    args = (_ptr(x, "x"), _DTYPES[x.dtype], x.numel(), _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"))
+    return Prepared(lib.qbn_quantize_q8, args, "qbn_quantize_q8", x.device, (x, q, d, bsums))
+
+
+def prepare_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: torch.Tensor, y: torch.Tensor) -> Prepared:
+    lib = _load()
+    ct = w._c()
+    args = (ctypes.byref(ct), _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"), _ptr(y, "y"),
+            _DTYPES.get(y.dtype, -1))
+    return Prepared(lib.qbn_quantized_gemv_q8, args, "qbn_quantized_gemv_q8", w.device, (w, q, d, bsums, y, ct))
 
 
 def prepare_gemm(w: QTensor, x: torch.Tensor, y: torch.Tensor) -> Prepared:

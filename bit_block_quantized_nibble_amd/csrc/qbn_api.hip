@@ -149,6 +149,34 @@ int32_t qbn_quantized_gemv(const qbn_tensor *w, const void *x, int32_t x_dtype, 
     return hip_status(qbn::launch_gemv(*w, x, x_dtype, (float *)y, s));
 }
 
+int32_t qbn_quantize_q8(const void *x, int32_t x_dtype, int64_t k, int8_t *q, float *d, int32_t *bsums,
+                        void *stream) {
+    if (x_dtype < QBN_F32 || x_dtype > QBN_F16) return QBN_ERR_FORMAT;
+    if (x_dtype != QBN_F32 && x_dtype != QBN_BF16) return QBN_ERR_DTYPE;
+    if (k < 0 || k > kMaxElems || k % 256) return QBN_ERR_SHAPE;
+    if (k == 0) return QBN_OK;
+    if (!x || !q || !d || !bsums) return QBN_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(d, 4) || !aligned(bsums, 8)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_quantize_q8(x, x_dtype, k, q, d, bsums, (hipStream_t)stream));
+}
+
+int32_t qbn_quantized_gemv_q8(const qbn_tensor *w, const int8_t *q, const float *d, const int32_t *bsums, void *y,
+                              int32_t y_dtype, void *stream) {
+    int32_t st = check_tensor(w);
+    if (st) return st;
+    if (w->format != QBN_Q4_K) return QBN_ERR_UNSUPPORTED;
+    if (y_dtype < QBN_F32 || y_dtype > QBN_F16) return QBN_ERR_FORMAT;
+    if (y_dtype != QBN_F32) return QBN_ERR_DTYPE;
+    if (w->n == 0) return QBN_OK;
+    if (!y) return QBN_ERR_NULL;
+    if (!aligned(y, 4)) return QBN_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (w->k == 0) return hip_status(qbn::launch_fill_zero(y, 4 * w->n, s));
+    if (!q || !d || !bsums) return QBN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(d, 4) || !aligned(bsums, 8)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_gemv_q8(*w, q, d, bsums, (float *)y, s));
+}
+
 int32_t qbn_quantized_gemm(const qbn_tensor *w, int64_t m, const void *x, int32_t x_dtype, int64_t ldx, void *y,
                            int32_t y_dtype, int64_t ldy, void *stream) {
     int32_t st = check_tensor(w);

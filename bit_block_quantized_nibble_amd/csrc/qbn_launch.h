@@ -16,6 +16,10 @@ hipError_t launch_dequant(const qbn_tensor &w, void *out, int out_dtype, int out
 hipError_t launch_repack(const qbn_tensor &src, int dst_format, int dst_group, void *dst_data, void *dst_scales,
                          void *dst_zeros, hipStream_t s);
 hipError_t launch_validate(const qbn_tensor &w, int64_t *first_bad, hipStream_t s);
+hipError_t launch_quantize_q8(const void *x, int x_dtype, int64_t k, int8_t *q, float *d, int32_t *bsums,
+                              hipStream_t s);
+hipError_t launch_gemv_q8(const qbn_tensor &w, const int8_t *q, const float *d, const int32_t *bsums, float *y,
+                          hipStream_t s);
 hipError_t launch_fill_zero(void *out, int64_t bytes, hipStream_t s);
 hipError_t launch_fill_zero_2d_u16(void *out, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
 

@@ -152,6 +152,33 @@ QBN_API int64_t qbn_bytes(int32_t format, int64_t n, int64_t k, int32_t group, i
 QBN_API int32_t qbn_quantized_gemv(const qbn_tensor *w, const void *x, int32_t x_dtype, void *y, int32_t y_dtype,
                            void *stream);
 
+/* W4A8 activation quantization ([WK] section 7, the W4A8 paragraph and its
+ * worked example; section 7c, the activation sums): x [k] (QBN_F32 or
+ * QBN_BF16, finite values) is cut into blocks of 256 elements; block b gets
+ *   amax = max |x|, d[b] = RN32(amax / 127), inv = RN32(127 / amax),
+ *   q[i] = RNE(RN32(x[i] * inv)) limited to [-127, 127]   (int8 [k]),
+ *   bsums[8b + j] = sum of the codes of elements 32j .. 32j+31 of the
+ *                   block                                  (int32 [k/32]).
+ * A block with amax < 2^-118 (all zeros included) gets d = 0 and codes 0.
+ * The scale rule is this library's choice: the pages fix only the worked
+ * example (s_x = 0.5, codes [1, -2, 4]). k % 256 == 0 (QBN_ERR_SHAPE).
+ * Alignment: x and q 16 bytes, d 4, bsums 8. Bit-exact and deterministic. */
+QBN_API int32_t qbn_quantize_q8(const void *x, int32_t x_dtype, int64_t k, int8_t *q, float *d, int32_t *bsums,
+                                void *stream);
+
+/* y[r] = sum_i W_hat[r][i] * d[i / 256] * q[i]  for r in 0..n: the Q4_K x int8
+ * decode GEMV of the W4A8 route ([WK] section 7, section 7b step 4 and
+ * section 7c), with q, d, bsums as written by qbn_quantize_q8 for the same k.
+ * Formats: Q4_K. y: QBN_F32 [n]. W_hat is d*s_j*q - dmin*m_j taken exactly.
+ * Per sub-block the codes meet in 4 x int8 integer dots; per block the
+ * integer sums are scaled as d * sum_j s_j dot_j - dmin * sum_j m_j bsums_j in
+ * binary64 (both products exact, one rounding), times d[b]; the lane sums
+ * are added in binary32 in a fixed order (repeated calls are bit-identical).
+ * Each y[r] satisfies |y - y_exact| <= 1e-5 * sum_i |W_hat[r][i] x_hat[i]| + 1e-6
+ * with x_hat = d[i / 256] * q[i]. Alignment: q 16 bytes, d 4, bsums 8, y 4. */
+QBN_API int32_t qbn_quantized_gemv_q8(const qbn_tensor *w, const int8_t *q, const float *d, const int32_t *bsums,
+                                      void *y, int32_t y_dtype, void *stream);
+
 /* Y[i][r] = sum_j X[i][j] * W_hat[r][j] for i in 0..m, r in 0..n  (prefill
  * GEMM with packed weights, [WK] sections 7 and 7d).
  * Formats: MXFP4. X: QBN_BF16 [m][ldx] row-major, ldx >= k, ldx % 8 == 0,

@@ -36,7 +36,7 @@ def T(fmt, n, k, data=A, scales=B, zeros=C, scale2=1.0, group=0, reserved=0):
 def test_exports_every_declared_symbol(lib):
     header = open(os.path.join(ROOT, "include", "qbn.h")).read()
     declared = re.findall(r"QBN_API\s+[\w\s\*]+?\b(qbn_\w+)\s*\(", header)
-    assert len(declared) == 10
+    assert len(declared) == 12
     assert set(declared) == set(qbn.EXPORTED)
     so = ctypes.CDLL(qbn.lib_path())
     for name in declared:
@@ -96,6 +96,43 @@ def test_gemv_rejections(lib):
         assert g(T(NV, 4, 64, scale2=bad), A, F32, B, F32, None) == SCALE2
     # empty: nothing to do, nothing launched
     assert g(T(MX, 0, 64, data=None, scales=None), None, F32, None, F32, None) == OK
+
+
+def test_quantize_q8_rejections(lib):
+    f = lib.qbn_quantize_q8
+    assert f(A, 7, 256, B, C, C, None) == FORMAT
+    assert f(A, 2, 256, B, C, C, None) == DTYPE
+    assert f(A, F32, 300, B, C, C, None) == SHAPE
+    assert f(A, F32, -256, B, C, C, None) == SHAPE
+    assert f(None, F32, 256, B, C, C, None) == NULL
+    assert f(A, F32, 256, None, C, C, None) == NULL
+    assert f(A, F32, 256, B, None, C, None) == NULL
+    assert f(A, F32, 256, B, C, None, None) == NULL
+    assert f(A + 8, F32, 256, B, C, C, None) == ALIGN
+    assert f(A, BF16, 256, B + 4, C, C, None) == ALIGN
+    assert f(A, F32, 256, B, C + 2, C, None) == ALIGN
+    assert f(A, F32, 256, B, C, C + 4, None) == ALIGN
+    assert f(None, F32, 0, None, None, None, None) == OK
+
+
+def test_gemv_q8_rejections(lib):
+    g = lib.qbn_quantized_gemv_q8
+    assert g(None, A, B, C, A, F32, None) == NULL
+    assert g(T(MX, 4, 256), A, B, C, A, F32, None) == UNSUP
+    assert g(T(Q0, 4, 256), A, B, C, A, F32, None) == UNSUP
+    assert g(T(QK, 4, 300), A, B, C, A, F32, None) == SHAPE
+    assert g(T(QK, 4, 256), A, B, C, A, BF16, None) == DTYPE
+    assert g(T(QK, 4, 256), A, B, C, A, 9, None) == FORMAT
+    assert g(T(QK, 4, 256), A, B, C, None, F32, None) == NULL
+    assert g(T(QK, 4, 256), A, B, C, A + 2, F32, None) == ALIGN
+    assert g(T(QK, 4, 256), None, B, C, A, F32, None) == NULL
+    assert g(T(QK, 4, 256), A, None, C, A, F32, None) == NULL
+    assert g(T(QK, 4, 256), A, B, None, A, F32, None) == NULL
+    assert g(T(QK, 4, 256), A + 4, B, C, A, F32, None) == ALIGN
+    assert g(T(QK, 4, 256), A, B + 1, C, A, F32, None) == ALIGN
+    assert g(T(QK, 4, 256), A, B, C + 4, A, F32, None) == ALIGN
+    assert g(T(QK, 4, 256, data=A + 8), A, B, C, A, F32, None) == ALIGN
+    assert g(T(QK, 0, 256, data=None), None, None, None, None, F32, None) == OK
 
 
 def test_gemm_rejections(lib):

@@ -29,6 +29,9 @@ Workloads (n = output rows, k = reduction length):
   5  int4 repack / dequant, K x N = 4096 x 11008, group 128: GPTQ qweight
      uniform u32 [K/8][N]; fp16 scales ~ U[1e-3,1e-2] [K/128][N]; zero points
      U{0..15} u8 [K/128][N].
+  6  W4A8 decode GEMV, Q4_K 14336 x 4096 times int8-quantized activations:
+     blocks and x drawn exactly as workload 3 (x f32 N(0,1) [k]); the
+     activation codes are made from x by the library / the oracle.
 """
 from __future__ import annotations
 
@@ -42,6 +45,7 @@ SHAPES = {
     3: dict(fmt="q4_k", n=14336, k=4096),
     4: dict(fmt="mxfp4", n=8192, k=8192, m=2048),
     5: dict(fmt="gptq4", K=4096, N=11008, group=128),
+    6: dict(fmt="q4_k", n=14336, k=4096),
 }
 
 
@@ -110,7 +114,7 @@ def x_bf16(rng, k: int):
 
 def workload(c: int, seed: int | None = None, n: int | None = None, k: int | None = None,
              m: int | None = None) -> dict:
-    """Inputs of workload c (1..5). n / k / m override the shape (same
+    """Inputs of workload c (1..6). n / k / m override the shape (same
     distributions) so that tests can run the same recipe at small sizes."""
     seed = 1000 + c if seed is None else seed
     rng = _rng(seed)
@@ -126,7 +130,7 @@ def workload(c: int, seed: int | None = None, n: int | None = None, k: int | Non
         codes, scales = nvfp4_weights(rng, n, k)
         return dict(fmt="nvfp4", n=n, k=k, data=codes, scales=scales, scale2=float(SCALE2_NVFP4),
                     x=x_bf16(rng, k), seed=seed)
-    if c == 3:
+    if c in (3, 6):
         n = n or sh["n"]
         k = k or sh["k"]
         blocks = q4k_weights(rng, n, k)
@@ -144,4 +148,4 @@ def workload(c: int, seed: int | None = None, n: int | None = None, k: int | Non
         g = sh["group"]
         qweight, scales, zeros = int4_affine(rng, K, N, g)
         return dict(fmt="gptq4", K=K, N=N, group=g, qweight=qweight, scales=scales, zeros=zeros, seed=seed)
-    raise ValueError("workload must be 1..5")
+    raise ValueError("workload must be 1..6")
