@@ -67,6 +67,11 @@ WORKLOADS = {
         cfg=3, kind="gemv", unit="GB/s",
         desc="Q4_K decode GEMV 14336x4096: 144-byte super-blocks of 256, x f32, y f32, batch 1",
         bytes=14336 * 16 * 144 + 4096 * 4 + 14336 * 4),
+    "q4k_w4a8_gemv": dict(
+        cfg=6, kind="w4a8", unit="GB/s", dtype="i8",
+        desc="W4A8 decode: int8 quantization of x f32 [4096] (scale per 256) + Q4_K x int8 GEMV 14336x4096, y f32",
+        bytes=14336 * 16 * 144 + 4096 * 4 + 2 * (4096 + 16 * 4 + 128 * 4) + 14336 * 4,
+        kernel_bytes=14336 * 16 * 144 + 4096 + 16 * 4 + 128 * 4 + 14336 * 4),
     "mxfp4_gemm": dict(
         cfg=4, kind="gemm", unit="TFLOP/s",
         desc="MXFP4 prefill GEMM: W 8192x8192 (E2M1, E8M0 per 32) x X bf16 2048x8192 -> Y bf16, fp32 accumulate",
@@ -133,7 +138,8 @@ def host_to_device(a, dev):
 
 
 def build_steps(name, spec, dev):
-    """Return (list of prepared calls, one per weight copy, description of R)."""
+    """Return (step calls, one per weight copy; R; the inputs; the dominant
+    kernel's own calls when a step launches more than one kernel, else None)."""
     import torch
 
     import bit_block_quantized_nibble_amd as qbn
@@ -141,6 +147,25 @@ def build_steps(name, spec, dev):
 
     inp = workloads.workload(spec["cfg"])
     calls = []
+    if spec["kind"] == "w4a8":
+        n, k = inp["n"], inp["k"]
+        R = max(1, math.ceil(ROTATE_BYTES / inp["data"].nbytes))
+        d0 = host_to_device(inp["data"], dev)
+        x = host_to_device(inp["x"], dev)
+        q = torch.empty(k, dtype=torch.int8, device=dev)
+        dx = torch.empty(k // 256, dtype=torch.float32, device=dev)
+        bs = torch.empty(k // 32, dtype=torch.int32, device=dev)
+        y = torch.empty(n, dtype=torch.float32, device=dev)
+        quant = qbn.prepare_quantize_q8(x, q, dx, bs)
+        gemvs = [qbn.prepare_gemv_q8(qbn.QTensor("q4_k", n, k, d0.clone()), q, dx, bs, y) for _ in range(R)]
+
+        def step(g):
+            def run():
+                quant()
+                g()
+            return run
+
+        return [step(g) for g in gemvs], R, inp, gemvs
     if spec["kind"] == "gemv":
         n, k = inp["n"], inp["k"]
         wbytes = inp["data"].nbytes + (0 if inp["scales"] is None else inp["scales"].nbytes)
@@ -154,7 +179,7 @@ def build_steps(name, spec, dev):
         for _ in range(R):
             w = qbn.QTensor(inp["fmt"], n, k, d0.clone(), None if s0 is None else s0.clone(), scale2=inp["scale2"])
             calls.append(qbn.prepare_gemv(w, x, y))
-        return calls, R, inp
+        return calls, R, inp, None
     if spec["kind"] == "gemm":
         n, k, m = inp["n"], inp["k"], inp["m"]
         R = 2
@@ -165,7 +190,7 @@ def build_steps(name, spec, dev):
         for _ in range(R):
             w = qbn.QTensor("mxfp4", n, k, d0.clone(), s0.clone())
             calls.append(qbn.prepare_gemm(w, X, Y))
-        return calls, R, inp
+        return calls, R, inp, None
     # cfg 5: repack / dequant from GPTQ (or from AWQ made by the library itself)
     K, N, g = inp["K"], inp["N"], inp["group"]
     qw = host_to_device(inp["qweight"], dev)
@@ -190,7 +215,7 @@ def build_steps(name, spec, dev):
             else:
                 dst = qbn.QTensor("q4_0", N, K, torch.empty((N, K // 32, 18), dtype=torch.uint8, device=dev))
             calls.append(qbn.prepare_repack(src, dst))
-    return calls, R, inp
+    return calls, R, inp, None
 
 
 def cpu_baseline(name, spec, inp, budget_s):
@@ -200,6 +225,19 @@ def cpu_baseline(name, spec, inp, budget_s):
     cores = 1
     reps = []
     t_end = time.perf_counter() + budget_s
+    if spec["kind"] == "w4a8":
+        n, k = inp["n"], inp["k"]
+        rows = np.arange(n)
+        while True:
+            t0 = time.perf_counter()
+            q, d, _ = oracle.q8_quantize(inp["x"])
+            oracle.q4k_w4a8_rows(inp["data"], k, q, d, rows)
+            reps.append(time.perf_counter() - t0)
+            if time.perf_counter() > t_end and len(reps) >= 3:
+                break
+        t = float(np.median(reps))
+        return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                    sample="full quantize + %dx%d W4A8 GEMV, median of %d runs (%.2f s each)" % (n, k, len(reps), t))
     if spec["kind"] == "gemv":
         fmt = {"mxfp4": oracle.MXFP4, "nvfp4": oracle.NVFP4, "q4_k": oracle.Q4_K}[inp["fmt"]]
         n, k = inp["n"], inp["k"]
@@ -266,7 +304,7 @@ def main():
     steps = args.steps or (2000 if spec["kind"] != "gemm" else 50)
     warmup = args.warmup if args.warmup is not None else (500 if spec["kind"] == "gemm" else 200)
     dev = torch.device("cuda:0")
-    calls, R, inp = build_steps(args.workload, spec, dev)
+    calls, R, inp, kcalls = build_steps(args.workload, spec, dev)
     torch.cuda.synchronize()
 
     # capture the K timed steps into one graph, then warm up (untimed) by
@@ -306,6 +344,23 @@ def main():
         torch.cuda.synchronize()
         spread.append(a.elapsed_time(b) / steps)
     kernel_ms = ms_step
+    if kcalls is not None:
+        # the dominant kernel alone: K launches of it, captured and replayed
+        # the same way (its inputs were written by the step graph above)
+        kg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(kg):
+            for i in range(steps):
+                kcalls[i % R]()
+        kg.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        kg.replay()
+        b.record()
+        torch.cuda.synchronize()
+        kernel_ms = a.elapsed_time(b) / steps
+        del kg
 
     # Context, outside the timed region: the same step with one weight copy
     # (cache-resident after the first launch: MALL / L2, not HBM), and a plain
@@ -352,10 +407,10 @@ def main():
         metric = "FP4 GEMM TFLOP/s (% MFMA peak)"
     else:
         value = spec["bytes"] / (ms_step * 1e-3) / 1e9
-        achieved = spec["bytes"] / (kernel_ms * 1e-3) / 1e9
+        achieved = spec.get("kernel_bytes", spec["bytes"]) / (kernel_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=recorded_traffic(args.workload))
-        metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] == "gemv" else (
+        metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] in ("gemv", "w4a8") else (
             "int4 repack GB/s (% HBM peak)" if spec["kind"] == "repack" else "bulk dequant GB/s (% HBM peak)")
 
     cpu = None
@@ -373,7 +428,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": spec.get("dtype", "f32"),
         "data": "synthetic",
         "config": {
             "workload": spec["desc"],
@@ -382,6 +437,9 @@ def main():
             "rotating_copies": R,
             "step_bytes": spec["bytes"],
             **({"step_flops": spec["flops"]} if "flops" in spec else {}),
+            **({"kernel_bytes": spec["kernel_bytes"], "kernel_note": "roofline is the GEMV kernel alone, timed "
+                "in its own graph of K launches; value is the whole step (quantize + GEMV)"}
+               if "kernel_bytes" in spec else {}),
             "kernel_ms_per_launch": round(kernel_ms, 6),
             "kernel_ms_other_replays": [round(v, 6) for v in spread],
             "cache_resident_ms_per_launch": round(warm_ms, 6),

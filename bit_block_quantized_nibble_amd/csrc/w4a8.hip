@@ -114,29 +114,35 @@ __global__ __launch_bounds__(WPB * 64) void k_quantize_q8(const XT *__restrict__
 // NBS * BPL blocks. The wave owns R consecutive row groups and requests all
 // of their weights before its activations.
 
-// (s_2c | s_2c+1 << 8, m_2c | m_2c+1 << 8) from the 12 packed scale bytes
-// (h.y = bytes 0..3, h.z = 4..7, h.w = 8..11). Pairs 0..3 are the low six
-// bits of bytes j and j+4; pairs 4..7 take four bits from byte j+4 and the
-// top two bits of bytes j-4 (scale) and j (minimum).
+// Scales and minimums of the lane's sub-blocks 2c and 2c+1 from the 12 packed
+// bytes B (h.y = B[0..3], h.z = B[4..7], h.w = B[8..11]), returned as the
+// bytes [s_2c, s_2c+1, m_2c, m_2c+1]. Pairs j < 4 are the low six bits of
+// B[j] (scale) and B[j+4] (minimum); pairs j >= 4 take the low / high nibble
+// of B[j+4] and, as bits 4-5, the top two bits of B[j-4] / B[j]. With
+// base = 2 (c & 1), both cases gather bytes base, base+1 of two words with
+// one byte permute: U from (B[0..3], B[4..7]) and V from (B[8..11],
+// B[8..11] >> 4).
 struct PairSel {
-    uint32_t sh, lm, tm;
-    bool hi;
+    uint32_t sel;    // byte selector of the permutes
+    uint32_t lmask;  // 0x3F3F3F3F (pairs 0..3) or 0x0F0F0F0F (pairs 4..7)
+    uint32_t tmask;  // 0 or 0xC0C0C0C0
+    bool hi;         // c >= 2
 };
 
 __device__ __forceinline__ PairSel pair_sel(int c) {
     PairSel p;
+    const uint32_t base = 2u * (uint32_t)(c & 1);
+    p.sel = base | ((base + 1u) << 8) | ((base + 4u) << 16) | ((base + 5u) << 24);
     p.hi = c >= 2;
-    p.sh = 16u * (uint32_t)(c & 1);
-    p.lm = p.hi ? 0x0F0Fu : 0x3F3Fu;
-    p.tm = p.hi ? 0xC0C0u : 0u;
+    p.lmask = p.hi ? 0x0F0F0F0Fu : 0x3F3F3F3Fu;
+    p.tmask = p.hi ? 0xC0C0C0C0u : 0u;
     return p;
 }
 
-__device__ __forceinline__ void scale_pairs(const u32x4 &h, const PairSel &p, uint32_t &sp, uint32_t &mp) {
-    const uint32_t srcS = p.hi ? h.w : h.y;
-    const uint32_t srcM = p.hi ? (h.w >> 4) : h.z;
-    sp = ((srcS >> p.sh) & p.lm) | (((h.y >> p.sh) & p.tm) >> 2);
-    mp = ((srcM >> p.sh) & p.lm) | (((h.z >> p.sh) & p.tm) >> 2);
+__device__ __forceinline__ uint32_t scale_bytes(const u32x4 &h, const PairSel &p) {
+    const uint32_t U = __builtin_amdgcn_perm(h.z, h.y, p.sel);
+    const uint32_t V = __builtin_amdgcn_perm(h.w >> 4, h.w, p.sel);
+    return ((p.hi ? V : U) & p.lmask) | ((U & p.tmask) >> 2);
 }
 
 struct XChunk {
@@ -175,11 +181,10 @@ __device__ __forceinline__ double block_term(const u32x4 &h, const u32x4 &w0, co
                                              const PairSel &ps) {
     int D0, D1;
     dot_chunk(w0, w1, xc, D0, D1);
-    uint32_t sp, mp;
-    scale_pairs(h, ps, sp, mp);
+    const uint32_t sm = scale_bytes(h, ps);
     // 24-bit multiplies suffice: scales < 64, |dot| < 2^16, |code sum| < 2^12
-    const int I1 = __mul24((int)(sp & 0xFFu), D0) + __mul24((int)(sp >> 8), D1);
-    const int I2 = __mul24((int)(mp & 0xFFu), xc.bs0) + __mul24((int)(mp >> 8), xc.bs1);
+    const int I1 = __mul24((int)(sm & 0xFFu), D0) + __mul24((int)((sm >> 8) & 0xFFu), D1);
+    const int I2 = __mul24((int)((sm >> 16) & 0xFFu), xc.bs0) + __mul24((int)(sm >> 24), xc.bs1);
     const double dd = (double)f16_bits_f32(h.x & 0xFFFFu);
     const double dm = (double)f16_bits_f32(h.x >> 16);
     const double t = __builtin_fma(-dm, (double)I2, dd * (double)I1);  // one rounding
@@ -262,6 +267,108 @@ __global__ __launch_bounds__(WPB * 64) void k_gemv_q4k_q8(const uint8_t *__restr
     }
 }
 
+// Row-loop form for rows of at most NBS * BPL blocks. The lane's activation
+// codes, code sums and scales are loaded once. Wave w then owns the
+// contiguous run of passes [w*q + min(w, r), ...) of length q or q + 1
+// (passes = q * waves + r), walked with two register sets: the weights of
+// pass i+1 are requested before pass i is computed. Every request inside the
+// loop is unconditional (the one past the run re-reads its last pass), so
+// each wait leaves exactly the newer requests in flight.
+template <int BPL>
+struct QFrag {
+    u32x4 h[BPL], w0[BPL], w1[BPL];
+};
+
+// row < 2^32 (n * k < 2^40 with k >= 256) and row_bytes <= 144 * 64, so the
+// row offset is one 32 x 32 -> 64-bit multiply.
+template <int SUB, int BPL>
+__device__ __forceinline__ void q8_load(QFrag<BPL> &f, const uint8_t *__restrict__ blocks, uint32_t row,
+                                        uint32_t row_bytes, int slot, int c, int64_t nb) {
+    constexpr int NBS = 16 / SUB;
+    const uint8_t *base = blocks + (uint64_t)row * row_bytes;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+        const uint8_t *blk = base + 144 * min((int64_t)(slot + NBS * j), nb - 1);
+        f.w0[j] = ld16(blk + 16 + 32 * c);
+        f.w1[j] = ld16(blk + 32 + 32 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) f.h[j] = ld16(base + 144 * min((int64_t)(slot + NBS * j), nb - 1));
+}
+
+template <int SUB, int BPL>
+__device__ __forceinline__ float q8_pass(const QFrag<BPL> &f, const XChunk *xc, const bool *live, const PairSel &ps) {
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+        const double t = block_term(f.h[j], f.w0[j], f.w1[j], xc[j], ps);
+        acc += live[j] ? t : 0.0;
+    }
+    return group_sum_last<kWave / SUB>((float)acc);
+}
+
+// Park the row-group sums of pass i (valid in the last lane of each group) in
+// lanes i*SUB .. i*SUB+SUB-1.
+template <int SUB, int BPL, int WPB>
+__global__ __launch_bounds__(WPB * 64) void k_gemv_q4k_q8_loop(const uint8_t *__restrict__ blocks,
+                                                               const int8_t *__restrict__ q,
+                                                               const float *__restrict__ dx,
+                                                               const int32_t *__restrict__ bsums,
+                                                               float *__restrict__ y, int64_t n, int64_t nb,
+                                                               int64_t per_q, int64_t per_r) {
+    constexpr int NBS = 16 / SUB;
+    constexpr int LPR = kWave / SUB;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int c = lane & 3;
+    const int slot = (lane >> 2) % NBS;
+    const int g = (lane >> 2) / NBS;
+    const uint32_t row_bytes = 144u * (uint32_t)nb;
+    const uint32_t last = (uint32_t)(n - 1);
+    const int64_t w = (int64_t)blockIdx.x * WPB + threadIdx.x / kWave;
+    const int64_t start = w * per_q + min(w, per_r);
+    const int m = (int)(per_q + (w < per_r ? 1 : 0));
+    const PairSel ps = pair_sel(c);
+    auto row_of = [&](int i) -> uint32_t { return min((uint32_t)(start + i) * SUB + g, last); };
+
+    QFrag<BPL> f0, f1;
+    q8_load<SUB, BPL>(f0, blocks, row_of(0), row_bytes, slot, c, nb);
+    XChunk xc[BPL];
+    bool live[BPL];
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+        live[j] = slot + NBS * j < nb;
+        const int64_t b = min((int64_t)(slot + NBS * j), nb - 1);
+        const int8_t *xp = q + 256 * b + 64 * c;
+        xc[j].lo[0] = ld16(xp);
+        xc[j].lo[1] = ld16(xp + 16);
+        xc[j].hi[0] = ld16(xp + 32);
+        xc[j].hi[1] = ld16(xp + 48);
+        const u32x2 s2 = ld8(bsums + 8 * b + 2 * c);
+        xc[j].bs0 = (int32_t)s2.x;
+        xc[j].bs1 = (int32_t)s2.y;
+        xc[j].dx = (double)dx[b];
+    }
+    const bool writer = (lane % LPR) == LPR - 1;
+    int i = 0;
+    for (; i + 1 < m; i += 2) {
+        q8_load<SUB, BPL>(f1, blocks, row_of(i + 1), row_bytes, slot, c, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        float v = q8_pass<SUB, BPL>(f0, xc, live, ps);
+        uint32_t row = (uint32_t)(start + i) * SUB + g;
+        if (writer && row < n) y[row] = v;
+        q8_load<SUB, BPL>(f0, blocks, row_of(min(i + 2, m - 1)), row_bytes, slot, c, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        v = q8_pass<SUB, BPL>(f1, xc, live, ps);
+        row += SUB;
+        if (writer && row < n) y[row] = v;
+    }
+    if (i < m) {
+        const float v = q8_pass<SUB, BPL>(f0, xc, live, ps);
+        const uint32_t row = (uint32_t)(start + i) * SUB + g;
+        if (writer && row < n) y[row] = v;
+    }
+}
+
 constexpr int kQWaves = 4;
 
 template <int SUB, int BPL, int R, int WPB>
@@ -272,6 +379,25 @@ hipError_t run_gemv_q8(const qbn_tensor &w, const int8_t *q, const float *d, con
     const int64_t grid = (waves + WPB - 1) / WPB;
     hipLaunchKernelGGL((k_gemv_q4k_q8<SUB, BPL, R, WPB>), dim3((unsigned)grid), dim3(WPB * kWave), 0, s,
                        (const uint8_t *)w.data, q, d, bs, y, w.n, nb);
+    return hipGetLastError();
+}
+
+// Grid of the row-loop kernel: at most PER_CU workgroups per compute unit,
+// fewer when there are not enough passes.
+template <int SUB, int BPL, int WPB, int PER_CU>
+hipError_t run_gemv_q8_loop(const qbn_tensor &w, const int8_t *q, const float *d, const int32_t *bs, float *y,
+                            hipStream_t s) {
+    const int64_t nb = w.k / 256;
+    const int64_t passes = (w.n + SUB - 1) / SUB;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const int64_t want = (passes + WPB - 1) / WPB;
+    const int64_t grid = want < (int64_t)cus * PER_CU ? want : (int64_t)cus * PER_CU;
+    const int64_t waves = grid * WPB;  // waves past the last pass get an empty run
+    hipLaunchKernelGGL((k_gemv_q4k_q8_loop<SUB, BPL, WPB>), dim3((unsigned)grid), dim3(WPB * kWave), 0, s,
+                       (const uint8_t *)w.data, q, d, bs, y, w.n, nb, passes / waves, passes % waves);
     return hipGetLastError();
 }
 
@@ -293,14 +419,16 @@ hipError_t launch_quantize_q8(const void *x, int x_dtype, int64_t k, int8_t *q, 
 hipError_t launch_gemv_q8(const qbn_tensor &w, const int8_t *q, const float *d, const int32_t *bsums, float *y,
                           hipStream_t s) {
     const int64_t nb = w.k / 256;
-    if (nb == 1) return run_gemv_q8<16, 1, 2, 4>(w, q, d, bsums, y, s);
-    if (nb == 2) return run_gemv_q8<8, 1, 2, 4>(w, q, d, bsums, y, s);
-    if (nb <= 4) return run_gemv_q8<4, 1, 2, 4>(w, q, d, bsums, y, s);
-    if (nb <= 8) return run_gemv_q8<2, 1, 2, 4>(w, q, d, bsums, y, s);
-    if (nb <= 16) return run_gemv_q8<1, 1, 2, 4>(w, q, d, bsums, y, s);
-    if (nb <= 32) return run_gemv_q8<1, 2, 2, 4>(w, q, d, bsums, y, s);
-    if (nb <= 48) return run_gemv_q8<1, 3, 1, 4>(w, q, d, bsums, y, s);
-    return run_gemv_q8<1, 4, 1, 4>(w, q, d, bsums, y, s);  // chunks of 64 blocks
+    if (w.n >= ((int64_t)1 << 31)) return run_gemv_q8<1, 4, 1, 4>(w, q, d, bsums, y, s);  // 32-bit row math below
+    if (nb == 1) return run_gemv_q8_loop<16, 1, 4, 3>(w, q, d, bsums, y, s);
+    if (nb == 2) return run_gemv_q8_loop<8, 1, 4, 3>(w, q, d, bsums, y, s);
+    if (nb <= 4) return run_gemv_q8_loop<4, 1, 4, 3>(w, q, d, bsums, y, s);
+    if (nb <= 8) return run_gemv_q8_loop<2, 1, 4, 3>(w, q, d, bsums, y, s);
+    if (nb <= 16) return run_gemv_q8_loop<1, 1, 4, 3>(w, q, d, bsums, y, s);
+    if (nb <= 32) return run_gemv_q8_loop<1, 2, 4, 3>(w, q, d, bsums, y, s);
+    if (nb <= 48) return run_gemv_q8_loop<1, 3, 4, 2>(w, q, d, bsums, y, s);
+    if (nb <= 64) return run_gemv_q8_loop<1, 4, 4, 2>(w, q, d, bsums, y, s);
+    return run_gemv_q8<1, 4, 1, 4>(w, q, d, bsums, y, s);  // one-shot, chunks of 64 blocks
 }
 
 }  // namespace qbn
