@@ -27,10 +27,10 @@
  * Dot products are formed in binary64 with Neumaier-compensated sums.
  *
  * W4A8 ([WK] section 7): activations are quantized to int8 codes with one
- * binary32 scale per 256 elements (a reading: the pages fix only the worked
- * example's scale and codes); the Q4_K x int8 dot then uses each weight's
- * exact value d*s_j*q - dmin*m_j, which is what the integer route
- * (integer dot, code sums, scales applied afterwards) computes.
+ * binary32 scale per 256 elements by the Q8_K rule of [NV] section 7.4.2;
+ * the Q4_K x int8 dot then uses each weight's exact value
+ * d*s_j*q - dmin*m_j, which is what the integer route (integer dot, code
+ * sums, scales applied afterwards) computes.
  */
 #include <math.h>
 #include <stddef.h>
@@ -503,49 +503,49 @@ ORACLE_API int oracle_gemm_entries(int fmt, const uint8_t *data, const uint8_t *
 /* W4A8: Q4_K weights times int8-quantized activations                 */
 /* ------------------------------------------------------------------ */
 
-/* One activation code: q = x * inv rounded to the nearest integer (ties to
- * even) after the binary32 product, limited to [-127, 127]. [WK] section 7:
- * activations quantized with a scale s_x to eight-bit codes. */
-ORACLE_API int oracle_q8_code(float x, float inv)
+/* One activation code: the binary32 product x * iscale rounded to the
+ * nearest integer (ties to even), limited to at most 127. [NV] section 7.4.2
+ * (round to nearest even, clamp at 127); [WK] section 7 (eight-bit codes). */
+ORACLE_API int oracle_q8_code(float x, float iscale)
 {
-    float t = x * inv; /* binary32 product, rounded to nearest */
+    float t = x * iscale; /* binary32 product, rounded to nearest */
     double r = nearbyint((double)t);
     if (r > 127.0)
         r = 127.0;
-    if (r < -127.0)
-        r = -127.0;
     return (int)r;
 }
 
-/* Activation quantization, one scale per 256-element block (the Q4_K
- * super-block): amax = max |x| (exact), inv = RN32(127 / amax),
- * d = RN32(amax / 127), q = oracle_q8_code(x, inv). A block with
- * amax < 2^-118 (all zeros included) has d = 0 and q = 0: below that,
- * 127 / amax is no longer safely inside binary32's range (it overflows for
- * amax < ~2^-121, where 0 * inf would leave the code undefined) and d would
- * be subnormal. bsums[j] = sum of the 32 codes of sub-block j.
+/* Q8_K-style activation quantization ([NV] section 7.4.2; the Q8_K
+ * activations of [WK] section 7c), one scale per 256-element block:
+ *   mx = the first element (lowest index) of largest magnitude, with its
+ *        sign; iscale = RN32(-127 / mx); q = oracle_q8_code(x, iscale);
+ *   d  = RN32(1 / iscale), so that x ~ d * q (d has the opposite sign of mx
+ *        and the code of mx itself is -127).
+ * A block with |mx| < 2^-118 (all zeros included) has d = 0 and q = 0: the
+ * pages give no rule there, and below that bound 127 / |mx| is no longer
+ * safely inside binary32's range (0 * inf would leave a code undefined).
+ * bsums[j] = sum of the 32 codes of sub-block j.
  * x: finite binary32 (xdtype 0) or bfloat16 bits (1); k a multiple of 256. */
 ORACLE_API void oracle_q8_quantize(const void *x, int xdtype, int64_t k, int8_t *q, float *d, int32_t *bsums)
 {
     for (int64_t b = 0; b < k / 256; ++b) {
         float v[256];
-        float amax = 0.0f;
+        float mx = 0.0f;
         for (int i = 0; i < 256; ++i) {
             int64_t e = 256 * b + i;
             v[i] = xdtype == 1 ? (float)oracle_bf16_value(((const uint16_t *)x)[e]) : ((const float *)x)[e];
-            float a = fabsf(v[i]);
-            if (a > amax)
-                amax = a;
+            if (fabsf(v[i]) > fabsf(mx))
+                mx = v[i];
         }
-        if (amax < 0x1p-118f) {
+        if (fabsf(mx) < 0x1p-118f) {
             d[b] = 0.0f;
             for (int i = 0; i < 256; ++i)
                 q[256 * b + i] = 0;
         } else {
-            float inv = 127.0f / amax;
-            d[b] = amax / 127.0f;
+            float iscale = -127.0f / mx;
+            d[b] = 1.0f / iscale;
             for (int i = 0; i < 256; ++i)
-                q[256 * b + i] = (int8_t)oracle_q8_code(v[i], inv);
+                q[256 * b + i] = (int8_t)oracle_q8_code(v[i], iscale);
         }
         for (int j = 0; j < 8; ++j) {
             int32_t t = 0;

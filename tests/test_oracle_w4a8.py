@@ -2,9 +2,10 @@
 Q4_K x int8 dot ("Why 4-Bit Quantization Is King", section 7 and its worked
 W4A8 example; section 7b step 4; section 7c).
 
-The activation quantizer is a reading (the pages fix only the example's
-s_x = 0.5 and q_x = [1, -2, 4]): one scale per 256 activations,
-d = RN32(amax / 127), codes RNE(RN32(x * RN32(127 / amax))) in [-127, 127].
+The activation quantizer is the Q8_K rule of "Chapter 7 - NVFP4: the native
+lane", section 7.4.2: per 256 activations, the first element of largest
+magnitude mx (signed), iscale = RN32(-127 / mx), codes RNE(RN32(x * iscale))
+clamped at 127, scale d = RN32(1 / iscale).
 """
 import json
 import os
@@ -67,17 +68,22 @@ def test_w4a8_worked_example():
 
 
 def test_w4a8_worked_example_through_quantizer_and_rows():
-    """A block whose max |x| is 63.5 has s_x = 63.5 / 127 = 0.5 exactly, so
-    the page's activations quantize to its codes; the Q4_K row built from the
+    """A block whose first largest-magnitude element is -63.5 has
+    iscale = -127 / -63.5 = 2 and scale 1 / 2 = 0.5, the page's s_x, so the
+    page's activations quantize to its codes; the Q4_K row built from the
     page's sub-block (d, dmin rounded to fp16) then gives the page's 0.30."""
     g = golden("q4k_fixture.json")["toy_subblock"]
     x = np.zeros(256, np.float32)
     x[0:3] = g["x"]
-    x[100] = 63.5  # sub-block 3, whose scale and min are 0
+    x[100] = -63.5  # sub-block 3, whose scale and min are 0
     q, d, bs = oracle.q8_quantize(x)
     assert d[0] == 0.5
-    assert list(q[0:3]) == g["w4a8"]["q_x"] and q[100] == 127
-    assert bs[0] == g["w4a8"]["code_sum"] and bs[3] == 127
+    assert list(q[0:3]) == g["w4a8"]["q_x"] and q[100] == -127
+    assert bs[0] == g["w4a8"]["code_sum"] and bs[3] == -127
+    # a positive maximum flips the sign convention: d = -0.5, codes negated
+    x[100] = 63.5
+    qn, dn, _ = oracle.q8_quantize(x)
+    assert dn[0] == -0.5 and list(qn[0:3]) == [-c for c in g["w4a8"]["q_x"]] and qn[100] == -127
     s = [g["s"]] + [0] * 7
     m = [g["m"]] + [0] * 7
     codes = np.zeros(256, np.uint8)
@@ -93,18 +99,37 @@ def test_w4a8_worked_example_through_quantizer_and_rows():
 
 
 def test_q8_textbook_case_is_round_half_even():
-    """With max |x| = 127 the scale is 1 and the inverse scale 1, so every
-    code is x rounded to the nearest integer, ties to even (numpy.rint)."""
+    """With a first maximum of -127 the inverse scale is 1 (the scale 1), with
+    +127 it is -1, so every code is +-x rounded to the nearest integer, ties to
+    even (numpy.rint)."""
     rng = np.random.default_rng(3)
-    x = np.concatenate([rng.integers(-254, 255, 512) / 2.0, rng.uniform(-127, 127, 512)]).astype(np.float32)
-    x = x.reshape(4, 256)
-    x[:, 7] = 127.0
-    x[1, 7] = -127.0
+    x = np.concatenate([rng.integers(-252, 253, 512) / 2.0, rng.uniform(-126, 126, 512)]).astype(np.float32)
+    x = x.reshape(4, 256)  # only the planted elements below reach magnitude 127
+    x[:, 7] = -127.0
+    x[1, 7] = 127.0
+    x[1, 200] = -127.0  # a later tie of the same magnitude does not change the first maximum
     x = x.ravel()
     q, d, bs = oracle.q8_quantize(x)
-    assert (d == 1.0).all()
-    assert np.array_equal(q.astype(np.float32), np.rint(x))
-    assert q[256 + 7] == -127
+    sign = np.array([1.0, -1.0, 1.0, 1.0], np.float32)
+    assert np.array_equal(d, sign)
+    assert np.array_equal(q.astype(np.float32), np.rint(x * np.repeat(sign, 256)))
+    assert q[256 + 7] == -127 and q[256 + 200] == 127
+
+
+def test_q8_scale_is_reciprocal_of_inverse_scale():
+    """d is RN32(1 / RN32(-127 / mx)), which differs in its last bit from
+    RN32(-mx / 127) for these maxima; the codes use the inverse scale."""
+    from exact import round_f32
+    for mx in (30.953386306762695, 57.052589416503906, 19.053972244262695):
+        x = np.zeros(256, np.float32)
+        x[5] = mx
+        x[6] = np.float32(mx / 3)
+        q, d, _ = oracle.q8_quantize(x)
+        isc = round_f32(Fraction(-127) / frac(np.float32(mx)))
+        assert float(d[0]) == round_f32(Fraction(1) / Fraction(isc))
+        assert float(d[0]) != round_f32(-frac(np.float32(mx)) / 127)
+        prod = round_f32(frac(x[6]) * Fraction(isc))
+        assert q[6] == round(Fraction(prod)) and q[5] == -127
 
 
 @pytest.mark.parametrize("bf16", [False, True])
@@ -140,21 +165,22 @@ def test_q8_invariants(bf16):
         if amax < 2.0 ** -118:
             assert d[b] == 0 and (Q[b] == 0).all()
             continue
-        # d is amax / 127 to within half an ulp of binary32
-        assert abs(float(d[b]) * 127 - amax) <= amax * 2.0 ** -23
-        # the largest magnitude maps to +-127 with its sign
-        i = int(np.abs(X[b]).argmax())
-        assert Q[b, i] == (127 if X[b, i] > 0 else -127)
-        # every code is the nearest integer to x / d, up to binary32 rounding of 127 / amax and the product
+        # the first element of largest magnitude gets code -127, and d has the opposite sign
+        i = int(np.abs(X[b]).argmax())  # argmax returns the first occurrence
+        assert Q[b, i] == -127
+        assert np.sign(d[b]) == -np.sign(X[b, i])
+        # |d| is amax / 127 to within two roundings of binary32
+        assert abs(abs(float(d[b])) * 127 - amax) <= amax * 2.0 ** -22
+        # every code is the nearest integer to x / d, up to binary32 rounding of iscale and the product
         assert (np.abs(X[b] / float(d[b]) - Q[b]) <= 0.5 + 1e-4).all()
         assert (np.abs(Q[b]) <= 127).all()
-        # codes are monotone in x
-        o = np.argsort(X[b], kind="stable")
+        # codes are monotone in x * sign(iscale)
+        o = np.argsort(X[b] * -np.sign(X[b, i]), kind="stable")
         assert (np.diff(Q[b][o]) >= 0).all()
     assert d[3] > 0 and Q[3, 17] == -127
     if not bf16:
         assert d[5] == 0 and d[7] == 0
-        assert Q[6, 40] == 127 and Q[6, 41] == -64  # -2^-119 * (127 / 2^-118) = -63.5, ties to even
+        assert Q[6, 40] == -127 and Q[6, 41] == 64  # -2^-119 * (-127 / 2^-118) = 63.5, ties to even
 
 
 def test_w4a8_rows_exact_on_dyadic_blocks():
@@ -222,4 +248,4 @@ def test_w4a8_rows_near_weight_only_dot():
     assert np.allclose(S, np.abs(W) @ np.abs(xhat), rtol=1e-6)
     assert (np.abs(y - W @ xhat) <= 2.0 ** -23 * S + 1e-12).all()
     # and x_hat approximates x: the quantization error is at most d / 2 per element
-    assert (np.abs(xhat - inp["x"]) <= np.repeat(d, 256) * 0.5001).all()
+    assert (np.abs(xhat - inp["x"]) <= np.repeat(np.abs(d), 256) * 0.5001).all()
