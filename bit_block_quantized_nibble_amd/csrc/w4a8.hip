@@ -2,11 +2,13 @@
 // GEMV ("Why 4-Bit Quantization Is King", section 7 and its W4A8 example,
 // section 7b step 4, section 7c).
 //
-// Activations: one binary32 scale per 256 elements (a Q4_K super-block),
-// d = amax / 127 and codes RNE(x * (127 / amax)) in [-127, 127], both
-// divisions correctly rounded; blocks with amax < 2^-118 quantize to zero.
-// The 32-element code sums of each block are written beside the codes, as
-// the activation sums the integer route subtracts the minimum term with.
+// Activations: the Q8_K grid of "Chapter 7 - NVFP4: the native lane",
+// section 7.4.2: per 256 elements (a Q4_K super-block) the first element of
+// largest magnitude mx, iscale = -127 / mx, codes RNE(x * iscale) clamped at
+// 127, scale d = 1 / iscale (both divisions correctly rounded); blocks with
+// |mx| < 2^-118 quantize to zero. The 32-element code sums of each block are
+// written beside the codes, as the activation sums the integer route
+// subtracts the minimum term with.
 //
 // GEMV: the integer route of section 7c. Weight nibbles stay small unsigned
 // integers (0..15, so the signed 4 x int8 dot instruction takes them as
@@ -69,10 +71,11 @@ struct X4<__bf16> {
     }
 };
 
-__device__ __forceinline__ int q8_code(float v, float inv) {
-    float t = __builtin_rintf(v * inv);  // binary32 product, then nearest integer (ties to even)
-    t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
-    return (int)t;
+// |v * iscale| <= 127 (1 + 2^-24)^2 for every element of the block, so the
+// rounded code never falls below -127; only the upper clamp is needed.
+__device__ __forceinline__ int q8_code(float v, float iscale) {
+    const float t = __builtin_rintf(v * iscale);  // binary32 product, then nearest integer (ties to even)
+    return (int)__builtin_fminf(t, 127.0f);
 }
 
 // One wave per 256-element block, lane l holding elements 4l .. 4l+3.
@@ -87,13 +90,23 @@ __global__ __launch_bounds__(WPB * 64) void k_quantize_q8(const XT *__restrict__
     const float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
                                     __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
     const float amax = wave_max_nonneg(a);
+    // the first element (lowest index) whose magnitude is amax: its lane is
+    // the lowest lane holding one, and within the lane the lowest slot
+    const float first = __builtin_fabsf(v.x) == amax ? v.x
+                        : __builtin_fabsf(v.y) == amax ? v.y
+                        : __builtin_fabsf(v.z) == amax ? v.z
+                                                       : v.w;
+    const uint64_t holders = __ballot(a == amax);
+    const int src = holders ? __builtin_ctzll(holders) : 0;
+    const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(first), src));
     uint32_t packed = 0;
     int part = 0;
     float scale = 0.0f;
     if (amax >= 0x1p-118f) {
-        const float inv = 127.0f / amax;
-        scale = amax / 127.0f;
-        const int c0 = q8_code(v.x, inv), c1 = q8_code(v.y, inv), c2 = q8_code(v.z, inv), c3 = q8_code(v.w, inv);
+        const float iscale = -127.0f / mx;
+        scale = 1.0f / iscale;
+        const int c0 = q8_code(v.x, iscale), c1 = q8_code(v.y, iscale), c2 = q8_code(v.z, iscale),
+                  c3 = q8_code(v.w, iscale);
         packed = (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) | ((uint32_t)(c2 & 0xFF) << 16) |
                  ((uint32_t)(c3 & 0xFF) << 24);
         part = c0 + c1 + c2 + c3;

@@ -152,17 +152,19 @@ QBN_API int64_t qbn_bytes(int32_t format, int64_t n, int64_t k, int32_t group, i
 QBN_API int32_t qbn_quantized_gemv(const qbn_tensor *w, const void *x, int32_t x_dtype, void *y, int32_t y_dtype,
                            void *stream);
 
-/* W4A8 activation quantization ([WK] section 7, the W4A8 paragraph and its
- * worked example; section 7c, the activation sums): x [k] (QBN_F32 or
- * QBN_BF16, finite values) is cut into blocks of 256 elements; block b gets
- *   amax = max |x|, d[b] = RN32(amax / 127), inv = RN32(127 / amax),
- *   q[i] = RNE(RN32(x[i] * inv)) limited to [-127, 127]   (int8 [k]),
+/* Q8_K activation quantization for the W4A8 route ([NV] section 7.4.2, the
+ * activation grid; [WK] section 7, the W4A8 paragraph, and section 7c, the
+ * activation sums): x [k] (QBN_F32 or QBN_BF16, finite values) is cut into
+ * blocks of 256 elements; block b gets
+ *   mx = its first element (lowest index) of largest magnitude, signed,
+ *   iscale = RN32(-127 / mx),  d[b] = RN32(1 / iscale)     (float [k/256]),
+ *   q[i] = RNE(RN32(x[i] * iscale)) clamped at 127         (int8 [k]),
  *   bsums[8b + j] = sum of the codes of elements 32j .. 32j+31 of the
  *                   block                                  (int32 [k/32]).
- * A block with amax < 2^-118 (all zeros included) gets d = 0 and codes 0.
- * The scale rule is this library's choice: the pages fix only the worked
- * example (s_x = 0.5, codes [1, -2, 4]). k % 256 == 0 (QBN_ERR_SHAPE).
- * Alignment: x and q 16 bytes, d 4, bsums 8. Bit-exact and deterministic. */
+ * So x ~ d * q, d has the sign opposite to mx, and mx's own code is -127.
+ * A block with |mx| < 2^-118 (all zeros included) gets d = 0 and codes 0.
+ * k % 256 == 0 (QBN_ERR_SHAPE). Alignment: x and q 16 bytes, d 4, bsums 8.
+ * Bit-exact and deterministic. */
 QBN_API int32_t qbn_quantize_q8(const void *x, int32_t x_dtype, int64_t k, int8_t *q, float *d, int32_t *bsums,
                                 void *stream);
 
