@@ -2,7 +2,8 @@
 
 Plain, slow reference definitions of the MXFP4, NVFP4, Q4_K and Q4_0 decoders,
 of the GPTQ / AWQ / Q4_0 int4 layouts, of the dot products built on them, and
-of the W4A8 route (int8 activation quantization, Q4_K x int8 dot).
+of the W4A8 route (int8 activation quantization, Q4_K x int8 dot) and of the
+integer-exact NVFP4 x Q8_K decode.
 The arithmetic lives in ``qbn_oracle.c`` (plain C, gcc -O2, no SIMD
 intrinsics, no fast-math); this module only compiles it and marshals numpy
 arrays.
@@ -100,6 +101,13 @@ def _load():
                                          ctypes.POINTER(I64), ctypes.POINTER(I64)]
         lib.oracle_w4a8_term.restype = ctypes.c_double
         lib.oracle_q4k_w4a8_rows.argtypes = [P, I64, P, P, P, I64, P, P]
+        lib.oracle_e2m1_q1.argtypes = [ctypes.c_uint]
+        lib.oracle_e2m1_q1.restype = ctypes.c_int
+        lib.oracle_e4m3fn_q9.argtypes = [ctypes.c_uint]
+        lib.oracle_e4m3fn_q9.restype = I64
+        lib.oracle_f16_rne.argtypes = [ctypes.c_float]
+        lib.oracle_f16_rne.restype = ctypes.c_uint
+        lib.oracle_nvfp4_a16q8_rows.argtypes = [P, P, ctypes.c_float, I64, P, P, P, I64, P, P]
         _lib = lib
         return lib
 
@@ -385,3 +393,35 @@ def q4k_w4a8_rows(blocks, k: int, q: np.ndarray, d: np.ndarray, rows):
     sa = np.zeros(r.size, np.float64)
     _load().oracle_q4k_w4a8_rows(_ptr(blk), k, _ptr(qa), _ptr(da), _ptr(r), r.size, _ptr(y), _ptr(sa))
     return y, sa
+
+
+# ---------------------------------------------------------------- NVFP4 x Q8_K, integer-exact
+
+def e2m1_q1(code: int) -> int:
+    return _load().oracle_e2m1_q1(code)
+
+
+def e4m3fn_q9(byte: int) -> int:
+    return _load().oracle_e4m3fn_q9(byte)
+
+
+def f16_rne(values) -> np.ndarray:
+    """binary16 bits (uint16) of binary32 values, round to nearest even."""
+    lib = _load()
+    v = np.ascontiguousarray(values, dtype=np.float32).ravel()
+    return np.array([lib.oracle_f16_rne(float(t)) for t in v], dtype=np.uint16)
+
+
+def nvfp4_a16q8_rows(codes, scales, scale2: float, k: int, q: np.ndarray, d: np.ndarray, rows):
+    """(y binary32, y binary16 bits) of the integer-exact NVFP4 x Q8_K decode."""
+    c = np.ascontiguousarray(codes).view(np.uint8)
+    s = np.ascontiguousarray(scales).view(np.uint8)
+    qa = np.ascontiguousarray(q, dtype=np.int8)
+    da = np.ascontiguousarray(d, dtype=np.float32)
+    assert qa.size == k and da.size == k // 256 and k % 256 == 0
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    y32 = np.zeros(r.size, np.float32)
+    y16 = np.zeros(r.size, np.uint16)
+    _load().oracle_nvfp4_a16q8_rows(_ptr(c), _ptr(s), scale2, k, _ptr(qa), _ptr(da), _ptr(r), r.size, _ptr(y32),
+                                    _ptr(y16))
+    return y32, y16

@@ -616,6 +616,97 @@ ORACLE_API void oracle_q4k_w4a8_rows(const uint8_t *blocks, int64_t k, const int
 }
 
 /* ------------------------------------------------------------------ */
+/* NVFP4 x Q8_K, integer-exact ("a16_q8")                              */
+/* ------------------------------------------------------------------ */
+
+/* E2M1 element as an integer in units of 2^-1 (Q1): 2 * e2m1(code), one of
+ * 0, +-1, +-2, +-3, +-4, +-6, +-8, +-12. [NV] section 7.4.2. */
+ORACLE_API int oracle_e2m1_q1(unsigned code) { return (int)(2.0 * oracle_e2m1(code & 15u)); }
+
+/* E4M3FN scale as an integer in units of 2^-9 (Q9): every finite E4M3FN
+ * value is a multiple of 2^-9 (the smallest subnormal), up to 448 * 512.
+ * The two NaN encodings have no Q9 value; they give 0 here and are rejected
+ * by load-time validation. [NV] section 7.4.2. */
+ORACLE_API int64_t oracle_e4m3fn_q9(unsigned b)
+{
+    double v = oracle_e4m3fn(b);
+    if (v != v)
+        return 0;
+    return (int64_t)(v * 512.0);
+}
+
+/* binary32 to IEEE binary16 bits, round to nearest even; magnitudes from
+ * 65520 up become infinity; subnormals are kept; NaN stays NaN (quiet). */
+ORACLE_API unsigned oracle_f16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    unsigned sign = (u >> 16) & 0x8000u;
+    double a = fabs((double)f);
+    if (a != a)
+        return sign | 0x7E00u;
+    if (a >= 65520.0)
+        return sign | 0x7C00u;
+    if (a < 0x1p-14) {
+        /* subnormal range: an integer count of 2^-24; 1024 is the smallest normal */
+        return sign | (unsigned)nearbyint(a * 0x1p24);
+    }
+    int e;
+    double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+    double frac = nearbyint((m * 2.0 - 1.0) * 1024.0);
+    e -= 1; /* a = (1 + frac / 1024) * 2^e */
+    if (frac == 1024.0) {
+        frac = 0.0;
+        e += 1;
+    }
+    if (e + 15 >= 31)
+        return sign | 0x7C00u;
+    return sign | ((unsigned)(e + 15) << 10) | (unsigned)frac;
+}
+
+/* Rows of the integer-exact NVFP4 decode of [NV] section 7.4.2 against
+ * Q8_K activations (q int8 [k], d = 1 / iscale per 256, from
+ * oracle_q8_quantize): for each 256-element block b of the row,
+ *   total_b = sum over its 16 groups g of
+ *             (sum over the group of Q1(code) * q) * Q9(scale_g)
+ * in int64 (exact, so the order of the additions does not matter), then
+ * exactly these binary32 steps, blocks in ascending order from +0:
+ *   c = fma(float(total_b), 2^-10, 0)     (Q1 x Q9 units)
+ *   c = fma(c, d_b, 0)                     (activation scale 1 / iscale)
+ *   c = fma(c, scale2, 0)                  (tensor scale)
+ *   acc = fma(1, c, acc)
+ * y32[i] = acc, y16[i] = binary16 bits of acc (round to nearest even).
+ * Codes u8 [n][k/2] (low nibble = even element), scales u8 [n][k/16];
+ * k a multiple of 256. */
+ORACLE_API void oracle_nvfp4_a16q8_rows(const uint8_t *codes, const uint8_t *scales, float scale2, int64_t k,
+                                        const int8_t *q, const float *d, const int64_t *rows, int64_t nrows,
+                                        float *y32, uint16_t *y16)
+{
+    for (int64_t ri = 0; ri < nrows; ++ri) {
+        const uint8_t *crow = codes + rows[ri] * (k / 2);
+        const uint8_t *srow = scales + rows[ri] * (k / 16);
+        float acc = 0.0f;
+        for (int64_t b = 0; b < k / 256; ++b) {
+            int64_t total = 0;
+            for (int g = 0; g < 16; ++g) {
+                int64_t dot = 0;
+                for (int i = 0; i < 16; ++i) {
+                    int64_t e = 256 * b + 16 * g + i;
+                    dot += (int64_t)oracle_e2m1_q1(nibble_lo_even(crow, e)) * q[e];
+                }
+                total += dot * oracle_e4m3fn_q9(srow[16 * b + g]);
+            }
+            float c = fmaf((float)total, 0x1p-10f, 0.0f);
+            c = fmaf(c, d[b], 0.0f);
+            c = fmaf(c, scale2, 0.0f);
+            acc = fmaf(1.0f, c, acc);
+        }
+        y32[ri] = acc;
+        y16[ri] = (uint16_t)oracle_f16_rne(acc);
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Encode-side helpers used only to reproduce the pages' worked facts  */
 /* ------------------------------------------------------------------ */
 
