@@ -72,6 +72,12 @@ WORKLOADS = {
         desc="W4A8 decode: int8 quantization of x f32 [4096] (scale per 256) + Q4_K x int8 GEMV 14336x4096, y f32",
         bytes=14336 * 16 * 144 + 4096 * 4 + 2 * (4096 + 16 * 4 + 128 * 4) + 14336 * 4,
         kernel_bytes=14336 * 16 * 144 + 4096 + 16 * 4 + 128 * 4 + 14336 * 4),
+    "nvfp4_a16q8_gemv": dict(
+        cfg=2, kind="a16q8", unit="GB/s", dtype="i64",
+        desc="integer-exact NVFP4 decode: Q8_K quantization of x bf16 [4096] + NVFP4 4096x4096 x int8 GEMV "
+             "(exact block totals, pinned binary32 epilogue), y f16",
+        bytes=4096 * 2048 + 4096 * 256 + 4096 * 2 + 2 * (4096 + 16 * 4 + 128 * 4) + 4096 * 2,
+        kernel_bytes=4096 * 2048 + 4096 * 256 + 4096 + 16 * 4 + 4096 * 2),
     "mxfp4_gemm": dict(
         cfg=4, kind="gemm", unit="TFLOP/s",
         desc="MXFP4 prefill GEMM: W 8192x8192 (E2M1, E8M0 per 32) x X bf16 2048x8192 -> Y bf16, fp32 accumulate",
@@ -147,17 +153,22 @@ def build_steps(name, spec, dev):
 
     inp = workloads.workload(spec["cfg"])
     calls = []
-    if spec["kind"] == "w4a8":
+    if spec["kind"] in ("w4a8", "a16q8"):
         n, k = inp["n"], inp["k"]
-        R = max(1, math.ceil(ROTATE_BYTES / inp["data"].nbytes))
+        wbytes = inp["data"].nbytes + (0 if inp["scales"] is None else inp["scales"].nbytes)
+        R = max(1, math.ceil(ROTATE_BYTES / wbytes))
         d0 = host_to_device(inp["data"], dev)
+        s0 = None if inp["scales"] is None else host_to_device(inp["scales"], dev)
         x = host_to_device(inp["x"], dev)
+        if inp["x"].dtype == np.uint16:
+            x = x.view(torch.bfloat16)
         q = torch.empty(k, dtype=torch.int8, device=dev)
         dx = torch.empty(k // 256, dtype=torch.float32, device=dev)
         bs = torch.empty(k // 32, dtype=torch.int32, device=dev)
-        y = torch.empty(n, dtype=torch.float32, device=dev)
+        y = torch.empty(n, dtype=torch.float32 if spec["kind"] == "w4a8" else torch.float16, device=dev)
         quant = qbn.prepare_quantize_q8(x, q, dx, bs)
-        gemvs = [qbn.prepare_gemv_q8(qbn.QTensor("q4_k", n, k, d0.clone()), q, dx, bs, y) for _ in range(R)]
+        gemvs = [qbn.prepare_gemv_q8(qbn.QTensor(inp["fmt"], n, k, d0.clone(), None if s0 is None else s0.clone(),
+                                                 scale2=inp["scale2"]), q, dx, bs, y) for _ in range(R)]
 
         def step(g):
             def run():
@@ -238,6 +249,20 @@ def cpu_baseline(name, spec, inp, budget_s):
         t = float(np.median(reps))
         return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
                     sample="full quantize + %dx%d W4A8 GEMV, median of %d runs (%.2f s each)" % (n, k, len(reps), t))
+    if spec["kind"] == "a16q8":
+        n, k = inp["n"], inp["k"]
+        rows = np.arange(n)
+        while True:
+            t0 = time.perf_counter()
+            q, d, _ = oracle.q8_quantize(inp["x"])
+            oracle.nvfp4_a16q8_rows(inp["data"], inp["scales"], inp["scale2"], k, q, d, rows)
+            reps.append(time.perf_counter() - t0)
+            if time.perf_counter() > t_end and len(reps) >= 3:
+                break
+        t = float(np.median(reps))
+        return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                    sample="full quantize + %dx%d integer-exact NVFP4 decode, median of %d runs (%.2f s each)"
+                    % (n, k, len(reps), t))
     if spec["kind"] == "gemv":
         fmt = {"mxfp4": oracle.MXFP4, "nvfp4": oracle.NVFP4, "q4_k": oracle.Q4_K}[inp["fmt"]]
         n, k = inp["n"], inp["k"]
@@ -410,7 +435,7 @@ def main():
         achieved = spec.get("kernel_bytes", spec["bytes"]) / (kernel_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=recorded_traffic(args.workload))
-        metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] in ("gemv", "w4a8") else (
+        metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] in ("gemv", "w4a8", "a16q8") else (
             "int4 repack GB/s (% HBM peak)" if spec["kind"] == "repack" else "bulk dequant GB/s (% HBM peak)")
 
     cpu = None
@@ -438,7 +463,7 @@ def main():
             "step_bytes": spec["bytes"],
             **({"step_flops": spec["flops"]} if "flops" in spec else {}),
             **({"kernel_bytes": spec["kernel_bytes"], "kernel_note": "roofline is the GEMV kernel alone, timed "
-                "in its own graph of K launches; value is the whole step (quantize + GEMV)"}
+                "in its own graph of K launches; value is the whole step (activation quantization + GEMV)"}
                if "kernel_bytes" in spec else {}),
             "kernel_ms_per_launch": round(kernel_ms, 6),
             "kernel_ms_other_replays": [round(v, 6) for v in spread],

@@ -198,9 +198,12 @@ def quantize_q8(x: torch.Tensor, q: Optional[torch.Tensor] = None, d: Optional[t
     return q, d, bsums
 
 
-def quantized_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: torch.Tensor,
+def quantized_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: Optional[torch.Tensor] = None,
                       y: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y = W_hat @ (d * q) (float32 [n]) for a Q4_K weight and activations from quantize_q8."""
+    """GEMV against Q8_K activations from quantize_q8. Q4_K: y = W_hat @ (d * q),
+    float32 [n] (bsums required). NVFP4: the integer-exact decode with the
+    pinned binary32 epilogue, rounded to binary16; y float16 or float32 [n]
+    (default float32)."""
     lib = _load()
     if y is None:
         y = torch.empty(w.n, dtype=torch.float32, device=w.device)
@@ -323,7 +326,8 @@ def prepare_quantize_q8(x: torch.Tensor, q: torch.Tensor, d: torch.Tensor, bsums
     return Prepared(lib.qbn_quantize_q8, args, "qbn_quantize_q8", x.device, (x, q, d, bsums))
 
 
-def prepare_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: torch.Tensor, y: torch.Tensor) -> Prepared:
+def prepare_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: Optional[torch.Tensor],
+                    y: torch.Tensor) -> Prepared:
     lib = _load()
     ct = w._c()
     args = (ctypes.byref(ct), _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"), _ptr(y, "y"),

@@ -164,16 +164,20 @@ int32_t qbn_quantized_gemv_q8(const qbn_tensor *w, const int8_t *q, const float 
                               int32_t y_dtype, void *stream) {
     int32_t st = check_tensor(w);
     if (st) return st;
-    if (w->format != QBN_Q4_K) return QBN_ERR_UNSUPPORTED;
+    const bool q4k = w->format == QBN_Q4_K;
+    if (!q4k && w->format != QBN_NVFP4) return QBN_ERR_UNSUPPORTED;
+    if (!q4k && w->k % 256) return QBN_ERR_SHAPE;  // one activation scale per 256
     if (y_dtype < QBN_F32 || y_dtype > QBN_F16) return QBN_ERR_FORMAT;
-    if (y_dtype != QBN_F32) return QBN_ERR_DTYPE;
+    if (y_dtype == QBN_BF16 || (q4k && y_dtype != QBN_F32)) return QBN_ERR_DTYPE;
     if (w->n == 0) return QBN_OK;
     if (!y) return QBN_ERR_NULL;
-    if (!aligned(y, 4)) return QBN_ERR_ALIGN;
+    const int64_t ysize = y_dtype == QBN_F16 ? 2 : 4;
+    if (!aligned(y, (uintptr_t)ysize)) return QBN_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    if (w->k == 0) return hip_status(qbn::launch_fill_zero(y, 4 * w->n, s));
-    if (!q || !d || !bsums) return QBN_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(d, 4) || !aligned(bsums, 8)) return QBN_ERR_ALIGN;
+    if (w->k == 0) return hip_status(qbn::launch_fill_zero(y, ysize * w->n, s));
+    if (!q || !d || (q4k && !bsums)) return QBN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(d, 4) || (q4k && !aligned(bsums, 8))) return QBN_ERR_ALIGN;
+    if (!q4k) return hip_status(qbn::launch_gemv_a16q8(*w, q, d, y, y_dtype, s));
     return hip_status(qbn::launch_gemv_q8(*w, q, d, bsums, (float *)y, s));
 }
 

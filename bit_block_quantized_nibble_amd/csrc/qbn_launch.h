@@ -20,6 +20,8 @@ hipError_t launch_quantize_q8(const void *x, int x_dtype, int64_t k, int8_t *q, 
                               hipStream_t s);
 hipError_t launch_gemv_q8(const qbn_tensor &w, const int8_t *q, const float *d, const int32_t *bsums, float *y,
                           hipStream_t s);
+hipError_t launch_gemv_a16q8(const qbn_tensor &w, const int8_t *q, const float *d, void *y, int y_dtype,
+                             hipStream_t s);
 hipError_t launch_fill_zero(void *out, int64_t bytes, hipStream_t s);
 hipError_t launch_fill_zero_2d_u16(void *out, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
 

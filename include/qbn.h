@@ -168,16 +168,31 @@ QBN_API int32_t qbn_quantized_gemv(const qbn_tensor *w, const void *x, int32_t x
 QBN_API int32_t qbn_quantize_q8(const void *x, int32_t x_dtype, int64_t k, int8_t *q, float *d, int32_t *bsums,
                                 void *stream);
 
-/* y[r] = sum_i W_hat[r][i] * d[i / 256] * q[i]  for r in 0..n: the Q4_K x int8
- * decode GEMV of the W4A8 route ([WK] section 7, section 7b step 4 and
- * section 7c), with q, d, bsums as written by qbn_quantize_q8 for the same k.
- * Formats: Q4_K. y: QBN_F32 [n]. W_hat is d*s_j*q - dmin*m_j taken exactly.
- * Per sub-block the codes meet in 4 x int8 integer dots; per block the
- * integer sums are scaled as d * sum_j s_j dot_j - dmin * sum_j m_j bsums_j in
- * binary64 (both products exact, one rounding), times d[b]; the lane sums
- * are added in binary32 in a fixed order (repeated calls are bit-identical).
- * Each y[r] satisfies |y - y_exact| <= 1e-5 * sum_i |W_hat[r][i] x_hat[i]| + 1e-6
- * with x_hat = d[i / 256] * q[i]. Alignment: q 16 bytes, d 4, bsums 8, y 4. */
+/* Decode GEMV against Q8_K activations (q, d, bsums as written by
+ * qbn_quantize_q8 for the same k), for r in 0..n:
+ *
+ * Q4_K, the W4A8 route ([WK] section 7, section 7b step 4, section 7c):
+ *   y[r] = sum_i W_hat[r][i] * d[i / 256] * q[i],  y QBN_F32 [n], bsums
+ *   required. W_hat is d*s_j*q - dmin*m_j taken exactly. Per sub-block the
+ *   codes meet in 4 x int8 integer dots; per block the integer sums are
+ *   scaled as d * sum_j s_j dot_j - dmin * sum_j m_j bsums_j in binary64
+ *   (both products exact, one rounding), times d[b]; the lane sums are added
+ *   in binary32 in a fixed order (repeated calls are bit-identical). Each
+ *   y[r] satisfies |y - y_exact| <= 1e-5 * sum_i |W_hat[r][i] x_hat[i]| + 1e-6
+ *   with x_hat = d[i / 256] * q[i].
+ *
+ * NVFP4, the integer-exact decode ([NV] section 7.4.2): k % 256 == 0;
+ *   bsums unused (may be NULL). Per 256-block b of the row, the integer
+ *   T_b = sum over its 16-groups of (sum Q1(code) * q) * Q9(scale), with
+ *   Q1 = 2 * e2m1 and Q9 = 512 * e4m3fn, is formed exactly; then, blocks
+ *   ascending from acc = +0, exactly these binary32 steps:
+ *     c = fma(float(T_b), 2^-10, 0); c = fma(c, d[b], 0);
+ *     c = fma(c, scale2, 0); acc = fma(1, c, acc);
+ *   and y[r] = acc rounded to binary16 (nearest even): QBN_F16 [n] stores it,
+ *   QBN_F32 [n] stores its binary32 value. The result is bit-exact and
+ *   independent of the machine's reduction order.
+ *
+ * Alignment: q 16 bytes, d 4, bsums 8, y 4 (QBN_F32) or 2 (QBN_F16). */
 QBN_API int32_t qbn_quantized_gemv_q8(const qbn_tensor *w, const int8_t *q, const float *d, const int32_t *bsums,
                                       void *y, int32_t y_dtype, void *stream);
 

@@ -133,6 +133,17 @@ def test_gemv_q8_rejections(lib):
     assert g(T(QK, 4, 256), A, B, C + 4, A, F32, None) == ALIGN
     assert g(T(QK, 4, 256, data=A + 8), A, B, C, A, F32, None) == ALIGN
     assert g(T(QK, 0, 256, data=None), None, None, None, None, F32, None) == OK
+    # NVFP4: the integer-exact route; k in whole 256-blocks, bsums unused, f16 or f32 output
+    F16 = 2
+    assert g(T(NV, 4, 272), A, B, None, A, F32, None) == SHAPE
+    assert g(T(NV, 4, 256), A, B, None, A, BF16, None) == DTYPE
+    assert g(T(NV, 4, 256, scale2=0.0), A, B, None, A, F32, None) == SCALE2
+    assert g(T(NV, 4, 256, scales=None), A, B, None, A, F32, None) == NULL
+    assert g(T(NV, 4, 256), A, B, None, A + 2, F32, None) == ALIGN
+    assert g(T(NV, 4, 256), A, B, None, A + 1, F16, None) == ALIGN
+    assert g(T(NV, 4, 256), A + 8, B, None, A, F16, None) == ALIGN
+    assert g(T(NV, 4, 256), A, None, None, A, F16, None) == NULL
+    assert g(T(QK, 4, 256), A, B, C, A, F16, None) == DTYPE
 
 
 def test_gemm_rejections(lib):
