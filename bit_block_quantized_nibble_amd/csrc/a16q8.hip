@@ -135,18 +135,22 @@ __device__ __forceinline__ void load_arow(ARow<BPL> &r, const uint8_t *__restric
     for (int j = 0; j < BPL; ++j) load_afrag(r.f[j], codes, scales, row, k, min((int64_t)(slot + 16 * j), nb - 1), c);
 }
 
-template <int BPL>
+// FULL: nb == 16 * BPL, so every slot holds a real block.
+template <int BPL, bool FULL = false>
 __device__ __forceinline__ float row_sum(const ARow<BPL> &r, const QPairs *x, float scale2, int64_t nb) {
     float cb[BPL];
 #pragma unroll
     for (int j = 0; j < BPL; ++j) cb[j] = block_contribution(lane_total(r.f[j], x[j]), x[j].d, scale2);
+    // Blocks past nb add +0, which leaves acc unchanged (acc is never -0:
+    // every contribution is an fma with a +0 addend).
     float acc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < BPL; ++j) {
-        const int ns = (int)min((int64_t)16, nb - 16 * j);
-        for (int s = 0; s < ns; ++s)
-            acc = acc + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cb[j]), 4 * s));
-    }
+    for (int j = 0; j < BPL; ++j)
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cb[j]), 4 * s));
+            acc = acc + ((FULL || 16 * j + s < nb) ? v : 0.0f);
+        }
     return acc;
 }
 
@@ -186,6 +190,36 @@ __global__ __launch_bounds__(WPB * 64) void k_gemv_nvfp4_a16q8(const uint8_t *__
     if (i < m) {
         const float v = row_sum<BPL>(r0, x, scale2, nb);
         if (lane == 0) put_y<YT>(y, (uint32_t)(start + i), v);
+    }
+}
+
+// One-shot form for rows of at most 16 blocks: a wave owns R consecutive
+// rows and requests all of their codes and scales before its activations
+// (at these sizes this is as fast as the row loop, whose prefetch has few
+// rows per wave to work with). Rows past n re-read row n-1 and are not
+// stored.
+template <int R, int WPB, bool FULL, typename YT>
+__global__ __launch_bounds__(WPB * 64) void k_gemv_nvfp4_a16q8_rows(const uint8_t *__restrict__ codes,
+                                                                    const uint8_t *__restrict__ scales, float scale2,
+                                                                    const int8_t *__restrict__ q,
+                                                                    const float *__restrict__ d, YT *__restrict__ y,
+                                                                    int64_t n, int64_t k) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int c = lane & 3;
+    const int slot = lane >> 2;
+    const int64_t nb = k / 256;
+    const int64_t row0 = ((int64_t)blockIdx.x * WPB + threadIdx.x / kWave) * R;
+    if (row0 >= n) return;  // whole waves only; no barrier follows
+    const int64_t b = min((int64_t)slot, nb - 1);
+    ARow<1> rr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_arow<1>(rr[r], codes, scales, (uint32_t)min(row0 + r, n - 1), k, nb, slot, c);
+    QPairs x[1];
+    load_qpairs(x[0], q, d, b, c);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float v = row_sum<1, FULL>(rr[r], x, scale2, nb);
+        if (lane == 0 && row0 + r < n) put_y<YT>(y, (uint32_t)(row0 + r), v);
     }
 }
 
@@ -232,11 +266,21 @@ hipError_t run_a16q8(const qbn_tensor &w, const int8_t *q, const float *d, YT *y
     return hipGetLastError();
 }
 
+template <int R, int WPB, bool FULL, typename YT>
+hipError_t run_a16q8_rows(const qbn_tensor &w, const int8_t *q, const float *d, YT *y, hipStream_t s) {
+    const int64_t waves = (w.n + R - 1) / R;
+    hipLaunchKernelGGL((k_gemv_nvfp4_a16q8_rows<R, WPB, FULL, YT>), dim3((unsigned)((waves + WPB - 1) / WPB)),
+                       dim3(WPB * kWave), 0, s, (const uint8_t *)w.data, (const uint8_t *)w.scales, w.scale2, q, d, y,
+                       w.n, w.k);
+    return hipGetLastError();
+}
+
 template <typename YT>
 hipError_t launch_a16q8_typed(const qbn_tensor &w, const int8_t *q, const float *d, YT *y, hipStream_t s) {
     const int64_t nb = w.k / 256;
     if (w.n < ((int64_t)1 << 31)) {  // 32-bit row indices in the row-loop kernel
-        if (nb <= 16) return run_a16q8<1, 4, 3, YT>(w, q, d, y, s);
+        if (nb == 16) return run_a16q8_rows<2, 8, true, YT>(w, q, d, y, s);
+        if (nb < 16) return run_a16q8_rows<2, 8, false, YT>(w, q, d, y, s);
         if (nb <= 32) return run_a16q8<2, 4, 2, YT>(w, q, d, y, s);
     }
     const int64_t grid = (w.n + 3) / 4;
