@@ -32,6 +32,7 @@ _BUILD = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_BUILD, "liboracle.so")
 
 MXFP4, NVFP4, Q4_K, Q4_0 = 1, 2, 3, 4
+MXFP8 = 7  # activation format: E4M3FN elements, E8M0 scale per 32
 
 _lock = threading.Lock()
 _lib = None
@@ -108,6 +109,14 @@ def _load():
         lib.oracle_f16_rne.argtypes = [ctypes.c_float]
         lib.oracle_f16_rne.restype = ctypes.c_uint
         lib.oracle_nvfp4_a16q8_rows.argtypes = [P, P, ctypes.c_float, I64, P, P, P, I64, P, P]
+        lib.oracle_e2m1_rne.argtypes = [ctypes.c_double]
+        lib.oracle_e2m1_rne.restype = ctypes.c_uint
+        lib.oracle_e4m3fn_rne.argtypes = [ctypes.c_double]
+        lib.oracle_e4m3fn_rne.restype = ctypes.c_uint
+        lib.oracle_mx_quantize.argtypes = [P, ctypes.c_int, I64, I64, I64, ctypes.c_int, P, P]
+        lib.oracle_mx_quantize.restype = ctypes.c_int
+        lib.oracle_mx_gemm_entries.argtypes = [P, P, I64, ctypes.c_int, P, P, P, P, I64, P, P]
+        lib.oracle_mx_gemm_entries.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -425,3 +434,50 @@ def nvfp4_a16q8_rows(codes, scales, scale2: float, k: int, q: np.ndarray, d: np.
     _load().oracle_nvfp4_a16q8_rows(_ptr(c), _ptr(s), scale2, k, _ptr(qa), _ptr(da), _ptr(r), r.size, _ptr(y32),
                                     _ptr(y16))
     return y32, y16
+
+
+# ---------------------------------------------------------------- MX activations and the MX x MX product
+
+def e2m1_rne(v: float) -> int:
+    return _load().oracle_e2m1_rne(v)
+
+
+def e4m3fn_rne(v: float) -> int:
+    return _load().oracle_e4m3fn_rne(v)
+
+
+def mx_quantize(X: np.ndarray, xfmt: int):
+    """(codes, scales) of X [m][k] (float32, or bfloat16 bits as uint16) quantized
+    to MX: xfmt MXFP4 -> E2M1 codes u8 [m][k/2]; MXFP8 -> E4M3FN bytes u8 [m][k];
+    E8M0 scales u8 [m][k/32]."""
+    Xa = np.ascontiguousarray(X)
+    if Xa.ndim == 1:
+        Xa = Xa[None, :]
+    xdt = 1 if Xa.dtype == np.uint16 else 0
+    if xdt == 0:
+        Xa = np.ascontiguousarray(Xa, dtype=np.float32)
+    m, k = Xa.shape
+    assert k % 32 == 0
+    codes = np.zeros((m, k // 2 if xfmt == MXFP4 else k), np.uint8)
+    scales = np.zeros((m, k // 32), np.uint8)
+    rc = _load().oracle_mx_quantize(_ptr(Xa), xdt, m, k, k, xfmt, _ptr(codes), _ptr(scales))
+    if rc:
+        raise ValueError("oracle: unsupported MX element format %r" % xfmt)
+    return codes, scales
+
+
+def mx_gemm_entries(wcodes, wscales, k: int, xfmt: int, xcodes, xscales, ms, ns):
+    """(Y, S) in binary64 for entries (ms[i], ns[i]) of X_hat @ W_hat^T."""
+    wc = np.ascontiguousarray(wcodes).view(np.uint8)
+    ws = np.ascontiguousarray(wscales).view(np.uint8)
+    xc = np.ascontiguousarray(xcodes).view(np.uint8)
+    xs = np.ascontiguousarray(xscales).view(np.uint8)
+    ms = np.ascontiguousarray(np.asarray(ms, dtype=np.int64))
+    ns = np.ascontiguousarray(np.asarray(ns, dtype=np.int64))
+    y = np.zeros(ms.size, np.float64)
+    sa = np.zeros(ms.size, np.float64)
+    rc = _load().oracle_mx_gemm_entries(_ptr(wc), _ptr(ws), k, xfmt, _ptr(xc), _ptr(xs), _ptr(ms), _ptr(ns), ms.size,
+                                        _ptr(y), _ptr(sa))
+    if rc:
+        raise ValueError("oracle: unsupported MX element format %r" % xfmt)
+    return y, sa

@@ -707,6 +707,145 @@ ORACLE_API void oracle_nvfp4_a16q8_rows(const uint8_t *codes, const uint8_t *sca
 }
 
 /* ------------------------------------------------------------------ */
+/* MX activations (OCP MX: E8M0 scale per 32) and the MX x MX product  */
+/* ------------------------------------------------------------------ */
+
+/* Nearest E2M1 code to v (already divided by the block scale), ties to the
+ * even code (the OCP MX conversion rounds ties to even), magnitudes above
+ * 6 saturate to 6. The sign of zero follows v. [FB] section 1 (the grid). */
+ORACLE_API unsigned oracle_e2m1_rne(double v)
+{
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    unsigned sign = signbit(v) ? 8u : 0u;
+    double a = fabs(v);
+    unsigned best = 0;
+    for (unsigned c = 1; c < 8; ++c) {
+        double dc = fabs(a - grid[c]), db = fabs(a - grid[best]);
+        if (dc < db || (dc == db && (c & 1u) == 0))
+            best = c;
+    }
+    return sign | best;
+}
+
+/* Nearest E4M3FN byte to v, ties to even, magnitudes above 448 saturate to
+ * 448 (0x7E); subnormals kept. [FB] section 4 (the format). */
+ORACLE_API unsigned oracle_e4m3fn_rne(double v)
+{
+    unsigned sign = signbit(v) ? 0x80u : 0u;
+    double a = fabs(v);
+    if (a >= 448.0)
+        return sign | 0x7Eu;
+    if (a < 0x1p-6) /* subnormal range: a multiple of 2^-9 */
+        return sign | (unsigned)nearbyint(a * 512.0); /* 8 -> 0x08, the smallest normal */
+    int e;
+    double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+    double f = nearbyint((m * 2.0 - 1.0) * 8.0);
+    e -= 1;
+    if (f == 8.0) {
+        f = 0.0;
+        e += 1;
+    }
+    if (e > 8)
+        return sign | 0x7Eu;
+    return sign | ((unsigned)(e + 7) << 3) | (unsigned)f;
+}
+
+/* MX quantization of the rows of X [m][k] (binary32 or bfloat16 bits, row
+ * stride ldx elements), k a multiple of 32, following the OCP MX
+ * specification that [FB] section 3 and [WK] section 5 name as the contract:
+ * per 32 consecutive elements, shared exponent e = floor(log2(max |x|)) -
+ * emax (emax 2 for E2M1, 8 for E4M3), clamped to [-127, 127] (-127 for an
+ * all-zero block); scale byte e + 127; each element quantized from x / 2^e to
+ * the element grid with ties to even and saturation.
+ * xfmt 1: E2M1 elements, codes [m][k/2] (low nibble = even element);
+ * xfmt 7: E4M3FN elements, codes [m][k]. Scales [m][k/32]. */
+ORACLE_API int oracle_mx_quantize(const void *x, int xdtype, int64_t m, int64_t k, int64_t ldx, int xfmt,
+                                  uint8_t *codes, uint8_t *scales)
+{
+    if (xfmt != 1 && xfmt != 7)
+        return 1;
+    int emax = xfmt == 1 ? 2 : 8;
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t b = 0; b < k / 32; ++b) {
+            double v[32];
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j) {
+                int64_t e = i * ldx + 32 * b + j;
+                v[j] = xdtype == 1 ? oracle_bf16_value(((const uint16_t *)x)[e]) : (double)((const float *)x)[e];
+                if (fabs(v[j]) > amax)
+                    amax = fabs(v[j]);
+            }
+            int se = -127;
+            if (amax > 0.0) {
+                int fe;
+                frexp(amax, &fe); /* amax = f * 2^fe, f in [0.5, 1): floor(log2 amax) = fe - 1 */
+                se = fe - 1 - emax;
+                if (se < -127)
+                    se = -127;
+                if (se > 127)
+                    se = 127;
+            }
+            scales[i * (k / 32) + b] = (uint8_t)(se + 127);
+            for (int j = 0; j < 32; ++j) {
+                double t = ldexp(v[j], -se);
+                int64_t e = 32 * b + j;
+                if (xfmt == 1) {
+                    unsigned c = oracle_e2m1_rne(t);
+                    uint8_t *p = codes + i * (k / 2) + e / 2;
+                    if (e % 2 == 0)
+                        *p = (uint8_t)((*p & 0xF0u) | c);
+                    else
+                        *p = (uint8_t)((*p & 0x0Fu) | (c << 4));
+                } else {
+                    codes[i * k + e] = (uint8_t)oracle_e4m3fn_rne(t);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* Value of element e of an MX-quantized row (exact in binary64). */
+static double mx_value(int xfmt, const uint8_t *codes_row, const uint8_t *scales_row, int64_t e)
+{
+    double s = oracle_e8m0(scales_row[e / 32]);
+    if (xfmt == 1)
+        return oracle_e2m1(nibble_lo_even(codes_row, e)) * s;
+    return oracle_e4m3fn(codes_row[e]) * s;
+}
+
+/* Entries (ms[i], ns[i]) of Y = X_hat W_hat^T for MX-quantized activations
+ * (xfmt 1 or 7, as above) and MXFP4 weights W [n][k/2] + E8M0 [n][k/32]:
+ * every product is exact in binary64 and the sum is compensated; s[i] =
+ * sum |x_hat w_hat|. */
+ORACLE_API int oracle_mx_gemm_entries(const uint8_t *wcodes, const uint8_t *wscales, int64_t k, int xfmt,
+                                      const uint8_t *xcodes, const uint8_t *xscales, const int64_t *ms,
+                                      const int64_t *ns, int64_t count, double *y, double *sabs)
+{
+    if (xfmt != 1 && xfmt != 7)
+        return 1;
+    int64_t xrow = xfmt == 1 ? k / 2 : k;
+    for (int64_t t = 0; t < count; ++t) {
+        const uint8_t *xc = xcodes + ms[t] * xrow, *xs = xscales + ms[t] * (k / 32);
+        const uint8_t *wc = wcodes + ns[t] * (k / 2), *ws = wscales + ns[t] * (k / 32);
+        double sum = 0.0, comp = 0.0, sa = 0.0;
+        for (int64_t e = 0; e < k; ++e) {
+            double p = mx_value(xfmt, xc, xs, e) * (oracle_e2m1(nibble_lo_even(wc, e)) * oracle_e8m0(ws[e / 32]));
+            double u = sum + p;
+            if (fabs(sum) >= fabs(p))
+                comp += (sum - u) + p;
+            else
+                comp += (p - u) + sum;
+            sum = u;
+            sa += fabs(p);
+        }
+        y[t] = sum + comp;
+        sabs[t] = sa;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Encode-side helpers used only to reproduce the pages' worked facts  */
 /* ------------------------------------------------------------------ */
 
