@@ -718,6 +718,8 @@ ORACLE_API unsigned oracle_e2m1_rne(double v)
     static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
     unsigned sign = signbit(v) ? 8u : 0u;
     double a = fabs(v);
+    if (a > 6.0)
+        a = 6.0; /* saturate first: for huge a every distance rounds to the same value */
     unsigned best = 0;
     for (unsigned c = 1; c < 8; ++c) {
         double dc = fabs(a - grid[c]), db = fabs(a - grid[best]);

@@ -24,7 +24,8 @@ E2M1 = json.load(open(os.path.join(GOLDEN, "e2m1_codebook.json")))["values"]
 def test_e2m1_rne_facts():
     # midpoints of the E2M1 grid go to the code with an even last bit
     facts = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0,
-             0.2: 0.0, 0.3: 0.5, 2.6: 3.0, 4.9: 4.0, 5.1: 6.0, 6.0: 6.0, 7.0: 6.0, 1e9: 6.0}
+             0.2: 0.0, 0.3: 0.5, 2.6: 3.0, 4.9: 4.0, 5.1: 6.0, 6.0: 6.0, 7.0: 6.0, 1e9: 6.0, 1e30: 6.0,
+             3e38: 6.0}
     for v, want in facts.items():
         assert E2M1[oracle.e2m1_rne(v)] == want, v
         assert E2M1[oracle.e2m1_rne(-v)] == -want, -v
