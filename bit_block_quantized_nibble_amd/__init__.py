@@ -36,7 +36,7 @@ _lib = None
 EXPORTED = (
     "qbn_abi_version", "qbn_tensor_struct_size", "qbn_status_string", "qbn_last_hip_error", "qbn_bytes",
     "qbn_quantized_gemv", "qbn_quantized_gemm", "qbn_dequantize", "qbn_repack", "qbn_validate",
-    "qbn_quantize_q8", "qbn_quantized_gemv_q8",
+    "qbn_quantize_q8", "qbn_quantized_gemv_q8", "qbn_quantize_mx", "qbn_quantized_gemm_mx",
 )
 
 
@@ -93,6 +93,10 @@ def _load():
         lib.qbn_quantize_q8.restype = I32
         lib.qbn_quantized_gemv_q8.argtypes = [T, P, P, P, P, I32, P]
         lib.qbn_quantized_gemv_q8.restype = I32
+        lib.qbn_quantize_mx.argtypes = [P, I32, I64, I64, I64, I32, P, P, P]
+        lib.qbn_quantize_mx.restype = I32
+        lib.qbn_quantized_gemm_mx.argtypes = [T, I64, I32, P, P, P, I32, I64, P]
+        lib.qbn_quantized_gemm_mx.restype = I32
         if lib.qbn_abi_version() != 1 or lib.qbn_tensor_struct_size() != ctypes.sizeof(_CTensor):
             raise RuntimeError("libqbn ABI mismatch: rebuild the library")
         _lib = lib
@@ -211,6 +215,47 @@ def quantized_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: Optio
     _check(lib.qbn_quantized_gemv_q8(ctypes.byref(ct), _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"),
                                      _ptr(y, "y"), _DTYPES.get(y.dtype, -1), _stream(w.device)),
            "qbn_quantized_gemv_q8")
+    return y
+
+
+MX_FORMATS = {"mxfp4": 1, "mxfp8": 7}
+
+
+def quantize_mx(x: torch.Tensor, fmt: str = "mxfp4", codes: Optional[torch.Tensor] = None,
+                scales: Optional[torch.Tensor] = None):
+    """OCP MX quantization of x (float32 or bfloat16 [m][k], rows contiguous):
+    returns (codes u8 [m][k/2] for mxfp4 or [m][k] for mxfp8, E8M0 scales u8 [m][k/32])."""
+    lib = _load()
+    if x.dtype not in _DTYPES:
+        raise TypeError("x dtype %s" % x.dtype)
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a device tensor with contiguous rows")
+    m, k = x.shape
+    if codes is None:
+        codes = torch.empty((m, k // 2 if fmt == "mxfp4" else k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    _check(lib.qbn_quantize_mx(ctypes.c_void_p(x.data_ptr()), _DTYPES[x.dtype], m, k, x.stride(0), MX_FORMATS[fmt],
+                               _ptr(codes, "codes"), _ptr(scales, "scales"), _stream(x.device)), "qbn_quantize_mx")
+    return codes, scales
+
+
+def quantized_gemm_mx(w: QTensor, xcodes: torch.Tensor, xscales: torch.Tensor, fmt: str = "mxfp4",
+                      y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X_hat @ W_hat^T for MX activations (from quantize_mx) and an MXFP4
+    weight, on the FP4 matrix cores. Y bfloat16 (default) or float32 [m][n]."""
+    lib = _load()
+    m = xcodes.shape[0]
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.bfloat16, device=w.device)
+    if not y.is_cuda or y.stride(1) != 1:
+        raise ValueError("y must be a device tensor with contiguous rows")
+    ct = w._c()
+    _check(lib.qbn_quantized_gemm_mx(ctypes.byref(ct), m, MX_FORMATS[fmt], _ptr(xcodes, "xcodes"),
+                                     _ptr(xscales, "xscales"), ctypes.c_void_p(y.data_ptr()), _DTYPES.get(y.dtype, -1),
+                                     y.stride(0), _stream(w.device)), "qbn_quantized_gemm_mx")
     return y
 
 
@@ -333,6 +378,23 @@ def prepare_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: Optiona
     args = (ctypes.byref(ct), _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"), _ptr(y, "y"),
             _DTYPES.get(y.dtype, -1))
     return Prepared(lib.qbn_quantized_gemv_q8, args, "qbn_quantized_gemv_q8", w.device, (w, q, d, bsums, y, ct))
+
+
+def prepare_quantize_mx(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, fmt: str = "mxfp4") -> Prepared:
+    lib = _load()
+    m, k = x.shape
+    args = (ctypes.c_void_p(x.data_ptr()), _DTYPES[x.dtype], m, k, x.stride(0), MX_FORMATS[fmt], _ptr(codes, "codes"),
+            _ptr(scales, "scales"))
+    return Prepared(lib.qbn_quantize_mx, args, "qbn_quantize_mx", x.device, (x, codes, scales))
+
+
+def prepare_gemm_mx(w: QTensor, xcodes: torch.Tensor, xscales: torch.Tensor, y: torch.Tensor,
+                    fmt: str = "mxfp4") -> Prepared:
+    lib = _load()
+    ct = w._c()
+    args = (ctypes.byref(ct), xcodes.shape[0], MX_FORMATS[fmt], _ptr(xcodes, "xcodes"), _ptr(xscales, "xscales"),
+            ctypes.c_void_p(y.data_ptr()), _DTYPES.get(y.dtype, -1), y.stride(0))
+    return Prepared(lib.qbn_quantized_gemm_mx, args, "qbn_quantized_gemm_mx", w.device, (w, xcodes, xscales, y, ct))
 
 
 def prepare_gemm(w: QTensor, x: torch.Tensor, y: torch.Tensor) -> Prepared:

@@ -181,6 +181,48 @@ int32_t qbn_quantized_gemv_q8(const qbn_tensor *w, const int8_t *q, const float 
     return hip_status(qbn::launch_gemv_q8(*w, q, d, bsums, (float *)y, s));
 }
 
+int32_t qbn_quantize_mx(const void *x, int32_t x_dtype, int64_t m, int64_t k, int64_t ldx, int32_t x_format,
+                        void *codes, void *scales, void *stream) {
+    if (x_format != QBN_MXFP4 && x_format != QBN_MXFP8) return x_format >= QBN_MXFP4 && x_format <= QBN_AWQ4
+                                                                   ? QBN_ERR_UNSUPPORTED
+                                                                   : QBN_ERR_FORMAT;
+    if (x_dtype < QBN_F32 || x_dtype > QBN_F16) return QBN_ERR_FORMAT;
+    if (x_dtype != QBN_F32 && x_dtype != QBN_BF16) return QBN_ERR_DTYPE;
+    if (m < 0 || k < 0 || k % 32 || m > kMaxElems || k > kMaxElems || (m > 0 && k > kMaxElems / m))
+        return QBN_ERR_SHAPE;
+    if (m == 0 || k == 0) return QBN_OK;
+    if (ldx < k || ldx > kMaxElems / m) return QBN_ERR_SHAPE;
+    if (!x || !codes || !scales) return QBN_ERR_NULL;
+    if (ldx % 4 || !aligned(x, x_dtype == QBN_F32 ? 16 : 8)) return QBN_ERR_ALIGN;
+    if (!aligned(codes, x_format == QBN_MXFP8 ? 4 : 2)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_quantize_mx(x, x_dtype, m, k, ldx, x_format, codes, scales, (hipStream_t)stream));
+}
+
+int32_t qbn_quantized_gemm_mx(const qbn_tensor *w, int64_t m, int32_t x_format, const void *xcodes,
+                              const void *xscales, void *y, int32_t y_dtype, int64_t ldy, void *stream) {
+    int32_t st = check_tensor(w);
+    if (st) return st;
+    if (w->format != QBN_MXFP4) return QBN_ERR_UNSUPPORTED;
+    if (x_format != QBN_MXFP4) return (x_format == QBN_MXFP8 || known_format(x_format)) ? QBN_ERR_UNSUPPORTED
+                                                                                        : QBN_ERR_FORMAT;
+    if (y_dtype < QBN_F32 || y_dtype > QBN_F16) return QBN_ERR_FORMAT;
+    if (y_dtype != QBN_F32 && y_dtype != QBN_BF16) return QBN_ERR_DTYPE;
+    if (m < 0 || m > kMaxElems) return QBN_ERR_SHAPE;
+    if (m == 0 || w->n == 0) return QBN_OK;
+    if (ldy < w->n || ldy > kMaxElems / m) return QBN_ERR_SHAPE;
+    if (!y) return QBN_ERR_NULL;
+    const int ysz = y_dtype == QBN_F32 ? 4 : 2;
+    if (!aligned(y, (uintptr_t)ysz)) return QBN_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (w->k == 0)
+        return hip_status(ysz == 2 ? qbn::launch_fill_zero_2d_u16(y, m, w->n, ldy, s)
+                                   : qbn::launch_fill_zero_2d_u16(y, m, 2 * w->n, 2 * ldy, s));
+    if (m > kMaxElems / w->k) return QBN_ERR_SHAPE;
+    if (!xcodes || !xscales) return QBN_ERR_NULL;
+    if (!aligned(xcodes, 16)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_gemm_mx(*w, m, x_format, xcodes, xscales, y, y_dtype, ldy, s));
+}
+
 int32_t qbn_quantized_gemm(const qbn_tensor *w, int64_t m, const void *x, int32_t x_dtype, int64_t ldx, void *y,
                            int32_t y_dtype, int64_t ldy, void *stream) {
     int32_t st = check_tensor(w);

@@ -22,6 +22,10 @@ hipError_t launch_gemv_q8(const qbn_tensor &w, const int8_t *q, const float *d, 
                           hipStream_t s);
 hipError_t launch_gemv_a16q8(const qbn_tensor &w, const int8_t *q, const float *d, void *y, int y_dtype,
                              hipStream_t s);
+hipError_t launch_quantize_mx(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int x_format,
+                              void *codes, void *scales, hipStream_t s);
+hipError_t launch_gemm_mx(const qbn_tensor &w, int64_t m, int x_format, const void *xcodes, const void *xscales,
+                          void *y, int y_dtype, int64_t ldy, hipStream_t s);
 hipError_t launch_fill_zero(void *out, int64_t bytes, hipStream_t s);
 hipError_t launch_fill_zero_2d_u16(void *out, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
 

@@ -100,7 +100,8 @@ typedef enum qbn_format {
     QBN_Q4_K = 3,
     QBN_Q4_0 = 4,
     QBN_GPTQ4 = 5,
-    QBN_AWQ4 = 6
+    QBN_AWQ4 = 6,
+    QBN_MXFP8 = 7 /* activations only (qbn_quantize_mx): E4M3FN elements, one E8M0 scale per 32 */
 } qbn_format;
 
 typedef enum qbn_dtype {
@@ -204,6 +205,33 @@ QBN_API int32_t qbn_quantized_gemv_q8(const qbn_tensor *w, const int8_t *q, cons
  * with binary32 accumulation, and Y is rounded to bf16 (nearest even). */
 QBN_API int32_t qbn_quantized_gemm(const qbn_tensor *w, int64_t m, const void *x, int32_t x_dtype, int64_t ldx, void *y,
                            int32_t y_dtype, int64_t ldy, void *stream);
+
+/* MX activation quantization (the OCP MX contract named by [FB] section 3
+ * and [WK] section 5): X [m][ldx] (QBN_F32 or QBN_BF16, finite values),
+ * k % 32 == 0, ldx >= k, ldx % 4 == 0. Per 32 consecutive elements of a row:
+ *   e = floor(log2 max|x|) - emax (emax 2 for E2M1, 8 for E4M3), clamped to
+ *   [-127, 127] (-127 for an all-zero block); scales[i][b] = e + 127 (E8M0);
+ *   each element is x * 2^-e rounded to the element grid, ties to even,
+ *   magnitudes past the largest finite value saturating to it.
+ * x_format QBN_MXFP4: E2M1 codes [m][k/2] (low nibble = even element),
+ * codes 2-byte aligned; QBN_MXFP8: E4M3FN bytes [m][k], 4-byte aligned.
+ * scales u8 [m][k/32]. x 16-byte (f32) or 8-byte (bf16) aligned. Bit-exact. */
+QBN_API int32_t qbn_quantize_mx(const void *x, int32_t x_dtype, int64_t m, int64_t k, int64_t ldx, int32_t x_format,
+                                void *codes, void *scales, void *stream);
+
+/* Y[i][r] = sum_j X_hat[i][j] * W_hat[r][j]: MX-quantized activations times
+ * MXFP4 weights on the gfx950 block-scaled FP4 matrix instruction
+ * (v_mfma_scale_f32_32x32x64_f8f6f4), both E8M0 scales applied by the matrix
+ * core ([WK] sections 5 and 7, the native FP4 path; [FB] section 3).
+ * w: QBN_MXFP4 [n][k/2] + E8M0 [n][k/32]; x_format: QBN_MXFP4 (codes
+ * [m][k/2] and scales [m][k/32] as written by qbn_quantize_mx, codes 16-byte
+ * aligned); QBN_MXFP8 is not accepted by this version (QBN_ERR_UNSUPPORTED).
+ * Y: QBN_BF16 (RNE of the binary32 sum) or QBN_F32, [m][ldy], ldy >= n.
+ * Products are exact; the sum is binary32 in k-steps of 64, within
+ * 1e-5 * sum |x_hat w_hat| + 1e-6 of the exact value (before the bf16
+ * rounding). */
+QBN_API int32_t qbn_quantized_gemm_mx(const qbn_tensor *w, int64_t m, int32_t x_format, const void *xcodes,
+                                      const void *xscales, void *y, int32_t y_dtype, int64_t ldy, void *stream);
 
 /* Materialize W_hat. out_layout 0: out [n][k] row-major; 1: out [k][n].
  * out_dtype QBN_F32: the exact binary32 value of each format's rule

@@ -36,7 +36,7 @@ def T(fmt, n, k, data=A, scales=B, zeros=C, scale2=1.0, group=0, reserved=0):
 def test_exports_every_declared_symbol(lib):
     header = open(os.path.join(ROOT, "include", "qbn.h")).read()
     declared = re.findall(r"QBN_API\s+[\w\s\*]+?\b(qbn_\w+)\s*\(", header)
-    assert len(declared) == 12
+    assert len(declared) == 14
     assert set(declared) == set(qbn.EXPORTED)
     so = ctypes.CDLL(qbn.lib_path())
     for name in declared:
@@ -144,6 +144,34 @@ def test_gemv_q8_rejections(lib):
     assert g(T(NV, 4, 256), A + 8, B, None, A, F16, None) == ALIGN
     assert g(T(NV, 4, 256), A, None, None, A, F16, None) == NULL
     assert g(T(QK, 4, 256), A, B, C, A, F16, None) == DTYPE
+
+
+def test_mx_rejections(lib):
+    q = lib.qbn_quantize_mx
+    MX8 = 7
+    assert q(A, F32, 4, 64, 64, 9, B, C, None) == FORMAT
+    assert q(A, F32, 4, 64, 64, QK, B, C, None) == UNSUP
+    assert q(A, 2, 4, 64, 64, MX, B, C, None) == DTYPE
+    assert q(A, F32, 4, 48, 48, MX, B, C, None) == SHAPE
+    assert q(A, F32, 4, 64, 32, MX, B, C, None) == SHAPE
+    assert q(A, F32, 4, 64, 66, MX, B, C, None) == ALIGN
+    assert q(A + 8, F32, 4, 64, 64, MX, B, C, None) == ALIGN
+    assert q(A, F32, 4, 64, 64, MX8, B + 2, C, None) == ALIGN
+    assert q(A, F32, 4, 64, 64, MX, B + 1, C, None) == ALIGN
+    assert q(None, F32, 4, 64, 64, MX, B, C, None) == NULL
+    assert q(None, F32, 0, 64, 64, MX, None, None, None) == OK
+    g = lib.qbn_quantized_gemm_mx
+    assert g(T(NV, 8, 64), 4, MX, A, B, C, BF16, 8, None) == UNSUP
+    assert g(T(MX, 8, 64), 4, MX8, A, B, C, BF16, 8, None) == UNSUP
+    assert g(T(MX, 8, 64), 4, 9, A, B, C, BF16, 8, None) == FORMAT
+    assert g(T(MX, 8, 64), 4, MX, A, B, C, 2, 8, None) == DTYPE
+    assert g(T(MX, 8, 64), 4, MX, A, B, C, BF16, 4, None) == SHAPE
+    assert g(T(MX, 8, 64), -1, MX, A, B, C, BF16, 8, None) == SHAPE
+    assert g(T(MX, 8, 64), 4, MX, A + 8, B, C, BF16, 8, None) == ALIGN
+    assert g(T(MX, 8, 64), 4, MX, A, B, C + 2, F32, 8, None) == ALIGN
+    assert g(T(MX, 8, 64), 4, MX, None, B, C, BF16, 8, None) == NULL
+    assert g(T(MX, 8, 64), 4, MX, A, None, C, BF16, 8, None) == NULL
+    assert g(T(MX, 8, 64), 0, MX, None, None, None, BF16, 8, None) == OK
 
 
 def test_gemm_rejections(lib):
