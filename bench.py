@@ -82,6 +82,13 @@ WORKLOADS = {
         cfg=4, kind="gemm", unit="TFLOP/s",
         desc="MXFP4 prefill GEMM: W 8192x8192 (E2M1, E8M0 per 32) x X bf16 2048x8192 -> Y bf16, fp32 accumulate",
         flops=2.0 * 2048 * 8192 * 8192, bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 * 2 * 2),
+    "mxfp4_w4a4_gemm": dict(
+        cfg=4, kind="mxgemm", unit="TFLOP/s", dtype="fp4",
+        desc="MX-native W4A4 GEMM: OCP MX quantization of X bf16 2048x8192 to MXFP4 + W 8192x8192 MXFP4 on the "
+             "block-scaled FP4 matrix cores -> Y bf16, fp32 accumulate",
+        flops=2.0 * 2048 * 8192 * 8192,
+        bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 * 2 + 2 * (2048 * 4096 + 2048 * 256) + 2048 * 8192 * 2,
+        kernel_bytes=8192 * 4096 + 8192 * 256 + 2048 * 4096 + 2048 * 256 + 2048 * 8192 * 2),
     "gptq_to_awq": dict(
         cfg=5, kind="repack", unit="GB/s", src="gptq4", dst="awq4",
         desc="int4 repack GPTQ int32 [K/8][N] -> AWQ int32 [K][N/8], K x N = 4096 x 11008",
@@ -191,6 +198,25 @@ def build_steps(name, spec, dev):
             w = qbn.QTensor(inp["fmt"], n, k, d0.clone(), None if s0 is None else s0.clone(), scale2=inp["scale2"])
             calls.append(qbn.prepare_gemv(w, x, y))
         return calls, R, inp, None
+    if spec["kind"] == "mxgemm":
+        n, k, m = inp["n"], inp["k"], inp["m"]
+        R = 2
+        d0 = host_to_device(inp["data"], dev)
+        s0 = host_to_device(inp["scales"], dev)
+        X = host_to_device(inp["X"], dev).view(torch.bfloat16)
+        xc = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+        xs = torch.empty((m, k // 32), dtype=torch.uint8, device=dev)
+        Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        quant = qbn.prepare_quantize_mx(X, xc, xs, "mxfp4")
+        gemms = [qbn.prepare_gemm_mx(qbn.QTensor("mxfp4", n, k, d0.clone(), s0.clone()), xc, xs, Y) for _ in range(R)]
+
+        def step(g):
+            def run():
+                quant()
+                g()
+            return run
+
+        return [step(g) for g in gemms], R, inp, gemms
     if spec["kind"] == "gemm":
         n, k, m = inp["n"], inp["k"], inp["m"]
         R = 2
@@ -276,6 +302,21 @@ def cpu_baseline(name, spec, inp, budget_s):
         t = float(np.median(reps))
         return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
                     sample="full %dx%d GEMV, median of %d runs (%.2f s each)" % (n, k, len(reps), t))
+    if spec["kind"] == "mxgemm":
+        n, k, m = inp["n"], inp["k"], inp["m"]
+        rng = np.random.default_rng(0)
+        done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            i = int(rng.integers(0, m))
+            xc, xs = oracle.mx_quantize(inp["X"][i:i + 1], oracle.MXFP4)
+            nn = rng.integers(0, n, 16)
+            oracle.mx_gemm_entries(inp["data"], inp["scales"], k, oracle.MXFP4, xc, xs, np.zeros(16, np.int64), nn)
+            done += 16
+        t = time.perf_counter() - t0
+        return dict(value=2.0 * k * done / t / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                    sample="%d sampled output entries (one quantized X row each 16 entries, 2k flops per entry), %.1f s"
+                    % (done, t))
     if spec["kind"] == "gemm":
         n, k, m = inp["n"], inp["k"], inp["m"]
         rng = np.random.default_rng(0)
@@ -326,8 +367,8 @@ def main():
 
         __graft_entry__.build()
     spec = WORKLOADS[args.workload]
-    steps = args.steps or (2000 if spec["kind"] != "gemm" else 50)
-    warmup = args.warmup if args.warmup is not None else (500 if spec["kind"] == "gemm" else 200)
+    steps = args.steps or (50 if spec["kind"] == "gemm" else 200 if spec["kind"] == "mxgemm" else 2000)
+    warmup = args.warmup if args.warmup is not None else (500 if spec["kind"] in ("gemm", "mxgemm") else 200)
     dev = torch.device("cuda:0")
     calls, R, inp, kcalls = build_steps(args.workload, spec, dev)
     torch.cuda.synchronize()
@@ -424,11 +465,12 @@ def main():
     copy_gbs = 2 * half / (a.elapsed_time(b) / csteps * 1e-3) / 1e9
     del cg, bufs
 
-    if spec["kind"] == "gemm":
+    if spec["kind"] in ("gemm", "mxgemm"):
+        peak = BF16_MFMA_PEAK_TFLOPS if spec["kind"] == "gemm" else FP4_MFMA_PEAK_TFLOPS
         value = spec["flops"] / (ms_step * 1e-3) / 1e12
         achieved = spec["flops"] / (kernel_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), traffic=recorded_traffic(args.workload))
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), traffic=recorded_traffic(args.workload))
         metric = "FP4 GEMM TFLOP/s (% MFMA peak)"
     else:
         value = spec["bytes"] / (ms_step * 1e-3) / 1e9
@@ -462,8 +504,8 @@ def main():
             "rotating_copies": R,
             "step_bytes": spec["bytes"],
             **({"step_flops": spec["flops"]} if "flops" in spec else {}),
-            **({"kernel_bytes": spec["kernel_bytes"], "kernel_note": "roofline is the GEMV kernel alone, timed "
-                "in its own graph of K launches; value is the whole step (activation quantization + GEMV)"}
+            **({"kernel_bytes": spec["kernel_bytes"], "kernel_note": "roofline is the dominant kernel alone, timed "
+                "in its own graph of K launches; value is the whole step (activation quantization + the kernel)"}
                if "kernel_bytes" in spec else {}),
             "kernel_ms_per_launch": round(kernel_ms, 6),
             "kernel_ms_other_replays": [round(v, 6) for v in spread],

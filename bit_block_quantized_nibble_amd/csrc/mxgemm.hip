@@ -100,8 +100,16 @@ __device__ __forceinline__ void dma4(const void *g, void *lds_base) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 constexpr int BM = 256, BN = 256, BKS = 256;  // tile rows, tile columns, k per LDS stage
-constexpr int WAVES = 8;                      // 4 x 2 waves, each 64 x 128 = 2 x 4 MFMA tiles
-constexpr int WGM = 4, WGN = 2, TM = 2, TN = 4;
+
+// s_waitcnt vmcnt(n), n < 64 (the count's high bits sit at 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0xF70 | (N & 15));
+}
+
+// s_waitcnt lgkmcnt(0): every LDS read issued so far has returned
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // LDS stage (k = 256): A (activation codes) and B (weight codes), 256 rows of
 // (256 / 2 / ELEM) bytes, then the 8 scale bytes of each row of A and of B.
@@ -121,28 +129,29 @@ struct Lay {
 
 __device__ __forceinline__ int gsw(int n) { return (n % 8) ^ ((n / 8) & 1); }
 
-// Copies of one stage: 32 row groups of 8 rows per operand (16-byte pieces,
-// swizzled on the global side so the LDS image is the layout above) and 8
-// groups of 32 rows per scale array (4 bytes per lane).
-// Rows past M (N) re-read row M-1 (N-1); their results are not stored.
-// Offsets are 32-bit from the (uniform) tensor bases: the launcher sends
-// tensors of 2 GB or more to the small kernel.
-template <bool A8>
+// Copies of one stage, dealt round-robin to the WAVES waves: 256 / RPC row
+// groups per operand (16-byte pieces, swizzled on the global side so that
+// the LDS image is the layout above) and 8 groups of 32 rows per scale array
+// (4 bytes per lane). Rows past M (N) re-read row M-1 (N-1); their results
+// are not stored. Offsets are 32-bit from the (uniform) tensor bases: the
+// launcher sends tensors of 2 GB or more to the small kernel.
+template <bool A8, int WAVES>
 struct StageCopy {
-    static constexpr int AP = Lay<A8>::AROW / 16;         // 16-byte pieces per A row
-    static constexpr int RPC = 64 / AP;                   // A rows per copy
-    static constexpr int NA = BM / RPC / WAVES;           // A copies per wave
-    static constexpr int NB = BN / 8 / WAVES;             // B copies per wave
-    static constexpr int COPIES = NA + NB + 2;
-    const uint8_t *xc, *xs, *wc, *ws;                     // tensor bases
-    uint32_t ag[NA], bg[NB], sag, sbg;                    // per-lane byte offsets at k = 0
-    int ao, bo, sao, sbo;                                 // LDS offsets of this wave's first copies
+    static constexpr int AP = Lay<A8>::AROW / 16;  // 16-byte pieces per A row
+    static constexpr int RPC = 64 / AP;            // A rows per copy
+    static constexpr int NA = BM / RPC / WAVES;    // A copies per wave
+    static constexpr int NB = BN / 8 / WAVES;      // B copies per wave
+    static constexpr int NS = 8 / WAVES;           // scale copies per wave, per array
+    static constexpr int COPIES = NA + NB + 2 * NS;
+    static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
+    const uint8_t *xc, *xs, *wc, *ws;              // tensor bases
+    uint32_t ag[NA], bg[NB], sag[NS], sbg[NS];     // per-lane byte offsets at k = 0
+    int wave;
 
     __device__ __forceinline__ StageCopy(const uint8_t *xc_, const uint8_t *xs_, const uint8_t *wc_,
                                          const uint8_t *ws_, int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
-                                         int lane, int wave)
-        : xc(xc_), xs(xs_), wc(wc_), ws(ws_) {
-        using L = Lay<A8>;
+                                         int lane, int wave_)
+        : xc(xc_), xs(xs_), wc(wc_), ws(ws_), wave(wave_) {
         const int64_t arow = A8 ? K : K / 2;
 #pragma unroll
         for (int q = 0; q < NA; ++q) {
@@ -156,23 +165,43 @@ struct StageCopy {
             const int r = (wave + WAVES * q) * 8 + lane / 8, sl = lane % 8;
             bg[q] = (uint32_t)(min(n0 + r, N - 1) * (K / 2) + 16 * (sl ^ gsw(r)));
         }
-        ao = L::A_OFF + wave * 1024;
-        bo = L::B_OFF + wave * 1024;
-        const int r = wave * 32 + lane / 2, h = lane % 2;  // one 4-byte copy per wave covers 32 rows
-        sag = (uint32_t)(min(m0 + r, M - 1) * (K / 32) + 4 * h);
-        sbg = (uint32_t)(min(n0 + r, N - 1) * (K / 32) + 4 * h);
-        sao = L::SA_OFF + wave * 256;
-        sbo = L::SB_OFF + wave * 256;
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            const int r = (wave + WAVES * q) * 32 + lane / 2, h = lane % 2;
+            sag[q] = (uint32_t)(min(m0 + r, M - 1) * (K / 32) + 4 * h);
+            sbg[q] = (uint32_t)(min(n0 + r, N - 1) * (K / 32) + 4 * h);
+        }
+    }
+
+    // copy number q of the stage (0 <= q < COPIES): A rows, B rows, A scales, B scales
+    __device__ __forceinline__ void copy_one(uint8_t *stage, int64_t k0, int q) const {
+        using L = Lay<A8>;
+        if (q < NA) {
+            dma16(xc + (ag[q] + (uint32_t)(A8 ? k0 : k0 / 2)), stage + L::A_OFF + (wave + WAVES * q) * 1024);
+        } else if (q < NA + NB) {
+            q -= NA;
+            dma16(wc + (bg[q] + (uint32_t)(k0 / 2)), stage + L::B_OFF + (wave + WAVES * q) * 1024);
+        } else if (q < NA + NB + NS) {
+            q -= NA + NB;
+            dma4(xs + (sag[q] + (uint32_t)(k0 / 32)), stage + L::SA_OFF + (wave + WAVES * q) * 256);
+        } else {
+            q -= NA + NB + NS;
+            dma4(ws + (sbg[q] + (uint32_t)(k0 / 32)), stage + L::SB_OFF + (wave + WAVES * q) * 256);
+        }
     }
 
     __device__ __forceinline__ void copy(uint8_t *stage, int64_t k0) const {
+        using L = Lay<A8>;
         const uint32_t ak = (uint32_t)(A8 ? k0 : k0 / 2), bk = (uint32_t)(k0 / 2), sk = (uint32_t)(k0 / 32);
 #pragma unroll
-        for (int q = 0; q < NA; ++q) dma16(xc + (ag[q] + ak), stage + ao + q * WAVES * 1024);
+        for (int q = 0; q < NA; ++q) dma16(xc + (ag[q] + ak), stage + L::A_OFF + (wave + WAVES * q) * 1024);
 #pragma unroll
-        for (int q = 0; q < NB; ++q) dma16(wc + (bg[q] + bk), stage + bo + q * WAVES * 1024);
-        dma4(xs + (sag + sk), stage + sao);
-        dma4(ws + (sbg + sk), stage + sbo);
+        for (int q = 0; q < NB; ++q) dma16(wc + (bg[q] + bk), stage + L::B_OFF + (wave + WAVES * q) * 1024);
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            dma4(xs + (sag[q] + sk), stage + L::SA_OFF + (wave + WAVES * q) * 256);
+            dma4(ws + (sbg[q] + sk), stage + L::SB_OFF + (wave + WAVES * q) * 256);
+        }
     }
 };
 
@@ -183,7 +212,7 @@ __device__ __forceinline__ v8i widen(u32x4 v) {
     return w;
 }
 
-template <bool A8>
+template <bool A8, int TM, int TN>
 __device__ __forceinline__ void read_frags(const uint8_t *sm, int aoff, int boff, v8i (&a)[TM], v8i (&b)[TN]) {
     using L = Lay<A8>;
 #pragma unroll
@@ -200,6 +229,45 @@ __device__ __forceinline__ void read_frags(const uint8_t *sm, int aoff, int boff
     for (int j = 0; j < TN; ++j) b[j] = widen(*reinterpret_cast<const u32x4 *>(sm + boff + j * 32 * L::BROW));
 }
 
+template <bool A8>
+__device__ __forceinline__ v8i read_a(const uint8_t *sm, int aoff, int i) {
+    using L = Lay<A8>;
+    if (A8) {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(sm + aoff + i * 32 * L::AROW);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(sm + (aoff ^ 16) + i * 32 * L::AROW);
+        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    return widen(*reinterpret_cast<const u32x4 *>(sm + aoff + i * 32 * L::AROW));
+}
+template <bool A8>
+__device__ __forceinline__ v8i read_b(const uint8_t *sm, int boff, int j) {
+    return widen(*reinterpret_cast<const u32x4 *>(sm + boff + j * 32 * Lay<A8>::BROW));
+}
+__device__ __forceinline__ void read_scale(const uint8_t *sm, int off, int lh, uint32_t (&w)[2]) {
+    const u32x2 v = *reinterpret_cast<const u32x2 *>(sm + off);
+    w[0] = v.x >> (8 * lh);
+    w[1] = v.y >> (8 * lh);
+}
+
+// The 8 scale bytes of each of the lane's rows for one stage, shifted so
+// that the byte of step s sits at bits 16 (s % 2) .. of word s / 2.
+template <int TM, int TN>
+__device__ __forceinline__ void read_scales(const uint8_t *sm, int saoff, int sboff, int lh, uint32_t (&sa)[TM][2],
+                                            uint32_t (&sb)[TN][2]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(sm + saoff + i * 32 * 8);
+        sa[i][0] = v.x >> (8 * lh);
+        sa[i][1] = v.y >> (8 * lh);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(sm + sboff + j * 32 * 8);
+        sb[j][0] = v.x >> (8 * lh);
+        sb[j][1] = v.y >> (8 * lh);
+    }
+}
+
 template <typename YT>
 __device__ __forceinline__ void put_out(YT *y, int64_t idx, float v);
 template <>
@@ -211,18 +279,66 @@ __device__ __forceinline__ void put_out<float>(float *y, int64_t idx, float v) {
     y[idx] = v;
 }
 
-// Y tile 256 x 256: wave (wm, wn) owns rows wm*64 .. +63 and columns
-// wn*128 .. +127 as 2 x 4 MFMA tiles of 32 x 32. A k-step of 64 is one MFMA
-// per tile: lane half lh holds k 32 lh .. 32 lh + 31 of the step (piece 2 s + lh
-// of a stage) for its row (A) or column (B), under one E8M0 byte each.
-template <bool A8, typename YT>
-__global__ __launch_bounds__(WAVES * 64) void k_mxgemm(const uint8_t *__restrict__ xc,
-                                                       const uint8_t *__restrict__ xs,
-                                                       const uint8_t *__restrict__ wc,
-                                                       const uint8_t *__restrict__ ws, YT *__restrict__ Y,
-                                                       int64_t ldy, int64_t M, int64_t N, int64_t K, int tiles_m,
-                                                       int tiles_n) {
+// Keeps the compiler from moving LDS reads across it (the MFMA steps are
+// then fed in order: the reads of step s + 1 overlap step s's MFMAs).
+__device__ __forceinline__ void mem_fence() { asm volatile("" ::: "memory"); }
+
+// One MFMA per 32 x 32 tile for a k-step of 64. The scale words hold the
+// step's E8M0 byte at byte OP (0 or 2), which the matrix core selects itself.
+template <int OP, bool A8, int TM, int TN>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[TM][TN], const v8i (&a)[TM], const v8i (&b)[TN],
+                                          const uint32_t (&sa)[TM][2], const uint32_t (&sb)[TN][2], int w) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], A8 ? 0 : 4, 4, OP,
+                                                                       (int)sa[i][w], OP, (int)sb[j][w]);
+}
+
+// Staging of a wave's output through LDS, 32 rows at a time: the 32 x COLS
+// block is written element by element in the MFMA layout, then read back in
+// 16-byte row pieces, so that each global store writes 16 contiguous bytes
+// per lane. The row pitch is padded so that the two lane halves of a write
+// (rows r and r + 4) fall in different banks.
+template <typename YT, int COLS>
+struct OutStage {
+    static constexpr int E = 16 / (int)sizeof(YT);            // elements per 16-byte piece
+    static constexpr int CH = COLS / E;                        // pieces per row
+    static constexpr int PITCH = COLS * (int)sizeof(YT) + 16 * (int)sizeof(YT) / 2;
+    static constexpr int BYTES = 32 * PITCH;
+    static constexpr int NI = 32 * CH / 64;                    // 16-byte reads per lane
+};
+
+template <typename YT>
+__device__ __forceinline__ void lds_put(uint8_t *p, float v);
+template <>
+__device__ __forceinline__ void lds_put<uint16_t>(uint8_t *p, float v) {
+    *reinterpret_cast<uint16_t *>(p) = bf16_bits_rne(v);
+}
+template <>
+__device__ __forceinline__ void lds_put<float>(uint8_t *p, float v) {
+    *reinterpret_cast<float *>(p) = v;
+}
+
+// Y tile 256 x 256: WGM x WGN waves, wave (wm, wn) owning a TM x TN block of
+// 32 x 32 MFMA tiles. A k-step of 64 is one MFMA per tile: lane half lh holds
+// k 32 lh .. 32 lh + 31 of the step (piece 2 s + lh of a stage) for its row (A)
+// or column (B), under one E8M0 byte each. Two LDS stages: the barrier of
+// stage st sits before its last step, after which stage st + 2 is copied into
+// st's buffer and stage st + 1's scales and first fragments are read while
+// the last step's MFMAs run.
+template <int WGM, int WGN, bool A8, typename YT>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_mxgemm(const uint8_t *__restrict__ xc,
+                                                           const uint8_t *__restrict__ xs,
+                                                           const uint8_t *__restrict__ wc,
+                                                           const uint8_t *__restrict__ ws, YT *__restrict__ Y,
+                                                           int64_t ldy, int64_t M, int64_t N, int64_t K, int tiles_m,
+                                                           int tiles_n) {
+    constexpr int WAVES = WGM * WGN, TM = BM / WGM / 32, TN = BN / WGN / 32;
     using L = Lay<A8>;
+    using CP = StageCopy<A8, WAVES>;
+    static_assert(L::NST == 2, "two-stage ring");
     __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
     // XCD-aware banded order (as in the bf16 GEMM): the workgroups of one XCD
     // cover a block of GM tile rows x (per-XCD count / GM) tile columns
@@ -243,9 +359,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_mxgemm(const uint8_t *__restrict
     const int lr = lane % 32, lh = lane / 32;
     const int nst = (int)(K / BKS);
 
-    // per-lane LDS offsets (row bases; the piece slot is added per step)
-    const int ra = wm * 64 + lr, rbn = wn * 128 + lr;
-    const int gl = gsw(lr);  // g(n) of every row this lane reads: n = 16 * (...) + lr
+    // per-lane LDS offsets; every row this lane reads is 32 t + (a multiple of
+    // 16) + lr, so g(n) = g(lr)
+    const int ra = wm * (32 * TM) + lr, rbn = wn * (32 * TN) + lr;
+    const int gl = gsw(lr);
     int a_off[4], b_off[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -262,65 +379,123 @@ __global__ __launch_bounds__(WAVES * 64) void k_mxgemm(const uint8_t *__restrict
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-    const StageCopy<A8> cp(xc, xs, wc, ws, M, N, K, m0, n0, lane, wave);
+    const CP cp(xc, xs, wc, ws, M, N, K, m0, n0, lane, wave);
     cp.copy(smem, 0);
-    if (L::NST > 1 && nst > 1) cp.copy(smem + L::STAGE, BKS);
+    if (nst > 1) {
+        cp.copy(smem + L::STAGE, BKS);
+        wait_vm<CP::COPIES>();
+    } else {
+        wait_vm<0>();
+    }
+    lds_barrier();
+    uint32_t sa[TM][2], sb[TN][2];
+    v8i a[2][TM], b[2][TN];
+    read_scales<TM, TN>(smem, sa_off, sb_off, lh, sa, sb);
+    read_frags<A8, TM, TN>(smem, a_off[0], b_off[0], a[0], b[0]);
 
+    // The stage body is straight-line, so that the order fixed by the
+    // scheduling barriers holds (the compiler otherwise sinks the MFMAs below
+    // every LDS read). Its tail is the same at every stage: past the barrier,
+    // stage min(st + 2, nst - 1) is copied into stage st's buffer and the
+    // other buffer's scales and first fragments are read. Near the end these
+    // are repeats that nothing uses; they stay in bounds.
     for (int st = 0; st < nst; ++st) {
-        uint8_t *const sm = smem + (L::NST > 1 ? (st & 1) * L::STAGE : 0);
-        // this stage's copies have landed once at most the next stage's remain
-        if (L::NST > 1 && st + 1 < nst) __builtin_amdgcn_s_waitcnt(0xF70 | StageCopy<A8>::COPIES);
-        else __builtin_amdgcn_s_waitcnt(0xF70);
-        lds_barrier();
-        uint32_t sa[TM][2], sb[TN][2];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const u32x2 v = *reinterpret_cast<const u32x2 *>(sm + sa_off + i * 32 * 8);
-            sa[i][0] = v.x >> (8 * lh);
-            sa[i][1] = v.y >> (8 * lh);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const u32x2 v = *reinterpret_cast<const u32x2 *>(sm + sb_off + j * 32 * 8);
-            sb[j][0] = v.x >> (8 * lh);
-            sb[j][1] = v.y >> (8 * lh);
-        }
-        // two fragment sets: step s + 1 is read while step s's MFMAs run
-        v8i a[2][TM], b[2][TN];
-        read_frags<A8>(sm, a_off[0], b_off[0], a[0], b[0]);
+        uint8_t *const sm = smem + (st & 1) * L::STAGE;
+        uint8_t *const nx = smem + ((st + 1) & 1) * L::STAGE;
+        const int64_t kc = (int64_t)min(st + 2, nst - 1) * BKS;
+        uint32_t na[TM][2], nb[TN][2];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            if (s < 3) read_frags<A8>(sm, a_off[s + 1], b_off[s + 1], a[(s + 1) & 1], b[(s + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
+            // step s's fragments were read one step ago; waiting for them
+            // here, before this step's reads are issued, keeps the count of
+            // reads in flight within what the counter tracks
+            wait_lds();
+            if (s < 3) {
+                read_frags<A8, TM, TN>(sm, a_off[s + 1], b_off[s + 1], a[(s + 1) & 1], b[(s + 1) & 1]);
+                mem_fence();
+                __builtin_amdgcn_sched_barrier(0);
+                if (s % 2 == 0)
+                    mfma_step<0, A8, TM, TN>(acc, a[s & 1], b[s & 1], sa, sb, s / 2);
+                else
+                    mfma_step<2, A8, TM, TN>(acc, a[s & 1], b[s & 1], sa, sb, s / 2);
+            } else {
+                // stage st + 1 (copied one stage ago) has landed once nothing
+                // is outstanding; past the barrier no wave reads stage st.
+                // The copies of stage st + 2 and the reads of stage st + 1's
+                // first fragments and scales are spread over this step's
+                // MFMAs, a few after each.
+                wait_vm<0>();
+                lds_barrier();
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int t = 0; t < TM * TN; ++t) {
+                    const int i = t / TN, j = t % TN;
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        a[1][i], b[1][j], acc[i][j], A8 ? 0 : 4, 4, 2, (int)sa[i][1], 2, (int)sb[j][1]);
+                    constexpr int PER = (CP::COPIES + TM * TN - 1) / (TM * TN);
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int sai = (int)(sa[i][s / 2] >> (16 * (s % 2)));
-                    const int sbj = (int)(sb[j][s / 2] >> (16 * (s % 2)));
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[s & 1][i], b[s & 1][j], acc[i][j],
-                                                                               A8 ? 0 : 4, 4, 0, sai, 0, sbj);
+                    for (int q = PER * t; q < PER * t + PER; ++q)
+                        if (q < CP::COPIES) cp.copy_one(sm, kc, q);
+                    if (t < TM)
+                        a[0][t] = read_a<A8>(nx, a_off[0], t);
+                    else if (t < TM + TN)
+                        b[0][t - TM] = read_b<A8>(nx, b_off[0], t - TM);
+                    else if (t < 2 * TM + TN)
+                        read_scale(nx, sa_off + (t - TM - TN) * 32 * 8, lh, na[t - TM - TN]);
+                    else if (t < 2 * TM + 2 * TN)
+                        read_scale(nx, sb_off + (t - 2 * TM - TN) * 32 * 8, lh, nb[t - 2 * TM - TN]);
+                    mem_fence();
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+            }
             __builtin_amdgcn_sched_barrier(0);
+            mem_fence();
         }
-        // every wave is done with this buffer before it is refilled
-        if (st + L::NST < nst) {
-            lds_barrier();
-            cp.copy(sm, (int64_t)(st + L::NST) * BKS);
-        }
-    }
-
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            sa[i][0] = na[i][0];
+            sa[i][1] = na[i][1];
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int64_t n = n0 + wn * 128 + 32 * j + lr;
+            sb[j][0] = nb[j][0];
+            sb[j][1] = nb[j][1];
+        }
+    }
+    wait_vm<0>();  // the last (unused) copies land before the waves end
+    lds_barrier();  // every wave is done with the stage buffers
+
+    using O = OutStage<YT, 32 * TN>;
+    static_assert(WAVES * O::BYTES <= L::BYTES, "output staging fits in LDS");
+    uint8_t *const ot = smem + wave * O::BYTES;
+    const int64_t rm0 = m0 + wm * (32 * TM), cn0 = n0 + wn * (32 * TN);
+    const bool vec = ((uintptr_t)Y % 16) == 0 && ((ldy * (int64_t)sizeof(YT)) % 16) == 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t m = m0 + wm * 64 + 32 * i + 8 * (v / 4) + 4 * lh + (v % 4);
-                if (m < M && n < N) put_out<YT>(Y, m * ldy + n, acc[i][j][v]);
+                const int r = 8 * (v / 4) + 4 * lh + (v % 4);
+                lds_put<YT>(ot + r * O::PITCH + (32 * j + lr) * (int)sizeof(YT), acc[i][j][v]);
+            }
+        mem_fence();  // one wave's LDS accesses are performed in order
+#pragma unroll
+        for (int t = 0; t < O::NI; ++t) {
+            const int id = t * 64 + lane, r = id / O::CH, c = (id % O::CH) * O::E;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + r * O::PITCH + c * (int)sizeof(YT));
+            const int64_t m = rm0 + 32 * i + r, n = cn0 + c;
+            YT *const dst = Y + m * ldy + n;
+            if (vec && m < M && n + O::E <= N) {
+                *reinterpret_cast<u32x4 *>(dst) = v;
+            } else if (m < M) {
+                const YT *e = reinterpret_cast<const YT *>(&v);
+#pragma unroll
+                for (int q = 0; q < O::E; ++q)
+                    if (n + q < N) dst[q] = e[q];
             }
         }
+        mem_fence();
+    }
 }
 
 // Any shape with k % 32 == 0: one wave per 32 x 32 tile of Y, fragments read
@@ -370,14 +545,18 @@ template <bool A8, typename YT>
 hipError_t run_mxgemm(const qbn_tensor &w, int64_t m, const void *xc, const void *xs, void *y, int64_t ldy,
                       hipStream_t s) {
     const int64_t xbytes = m * (A8 ? w.k : w.k / 2), wbytes = w.n * (w.k / 2);
-    const bool big = m >= BM && w.n >= BN && (w.k % BKS) == 0 && xbytes < ((int64_t)1 << 31) &&
+    const bool big = !A8 && m >= BM && w.n >= BN && (w.k % BKS) == 0 && xbytes < ((int64_t)1 << 31) &&
                      wbytes < ((int64_t)1 << 31) && ((uintptr_t)xs % 4) == 0 && ((uintptr_t)w.scales % 4) == 0;
-    if (big) {
-        const int64_t tm = (m + BM - 1) / BM, tn = (w.n + BN - 1) / BN;
-        hipLaunchKernelGGL((k_mxgemm<A8, YT>), dim3((unsigned)(tm * tn)), dim3(WAVES * 64), 0, s,
-                           (const uint8_t *)xc, (const uint8_t *)xs, (const uint8_t *)w.data,
-                           (const uint8_t *)w.scales, (YT *)y, ldy, m, w.n, w.k, (int)tm, (int)tn);
-    } else {
+    if constexpr (!A8) {
+        if (big) {
+            const int64_t tm = (m + BM - 1) / BM, tn = (w.n + BN - 1) / BN;
+            hipLaunchKernelGGL((k_mxgemm<2, 2, false, YT>), dim3((unsigned)(tm * tn)), dim3(4 * 64), 0, s,
+                               (const uint8_t *)xc, (const uint8_t *)xs, (const uint8_t *)w.data,
+                               (const uint8_t *)w.scales, (YT *)y, ldy, m, w.n, w.k, (int)tm, (int)tn);
+            return hipGetLastError();
+        }
+    }
+    {
         const int64_t tm = (m + 31) / 32, tn = (w.n + 31) / 32;
         hipLaunchKernelGGL((k_mxgemm_small<A8, YT>), dim3((unsigned)((tm * tn + 3) / 4)), dim3(256), 0, s,
                            (const uint8_t *)xc, (const uint8_t *)xs, (const uint8_t *)w.data,

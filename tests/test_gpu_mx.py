@@ -100,9 +100,11 @@ def _inputs(rng, m, n, k):
 
 
 # Shapes reach the small kernel (m or n below 256, or k not a multiple of 256,
-# including k % 64 == 32) and the 256 x 256 kernel with full and edge tiles.
+# including k % 64 == 32) and the 256 x 256 kernel with full and edge tiles,
+# from one k-stage of 256 to many.
 @pytest.mark.parametrize("m,n,k", [(1, 32, 32), (37, 70, 96), (130, 200, 1056), (64, 512, 2048), (256, 256, 256),
-                                   (300, 520, 1024), (512, 256, 4096), (256, 384, 768), (512, 512, 8192)])
+                                   (300, 520, 1024), (512, 256, 4096), (256, 384, 768), (512, 512, 8192),
+                                   (256, 256, 128), (260, 512, 640), (384, 300, 1280), (256, 256, 352)])
 def test_gemm_mx_all_entries(m, n, k):
     rng = np.random.default_rng(m + 7 * n + k)
     xc, xs, wc, ws = _inputs(rng, m, n, k)
