@@ -244,8 +244,9 @@ def quantize_mx(x: torch.Tensor, fmt: str = "mxfp4", codes: Optional[torch.Tenso
 
 def quantized_gemm_mx(w: QTensor, xcodes: torch.Tensor, xscales: torch.Tensor, fmt: str = "mxfp4",
                       y: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = X_hat @ W_hat^T for MX activations (from quantize_mx) and an MXFP4
-    weight, on the FP4 matrix cores. Y bfloat16 (default) or float32 [m][n]."""
+    """Y = X_hat @ W_hat^T for MX activations (from quantize_mx; "mxfp4" for
+    W4A4, "mxfp8" for W4A8) and an MXFP4 weight, on the block-scaled matrix
+    cores. Y bfloat16 (default) or float32 [m][n]."""
     lib = _load()
     m = xcodes.shape[0]
     if y is None:

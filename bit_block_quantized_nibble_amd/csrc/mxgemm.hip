@@ -99,7 +99,7 @@ __device__ __forceinline__ void dma4(const void *g, void *lds_base) {
 }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-constexpr int BM = 256, BN = 256, BKS = 256;  // tile rows, tile columns, k per LDS stage
+constexpr int BM = 256, BN = 256;  // tile rows, tile columns
 
 // s_waitcnt vmcnt(n), n < 64 (the count's high bits sit at 15:14)
 template <int N>
@@ -111,41 +111,54 @@ __device__ __forceinline__ void wait_vm() {
 // s_waitcnt lgkmcnt(0): every LDS read issued so far has returned
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// LDS stage (k = 256): A (activation codes) and B (weight codes), 256 rows of
-// (256 / 2 / ELEM) bytes, then the 8 scale bytes of each row of A and of B.
-// Code piece p (16 bytes = 32 E2M1 values) of row n sits at
-//   n * ROW + ((p ^ g(n)) * 16),  g(n) = (n % 8) ^ ((n / 8) & 1)
-// so that 8 or 16 consecutive rows read at one p hit distinct banks.
+// XOR swizzle of the 16-byte pieces of an LDS row, over 8 pieces (128-byte
+// rows) or 4 (64-byte rows): 16 consecutive rows read at one piece index
+// fill 16 distinct 16-byte bank groups.
+template <int PIECES>
+__device__ __forceinline__ int swz(int n) {
+    if (PIECES == 8) return (n % 8) ^ ((n / 8) & 1);
+    return (n / 4) % 4;
+}
+
+// One LDS stage: A (activation codes) and B (weight codes), 256 rows each,
+// then the scale bytes of each row of A and of B. E2M1 activations: k = 256
+// per stage (128-byte rows of A and B, 8 scale bytes per row). E4M3
+// activations: k = 128 per stage (128-byte rows of A, 64-byte rows of B, 4
+// scale bytes per row), so that two stages still fit in LDS. Piece p of row
+// n (16 bytes) sits at n * ROW + ((p ^ swz(n)) * 16).
 template <bool A8>
 struct Lay {
-    static constexpr int AROW = A8 ? 256 : 128;  // bytes of A codes per row per stage
-    static constexpr int BROW = 128;
+    static constexpr int BK = A8 ? 128 : 256;     // k per stage
+    static constexpr int STEPS = BK / 64;         // MFMA k-steps per stage
+    static constexpr int AROW = A8 ? BK : BK / 2;  // bytes of A codes per row per stage
+    static constexpr int BROW = BK / 2;
+    static constexpr int SROW = BK / 32;           // scale bytes per row per stage
+    static constexpr int SW = SROW / 4;            // scale words per row
     static constexpr int A_OFF = 0, B_OFF = BM * AROW;
-    static constexpr int SA_OFF = B_OFF + BN * BROW, SB_OFF = SA_OFF + BM * 8;
-    static constexpr int STAGE = SB_OFF + BN * 8;
-    static constexpr int NST = A8 ? 1 : 2;  // stages in the ring (LDS holds 160 KB)
-    static constexpr int BYTES = NST * STAGE;
+    static constexpr int SA_OFF = B_OFF + BN * BROW, SB_OFF = SA_OFF + BM * SROW;
+    static constexpr int STAGE = SB_OFF + BN * SROW;
+    static constexpr int BYTES = 2 * STAGE;  // a two-stage ring
 };
 
-__device__ __forceinline__ int gsw(int n) { return (n % 8) ^ ((n / 8) & 1); }
-
-// Copies of one stage, dealt round-robin to the WAVES waves: 256 / RPC row
-// groups per operand (16-byte pieces, swizzled on the global side so that
-// the LDS image is the layout above) and 8 groups of 32 rows per scale array
-// (4 bytes per lane). Rows past M (N) re-read row M-1 (N-1); their results
-// are not stored. Offsets are 32-bit from the (uniform) tensor bases: the
-// launcher sends tensors of 2 GB or more to the small kernel.
+// Copies of one stage, dealt round-robin to the WAVES waves: 1 KB row groups
+// per code array (16-byte pieces, swizzled on the global side so that the LDS
+// image is the layout above) and 256-byte groups per scale array (4 bytes per
+// lane). Rows past M (N) re-read row M-1 (N-1); their results are not stored.
+// Offsets are 32-bit from the (uniform) tensor bases: the launcher sends
+// tensors of 2 GB or more to the small kernel.
 template <bool A8, int WAVES>
 struct StageCopy {
-    static constexpr int AP = Lay<A8>::AROW / 16;  // 16-byte pieces per A row
-    static constexpr int RPC = 64 / AP;            // A rows per copy
-    static constexpr int NA = BM / RPC / WAVES;    // A copies per wave
-    static constexpr int NB = BN / 8 / WAVES;      // B copies per wave
-    static constexpr int NS = 8 / WAVES;           // scale copies per wave, per array
+    using L = Lay<A8>;
+    static constexpr int AP = L::AROW / 16, ARPC = 64 / AP;  // pieces per A row, A rows per copy
+    static constexpr int BP = L::BROW / 16, BRPC = 64 / BP;
+    static constexpr int SLPR = L::SROW / 4, SRPC = 64 / SLPR;  // lanes per scale row, rows per copy
+    static constexpr int NA = BM / ARPC / WAVES;  // A copies per wave
+    static constexpr int NB = BN / BRPC / WAVES;  // B copies per wave
+    static constexpr int NS = BM / SRPC / WAVES;  // scale copies per wave, per array
     static constexpr int COPIES = NA + NB + 2 * NS;
-    static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
-    const uint8_t *xc, *xs, *wc, *ws;              // tensor bases
-    uint32_t ag[NA], bg[NB], sag[NS], sbg[NS];     // per-lane byte offsets at k = 0
+    static_assert(WAVES == 4 && NS >= 1, "four waves");
+    const uint8_t *xc, *xs, *wc, *ws;           // tensor bases
+    uint32_t ag[NA], bg[NB], sag[NS], sbg[NS];  // per-lane byte offsets at k = 0
     int wave;
 
     __device__ __forceinline__ StageCopy(const uint8_t *xc_, const uint8_t *xs_, const uint8_t *wc_,
@@ -155,27 +168,26 @@ struct StageCopy {
         const int64_t arow = A8 ? K : K / 2;
 #pragma unroll
         for (int q = 0; q < NA; ++q) {
-            // copy c = wave + WAVES q holds rows RPC c .. RPC c + RPC - 1
-            const int r = (wave + WAVES * q) * RPC + lane / AP, sl = lane % AP;
-            const int p = sl ^ (gsw(r) & (AP - 1));
-            ag[q] = (uint32_t)(min(m0 + r, M - 1) * arow + 16 * p);
+            // copy c = wave + WAVES q holds rows ARPC c .. ARPC c + ARPC - 1
+            const int r = (wave + WAVES * q) * ARPC + lane / AP, sl = lane % AP;
+            ag[q] = (uint32_t)(min(m0 + r, M - 1) * arow + 16 * (sl ^ swz<AP>(r)));
         }
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-            const int r = (wave + WAVES * q) * 8 + lane / 8, sl = lane % 8;
-            bg[q] = (uint32_t)(min(n0 + r, N - 1) * (K / 2) + 16 * (sl ^ gsw(r)));
+            const int r = (wave + WAVES * q) * BRPC + lane / BP, sl = lane % BP;
+            bg[q] = (uint32_t)(min(n0 + r, N - 1) * (K / 2) + 16 * (sl ^ swz<BP>(r)));
         }
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
-            const int r = (wave + WAVES * q) * 32 + lane / 2, h = lane % 2;
+            const int r = (wave + WAVES * q) * SRPC + lane / SLPR, h = lane % SLPR;
             sag[q] = (uint32_t)(min(m0 + r, M - 1) * (K / 32) + 4 * h);
             sbg[q] = (uint32_t)(min(n0 + r, N - 1) * (K / 32) + 4 * h);
         }
     }
 
-    // copy number q of the stage (0 <= q < COPIES): A rows, B rows, A scales, B scales
+    // copy number q of the stage at k0 (0 <= q < COPIES): A rows, B rows,
+    // A scales, B scales
     __device__ __forceinline__ void copy_one(uint8_t *stage, int64_t k0, int q) const {
-        using L = Lay<A8>;
         if (q < NA) {
             dma16(xc + (ag[q] + (uint32_t)(A8 ? k0 : k0 / 2)), stage + L::A_OFF + (wave + WAVES * q) * 1024);
         } else if (q < NA + NB) {
@@ -191,80 +203,60 @@ struct StageCopy {
     }
 
     __device__ __forceinline__ void copy(uint8_t *stage, int64_t k0) const {
-        using L = Lay<A8>;
-        const uint32_t ak = (uint32_t)(A8 ? k0 : k0 / 2), bk = (uint32_t)(k0 / 2), sk = (uint32_t)(k0 / 32);
 #pragma unroll
-        for (int q = 0; q < NA; ++q) dma16(xc + (ag[q] + ak), stage + L::A_OFF + (wave + WAVES * q) * 1024);
-#pragma unroll
-        for (int q = 0; q < NB; ++q) dma16(wc + (bg[q] + bk), stage + L::B_OFF + (wave + WAVES * q) * 1024);
-#pragma unroll
-        for (int q = 0; q < NS; ++q) {
-            dma4(xs + (sag[q] + sk), stage + L::SA_OFF + (wave + WAVES * q) * 256);
-            dma4(ws + (sbg[q] + sk), stage + L::SB_OFF + (wave + WAVES * q) * 256);
-        }
+        for (int q = 0; q < COPIES; ++q) copy_one(stage, k0, q);
     }
 };
 
-// A 4-byte-element operand (E2M1) uses the low half of the register block;
-// the upper half is left undefined so that no registers are spent on it.
+// An E2M1 operand uses the low half of the register block; the upper half is
+// left undefined so that no registers are spent on it.
 __device__ __forceinline__ v8i widen(u32x4 v) {
     const v8i w = __builtin_bit_cast(v8i, __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1));
     return w;
 }
 
-template <bool A8, int TM, int TN>
-__device__ __forceinline__ void read_frags(const uint8_t *sm, int aoff, int boff, v8i (&a)[TM], v8i (&b)[TN]) {
-    using L = Lay<A8>;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        if (A8) {
-            const u32x4 lo = *reinterpret_cast<const u32x4 *>(sm + aoff + i * 32 * L::AROW);
-            const u32x4 hi = *reinterpret_cast<const u32x4 *>(sm + (aoff ^ 16) + i * 32 * L::AROW);
-            a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        } else {
-            a[i] = widen(*reinterpret_cast<const u32x4 *>(sm + aoff + i * 32 * L::AROW));
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = widen(*reinterpret_cast<const u32x4 *>(sm + boff + j * 32 * L::BROW));
-}
+// Per-lane LDS offsets of one k-step's fragments. E2M1 A and B: piece
+// 2 s + lh of the lane's row. E4M3 A: the lane holds k 16 lh .. 16 lh + 15
+// and 32 + 16 lh .. 32 + 16 lh + 15 of the step (pieces 4 s + lh and
+// 4 s + 2 + lh), a layout verified with in-bounds one-hot probes.
+template <bool A8>
+struct FragOff {
+    int a_lo, a_hi, b;
+};
 
 template <bool A8>
-__device__ __forceinline__ v8i read_a(const uint8_t *sm, int aoff, int i) {
+__device__ __forceinline__ v8i read_a(const uint8_t *sm, const FragOff<A8> &o, int i) {
     using L = Lay<A8>;
     if (A8) {
-        const u32x4 lo = *reinterpret_cast<const u32x4 *>(sm + aoff + i * 32 * L::AROW);
-        const u32x4 hi = *reinterpret_cast<const u32x4 *>(sm + (aoff ^ 16) + i * 32 * L::AROW);
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(sm + o.a_lo + i * 32 * L::AROW);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(sm + o.a_hi + i * 32 * L::AROW);
         return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    return widen(*reinterpret_cast<const u32x4 *>(sm + aoff + i * 32 * L::AROW));
+    return widen(*reinterpret_cast<const u32x4 *>(sm + o.a_lo + i * 32 * L::AROW));
 }
 template <bool A8>
-__device__ __forceinline__ v8i read_b(const uint8_t *sm, int boff, int j) {
-    return widen(*reinterpret_cast<const u32x4 *>(sm + boff + j * 32 * Lay<A8>::BROW));
+__device__ __forceinline__ v8i read_b(const uint8_t *sm, const FragOff<A8> &o, int j) {
+    return widen(*reinterpret_cast<const u32x4 *>(sm + o.b + j * 32 * Lay<A8>::BROW));
 }
-__device__ __forceinline__ void read_scale(const uint8_t *sm, int off, int lh, uint32_t (&w)[2]) {
-    const u32x2 v = *reinterpret_cast<const u32x2 *>(sm + off);
-    w[0] = v.x >> (8 * lh);
-    w[1] = v.y >> (8 * lh);
+template <bool A8, int TM, int TN>
+__device__ __forceinline__ void read_frags(const uint8_t *sm, const FragOff<A8> &o, v8i (&a)[TM], v8i (&b)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = read_a<A8>(sm, o, i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = read_b<A8>(sm, o, j);
 }
 
-// The 8 scale bytes of each of the lane's rows for one stage, shifted so
-// that the byte of step s sits at bits 16 (s % 2) .. of word s / 2.
-template <int TM, int TN>
-__device__ __forceinline__ void read_scales(const uint8_t *sm, int saoff, int sboff, int lh, uint32_t (&sa)[TM][2],
-                                            uint32_t (&sb)[TN][2]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const u32x2 v = *reinterpret_cast<const u32x2 *>(sm + saoff + i * 32 * 8);
-        sa[i][0] = v.x >> (8 * lh);
-        sa[i][1] = v.y >> (8 * lh);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const u32x2 v = *reinterpret_cast<const u32x2 *>(sm + sboff + j * 32 * 8);
-        sb[j][0] = v.x >> (8 * lh);
-        sb[j][1] = v.y >> (8 * lh);
+// The scale bytes of a row for one stage, shifted by the lane half: the byte
+// of step s then sits at byte 2 (s % 2) of word s / 2, where the MFMA's byte
+// select picks it.
+template <int SW>
+__device__ __forceinline__ void read_scale(const uint8_t *p, int lh, uint32_t (&w)[SW]) {
+    if (SW == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+        w[0] = v.x >> (8 * lh);
+        w[SW - 1] = v.y >> (8 * lh);
+    } else {
+        w[0] = *reinterpret_cast<const uint32_t *>(p) >> (8 * lh);
     }
 }
 
@@ -279,15 +271,14 @@ __device__ __forceinline__ void put_out<float>(float *y, int64_t idx, float v) {
     y[idx] = v;
 }
 
-// Keeps the compiler from moving LDS reads across it (the MFMA steps are
-// then fed in order: the reads of step s + 1 overlap step s's MFMAs).
+// Keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void mem_fence() { asm volatile("" ::: "memory"); }
 
 // One MFMA per 32 x 32 tile for a k-step of 64. The scale words hold the
 // step's E8M0 byte at byte OP (0 or 2), which the matrix core selects itself.
-template <int OP, bool A8, int TM, int TN>
+template <int OP, bool A8, int TM, int TN, int SW>
 __device__ __forceinline__ void mfma_step(f32x16 (&acc)[TM][TN], const v8i (&a)[TM], const v8i (&b)[TN],
-                                          const uint32_t (&sa)[TM][2], const uint32_t (&sb)[TN][2], int w) {
+                                          const uint32_t (&sa)[TM][SW], const uint32_t (&sb)[TN][SW], int w) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -303,11 +294,11 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[TM][TN], const v8i (&a)[
 // (rows r and r + 4) fall in different banks.
 template <typename YT, int COLS>
 struct OutStage {
-    static constexpr int E = 16 / (int)sizeof(YT);            // elements per 16-byte piece
-    static constexpr int CH = COLS / E;                        // pieces per row
-    static constexpr int PITCH = COLS * (int)sizeof(YT) + 16 * (int)sizeof(YT) / 2;
+    static constexpr int E = 16 / (int)sizeof(YT);  // elements per 16-byte piece
+    static constexpr int CH = COLS / E;              // pieces per row
+    static constexpr int PITCH = COLS * (int)sizeof(YT) + 8 * (int)sizeof(YT);
     static constexpr int BYTES = 32 * PITCH;
-    static constexpr int NI = 32 * CH / 64;                    // 16-byte reads per lane
+    static constexpr int NI = 32 * CH / 64;          // 16-byte reads per lane
 };
 
 template <typename YT>
@@ -321,24 +312,25 @@ __device__ __forceinline__ void lds_put<float>(uint8_t *p, float v) {
     *reinterpret_cast<float *>(p) = v;
 }
 
-// Y tile 256 x 256: WGM x WGN waves, wave (wm, wn) owning a TM x TN block of
-// 32 x 32 MFMA tiles. A k-step of 64 is one MFMA per tile: lane half lh holds
-// k 32 lh .. 32 lh + 31 of the step (piece 2 s + lh of a stage) for its row (A)
-// or column (B), under one E8M0 byte each. Two LDS stages: the barrier of
-// stage st sits before its last step, after which stage st + 2 is copied into
-// st's buffer and stage st + 1's scales and first fragments are read while
-// the last step's MFMAs run.
-template <int WGM, int WGN, bool A8, typename YT>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_mxgemm(const uint8_t *__restrict__ xc,
-                                                           const uint8_t *__restrict__ xs,
-                                                           const uint8_t *__restrict__ wc,
-                                                           const uint8_t *__restrict__ ws, YT *__restrict__ Y,
-                                                           int64_t ldy, int64_t M, int64_t N, int64_t K, int tiles_m,
-                                                           int tiles_n) {
-    constexpr int WAVES = WGM * WGN, TM = BM / WGM / 32, TN = BN / WGN / 32;
+// Y tile 256 x 256 from four waves (2 x 2), wave (wm, wn) owning a 4 x 4 block
+// of 32 x 32 MFMA tiles. A k-step of 64 is one MFMA per tile: lane half lh
+// holds its share of the step's k for its row (A) or column (B); the E8M0
+// byte of k-block 2 s + lh goes with it. Each stage is a straight-line block
+// (a branch inside it lets the compiler sink every MFMA below every LDS
+// read): step s's fragments are read during step s - 1's MFMAs. Before the
+// last step, stage st + 1 has landed and every wave has finished reading
+// stage st (barrier); the copies of stage st + 2 into st's buffer and the
+// reads of stage st + 1's scales and first fragments are then spread over
+// the last step's MFMAs.
+template <bool A8, typename YT>
+__global__ __launch_bounds__(256) void k_mxgemm(const uint8_t *__restrict__ xc, const uint8_t *__restrict__ xs,
+                                                const uint8_t *__restrict__ wc, const uint8_t *__restrict__ ws,
+                                                YT *__restrict__ Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                                int tiles_m, int tiles_n) {
+    constexpr int WGM = 2, WGN = 2, WAVES = WGM * WGN, TM = BM / WGM / 32, TN = BN / WGN / 32;
     using L = Lay<A8>;
     using CP = StageCopy<A8, WAVES>;
-    static_assert(L::NST == 2, "two-stage ring");
+    constexpr int S = L::STEPS, SW = L::SW;
     __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
     // XCD-aware banded order (as in the bf16 GEMM): the workgroups of one XCD
     // cover a block of GM tile rows x (per-XCD count / GM) tile columns
@@ -357,21 +349,21 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_mxgemm(const uint8_t *__rest
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wave / WGN, wn = wave % WGN;
     const int lr = lane % 32, lh = lane / 32;
-    const int nst = (int)(K / BKS);
+    const int nst = (int)(K / L::BK);
 
-    // per-lane LDS offsets; every row this lane reads is 32 t + (a multiple of
-    // 16) + lr, so g(n) = g(lr)
+    // per-lane LDS offsets; every row this lane reads is a multiple of 32
+    // plus lr, so its swizzle is that of lr
     const int ra = wm * (32 * TM) + lr, rbn = wn * (32 * TN) + lr;
-    const int gl = gsw(lr);
-    int a_off[4], b_off[4];
+    FragOff<A8> fo[S];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int p = 2 * s + lh;
-        a_off[s] = A8 ? (L::A_OFF + ra * L::AROW + (((2 * p) ^ gl) * 16))  // fp8: 32 bytes = pieces 2p, 2p+1
-                      : (L::A_OFF + ra * L::AROW + ((p ^ gl) * 16));
-        b_off[s] = L::B_OFF + rbn * L::BROW + ((p ^ gl) * 16);
+    for (int s = 0; s < S; ++s) {
+        const int ga = swz<L::AROW / 16>(lr), gb = swz<L::BROW / 16>(lr);
+        const int pa = A8 ? 4 * s + lh : 2 * s + lh;
+        fo[s].a_lo = L::A_OFF + ra * L::AROW + ((pa ^ ga) * 16);
+        fo[s].a_hi = L::A_OFF + ra * L::AROW + (((pa + 2) ^ ga) * 16);
+        fo[s].b = L::B_OFF + rbn * L::BROW + (((2 * s + lh) ^ gb) * 16);
     }
-    const int sa_off = L::SA_OFF + ra * 8, sb_off = L::SB_OFF + rbn * 8;
+    const int sa_off = L::SA_OFF + ra * L::SROW, sb_off = L::SB_OFF + rbn * L::SROW;
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -382,67 +374,68 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_mxgemm(const uint8_t *__rest
     const CP cp(xc, xs, wc, ws, M, N, K, m0, n0, lane, wave);
     cp.copy(smem, 0);
     if (nst > 1) {
-        cp.copy(smem + L::STAGE, BKS);
+        cp.copy(smem + L::STAGE, L::BK);
         wait_vm<CP::COPIES>();
     } else {
         wait_vm<0>();
     }
     lds_barrier();
-    uint32_t sa[TM][2], sb[TN][2];
+    uint32_t sa[TM][SW], sb[TN][SW];
     v8i a[2][TM], b[2][TN];
-    read_scales<TM, TN>(smem, sa_off, sb_off, lh, sa, sb);
-    read_frags<A8, TM, TN>(smem, a_off[0], b_off[0], a[0], b[0]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) read_scale<SW>(smem + sa_off + i * 32 * L::SROW, lh, sa[i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) read_scale<SW>(smem + sb_off + j * 32 * L::SROW, lh, sb[j]);
+    read_frags<A8, TM, TN>(smem, fo[0], a[0], b[0]);
 
-    // The stage body is straight-line, so that the order fixed by the
-    // scheduling barriers holds (the compiler otherwise sinks the MFMAs below
-    // every LDS read). Its tail is the same at every stage: past the barrier,
-    // stage min(st + 2, nst - 1) is copied into stage st's buffer and the
-    // other buffer's scales and first fragments are read. Near the end these
-    // are repeats that nothing uses; they stay in bounds.
+    // The tail of every stage is the same: past the barrier, stage
+    // min(st + 2, nst - 1) is copied into stage st's buffer and the other
+    // buffer's scales and first fragments are read. Near the end these are
+    // repeats that nothing uses; they stay in bounds and keep every wait's
+    // count fixed.
     for (int st = 0; st < nst; ++st) {
         uint8_t *const sm = smem + (st & 1) * L::STAGE;
         uint8_t *const nx = smem + ((st + 1) & 1) * L::STAGE;
-        const int64_t kc = (int64_t)min(st + 2, nst - 1) * BKS;
-        uint32_t na[TM][2], nb[TN][2];
+        const int64_t kc = (int64_t)min(st + 2, nst - 1) * L::BK;
+        uint32_t na[TM][SW], nb[TN][SW];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < S; ++s) {
             // step s's fragments were read one step ago; waiting for them
             // here, before this step's reads are issued, keeps the count of
             // reads in flight within what the counter tracks
             wait_lds();
-            if (s < 3) {
-                read_frags<A8, TM, TN>(sm, a_off[s + 1], b_off[s + 1], a[(s + 1) & 1], b[(s + 1) & 1]);
+            if (s < S - 1) {
+                read_frags<A8, TM, TN>(sm, fo[s + 1], a[(s + 1) & 1], b[(s + 1) & 1]);
                 mem_fence();
                 __builtin_amdgcn_sched_barrier(0);
                 if (s % 2 == 0)
-                    mfma_step<0, A8, TM, TN>(acc, a[s & 1], b[s & 1], sa, sb, s / 2);
+                    mfma_step<0, A8, TM, TN, SW>(acc, a[s & 1], b[s & 1], sa, sb, s / 2);
                 else
-                    mfma_step<2, A8, TM, TN>(acc, a[s & 1], b[s & 1], sa, sb, s / 2);
+                    mfma_step<2, A8, TM, TN, SW>(acc, a[s & 1], b[s & 1], sa, sb, s / 2);
             } else {
                 // stage st + 1 (copied one stage ago) has landed once nothing
-                // is outstanding; past the barrier no wave reads stage st.
-                // The copies of stage st + 2 and the reads of stage st + 1's
-                // first fragments and scales are spread over this step's
-                // MFMAs, a few after each.
+                // is outstanding; past the barrier no wave reads stage st
                 wait_vm<0>();
                 lds_barrier();
+                constexpr int OPL = 2 * ((S - 1) % 2), WL = (S - 1) / 2;
 #pragma unroll
                 for (int t = 0; t < TM * TN; ++t) {
                     const int i = t / TN, j = t % TN;
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        a[1][i], b[1][j], acc[i][j], A8 ? 0 : 4, 4, 2, (int)sa[i][1], 2, (int)sb[j][1]);
+                        a[(S - 1) & 1][i], b[(S - 1) & 1][j], acc[i][j], A8 ? 0 : 4, 4, OPL, (int)sa[i][WL], OPL,
+                        (int)sb[j][WL]);
                     constexpr int PER = (CP::COPIES + TM * TN - 1) / (TM * TN);
 #pragma unroll
                     for (int q = PER * t; q < PER * t + PER; ++q)
                         if (q < CP::COPIES) cp.copy_one(sm, kc, q);
                     if (t < TM)
-                        a[0][t] = read_a<A8>(nx, a_off[0], t);
+                        a[0][t] = read_a<A8>(nx, fo[0], t);
                     else if (t < TM + TN)
-                        b[0][t - TM] = read_b<A8>(nx, b_off[0], t - TM);
+                        b[0][t - TM] = read_b<A8>(nx, fo[0], t - TM);
                     else if (t < 2 * TM + TN)
-                        read_scale(nx, sa_off + (t - TM - TN) * 32 * 8, lh, na[t - TM - TN]);
+                        read_scale<SW>(nx + sa_off + (t - TM - TN) * 32 * L::SROW, lh, na[t - TM - TN]);
                     else if (t < 2 * TM + 2 * TN)
-                        read_scale(nx, sb_off + (t - 2 * TM - TN) * 32 * 8, lh, nb[t - 2 * TM - TN]);
+                        read_scale<SW>(nx + sb_off + (t - 2 * TM - TN) * 32 * L::SROW, lh, nb[t - 2 * TM - TN]);
                     mem_fence();
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -451,17 +444,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_mxgemm(const uint8_t *__rest
             mem_fence();
         }
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            sa[i][0] = na[i][0];
-            sa[i][1] = na[i][1];
-        }
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            sb[j][0] = nb[j][0];
-            sb[j][1] = nb[j][1];
-        }
+            for (int w = 0; w < SW; ++w) sa[i][w] = na[i][w];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int w = 0; w < SW; ++w) sb[j][w] = nb[j][w];
     }
-    wait_vm<0>();  // the last (unused) copies land before the waves end
+    wait_vm<0>();   // the last (unused) copies land before the waves end
     lds_barrier();  // every wave is done with the stage buffers
 
     using O = OutStage<YT, 32 * TN>;
@@ -520,8 +511,10 @@ __global__ __launch_bounds__(256) void k_mxgemm_small(const uint8_t *__restrict_
         const bool in = kk < K;
         v8i a, b;
         if (A8) {
-            const u32x4 lo = in ? ld16(xc + ma * xrow + kk) : u32x4{0u, 0u, 0u, 0u};
-            const u32x4 hi = in ? ld16(xc + ma * xrow + kk + 16) : u32x4{0u, 0u, 0u, 0u};
+            // E4M3: k 16 lh .. 16 lh + 15 and 32 + 16 lh .. 32 + 16 lh + 15 of the step
+            const bool hin = k0 + 32 < K;
+            const u32x4 lo = ld16(xc + ma * xrow + k0 + 16 * lh);
+            const u32x4 hi = hin ? ld16(xc + ma * xrow + k0 + 32 + 16 * lh) : u32x4{0u, 0u, 0u, 0u};
             a = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         } else {
             const u32x4 v = in ? ld16(xc + ma * xrow + kk / 2) : u32x4{0u, 0u, 0u, 0u};
@@ -545,18 +538,14 @@ template <bool A8, typename YT>
 hipError_t run_mxgemm(const qbn_tensor &w, int64_t m, const void *xc, const void *xs, void *y, int64_t ldy,
                       hipStream_t s) {
     const int64_t xbytes = m * (A8 ? w.k : w.k / 2), wbytes = w.n * (w.k / 2);
-    const bool big = !A8 && m >= BM && w.n >= BN && (w.k % BKS) == 0 && xbytes < ((int64_t)1 << 31) &&
+    const bool big = m >= BM && w.n >= BN && (w.k % Lay<A8>::BK) == 0 && xbytes < ((int64_t)1 << 31) &&
                      wbytes < ((int64_t)1 << 31) && ((uintptr_t)xs % 4) == 0 && ((uintptr_t)w.scales % 4) == 0;
-    if constexpr (!A8) {
-        if (big) {
-            const int64_t tm = (m + BM - 1) / BM, tn = (w.n + BN - 1) / BN;
-            hipLaunchKernelGGL((k_mxgemm<2, 2, false, YT>), dim3((unsigned)(tm * tn)), dim3(4 * 64), 0, s,
-                               (const uint8_t *)xc, (const uint8_t *)xs, (const uint8_t *)w.data,
-                               (const uint8_t *)w.scales, (YT *)y, ldy, m, w.n, w.k, (int)tm, (int)tn);
-            return hipGetLastError();
-        }
-    }
-    {
+    if (big) {
+        const int64_t tm = (m + BM - 1) / BM, tn = (w.n + BN - 1) / BN;
+        hipLaunchKernelGGL((k_mxgemm<A8, YT>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, (const uint8_t *)xc,
+                           (const uint8_t *)xs, (const uint8_t *)w.data, (const uint8_t *)w.scales, (YT *)y, ldy, m,
+                           w.n, w.k, (int)tm, (int)tn);
+    } else {
         const int64_t tm = (m + 31) / 32, tn = (w.n + 31) / 32;
         hipLaunchKernelGGL((k_mxgemm_small<A8, YT>), dim3((unsigned)((tm * tn + 3) / 4)), dim3(256), 0, s,
                            (const uint8_t *)xc, (const uint8_t *)xs, (const uint8_t *)w.data,

@@ -203,8 +203,8 @@ int32_t qbn_quantized_gemm_mx(const qbn_tensor *w, int64_t m, int32_t x_format, 
     int32_t st = check_tensor(w);
     if (st) return st;
     if (w->format != QBN_MXFP4) return QBN_ERR_UNSUPPORTED;
-    if (x_format != QBN_MXFP4) return (x_format == QBN_MXFP8 || known_format(x_format)) ? QBN_ERR_UNSUPPORTED
-                                                                                        : QBN_ERR_FORMAT;
+    if (x_format != QBN_MXFP4 && x_format != QBN_MXFP8)
+        return known_format(x_format) ? QBN_ERR_UNSUPPORTED : QBN_ERR_FORMAT;
     if (y_dtype < QBN_F32 || y_dtype > QBN_F16) return QBN_ERR_FORMAT;
     if (y_dtype != QBN_F32 && y_dtype != QBN_BF16) return QBN_ERR_DTYPE;
     if (m < 0 || m > kMaxElems) return QBN_ERR_SHAPE;

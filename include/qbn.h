@@ -101,7 +101,7 @@ typedef enum qbn_format {
     QBN_Q4_0 = 4,
     QBN_GPTQ4 = 5,
     QBN_AWQ4 = 6,
-    QBN_MXFP8 = 7 /* activations only (qbn_quantize_mx): E4M3FN elements, one E8M0 scale per 32 */
+    QBN_MXFP8 = 7 /* activations only (qbn_quantize_mx, qbn_quantized_gemm_mx): E4M3FN elements, one E8M0 scale per 32 */
 } qbn_format;
 
 typedef enum qbn_dtype {
@@ -223,9 +223,10 @@ QBN_API int32_t qbn_quantize_mx(const void *x, int32_t x_dtype, int64_t m, int64
  * MXFP4 weights on the gfx950 block-scaled FP4 matrix instruction
  * (v_mfma_scale_f32_32x32x64_f8f6f4), both E8M0 scales applied by the matrix
  * core ([WK] sections 5 and 7, the native FP4 path; [FB] section 3).
- * w: QBN_MXFP4 [n][k/2] + E8M0 [n][k/32]; x_format: QBN_MXFP4 (codes
- * [m][k/2] and scales [m][k/32] as written by qbn_quantize_mx, codes 16-byte
- * aligned); QBN_MXFP8 is not accepted by this version (QBN_ERR_UNSUPPORTED).
+ * w: QBN_MXFP4 [n][k/2] + E8M0 [n][k/32]; x_format: QBN_MXFP4 (W4A4: E2M1
+ * codes [m][k/2]) or QBN_MXFP8 (W4A8: E4M3FN bytes [m][k], run as E4M3 x
+ * E2M1 on the same instruction), codes and scales [m][k/32] as written by
+ * qbn_quantize_mx, codes 16-byte aligned.
  * Y: QBN_BF16 (RNE of the binary32 sum) or QBN_F32, [m][ldy], ldy >= n.
  * Products are exact; the sum is binary32 in k-steps of 64, within
  * 1e-5 * sum |x_hat w_hat| + 1e-6 of the exact value (before the bf16

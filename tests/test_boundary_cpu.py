@@ -162,7 +162,7 @@ def test_mx_rejections(lib):
     assert q(None, F32, 0, 64, 64, MX, None, None, None) == OK
     g = lib.qbn_quantized_gemm_mx
     assert g(T(NV, 8, 64), 4, MX, A, B, C, BF16, 8, None) == UNSUP
-    assert g(T(MX, 8, 64), 4, MX8, A, B, C, BF16, 8, None) == UNSUP
+    assert g(T(MX, 8, 64), 4, MX8, A + 8, B, C, BF16, 8, None) == ALIGN
     assert g(T(MX, 8, 64), 4, 9, A, B, C, BF16, 8, None) == FORMAT
     assert g(T(MX, 8, 64), 4, MX, A, B, C, 2, 8, None) == DTYPE
     assert g(T(MX, 8, 64), 4, MX, A, B, C, BF16, 4, None) == SHAPE
