@@ -51,6 +51,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD published
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak, AMD published (context only)
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 matrix peak, AMD published
 ROTATE_BYTES = 600e6
 
 # Algorithmic bytes / flops per step (read + write of every operand once).
@@ -89,6 +90,13 @@ WORKLOADS = {
         flops=2.0 * 2048 * 8192 * 8192,
         bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 * 2 + 2 * (2048 * 4096 + 2048 * 256) + 2048 * 8192 * 2,
         kernel_bytes=8192 * 4096 + 8192 * 256 + 2048 * 4096 + 2048 * 256 + 2048 * 8192 * 2),
+    "mxfp8_w4a8_gemm": dict(
+        cfg=4, kind="mxgemm", xfmt="mxfp8", unit="TFLOP/s", dtype="fp8 x fp4",
+        desc="MX-native W4A8 GEMM: OCP MX quantization of X bf16 2048x8192 to MXFP8 (E4M3) + W 8192x8192 MXFP4 on the "
+             "block-scaled FP8 x FP4 matrix cores -> Y bf16, fp32 accumulate",
+        flops=2.0 * 2048 * 8192 * 8192,
+        bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 * 2 + 2 * (2048 * 8192 + 2048 * 256) + 2048 * 8192 * 2,
+        kernel_bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 + 2048 * 256 + 2048 * 8192 * 2),
     "gptq_to_awq": dict(
         cfg=5, kind="repack", unit="GB/s", src="gptq4", dst="awq4",
         desc="int4 repack GPTQ int32 [K/8][N] -> AWQ int32 [K][N/8], K x N = 4096 x 11008",
@@ -204,11 +212,13 @@ def build_steps(name, spec, dev):
         d0 = host_to_device(inp["data"], dev)
         s0 = host_to_device(inp["scales"], dev)
         X = host_to_device(inp["X"], dev).view(torch.bfloat16)
-        xc = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+        xfmt = spec.get("xfmt", "mxfp4")
+        xc = torch.empty((m, k if xfmt == "mxfp8" else k // 2), dtype=torch.uint8, device=dev)
         xs = torch.empty((m, k // 32), dtype=torch.uint8, device=dev)
         Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        quant = qbn.prepare_quantize_mx(X, xc, xs, "mxfp4")
-        gemms = [qbn.prepare_gemm_mx(qbn.QTensor("mxfp4", n, k, d0.clone(), s0.clone()), xc, xs, Y) for _ in range(R)]
+        quant = qbn.prepare_quantize_mx(X, xc, xs, xfmt)
+        gemms = [qbn.prepare_gemm_mx(qbn.QTensor("mxfp4", n, k, d0.clone(), s0.clone()), xc, xs, Y, xfmt)
+                 for _ in range(R)]
 
         def step(g):
             def run():
@@ -309,9 +319,10 @@ def cpu_baseline(name, spec, inp, budget_s):
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < budget_s:
             i = int(rng.integers(0, m))
-            xc, xs = oracle.mx_quantize(inp["X"][i:i + 1], oracle.MXFP4)
+            xf = oracle.MXFP8 if spec.get("xfmt") == "mxfp8" else oracle.MXFP4
+            xc, xs = oracle.mx_quantize(inp["X"][i:i + 1], xf)
             nn = rng.integers(0, n, 16)
-            oracle.mx_gemm_entries(inp["data"], inp["scales"], k, oracle.MXFP4, xc, xs, np.zeros(16, np.int64), nn)
+            oracle.mx_gemm_entries(inp["data"], inp["scales"], k, xf, xc, xs, np.zeros(16, np.int64), nn)
             done += 16
         t = time.perf_counter() - t0
         return dict(value=2.0 * k * done / t / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
@@ -466,12 +477,13 @@ def main():
     del cg, bufs
 
     if spec["kind"] in ("gemm", "mxgemm"):
-        peak = BF16_MFMA_PEAK_TFLOPS if spec["kind"] == "gemm" else FP4_MFMA_PEAK_TFLOPS
+        peak = BF16_MFMA_PEAK_TFLOPS if spec["kind"] == "gemm" else (
+            FP8_MFMA_PEAK_TFLOPS if spec.get("xfmt") == "mxfp8" else FP4_MFMA_PEAK_TFLOPS)
         value = spec["flops"] / (ms_step * 1e-3) / 1e12
         achieved = spec["flops"] / (kernel_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
                     frac=round(achieved / peak, 4), traffic=recorded_traffic(args.workload))
-        metric = "FP4 GEMM TFLOP/s (% MFMA peak)"
+        metric = "FP8 x FP4 GEMM TFLOP/s (% MFMA peak)" if spec.get("xfmt") == "mxfp8" else "FP4 GEMM TFLOP/s (% MFMA peak)"
     else:
         value = spec["bytes"] / (ms_step * 1e-3) / 1e9
         achieved = spec.get("kernel_bytes", spec["bytes"]) / (kernel_ms * 1e-3) / 1e9
@@ -514,7 +526,7 @@ def main():
             "device_copy_gbs": round(copy_gbs, 1),
             "device_copy_note": "plain device-to-device copy of the step's byte count, read + write (context only)",
             **({"fp4_peak_frac": round(spec["flops"] / (kernel_ms * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS, 4)}
-               if "flops" in spec else {}),
+               if "flops" in spec and spec.get("xfmt") != "mxfp8" else {}),
             "timed_wall_s": round(wall, 4),
             "gpu": torch.cuda.get_device_name(0),
             "host": platform.processor() or platform.machine(),
