@@ -81,6 +81,7 @@ def _load():
         lib.oracle_q4_0_pack.argtypes = [P, P, I64, I64, P]
         lib.oracle_q4_0_unpack.argtypes = [P, I64, I64, P, P]
         lib.oracle_affine_dequant.argtypes = [P, P, P, I64, I64, I64, P]
+        lib.oracle_gemv_kn.argtypes = [P, I64, I64, P, ctypes.c_int, P, I64, P, P, P]
         lib.oracle_dequant_rows.argtypes = [ctypes.c_int, P, P, ctypes.c_float, I64, P, I64, P]
         lib.oracle_dequant_rows.restype = ctypes.c_int
         lib.oracle_gemv_rows.argtypes = [ctypes.c_int, P, P, ctypes.c_float, I64, P, ctypes.c_int, P, I64,
@@ -280,6 +281,38 @@ def affine_dequant(q: np.ndarray, scale_bits: np.ndarray, zeros: np.ndarray, gro
     out = np.zeros((K, N), dtype=np.float32)
     _load().oracle_affine_dequant(_ptr(q), _ptr(s), _ptr(z), K, N, group, _ptr(out))
     return out
+
+
+def gemv_kn(W: np.ndarray, x: np.ndarray, cols):
+    """(y, S) in binary64 for columns cols of a [K][N] binary32 weight:
+    y = x @ W[:, cols], S = |x| @ |W[:, cols]|. x float32 or bfloat16 bits."""
+    Wc = np.ascontiguousarray(W, dtype=np.float32)
+    K, N = Wc.shape
+    xa = np.ascontiguousarray(x)
+    if xa.dtype == np.float32:
+        xdt = 0
+    elif xa.dtype == np.uint16:
+        xdt = 1
+    else:
+        raise TypeError("x must be float32 or bfloat16 bits (uint16)")
+    assert xa.size == K
+    c = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
+    y = np.zeros(c.size, np.float64)
+    sa = np.zeros(c.size, np.float64)
+    xscr = np.zeros(K, np.float64)
+    _load().oracle_gemv_kn(_ptr(Wc), K, N, _ptr(xa), xdt, _ptr(c), c.size, _ptr(y), _ptr(sa), _ptr(xscr))
+    return y, sa
+
+
+def int4_gemv(fmt: str, data: np.ndarray, scale_bits: np.ndarray, zeros: np.ndarray, group: int, x: np.ndarray,
+              cols):
+    """(y, S) for an int4 K x N weight: fmt "gptq4" (int32 [K/8][N]) or
+    "awq4" (int32 [K][N/8]), unpacked to the logical matrix, dequantized as
+    s * (q - z), then y[c] = sum_k w[k][c] x[k]."""
+    q = gptq_unpack(data) if fmt == "gptq4" else awq_unpack(data)
+    sb = np.asarray(scale_bits)
+    sb = sb.view(np.uint16) if sb.dtype == np.float16 else sb
+    return gemv_kn(affine_dequant(q, sb, zeros, group), x, cols)
 
 
 # ---------------------------------------------------------------- dequant and dots

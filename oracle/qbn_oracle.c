@@ -478,6 +478,31 @@ ORACLE_API int oracle_gemv_rows(int fmt, const uint8_t *data, const uint8_t *sca
     return 0;
 }
 
+/* GEMV over a K x N weight stored input-major, as the GPTQ / AWQ logical
+ * matrix is ([BP] "Real layouts compared"): y[i] = sum_k W[k][cols[i]] *
+ * x[k] and s[i] = sum_k |W x|, with W the binary32 values of
+ * oracle_affine_dequant. xscratch holds K doubles (caller-provided). */
+ORACLE_API void oracle_gemv_kn(const float *W, int64_t K, int64_t N, const void *x, int xdtype,
+                               const int64_t *cols, int64_t ncols, double *y, double *sabs, double *xscratch)
+{
+    load_x(x, xdtype, K, xscratch);
+    for (int64_t i = 0; i < ncols; ++i) {
+        double sum = 0.0, comp = 0.0, a = 0.0;
+        for (int64_t kk = 0; kk < K; ++kk) {
+            double p = (double)W[kk * N + cols[i]] * xscratch[kk];
+            double t = sum + p;
+            if (fabs(sum) >= fabs(p))
+                comp += (sum - t) + p;
+            else
+                comp += (p - t) + sum;
+            sum = t;
+            a += fabs(p);
+        }
+        y[i] = sum + comp;
+        sabs[i] = a;
+    }
+}
+
 /* Sampled GEMM entries: Y[m][n] = sum_k X[m][k] * w[n][k] for the pairs
  * (ms[i], ns[i]); X is bfloat16 bits [M][ldx]. Entries are grouped by the
  * caller; each weight row is decoded once per call of this function for

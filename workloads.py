@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five workloads (host numpy arrays).
+"""Seeded synthetic inputs for the seven workloads (host numpy arrays).
 
 This module holds no decoding, dot-product or repacking arithmetic: it only
 draws random bytes and numbers with the distributions below and lays them
@@ -32,6 +32,12 @@ Workloads (n = output rows, k = reduction length):
   6  W4A8 decode GEMV, Q4_K 14336 x 4096 times int8-quantized activations:
      blocks and x drawn exactly as workload 3 (x f32 N(0,1) [k]); the
      activation codes are made from x by the library / the oracle.
+  7  int4 decode GEMV, K x N = 4096 x 11008, group 128 (the weights of
+     workload 5 in each int4 layout, drawn independently): GPTQ qweight
+     uniform u32 [K/8][N]; AWQ qweight uniform u32 [K][N/8]; fp16 scales
+     ~ U[1e-3,1e-2] [K/128][N]; zero points U{0..15} u8 [K/128][N]; Q4_0
+     blocks [N][K/32][18] with fp16 d ~ U[1e-3,1e-2] and 16 uniform code
+     bytes; x f32 N(0,1) [K].
 """
 from __future__ import annotations
 
@@ -46,6 +52,7 @@ SHAPES = {
     4: dict(fmt="mxfp4", n=8192, k=8192, m=2048),
     5: dict(fmt="gptq4", K=4096, N=11008, group=128),
     6: dict(fmt="q4_k", n=14336, k=4096),
+    7: dict(fmt="int4", K=4096, N=11008, group=128),
 }
 
 
@@ -104,6 +111,16 @@ def int4_affine(rng, K: int, N: int, group: int):
     return qweight, scales, zeros
 
 
+def q4_0_blocks(rng, n: int, k: int):
+    """Q4_0 blocks u8 [n][k/32][18]: fp16 d ~ U[1e-3, 1e-2] in bytes 0-1
+    (little-endian), 16 uniform code bytes."""
+    d = rng.uniform(1e-3, 1e-2, size=(n, k // 32)).astype(np.float16)
+    blocks = np.zeros((n, k // 32, 18), np.uint8)
+    blocks[:, :, :2] = d.view(np.uint8).reshape(n, k // 32, 2)
+    blocks[:, :, 2:] = rng.integers(0, 256, size=(n, k // 32, 16), dtype=np.uint8)
+    return blocks
+
+
 def x_f32(rng, k: int):
     return rng.standard_normal(k).astype(np.float32)
 
@@ -114,7 +131,7 @@ def x_bf16(rng, k: int):
 
 def workload(c: int, seed: int | None = None, n: int | None = None, k: int | None = None,
              m: int | None = None) -> dict:
-    """Inputs of workload c (1..6). n / k / m override the shape (same
+    """Inputs of workload c (1..7). n / k / m override the shape (same
     distributions) so that tests can run the same recipe at small sizes."""
     seed = 1000 + c if seed is None else seed
     rng = _rng(seed)
@@ -148,4 +165,16 @@ def workload(c: int, seed: int | None = None, n: int | None = None, k: int | Non
         g = sh["group"]
         qweight, scales, zeros = int4_affine(rng, K, N, g)
         return dict(fmt="gptq4", K=K, N=N, group=g, qweight=qweight, scales=scales, zeros=zeros, seed=seed)
-    raise ValueError("workload must be 1..6")
+    if c == 7:
+        K = k or sh["K"]
+        N = n or sh["N"]
+        g = sh["group"]
+        gptq = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
+        awq = rng.integers(0, 2**32, size=(K, N // 8), dtype=np.uint32)
+        scales = rng.uniform(1e-3, 1e-2, size=(K // g, N)).astype(np.float16)
+        zeros = rng.integers(0, 16, size=(K // g, N)).astype(np.uint8)
+        q4_0 = q4_0_blocks(rng, N, K)
+        x = x_f32(rng, K)
+        return dict(fmt="int4", K=K, N=N, group=g, gptq=gptq, awq=awq, scales=scales, zeros=zeros, q4_0=q4_0, x=x,
+                    seed=seed)
+    raise ValueError("workload must be 1..7")
