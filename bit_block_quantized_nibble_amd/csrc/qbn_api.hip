@@ -136,7 +136,6 @@ int32_t qbn_quantized_gemv(const qbn_tensor *w, const void *x, int32_t x_dtype, 
                            void *stream) {
     int32_t st = check_tensor(w);
     if (st) return st;
-    if (w->format != QBN_MXFP4 && w->format != QBN_NVFP4 && w->format != QBN_Q4_K) return QBN_ERR_UNSUPPORTED;
     if (x_dtype < QBN_F32 || x_dtype > QBN_F16 || y_dtype < QBN_F32 || y_dtype > QBN_F16) return QBN_ERR_FORMAT;
     if ((x_dtype != QBN_F32 && x_dtype != QBN_BF16) || y_dtype != QBN_F32) return QBN_ERR_DTYPE;
     if (w->n == 0) return QBN_OK;
@@ -146,7 +145,9 @@ int32_t qbn_quantized_gemv(const qbn_tensor *w, const void *x, int32_t x_dtype, 
     if (w->k == 0) return hip_status(qbn::launch_fill_zero(y, 4 * w->n, s));
     if (!x) return QBN_ERR_NULL;
     if (!aligned(x, 16)) return QBN_ERR_ALIGN;
-    return hip_status(qbn::launch_gemv(*w, x, x_dtype, (float *)y, s));
+    const bool int4 = w->format == QBN_Q4_0 || w->format == QBN_GPTQ4 || w->format == QBN_AWQ4;
+    return hip_status(int4 ? qbn::launch_gemv_int4(*w, x, x_dtype, (float *)y, s)
+                           : qbn::launch_gemv(*w, x, x_dtype, (float *)y, s));
 }
 
 int32_t qbn_quantize_q8(const void *x, int32_t x_dtype, int64_t k, int8_t *q, float *d, int32_t *bsums,

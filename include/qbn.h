@@ -145,7 +145,11 @@ QBN_API int64_t qbn_bytes(int32_t format, int64_t n, int64_t k, int32_t group, i
 /* y[r] = sum_i W_hat[r][i] * x[i] for r in 0..n  (decode GEMV, batch 1).
  * Fused: W_hat is decoded in registers and never written to memory
  * ([WK] sections 1, 7 and 7d; [FB] section 8).
- * Formats: MXFP4, NVFP4, Q4_K. x: QBN_F32 or QBN_BF16 [k]; y: QBN_F32 [n].
+ * Formats: MXFP4, NVFP4, Q4_K, and the integer int4 layouts ([BP] "Real
+ * layouts compared"): Q4_0 (rows of 18-byte blocks, w = d * (q - 8)),
+ * GPTQ4 and AWQ4 (the k x n logical matrix packed along k or along n,
+ * w = s[k/group][r] * (q - z[k/group][r]), z the logical zero point).
+ * x: QBN_F32 or QBN_BF16 [k]; y: QBN_F32 [n].
  * Accumulation is binary32 with a fixed, atomics-free reduction order, so
  * repeated calls give bit-identical y. Each y[r] satisfies
  * |y - y_exact| <= 1e-5 * sum_i |W_hat[r][i] x[i]| + 1e-6.

@@ -80,8 +80,11 @@ def test_gemv_rejections(lib):
     assert g(T(MX, 4, 48), A, F32, B, F32, None) == SHAPE
     assert g(T(NV, 4, 40), A, F32, B, F32, None) == SHAPE
     assert g(T(QK, 4, 512 + 32), A, F32, B, F32, None) == SHAPE
-    assert g(T(Q0, 4, 64), A, F32, B, F32, None) == UNSUP
-    assert g(T(GP, 16, 64, group=32), A, F32, B, F32, None) == UNSUP
+    assert g(T(Q0, 4, 64), A + 8, F32, B, F32, None) == ALIGN
+    assert g(T(GP, 16, 64, group=32), A, F32, B + 2, F32, None) == ALIGN
+    assert g(T(GP, 16, 64, group=32, zeros=None), A, F32, B, F32, None) == NULL
+    assert g(T(GP, 16, 64, group=12), A, F32, B, F32, None) == GROUP
+    assert g(T(AW, 12, 64, group=32), A, F32, B, F32, None) == SHAPE
     assert g(T(MX, 4, 64), A, 7, B, F32, None) == FORMAT
     assert g(T(MX, 4, 64), A, 2, B, F32, None) == DTYPE
     assert g(T(MX, 4, 64), A, F32, B, BF16, None) == DTYPE
