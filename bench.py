@@ -79,6 +79,20 @@ WORKLOADS = {
              "(exact block totals, pinned binary32 epilogue), y f16",
         bytes=4096 * 2048 + 4096 * 256 + 4096 * 2 + 2 * (4096 + 16 * 4 + 128 * 4) + 4096 * 2,
         kernel_bytes=4096 * 2048 + 4096 * 256 + 4096 + 16 * 4 + 4096 * 2),
+    "gptq_gemv": dict(
+        cfg=7, kind="int4gemv", fmt="gptq4", unit="GB/s",
+        desc="GPTQ int4 decode GEMV 11008x4096 (int32 [K/8][N] packed along k, fp16 scales and u8 zero points per "
+             "group of 128), x f32, y f32, batch 1",
+        bytes=(4096 // 8) * 11008 * 4 + 32 * 11008 * 2 + 32 * 11008 + 4096 * 4 + 11008 * 4),
+    "awq_gemv": dict(
+        cfg=7, kind="int4gemv", fmt="awq4", unit="GB/s",
+        desc="AWQ int4 decode GEMV 11008x4096 (int32 [K][N/8] packed along n in the 0,2,4,6,1,3,5,7 slot order, "
+             "fp16 scales and u8 zero points per group of 128), x f32, y f32, batch 1",
+        bytes=4096 * (11008 // 8) * 4 + 32 * 11008 * 2 + 32 * 11008 + 4096 * 4 + 11008 * 4),
+    "q4_0_gemv": dict(
+        cfg=7, kind="int4gemv", fmt="q4_0", unit="GB/s",
+        desc="Q4_0 decode GEMV 11008x4096 (18-byte blocks of 32: fp16 d, w = d(q-8)), x f32, y f32, batch 1",
+        bytes=11008 * 128 * 18 + 4096 * 4 + 11008 * 4),
     "mxfp4_gemm": dict(
         cfg=4, kind="gemm", unit="TFLOP/s",
         desc="MXFP4 prefill GEMM: W 8192x8192 (E2M1, E8M0 per 32) x X bf16 2048x8192 -> Y bf16, fp32 accumulate",
@@ -192,6 +206,25 @@ def build_steps(name, spec, dev):
             return run
 
         return [step(g) for g in gemvs], R, inp, gemvs
+    if spec["kind"] == "int4gemv":
+        K, N, g = inp["K"], inp["N"], inp["group"]
+        fmt = spec["fmt"]
+        x = host_to_device(inp["x"], dev)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+        if fmt == "q4_0":
+            d0, s0, z0 = host_to_device(inp["q4_0"], dev), None, None
+            wbytes = inp["q4_0"].nbytes
+        else:
+            d0 = host_to_device(inp["gptq"] if fmt == "gptq4" else inp["awq"], dev)
+            s0 = host_to_device(inp["scales"].view(np.uint16), dev)
+            z0 = host_to_device(inp["zeros"], dev)
+            wbytes = d0.numel() * 4 + s0.numel() * 2 + z0.numel()
+        R = max(1, math.ceil(ROTATE_BYTES / wbytes))
+        for _ in range(R):
+            w = qbn.QTensor(fmt, N, K, d0.clone(), None if s0 is None else s0.clone(),
+                            None if z0 is None else z0.clone(), group=g)
+            calls.append(qbn.prepare_gemv(w, x, y))
+        return calls, R, inp, None
     if spec["kind"] == "gemv":
         n, k = inp["n"], inp["k"]
         wbytes = inp["data"].nbytes + (0 if inp["scales"] is None else inp["scales"].nbytes)
@@ -299,6 +332,22 @@ def cpu_baseline(name, spec, inp, budget_s):
         return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
                     sample="full quantize + %dx%d integer-exact NVFP4 decode, median of %d runs (%.2f s each)"
                     % (n, k, len(reps), t))
+    if spec["kind"] == "int4gemv":
+        K, N, g = inp["K"], inp["N"], inp["group"]
+        fmt = spec["fmt"]
+        while True:
+            t0 = time.perf_counter()
+            if fmt == "q4_0":
+                oracle.gemv_rows(oracle.Q4_0, inp["q4_0"], None, 1.0, K, inp["x"], np.arange(N))
+            else:
+                oracle.int4_gemv(fmt, inp["gptq"] if fmt == "gptq4" else inp["awq"], inp["scales"], inp["zeros"], g,
+                                 inp["x"], np.arange(N))
+            reps.append(time.perf_counter() - t0)
+            if time.perf_counter() > t_end and len(reps) >= 3:
+                break
+        t = float(np.median(reps))
+        return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                    sample="full %dx%d GEMV, median of %d runs (%.2f s each)" % (N, K, len(reps), t))
     if spec["kind"] == "gemv":
         fmt = {"mxfp4": oracle.MXFP4, "nvfp4": oracle.NVFP4, "q4_k": oracle.Q4_K}[inp["fmt"]]
         n, k = inp["n"], inp["k"]
@@ -489,7 +538,7 @@ def main():
         achieved = spec.get("kernel_bytes", spec["bytes"]) / (kernel_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=recorded_traffic(args.workload))
-        metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] in ("gemv", "w4a8", "a16q8") else (
+        metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] in ("gemv", "w4a8", "a16q8", "int4gemv") else (
             "int4 repack GB/s (% HBM peak)" if spec["kind"] == "repack" else "bulk dequant GB/s (% HBM peak)")
 
     cpu = None

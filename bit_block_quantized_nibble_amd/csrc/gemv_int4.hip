@@ -17,19 +17,25 @@ namespace qbn {
 namespace {
 
 template <typename XT>
-struct X8;  // eight consecutive activations as binary32
+struct X8;  // eight consecutive activations: raw load, then binary32
 template <>
 struct X8<float> {
-    __device__ __forceinline__ static void at(const float *x, int64_t k, float (&v)[8]) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(x + k);
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(x + k + 4);
-        v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+    struct Raw {
+        f32x4 a, b;
+    };
+    __device__ __forceinline__ static Raw raw(const float *x, int64_t k) {
+        return Raw{*reinterpret_cast<const f32x4 *>(x + k), *reinterpret_cast<const f32x4 *>(x + k + 4)};
+    }
+    __device__ __forceinline__ static void unpack(const Raw &r, float (&v)[8]) {
+        v[0] = r.a.x, v[1] = r.a.y, v[2] = r.a.z, v[3] = r.a.w, v[4] = r.b.x, v[5] = r.b.y, v[6] = r.b.z,
+        v[7] = r.b.w;
     }
 };
 template <>
 struct X8<__bf16> {
-    __device__ __forceinline__ static void at(const __bf16 *x, int64_t k, float (&v)[8]) {
-        const u32x4 w = ld16(x + k);
+    typedef u32x4 Raw;
+    __device__ __forceinline__ static Raw raw(const __bf16 *x, int64_t k) { return ld16(x + k); }
+    __device__ __forceinline__ static void unpack(const Raw &w, float (&v)[8]) {
         const uint32_t p[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -45,136 +51,204 @@ __device__ __forceinline__ float ubyte(uint32_t w) {
     return (float)((w >> (8 * B)) & 0xFFu);
 }
 
-// The eight 4-bit codes of a word as binary32, in nibble order.
-__device__ __forceinline__ void nibbles_f32(uint32_t w, float (&q)[8]) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    q[0] = ubyte<0>(lo);
-    q[1] = ubyte<0>(hi);
-    q[2] = ubyte<1>(lo);
-    q[3] = ubyte<1>(hi);
-    q[4] = ubyte<2>(lo);
-    q[5] = ubyte<2>(hi);
-    q[6] = ubyte<3>(lo);
-    q[7] = ubyte<3>(hi);
+// q_m - z[m] (exact) for the eight 4-bit codes q_m of a word (bits 4m..4m+3).
+// Each nibble is read as a binary16 subnormal (q * 2^-24, or 16 q * 2^-24
+// for the high nibble of a byte) straight from masked bits, and one mixed
+// fma per code scales it back and subtracts the zero point.
+__device__ __forceinline__ void nib_minus(uint32_t v, const float (&z)[8], float (&w)[8]) {
+    const uint32_t v8 = v >> 8;
+    const f16x2 p0 = __builtin_bit_cast(f16x2, v & 0x000F000Fu);   // nibbles 0, 4
+    const f16x2 p1 = __builtin_bit_cast(f16x2, v8 & 0x000F000Fu);  // nibbles 2, 6
+    const f16x2 p2 = __builtin_bit_cast(f16x2, v & 0x00F000F0u);   // 16 x nibbles 1, 5
+    const f16x2 p3 = __builtin_bit_cast(f16x2, v8 & 0x00F000F0u);  // 16 x nibbles 3, 7
+    w[0] = __builtin_fmaf((float)p0.x, 0x1p24f, -z[0]);
+    w[4] = __builtin_fmaf((float)p0.y, 0x1p24f, -z[4]);
+    w[2] = __builtin_fmaf((float)p1.x, 0x1p24f, -z[2]);
+    w[6] = __builtin_fmaf((float)p1.y, 0x1p24f, -z[6]);
+    w[1] = __builtin_fmaf((float)p2.x, 0x1p20f, -z[1]);
+    w[5] = __builtin_fmaf((float)p2.y, 0x1p20f, -z[5]);
+    w[3] = __builtin_fmaf((float)p3.x, 0x1p20f, -z[3]);
+    w[7] = __builtin_fmaf((float)p3.y, 0x1p20f, -z[7]);
 }
 
 // ------------------------------------------------------------------ GPTQ / AWQ
-// A workgroup covers 32 columns (4 lanes x 8 columns) and all of K, split
-// into 64 slices of whole 8-row steps; each lane keeps 8 column sums.
-constexpr int kAffCW = 4, kAffSL = 64;
+// A workgroup covers CW lanes x 8 columns and all of K, split into SL =
+// threads / CW slices; a lane takes rounds of SPL consecutive 8-row steps
+// (SPL divides group / 8, so a round lies in one group), requests all of a
+// round's codes, activations, scales and zero points before multiplying,
+// and keeps 8 column sums. (Holding a second round in registers to overlap
+// the next requests with the arithmetic measured no faster.) GPTQ: CW = 4 (a lane's 8 columns
+// are 32 contiguous bytes, 4 lanes a 128-byte line per step), 256 threads.
+// AWQ: CW = 8 (one word of 8 columns per lane per row, 32 bytes per row
+// across the 8 lanes), 512 threads.
+template <int FMT>
+struct AffShape {
+    static constexpr int CW = FMT == QBN_GPTQ4 ? 4 : 8;
+    static constexpr int THREADS = FMT == QBN_GPTQ4 ? 256 : 512;
+    static constexpr int SL = THREADS / CW;
+    static constexpr int WAVES = THREADS / 64;
+};
 
-// VEC: the 8 columns of a lane are loaded as 16-byte (codes, scales) and
-// 8-byte (zeros) vectors; needs n % 8 == 0 and 16-byte aligned data and
-// scales. Otherwise element loads with columns past n clamped (not stored).
-template <int FMT, typename XT, bool VEC>
-__global__ __launch_bounds__(256) void k_gemv_affine(const uint32_t *__restrict__ qw, const uint16_t *__restrict__ sc,
-                                                     const uint8_t *__restrict__ zp, const XT *__restrict__ x,
-                                                     float *__restrict__ y, int64_t n, int64_t k, int64_t group) {
-    __shared__ float red[4][kAffCW][8];
-    const int t = threadIdx.x;
-    const int cw = t % kAffCW, sl = t / kAffCW;
-    const int64_t c0 = (int64_t)blockIdx.x * (8 * kAffCW) + 8 * cw;
-    const int64_t nsteps = k / 8, per = (nsteps + kAffSL - 1) / kAffSL;
-    const int64_t j0 = sl * per, j1 = min(nsteps, j0 + per);
-    int64_t cc[8];  // clamped columns (element loads)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cc[i] = min(c0 + i, n - 1);
-    const bool live = c0 < n;
+// The raw bytes of one round: SPL steps of codes and activations, and the
+// round's group scales and zero points (VEC: as vectors; else per column).
+template <int SPL, typename XT>
+struct AffRound {
+    uint32_t w[SPL][8];
+    typename X8<XT>::Raw x[SPL];
+    u32x4 s4;
+    u32x2 z2;
+    uint16_t se[8];
+    uint8_t ze[8];
+};
 
-    float tot[8], acc[8], zf[8], sf[8];
+template <int FMT, bool VEC, int SPL, typename XT>
+__device__ __forceinline__ void aff_load(AffRound<SPL, XT> &rd, const uint32_t *__restrict__ qw,
+                                         const uint16_t *__restrict__ sc, const uint8_t *__restrict__ zp,
+                                         const XT *__restrict__ x, int64_t n, int64_t group, int64_t c0,
+                                         const int64_t (&cc)[8], int64_t jb) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tot[i] = acc[i] = zf[i] = sf[i] = 0.0f;
-    int64_t cur = -1;
-    for (int64_t j = live ? j0 : j1; j < j1; ++j) {
-        const int64_t gi = (8 * j) / group;
-        if (gi != cur) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                tot[i] = fmaf(sf[i], acc[i], tot[i]);
-                acc[i] = 0.0f;
-            }
-            cur = gi;
-            if (VEC) {
-                const u32x4 s4 = ld16(sc + gi * n + c0);
-                const u32x2 z2 = ld8(zp + gi * n + c0);
-                const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sf[2 * i] = f16_bits_f32(sw[i] & 0xFFFFu);
-                    sf[2 * i + 1] = f16_bits_f32(sw[i] >> 16);
-                }
-                zf[0] = ubyte<0>(z2.x);
-                zf[1] = ubyte<1>(z2.x);
-                zf[2] = ubyte<2>(z2.x);
-                zf[3] = ubyte<3>(z2.x);
-                zf[4] = ubyte<0>(z2.y);
-                zf[5] = ubyte<1>(z2.y);
-                zf[6] = ubyte<2>(z2.y);
-                zf[7] = ubyte<3>(z2.y);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    sf[i] = f16_bits_f32(sc[gi * n + cc[i]]);
-                    zf[i] = (float)zp[gi * n + cc[i]];
-                }
-            }
-        }
-        float xv[8];
-        X8<XT>::at(x, 8 * j, xv);
+    for (int st = 0; st < SPL; ++st) {
+        const int64_t j = jb + st;
         if (FMT == QBN_GPTQ4) {
             // word i holds rows 8j .. 8j+7 of column c0 + i, row 8j + e at bits 4e
-            uint32_t w[8];
             if (VEC) {
                 const u32x4 a = ld16(qw + j * n + c0), b = ld16(qw + j * n + c0 + 4);
-                w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w, w[4] = b.x, w[5] = b.y, w[6] = b.z, w[7] = b.w;
+                rd.w[st][0] = a.x, rd.w[st][1] = a.y, rd.w[st][2] = a.z, rd.w[st][3] = a.w;
+                rd.w[st][4] = b.x, rd.w[st][5] = b.y, rd.w[st][6] = b.z, rd.w[st][7] = b.w;
             } else {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) w[i] = qw[j * n + cc[i]];
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float q[8];
-                nibbles_f32(w[i], q);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[i] = fmaf(q[e] - zf[i], xv[e], acc[i]);
+                for (int i = 0; i < 8; ++i) rd.w[st][i] = qw[j * n + cc[i]];
             }
         } else {
-            // word e holds columns c0 .. c0+7 of row 8j + e; slot t is column
-            // 0,2,4,6,1,3,5,7 [t]
-            const int64_t nw = n / 8;
+            // word e holds columns c0 .. c0+7 of row 8j + e
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rd.w[st][e] = qw[(8 * j + e) * (n / 8) + c0 / 8];
+        }
+        rd.x[st] = X8<XT>::raw(x, 8 * j);
+    }
+    const int64_t gi = (8 * jb) / group;
+    if (VEC) {
+        rd.s4 = ld16(sc + gi * n + c0);
+        rd.z2 = ld8(zp + gi * n + c0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            rd.se[i] = sc[gi * n + cc[i]];
+            rd.ze[i] = zp[gi * n + cc[i]];
+        }
+    }
+}
+
+// Multiply one round into the 8 column sums: per step, q - z times x; the
+// round's group scale multiplies its partial sums once.
+template <int FMT, bool VEC, int SPL, typename XT>
+__device__ __forceinline__ void aff_compute(const AffRound<SPL, XT> &cur, float (&tot)[8]) {
+    float sf[8], zf[8];
+    if (VEC) {
+        const uint32_t sw[4] = {cur.s4.x, cur.s4.y, cur.s4.z, cur.s4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sf[2 * i] = f16_bits_f32(sw[i] & 0xFFFFu);
+            sf[2 * i + 1] = f16_bits_f32(sw[i] >> 16);
+        }
+        zf[0] = ubyte<0>(cur.z2.x), zf[1] = ubyte<1>(cur.z2.x), zf[2] = ubyte<2>(cur.z2.x);
+        zf[3] = ubyte<3>(cur.z2.x), zf[4] = ubyte<0>(cur.z2.y), zf[5] = ubyte<1>(cur.z2.y);
+        zf[6] = ubyte<2>(cur.z2.y), zf[7] = ubyte<3>(cur.z2.y);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sf[i] = f16_bits_f32(cur.se[i]);
+            zf[i] = (float)cur.ze[i];
+        }
+    }
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < SPL; ++st) {
+        float xv[8];
+        X8<XT>::unpack(cur.x[st], xv);
+        if (FMT == QBN_GPTQ4) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float zi[8] = {zf[i], zf[i], zf[i], zf[i], zf[i], zf[i], zf[i], zf[i]};
+                float d[8];
+                nib_minus(cur.w[st][i], zi, d);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[i] = fmaf(d[e], xv[e], acc[i]);
+            }
+        } else {
+            // slot tt of a word is column 0,2,4,6,1,3,5,7 [tt]
+            constexpr int col[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+            const float zs[8] = {zf[0], zf[2], zf[4], zf[6], zf[1], zf[3], zf[5], zf[7]};  // by slot
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float q[8];
-                nibbles_f32(qw[(8 * j + e) * nw + c0 / 8], q);
-                constexpr int col[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+                float d[8];
+                nib_minus(cur.w[st][e], zs, d);
 #pragma unroll
-                for (int tt = 0; tt < 8; ++tt) acc[col[tt]] = fmaf(q[tt] - zf[col[tt]], xv[e], acc[col[tt]]);
+                for (int tt = 0; tt < 8; ++tt) acc[col[tt]] = fmaf(d[tt], xv[e], acc[col[tt]]);
             }
         }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) tot[i] = fmaf(sf[i], acc[i], tot[i]);
+}
 
-    // slices: 16 per wave (lane bits 2..5), then the four waves in order
+// VEC: the 8 columns of a lane are loaded as 16-byte (codes, scales) and
+// 8-byte (zeros) vectors; needs n % 8 == 0 and 16-byte aligned data and
+// scales. Otherwise element loads with columns past n clamped (not stored).
+template <int FMT, typename XT, bool VEC, int SPL>
+__global__ __launch_bounds__(AffShape<FMT>::THREADS) void k_gemv_affine(const uint32_t *__restrict__ qw, const uint16_t *__restrict__ sc,
+                                                     const uint8_t *__restrict__ zp, const XT *__restrict__ x,
+                                                     float *__restrict__ y, int64_t n, int64_t k, int64_t group) {
+    constexpr int CW = AffShape<FMT>::CW, SL = AffShape<FMT>::SL, WAVES = AffShape<FMT>::WAVES;
+    __shared__ float red[WAVES][CW][8];
+    const int t = threadIdx.x;
+    const int cw = t % CW, sl = t / CW;
+    // Workgroups are dealt to the 8 XCDs in turn (block b to XCD b % 8). The
+    // column blocks that share cache lines (AWQ: four blocks per 128-byte
+    // line) are given to one XCD, so that its L2 serves the line once:
+    // XCD x takes logical blocks x * q + min(x, r) onwards (q, r = grid / 8,
+    // grid % 8), in dispatch order.
+    const int64_t nblk = gridDim.x, q8 = nblk / 8, r8 = nblk % 8, xcd = blockIdx.x % 8;
+    const int64_t blk = xcd * q8 + min(xcd, r8) + blockIdx.x / 8;
+    const int64_t c0 = blk * (8 * CW) + 8 * cw;
+    const int64_t nsteps = k / 8;  // a multiple of SPL
+    int64_t cc[8];                 // clamped columns (element loads)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cc[i] = min(c0 + i, n - 1);
+    const bool live = c0 < n;
+
+    float tot[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tot[i] = 0.0f;
+    // rounds of this lane: jb = sl * SPL + r * SL * SPL
+    for (int64_t jb = live ? (int64_t)sl * SPL : nsteps; jb < nsteps; jb += (int64_t)SL * SPL) {
+        AffRound<SPL, XT> rd;
+        aff_load<FMT, VEC>(rd, qw, sc, zp, x, n, group, c0, cc, jb);
+        aff_compute<FMT, VEC>(rd, tot);
+    }
+
+    // slices: the wave's 64 / CW, then the waves in order
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float v = tot[i];
-        v += __shfl_xor(v, 4, 64);
-        v += __shfl_xor(v, 8, 64);
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
+#pragma unroll
+        for (int off = CW; off < 64; off *= 2) v += __shfl_xor(v, off, 64);
         tot[i] = v;
     }
     const int lane = t % 64, wave = t / 64;
-    if (lane < kAffCW) {
+    if (lane < CW) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) red[wave][lane][i] = tot[i];
     }
     __syncthreads();
-    if (wave == 0 && lane < kAffCW && live) {
+    if (wave == 0 && lane < CW && live) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float v = ((red[0][lane][i] + red[1][lane][i]) + red[2][lane][i]) + red[3][lane][i];
+            float v = red[0][lane][i];
+#pragma unroll
+            for (int wv = 1; wv < WAVES; ++wv) v += red[wv][lane][i];
             if (c0 + i < n) y[c0 + i] = v;
         }
     }
@@ -216,36 +290,81 @@ struct X32<__bf16> {
     }
 };
 
-template <typename XT, int R>
+// x is staged once per workgroup in LDS as binary32, 36 floats per block (32
+// values and 4 of padding, so that 16 lanes reading their blocks' pieces at
+// one index hit distinct banks). A lane's blocks (BPL of them, 64 apart) of
+// all R rows are requested before any arithmetic. Rounds of 64 * BPL blocks.
+constexpr int kQ40Pitch = 36;  // floats per staged block
+
+// LX = false (k too long for the staging buffer): x is read from global
+// memory instead.
+template <typename XT, int R, int BPL, bool LX>
 __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ blocks, const XT *__restrict__ x,
                                                    float *__restrict__ y, int64_t n, int64_t k) {
+    extern __shared__ __attribute__((aligned(16))) float xs[];
+    const int64_t nb = k / 32;
+    // stage x: 16-byte pieces, piece p of block b at xs[36 b + 4 p]
+    for (int64_t c = threadIdx.x; LX && c < 8 * nb; c += 256) {
+        float v[4];
+        if (sizeof(XT) == 4) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) + 4 * c);
+            v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w;
+        } else {
+            const u32x2 a = ld8(reinterpret_cast<const uint16_t *>(x) + 4 * c);
+            v[0] = __builtin_bit_cast(float, a.x << 16), v[1] = __builtin_bit_cast(float, a.x & 0xFFFF0000u);
+            v[2] = __builtin_bit_cast(float, a.y << 16), v[3] = __builtin_bit_cast(float, a.y & 0xFFFF0000u);
+        }
+        *reinterpret_cast<f32x4 *>(xs + kQ40Pitch * (c / 8) + 4 * (c % 8)) = f32x4{v[0], v[1], v[2], v[3]};
+    }
+    __syncthreads();
     const int lane = threadIdx.x % kWave;
     const int64_t r0 = ((int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave) * R;
-    if (r0 >= n) return;  // whole waves only; no barrier follows
-    const int64_t nb = k / 32;
+    if (r0 >= n) return;  // whole waves, after the only barrier
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-    for (int64_t b = lane; b < nb; b += kWave) {
-        float xv[32];
-        X32<XT>::at(x, 32 * b, xv);
+    for (int64_t bb = lane; bb < nb; bb += (int64_t)kWave * BPL) {
+        Q40 blk[BPL][R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int64_t row = min(r0 + r, n - 1);
-            const Q40 blk = *reinterpret_cast<const Q40 *>(blocks + (row * nb + b) * 18);
-            float part = 0.0f;
+        for (int u = 0; u < BPL; ++u) {
+            const int64_t b = min(bb + (int64_t)kWave * u, nb - 1);
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // byte 4w + i holds elements 4w + i (low) and 16 + 4w + i (high)
-                float q[8];
-                nibbles_f32(blk.c[w], q);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    part = fmaf(q[2 * i] - 8.0f, xv[4 * w + i], part);
-                    part = fmaf(q[2 * i + 1] - 8.0f, xv[16 + 4 * w + i], part);
-                }
+            for (int r = 0; r < R; ++r) {
+                const int64_t row = min(r0 + r, n - 1);
+                blk[u][r] = *reinterpret_cast<const Q40 *>(blocks + (row * nb + b) * 18);
             }
-            acc[r] = fmaf(f16_bits_f32(blk.d), part, acc[r]);
+        }
+#pragma unroll
+        for (int u = 0; u < BPL; ++u) {
+            const int64_t b = bb + (int64_t)kWave * u;
+            if (b >= nb) break;
+            float xv[32];
+            if (LX) {
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const f32x4 a = *reinterpret_cast<const f32x4 *>(xs + kQ40Pitch * b + 4 * p);
+                    xv[4 * p] = a.x, xv[4 * p + 1] = a.y, xv[4 * p + 2] = a.z, xv[4 * p + 3] = a.w;
+                }
+            } else {
+                X32<XT>::at(x, 32 * b, xv);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float part = 0.0f;
+                constexpr float z8[8] = {8.0f, 8.0f, 8.0f, 8.0f, 8.0f, 8.0f, 8.0f, 8.0f};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    // byte 4w + i holds elements 4w + i (nibble 2i) and 16 + 4w + i (nibble 2i + 1)
+                    float d[8];
+                    nib_minus(blk[u][r].c[w], z8, d);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        part = fmaf(d[2 * i], xv[4 * w + i], part);
+                        part = fmaf(d[2 * i + 1], xv[16 + 4 * w + i], part);
+                    }
+                }
+                acc[r] = fmaf(f16_bits_f32(blk[u][r].d), part, acc[r]);
+            }
         }
     }
 #pragma unroll
@@ -257,26 +376,44 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ b
     }
 }
 
+template <int FMT, typename XT, bool VEC>
+hipError_t run_affine_spl(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+    constexpr int CW = AffShape<FMT>::CW;
+    const unsigned grid = (unsigned)((w.n + 8 * CW - 1) / (8 * CW));
+    const int64_t gs = w.group / 8;  // steps per group; a round of SPL steps stays inside one
+    if (gs % 8 == 0)
+        hipLaunchKernelGGL((k_gemv_affine<FMT, XT, VEC, 8>), dim3(grid), dim3(AffShape<FMT>::THREADS), 0, s,
+                           (const uint32_t *)w.data, (const uint16_t *)w.scales, (const uint8_t *)w.zeros, x, y, w.n,
+                           w.k, (int64_t)w.group);
+    else if (gs % 4 == 0)
+        hipLaunchKernelGGL((k_gemv_affine<FMT, XT, VEC, 4>), dim3(grid), dim3(AffShape<FMT>::THREADS), 0, s,
+                           (const uint32_t *)w.data, (const uint16_t *)w.scales, (const uint8_t *)w.zeros, x, y, w.n,
+                           w.k, (int64_t)w.group);
+    else
+        hipLaunchKernelGGL((k_gemv_affine<FMT, XT, VEC, 1>), dim3(grid), dim3(AffShape<FMT>::THREADS), 0, s,
+                           (const uint32_t *)w.data, (const uint16_t *)w.scales, (const uint8_t *)w.zeros, x, y, w.n,
+                           w.k, (int64_t)w.group);
+    return hipGetLastError();
+}
+
 template <int FMT, typename XT>
 hipError_t run_affine(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
-    const unsigned grid = (unsigned)((w.n + 8 * kAffCW - 1) / (8 * kAffCW));
     const bool vec = (w.n % 8) == 0 && ((uintptr_t)w.data % 16) == 0 && ((uintptr_t)w.scales % 16) == 0 &&
                      ((uintptr_t)w.zeros % 8) == 0;
-    if (vec)
-        hipLaunchKernelGGL((k_gemv_affine<FMT, XT, true>), dim3(grid), dim3(256), 0, s, (const uint32_t *)w.data,
-                           (const uint16_t *)w.scales, (const uint8_t *)w.zeros, x, y, w.n, w.k, (int64_t)w.group);
-    else
-        hipLaunchKernelGGL((k_gemv_affine<FMT, XT, false>), dim3(grid), dim3(256), 0, s, (const uint32_t *)w.data,
-                           (const uint16_t *)w.scales, (const uint8_t *)w.zeros, x, y, w.n, w.k, (int64_t)w.group);
-    return hipGetLastError();
+    return vec ? run_affine_spl<FMT, XT, true>(w, x, y, s) : run_affine_spl<FMT, XT, false>(w, x, y, s);
 }
 
 template <typename XT>
 hipError_t run_q4_0(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
-    constexpr int R = 8;
+    constexpr int R = 8, BPL = 2;
     const int64_t waves = (w.n + R - 1) / R;
-    hipLaunchKernelGGL((k_gemv_q4_0<XT, R>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
-                       (const uint8_t *)w.data, x, y, w.n, w.k);
+    const size_t lds = (size_t)(w.k / 32) * kQ40Pitch * sizeof(float);
+    if (lds <= 64 * 1024)
+        hipLaunchKernelGGL((k_gemv_q4_0<XT, R, BPL, true>), dim3((unsigned)((waves + 3) / 4)), dim3(256), lds, s,
+                           (const uint8_t *)w.data, x, y, w.n, w.k);
+    else
+        hipLaunchKernelGGL((k_gemv_q4_0<XT, R, BPL, false>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
+                           (const uint8_t *)w.data, x, y, w.n, w.k);
     return hipGetLastError();
 }
 

@@ -71,7 +71,8 @@ def test_affine_gemv_misaligned_buffers(fmt):
     assert_within_tolerance(a, y_ref, s_ref, fmt + " vector loads")
 
 
-@pytest.mark.parametrize("n,k", [(1, 32), (7, 96), (33, 4096), (9, 160), (130, 1024), (5, 32 * 200)])
+# k = 32 * 500: past the activation staging buffer (activations read from global memory)
+@pytest.mark.parametrize("n,k", [(1, 32), (7, 96), (33, 4096), (9, 160), (130, 1024), (5, 32 * 200), (11, 32 * 500)])
 @pytest.mark.parametrize("xdt", ["f32", "bf16"])
 def test_q4_0_gemv_shapes(n, k, xdt):
     rng = np.random.default_rng(n * 5 + k)
