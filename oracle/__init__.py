@@ -82,6 +82,12 @@ def _load():
         lib.oracle_q4_0_unpack.argtypes = [P, I64, I64, P, P]
         lib.oracle_affine_dequant.argtypes = [P, P, P, I64, I64, I64, P]
         lib.oracle_gemv_kn.argtypes = [P, I64, I64, P, ctypes.c_int, P, I64, P, P, P]
+        lib.oracle_qzeros_unpack.argtypes = [P, I64, I64, ctypes.c_int, P]
+        lib.oracle_qzeros_unpack.restype = ctypes.c_int
+        lib.oracle_qzeros_pack.argtypes = [P, I64, I64, ctypes.c_int, P]
+        lib.oracle_qzeros_pack.restype = ctypes.c_int
+        lib.oracle_resolve_g_idx.argtypes = [P, I64, I64, P]
+        lib.oracle_resolve_g_idx.restype = ctypes.c_int
         lib.oracle_dequant_rows.argtypes = [ctypes.c_int, P, P, ctypes.c_float, I64, P, I64, P]
         lib.oracle_dequant_rows.restype = ctypes.c_int
         lib.oracle_gemv_rows.argtypes = [ctypes.c_int, P, P, ctypes.c_float, I64, P, ctypes.c_int, P, I64,
@@ -281,6 +287,35 @@ def affine_dequant(q: np.ndarray, scale_bits: np.ndarray, zeros: np.ndarray, gro
     out = np.zeros((K, N), dtype=np.float32)
     _load().oracle_affine_dequant(_ptr(q), _ptr(s), _ptr(z), K, N, group, _ptr(out))
     return out
+
+
+def qzeros_unpack(qz: np.ndarray, version: int) -> np.ndarray:
+    """GPTQ qzeros uint32 [G][N/8] -> logical zero points u8 [G][N]."""
+    q = np.ascontiguousarray(qz).view(np.uint32)
+    G, N8 = q.shape
+    out = np.zeros((G, N8 * 8), np.uint8)
+    if _load().oracle_qzeros_unpack(_ptr(q), G, N8 * 8, version, _ptr(out)):
+        raise ValueError("qzeros version must be 1 or 2")
+    return out
+
+
+def qzeros_pack(zeros: np.ndarray, version: int) -> np.ndarray:
+    """Logical zero points u8 [G][N] -> GPTQ qzeros uint32 [G][N/8]."""
+    z = np.ascontiguousarray(zeros, dtype=np.uint8)
+    G, N = z.shape
+    out = np.zeros((G, N // 8), np.uint32)
+    if _load().oracle_qzeros_pack(_ptr(z), G, N, version, _ptr(out)):
+        raise ValueError("qzeros version must be 1 or 2")
+    return out
+
+
+def resolve_g_idx(g_idx: np.ndarray, group: int):
+    """(status, perm int32 [K]): rows ordered by group, stable; status 0,
+    -1 (a g_idx out of range) or -2 (a group without exactly `group` rows)."""
+    g = np.ascontiguousarray(g_idx, dtype=np.int32)
+    perm = np.zeros(g.size, np.int32)
+    rc = _load().oracle_resolve_g_idx(_ptr(g), g.size, group, _ptr(perm))
+    return rc, perm
 
 
 def gemv_kn(W: np.ndarray, x: np.ndarray, cols):

@@ -347,6 +347,69 @@ ORACLE_API void oracle_awq_unpack(const uint32_t *qw, int64_t K, int64_t N, uint
         }
 }
 
+/* GPTQ qzeros: int32 [G][N/8], packed along the output dimension as a
+ * 4-bit stream, column 8c + j at bits 4j of word [g][c] ([BP] "Real layouts
+ * compared"). version 1 (AutoGPTQ's pack step) stores z - 1, version 2
+ * stores z ([BP] ibid. and "Repacking between formats", step 2). Unpacking
+ * adds the one back for version 1, so a stored nibble s reads as s + 1
+ * (1..16); packing version 1 stores (z - 1) mod 16, so z = 0 reads back as
+ * 16. Returns -1 for an unknown version. */
+ORACLE_API int oracle_qzeros_unpack(const uint32_t *qz, int64_t G, int64_t N, int version, uint8_t *zeros)
+{
+    if (version != 1 && version != 2)
+        return -1;
+    uint32_t vals[8];
+    for (int64_t g = 0; g < G; ++g)
+        for (int64_t c = 0; c < N / 8; ++c) {
+            oracle_unpack_bits(&qz[g * (N / 8) + c], 8, 4, vals);
+            for (int j = 0; j < 8; ++j)
+                zeros[g * N + 8 * c + j] = (uint8_t)(vals[j] + (version == 1 ? 1u : 0u));
+        }
+    return 0;
+}
+
+ORACLE_API int oracle_qzeros_pack(const uint8_t *zeros, int64_t G, int64_t N, int version, uint32_t *qz)
+{
+    if (version != 1 && version != 2)
+        return -1;
+    uint32_t vals[8];
+    for (int64_t g = 0; g < G; ++g)
+        for (int64_t c = 0; c < N / 8; ++c) {
+            for (int j = 0; j < 8; ++j)
+                vals[j] = ((uint32_t)zeros[g * N + 8 * c + j] - (version == 1 ? 1u : 0u)) & 15u;
+            oracle_pack_bits(vals, 8, 4, &qz[g * (N / 8) + c]);
+        }
+    return 0;
+}
+
+/* GPTQ act-order: g_idx[k] is the group of input row k ([BP] "Real layouts
+ * compared"). Resolving it ([BP] "Repacking between formats", step 3) orders
+ * the rows by group, keeping the original order inside a group: perm[i] is
+ * the source row placed at i, so that rows of group g fill g*group ..
+ * g*group + group - 1 and a layout without g_idx applies. Applying the same
+ * perm to the activations leaves every dot product's terms unchanged.
+ * Returns 0; -1 if a g_idx is outside 0..K/group-1; -2 if a group does not
+ * hold exactly `group` rows. */
+ORACLE_API int oracle_resolve_g_idx(const int32_t *g_idx, int64_t K, int64_t group, int32_t *perm)
+{
+    int64_t G = K / group;
+    for (int64_t k = 0; k < K; ++k)
+        if (g_idx[k] < 0 || g_idx[k] >= G)
+            return -1;
+    int64_t i = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        int64_t count = 0;
+        for (int64_t k = 0; k < K; ++k)
+            if (g_idx[k] == g) {
+                perm[i++] = (int32_t)k;
+                ++count;
+            }
+        if (count != group)
+            return -2;
+    }
+    return 0;
+}
+
 /* Q4_0 code layout for a K x N logical matrix: blocks run along K within
  * each output column n and are stored [N][K/32] x 18 bytes; block (n, b)
  * holds q[32b .. 32b+31][n], byte j = element j (low) | element j+16 (high).
