@@ -37,6 +37,7 @@ EXPORTED = (
     "qbn_abi_version", "qbn_tensor_struct_size", "qbn_status_string", "qbn_last_hip_error", "qbn_bytes",
     "qbn_quantized_gemv", "qbn_quantized_gemm", "qbn_dequantize", "qbn_repack", "qbn_validate",
     "qbn_quantize_q8", "qbn_quantized_gemv_q8", "qbn_quantize_mx", "qbn_quantized_gemm_mx",
+    "qbn_gptq_qzeros", "qbn_gptq_resolve_g_idx", "qbn_permute",
 )
 
 
@@ -87,6 +88,12 @@ def _load():
         lib.qbn_dequantize.restype = I32
         lib.qbn_repack.argtypes = [T, I32, I32, P, P, P, P]
         lib.qbn_repack.restype = I32
+        lib.qbn_gptq_qzeros.argtypes = [P, P, I64, I64, I32, I32, P]
+        lib.qbn_gptq_qzeros.restype = I32
+        lib.qbn_gptq_resolve_g_idx.argtypes = [P, P, I64, I64, I32, P, P, P, P]
+        lib.qbn_gptq_resolve_g_idx.restype = I32
+        lib.qbn_permute.argtypes = [P, P, I64, I32, P, P]
+        lib.qbn_permute.restype = I32
         lib.qbn_validate.argtypes = [T, P, P]
         lib.qbn_validate.restype = I32
         lib.qbn_quantize_q8.argtypes = [P, I32, I64, P, P, P, P]
@@ -168,6 +175,46 @@ def status_string(status: int) -> str:
 def nbytes(format: str, n: int, k: int, group: int = 0, part: int = 0) -> int:
     """Bytes of part 0 (data), 1 (scales) or 2 (zeros); -1 if invalid."""
     return int(_load().qbn_bytes(FORMATS[format], n, k, group, part))
+
+
+def gptq_qzeros(src: torch.Tensor, version: int, to_logical: bool, n: int,
+                dst: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GPTQ qzeros int32 [groups][n/8] <-> logical zero points uint8 [groups][n]
+    (version 1 stores z - 1, version 2 stores z)."""
+    lib = _load()
+    groups = src.shape[0]
+    if dst is None:
+        dst = (torch.empty((groups, n), dtype=torch.uint8, device=src.device) if to_logical
+               else torch.empty((groups, n // 8), dtype=torch.int32, device=src.device))
+    _check(lib.qbn_gptq_qzeros(_ptr(src, "src"), _ptr(dst, "dst"), groups, n, int(version), int(bool(to_logical)),
+                               _stream(src.device)), "qbn_gptq_qzeros")
+    return dst
+
+
+def gptq_resolve_g_idx(qweight: torch.Tensor, g_idx: torch.Tensor, group: int):
+    """Act-order resolution: returns (qweight_out int32 [k/8][n], perm int32 [k],
+    status int32 [1]) on the device; apply perm to the activations with permute()."""
+    lib = _load()
+    k, n = g_idx.numel(), qweight.shape[1]
+    out = torch.empty_like(qweight)
+    perm = torch.empty(k, dtype=torch.int32, device=qweight.device)
+    status = torch.empty(1, dtype=torch.int32, device=qweight.device)
+    _check(lib.qbn_gptq_resolve_g_idx(_ptr(qweight, "qweight"), _ptr(g_idx, "g_idx"), k, n, int(group),
+                                      _ptr(out, "qweight_out"), _ptr(perm, "perm"), _ptr(status, "status"),
+                                      _stream(qweight.device)), "qbn_gptq_resolve_g_idx")
+    return out, perm, status
+
+
+def permute(src: torch.Tensor, perm: torch.Tensor, dst: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dst[i] = src[perm[i]] (float32, bfloat16 or float16 vectors)."""
+    lib = _load()
+    if src.dtype not in _DTYPES:
+        raise TypeError("src dtype %s" % src.dtype)
+    if dst is None:
+        dst = torch.empty_like(src)
+    _check(lib.qbn_permute(_ptr(src, "src"), _ptr(perm, "perm"), src.numel(), _DTYPES[src.dtype], _ptr(dst, "dst"),
+                           _stream(src.device)), "qbn_permute")
+    return dst
 
 
 def quantized_gemv(w: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:

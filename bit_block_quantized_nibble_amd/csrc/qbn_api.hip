@@ -257,6 +257,44 @@ int32_t qbn_dequantize(const qbn_tensor *w, void *out, int32_t out_dtype, int32_
     return hip_status(qbn::launch_dequant(*w, out, out_dtype, out_layout, (hipStream_t)stream));
 }
 
+int32_t qbn_gptq_qzeros(const void *src, void *dst, int64_t groups, int64_t n, int32_t version, int32_t to_logical,
+                        void *stream) {
+    if (version != 1 && version != 2) return QBN_ERR_FORMAT;
+    if (to_logical != 0 && to_logical != 1) return QBN_ERR_FORMAT;
+    if (groups < 0 || n < 0 || groups > kMaxElems || n > kMaxElems || (n > 0 && groups > kMaxElems / n) || n % 8)
+        return QBN_ERR_SHAPE;
+    if (groups == 0 || n == 0) return QBN_OK;
+    if (!src || !dst) return QBN_ERR_NULL;
+    const void *packed = to_logical ? src : dst, *logical = to_logical ? dst : src;
+    if (!aligned(packed, 4) || !aligned(logical, 8)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_gptq_qzeros(src, dst, groups, n, version, to_logical, (hipStream_t)stream));
+}
+
+int32_t qbn_gptq_resolve_g_idx(const void *qweight, const int32_t *g_idx, int64_t k, int64_t n, int32_t group,
+                               void *qweight_out, int32_t *perm, int32_t *status, void *stream) {
+    if (k < 0 || n < 0 || k > kMaxElems || n > kMaxElems || (n > 0 && k > kMaxElems / n)) return QBN_ERR_SHAPE;
+    if (group <= 0 || group % 8) return QBN_ERR_GROUP;
+    if (k % 8 || k % group) return QBN_ERR_SHAPE;
+    if (!qbn::gptq_groups_fit(k, group)) return QBN_ERR_SHAPE;
+    if (!g_idx || !perm || !status || (k > 0 && n > 0 && (!qweight || !qweight_out))) return QBN_ERR_NULL;
+    if (!aligned(g_idx, 4) || !aligned(perm, 4) || !aligned(status, 4)) return QBN_ERR_ALIGN;
+    if (n > 0 && k > 0 && (!aligned(qweight, 4) || !aligned(qweight_out, 4))) return QBN_ERR_ALIGN;
+    if (qweight_out == qweight && n > 0 && k > 0) return QBN_ERR_UNSUPPORTED;  // rows move: not in place
+    return hip_status(qbn::launch_gptq_resolve_g_idx(qweight, g_idx, k, n, group, qweight_out, perm, status,
+                                                     (hipStream_t)stream));
+}
+
+int32_t qbn_permute(const void *src, const int32_t *perm, int64_t count, int32_t dtype, void *dst, void *stream) {
+    if (dtype < QBN_F32 || dtype > QBN_F16) return QBN_ERR_FORMAT;
+    if (count < 0 || count > kMaxElems) return QBN_ERR_SHAPE;
+    if (count == 0) return QBN_OK;
+    if (!src || !perm || !dst) return QBN_ERR_NULL;
+    const int eb = dtype == QBN_F32 ? 4 : 2;
+    if (!aligned(src, (uintptr_t)eb) || !aligned(dst, (uintptr_t)eb) || !aligned(perm, 4)) return QBN_ERR_ALIGN;
+    if (src == dst) return QBN_ERR_UNSUPPORTED;
+    return hip_status(qbn::launch_permute(src, perm, count, eb, dst, (hipStream_t)stream));
+}
+
 int32_t qbn_repack(const qbn_tensor *src, int32_t dst_format, int32_t dst_group, void *dst_data, void *dst_scales,
                    void *dst_zeros, void *stream) {
     int32_t st = check_tensor(src);

@@ -11,6 +11,13 @@ namespace qbn {
 
 hipError_t launch_gemv(const qbn_tensor &w, const void *x, int x_dtype, float *y, hipStream_t s);
 hipError_t launch_gemv_int4(const qbn_tensor &w, const void *x, int x_dtype, float *y, hipStream_t s);
+hipError_t launch_gptq_qzeros(const void *src, void *dst, int64_t groups, int64_t n, int version, int to_logical,
+                              hipStream_t s);
+hipError_t launch_gptq_resolve_g_idx(const void *qweight, const int32_t *g_idx, int64_t k, int64_t n, int64_t group,
+                                     void *qweight_out, int32_t *perm, int32_t *status, hipStream_t s);
+hipError_t launch_permute(const void *src, const int32_t *perm, int64_t count, int elem_bytes, void *dst,
+                          hipStream_t s);
+bool gptq_groups_fit(int64_t k, int64_t group);
 hipError_t launch_gemm(const qbn_tensor &w, int64_t m, const void *x, int64_t ldx, void *y, int64_t ldy,
                        hipStream_t s);
 hipError_t launch_dequant(const qbn_tensor &w, void *out, int out_dtype, int out_layout, hipStream_t s);

@@ -246,6 +246,39 @@ QBN_API int32_t qbn_quantized_gemm_mx(const qbn_tensor *w, int64_t m, int32_t x_
  * negative zero; a scale byte that qbn_validate rejects decodes to NaN. */
 QBN_API int32_t qbn_dequantize(const qbn_tensor *w, void *out, int32_t out_dtype, int32_t out_layout, void *stream);
 
+/* GPTQ qzeros <-> logical zero points ([BP] "Real layouts compared";
+ * "Repacking between formats", step 2). qzeros: int32 [groups][n/8], a 4-bit
+ * stream along the output dimension (column 8c + j at bits 4j of word c);
+ * version 1 (AutoGPTQ's pack step) stores z - 1, version 2 stores z.
+ * Logical zero points: u8 [groups][n], as qbn_tensor.zeros takes them.
+ * to_logical 1: src = qzeros, dst = zero points (version 1 reads a stored s
+ * as s + 1, so 1..16); 0: src = zero points, dst = qzeros (version 1 stores
+ * (z - 1) mod 16: zero point 0 is not representable and reads back as 16).
+ * n % 8 == 0; qzeros 4-byte and zero points 8-byte aligned. Bit-exact. */
+QBN_API int32_t qbn_gptq_qzeros(const void *src, void *dst, int64_t groups, int64_t n, int32_t version,
+                                int32_t to_logical, void *stream);
+
+/* GPTQ act-order resolution ([BP] "Real layouts compared": g_idx maps each
+ * input row to its group; "Repacking between formats", step 3). g_idx int32
+ * [k] (device). Writes perm int32 [k] (device): the source row placed at
+ * each position, rows ordered by group with their original order inside a
+ * group; qweight_out int32 [k/8][n] = qweight with its rows permuted alike
+ * (a GPTQ4 tensor with contiguous groups: scales and zeros [k/group][n] are
+ * unchanged). Apply perm to the activations with qbn_permute before the
+ * GEMV. *status (device int32) receives 0, -1 (a g_idx outside
+ * 0..k/group-1) or -2 (a group without exactly `group` rows); on an error
+ * perm is the identity and qweight_out a plain copy. group % 8 == 0,
+ * k % group == 0, k / group <= 8192; qweight_out must not alias qweight. */
+QBN_API int32_t qbn_gptq_resolve_g_idx(const void *qweight, const int32_t *g_idx, int64_t k, int64_t n,
+                                       int32_t group, void *qweight_out, int32_t *perm, int32_t *status,
+                                       void *stream);
+
+/* dst[i] = src[perm[i]] for i < count; dtype QBN_F32, QBN_BF16 or QBN_F16
+ * (the activation permutation of an act-order layer). perm values must lie
+ * in 0..count-1 (as qbn_gptq_resolve_g_idx writes them). Not in place. */
+QBN_API int32_t qbn_permute(const void *src, const int32_t *perm, int64_t count, int32_t dtype, void *dst,
+                            void *stream);
+
 /* Bit-exact repack of the int4 codes through the logical matrix
  * ([BP] "Repacking between formats"): src and destination share n and k.
  * Directions: GPTQ4 <-> AWQ4, GPTQ4 <-> Q4_0, AWQ4 <-> Q4_0.

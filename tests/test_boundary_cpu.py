@@ -36,7 +36,7 @@ def T(fmt, n, k, data=A, scales=B, zeros=C, scale2=1.0, group=0, reserved=0):
 def test_exports_every_declared_symbol(lib):
     header = open(os.path.join(ROOT, "include", "qbn.h")).read()
     declared = re.findall(r"QBN_API\s+[\w\s\*]+?\b(qbn_\w+)\s*\(", header)
-    assert len(declared) == 14
+    assert len(declared) == 17
     assert set(declared) == set(qbn.EXPORTED)
     so = ctypes.CDLL(qbn.lib_path())
     for name in declared:
@@ -238,3 +238,30 @@ def test_binding_refuses_host_tensors():
     w = qbn.QTensor("mxfp4", 2, 32, torch.zeros(2, 16, dtype=torch.uint8), torch.zeros(2, 1, dtype=torch.uint8))
     with pytest.raises(ValueError):
         qbn.quantized_gemv(w, torch.zeros(32), torch.zeros(2))
+
+
+def test_gptq_meta_rejections(lib):
+    z = lib.qbn_gptq_qzeros
+    assert z(A, B, 4, 64, 3, 1, None) == FORMAT
+    assert z(A, B, 4, 64, 1, 2, None) == FORMAT
+    assert z(A, B, 4, 60, 2, 1, None) == SHAPE
+    assert z(A, B, -1, 64, 2, 1, None) == SHAPE
+    assert z(None, B, 4, 64, 2, 1, None) == NULL
+    assert z(A + 2, B, 4, 64, 2, 1, None) == ALIGN     # qzeros words 4-byte aligned
+    assert z(A, B + 4, 4, 64, 2, 1, None) == ALIGN     # zero points 8-byte aligned
+    assert z(None, None, 0, 64, 2, 1, None) == OK
+    r = lib.qbn_gptq_resolve_g_idx
+    assert r(A, B, 256, 64, 12, C, A, B, None) == GROUP
+    assert r(A, B, 250, 64, 8, C, A, B, None) == SHAPE
+    assert r(A, B, 256, 64, 96, C, A, B, None) == SHAPE   # k % group
+    assert r(A, B, 8 * 9000, 64, 8, C, A, B, None) == SHAPE  # more than 8192 groups
+    assert r(A, None, 256, 64, 32, C, A, B, None) == NULL
+    assert r(A, B, 256, 64, 32, A, C, B, None) == UNSUP     # qweight_out aliases qweight
+    assert r(A, B + 2, 256, 64, 32, C, A, B, None) == ALIGN
+    p = lib.qbn_permute
+    assert p(A, B, 16, 7, C, None) == FORMAT
+    assert p(A, B, -1, F32, C, None) == SHAPE
+    assert p(A, B, 16, F32, A, None) == UNSUP
+    assert p(A + 2, B, 16, F32, C, None) == ALIGN
+    assert p(None, B, 16, F32, C, None) == NULL
+    assert p(None, None, 0, F32, None, None) == OK
