@@ -88,6 +88,13 @@ def _load():
         lib.oracle_qzeros_pack.restype = ctypes.c_int
         lib.oracle_resolve_g_idx.argtypes = [P, I64, I64, P]
         lib.oracle_resolve_g_idx.restype = ctypes.c_int
+        lib.oracle_e2m1_round.argtypes = [ctypes.c_double, ctypes.c_int]
+        lib.oracle_e2m1_round.restype = ctypes.c_uint
+        lib.oracle_nvfp4_quantize.argtypes = [P, ctypes.c_int, I64, I64, I64, ctypes.c_float, ctypes.c_int, P, P]
+        lib.oracle_nvfp4_quantize.restype = ctypes.c_int
+        lib.oracle_int4_sym_quantize.argtypes = [P, ctypes.c_int, I64, I64, I64, I64, P, P]
+        lib.oracle_pack_planes.argtypes = [P, I64, ctypes.c_int, ctypes.c_int, P, P, P]
+        lib.oracle_unpack_planes.argtypes = [P, P, I64, ctypes.c_int, ctypes.c_int, P, P]
         lib.oracle_dequant_rows.argtypes = [ctypes.c_int, P, P, ctypes.c_float, I64, P, I64, P]
         lib.oracle_dequant_rows.restype = ctypes.c_int
         lib.oracle_gemv_rows.argtypes = [ctypes.c_int, P, P, ctypes.c_float, I64, P, ctypes.c_int, P, I64,
@@ -549,3 +556,64 @@ def mx_gemm_entries(wcodes, wscales, k: int, xfmt: int, xcodes, xscales, ms, ns)
     if rc:
         raise ValueError("oracle: unsupported MX element format %r" % xfmt)
     return y, sa
+
+
+# ---------------------------------------------------------------- encode side
+
+TIE_EVEN, TIE_LOWEST = 0, 1
+
+
+def e2m1_round(v: float, tie: int) -> int:
+    """Nearest E2M1 code, ties to the even code (0) or the lowest code (1)."""
+    return int(_load().oracle_e2m1_round(float(v), int(tie)))
+
+
+def _rows(X):
+    Xa = np.ascontiguousarray(X)
+    if Xa.dtype == np.float32:
+        return Xa, 0
+    if Xa.dtype == np.uint16:
+        return Xa, 1
+    raise TypeError("X must be float32 or bfloat16 bits (uint16)")
+
+
+def nvfp4_quantize(X: np.ndarray, scale2: float, tie: int):
+    """NVFP4 codes u8 [m][k/2] and E4M3FN scale bytes [m][k/16] of X [m][k]."""
+    Xa, dt = _rows(X)
+    m, k = Xa.shape
+    codes = np.zeros((m, k // 2), np.uint8)
+    scales = np.zeros((m, k // 16), np.uint8)
+    if _load().oracle_nvfp4_quantize(_ptr(Xa), dt, m, k, k, float(np.float32(scale2)), int(tie), _ptr(codes),
+                                     _ptr(scales)):
+        raise ValueError("tie must be 0 or 1")
+    return codes, scales
+
+
+def int4_sym_quantize(W: np.ndarray, group: int):
+    """Signed INT4 codes u8 [m][k/2] (two's complement nibbles, low = even)
+    and binary32 scales [m][k/group] of W [m][k]."""
+    Wa, dt = _rows(W)
+    m, k = Wa.shape
+    codes = np.zeros((m, k // 2), np.uint8)
+    scales = np.zeros((m, k // group), np.float32)
+    _load().oracle_int4_sym_quantize(_ptr(Wa), dt, m, k, k, group, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def pack_planes(vals, bits: int, lo: int):
+    v = np.ascontiguousarray(vals, dtype=np.uint32)
+    n = v.size
+    lo_w = np.zeros((n * lo + 31) // 32, np.uint32)
+    hi_w = np.zeros((n * (bits - lo) + 31) // 32, np.uint32)
+    scr = np.zeros(n, np.uint32)
+    _load().oracle_pack_planes(_ptr(v), n, bits, lo, _ptr(lo_w), _ptr(hi_w), _ptr(scr))
+    return lo_w, hi_w
+
+
+def unpack_planes(lo_w, hi_w, count: int, bits: int, lo: int) -> np.ndarray:
+    a = np.ascontiguousarray(lo_w, dtype=np.uint32)
+    b = np.ascontiguousarray(hi_w, dtype=np.uint32)
+    out = np.zeros(count, np.uint32)
+    scr = np.zeros(count, np.uint32)
+    _load().oracle_unpack_planes(_ptr(a), _ptr(b), count, bits, lo, _ptr(out), _ptr(scr))
+    return out

@@ -972,3 +972,128 @@ ORACLE_API int oracle_int4_sym_value(unsigned code)
     code &= 15u;
     return (code & 8u) ? (int)code - 16 : (int)code;
 }
+
+/* ------------------------------------------------------------------ */
+/* Encode side: E2M1 with the two tie rules, NVFP4, INT4 symmetric,    */
+/* bit planes                                                          */
+/* ------------------------------------------------------------------ */
+
+/* Nearest E2M1 code to v, magnitudes above 6 saturating to 6. tie 0: ties
+ * to the even code (ModelOpt's midpoints, [NV] section 7.2); tie 1: the
+ * lowest unsigned code ([FB] section 2, the lab convention). The sign of
+ * zero follows v. */
+ORACLE_API unsigned oracle_e2m1_round(double v, int tie)
+{
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    unsigned sign = signbit(v) ? 8u : 0u;
+    double a = fabs(v);
+    if (a > 6.0)
+        a = 6.0;
+    unsigned best = 0;
+    for (unsigned c = 1; c < 8; ++c) {
+        double dc = fabs(a - grid[c]), db = fabs(a - grid[best]);
+        if (dc < db || (dc == db && tie == 0 && (c & 1u) == 0))
+            best = c; /* tie 1 keeps the lower code on an exact tie */
+    }
+    return sign | best;
+}
+
+/* NVFP4 quantization of the rows of X [m][k] (binary32 or bfloat16 bits,
+ * row stride ldx), k a multiple of 16, for a given positive scale2 ([WK]
+ * section 5: x = q_E2M1 * s_block(E4M3) * s_global; [NV] sections 7.1-7.2).
+ * Per block of 16, in binary32 arithmetic:
+ *   amax = max |x|; s = E4M3FN_RNE(RN32(amax / RN32(6 * scale2))) (the block
+ *   maximum lands on the top E2M1 magnitude 6; saturating at 448);
+ *   t = RN32(E4M3FN(s) * scale2);
+ *   if t == 0 every code is +0; else code_i = E2M1(RN32(x_i / t)) with the
+ *   tie rule (0 ties-to-even, 1 lowest code).
+ * Codes [m][k/2] (low nibble = even element), scale bytes [m][k/16]. */
+ORACLE_API int oracle_nvfp4_quantize(const void *x, int xdtype, int64_t m, int64_t k, int64_t ldx, float scale2,
+                                     int tie, uint8_t *codes, uint8_t *scales)
+{
+    if (tie != 0 && tie != 1)
+        return 1;
+    const float den = 6.0f * scale2;
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t b = 0; b < k / 16; ++b) {
+            float v[16], amax = 0.0f;
+            for (int j = 0; j < 16; ++j) {
+                int64_t e = i * ldx + 16 * b + j;
+                v[j] = xdtype == 1 ? (float)oracle_bf16_value(((const uint16_t *)x)[e]) : ((const float *)x)[e];
+                if (fabsf(v[j]) > amax)
+                    amax = fabsf(v[j]);
+            }
+            const float qs = amax / den;
+            const unsigned sb = oracle_e4m3fn_rne((double)qs) & 0x7Fu;
+            scales[i * (k / 16) + b] = (uint8_t)sb;
+            const float t = (float)oracle_e4m3fn(sb) * scale2;
+            for (int j = 0; j < 16; j += 2) {
+                unsigned lo = 0, hi = 0;
+                if (t != 0.0f) {
+                    lo = oracle_e2m1_round((double)(v[j] / t), tie);
+                    hi = oracle_e2m1_round((double)(v[j + 1] / t), tie);
+                }
+                codes[i * (k / 2) + 8 * b + j / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    return 0;
+}
+
+/* Signed INT4 symmetric quantization ([WK] section 1): per group of `group`
+ * consecutive elements of a row, s = RN32(max |w| / 7) and
+ * q = clip(round_half_even(RN32(w / s)), -8, 7) (a zero group has s = 0 and
+ * q = 0); codes two's-complement nibbles [m][k/2], the earlier element in
+ * the low nibble; scales binary32 [m][k/group]. */
+ORACLE_API void oracle_int4_sym_quantize(const void *w, int wdtype, int64_t m, int64_t k, int64_t ldw,
+                                         int64_t group, uint8_t *codes, float *scales)
+{
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t g = 0; g < k / group; ++g) {
+            float amax = 0.0f;
+            for (int64_t j = 0; j < group; ++j) {
+                int64_t e = i * ldw + g * group + j;
+                float v = wdtype == 1 ? (float)oracle_bf16_value(((const uint16_t *)w)[e]) : ((const float *)w)[e];
+                if (fabsf(v) > amax)
+                    amax = fabsf(v);
+            }
+            const float sc = amax / 7.0f;
+            scales[i * (k / group) + g] = sc;
+            for (int64_t j = 0; j < group; ++j) {
+                int64_t e = i * ldw + g * group + j;
+                float v = wdtype == 1 ? (float)oracle_bf16_value(((const uint16_t *)w)[e]) : ((const float *)w)[e];
+                int q = 0;
+                if (sc != 0.0f) {
+                    double r = nearbyint((double)(v / sc));
+                    q = r < -8.0 ? -8 : r > 7.0 ? 7 : (int)r;
+                }
+                int64_t c = g * group + j;
+                uint8_t *byte = &codes[i * (k / 2) + c / 2];
+                unsigned nib = (unsigned)q & 15u;
+                *byte = (c & 1) ? (uint8_t)((*byte & 0x0Fu) | (nib << 4)) : (uint8_t)((*byte & 0xF0u) | nib);
+            }
+        }
+}
+
+/* Bit-plane split of b-bit codes ([BP] "Odd widths"): the low `lo` bits of
+ * every value form one little-endian word stream and the high b - lo bits
+ * another, each packed as oracle_pack_bits does (GGUF's Q6_K keeps 4 + 2).
+ * count * lo and count * (b - lo) must be multiples of 32. */
+ORACLE_API void oracle_pack_planes(const uint32_t *vals, int64_t count, int bits, int lo, uint32_t *lo_words,
+                                   uint32_t *hi_words, uint32_t *scratch)
+{
+    for (int64_t i = 0; i < count; ++i)
+        scratch[i] = vals[i] & ((1u << lo) - 1u);
+    oracle_pack_bits(scratch, count, lo, lo_words);
+    for (int64_t i = 0; i < count; ++i)
+        scratch[i] = vals[i] >> lo;
+    oracle_pack_bits(scratch, count, bits - lo, hi_words);
+}
+
+ORACLE_API void oracle_unpack_planes(const uint32_t *lo_words, const uint32_t *hi_words, int64_t count, int bits,
+                                     int lo, uint32_t *vals, uint32_t *scratch)
+{
+    oracle_unpack_bits(lo_words, count, lo, vals);
+    oracle_unpack_bits(hi_words, count, bits - lo, scratch);
+    for (int64_t i = 0; i < count; ++i)
+        vals[i] |= scratch[i] << lo;
+}
