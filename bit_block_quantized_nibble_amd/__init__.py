@@ -38,6 +38,7 @@ EXPORTED = (
     "qbn_quantized_gemv", "qbn_quantized_gemm", "qbn_dequantize", "qbn_repack", "qbn_validate",
     "qbn_quantize_q8", "qbn_quantized_gemv_q8", "qbn_quantize_mx", "qbn_quantized_gemm_mx",
     "qbn_gptq_qzeros", "qbn_gptq_resolve_g_idx", "qbn_permute",
+    "qbn_quantize_nvfp4", "qbn_quantize_int4_sym", "qbn_pack_bits", "qbn_unpack_bits",
 )
 
 
@@ -94,6 +95,14 @@ def _load():
         lib.qbn_gptq_resolve_g_idx.restype = I32
         lib.qbn_permute.argtypes = [P, P, I64, I32, P, P]
         lib.qbn_permute.restype = I32
+        lib.qbn_quantize_nvfp4.argtypes = [P, I32, I64, I64, I64, ctypes.c_float, I32, P, P, P]
+        lib.qbn_quantize_nvfp4.restype = I32
+        lib.qbn_quantize_int4_sym.argtypes = [P, I32, I64, I64, I64, I32, P, P, P]
+        lib.qbn_quantize_int4_sym.restype = I32
+        lib.qbn_pack_bits.argtypes = [P, I64, I32, I32, P, P, P]
+        lib.qbn_pack_bits.restype = I32
+        lib.qbn_unpack_bits.argtypes = [P, P, I64, I32, I32, P, P]
+        lib.qbn_unpack_bits.restype = I32
         lib.qbn_validate.argtypes = [T, P, P]
         lib.qbn_validate.restype = I32
         lib.qbn_quantize_q8.argtypes = [P, I32, I64, P, P, P, P]
@@ -215,6 +224,61 @@ def permute(src: torch.Tensor, perm: torch.Tensor, dst: Optional[torch.Tensor] =
     _check(lib.qbn_permute(_ptr(src, "src"), _ptr(perm, "perm"), src.numel(), _DTYPES[src.dtype], _ptr(dst, "dst"),
                            _stream(src.device)), "qbn_permute")
     return dst
+
+
+def quantize_nvfp4(x: torch.Tensor, scale2: float, tie: int = 0):
+    """NVFP4 encode of x [m][k] (float32 or bfloat16): (codes uint8 [m][k/2],
+    E4M3FN scale bytes uint8 [m][k/16]); tie 0 ties-to-even, 1 lowest code."""
+    lib = _load()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    m, k = x.shape
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((m, k // 16), dtype=torch.uint8, device=x.device)
+    ldx = x.stride(0) if m > 1 else k
+    _check(lib.qbn_quantize_nvfp4(_ptr(x, "x"), _DTYPES.get(x.dtype, -1), m, k, ldx, float(scale2), int(tie),
+                                  _ptr(codes, "codes"), _ptr(scales, "scales"), _stream(x.device)),
+           "qbn_quantize_nvfp4")
+    return codes, scales
+
+
+def quantize_int4_sym(w: torch.Tensor, group: int):
+    """Signed INT4 symmetric encode of w [m][k]: (codes uint8 [m][k/2],
+    scales float32 [m][k/group])."""
+    lib = _load()
+    if w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be 2-D with contiguous rows")
+    m, k = w.shape
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((m, k // group), dtype=torch.float32, device=w.device)
+    ldw = w.stride(0) if m > 1 else k
+    _check(lib.qbn_quantize_int4_sym(_ptr(w, "w"), _DTYPES.get(w.dtype, -1), m, k, ldw, int(group),
+                                     _ptr(codes, "codes"), _ptr(scales, "scales"), _stream(w.device)),
+           "qbn_quantize_int4_sym")
+    return codes, scales
+
+
+def pack_bits(values: torch.Tensor, bits: int, lo_bits: int = 0):
+    """Pack uint8 values (one per element) into int32 word streams: one
+    stream (lo_bits 0) or two bit planes. Returns (words_lo, words_hi or None)."""
+    lib = _load()
+    n = values.numel()
+    w0 = lo_bits if lo_bits else bits
+    lo = torch.empty((n * w0 + 31) // 32, dtype=torch.int32, device=values.device)
+    hi = (torch.empty((n * (bits - lo_bits) + 31) // 32, dtype=torch.int32, device=values.device) if lo_bits
+          else None)
+    _check(lib.qbn_pack_bits(_ptr(values, "values"), n, int(bits), int(lo_bits), _ptr(lo, "words_lo"),
+                             _ptr(hi, "words_hi"), _stream(values.device)), "qbn_pack_bits")
+    return lo, hi
+
+
+def unpack_bits(words_lo: torch.Tensor, words_hi: Optional[torch.Tensor], count: int, bits: int,
+                lo_bits: int = 0) -> torch.Tensor:
+    lib = _load()
+    out = torch.empty(count, dtype=torch.uint8, device=words_lo.device)
+    _check(lib.qbn_unpack_bits(_ptr(words_lo, "words_lo"), _ptr(words_hi, "words_hi"), count, int(bits),
+                               int(lo_bits), _ptr(out, "values"), _stream(words_lo.device)), "qbn_unpack_bits")
+    return out
 
 
 def quantized_gemv(w: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -295,6 +295,54 @@ int32_t qbn_permute(const void *src, const int32_t *perm, int64_t count, int32_t
     return hip_status(qbn::launch_permute(src, perm, count, eb, dst, (hipStream_t)stream));
 }
 
+int32_t qbn_quantize_nvfp4(const void *x, int32_t x_dtype, int64_t m, int64_t k, int64_t ldx, float scale2,
+                           int32_t tie, void *codes, void *scales, void *stream) {
+    if (x_dtype < QBN_F32 || x_dtype > QBN_F16 || (tie != 0 && tie != 1)) return QBN_ERR_FORMAT;
+    if (x_dtype == QBN_F16) return QBN_ERR_DTYPE;
+    if (!(isfinite(scale2) && scale2 > 0.0f)) return QBN_ERR_SCALE2;
+    if (m < 0 || k < 0 || k % 16 || m > kMaxElems || k > kMaxElems || (m > 0 && k > kMaxElems / m)) return QBN_ERR_SHAPE;
+    if (m == 0 || k == 0) return QBN_OK;
+    if (ldx < k || ldx > kMaxElems / m) return QBN_ERR_SHAPE;
+    if (!x || !codes || !scales) return QBN_ERR_NULL;
+    if (!aligned(x, x_dtype == QBN_F32 ? 4 : 2) || !aligned(codes, 8)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_quantize_nvfp4(x, x_dtype, m, k, ldx, scale2, tie, codes, scales,
+                                                 (hipStream_t)stream));
+}
+
+int32_t qbn_quantize_int4_sym(const void *w, int32_t w_dtype, int64_t m, int64_t k, int64_t ldw, int32_t group,
+                              void *codes, float *scales, void *stream) {
+    if (w_dtype < QBN_F32 || w_dtype > QBN_F16) return QBN_ERR_FORMAT;
+    if (w_dtype == QBN_F16) return QBN_ERR_DTYPE;
+    if (group <= 0 || group % 2) return QBN_ERR_GROUP;
+    if (m < 0 || k < 0 || k % group || m > kMaxElems || k > kMaxElems || (m > 0 && k > kMaxElems / m))
+        return QBN_ERR_SHAPE;
+    if (m == 0 || k == 0) return QBN_OK;
+    if (ldw < k || ldw > kMaxElems / m) return QBN_ERR_SHAPE;
+    if (!w || !codes || !scales) return QBN_ERR_NULL;
+    if (!aligned(w, w_dtype == QBN_F32 ? 4 : 2) || !aligned(scales, 4)) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_quantize_int4_sym(w, w_dtype, m, k, ldw, group, codes, scales, (hipStream_t)stream));
+}
+
+int32_t qbn_pack_bits(const void *values, int64_t count, int32_t bits, int32_t lo_bits, void *words_lo,
+                      void *words_hi, void *stream) {
+    if (bits < 1 || bits > 8 || lo_bits < 0 || lo_bits >= bits) return QBN_ERR_FORMAT;
+    if (count < 0 || count > kMaxElems) return QBN_ERR_SHAPE;
+    if (count == 0) return QBN_OK;
+    if (!values || !words_lo || (lo_bits > 0 && !words_hi)) return QBN_ERR_NULL;
+    if (!aligned(words_lo, 4) || (lo_bits > 0 && !aligned(words_hi, 4))) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_pack_bits(values, count, bits, lo_bits, words_lo, words_hi, (hipStream_t)stream));
+}
+
+int32_t qbn_unpack_bits(const void *words_lo, const void *words_hi, int64_t count, int32_t bits, int32_t lo_bits,
+                        void *values, void *stream) {
+    if (bits < 1 || bits > 8 || lo_bits < 0 || lo_bits >= bits) return QBN_ERR_FORMAT;
+    if (count < 0 || count > kMaxElems) return QBN_ERR_SHAPE;
+    if (count == 0) return QBN_OK;
+    if (!values || !words_lo || (lo_bits > 0 && !words_hi)) return QBN_ERR_NULL;
+    if (!aligned(words_lo, 4) || (lo_bits > 0 && !aligned(words_hi, 4))) return QBN_ERR_ALIGN;
+    return hip_status(qbn::launch_unpack_bits(words_lo, words_hi, count, bits, lo_bits, values, (hipStream_t)stream));
+}
+
 int32_t qbn_repack(const qbn_tensor *src, int32_t dst_format, int32_t dst_group, void *dst_data, void *dst_scales,
                    void *dst_zeros, void *stream) {
     int32_t st = check_tensor(src);

@@ -18,6 +18,14 @@ hipError_t launch_gptq_resolve_g_idx(const void *qweight, const int32_t *g_idx, 
 hipError_t launch_permute(const void *src, const int32_t *perm, int64_t count, int elem_bytes, void *dst,
                           hipStream_t s);
 bool gptq_groups_fit(int64_t k, int64_t group);
+hipError_t launch_quantize_nvfp4(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, float scale2, int tie,
+                                 void *codes, void *scales, hipStream_t s);
+hipError_t launch_quantize_int4_sym(const void *w, int w_dtype, int64_t m, int64_t k, int64_t ldw, int64_t group,
+                                    void *codes, float *scales, hipStream_t s);
+hipError_t launch_pack_bits(const void *values, int64_t count, int bits, int lo, void *words_lo, void *words_hi,
+                            hipStream_t s);
+hipError_t launch_unpack_bits(const void *words_lo, const void *words_hi, int64_t count, int bits, int lo,
+                              void *values, hipStream_t s);
 hipError_t launch_gemm(const qbn_tensor &w, int64_t m, const void *x, int64_t ldx, void *y, int64_t ldy,
                        hipStream_t s);
 hipError_t launch_dequant(const qbn_tensor &w, void *out, int out_dtype, int out_layout, hipStream_t s);

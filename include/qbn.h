@@ -279,6 +279,44 @@ QBN_API int32_t qbn_gptq_resolve_g_idx(const void *qweight, const int32_t *g_idx
 QBN_API int32_t qbn_permute(const void *src, const int32_t *perm, int64_t count, int32_t dtype, void *dst,
                             void *stream);
 
+/* NVFP4 quantization (the encode step; [WK] section 5: x = q_E2M1 *
+ * s_block(E4M3) * s_global; [NV] section 7.2: ModelOpt's ties-to-even E2M1
+ * midpoints; [FB] section 2: the lowest code on a tie). X [m][ldx]
+ * (QBN_F32 or QBN_BF16, finite), k % 16 == 0, scale2 finite and > 0 (the
+ * caller's per-tensor scale). Per block of 16, in binary32:
+ *   s = E4M3FN(amax / (6 * scale2)) (nearest, ties to even, <= 448),
+ *   t = s * scale2, code = E2M1(x / t) (a t of 0 gives codes +0),
+ * tie 0: ties to the even code; tie 1: ties to the lowest code; magnitudes
+ * past 6 saturate. codes [m][k/2] (low nibble = even element, 8-byte
+ * aligned), scales u8 [m][k/16]: a QBN_NVFP4 tensor with this scale2.
+ * Bit-exact. */
+QBN_API int32_t qbn_quantize_nvfp4(const void *x, int32_t x_dtype, int64_t m, int64_t k, int64_t ldx, float scale2,
+                                   int32_t tie, void *codes, void *scales, void *stream);
+
+/* Signed INT4 symmetric quantization ([WK] section 1): W [m][ldw] (QBN_F32
+ * or QBN_BF16), per group of `group` (even) consecutive elements of a row,
+ * s = amax / 7 (binary32; 0 for a zero group, whose codes are 0) and
+ * q = clip(round_half_even(w / s), -8, 7). codes u8 [m][k/2]: two's-
+ * complement nibbles, the earlier element in the low nibble; scales
+ * binary32 [m][k/group]. Bit-exact. */
+QBN_API int32_t qbn_quantize_int4_sym(const void *w, int32_t w_dtype, int64_t m, int64_t k, int64_t ldw,
+                                      int32_t group, void *codes, float *scales, void *stream);
+
+/* b-bit packing ([BP] "The packing arithmetic", "Odd widths"), 1 <= bits
+ * <= 8, values u8 [count] (bits above `bits` ignored). lo_bits == 0: one
+ * little-endian stream of 32-bit words, element i at bits [i*bits,
+ * i*bits + bits) (fields straddle words when bits does not divide 32),
+ * words_lo [ceil(count*bits/32)], the last word zero-padded. 0 < lo_bits <
+ * bits: bit planes, the low lo_bits of each value in words_lo
+ * [ceil(count*lo_bits/32)] and the high bits - lo_bits in words_hi, each a
+ * stream as above (GGUF's Q6_K keeps 4 + 2). Bit-exact. */
+QBN_API int32_t qbn_pack_bits(const void *values, int64_t count, int32_t bits, int32_t lo_bits, void *words_lo,
+                              void *words_hi, void *stream);
+
+/* The inverse of qbn_pack_bits: values u8 [count]. */
+QBN_API int32_t qbn_unpack_bits(const void *words_lo, const void *words_hi, int64_t count, int32_t bits,
+                                int32_t lo_bits, void *values, void *stream);
+
 /* Bit-exact repack of the int4 codes through the logical matrix
  * ([BP] "Repacking between formats"): src and destination share n and k.
  * Directions: GPTQ4 <-> AWQ4, GPTQ4 <-> Q4_0, AWQ4 <-> Q4_0.

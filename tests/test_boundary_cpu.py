@@ -36,7 +36,7 @@ def T(fmt, n, k, data=A, scales=B, zeros=C, scale2=1.0, group=0, reserved=0):
 def test_exports_every_declared_symbol(lib):
     header = open(os.path.join(ROOT, "include", "qbn.h")).read()
     declared = re.findall(r"QBN_API\s+[\w\s\*]+?\b(qbn_\w+)\s*\(", header)
-    assert len(declared) == 17
+    assert len(declared) == 21
     assert set(declared) == set(qbn.EXPORTED)
     so = ctypes.CDLL(qbn.lib_path())
     for name in declared:
@@ -265,3 +265,35 @@ def test_gptq_meta_rejections(lib):
     assert p(A + 2, B, 16, F32, C, None) == ALIGN
     assert p(None, B, 16, F32, C, None) == NULL
     assert p(None, None, 0, F32, None, None) == OK
+
+
+def test_encode_rejections(lib):
+    q = lib.qbn_quantize_nvfp4
+    assert q(A, F32, 4, 64, 64, ctypes.c_float(1.0), 2, B, C, None) == FORMAT
+    assert q(A, 2, 4, 64, 64, ctypes.c_float(1.0), 0, B, C, None) == DTYPE
+    assert q(A, F32, 4, 64, 64, ctypes.c_float(0.0), 0, B, C, None) == SCALE2
+    assert q(A, F32, 4, 64, 64, ctypes.c_float(float("inf")), 0, B, C, None) == SCALE2
+    assert q(A, F32, 4, 40, 40, ctypes.c_float(1.0), 0, B, C, None) == SHAPE
+    assert q(A, F32, 4, 64, 32, ctypes.c_float(1.0), 0, B, C, None) == SHAPE
+    assert q(None, F32, 4, 64, 64, ctypes.c_float(1.0), 0, B, C, None) == NULL
+    assert q(A + 2, F32, 4, 64, 64, ctypes.c_float(1.0), 0, B, C, None) == ALIGN
+    assert q(A, F32, 4, 64, 64, ctypes.c_float(1.0), 0, B + 4, C, None) == ALIGN
+    assert q(None, F32, 0, 64, 64, ctypes.c_float(1.0), 0, None, None, None) == OK
+    i = lib.qbn_quantize_int4_sym
+    assert i(A, F32, 4, 64, 64, 3, B, C, None) == GROUP
+    assert i(A, F32, 4, 64, 64, 0, B, C, None) == GROUP
+    assert i(A, F32, 4, 60, 60, 8, B, C, None) == SHAPE
+    assert i(A, 2, 4, 64, 64, 8, B, C, None) == DTYPE
+    assert i(A, F32, 4, 64, 64, 8, B, C + 2, None) == ALIGN
+    assert i(A, F32, 4, 64, 64, 8, None, C, None) == NULL
+    p = lib.qbn_pack_bits
+    assert p(A, 64, 9, 0, B, None, None) == FORMAT
+    assert p(A, 64, 6, 6, B, C, None) == FORMAT
+    assert p(A, 64, 6, 4, B, None, None) == NULL
+    assert p(A, 64, 3, 0, B + 2, None, None) == ALIGN
+    assert p(A, -1, 3, 0, B, None, None) == SHAPE
+    assert p(None, 0, 3, 0, None, None, None) == OK
+    u = lib.qbn_unpack_bits
+    assert u(A, None, 64, 0, 0, B, None) == FORMAT
+    assert u(A, None, 64, 6, 2, B, None) == NULL
+    assert u(A + 1, None, 64, 5, 0, B, None) == ALIGN
