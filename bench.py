@@ -93,6 +93,11 @@ WORKLOADS = {
         cfg=7, kind="int4gemv", fmt="q4_0", unit="GB/s",
         desc="Q4_0 decode GEMV 11008x4096 (18-byte blocks of 32: fp16 d, w = d(q-8)), x f32, y f32, batch 1",
         bytes=11008 * 128 * 18 + 4096 * 4 + 11008 * 4),
+    "nvfp4_encode": dict(
+        cfg=2, kind="encode", unit="GB/s", dtype="f32",
+        desc="NVFP4 encode of a bf16 4096x4096 weight (block scale E4M3(amax / 6 scale2), E2M1 ties to even, "
+             "scale2 = 0.01): read bf16, write codes and scale bytes",
+        bytes=4096 * 4096 * 2 + 4096 * 2048 + 4096 * 256),
     "mxfp4_gemm": dict(
         cfg=4, kind="gemm", unit="TFLOP/s",
         desc="MXFP4 prefill GEMM: W 8192x8192 (E2M1, E8M0 per 32) x X bf16 2048x8192 -> Y bf16, fp32 accumulate",
@@ -206,6 +211,20 @@ def build_steps(name, spec, dev):
             return run
 
         return [step(g) for g in gemvs], R, inp, gemvs
+    if spec["kind"] == "encode":
+        n, k = inp["n"], inp["k"]
+        # the weight to encode: the NVFP4 workload's dequantized values, as bf16 (generated on the device)
+        w = qbn.QTensor("nvfp4", n, k, host_to_device(inp["data"], dev), host_to_device(inp["scales"], dev),
+                        scale2=inp["scale2"])
+        Wb = qbn.dequantize(w, dtype=torch.bfloat16)
+        wbytes = Wb.numel() * 2
+        R = max(1, math.ceil(ROTATE_BYTES / wbytes))
+        srcs = [Wb.clone() for _ in range(R)]
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+        for W in srcs:
+            calls.append(qbn.prepare_quantize_nvfp4(W, inp["scale2"], 0, codes, scales))
+        return calls, R, dict(inp, W=Wb), None
     if spec["kind"] == "int4gemv":
         K, N, g = inp["K"], inp["N"], inp["group"]
         fmt = spec["fmt"]
@@ -332,6 +351,19 @@ def cpu_baseline(name, spec, inp, budget_s):
         return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
                     sample="full quantize + %dx%d integer-exact NVFP4 decode, median of %d runs (%.2f s each)"
                     % (n, k, len(reps), t))
+    if spec["kind"] == "encode":
+        import torch
+        n, k = inp["n"], inp["k"]
+        Wb = inp["W"].view(torch.int16).cpu().numpy().view(np.uint16)
+        while True:
+            t0 = time.perf_counter()
+            oracle.nvfp4_quantize(Wb, inp["scale2"], 0)
+            reps.append(time.perf_counter() - t0)
+            if time.perf_counter() > t_end and len(reps) >= 3:
+                break
+        t = float(np.median(reps))
+        return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                    sample="full %dx%d encode, median of %d runs (%.2f s each)" % (n, k, len(reps), t))
     if spec["kind"] == "int4gemv":
         K, N, g = inp["K"], inp["N"], inp["group"]
         fmt = spec["fmt"]
@@ -538,7 +570,8 @@ def main():
         achieved = spec.get("kernel_bytes", spec["bytes"]) / (kernel_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=recorded_traffic(args.workload))
-        metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] in ("gemv", "w4a8", "a16q8", "int4gemv") else (
+        metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] in ("gemv", "w4a8", "a16q8", "int4gemv") else \
+            "NVFP4 encode GB/s (% HBM peak)" if spec["kind"] == "encode" else (
             "int4 repack GB/s (% HBM peak)" if spec["kind"] == "repack" else "bulk dequant GB/s (% HBM peak)")
 
     cpu = None

@@ -509,6 +509,15 @@ def prepare_gemm_mx(w: QTensor, xcodes: torch.Tensor, xscales: torch.Tensor, y: 
     return Prepared(lib.qbn_quantized_gemm_mx, args, "qbn_quantized_gemm_mx", w.device, (w, xcodes, xscales, y, ct))
 
 
+def prepare_quantize_nvfp4(x: torch.Tensor, scale2: float, tie: int, codes: torch.Tensor,
+                           scales: torch.Tensor) -> Prepared:
+    lib = _load()
+    m, k = x.shape
+    args = (ctypes.c_void_p(x.data_ptr()), _DTYPES.get(x.dtype, -1), m, k, x.stride(0) if m > 1 else k,
+            ctypes.c_float(scale2), int(tie), _ptr(codes, "codes"), _ptr(scales, "scales"))
+    return Prepared(lib.qbn_quantize_nvfp4, args, "qbn_quantize_nvfp4", x.device, (x, codes, scales))
+
+
 def prepare_gemm(w: QTensor, x: torch.Tensor, y: torch.Tensor) -> Prepared:
     lib = _load()
     if not (x.is_cuda and y.is_cuda) or x.stride(1) != 1 or y.stride(1) != 1:
