@@ -1,6 +1,7 @@
 """CPU oracle for 4-bit block-quantized weights (test infrastructure only).
 
-Plain, slow reference definitions of the MXFP4, NVFP4, Q4_K and Q4_0 decoders,
+Plain, slow reference definitions of the MXFP4, NVFP4 (also in CKE's split-half
+blocks), Q4_K and Q4_0 decoders,
 of the GPTQ / AWQ / Q4_0 int4 layouts, of the dot products built on them, and
 of the W4A8 route (int8 activation quantization, Q4_K x int8 dot) and of the
 integer-exact NVFP4 x Q8_K decode.
@@ -33,6 +34,7 @@ _LIB_PATH = os.path.join(_BUILD, "liboracle.so")
 
 MXFP4, NVFP4, Q4_K, Q4_0 = 1, 2, 3, 4
 MXFP8 = 7  # activation format: E4M3FN elements, E8M0 scale per 32
+NVFP4_CKE = 8  # NVFP4 in CKE's 36-byte split-half blocks of 64 weights
 
 _lock = threading.Lock()
 _lib = None
@@ -79,6 +81,8 @@ def _load():
         for name in ("oracle_gptq_pack", "oracle_gptq_unpack", "oracle_awq_pack", "oracle_awq_unpack"):
             getattr(lib, name).argtypes = [P, I64, I64, P]
         lib.oracle_q4_0_pack.argtypes = [P, P, I64, I64, P]
+        lib.oracle_cke_pack.argtypes = [P, P, I64, I64, P]
+        lib.oracle_cke_unpack.argtypes = [P, I64, I64, P, P]
         lib.oracle_q4_0_unpack.argtypes = [P, I64, I64, P, P]
         lib.oracle_affine_dequant.argtypes = [P, P, P, I64, I64, I64, P]
         lib.oracle_gemv_kn.argtypes = [P, I64, I64, P, ctypes.c_int, P, I64, P, P, P]
@@ -262,6 +266,32 @@ def awq_unpack(qw: np.ndarray) -> np.ndarray:
     out = np.zeros((K, N8 * 8), dtype=np.uint8)
     _load().oracle_awq_unpack(_ptr(qw), K, N8 * 8, _ptr(out))
     return out
+
+
+def cke_pack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Logical E2M1 codes u8 [n][k] and E4M3FN subscales u8 [n][k/16] ->
+    CKE split-half NVFP4 blocks u8 [n][k/64][36] ("Why 4-Bit Quantization Is
+    King", section 5: four subscales, then 32 code bytes; inside a 16-weight
+    subblock the low nibbles of its eight bytes are weights 0-7 and the high
+    nibbles weights 8-15)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    n, k = c.shape
+    assert k % 64 == 0
+    s = np.ascontiguousarray(scales, dtype=np.uint8)
+    assert s.shape == (n, k // 16)
+    out = np.zeros((n, k // 64, 36), dtype=np.uint8)
+    _load().oracle_cke_pack(_ptr(c), _ptr(s), n, k, _ptr(out))
+    return out
+
+
+def cke_unpack(blocks: np.ndarray, n: int, k: int) -> tuple[np.ndarray, np.ndarray]:
+    """CKE blocks -> (logical codes u8 [n][k], subscales u8 [n][k/16])."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    assert b.size == n * (k // 64) * 36
+    codes = np.zeros((n, k), dtype=np.uint8)
+    scales = np.zeros((n, k // 16), dtype=np.uint8)
+    _load().oracle_cke_unpack(_ptr(b), n, k, _ptr(codes), _ptr(scales))
+    return codes, scales
 
 
 def q4_0_pack(q: np.ndarray, d_bits: np.ndarray) -> np.ndarray:

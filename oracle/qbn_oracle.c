@@ -206,6 +206,28 @@ static void nvfp4_row(const uint8_t *codes, const uint8_t *scales, float scale2,
     }
 }
 
+/* CKE's NVFP4 storage block ([WK] section 5): [n][k/64] blocks of 36 bytes
+ * holding 64 consecutive weights of a row. Bytes 0..3 are the E4M3FN
+ * subscales of the four 16-weight subblocks, in order; bytes 4..35 are the
+ * codes, eight bytes per subblock in subblock order. Inside subblock j, the
+ * low nibble of its byte i is weight 16j + i and the high nibble weight
+ * 16j + 8 + i (split-half order, not adjacent pairs). The per-tensor scale2
+ * is a separate operand. Reconstruction is the NVFP4 rule: (E2M1 * E4M3FN)
+ * exactly, then times scale2 with one rounding. */
+static void nvfp4_cke_row(const uint8_t *data, float scale2, int64_t k, int64_t r, float *out)
+{
+    const uint8_t *row = data + r * (k / 64) * 36;
+    for (int64_t i = 0; i < k; ++i) {
+        const uint8_t *blk = row + (i / 64) * 36;
+        const int64_t j = (i % 64) / 16; /* subblock */
+        const int64_t l = i % 16;        /* weight inside the subblock */
+        const unsigned byte = blk[4 + 8 * j + (l % 8)];
+        const unsigned code = l < 8 ? (byte & 15u) : (byte >> 4);
+        float local = (float)(oracle_e2m1(code) * oracle_e4m3fn(blk[j]));
+        out[i] = (float)((double)local * (double)scale2);
+    }
+}
+
 /* Q4_K: 144-byte super-blocks of 256 weights, [n][k/256]. Byte layout:
  * fp16 d at 0, fp16 dmin at 2, 12 metadata bytes at 4, 128 code bytes at 16.
  * Code byte 32c+l (c = 0..3, l = 0..31) holds, in its low nibble, output
@@ -414,6 +436,39 @@ ORACLE_API int oracle_resolve_g_idx(const int32_t *g_idx, int64_t K, int64_t gro
  * each output column n and are stored [N][K/32] x 18 bytes; block (n, b)
  * holds q[32b .. 32b+31][n], byte j = element j (low) | element j+16 (high).
  * d_bits[(n*(K/32)) + b] is written as the fp16 d of each block. */
+/* CKE split-half NVFP4 blocks (layout in nvfp4_cke_row above) from
+ * logical E2M1 codes u8 [n][k] (0..15) and E4M3FN subscale bytes
+ * u8 [n][k/16]; blocks u8 [n][k/64][36]. */
+ORACLE_API void oracle_cke_pack(const uint8_t *codes, const uint8_t *scales, int64_t n, int64_t k, uint8_t *blocks)
+{
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < k / 64; ++b) {
+            uint8_t *blk = blocks + (r * (k / 64) + b) * 36;
+            for (int j = 0; j < 4; ++j) {
+                blk[j] = scales[r * (k / 16) + 4 * b + j];
+                const uint8_t *c = codes + r * k + 64 * b + 16 * j;
+                for (int i = 0; i < 8; ++i)
+                    blk[4 + 8 * j + i] = (uint8_t)((c[i] & 15u) | ((c[i + 8] & 15u) << 4));
+            }
+        }
+}
+
+ORACLE_API void oracle_cke_unpack(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *codes, uint8_t *scales)
+{
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < k / 64; ++b) {
+            const uint8_t *blk = blocks + (r * (k / 64) + b) * 36;
+            for (int j = 0; j < 4; ++j) {
+                scales[r * (k / 16) + 4 * b + j] = blk[j];
+                uint8_t *c = codes + r * k + 64 * b + 16 * j;
+                for (int i = 0; i < 8; ++i) {
+                    c[i] = blk[4 + 8 * j + i] & 15u;
+                    c[i + 8] = blk[4 + 8 * j + i] >> 4;
+                }
+            }
+        }
+}
+
 ORACLE_API void oracle_q4_0_pack(const uint8_t *q, const uint16_t *d_bits, int64_t K, int64_t N,
                                  uint8_t *blocks)
 {
@@ -465,7 +520,7 @@ ORACLE_API void oracle_affine_dequant(const uint8_t *q, const uint16_t *scale_bi
 /* Format dispatch: dequantize chosen rows of an n x k weight          */
 /* ------------------------------------------------------------------ */
 
-enum { OR_MXFP4 = 1, OR_NVFP4 = 2, OR_Q4_K = 3, OR_Q4_0 = 4 };
+enum { OR_MXFP4 = 1, OR_NVFP4 = 2, OR_Q4_K = 3, OR_Q4_0 = 4, OR_NVFP4_CKE = 8 };
 
 static int row_dequant(int fmt, const uint8_t *data, const uint8_t *scales, float scale2, int64_t k,
                        int64_t r, float *out)
@@ -475,6 +530,7 @@ static int row_dequant(int fmt, const uint8_t *data, const uint8_t *scales, floa
     case OR_NVFP4: nvfp4_row(data, scales, scale2, k, r, out); return 0;
     case OR_Q4_K: q4k_row(data, k, r, out); return 0;
     case OR_Q4_0: q4_0_row(data, k, r, out); return 0;
+    case OR_NVFP4_CKE: nvfp4_cke_row(data, scale2, k, r, out); return 0;
     default: return -1;
     }
 }
