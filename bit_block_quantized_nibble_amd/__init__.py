@@ -24,7 +24,7 @@ __all__ = [
     "prepare_repack",
 ]
 
-FORMATS = {"mxfp4": 1, "nvfp4": 2, "q4_k": 3, "q4_0": 4, "gptq4": 5, "awq4": 6}
+FORMATS = {"mxfp4": 1, "nvfp4": 2, "q4_k": 3, "q4_0": 4, "gptq4": 5, "awq4": 6, "nvfp4_cke": 8}
 _F32, _BF16, _F16 = 0, 1, 2
 _DTYPES = {torch.float32: _F32, torch.bfloat16: _BF16, torch.float16: _F16}
 
@@ -141,7 +141,8 @@ class QTensor:
     bytes [n][k/32] / [n][k/16] (NVFP4 also takes scale2); Q4_K data u8
     [n][k/256][144]; Q4_0 data u8 [n][k/32][18]; GPTQ4 data int32 [k/8][n],
     AWQ4 data int32 [k][n/8], both with fp16 scales and u8 logical zero points
-    [k/group][n].
+    [k/group][n]; NVFP4_CKE data u8 [n][k/64][36] split-half blocks (subscales
+    inside the blocks, no scales tensor) with scale2.
     """
     format: str
     n: int
@@ -408,10 +409,23 @@ def dequantize(w: QTensor, out: Optional[torch.Tensor] = None, dtype: torch.dtyp
 
 def repack(src: QTensor, dst_format: str, dst_group: Optional[int] = None, data: Optional[torch.Tensor] = None,
            scales: Optional[torch.Tensor] = None, zeros: Optional[torch.Tensor] = None) -> QTensor:
-    """Repack int4 codes between GPTQ4, AWQ4 and Q4_0 (bit-exact)."""
+    """Repack int4 codes between GPTQ4, AWQ4 and Q4_0, or NVFP4 codes between
+    the adjacent-pair and CKE split-half layouts (bit-exact)."""
     lib = _load()
     n, k, dev = src.n, src.k, src.device
     fmt = FORMATS[dst_format]
+    if dst_format in ("nvfp4", "nvfp4_cke"):
+        if data is None:
+            data = (torch.empty((n, k // 2), dtype=torch.uint8, device=dev) if dst_format == "nvfp4"
+                    else torch.empty((n, k // 64, 36), dtype=torch.uint8, device=dev))
+        if dst_format == "nvfp4" and scales is None:
+            scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+        if dst_format == "nvfp4_cke":
+            scales = None
+        ct = src._c()
+        _check(lib.qbn_repack(ctypes.byref(ct), fmt, 0, _ptr(data, "data"), _ptr(scales, "scales"), None,
+                              _stream(dev)), "qbn_repack")
+        return QTensor(dst_format, n, k, data, scales, scale2=src.scale2)
     if dst_group is None:
         dst_group = src.group if dst_format != "q4_0" else 0
     if data is None:

@@ -25,7 +25,8 @@ int32_t hip_status(hipError_t e) {
     return QBN_ERR_HIP;
 }
 
-bool known_format(int32_t f) { return f >= QBN_MXFP4 && f <= QBN_AWQ4; }
+// Weight formats a qbn_tensor may carry (QBN_MXFP8 is an activation format only).
+bool known_format(int32_t f) { return (f >= QBN_MXFP4 && f <= QBN_AWQ4) || f == QBN_NVFP4_CKE; }
 
 // Shape, group and pointer rules of a tensor; `need_buffers` is false only
 // when the tensor is empty.
@@ -41,6 +42,10 @@ int32_t check_tensor(const qbn_tensor *w) {
         break;
     case QBN_NVFP4:
         if (w->k % 16) return QBN_ERR_SHAPE;
+        if (!(isfinite(w->scale2) && w->scale2 > 0.0f)) return QBN_ERR_SCALE2;
+        break;
+    case QBN_NVFP4_CKE:
+        if (w->k % 64) return QBN_ERR_SHAPE;
         if (!(isfinite(w->scale2) && w->scale2 > 0.0f)) return QBN_ERR_SCALE2;
         break;
     case QBN_Q4_K:
@@ -70,6 +75,9 @@ int32_t check_tensor(const qbn_tensor *w) {
         break;
     case QBN_Q4_0:
         if (!aligned(w->data, 2)) return QBN_ERR_ALIGN;
+        break;
+    case QBN_NVFP4_CKE:
+        if (!aligned(w->data, 4)) return QBN_ERR_ALIGN;
         break;
     case QBN_GPTQ4:
     case QBN_AWQ4:
@@ -123,6 +131,9 @@ int64_t qbn_bytes(int32_t format, int64_t n, int64_t k, int32_t group, int32_t p
     case QBN_Q4_0:
         if (k % 32) return -1;
         return part == 0 ? n * (k / 32) * 18 : 0;
+    case QBN_NVFP4_CKE:
+        if (k % 64) return -1;
+        return part == 0 ? n * (k / 64) * 36 : 0;
     case QBN_GPTQ4:
     case QBN_AWQ4:
         if (group <= 0 || group % 8 || k % 8 || k % group) return -1;
@@ -146,6 +157,7 @@ int32_t qbn_quantized_gemv(const qbn_tensor *w, const void *x, int32_t x_dtype, 
     if (!x) return QBN_ERR_NULL;
     if (!aligned(x, 16)) return QBN_ERR_ALIGN;
     const bool int4 = w->format == QBN_Q4_0 || w->format == QBN_GPTQ4 || w->format == QBN_AWQ4;
+    if (w->format == QBN_NVFP4_CKE) return hip_status(qbn::launch_gemv_cke(*w, x, x_dtype, (float *)y, s));
     return hip_status(int4 ? qbn::launch_gemv_int4(*w, x, x_dtype, (float *)y, s)
                            : qbn::launch_gemv(*w, x, x_dtype, (float *)y, s));
 }
@@ -254,6 +266,8 @@ int32_t qbn_dequantize(const qbn_tensor *w, void *out, int32_t out_dtype, int32_
     if (w->n == 0 || w->k == 0) return QBN_OK;
     if (!out) return QBN_ERR_NULL;
     if (!aligned(out, 16)) return QBN_ERR_ALIGN;
+    if (w->format == QBN_NVFP4_CKE)
+        return hip_status(qbn::launch_dequant_cke(*w, out, out_dtype, out_layout, (hipStream_t)stream));
     return hip_status(qbn::launch_dequant(*w, out, out_dtype, out_layout, (hipStream_t)stream));
 }
 
@@ -348,6 +362,17 @@ int32_t qbn_repack(const qbn_tensor *src, int32_t dst_format, int32_t dst_group,
     int32_t st = check_tensor(src);
     if (st) return st;
     if (!known_format(dst_format)) return QBN_ERR_FORMAT;
+    // NVFP4 <-> CKE split-half blocks: the codes and subscale bytes move, scale2 is unchanged
+    const bool nv_src = src->format == QBN_NVFP4 || src->format == QBN_NVFP4_CKE;
+    const bool nv_dst = dst_format == QBN_NVFP4 || dst_format == QBN_NVFP4_CKE;
+    if (nv_src || nv_dst) {
+        if (!nv_src || !nv_dst || src->format == dst_format) return QBN_ERR_UNSUPPORTED;
+        if (src->k % 64) return QBN_ERR_SHAPE;
+        if (src->n == 0 || src->k == 0) return QBN_OK;
+        if (!dst_data || (dst_format == QBN_NVFP4 && !dst_scales)) return QBN_ERR_NULL;
+        if (!aligned(dst_data, dst_format == QBN_NVFP4 ? 16 : 4)) return QBN_ERR_ALIGN;
+        return hip_status(qbn::launch_repack_cke(*src, dst_data, dst_scales, (hipStream_t)stream));
+    }
     const bool src_int4 = src->format == QBN_GPTQ4 || src->format == QBN_AWQ4 || src->format == QBN_Q4_0;
     const bool dst_int4 = dst_format == QBN_GPTQ4 || dst_format == QBN_AWQ4 || dst_format == QBN_Q4_0;
     if (!src_int4 || !dst_int4 || src->format == dst_format) return QBN_ERR_UNSUPPORTED;

@@ -10,6 +10,9 @@
 namespace qbn {
 
 hipError_t launch_gemv(const qbn_tensor &w, const void *x, int x_dtype, float *y, hipStream_t s);
+hipError_t launch_gemv_cke(const qbn_tensor &w, const void *x, int x_dtype, float *y, hipStream_t s);
+hipError_t launch_dequant_cke(const qbn_tensor &w, void *out, int out_dtype, int out_layout, hipStream_t s);
+hipError_t launch_repack_cke(const qbn_tensor &src, void *dst_data, void *dst_scales, hipStream_t s);
 hipError_t launch_gemv_int4(const qbn_tensor &w, const void *x, int x_dtype, float *y, hipStream_t s);
 hipError_t launch_gptq_qzeros(const void *src, void *dst, int64_t groups, int64_t n, int version, int to_logical,
                               hipStream_t s);

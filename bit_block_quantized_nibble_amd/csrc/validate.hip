@@ -38,6 +38,17 @@ __global__ __launch_bounds__(kBlock) void k_scan_bytes(const uint8_t *__restrict
     }
 }
 
+// CKE split-half NVFP4 blocks: subscale i (logical order, row-major over
+// [n][k/16]) is byte i % 4 of block i / 4; E4M3FN NaN is 0x7F / 0xFF.
+__global__ __launch_bounds__(kBlock) void k_scan_cke(const uint8_t *__restrict__ blocks, int64_t count,
+                                                      unsigned long long *first) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        const uint32_t b = blocks[36 * (i / 4) + (i % 4)];
+        if ((b & 0x7Fu) == 0x7Fu) atomicMin(first, (unsigned long long)i);
+    }
+}
+
 // Q4_K blocks: d or dmin not finite.
 __global__ __launch_bounds__(kBlock) void k_scan_q4k(const uint8_t *__restrict__ blocks, int64_t nblocks,
                                                       unsigned long long *first) {
@@ -130,6 +141,12 @@ hipError_t launch_validate(const qbn_tensor &w, int64_t *first_bad, hipStream_t 
         if (count > 0)
             hipLaunchKernelGGL(k_scan_bytes<1>, dim3((unsigned)scan_grid(count)), dim3(kBlock), 0, s,
                                (const uint8_t *)w.scales, count, f);
+        break;
+    case QBN_NVFP4_CKE:
+        count = n * (k / 16);
+        if (count > 0)
+            hipLaunchKernelGGL(k_scan_cke, dim3((unsigned)scan_grid(count)), dim3(kBlock), 0, s,
+                               (const uint8_t *)w.data, count, f);
         break;
     case QBN_Q4_K:
         count = n * (k / 256);

@@ -54,9 +54,17 @@
  *  QBN_AWQ4  [BP]: data int32 [k][n/8], packed along n, the word's slots hold
  *            columns 0,2,4,6,1,3,5,7 of its group of eight; scales and zeros
  *            as GPTQ4. n % 8 == 0, k % group == 0.
+ *  QBN_NVFP4_CKE [WK] section 5 (CKE's NVFP4 storage block): data = [n][k/64]
+ *            blocks of 36 bytes, 64 consecutive weights of a row each: bytes
+ *            0..3 are the E4M3FN subscales of the block's four 16-weight
+ *            subblocks, bytes 4+8j .. 4+8j+7 the codes of subblock j, whose
+ *            byte i holds weight i (low nibble) and weight i+8 (high nibble):
+ *            split-half order, not NVFP4's adjacent pairs. scales = NULL
+ *            (ignored); scale2 as NVFP4; the same dequantized value
+ *            (e2m1 * e4m3fn) * scale2. 4.5 bits per weight. k % 64 == 0.
  *
  * Alignment: MXFP4 / NVFP4 / Q4_K data 16-byte aligned; Q4_0 data 2-byte;
- * GPTQ4 / AWQ4 data 4-byte; fp16 scales 2-byte; GEMV x 16-byte and y 4-byte;
+ * GPTQ4 / AWQ4 / NVFP4_CKE data 4-byte; fp16 scales 2-byte; GEMV x 16-byte and y 4-byte;
  * GEMM X 16-byte and Y 2-byte; dequantize outputs 16-byte. Scale bytes of MXFP4 / NVFP4
  * and zero points have no alignment requirement. A violation returns
  * QBN_ERR_ALIGN.
@@ -101,7 +109,8 @@ typedef enum qbn_format {
     QBN_Q4_0 = 4,
     QBN_GPTQ4 = 5,
     QBN_AWQ4 = 6,
-    QBN_MXFP8 = 7 /* activations only (qbn_quantize_mx, qbn_quantized_gemm_mx): E4M3FN elements, one E8M0 scale per 32 */
+    QBN_MXFP8 = 7, /* activations only (qbn_quantize_mx, qbn_quantized_gemm_mx): E4M3FN elements, one E8M0 scale per 32 */
+    QBN_NVFP4_CKE = 8 /* NVFP4 in 36-byte split-half blocks of 64 weights (layout above) */
 } qbn_format;
 
 typedef enum qbn_dtype {
@@ -139,13 +148,13 @@ QBN_API int32_t qbn_last_hip_error(void);
  * part or shape, 0 for a part the format does not have. The per-weight
  * storage cost follows [FB] sections 3-5 and [NV] section 7.1:
  * MXFP4 17 bytes per 32 weights, NVFP4 9 per 16 (+4 per tensor for scale2,
- * not counted here), Q4_K 144 per 256, Q4_0 18 per 32. */
+ * not counted here), NVFP4_CKE 36 per 64, Q4_K 144 per 256, Q4_0 18 per 32. */
 QBN_API int64_t qbn_bytes(int32_t format, int64_t n, int64_t k, int32_t group, int32_t part);
 
 /* y[r] = sum_i W_hat[r][i] * x[i] for r in 0..n  (decode GEMV, batch 1).
  * Fused: W_hat is decoded in registers and never written to memory
  * ([WK] sections 1, 7 and 7d; [FB] section 8).
- * Formats: MXFP4, NVFP4, Q4_K, and the integer int4 layouts ([BP] "Real
+ * Formats: MXFP4, NVFP4 (either layout), Q4_K, and the integer int4 layouts ([BP] "Real
  * layouts compared"): Q4_0 (rows of 18-byte blocks, w = d * (q - 8)),
  * GPTQ4 and AWQ4 (the k x n logical matrix packed along k or along n,
  * w = s[k/group][r] * (q - z[k/group][r]), z the logical zero point).
@@ -242,7 +251,7 @@ QBN_API int32_t qbn_quantized_gemm_mx(const qbn_tensor *w, int64_t m, int32_t x_
  * out_dtype QBN_F32: the exact binary32 value of each format's rule
  * (NVFP4 rounded once after the multiply by scale2, Q4_K rounded once
  * after the subtraction); QBN_BF16: that binary32 value rounded to bf16,
- * nearest even. All six formats. Bit-exact with the definitions, including
+ * nearest even. Every weight format. Bit-exact with the definitions, including
  * negative zero; a scale byte that qbn_validate rejects decodes to NaN. */
 QBN_API int32_t qbn_dequantize(const qbn_tensor *w, void *out, int32_t out_dtype, int32_t out_layout, void *stream);
 
@@ -319,7 +328,14 @@ QBN_API int32_t qbn_unpack_bits(const void *words_lo, const void *words_hi, int6
 
 /* Bit-exact repack of the int4 codes through the logical matrix
  * ([BP] "Repacking between formats"): src and destination share n and k.
- * Directions: GPTQ4 <-> AWQ4, GPTQ4 <-> Q4_0, AWQ4 <-> Q4_0.
+ * Directions: GPTQ4 <-> AWQ4, GPTQ4 <-> Q4_0, AWQ4 <-> Q4_0, and
+ * NVFP4 <-> NVFP4_CKE ([WK] section 5: split-half versus adjacent-pair
+ * order of the same codes).
+ *  - NVFP4 <-> NVFP4_CKE: k % 64 == 0. To CKE, dst_data receives the 36-byte
+ *    blocks (4-byte aligned); to NVFP4, dst_data the codes [n][k/2] (16-byte
+ *    aligned) and dst_scales the E4M3FN bytes [n][k/16]. scale2 is not
+ *    stored by either layout and stays the caller's. dst_group and
+ *    dst_zeros are ignored.
  *  - GPTQ4 <-> AWQ4: dst_data receives the qweight; scales and zeros keep
  *    their [k/group][n] layout and are copied to dst_scales / dst_zeros when
  *    those are non-NULL. dst_group must equal src->group.
@@ -341,6 +357,8 @@ QBN_API int32_t qbn_repack(const qbn_tensor *src, int32_t dst_format, int32_t ds
  *  MXFP4: scale byte 0xFF (E8M0 NaN), index into scales;
  *  NVFP4: scale byte 0x7F or 0xFF (E4M3FN NaN), index into scales
  *         (scale2 itself is checked on the host, QBN_ERR_SCALE2);
+ *  NVFP4_CKE: the same test on the subscales, index in [n][k/16] order
+ *         (subscale j of block b of row r is r * (k/16) + 4b + j);
  *  Q4_K:  d or dmin not finite, index = block;
  *  Q4_0:  d not finite, or (group > 0) a block whose d differs from the
  *         first block of its group of group/32 blocks, index = block;

@@ -14,6 +14,7 @@ import bit_block_quantized_nibble_amd as qbn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, NULL, FORMAT, UNSUP, SHAPE, ALIGN, SCALE2, NANS, DTYPE, HIP, GROUP = range(11)
 MX, NV, QK, Q0, GP, AW = 1, 2, 3, 4, 5, 6
+CKE = 8
 F32, BF16 = 0, 1
 A = 0x10000  # an aligned fake address
 B = 0x20000
@@ -69,6 +70,10 @@ def test_bytes_match_page_bit_budgets(lib):
     assert lib.qbn_bytes(7, 1, 32, 0, 0) == -1
     assert lib.qbn_bytes(MX, 1, 32, 0, 3) == -1
     assert lib.qbn_bytes(QK, 1, 256, 0, 1) == 0
+    # Why 4-Bit Quantization Is King, section 5: 36 bytes per 64 weights
+    cke = lib.qbn_bytes(CKE, n, k, 0, 0)
+    assert cke * 8 / (n * k) == 4.5 and lib.qbn_bytes(CKE, 1, 64, 0, 0) == 36
+    assert lib.qbn_bytes(CKE, 1, 64, 0, 1) == 0 and lib.qbn_bytes(CKE, 1, 96, 0, 0) == -1
 
 
 def test_gemv_rejections(lib):
@@ -297,3 +302,32 @@ def test_encode_rejections(lib):
     assert u(A, None, 64, 0, 0, B, None) == FORMAT
     assert u(A, None, 64, 6, 2, B, None) == NULL
     assert u(A + 1, None, 64, 5, 0, B, None) == ALIGN
+
+
+def test_cke_rejections(lib):
+    g = lib.qbn_quantized_gemv
+    assert g(T(CKE, 4, 96, scale2=0.01), A, F32, B, F32, None) == SHAPE
+    assert g(T(CKE, 4, 64, scale2=0.0), A, F32, B, F32, None) == SCALE2
+    assert g(T(CKE, 4, 64, scale2=float("inf")), A, F32, B, F32, None) == SCALE2
+    assert g(T(CKE, 4, 64, data=A + 2, scale2=0.01), A, F32, B, F32, None) == ALIGN
+    assert g(T(CKE, 4, 64, data=None, scale2=0.01), A, F32, B, F32, None) == NULL
+    assert g(T(CKE, 4, 64, scale2=0.01), A, F32, B, BF16, None) == DTYPE
+    assert g(T(CKE, 0, 64, scale2=0.01), A, F32, B, F32, None) == OK
+    # scales are ignored by this format: NULL is accepted (and A + 4 is aligned)
+    assert g(T(CKE, 0, 64, data=A + 4, scales=None, scale2=0.01), A, F32, B, F32, None) == OK
+    assert lib.qbn_quantized_gemm(T(CKE, 8, 64, scale2=0.01), 4, A, BF16, 64, B, BF16, 8, None) == UNSUP
+    assert lib.qbn_quantized_gemv_q8(T(CKE, 8, 256, scale2=0.01), A, B, C, B, F32, None) == UNSUP
+    assert lib.qbn_dequantize(T(CKE, 4, 96, scale2=0.01), B, F32, 0, None) == SHAPE
+    assert lib.qbn_dequantize(T(CKE, 4, 64, scale2=0.01), B + 8, F32, 0, None) == ALIGN
+    r = lib.qbn_repack
+    assert r(T(CKE, 4, 64, scale2=0.01), GP, 128, B, None, None, None) == UNSUP
+    assert r(T(GP, 4, 64, group=64), CKE, 0, B, None, None, None) == UNSUP
+    assert r(T(NV, 4, 64, scale2=0.01), NV, 0, B, C, None, None) == UNSUP
+    assert r(T(NV, 4, 32, scale2=0.01), CKE, 0, B, None, None, None) == SHAPE
+    assert r(T(NV, 4, 64, scale2=0.01), CKE, 0, B + 2, None, None, None) == ALIGN
+    assert r(T(NV, 4, 64, scale2=0.01), CKE, 0, None, None, None, None) == NULL
+    assert r(T(CKE, 4, 64, scale2=0.01), NV, 0, B + 4, C, None, None) == ALIGN
+    assert r(T(CKE, 4, 64, scale2=0.01), NV, 0, B, None, None, None) == NULL
+    assert r(T(CKE, 0, 64, scale2=0.01), NV, 0, None, None, None, None) == OK
+    assert lib.qbn_validate(T(CKE, 4, 96, scale2=0.01), B, None) == SHAPE
+    assert lib.qbn_validate(T(CKE, 4, 64, scale2=0.01), None, None) == NULL

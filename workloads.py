@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the seven workloads (host numpy arrays).
+"""Seeded synthetic inputs for the eight workloads (host numpy arrays).
 
 This module holds no decoding, dot-product or repacking arithmetic: it only
 draws random bytes and numbers with the distributions below and lays them
@@ -38,6 +38,10 @@ Workloads (n = output rows, k = reduction length):
      ~ U[1e-3,1e-2] [K/128][N]; zero points U{0..15} u8 [K/128][N]; Q4_0
      blocks [N][K/32][18] with fp16 d ~ U[1e-3,1e-2] and 16 uniform code
      bytes; x f32 N(0,1) [K].
+  8  NVFP4 GEMV 4096 x 4096 in CKE's 36-byte split-half blocks: per block the
+     four subscale bytes U{0x18..0x50} (drawn for all blocks first, as
+     workload 2's scales), then 32 uniform code bytes; scale2 =
+     float32(0.01); x bf16 N(0,1) [k].
 """
 from __future__ import annotations
 
@@ -53,6 +57,7 @@ SHAPES = {
     5: dict(fmt="gptq4", K=4096, N=11008, group=128),
     6: dict(fmt="q4_k", n=14336, k=4096),
     7: dict(fmt="int4", K=4096, N=11008, group=128),
+    8: dict(fmt="nvfp4_cke", n=4096, k=4096),
 }
 
 
@@ -111,6 +116,14 @@ def int4_affine(rng, K: int, N: int, group: int):
     return qweight, scales, zeros
 
 
+def cke_blocks(rng, n: int, k: int):
+    """CKE NVFP4 blocks u8 [n][k/64][36]: bytes 0-3 subscales U{0x18..0x50},
+    bytes 4-35 uniform code bytes."""
+    sub = rng.integers(0x18, 0x51, size=(n, k // 64, 4)).astype(np.uint8)
+    codes = rng.integers(0, 256, size=(n, k // 64, 32), dtype=np.uint8)
+    return np.ascontiguousarray(np.concatenate([sub, codes], axis=2))
+
+
 def q4_0_blocks(rng, n: int, k: int):
     """Q4_0 blocks u8 [n][k/32][18]: fp16 d ~ U[1e-3, 1e-2] in bytes 0-1
     (little-endian), 16 uniform code bytes."""
@@ -131,7 +144,7 @@ def x_bf16(rng, k: int):
 
 def workload(c: int, seed: int | None = None, n: int | None = None, k: int | None = None,
              m: int | None = None) -> dict:
-    """Inputs of workload c (1..7). n / k / m override the shape (same
+    """Inputs of workload c (1..8). n / k / m override the shape (same
     distributions) so that tests can run the same recipe at small sizes."""
     seed = 1000 + c if seed is None else seed
     rng = _rng(seed)
@@ -177,4 +190,10 @@ def workload(c: int, seed: int | None = None, n: int | None = None, k: int | Non
         x = x_f32(rng, K)
         return dict(fmt="int4", K=K, N=N, group=g, gptq=gptq, awq=awq, scales=scales, zeros=zeros, q4_0=q4_0, x=x,
                     seed=seed)
-    raise ValueError("workload must be 1..7")
+    if c == 8:
+        n = n or sh["n"]
+        k = k or sh["k"]
+        blocks = cke_blocks(rng, n, k)
+        return dict(fmt="nvfp4_cke", n=n, k=k, data=blocks, scales=None, scale2=float(SCALE2_NVFP4),
+                    x=x_bf16(rng, k), seed=seed)
+    raise ValueError("workload must be 1..8")
