@@ -60,6 +60,11 @@ WORKLOADS = {
         cfg=2, kind="gemv", unit="GB/s",
         desc="NVFP4 decode GEMV 4096x4096: E2M1 codes, E4M3FN scale per 16, f32 scale2=0.01, x bf16, y f32, batch 1",
         bytes=4096 * 2048 + 4096 * 256 + 4 + 4096 * 2 + 4096 * 4),
+    "nvfp4_cke_gemv": dict(
+        cfg=8, kind="gemv", unit="GB/s",
+        desc="NVFP4 decode GEMV 4096x4096 in CKE's 36-byte split-half blocks of 64 (four E4M3FN subscales, "
+             "32 code bytes), f32 scale2=0.01, x bf16, y f32, batch 1",
+        bytes=4096 * 64 * 36 + 4 + 4096 * 2 + 4096 * 4),
     "mxfp4_gemv": dict(
         cfg=1, kind="gemv", unit="GB/s",
         desc="MXFP4 dequant-GEMV 256x1024: E2M1 codes, E8M0 scale per 32, x f32, y f32, batch 1",
@@ -381,7 +386,8 @@ def cpu_baseline(name, spec, inp, budget_s):
         return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
                     sample="full %dx%d GEMV, median of %d runs (%.2f s each)" % (N, K, len(reps), t))
     if spec["kind"] == "gemv":
-        fmt = {"mxfp4": oracle.MXFP4, "nvfp4": oracle.NVFP4, "q4_k": oracle.Q4_K}[inp["fmt"]]
+        fmt = {"mxfp4": oracle.MXFP4, "nvfp4": oracle.NVFP4, "q4_k": oracle.Q4_K,
+               "nvfp4_cke": oracle.NVFP4_CKE}[inp["fmt"]]
         n, k = inp["n"], inp["k"]
         rows = np.arange(n)
         while True:
