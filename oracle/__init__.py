@@ -387,6 +387,30 @@ def int4_gemv(fmt: str, data: np.ndarray, scale_bits: np.ndarray, zeros: np.ndar
     return gemv_kn(affine_dequant(q, sb, zeros, group), x, cols)
 
 
+def int4_gemm_entries(fmt: str, data: np.ndarray, scale_bits, zeros, group: int, X_bits: np.ndarray, ms, ns):
+    """(Y, S) in binary64 for entries (ms[i], ns[i]) of Y = X @ W_hat with X
+    bfloat16 bits [M][K] and an int4 K x N weight: "gptq4" / "awq4" (data as
+    for int4_gemv, w = s * (q - z)) or "q4_0" (blocks u8 [N][K/32][18],
+    w = d * (q - 8)). Entry (m, n) is the dot of row m of X with column n of
+    W_hat, the same sum as the GEMV of that row."""
+    X = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    K = X.shape[1]
+    ms = np.asarray(ms, dtype=np.int64)
+    ns = np.asarray(ns, dtype=np.int64)
+    if fmt == "q4_0":
+        return gemm_entries(Q4_0, data, None, 1.0, K, X, ms, ns)
+    q = gptq_unpack(data) if fmt == "gptq4" else awq_unpack(data)
+    sb = np.asarray(scale_bits)
+    sb = sb.view(np.uint16) if sb.dtype == np.float16 else sb
+    W = affine_dequant(q, sb, zeros, group)
+    y = np.zeros(ms.size, np.float64)
+    sa = np.zeros(ms.size, np.float64)
+    for m in np.unique(ms):
+        sel = np.nonzero(ms == m)[0]
+        y[sel], sa[sel] = gemv_kn(W, X[m], ns[sel])
+    return y, sa
+
+
 # ---------------------------------------------------------------- dequant and dots
 
 def _scales_or_null(scales):
