@@ -373,7 +373,8 @@ def quantized_gemm_mx(w: QTensor, xcodes: torch.Tensor, xscales: torch.Tensor, f
 
 
 def quantized_gemm(w: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = X @ W_hat^T, X bfloat16 [m][k] -> Y bfloat16 [m][n]."""
+    """Y = X @ W_hat^T, X bfloat16 [m][k] -> Y bfloat16 [m][n] (MXFP4, GPTQ4,
+    AWQ4, Q4_0; the int4 layouts also write a float32 y passed in)."""
     lib = _load()
     if x.dim() != 2:
         raise ValueError("x must be 2-D [m][k]")

@@ -240,21 +240,29 @@ int32_t qbn_quantized_gemm(const qbn_tensor *w, int64_t m, const void *x, int32_
                            int32_t y_dtype, int64_t ldy, void *stream) {
     int32_t st = check_tensor(w);
     if (st) return st;
-    if (w->format != QBN_MXFP4) return QBN_ERR_UNSUPPORTED;
+    const bool int4 = w->format == QBN_GPTQ4 || w->format == QBN_AWQ4 || w->format == QBN_Q4_0;
+    if (w->format != QBN_MXFP4 && !int4) return QBN_ERR_UNSUPPORTED;
     if (x_dtype < QBN_F32 || x_dtype > QBN_F16 || y_dtype < QBN_F32 || y_dtype > QBN_F16) return QBN_ERR_FORMAT;
-    if (x_dtype != QBN_BF16 || y_dtype != QBN_BF16) return QBN_ERR_DTYPE;
+    if (x_dtype != QBN_BF16 || (y_dtype != QBN_BF16 && !(int4 && y_dtype == QBN_F32))) return QBN_ERR_DTYPE;
+    if (int4 && w->format != QBN_Q4_0 && w->group % 32) return QBN_ERR_GROUP;  // scales per 32-k sub-block
+    if (int4 && w->k % 32) return QBN_ERR_SHAPE;
     if (m < 0 || m > kMaxElems) return QBN_ERR_SHAPE;
     if (m == 0 || w->n == 0) return QBN_OK;
     if (ldy < w->n) return QBN_ERR_SHAPE;
     if (ldy > kMaxElems / m) return QBN_ERR_SHAPE;
+    if (int4 && !qbn::gemm_int4_grid_fits(m, w->n)) return QBN_ERR_SHAPE;
     if (!y) return QBN_ERR_NULL;
-    if (!aligned(y, 2)) return QBN_ERR_ALIGN;
+    const int ysz = y_dtype == QBN_F32 ? 4 : 2;
+    if (!aligned(y, (uintptr_t)ysz)) return QBN_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    if (w->k == 0) return hip_status(qbn::launch_fill_zero_2d_u16(y, m, w->n, ldy, s));
+    if (w->k == 0)
+        return hip_status(ysz == 2 ? qbn::launch_fill_zero_2d_u16(y, m, w->n, ldy, s)
+                                   : qbn::launch_fill_zero_2d_u16(y, m, 2 * w->n, 2 * ldy, s));
     if (ldx < w->k || ldx % 8) return ldx < w->k ? QBN_ERR_SHAPE : QBN_ERR_ALIGN;
     if (ldx > kMaxElems / m) return QBN_ERR_SHAPE;
     if (!x) return QBN_ERR_NULL;
     if (!aligned(x, 16)) return QBN_ERR_ALIGN;
+    if (int4) return hip_status(qbn::launch_gemm_int4(*w, m, x, ldx, y, y_dtype, ldy, s));
     return hip_status(qbn::launch_gemm(*w, m, x, ldx, y, ldy, s));
 }
 

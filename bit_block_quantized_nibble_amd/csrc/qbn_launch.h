@@ -31,6 +31,9 @@ hipError_t launch_unpack_bits(const void *words_lo, const void *words_hi, int64_
                               void *values, hipStream_t s);
 hipError_t launch_gemm(const qbn_tensor &w, int64_t m, const void *x, int64_t ldx, void *y, int64_t ldy,
                        hipStream_t s);
+hipError_t launch_gemm_int4(const qbn_tensor &w, int64_t m, const void *x, int64_t ldx, void *y, int y_dtype,
+                            int64_t ldy, hipStream_t s);
+bool gemm_int4_grid_fits(int64_t m, int64_t n);
 hipError_t launch_dequant(const qbn_tensor &w, void *out, int out_dtype, int out_layout, hipStream_t s);
 hipError_t launch_repack(const qbn_tensor &src, int dst_format, int dst_group, void *dst_data, void *dst_scales,
                          void *dst_zeros, hipStream_t s);

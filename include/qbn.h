@@ -215,7 +215,16 @@ QBN_API int32_t qbn_quantized_gemv_q8(const qbn_tensor *w, const int8_t *q, cons
  * Formats: MXFP4. X: QBN_BF16 [m][ldx] row-major, ldx >= k, ldx % 8 == 0,
  * X 16-byte aligned; Y: QBN_BF16 [m][ldy], ldy >= n, Y 2-byte aligned. W_hat is expanded to bf16
  * exactly (E2M1 x 2^e is exact in bf16), products run on bf16 matrix cores
- * with binary32 accumulation, and Y is rounded to bf16 (nearest even). */
+ * with binary32 accumulation, and Y is rounded to bf16 (nearest even).
+ * Formats GPTQ4, AWQ4, Q4_0 ([BP] "Real layouts compared"; w = s(q - z),
+ * d(q - 8)): the same X; Y QBN_BF16 or QBN_F32 ([m][ldy], 2- or 4-byte
+ * aligned); k % 32 == 0 and, for GPTQ4 / AWQ4, group % 32 == 0
+ * (QBN_ERR_GROUP). The codes are expanded to bf16 (q - z), exact, summed
+ * against X on the bf16 matrix cores per 32-long sub-block of k, and each
+ * group's sum is multiplied by its binary32 scale and added in binary32,
+ * so every product is exact. Each Y entry satisfies
+ * |y - y_exact| <= 1e-5 * sum_j |X[i][j] W_hat[r][j]| + 1e-6 before the bf16
+ * rounding. */
 QBN_API int32_t qbn_quantized_gemm(const qbn_tensor *w, int64_t m, const void *x, int32_t x_dtype, int64_t ldx, void *y,
                            int32_t y_dtype, int64_t ldy, void *stream);
 

@@ -194,6 +194,15 @@ def test_gemm_rejections(lib):
     assert g(T(MX, 8, 64), 4, A, BF16, 64, B + 1, BF16, 12, None) == ALIGN
     assert g(T(MX, 8, 64), 4, A + 8, BF16, 64, B, BF16, 8, None) == ALIGN
     assert g(T(MX, 8, 64), 0, None, BF16, 64, None, BF16, 8, None) == OK
+    # int4 layouts: f32 output allowed, groups and k in units of 32
+    assert g(T(GP, 8, 64, group=8), 4, A, BF16, 64, B, BF16, 8, None) == GROUP
+    assert g(T(AW, 8, 96, group=48), 4, A, BF16, 96, B, BF16, 8, None) == GROUP
+    assert g(T(GP, 8, 64, group=64), 4, A, F32, 64, B, F32, 8, None) == DTYPE
+    assert g(T(GP, 8, 64, group=64), 4, A, BF16, 64, B + 2, F32, 8, None) == ALIGN
+    assert g(T(Q0, 8, 48), 4, A, BF16, 64, B, BF16, 8, None) == SHAPE
+    assert g(T(GP, 8, 64, group=32), 4, A, BF16, 60, B, F32, 8, None) == SHAPE
+    assert g(T(GP, 8, 64, group=32), 0, None, BF16, 64, None, F32, 8, None) == OK
+    assert g(T(CKE, 8, 64, scale2=0.01), 4, A, BF16, 64, B, BF16, 8, None) == UNSUP
 
 
 def test_dequant_rejections(lib):

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the eight workloads (host numpy arrays).
+"""Seeded synthetic inputs for the nine workloads (host numpy arrays).
 
 This module holds no decoding, dot-product or repacking arithmetic: it only
 draws random bytes and numbers with the distributions below and lays them
@@ -42,6 +42,10 @@ Workloads (n = output rows, k = reduction length):
      four subscale bytes U{0x18..0x50} (drawn for all blocks first, as
      workload 2's scales), then 32 uniform code bytes; scale2 =
      float32(0.01); x bf16 N(0,1) [k].
+  9  int4 prefill GEMM, K x N = 4096 x 11008, group 128, M = 2048: the
+     weights drawn exactly as workload 7 (GPTQ, AWQ, scales, zero points,
+     Q4_0 blocks, in that order, then workload 7's x, unused), then X bf16
+     N(0,1) [M][K].
 """
 from __future__ import annotations
 
@@ -58,6 +62,7 @@ SHAPES = {
     6: dict(fmt="q4_k", n=14336, k=4096),
     7: dict(fmt="int4", K=4096, N=11008, group=128),
     8: dict(fmt="nvfp4_cke", n=4096, k=4096),
+    9: dict(fmt="int4", K=4096, N=11008, group=128, M=2048),
 }
 
 
@@ -144,7 +149,7 @@ def x_bf16(rng, k: int):
 
 def workload(c: int, seed: int | None = None, n: int | None = None, k: int | None = None,
              m: int | None = None) -> dict:
-    """Inputs of workload c (1..8). n / k / m override the shape (same
+    """Inputs of workload c (1..9). n / k / m override the shape (same
     distributions) so that tests can run the same recipe at small sizes."""
     seed = 1000 + c if seed is None else seed
     rng = _rng(seed)
@@ -178,7 +183,7 @@ def workload(c: int, seed: int | None = None, n: int | None = None, k: int | Non
         g = sh["group"]
         qweight, scales, zeros = int4_affine(rng, K, N, g)
         return dict(fmt="gptq4", K=K, N=N, group=g, qweight=qweight, scales=scales, zeros=zeros, seed=seed)
-    if c == 7:
+    if c in (7, 9):
         K = k or sh["K"]
         N = n or sh["N"]
         g = sh["group"]
@@ -188,12 +193,17 @@ def workload(c: int, seed: int | None = None, n: int | None = None, k: int | Non
         zeros = rng.integers(0, 16, size=(K // g, N)).astype(np.uint8)
         q4_0 = q4_0_blocks(rng, N, K)
         x = x_f32(rng, K)
-        return dict(fmt="int4", K=K, N=N, group=g, gptq=gptq, awq=awq, scales=scales, zeros=zeros, q4_0=q4_0, x=x,
-                    seed=seed)
+        out = dict(fmt="int4", K=K, N=N, group=g, gptq=gptq, awq=awq, scales=scales, zeros=zeros, q4_0=q4_0, x=x,
+                   seed=seed)
+        if c == 9:
+            M = m or sh["M"]
+            out["M"] = M
+            out["X"] = bf16_bits_from_f32(rng.standard_normal((M, K)).astype(np.float32))
+        return out
     if c == 8:
         n = n or sh["n"]
         k = k or sh["k"]
         blocks = cke_blocks(rng, n, k)
         return dict(fmt="nvfp4_cke", n=n, k=k, data=blocks, scales=None, scale2=float(SCALE2_NVFP4),
                     x=x_bf16(rng, k), seed=seed)
-    raise ValueError("workload must be 1..8")
+    raise ValueError("workload must be 1..9")
