@@ -107,6 +107,21 @@ WORKLOADS = {
         cfg=4, kind="gemm", unit="TFLOP/s",
         desc="MXFP4 prefill GEMM: W 8192x8192 (E2M1, E8M0 per 32) x X bf16 2048x8192 -> Y bf16, fp32 accumulate",
         flops=2.0 * 2048 * 8192 * 8192, bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 * 2 * 2),
+    "gptq_gemm": dict(
+        cfg=9, kind="int4gemm", fmt="gptq4", unit="TFLOP/s", dtype="bf16",
+        desc="int4 prefill GEMM straight from GPTQ (int32 [K/8][N], fp16 scales, u8 zeros, group 128): "
+             "X bf16 2048x4096 x W 4096x11008 -> Y bf16, bf16 MFMA on (q - z), fp32 group rescale",
+        flops=2.0 * 2048 * 4096 * 11008, bytes=22544384 + 704512 + 352256 + 2048 * 4096 * 2 + 2048 * 11008 * 2),
+    "awq_gemm": dict(
+        cfg=9, kind="int4gemm", fmt="awq4", unit="TFLOP/s", dtype="bf16",
+        desc="int4 prefill GEMM straight from AWQ (int32 [K][N/8], fp16 scales, u8 zeros, group 128): "
+             "X bf16 2048x4096 x W 4096x11008 -> Y bf16, bf16 MFMA on (q - z), fp32 group rescale",
+        flops=2.0 * 2048 * 4096 * 11008, bytes=22544384 + 704512 + 352256 + 2048 * 4096 * 2 + 2048 * 11008 * 2),
+    "q4_0_gemm": dict(
+        cfg=9, kind="int4gemm", fmt="q4_0", unit="TFLOP/s", dtype="bf16",
+        desc="int4 prefill GEMM straight from GGUF Q4_0 (18-byte blocks of 32 along k): "
+             "X bf16 2048x4096 x W 4096x11008 -> Y bf16, bf16 MFMA on (q - 8), fp32 rescale per block",
+        flops=2.0 * 2048 * 4096 * 11008, bytes=25362432 + 2048 * 4096 * 2 + 2048 * 11008 * 2),
     "mxfp4_w4a4_gemm": dict(
         cfg=4, kind="mxgemm", unit="TFLOP/s", dtype="fp4",
         desc="MX-native W4A4 GEMM: OCP MX quantization of X bf16 2048x8192 to MXFP4 + W 8192x8192 MXFP4 on the "
@@ -230,6 +245,23 @@ def build_steps(name, spec, dev):
         for W in srcs:
             calls.append(qbn.prepare_quantize_nvfp4(W, inp["scale2"], 0, codes, scales))
         return calls, R, dict(inp, W=Wb), None
+    if spec["kind"] == "int4gemm":
+        K, N, g, M = inp["K"], inp["N"], inp["group"], inp["M"]
+        fmt = spec["fmt"]
+        R = 2  # compute-bound: two weight copies suffice
+        X = host_to_device(inp["X"], dev).view(torch.bfloat16)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        if fmt == "q4_0":
+            d0, s0, z0 = host_to_device(inp["q4_0"], dev), None, None
+        else:
+            d0 = host_to_device(inp["gptq"] if fmt == "gptq4" else inp["awq"], dev)
+            s0 = host_to_device(inp["scales"].view(np.uint16), dev)
+            z0 = host_to_device(inp["zeros"], dev)
+        for _ in range(R):
+            w = qbn.QTensor(fmt, N, K, d0.clone(), None if s0 is None else s0.clone(),
+                            None if z0 is None else z0.clone(), group=g)
+            calls.append(qbn.prepare_gemm(w, X, Y))
+        return calls, R, inp, None
     if spec["kind"] == "int4gemv":
         K, N, g = inp["K"], inp["N"], inp["group"]
         fmt = spec["fmt"]
@@ -415,6 +447,23 @@ def cpu_baseline(name, spec, inp, budget_s):
         return dict(value=2.0 * k * done / t / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
                     sample="%d sampled output entries (one quantized X row each 16 entries, 2k flops per entry), %.1f s"
                     % (done, t))
+    if spec["kind"] == "int4gemm":
+        K, N, g, M = inp["K"], inp["N"], inp["group"], inp["M"]
+        fmt = spec["fmt"]
+        data = inp["q4_0"] if fmt == "q4_0" else (inp["gptq"] if fmt == "gptq4" else inp["awq"])
+        rng = np.random.default_rng(0)
+        done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            nn = rng.integers(0, N, 8)
+            ms_ = np.repeat(np.arange(M), nn.size)
+            ns_ = np.tile(nn, M)
+            oracle.int4_gemm_entries(fmt, data, inp["scales"], inp["zeros"], g, inp["X"], ms_, ns_)
+            done += ms_.size
+        t = time.perf_counter() - t0
+        return dict(value=2.0 * K * done / t / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                    sample="%d output entries (8 whole columns of the %dx%d output per oracle call, 2k flops each), "
+                    "%.1f s" % (done, M, N, t))
     if spec["kind"] == "gemm":
         n, k, m = inp["n"], inp["k"], inp["m"]
         rng = np.random.default_rng(0)
@@ -465,8 +514,9 @@ def main():
 
         __graft_entry__.build()
     spec = WORKLOADS[args.workload]
-    steps = args.steps or (50 if spec["kind"] == "gemm" else 200 if spec["kind"] == "mxgemm" else 2000)
-    warmup = args.warmup if args.warmup is not None else (500 if spec["kind"] in ("gemm", "mxgemm") else 200)
+    steps = args.steps or (50 if spec["kind"] in ("gemm", "int4gemm") else 200 if spec["kind"] == "mxgemm" else 2000)
+    warmup = args.warmup if args.warmup is not None else (500 if spec["kind"] in ("gemm", "mxgemm", "int4gemm")
+                                                          else 200)
     dev = torch.device("cuda:0")
     calls, R, inp, kcalls = build_steps(args.workload, spec, dev)
     torch.cuda.synchronize()
@@ -563,14 +613,15 @@ def main():
     copy_gbs = 2 * half / (a.elapsed_time(b) / csteps * 1e-3) / 1e9
     del cg, bufs
 
-    if spec["kind"] in ("gemm", "mxgemm"):
-        peak = BF16_MFMA_PEAK_TFLOPS if spec["kind"] == "gemm" else (
+    if spec["kind"] in ("gemm", "mxgemm", "int4gemm"):
+        peak = BF16_MFMA_PEAK_TFLOPS if spec["kind"] in ("gemm", "int4gemm") else (
             FP8_MFMA_PEAK_TFLOPS if spec.get("xfmt") == "mxfp8" else FP4_MFMA_PEAK_TFLOPS)
         value = spec["flops"] / (ms_step * 1e-3) / 1e12
         achieved = spec["flops"] / (kernel_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
                     frac=round(achieved / peak, 4), traffic=recorded_traffic(args.workload))
-        metric = "FP8 x FP4 GEMM TFLOP/s (% MFMA peak)" if spec.get("xfmt") == "mxfp8" else "FP4 GEMM TFLOP/s (% MFMA peak)"
+        metric = "FP8 x FP4 GEMM TFLOP/s (% MFMA peak)" if spec.get("xfmt") == "mxfp8" else (
+            "int4 GEMM TFLOP/s (% MFMA peak)" if spec["kind"] == "int4gemm" else "FP4 GEMM TFLOP/s (% MFMA peak)")
     else:
         value = spec["bytes"] / (ms_step * 1e-3) / 1e9
         achieved = spec.get("kernel_bytes", spec["bytes"]) / (kernel_ms * 1e-3) / 1e9

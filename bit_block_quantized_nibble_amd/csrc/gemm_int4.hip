@@ -35,10 +35,10 @@ constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kThreads = 256;
 constexpr int LDK = BK + 8;  // LDS row pitch in bf16 (16 bytes of padding against bank conflicts)
 
-struct Smem {
-    uint16_t a[2][BM * LDK];  // X tile, [m][k]
-    uint16_t b[2][BN * LDK];  // decoded codes (q - z) as bf16, [n][k]
-    float s[2][2][BN];        // scale of each column for the tile's two 32-k sub-blocks
+struct alignas(16) Smem {
+    alignas(16) uint16_t a[2][BM * LDK];  // X tile, [m][k]
+    alignas(16) uint16_t b[2][BN * LDK];  // decoded codes (q - z) as bf16, [n][k]
+    alignas(16) float s[2][2][BN];        // scale of each column for the tile's two 32-k sub-blocks
 };
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
@@ -76,8 +76,13 @@ struct __attribute__((packed, aligned(2))) Q40B {
 // ------------------------------------------------------------------ stage
 // X: thread t loads rows t/8 + 32i (i < 4), 16 bytes at k chunk t % 8.
 // Codes (per format):
-//   GPTQ4: word row r = t/32 (k = 8r .. 8r+7 of the tile), 4 columns 4(t%32) .. +3;
-//   AWQ4:  k rows 4(t/16) .. +3, word column t % 16 (columns 8(t%16) .. +7);
+//   GPTQ4: word row r = t%8 (k = 8r .. 8r+7 of the tile), 4 columns 4(t/8) .. +3
+//          (lanes step along the word rows first: the 16-byte LDS stores of
+//          a wave then cover all 16 bank slots);
+//   AWQ4:  k rows 4(t%16) .. +3, word column t / 16 (columns 8(t/16) .. +7):
+//          consecutive lanes step along k, so the 8-byte LDS stores of a wave
+//          fill 256 distinct bytes (with lanes stepping along n instead, the
+//          1152-byte column stride folded them onto two bank offsets);
 //   Q4_0:  block t % 2 (k = 32(t%2) .. +31) of column t / 2.
 // Scales for LDS: GPTQ4 / AWQ4 thread t writes column t % 128 of sub-block
 // t / 128; Q4_0 its own block's d.
@@ -101,8 +106,23 @@ struct Args {
     int64_t M, N, K;
 };
 
-template <int FMT>
-__device__ __forceinline__ void stage_load(Stage<FMT> &st, const Args &p, int64_t m0, int64_t n0, int64_t k0) {
+// Group of element k0 + off (0 <= off < 64) of a k-tile whose first element
+// lies in group g0 at offset rem0 (a multiple of 32, at most group - 32): the
+// tile crosses at most two group boundaries, so two compares replace a
+// division.
+__device__ __forceinline__ int64_t group_of(int64_t g0, int64_t rem0, int64_t group, int off) {
+    const int64_t r = rem0 + off;
+    return g0 + (r >= group ? 1 : 0) + (r >= 2 * group ? 1 : 0);
+}
+
+// Every load below reads a valid address: an index outside the operand is
+// replaced by 0 and the loaded value by 0 (selects, not branches).
+// VEC (n % 8 == 0, 16-byte aligned codes, 8-byte aligned zero points): GPTQ
+// reads its four words in one 16-byte load and its four zero points in one
+// dword; AWQ its eight zero points in one 8-byte load.
+template <int FMT, bool VEC>
+__device__ __forceinline__ void stage_load(Stage<FMT> &st, const Args &p, int64_t m0, int64_t n0, int64_t k0,
+                                           int64_t g0, int64_t rem0) {
     const int t = threadIdx.x;
     {
         const int c16 = t % 8;
@@ -110,59 +130,83 @@ __device__ __forceinline__ void stage_load(Stage<FMT> &st, const Args &p, int64_
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t m = m0 + t / 8 + 32 * i;
-            st.a[i] = (m < p.M && k < p.K) ? ld16(p.X + m * p.ldx + k) : u32x4{0u, 0u, 0u, 0u};
+            const bool ok = m < p.M && k < p.K;
+            const u32x4 v = ld16(p.X + (ok ? m * p.ldx + k : 0));
+            st.a[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
         }
     }
     if (FMT == QBN_GPTQ4) {
-        const int r = t / 32;
+        const int r = t % 8;
         const int64_t kk = k0 + 8 * r;
-        const int64_t n = n0 + 4 * (t % 32);
+        const int64_t n = n0 + 4 * (t / 8);
         const bool kok = kk < p.K;
-        const int64_t g = (kok ? kk : 0) / p.group;
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(p.data) + (kk / 8) * p.N + n;
-        uint32_t zz = 0;
+        const int64_t g = kok ? group_of(g0, rem0, p.group, 8 * r) : 0;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(p.data);
+        if (VEC) {  // n % 4 == 0 here, so the four columns are all in or all out
+            const bool ok = kok && n < p.N;
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(src + (ok ? (kk / 8) * p.N + n : 0));
+            const uint32_t z = *reinterpret_cast<const uint32_t *>(p.zeros + (ok ? g * p.N + n : 0));
+            st.w[0] = ok ? w.x : 0u;
+            st.w[1] = ok ? w.y : 0u;
+            st.w[2] = ok ? w.z : 0u;
+            st.w[3] = ok ? w.w : 0u;
+            st.zb[0] = ok ? z : 0u;
+        } else {
+            uint32_t zz = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = kok && (n + i < p.N);
-            st.w[i] = ok ? src[i] : 0u;
-            zz |= (ok ? (uint32_t)p.zeros[g * p.N + n + i] : 0u) << (8 * i);
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = kok && (n + i < p.N);
+                const uint32_t w = src[ok ? (kk / 8) * p.N + n + i : 0];
+                const uint32_t z = p.zeros[ok ? g * p.N + n + i : 0];
+                st.w[i] = ok ? w : 0u;
+                zz |= (ok ? z : 0u) << (8 * i);
+            }
+            st.zb[0] = zz;
         }
-        st.zb[0] = zz;
     } else if (FMT == QBN_AWQ4) {
-        const int h = t / 16, c = t % 16;
+        const int h = t % 16, c = t / 16;
         const int64_t n = n0 + 8 * c;
         const int64_t kk = k0 + 4 * h;
         const bool nok = n < p.N;
-        const int64_t g = (kk < p.K ? kk : 0) / p.group;
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(p.data) + kk * (p.N / 8) + n / 8;
+        const int64_t g = kk < p.K ? group_of(g0, rem0, p.group, 4 * h) : 0;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(p.data);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st.w[i] = (nok && kk + i < p.K) ? src[i * (p.N / 8)] : 0u;
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = nok && kk + i < p.K;
+            const uint32_t w = src[ok ? (kk + i) * (p.N / 8) + n / 8 : 0];
+            st.w[i] = ok ? w : 0u;
+        }
+        const uint8_t *zp = p.zeros + (nok ? g * p.N + n : 0);
         uint32_t z0 = 0, z1 = 0;
-        if (nok) {
-            const uint8_t *zp = p.zeros + g * p.N + n;
+        if (VEC) {
+            const u32x2 z = *reinterpret_cast<const u32x2 *>(zp);
+            z0 = z.x;
+            z1 = z.y;
+        } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 z0 |= (uint32_t)zp[j] << (8 * j);
                 z1 |= (uint32_t)zp[4 + j] << (8 * j);
             }
         }
-        st.zb[0] = z0;
-        st.zb[1] = z1;
+        st.zb[0] = nok ? z0 : 0u;
+        st.zb[1] = nok ? z1 : 0u;
     } else {  // Q4_0
         const int64_t n = n0 + t / 2;
         const int64_t b = k0 / 32 + (t % 2);
         const bool ok = n < p.N && 32 * b < p.K;
-        Q40B blk = {0, {0u, 0u, 0u, 0u}};
-        if (ok) blk = *reinterpret_cast<const Q40B *>(p.data + (n * (p.K / 32) + b) * 18);
+        const Q40B blk = *reinterpret_cast<const Q40B *>(p.data + (ok ? (n * (p.K / 32) + b) * 18 : 0));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st.w[i] = blk.c[i];
-        st.s = f16_to_f32(blk.d);
+        for (int i = 0; i < 4; ++i) st.w[i] = ok ? blk.c[i] : 0u;
+        st.s = ok ? f16_to_f32(blk.d) : 0.0f;
     }
     if (FMT != QBN_Q4_0) {
         const int sb = t / 128;
         const int64_t n = n0 + t % 128;
         const int64_t kk = k0 + 32 * sb;
-        st.s = (n < p.N && kk < p.K) ? f16_to_f32(p.scales[(kk / p.group) * p.N + n]) : 0.0f;
+        const bool ok = n < p.N && kk < p.K;
+        const float v = f16_to_f32(p.scales[ok ? group_of(g0, rem0, p.group, 32 * sb) * p.N + n : 0]);
+        st.s = ok ? v : 0.0f;
     }
 }
 
@@ -176,8 +220,8 @@ __device__ __forceinline__ void stage_store(const Stage<FMT> &st, Smem &sm, int 
             *reinterpret_cast<u32x4 *>(&sm.a[buf][(t / 8 + 32 * i) * LDK + 8 * c16]) = st.a[i];
     }
     if (FMT == QBN_GPTQ4) {
-        const int r = t / 32;
-        const int c = 4 * (t % 32);
+        const int r = t % 8;
+        const int c = 4 * (t / 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float z = (float)((st.zb[0] >> (8 * i)) & 0xFFu);
@@ -189,7 +233,7 @@ __device__ __forceinline__ void stage_store(const Stage<FMT> &st, Smem &sm, int 
         }
         sm.s[buf][t / 128][t % 128] = st.s;
     } else if (FMT == QBN_AWQ4) {
-        const int h = t / 16, c = t % 16;
+        const int h = t % 16, c = t / 16;
         // slot tt of a word holds column 0,2,4,6,1,3,5,7 [tt] of its eight
         float zs[8];
 #pragma unroll
@@ -197,41 +241,82 @@ __device__ __forceinline__ void stage_store(const Stage<FMT> &st, Smem &sm, int 
             constexpr int col[8] = {0, 2, 4, 6, 1, 3, 5, 7};
             zs[tt] = (float)((st.zb[col[tt] / 4] >> (8 * (col[tt] % 4))) & 0xFFu);
         }
-        float v[4][8];
+        // two rows at a time (fewer live registers): pr[tt] = bf16 pair of
+        // rows (2 ih, 2 ih + 1) of the slot-tt column
+        uint32_t pr[2][8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) nibbles_minus(st.w[i], zs, v[i]);  // v[i][slot]: k = 4h + i
+        for (int ih = 0; ih < 2; ++ih) {
+            float v0[8], v1[8];
+            nibbles_minus(st.w[2 * ih], zs, v0);  // v0[slot]: k = 4h + 2ih
+            nibbles_minus(st.w[2 * ih + 1], zs, v1);
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) pr[ih][tt] = bf16_pair(v0[tt], v1[tt]);
+        }
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
             constexpr int col[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-            *reinterpret_cast<u32x2 *>(&sm.b[buf][(8 * c + col[tt]) * LDK + 4 * h]) =
-                u32x2{bf16_pair(v[0][tt], v[1][tt]), bf16_pair(v[2][tt], v[3][tt])};
+            *reinterpret_cast<u32x2 *>(&sm.b[buf][(8 * c + col[tt]) * LDK + 4 * h]) = u32x2{pr[0][tt], pr[1][tt]};
         }
         sm.s[buf][t / 128][t % 128] = st.s;
     } else {
         // code dword d holds bytes 4d .. 4d+3: nibble 2j of it is element 4d + j,
         // nibble 2j + 1 element 16 + 4d + j
         const float z8[8] = {8.0f, 8.0f, 8.0f, 8.0f, 8.0f, 8.0f, 8.0f, 8.0f};
-        uint32_t lo[8], hi[8];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            float v[8];
-            nibbles_minus(st.w[d], z8, v);
-            lo[2 * d] = bf16_pair(v[0], v[2]);
-            lo[2 * d + 1] = bf16_pair(v[4], v[6]);
-            hi[2 * d] = bf16_pair(v[1], v[3]);
-            hi[2 * d + 1] = bf16_pair(v[5], v[7]);
-        }
         uint16_t *dst = &sm.b[buf][(t / 2) * LDK + 32 * (t % 2)];
-        *reinterpret_cast<u32x4 *>(dst) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-        *reinterpret_cast<u32x4 *>(dst + 8) = u32x4{lo[4], lo[5], lo[6], lo[7]};
-        *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<u32x4 *>(dst + 24) = u32x4{hi[4], hi[5], hi[6], hi[7]};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {  // code dwords 2 half, 2 half + 1: elements 8 half .. +7 and 16 + the same
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+                float v[8];
+                nibbles_minus(st.w[2 * half + dd], z8, v);
+                lo[2 * dd] = bf16_pair(v[0], v[2]);
+                lo[2 * dd + 1] = bf16_pair(v[4], v[6]);
+                hi[2 * dd] = bf16_pair(v[1], v[3]);
+                hi[2 * dd + 1] = bf16_pair(v[5], v[7]);
+            }
+            *reinterpret_cast<u32x4 *>(dst + 8 * half) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            *reinterpret_cast<u32x4 *>(dst + 16 + 8 * half) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        }
         sm.s[buf][t % 2][t / 2] = st.s;
     }
 }
 
-template <int FMT, bool YF32>
-__global__ __launch_bounds__(kThreads) void k_gemm_int4(Args p) {
+// One k-tile's MFMA work on buffer buf: step ks (0..3) covers k = 16 ks ..
+// 16 ks + 15 of the tile. FRESH starts the partial sums at zero (the
+// matrix core's accumulator input is the constant 0).
+template <bool FRESH>
+__device__ __forceinline__ void mfma_step(const Smem &sm, int buf, int ks, int arow, int brow, int kofs,
+                                          f32x16 (&part)[2][2]) {
+    const bf16x8 a0 = lds_frag(&sm.a[buf][(arow)*LDK + 16 * ks + kofs]);
+    const bf16x8 a1 = lds_frag(&sm.a[buf][(arow + 32) * LDK + 16 * ks + kofs]);
+    const bf16x8 b0 = lds_frag(&sm.b[buf][(brow)*LDK + 16 * ks + kofs]);
+    const bf16x8 b1 = lds_frag(&sm.b[buf][(brow + 32) * LDK + 16 * ks + kofs]);
+    const f32x16 zero = {};
+    part[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, FRESH ? zero : part[0][0], 0, 0, 0);
+    part[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, FRESH ? zero : part[0][1], 0, 0, 0);
+    part[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, FRESH ? zero : part[1][0], 0, 0, 0);
+    part[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, FRESH ? zero : part[1][1], 0, 0, 0);
+}
+
+// tot += s (column scale) * part.
+__device__ __forceinline__ void rescale(float s0, float s1, const f32x16 (&part)[2][2], f32x16 (&tot)[2][2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            tot[i][0][v] = __builtin_fmaf(s0, part[i][0][v], tot[i][0][v]);
+            tot[i][1][v] = __builtin_fmaf(s1, part[i][1][v], tot[i][1][v]);
+        }
+}
+
+// PER_GROUP (GPTQ4 / AWQ4 with group % 64 == 0): the partial sums run over a
+// whole group (group / 64 k-tiles) before one rescale. Otherwise (Q4_0,
+// groups of 32 or any odd multiple of 32) every 32-k sub-block is rescaled
+// with its own scale; within a group that scale is the same, so both forms
+// compute the same sum up to rounding.
+template <int FMT, bool YF32, bool PER_GROUP, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
     __shared__ Smem sm;
     const int64_t tiles_n = (p.N + BN - 1) / BN;
     const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM;
@@ -240,8 +325,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_int4(Args p) {
     const int wave = threadIdx.x / kWave;
     const int wm = wave / 2, wn = wave % 2;
     const int nk = (int)((p.K + BK - 1) / BK);
-    const int nsub = (int)(p.K / 32);                       // 32-k sub-blocks of k (k % 32 == 0)
-    const int spg = FMT == QBN_Q4_0 ? 1 : (int)(p.group / 32);  // sub-blocks per group
+    const int tpg = PER_GROUP ? (int)(p.group / BK) : 1;  // k-tiles per group
 
     f32x16 part[2][2], tot[2][2];
 #pragma unroll
@@ -252,47 +336,52 @@ __global__ __launch_bounds__(kThreads) void k_gemm_int4(Args p) {
             tot[i][j] = f32x16{};
         }
 
+    // group cursor of the next k-tile to load (uniform): its first element is
+    // element lrem of group lg
+    int64_t lg = 0, lrem = 0;
     Stage<FMT> st;
-    stage_load<FMT>(st, p, m0, n0, 0);
+    stage_load<FMT, VEC>(st, p, m0, n0, 0, lg, lrem);
     stage_store<FMT>(st, sm, 0);
     __syncthreads();
 
     const int arow = wm * 64 + (lane % 32);
     const int brow = wn * 64 + (lane % 32);
     const int kofs = 8 * (lane / 32);
+    const int scol = wn * 64 + (lane % 32);  // lane holds column lane % 32 of each MFMA tile
+    int tig = 0;                             // k-tile index inside its group
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) stage_load<FMT>(st, p, m0, n0, (int64_t)(kt + 1) * BK);
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-            for (int ks = 2 * sb; ks < 2 * sb + 2; ++ks) {
-                const bf16x8 a0 = lds_frag(&sm.a[buf][(arow)*LDK + 16 * ks + kofs]);
-                const bf16x8 a1 = lds_frag(&sm.a[buf][(arow + 32) * LDK + 16 * ks + kofs]);
-                const bf16x8 b0 = lds_frag(&sm.b[buf][(brow)*LDK + 16 * ks + kofs]);
-                const bf16x8 b1 = lds_frag(&sm.b[buf][(brow + 32) * LDK + 16 * ks + kofs]);
-                part[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, part[0][0], 0, 0, 0);
-                part[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, part[0][1], 0, 0, 0);
-                part[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, part[1][0], 0, 0, 0);
-                part[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, part[1][1], 0, 0, 0);
+        if (kt + 1 < nk) {
+            lrem += BK;
+            while (lrem >= p.group) {
+                lrem -= p.group;
+                ++lg;
             }
-            const int gsb = 2 * kt + sb;  // global sub-block index (uniform)
-            if ((gsb + 1) % spg == 0 || gsb + 1 >= nsub) {
-                // lane holds column n = lane % 32 of each MFMA tile
-                const float s0 = sm.s[buf][sb][wn * 64 + (lane % 32)];
-                const float s1 = sm.s[buf][sb][wn * 64 + 32 + (lane % 32)];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        tot[i][0][v] = __builtin_fmaf(s0, part[i][0][v], tot[i][0][v]);
-                        tot[i][1][v] = __builtin_fmaf(s1, part[i][1][v], tot[i][1][v]);
-                    }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) part[i][j] = f32x16{};
+            stage_load<FMT, VEC>(st, p, m0, n0, (int64_t)(kt + 1) * BK, lg, lrem);
+        }
+        if (PER_GROUP) {
+            if (tig == 0) {
+                mfma_step<true>(sm, buf, 0, arow, brow, kofs, part);
+            } else {
+                mfma_step<false>(sm, buf, 0, arow, brow, kofs, part);
             }
+            mfma_step<false>(sm, buf, 1, arow, brow, kofs, part);
+            mfma_step<false>(sm, buf, 2, arow, brow, kofs, part);
+            mfma_step<false>(sm, buf, 3, arow, brow, kofs, part);
+            if (++tig == tpg) {
+                tig = 0;
+                rescale(sm.s[buf][1][scol], sm.s[buf][1][scol + 32], part, tot);
+            }
+        } else {
+            mfma_step<true>(sm, buf, 0, arow, brow, kofs, part);
+            mfma_step<false>(sm, buf, 1, arow, brow, kofs, part);
+            rescale(sm.s[buf][0][scol], sm.s[buf][0][scol + 32], part, tot);
+            // keep the second sub-block's work below the rescale, so that one
+            // set of partial sums is live at a time (no spills)
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step<true>(sm, buf, 2, arow, brow, kofs, part);
+            mfma_step<false>(sm, buf, 3, arow, brow, kofs, part);
+            rescale(sm.s[buf][1][scol], sm.s[buf][1][scol + 32], part, tot);
         }
         if (kt + 1 < nk) stage_store<FMT>(st, sm, buf ^ 1);
         __syncthreads();
@@ -317,14 +406,26 @@ __global__ __launch_bounds__(kThreads) void k_gemm_int4(Args p) {
         }
 }
 
-template <int FMT>
-hipError_t run(const Args &a, bool yf32, hipStream_t s) {
+template <int FMT, bool PER_GROUP, bool VEC>
+hipError_t run3(const Args &a, bool yf32, hipStream_t s) {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (yf32)
-        hipLaunchKernelGGL((k_gemm_int4<FMT, true>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_gemm_int4<FMT, true, PER_GROUP, VEC>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((k_gemm_int4<FMT, false>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_gemm_int4<FMT, false, PER_GROUP, VEC>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
     return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t run(const Args &a, bool yf32, hipStream_t s) {
+    if constexpr (FMT == QBN_Q4_0) {
+        return run3<FMT, false, false>(a, yf32, s);
+    } else {
+        const bool vec = a.N % 8 == 0 && (uintptr_t)a.data % 16 == 0 && (uintptr_t)a.zeros % 8 == 0;
+        if (a.group % BK == 0)
+            return vec ? run3<FMT, true, true>(a, yf32, s) : run3<FMT, true, false>(a, yf32, s);
+        return vec ? run3<FMT, false, true>(a, yf32, s) : run3<FMT, false, false>(a, yf32, s);
+    }
 }
 
 }  // namespace

@@ -62,8 +62,11 @@ def _inputs(seed, M, N, K, g):
     return inp
 
 
+# n % 8 != 0 (70, 130) takes the element-load path for GPTQ; group 96 and 32
+# the per-32-k rescale; group a multiple of 64 the per-group rescale.
 SHAPES = [(1, 40, 96, 32), (37, 72, 128, 64), (130, 264, 256, 128), (256, 256, 1024, 128), (5, 136, 4096, 4096),
-          (129, 128, 160, 32), (64, 8, 2048, 256), (200, 520, 512, 512)]
+          (129, 128, 160, 32), (64, 8, 2048, 256), (200, 520, 512, 512), (33, 70, 128, 32), (20, 64, 192, 96),
+          (140, 130, 384, 128), (3, 96, 576, 96)]
 
 
 @pytest.mark.parametrize("fmt", ["gptq4", "awq4", "q4_0"])
@@ -83,6 +86,28 @@ def test_int4_gemm_all_entries(fmt, M, N, K, g, ydt):
     ms, ns = ms.ravel(), ns.ravel()
     y_ref, s_ref = _ref(fmt, inp, g, ms, ns)
     _check(Y, y_ref, s_ref, ms, ns, "%s %dx%dx%d g=%d %s" % (fmt, M, N, K, g, ydt))
+
+
+@pytest.mark.parametrize("fmt", ["gptq4", "awq4"])
+def test_int4_gemm_misaligned_codes_and_zeros(fmt):
+    """Codes and zero points at odd offsets: the element-load path."""
+    M, N, K, g = 40, 136, 256, 64
+    inp = _inputs(17, M, N, K, g)
+    data = inp["gptq"] if fmt == "gptq4" else inp["awq"]
+    dd = torch.zeros(data.size + 1, dtype=torch.int32, device=DEV)
+    dd[1:] = dev(data).flatten()
+    zd = torch.zeros(inp["zeros"].size + 1, dtype=torch.uint8, device=DEV)
+    zd[1:] = dev(inp["zeros"]).flatten()
+    w = qbn.QTensor(fmt, N, K, dd[1:], dev(inp["scales"].view(np.uint16)), zd[1:], group=g)
+    X = dev(inp["X"]).view(torch.bfloat16)
+    say("int4 gemm misaligned", fmt)
+    Y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    qbn.quantized_gemm(w, X, Y)
+    torch.cuda.synchronize()
+    ms, ns = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ms, ns = ms.ravel(), ns.ravel()
+    y_ref, s_ref = _ref(fmt, inp, g, ms, ns)
+    _check(Y, y_ref, s_ref, ms, ns, fmt + " misaligned")
 
 
 def test_int4_gemm_strided_activations_and_output():
