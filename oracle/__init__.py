@@ -2,7 +2,7 @@
 
 Plain, slow reference definitions of the MXFP4, NVFP4 (also in CKE's split-half
 blocks), Q4_K and Q4_0 decoders,
-of the GPTQ / AWQ / Q4_0 int4 layouts, of the dot products built on them, and
+of the GPTQ / AWQ / Q4_0 int4 layouts, of the dot products and GEMM entries built on them, and
 of the W4A8 route (int8 activation quantization, Q4_K x int8 dot) and of the
 integer-exact NVFP4 x Q8_K decode.
 The arithmetic lives in ``qbn_oracle.c`` (plain C, gcc -O2, no SIMD
