@@ -78,13 +78,14 @@ __device__ __forceinline__ void nib_minus(uint32_t v, const float (&z)[8], float
 // round's codes, activations, scales and zero points before multiplying,
 // and keeps 8 column sums. (Holding a second round in registers to overlap
 // the next requests with the arithmetic measured no faster.) GPTQ: CW = 4 (a lane's 8 columns
-// are 32 contiguous bytes, 4 lanes a 128-byte line per step), 256 threads.
-// AWQ: CW = 8 (one word of 8 columns per lane per row, 32 bytes per row
-// across the 8 lanes), 512 threads.
-template <int FMT>
+// are 32 contiguous bytes, 4 lanes a 128-byte line per step). AWQ: CW = 8
+// (one word of 8 columns per lane per row, 32 bytes per row across the 8
+// lanes). Narrower column blocks (CW = 1 or 2, more workgroups for the 256
+// CUs) lose the whole-line loads and measured 10-60% slower.
+template <int FMT, int THREADS_ = (FMT == QBN_GPTQ4 ? 256 : 512), int CW_ = (FMT == QBN_GPTQ4 ? 4 : 8)>
 struct AffShape {
-    static constexpr int CW = FMT == QBN_GPTQ4 ? 4 : 8;
-    static constexpr int THREADS = FMT == QBN_GPTQ4 ? 256 : 512;
+    static constexpr int CW = CW_;
+    static constexpr int THREADS = THREADS_;
     static constexpr int SL = THREADS / CW;
     static constexpr int WAVES = THREADS / 64;
 };
@@ -197,11 +198,13 @@ __device__ __forceinline__ void aff_compute(const AffRound<SPL, XT> &cur, float 
 // VEC: the 8 columns of a lane are loaded as 16-byte (codes, scales) and
 // 8-byte (zeros) vectors; needs n % 8 == 0 and 16-byte aligned data and
 // scales. Otherwise element loads with columns past n clamped (not stored).
-template <int FMT, typename XT, bool VEC, int SPL>
-__global__ __launch_bounds__(AffShape<FMT>::THREADS) void k_gemv_affine(const uint32_t *__restrict__ qw, const uint16_t *__restrict__ sc,
+template <int FMT, typename XT, bool VEC, int SPL, int THREADS = AffShape<FMT>::THREADS,
+          int CWT = AffShape<FMT>::CW>
+__global__ __launch_bounds__(THREADS) void k_gemv_affine(const uint32_t *__restrict__ qw, const uint16_t *__restrict__ sc,
                                                      const uint8_t *__restrict__ zp, const XT *__restrict__ x,
                                                      float *__restrict__ y, int64_t n, int64_t k, int64_t group) {
-    constexpr int CW = AffShape<FMT>::CW, SL = AffShape<FMT>::SL, WAVES = AffShape<FMT>::WAVES;
+    using Sh = AffShape<FMT, THREADS, CWT>;
+    constexpr int CW = Sh::CW, SL = Sh::SL, WAVES = Sh::WAVES;
     __shared__ float red[WAVES][CW][8];
     const int t = threadIdx.x;
     const int cw = t % CW, sl = t / CW;
@@ -376,24 +379,28 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ b
     }
 }
 
-template <int FMT, typename XT, bool VEC>
-hipError_t run_affine_spl(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+template <int FMT, typename XT, bool VEC, int TH, int SPL>
+hipError_t launch_affine(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     constexpr int CW = AffShape<FMT>::CW;
     const unsigned grid = (unsigned)((w.n + 8 * CW - 1) / (8 * CW));
-    const int64_t gs = w.group / 8;  // steps per group; a round of SPL steps stays inside one
-    if (gs % 8 == 0)
-        hipLaunchKernelGGL((k_gemv_affine<FMT, XT, VEC, 8>), dim3(grid), dim3(AffShape<FMT>::THREADS), 0, s,
-                           (const uint32_t *)w.data, (const uint16_t *)w.scales, (const uint8_t *)w.zeros, x, y, w.n,
-                           w.k, (int64_t)w.group);
-    else if (gs % 4 == 0)
-        hipLaunchKernelGGL((k_gemv_affine<FMT, XT, VEC, 4>), dim3(grid), dim3(AffShape<FMT>::THREADS), 0, s,
-                           (const uint32_t *)w.data, (const uint16_t *)w.scales, (const uint8_t *)w.zeros, x, y, w.n,
-                           w.k, (int64_t)w.group);
-    else
-        hipLaunchKernelGGL((k_gemv_affine<FMT, XT, VEC, 1>), dim3(grid), dim3(AffShape<FMT>::THREADS), 0, s,
-                           (const uint32_t *)w.data, (const uint16_t *)w.scales, (const uint8_t *)w.zeros, x, y, w.n,
-                           w.k, (int64_t)w.group);
+    hipLaunchKernelGGL((k_gemv_affine<FMT, XT, VEC, SPL, TH>), dim3(grid), dim3(TH), 0, s, (const uint32_t *)w.data,
+                       (const uint16_t *)w.scales, (const uint8_t *)w.zeros, x, y, w.n, w.k, (int64_t)w.group);
     return hipGetLastError();
+}
+
+template <int FMT, typename XT, bool VEC>
+hipError_t run_affine_spl(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+    const int64_t gs = w.group / 8;  // steps per group; a round of SPL steps stays inside one
+    if (FMT == QBN_GPTQ4) {
+        // 512 threads with rounds of 4 steps measured 5% faster than 256 with
+        // rounds of 8 on the 11008 x 4096 layer (more waves over the same columns)
+        if (gs % 4 == 0) return launch_affine<FMT, XT, VEC, 512, 4>(w, x, y, s);
+        return launch_affine<FMT, XT, VEC, 512, 1>(w, x, y, s);
+    }
+    // AWQ: 512 threads (1024 would cap registers at 128 and spill)
+    if (gs % 8 == 0) return launch_affine<FMT, XT, VEC, 512, 8>(w, x, y, s);
+    if (gs % 4 == 0) return launch_affine<FMT, XT, VEC, 512, 4>(w, x, y, s);
+    return launch_affine<FMT, XT, VEC, 512, 1>(w, x, y, s);
 }
 
 template <int FMT, typename XT>
