@@ -107,6 +107,18 @@ def test_int4_sym_brute_force():
             assert abs(q - r) == best and (abs(q - r) < 0.5 or q % 2 == 0)
 
 
+def test_int4_sym_ties_round_half_to_even():
+    """Exact ties: with max |w| = 7 the scale is exactly 1, so w / s = w.
+    Round half to even sends 2.5 -> 2, -2.5 -> -2, 0.5 -> 0, -0.5 -> 0,
+    3.5 -> 4, 1.5 -> 2, -6.5 -> -6 (written out by hand)."""
+    w = np.array([[7.0, 2.5, -2.5, 0.5, -0.5, 3.5, 1.5, -6.5]], np.float32)
+    codes, scales = oracle.int4_sym_quantize(w, 8)
+    assert scales[0, 0] == 1.0
+    want = [7, 2, -2, 0, 0, 4, 2, -6]
+    got = [int((codes[0, i // 2] >> (4 * (i % 2))) & 15) for i in range(8)]
+    assert [q - 16 if q >= 8 else q for q in got] == want
+
+
 def test_bit_planes_split_6_bit():
     rng = np.random.default_rng(7)
     v = rng.integers(0, 64, 96).astype(np.uint32)
