@@ -318,9 +318,22 @@ __device__ __forceinline__ void rescale(float s0, float s1, const f32x16 (&part)
 template <int FMT, bool YF32, bool PER_GROUP, bool VEC>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
     __shared__ Smem sm;
+    // Tile order: workgroups go to the 8 XCDs in turn (block b to XCD b % 8),
+    // so XCD x is given a contiguous run of logical tiles (x q + min(x, r)
+    // onwards, q, r = grid / 8, grid % 8); logical tiles walk groups of 8 row
+    // tiles column by column. The ~64 workgroups an XCD runs at once then
+    // cover about 8 x 8 tiles and share their X rows and weight columns in
+    // that XCD's L2.
     const int64_t tiles_n = (p.N + BN - 1) / BN;
-    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM;
-    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * BN;
+    const int64_t tiles_m = (p.M + BM - 1) / BM;
+    const int64_t nblk = gridDim.x, q8 = nblk / 8, r8 = nblk % 8, xcd = blockIdx.x % 8;
+    const int64_t lt = xcd * q8 + min(xcd, r8) + blockIdx.x / 8;
+    constexpr int64_t GM = 8;
+    const int64_t per_group = GM * tiles_n;
+    const int64_t first_m = (lt / per_group) * GM;
+    const int64_t gm = min(tiles_m - first_m, GM);
+    const int64_t m0 = (first_m + (lt % per_group) % gm) * BM;
+    const int64_t n0 = ((lt % per_group) / gm) * BN;
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     const int wm = wave / 2, wn = wave % 2;
