@@ -210,6 +210,75 @@ __device__ __forceinline__ void stage_load(Stage<FMT> &st, const Args &p, int64_
     }
 }
 
+// Buffer-resource path (GPTQ4 / AWQ4, group % 64 == 0, VEC layout, every
+// operand under 2 GiB). Each lane's byte offsets into X, the codes, the zero
+// points and the scales are fixed for the whole k loop; a k-tile only moves
+// the uniform offset (k0 and its group), which the buffer loads take in a
+// scalar register. No guards: k % 64 == 0 here (k % group == 0), rows past m
+// lie beyond the X descriptor's range and read as 0, and columns past n
+// feed only outputs that are never stored.
+struct BufOffsets {
+    uint32_t x[4];  // X row t/8 + 32i of the tile, chunk t % 8
+    uint32_t w;     // GPTQ: word row t % 8, columns 4(t/8)..; AWQ: rows 4(t%16).., word column t/16
+    uint32_t z;     // zero points of this thread's columns, group 0
+    uint32_t sc;    // scale of column t % 128, group 0
+};
+
+constexpr int32_t kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+template <int FMT>
+__device__ __forceinline__ BufOffsets buf_offsets(const Args &p, int64_t m0, int64_t n0) {
+    const int t = threadIdx.x;
+    BufOffsets o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.x[i] = (uint32_t)(((m0 + t / 8 + 32 * i) * p.ldx + 8 * (t % 8)) * 2);
+    if (FMT == QBN_GPTQ4) {
+        const int64_t n = n0 + 4 * (t / 8);
+        o.w = (uint32_t)(((t % 8) * p.N + n) * 4);
+        o.z = (uint32_t)n;
+    } else {
+        const int64_t n = n0 + 8 * (t / 16);
+        o.w = (uint32_t)(((4 * (t % 16)) * (p.N / 8) + n / 8) * 4);
+        o.z = (uint32_t)n;
+    }
+    o.sc = (uint32_t)((n0 + t % 128) * 2);
+    return o;
+}
+
+template <int FMT>
+__device__ __forceinline__ void stage_load_buf(Stage<FMT> &st, const Args &p, const BufOffsets &o,
+                                               __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
+                                               __amdgpu_buffer_rsrc_t rz, __amdgpu_buffer_rsrc_t rs, int64_t k0,
+                                               int64_t g) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        st.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, o.x[i], (int)(k0 * 2), 0));
+    const int zoff = (int)(g * p.N);
+    if (FMT == QBN_GPTQ4) {
+        const u32x4 w = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, o.w, (int)((k0 / 8) * p.N * 4), 0));
+        st.w[0] = w.x;
+        st.w[1] = w.y;
+        st.w[2] = w.z;
+        st.w[3] = w.w;
+        st.zb[0] = __builtin_amdgcn_raw_buffer_load_b32(rz, o.z, zoff, 0);
+    } else {
+        const int base = (int)(k0 * (p.N / 8) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, o.w + (uint32_t)(i * (p.N / 8) * 4), base, 0);
+        const u32x2 z = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rz, o.z, zoff, 0));
+        st.zb[0] = z.x;
+        st.zb[1] = z.y;
+    }
+    const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b16(rs, o.sc, zoff * 2, 0);
+    st.s = f16_to_f32(sv);
+}
+
 template <int FMT>
 __device__ __forceinline__ void stage_store(const Stage<FMT> &st, Smem &sm, int buf) {
     const int t = threadIdx.x;
@@ -315,7 +384,7 @@ __device__ __forceinline__ void rescale(float s0, float s1, const f32x16 (&part)
 // groups of 32 or any odd multiple of 32) every 32-k sub-block is rescaled
 // with its own scale; within a group that scale is the same, so both forms
 // compute the same sum up to rounding.
-template <int FMT, bool YF32, bool PER_GROUP, bool VEC>
+template <int FMT, bool YF32, bool PER_GROUP, bool VEC, bool BUF>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
     __shared__ Smem sm;
     // Tile order: workgroups go to the 8 XCDs in turn (block b to XCD b % 8),
@@ -353,7 +422,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
     // element lrem of group lg
     int64_t lg = 0, lrem = 0;
     Stage<FMT> st;
-    stage_load<FMT, VEC>(st, p, m0, n0, 0, lg, lrem);
+    BufOffsets bo;
+    __amdgpu_buffer_rsrc_t rx, rw, rz, rs;
+    if constexpr (BUF) {
+        bo = buf_offsets<FMT>(p, m0, n0);
+        rx = rsrc(p.X, (uint32_t)(((p.M - 1) * p.ldx + p.K) * 2));
+        rw = rsrc(p.data, (uint32_t)(p.K * p.N / 2));
+        rz = rsrc(p.zeros, (uint32_t)((p.K / p.group) * p.N));
+        rs = rsrc(p.scales, (uint32_t)((p.K / p.group) * p.N * 2));
+        stage_load_buf<FMT>(st, p, bo, rx, rw, rz, rs, 0, 0);
+    } else {
+        stage_load<FMT, VEC>(st, p, m0, n0, 0, lg, lrem);
+    }
     stage_store<FMT>(st, sm, 0);
     __syncthreads();
 
@@ -370,7 +450,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
                 lrem -= p.group;
                 ++lg;
             }
-            stage_load<FMT, VEC>(st, p, m0, n0, (int64_t)(kt + 1) * BK, lg, lrem);
+            if constexpr (BUF)
+                stage_load_buf<FMT>(st, p, bo, rx, rw, rz, rs, (int64_t)(kt + 1) * BK, lg);
+            else
+                stage_load<FMT, VEC>(st, p, m0, n0, (int64_t)(kt + 1) * BK, lg, lrem);
         }
         if (PER_GROUP) {
             if (tig == 0) {
@@ -419,14 +502,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
         }
 }
 
-template <int FMT, bool PER_GROUP, bool VEC>
+template <int FMT, bool PER_GROUP, bool VEC, bool BUF = false>
 hipError_t run3(const Args &a, bool yf32, hipStream_t s) {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (yf32)
-        hipLaunchKernelGGL((k_gemm_int4<FMT, true, PER_GROUP, VEC>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_gemm_int4<FMT, true, PER_GROUP, VEC, BUF>), dim3((unsigned)tiles), dim3(kThreads), 0, s,
+                           a);
     else
-        hipLaunchKernelGGL((k_gemm_int4<FMT, false, PER_GROUP, VEC>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_gemm_int4<FMT, false, PER_GROUP, VEC, BUF>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                           s, a);
     return hipGetLastError();
+}
+
+// Every byte offset of the buffer path fits in 31 bits.
+bool buf_fits(const Args &a) {
+    constexpr int64_t L = (int64_t)1 << 31;
+    const int64_t xb = ((a.M + BM) * a.ldx + a.K) * 2;  // rows of the last tile included
+    return xb < L && a.K * a.N / 2 < L && (a.K / a.group) * a.N * 2 + (int64_t)BN * 8 < L &&
+           (int64_t)(a.N + BN) * 4 * 8 < L;
 }
 
 template <int FMT>
@@ -435,8 +528,10 @@ hipError_t run(const Args &a, bool yf32, hipStream_t s) {
         return run3<FMT, false, false>(a, yf32, s);
     } else {
         const bool vec = a.N % 8 == 0 && (uintptr_t)a.data % 16 == 0 && (uintptr_t)a.zeros % 8 == 0;
-        if (a.group % BK == 0)
+        if (a.group % BK == 0) {
+            if (vec && buf_fits(a)) return run3<FMT, true, true, true>(a, yf32, s);
             return vec ? run3<FMT, true, true>(a, yf32, s) : run3<FMT, true, false>(a, yf32, s);
+        }
         return vec ? run3<FMT, false, true>(a, yf32, s) : run3<FMT, false, false>(a, yf32, s);
     }
 }
