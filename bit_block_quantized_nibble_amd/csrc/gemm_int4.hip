@@ -120,11 +120,16 @@ __device__ __forceinline__ int64_t group_of(int64_t g0, int64_t rem0, int64_t gr
 // VEC (n % 8 == 0, 16-byte aligned codes, 8-byte aligned zero points): GPTQ
 // reads its four words in one 16-byte load and its four zero points in one
 // dword; AWQ its eight zero points in one 8-byte load.
-template <int FMT, bool VEC>
+template <int FMT, bool VEC, bool XB = false>
 __device__ __forceinline__ void stage_load(Stage<FMT> &st, const Args &p, int64_t m0, int64_t n0, int64_t k0,
-                                           int64_t g0, int64_t rem0) {
+                                           int64_t g0, int64_t rem0, const uint32_t (&xo)[4],
+                                           __amdgpu_buffer_rsrc_t rx) {
     const int t = threadIdx.x;
-    {
+    if constexpr (XB) {  // k % 64 == 0: X through its descriptor, rows past m read as 0
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo[i], (int)(k0 * 2), 0));
+    } else {
         const int c16 = t % 8;
         const int64_t k = k0 + 8 * c16;
 #pragma unroll
@@ -384,7 +389,9 @@ __device__ __forceinline__ void rescale(float s0, float s1, const f32x16 (&part)
 // groups of 32 or any odd multiple of 32) every 32-k sub-block is rescaled
 // with its own scale; within a group that scale is the same, so both forms
 // compute the same sum up to rounding.
-template <int FMT, bool YF32, bool PER_GROUP, bool VEC, bool BUF>
+// BUF: the buffer path for everything (per-group, VEC); XB: X alone through
+// its descriptor (k % 64 == 0), the weights through the general loader.
+template <int FMT, bool YF32, bool PER_GROUP, bool VEC, bool BUF, bool XB = BUF>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
     __shared__ Smem sm;
     // Tile order: workgroups go to the 8 XCDs in turn (block b to XCD b % 8),
@@ -422,17 +429,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
     // element lrem of group lg
     int64_t lg = 0, lrem = 0;
     Stage<FMT> st;
-    BufOffsets bo;
-    __amdgpu_buffer_rsrc_t rx, rw, rz, rs;
+    BufOffsets bo = buf_offsets<FMT>(p, m0, n0);
+    const __amdgpu_buffer_rsrc_t rx = rsrc(p.X, XB ? (uint32_t)(((p.M - 1) * p.ldx + p.K) * 2) : 0u);
+    __amdgpu_buffer_rsrc_t rw, rz, rs;
     if constexpr (BUF) {
-        bo = buf_offsets<FMT>(p, m0, n0);
-        rx = rsrc(p.X, (uint32_t)(((p.M - 1) * p.ldx + p.K) * 2));
         rw = rsrc(p.data, (uint32_t)(p.K * p.N / 2));
         rz = rsrc(p.zeros, (uint32_t)((p.K / p.group) * p.N));
         rs = rsrc(p.scales, (uint32_t)((p.K / p.group) * p.N * 2));
         stage_load_buf<FMT>(st, p, bo, rx, rw, rz, rs, 0, 0);
     } else {
-        stage_load<FMT, VEC>(st, p, m0, n0, 0, lg, lrem);
+        stage_load<FMT, VEC, XB>(st, p, m0, n0, 0, lg, lrem, bo.x, rx);
     }
     stage_store<FMT>(st, sm, 0);
     __syncthreads();
@@ -453,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
             if constexpr (BUF)
                 stage_load_buf<FMT>(st, p, bo, rx, rw, rz, rs, (int64_t)(kt + 1) * BK, lg);
             else
-                stage_load<FMT, VEC>(st, p, m0, n0, (int64_t)(kt + 1) * BK, lg, lrem);
+                stage_load<FMT, VEC, XB>(st, p, m0, n0, (int64_t)(kt + 1) * BK, lg, lrem, bo.x, rx);
         }
         if (PER_GROUP) {
             if (tig == 0) {
@@ -502,17 +508,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
         }
 }
 
-template <int FMT, bool PER_GROUP, bool VEC, bool BUF = false>
+template <int FMT, bool PER_GROUP, bool VEC, bool BUF = false, bool XB = BUF>
 hipError_t run3(const Args &a, bool yf32, hipStream_t s) {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (yf32)
-        hipLaunchKernelGGL((k_gemm_int4<FMT, true, PER_GROUP, VEC, BUF>), dim3((unsigned)tiles), dim3(kThreads), 0, s,
-                           a);
-    else
-        hipLaunchKernelGGL((k_gemm_int4<FMT, false, PER_GROUP, VEC, BUF>), dim3((unsigned)tiles), dim3(kThreads), 0,
+        hipLaunchKernelGGL((k_gemm_int4<FMT, true, PER_GROUP, VEC, BUF, XB>), dim3((unsigned)tiles), dim3(kThreads), 0,
                            s, a);
+    else
+        hipLaunchKernelGGL((k_gemm_int4<FMT, false, PER_GROUP, VEC, BUF, XB>), dim3((unsigned)tiles), dim3(kThreads),
+                           0, s, a);
     return hipGetLastError();
 }
+
+// X's byte offsets (rows of the last tile included) fit in 31 bits.
+bool x_buf_fits(const Args &a) { return ((a.M + BM) * a.ldx + a.K) * 2 < ((int64_t)1 << 31); }
 
 // Every byte offset of the buffer path fits in 31 bits.
 bool buf_fits(const Args &a) {
@@ -524,14 +533,19 @@ bool buf_fits(const Args &a) {
 
 template <int FMT>
 hipError_t run(const Args &a, bool yf32, hipStream_t s) {
+    // X through its descriptor when k % 64 == 0: measured 4-6% faster for
+    // Q4_0 and GPTQ; AWQ's general path spills more with it and is slower.
+    const bool xb = FMT != QBN_AWQ4 && a.K % BK == 0 && x_buf_fits(a);
     if constexpr (FMT == QBN_Q4_0) {
-        return run3<FMT, false, false>(a, yf32, s);
+        return xb ? run3<FMT, false, false, false, true>(a, yf32, s) : run3<FMT, false, false>(a, yf32, s);
     } else {
         const bool vec = a.N % 8 == 0 && (uintptr_t)a.data % 16 == 0 && (uintptr_t)a.zeros % 8 == 0;
         if (a.group % BK == 0) {
             if (vec && buf_fits(a)) return run3<FMT, true, true, true>(a, yf32, s);
+            if (xb) return vec ? run3<FMT, true, true, false, true>(a, yf32, s) : run3<FMT, true, false, false, true>(a, yf32, s);
             return vec ? run3<FMT, true, true>(a, yf32, s) : run3<FMT, true, false>(a, yf32, s);
         }
+        if (xb) return vec ? run3<FMT, false, true, false, true>(a, yf32, s) : run3<FMT, false, false, false, true>(a, yf32, s);
         return vec ? run3<FMT, false, true>(a, yf32, s) : run3<FMT, false, false>(a, yf32, s);
     }
 }
