@@ -44,3 +44,37 @@ def test_recorded_traffic_is_dropped_when_a_kernel_source_changes(tmp_path, monk
     changed = bench.recorded_traffic(name)
     assert unchanged == rec["traffic_bytes"] or unchanged is None  # None if the tree itself changed since
     assert changed is None
+
+
+def _small_inputs(spec):
+    """The workload's recipe at a small shape (the CPU-baseline leg reads the
+    shapes from its inputs)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    cfg = spec["cfg"]
+    if cfg in (1, 2, 3, 6, 8):
+        inp = workloads.workload(cfg, n=24, k=512)
+    elif cfg == 4:
+        inp = workloads.workload(4, n=16, k=256, m=8)
+    elif cfg == 5:
+        inp = workloads.workload(5, n=64, k=256)
+    elif cfg == 7:
+        inp = workloads.workload(7, n=64, k=256)
+    else:
+        inp = workloads.workload(9, n=64, k=256, m=8)
+    if spec["kind"] == "encode":  # the bench dequantizes the weights on the device; here the oracle does
+        w = oracle.dequant_rows(oracle.NVFP4, inp["data"], inp["scales"], inp["scale2"], inp["k"], range(inp["n"]))
+        inp = dict(inp, W=torch.from_numpy(oracle.bf16_rne_array(w).view(np.int16)).view(torch.bfloat16))
+    return inp
+
+
+def test_cpu_baseline_leg_runs_for_every_workload():
+    for name, spec in bench.WORKLOADS.items():
+        out = bench.cpu_baseline(name, spec, _small_inputs(spec), 0.02)
+        assert out["kind"] == "oracle" and out["cores"] >= 1, name
+        assert out["value"] > 0 and out["unit"] == spec["unit"], name
+        assert isinstance(out["sample"], str) and out["sample"], name
