@@ -169,15 +169,57 @@ __device__ __forceinline__ void get_block(const uint8_t *run, int b, uint32_t *D
 // column col(r) (skipped when col(r) >= N) and holds blocks b0 .. b0+nb-1 of
 // it, contiguous at (col * nbr + b0) * 18. Wave w moves runs w, w + 4, ...,
 // BATCH runs at a time with all of a batch's loads issued before its stores.
-// WORDS: every run starts on a 4-byte boundary and has an even block count
-// (a run is then at most 36 words, one per lane); otherwise 2-byte units.
+// MODE 2: every run is a whole RB = 8 blocks (144 bytes, nine 16-byte
+// pieces) starting on a 16-byte boundary (k % 256 == 0, 16-byte aligned
+// base): lane l moves piece l % 9 of run l / 9, so one instruction moves 7
+// runs; all of a wave's loads are issued before its stores. MODE 1 (WORDS):
+// every run starts on a 4-byte boundary and has an even block count (a run
+// is then at most 36 words, one per lane); MODE 0: 2-byte units.
+struct alignas(4) Piece16 {  // 16 bytes at a 4-byte aligned LDS address (runs sit RS apart)
+    uint32_t v[4];
+};
+
 template <bool TO_LDS, int NR, typename ColOf>
 __device__ __forceinline__ void move_runs(uint8_t *lds, uint8_t *__restrict__ blocks, ColOf col, int64_t N,
-                                          int64_t nbr, int64_t b0, int nb, bool words) {
+                                          int64_t nbr, int64_t b0, int nb, int mode) {
     constexpr int PER_WAVE = NR / 4;
     constexpr int BATCH = PER_WAVE < 16 ? PER_WAVE : 16;
     static_assert(NR % (4 * BATCH) == 0, "whole batches");
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    if (mode == 2) {
+        constexpr int IT = (NR + 27) / 28;  // 4 waves x 7 runs per step
+        const int j = lane / 9, pc = lane % 9;
+        u32x4 v[IT];
+        bool ok[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int r = 28 * it + 7 * wave + j;
+            ok[it] = j < 7 && r < NR && col(r < NR ? r : 0) < N;
+            if (ok[it]) {
+                if (TO_LDS) {
+                    v[it] = reinterpret_cast<const u32x4 *>(blocks + (col(r) * nbr + b0) * 18)[pc];
+                } else {
+                    const Piece16 q = *reinterpret_cast<const Piece16 *>(lds + r * RS + 16 * pc);
+                    v[it] = u32x4{q.v[0], q.v[1], q.v[2], q.v[3]};
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int r = 28 * it + 7 * wave + j;
+            if (ok[it]) {
+                if (TO_LDS) {
+                    Piece16 q;
+                    q.v[0] = v[it].x, q.v[1] = v[it].y, q.v[2] = v[it].z, q.v[3] = v[it].w;
+                    *reinterpret_cast<Piece16 *>(lds + r * RS + 16 * pc) = q;
+                } else {
+                    reinterpret_cast<u32x4 *>(blocks + (col(r) * nbr + b0) * 18)[pc] = v[it];
+                }
+            }
+        }
+        return;
+    }
+    const bool words = mode != 0;
     const int L = nb * 18;
     for (int r0 = wave; r0 < NR; r0 += 4 * BATCH) {
         if (words) {
@@ -257,7 +299,7 @@ __global__ __launch_bounds__(256) void k_gptq_to_q4_0(const uint32_t *__restrict
         }
     }
     __syncthreads();
-    move_runs<false, 64>(runs, dst, [&](int r) { return n0 + r; }, N, nbr, b0, nb, words != 0);
+    move_runs<false, 64>(runs, dst, [&](int r) { return n0 + r; }, N, nbr, b0, nb, words);
 }
 
 // Q4_0 -> GPTQ / AWQ also write the companions of the target: for every
@@ -271,7 +313,7 @@ __global__ __launch_bounds__(256) void k_q4_0_to_gptq(const uint8_t *__restrict_
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, n0 = (int64_t)(blockIdx.x / nbt) * 64;
     const int nb = (int)((nbr - b0) < RB ? (nbr - b0) : RB);
     move_runs<true, 64>(runs, const_cast<uint8_t *>(src), [&](int r) { return n0 + r; }, N, nbr, b0, nb,
-                        words != 0);
+                        words);
     __syncthreads();
     const int c = threadIdx.x % 64;
     const int64_t n = n0 + c;
@@ -323,7 +365,7 @@ __global__ __launch_bounds__(256) void k_awq_to_q4_0(const uint32_t *__restrict_
     }
     __syncthreads();
     move_runs<false, 256>(runs, dst, [&](int r) { return 8 * (g0 + r % 32) + awq_col(r / 32); }, N, nbr, b0, nb,
-                          words != 0);
+                          words);
 }
 
 __global__ __launch_bounds__(256) void k_q4_0_to_awq(const uint8_t *__restrict__ src, uint32_t *__restrict__ dst,
@@ -334,7 +376,7 @@ __global__ __launch_bounds__(256) void k_q4_0_to_awq(const uint8_t *__restrict__
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, g0 = (int64_t)(blockIdx.x / nbt) * 32;
     const int nb = (int)((nbr - b0) < RB ? (nbr - b0) : RB);
     move_runs<true, 256>(runs, const_cast<uint8_t *>(src),
-                         [&](int r) { return 8 * (g0 + r % 32) + awq_col(r / 32); }, N, nbr, b0, nb, words != 0);
+                         [&](int r) { return 8 * (g0 + r % 32) + awq_col(r / 32); }, N, nbr, b0, nb, words);
     __syncthreads();
     const int g = threadIdx.x % 32, b = threadIdx.x / 32;
     if (g0 + g >= G || b >= nb) return;
@@ -407,7 +449,11 @@ hipError_t launch_repack(const qbn_tensor &src, int dst_format, int dst_group, v
     // word: an even block count per column (then every tile's count is even
     // too) and a word-aligned base.
     const void *q4 = to_q4 ? dst_data : src.data;
-    const int words = (nbr % 2 == 0) && (reinterpret_cast<uintptr_t>(q4) % 4 == 0);
+    // 16-byte pieces (mode 2) when every run is 8 whole blocks on a 16-byte
+    // boundary: (n nbr + b0) * 18 is a multiple of 144 when nbr % 8 == 0
+    const int words = ((nbr % RB == 0) && (reinterpret_cast<uintptr_t>(q4) % 16 == 0)) ? 2
+                      : ((nbr % 2 == 0) && (reinterpret_cast<uintptr_t>(q4) % 4 == 0)) ? 1
+                                                                                        : 0;
     const bool awq = (sf == QBN_AWQ4) || (dst_format == QBN_AWQ4);
     const int64_t ntile = awq ? (N / 8 + 31) / 32 : (N + 63) / 64;
     const int64_t tiles = nbt * ntile;

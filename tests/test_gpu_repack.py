@@ -135,3 +135,33 @@ def test_repack_validate_q4_0_group_scales():
     blocks[3, 5, 0] ^= 0x10
     w = qbn.QTensor("q4_0", N, K, dev(blocks), group=g)
     assert qbn.validate(w) == 3 * (K // 32) + 5
+
+
+@pytest.mark.parametrize("src,dst", [("gptq4", "q4_0"), ("awq4", "q4_0"), ("q4_0", "gptq4"), ("q4_0", "awq4")])
+@pytest.mark.parametrize("offset", [0, 4, 2])
+def test_repack_q4_0_run_modes(src, dst, offset):
+    """k % 256 == 0: 16-byte run pieces on a 16-byte aligned Q4_0 buffer,
+    4-byte words at a 4-byte offset, 2-byte units at a 2-byte offset."""
+    K, N, g = 512, 264, 128
+    rng = np.random.default_rng(offset * 11 + len(src))
+    q = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    scales = rng.uniform(-0.01, 0.01, (K // g, N)).astype(np.float16).view(np.uint16)
+    zeros = np.full((K // g, N), 8, np.uint8)
+    nbytes = N * (K // 32) * 18
+    raw = torch.zeros(nbytes + 16, dtype=torch.uint8, device=DEV)
+    q4 = raw[offset:offset + nbytes].view(N, K // 32, 18)
+    say("repack run mode", src, "->", dst, "offset", offset)
+    if src == "q4_0":
+        q4.copy_(dev(_expect("q4_0", q, scales, g)))
+        w = qbn.QTensor("q4_0", N, K, q4)
+        out = qbn.repack(w, dst, dst_group=g)
+        torch.cuda.synchronize()
+        want = _expect(dst, q, scales, g)
+        assert np.array_equal(host_bits(out.data).reshape(want.shape).view(np.uint8), want.view(np.uint8))
+    else:
+        w = _mk(src, q, scales, zeros, g)
+        qbn.repack(w, "q4_0", data=q4)
+        torch.cuda.synchronize()
+        want = _expect("q4_0", q, scales, g)
+        assert np.array_equal(q4.cpu().numpy().reshape(want.shape), want)
+        assert (raw[:offset].cpu() == 0).all() and (raw[offset + nbytes:].cpu() == 0).all()
