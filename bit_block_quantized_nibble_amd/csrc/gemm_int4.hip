@@ -215,8 +215,9 @@ __device__ __forceinline__ void stage_load(Stage<FMT> &st, const Args &p, int64_
     }
 }
 
-// Buffer-resource path (GPTQ4 / AWQ4, group % 64 == 0, VEC layout, every
-// operand under 2 GiB). Each lane's byte offsets into X, the codes, the zero
+// Buffer-resource path (GPTQ4 / AWQ4 with group % 64 == 0 and the VEC
+// layout, or Q4_0 with k % 64 == 0 and dword-aligned blocks; every operand
+// under 2 GiB). Each lane's byte offsets into X, the codes, the zero
 // points and the scales are fixed for the whole k loop; a k-tile only moves
 // the uniform offset (k0 and its group), which the buffer loads take in a
 // scalar register. No guards: k % 64 == 0 here (k % group == 0), rows past m
@@ -245,6 +246,12 @@ __device__ __forceinline__ BufOffsets buf_offsets(const Args &p, int64_t m0, int
         const int64_t n = n0 + 4 * (t / 8);
         o.w = (uint32_t)(((t % 8) * p.N + n) * 4);
         o.z = (uint32_t)n;
+    } else if (FMT == QBN_Q4_0) {
+        // block (column n0 + t/2, t % 2) of the first k-tile; with k % 64 == 0 a
+        // block starts 2 bytes past a dword boundary exactly when t is odd, so
+        // the dword-aligned read starts at the block (t even) or 2 bytes before it
+        o.w = (uint32_t)(((n0 + t / 2) * (p.K / 32) + (t % 2)) * 18 - 2 * (t % 2));
+        o.z = 0;
     } else {
         const int64_t n = n0 + 8 * (t / 16);
         o.w = (uint32_t)(((4 * (t % 16)) * (p.N / 8) + n / 8) * 4);
@@ -263,6 +270,19 @@ __device__ __forceinline__ void stage_load_buf(Stage<FMT> &st, const Args &p, co
     for (int i = 0; i < 4; ++i)
         st.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, o.x[i], (int)(k0 * 2), 0));
     const int zoff = (int)(g * p.N);
+    if (FMT == QBN_Q4_0) {
+        // 20 dword-aligned bytes covering the 18-byte block (see buf_offsets)
+        const int soff = (int)((k0 / 32) * 18);
+        const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, o.w, soff, 0));
+        const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(rw, o.w + 16, soff, 0);
+        const bool odd = (threadIdx.x & 1) != 0;
+        const uint32_t dw[5] = {a.x, a.y, a.z, a.w, e};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)  // odd: codes start on dword 1; even: 2 bytes into dword 0
+            st.w[i] = odd ? dw[i + 1] : __builtin_amdgcn_alignbyte(dw[i + 1], dw[i], 2);
+        st.s = f16_to_f32(odd ? (a.x >> 16) : (a.x & 0xFFFFu));
+        return;
+    }
     if (FMT == QBN_GPTQ4) {
         const u32x4 w = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, o.w, (int)((k0 / 8) * p.N * 4), 0));
@@ -389,8 +409,9 @@ __device__ __forceinline__ void rescale(float s0, float s1, const f32x16 (&part)
 // groups of 32 or any odd multiple of 32) every 32-k sub-block is rescaled
 // with its own scale; within a group that scale is the same, so both forms
 // compute the same sum up to rounding.
-// BUF: the buffer path for everything (per-group, VEC); XB: X alone through
-// its descriptor (k % 64 == 0), the weights through the general loader.
+// BUF: the buffer path for everything (GPTQ4 / AWQ4 per group with VEC, or
+// Q4_0); XB: X alone through its descriptor (k % 64 == 0), the weights
+// through the general loader.
 template <int FMT, bool YF32, bool PER_GROUP, bool VEC, bool BUF, bool XB = BUF>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
     __shared__ Smem sm;
@@ -433,9 +454,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
     const __amdgpu_buffer_rsrc_t rx = rsrc(p.X, XB ? (uint32_t)(((p.M - 1) * p.ldx + p.K) * 2) : 0u);
     __amdgpu_buffer_rsrc_t rw, rz, rs;
     if constexpr (BUF) {
-        rw = rsrc(p.data, (uint32_t)(p.K * p.N / 2));
-        rz = rsrc(p.zeros, (uint32_t)((p.K / p.group) * p.N));
-        rs = rsrc(p.scales, (uint32_t)((p.K / p.group) * p.N * 2));
+        if constexpr (FMT == QBN_Q4_0) {
+            rw = rsrc(p.data, (uint32_t)(p.N * (p.K / 32) * 18));
+            rz = rw;
+            rs = rw;
+        } else {
+            rw = rsrc(p.data, (uint32_t)(p.K * p.N / 2));
+            rz = rsrc(p.zeros, (uint32_t)((p.K / p.group) * p.N));
+            rs = rsrc(p.scales, (uint32_t)((p.K / p.group) * p.N * 2));
+        }
         stage_load_buf<FMT>(st, p, bo, rx, rw, rz, rs, 0, 0);
     } else {
         stage_load<FMT, VEC, XB>(st, p, m0, n0, 0, lg, lrem, bo.x, rx);
@@ -537,6 +564,9 @@ hipError_t run(const Args &a, bool yf32, hipStream_t s) {
     // Q4_0 and GPTQ; AWQ's general path spills more with it and is slower.
     const bool xb = FMT != QBN_AWQ4 && a.K % BK == 0 && x_buf_fits(a);
     if constexpr (FMT == QBN_Q4_0) {
+        // buffer path: k % 64 == 0, dword-aligned blocks, offsets in 31 bits
+        const bool qb = xb && (uintptr_t)a.data % 4 == 0 && (a.N + BN) * (a.K / 32) * 18 + 64 < ((int64_t)1 << 31);
+        if (qb) return run3<FMT, false, false, true, true>(a, yf32, s);
         return xb ? run3<FMT, false, false, false, true>(a, yf32, s) : run3<FMT, false, false>(a, yf32, s);
     } else {
         const bool vec = a.N % 8 == 0 && (uintptr_t)a.data % 16 == 0 && (uintptr_t)a.zeros % 8 == 0;
