@@ -215,14 +215,15 @@ __device__ __forceinline__ void stage_load(Stage<FMT> &st, const Args &p, int64_
     }
 }
 
-// Buffer-resource path (GPTQ4 / AWQ4 with group % 64 == 0 and the VEC
-// layout, or Q4_0 with k % 64 == 0 and dword-aligned blocks; every operand
-// under 2 GiB). Each lane's byte offsets into X, the codes, the zero
-// points and the scales are fixed for the whole k loop; a k-tile only moves
-// the uniform offset (k0 and its group), which the buffer loads take in a
-// scalar register. No guards: k % 64 == 0 here (k % group == 0), rows past m
-// lie beyond the X descriptor's range and read as 0, and columns past n
-// feed only outputs that are never stored.
+// Buffer-resource path (k % 64 == 0; GPTQ4 / AWQ4 in the VEC layout, or
+// Q4_0 with dword-aligned blocks; every operand under 2 GiB). Each lane's
+// byte offsets into X, the codes, the zero points and the scales are fixed
+// for the whole k loop; a k-tile only moves the uniform offset (k0 and its
+// group), which the buffer loads take in a scalar register. With groups that
+// are not a multiple of 64 a tile spans two groups, and a lane whose rows lie
+// in the second adds one group row to its zero-point and scale offsets. No
+// guards: k % 64 == 0, rows past m lie beyond the X descriptor's range and
+// read as 0, and columns past n feed only outputs that are never stored.
 struct BufOffsets {
     uint32_t x[4];  // X row t/8 + 32i of the tile, chunk t % 8
     uint32_t w;     // GPTQ: word row t % 8, columns 4(t/8)..; AWQ: rows 4(t%16).., word column t/16
@@ -261,11 +262,15 @@ __device__ __forceinline__ BufOffsets buf_offsets(const Args &p, int64_t m0, int
     return o;
 }
 
-template <int FMT>
+template <int FMT, bool PG>
 __device__ __forceinline__ void stage_load_buf(Stage<FMT> &st, const Args &p, const BufOffsets &o,
                                                __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
                                                __amdgpu_buffer_rsrc_t rz, __amdgpu_buffer_rsrc_t rs, int64_t k0,
-                                               int64_t g) {
+                                               int64_t g, int64_t rem0) {
+    // PG (group % 64 == 0): the whole tile lies in group g. Otherwise
+    // rem0 + off < 2 group for every offset off < 64 of the tile (rem0 < group,
+    // and rem0 == 0 when group == 32), so a lane's group is g or g + 1.
+    const uint32_t t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         st.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, o.x[i], (int)(k0 * 2), 0));
@@ -275,7 +280,7 @@ __device__ __forceinline__ void stage_load_buf(Stage<FMT> &st, const Args &p, co
         const int soff = (int)((k0 / 32) * 18);
         const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, o.w, soff, 0));
         const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(rw, o.w + 16, soff, 0);
-        const bool odd = (threadIdx.x & 1) != 0;
+        const bool odd = (t & 1) != 0;
         const uint32_t dw[5] = {a.x, a.y, a.z, a.w, e};
 #pragma unroll
         for (int i = 0; i < 4; ++i)  // odd: codes start on dword 1; even: 2 bytes into dword 0
@@ -290,21 +295,27 @@ __device__ __forceinline__ void stage_load_buf(Stage<FMT> &st, const Args &p, co
         st.w[1] = w.y;
         st.w[2] = w.z;
         st.w[3] = w.w;
-        st.zb[0] = __builtin_amdgcn_raw_buffer_load_b32(rz, o.z, zoff, 0);
+        const uint32_t dz = !PG && rem0 + 8 * (t % 8) >= p.group ? (uint32_t)p.N : 0u;
+        st.zb[0] = __builtin_amdgcn_raw_buffer_load_b32(rz, o.z + dz, zoff, 0);
     } else {
         const int base = (int)(k0 * (p.N / 8) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             st.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, o.w + (uint32_t)(i * (p.N / 8) * 4), base, 0);
-        const u32x2 z = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rz, o.z, zoff, 0));
+        const uint32_t dz = !PG && rem0 + 4 * (t % 16) >= p.group ? (uint32_t)p.N : 0u;
+        const u32x2 z = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rz, o.z + dz, zoff, 0));
         st.zb[0] = z.x;
         st.zb[1] = z.y;
     }
-    const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b16(rs, o.sc, zoff * 2, 0);
+    const uint32_t ds = !PG && rem0 + 32 * (t / 128) >= p.group ? 2 * (uint32_t)p.N : 0u;
+    const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b16(rs, o.sc + ds, zoff * 2, 0);
     st.s = f16_to_f32(sv);
 }
 
-template <int FMT>
+// NARROW (AWQ4): each row pair of a column goes to LDS on its own (4-byte
+// stores) as soon as it is decoded, instead of both pairs in one 8-byte
+// store; fewer live registers, which the per-32-k rescale path needs.
+template <int FMT, bool NARROW = false>
 __device__ __forceinline__ void stage_store(const Stage<FMT> &st, Smem &sm, int buf) {
     const int t = threadIdx.x;
     {
@@ -335,21 +346,36 @@ __device__ __forceinline__ void stage_store(const Stage<FMT> &st, Smem &sm, int 
             constexpr int col[8] = {0, 2, 4, 6, 1, 3, 5, 7};
             zs[tt] = (float)((st.zb[col[tt] / 4] >> (8 * (col[tt] % 4))) & 0xFFu);
         }
-        // two rows at a time (fewer live registers): pr[tt] = bf16 pair of
-        // rows (2 ih, 2 ih + 1) of the slot-tt column
-        uint32_t pr[2][8];
+        if constexpr (NARROW) {
 #pragma unroll
-        for (int ih = 0; ih < 2; ++ih) {
-            float v0[8], v1[8];
-            nibbles_minus(st.w[2 * ih], zs, v0);  // v0[slot]: k = 4h + 2ih
-            nibbles_minus(st.w[2 * ih + 1], zs, v1);
+            for (int ih = 0; ih < 2; ++ih) {
+                float v0[8], v1[8];
+                nibbles_minus(st.w[2 * ih], zs, v0);  // v0[slot]: k = 4h + 2ih
+                nibbles_minus(st.w[2 * ih + 1], zs, v1);
 #pragma unroll
-            for (int tt = 0; tt < 8; ++tt) pr[ih][tt] = bf16_pair(v0[tt], v1[tt]);
-        }
+                for (int tt = 0; tt < 8; ++tt) {
+                    constexpr int col[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+                    *reinterpret_cast<uint32_t *>(&sm.b[buf][(8 * c + col[tt]) * LDK + 4 * h + 2 * ih]) =
+                        bf16_pair(v0[tt], v1[tt]);
+                }
+            }
+        } else {
+            // two rows at a time: pr[ih][tt] = bf16 pair of rows (2 ih, 2 ih + 1)
+            // of the slot-tt column
+            uint32_t pr[2][8];
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-            constexpr int col[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-            *reinterpret_cast<u32x2 *>(&sm.b[buf][(8 * c + col[tt]) * LDK + 4 * h]) = u32x2{pr[0][tt], pr[1][tt]};
+            for (int ih = 0; ih < 2; ++ih) {
+                float v0[8], v1[8];
+                nibbles_minus(st.w[2 * ih], zs, v0);  // v0[slot]: k = 4h + 2ih
+                nibbles_minus(st.w[2 * ih + 1], zs, v1);
+#pragma unroll
+                for (int tt = 0; tt < 8; ++tt) pr[ih][tt] = bf16_pair(v0[tt], v1[tt]);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+                constexpr int col[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+                *reinterpret_cast<u32x2 *>(&sm.b[buf][(8 * c + col[tt]) * LDK + 4 * h]) = u32x2{pr[0][tt], pr[1][tt]};
+            }
         }
         sm.s[buf][t / 128][t % 128] = st.s;
     } else {
@@ -409,8 +435,8 @@ __device__ __forceinline__ void rescale(float s0, float s1, const f32x16 (&part)
 // groups of 32 or any odd multiple of 32) every 32-k sub-block is rescaled
 // with its own scale; within a group that scale is the same, so both forms
 // compute the same sum up to rounding.
-// BUF: the buffer path for everything (GPTQ4 / AWQ4 per group with VEC, or
-// Q4_0); XB: X alone through its descriptor (k % 64 == 0), the weights
+// BUF: the buffer path for everything (k % 64 == 0; GPTQ4 / AWQ4 with VEC,
+// or Q4_0); XB: X alone through its descriptor (k % 64 == 0), the weights
 // through the general loader.
 template <int FMT, bool YF32, bool PER_GROUP, bool VEC, bool BUF, bool XB = BUF>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
@@ -463,11 +489,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
             rz = rsrc(p.zeros, (uint32_t)((p.K / p.group) * p.N));
             rs = rsrc(p.scales, (uint32_t)((p.K / p.group) * p.N * 2));
         }
-        stage_load_buf<FMT>(st, p, bo, rx, rw, rz, rs, 0, 0);
+        stage_load_buf<FMT, PER_GROUP>(st, p, bo, rx, rw, rz, rs, 0, 0, 0);
     } else {
         stage_load<FMT, VEC, XB>(st, p, m0, n0, 0, lg, lrem, bo.x, rx);
     }
-    stage_store<FMT>(st, sm, 0);
+    stage_store<FMT, !PER_GROUP>(st, sm, 0);
     __syncthreads();
 
     const int arow = wm * 64 + (lane % 32);
@@ -484,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
                 ++lg;
             }
             if constexpr (BUF)
-                stage_load_buf<FMT>(st, p, bo, rx, rw, rz, rs, (int64_t)(kt + 1) * BK, lg);
+                stage_load_buf<FMT, PER_GROUP>(st, p, bo, rx, rw, rz, rs, (int64_t)(kt + 1) * BK, lg, lrem);
             else
                 stage_load<FMT, VEC, XB>(st, p, m0, n0, (int64_t)(kt + 1) * BK, lg, lrem, bo.x, rx);
         }
@@ -512,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_int4(Args p) {
             mfma_step<false>(sm, buf, 3, arow, brow, kofs, part);
             rescale(sm.s[buf][1][scol], sm.s[buf][1][scol + 32], part, tot);
         }
-        if (kt + 1 < nk) stage_store<FMT>(st, sm, buf ^ 1);
+        if (kt + 1 < nk) stage_store<FMT, !PER_GROUP>(st, sm, buf ^ 1);
         __syncthreads();
     }
 
@@ -575,6 +601,9 @@ hipError_t run(const Args &a, bool yf32, hipStream_t s) {
             if (xb) return vec ? run3<FMT, true, true, false, true>(a, yf32, s) : run3<FMT, true, false, false, true>(a, yf32, s);
             return vec ? run3<FMT, true, true>(a, yf32, s) : run3<FMT, true, false>(a, yf32, s);
         }
+        // per-32-k path: the buffer loads pay off for GPTQ4 only (AWQ4 measured
+        // slower with them than with the general loader)
+        if (FMT == QBN_GPTQ4 && vec && a.K % BK == 0 && buf_fits(a)) return run3<FMT, false, true, true>(a, yf32, s);
         if (xb) return vec ? run3<FMT, false, true, false, true>(a, yf32, s) : run3<FMT, false, false, false, true>(a, yf32, s);
         return vec ? run3<FMT, false, true>(a, yf32, s) : run3<FMT, false, false>(a, yf32, s);
     }
