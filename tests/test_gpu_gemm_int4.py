@@ -63,10 +63,12 @@ def _inputs(seed, M, N, K, g):
 
 
 # n % 8 != 0 (70, 130) takes the element-load path for GPTQ; group 96 and 32
-# the per-32-k rescale; group a multiple of 64 the per-group rescale.
+# the per-32-k rescale; group a multiple of 64 the per-group rescale, whose
+# loads run two k-tiles ahead (one, three and five k-tiles in the last three
+# shapes: the odd tails of that two-tile loop).
 SHAPES = [(1, 40, 96, 32), (37, 72, 128, 64), (130, 264, 256, 128), (256, 256, 1024, 128), (5, 136, 4096, 4096),
           (129, 128, 160, 32), (64, 8, 2048, 256), (200, 520, 512, 512), (33, 70, 128, 32), (20, 64, 192, 96),
-          (140, 130, 384, 128), (3, 96, 576, 96)]
+          (140, 130, 384, 128), (3, 96, 576, 96), (9, 128, 64, 64), (24, 64, 192, 64), (70, 200, 320, 64)]
 
 
 @pytest.mark.parametrize("fmt", ["gptq4", "awq4", "q4_0"])
