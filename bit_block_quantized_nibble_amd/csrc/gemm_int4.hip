@@ -11,9 +11,11 @@
 // codes is decoded once per workgroup into LDS as bf16 (q - z), a small
 // integer and exact, and v_mfma_f32_32x32x16_bf16 sums X (q - z) over each
 // 32-long sub-block of k into a partial accumulator. At the end of every
-// group (every sub-block for Q4_0) the partial is multiplied by its column's
-// scale and added to the running total, so every product is exact and each
-// output sees k/16 MFMA steps plus k/group scaled additions in binary32.
+// group whose size is a multiple of 64, and otherwise at the end of every
+// 32-k sub-block (Q4_0, groups of 32, 96, ...), the partial is multiplied by
+// its column's scale and added to the running total, so every product is
+// exact and each output sees k/16 MFMA steps plus k/group (or k/32) scaled
+// additions in binary32.
 //
 // Tiling: workgroup 128 x 128 of Y, four waves in 2 x 2, each 64 x 64 (2 x 2
 // MFMA tiles); k advances 64 at a time. The next tile's X, codes, zero points
