@@ -62,13 +62,16 @@ def _inputs(seed, M, N, K, g):
     return inp
 
 
-# n % 8 != 0 (70, 130) takes the element-load path for GPTQ; group 96 and 32
-# the per-32-k rescale; group a multiple of 64 the per-group rescale, whose
-# loads run two k-tiles ahead (one, three and five k-tiles in the last three
-# shapes: the odd tails of that two-tile loop).
+# n % 8 != 0 (70, 130) takes the element-load path for GPTQ; groups of 32, 96
+# and 160 the per-32-k rescale; a group that is a multiple of 64 the
+# per-group rescale (one, three and five k-tiles in three shapes). With
+# k % 64 == 0 and n % 8 == 0, groups of 32, 96 and 160 take GPTQ's buffer
+# path, where a k-tile may span two groups and the lanes in the second add
+# one group row.
 SHAPES = [(1, 40, 96, 32), (37, 72, 128, 64), (130, 264, 256, 128), (256, 256, 1024, 128), (5, 136, 4096, 4096),
           (129, 128, 160, 32), (64, 8, 2048, 256), (200, 520, 512, 512), (33, 70, 128, 32), (20, 64, 192, 96),
-          (140, 130, 384, 128), (3, 96, 576, 96), (9, 128, 64, 64), (24, 64, 192, 64), (70, 200, 320, 64)]
+          (140, 130, 384, 128), (3, 96, 576, 96), (9, 128, 64, 64), (24, 64, 192, 64), (70, 200, 320, 64),
+          (48, 136, 256, 32), (70, 200, 640, 160)]
 
 
 @pytest.mark.parametrize("fmt", ["gptq4", "awq4", "q4_0"])
