@@ -297,7 +297,35 @@ struct X32<__bf16> {
 // values and 4 of padding, so that 16 lanes reading their blocks' pieces at
 // one index hit distinct banks). A lane's blocks (BPL of them, 64 apart) of
 // all R rows are requested before any arithmetic. Rounds of 64 * BPL blocks.
+// The first round's blocks are requested together with the workgroup's x
+// pieces, before the staging barrier, which orders LDS only, so that the two
+// memory latencies overlap instead of following one another.
 constexpr int kQ40Pitch = 36;  // floats per staged block
+constexpr int kQ40XP = 4;      // x pieces per thread issued ahead of the blocks (k <= 4096)
+
+// Workgroup barrier ordering LDS only: unlike __syncthreads it does not wait
+// for the blocks already requested.
+__device__ __forceinline__ void q40_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename XT>
+struct XPiece;  // four x values (16-byte piece c of the staged row = x[4c .. 4c+3])
+template <>
+struct XPiece<float> {
+    f32x4 v;
+    __device__ __forceinline__ void load(const float *x, int64_t c) { v = *reinterpret_cast<const f32x4 *>(x + 4 * c); }
+    __device__ __forceinline__ f32x4 f32() const { return v; }
+};
+template <>
+struct XPiece<__bf16> {
+    u32x2 v;
+    __device__ __forceinline__ void load(const __bf16 *x, int64_t c) {
+        v = ld8(reinterpret_cast<const uint16_t *>(x) + 4 * c);
+    }
+    __device__ __forceinline__ f32x4 f32() const {
+        return f32x4{__builtin_bit_cast(float, v.x << 16), __builtin_bit_cast(float, v.x & 0xFFFF0000u),
+                     __builtin_bit_cast(float, v.y << 16), __builtin_bit_cast(float, v.y & 0xFFFF0000u)};
+    }
+};
 
 // LX = false (k too long for the staging buffer): x is read from global
 // memory instead.
@@ -306,28 +334,11 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ b
                                                    float *__restrict__ y, int64_t n, int64_t k) {
     extern __shared__ __attribute__((aligned(16))) float xs[];
     const int64_t nb = k / 32;
-    // stage x: 16-byte pieces, piece p of block b at xs[36 b + 4 p]
-    for (int64_t c = threadIdx.x; LX && c < 8 * nb; c += 256) {
-        float v[4];
-        if (sizeof(XT) == 4) {
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) + 4 * c);
-            v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w;
-        } else {
-            const u32x2 a = ld8(reinterpret_cast<const uint16_t *>(x) + 4 * c);
-            v[0] = __builtin_bit_cast(float, a.x << 16), v[1] = __builtin_bit_cast(float, a.x & 0xFFFF0000u);
-            v[2] = __builtin_bit_cast(float, a.y << 16), v[3] = __builtin_bit_cast(float, a.y & 0xFFFF0000u);
-        }
-        *reinterpret_cast<f32x4 *>(xs + kQ40Pitch * (c / 8) + 4 * (c % 8)) = f32x4{v[0], v[1], v[2], v[3]};
-    }
-    __syncthreads();
     const int lane = threadIdx.x % kWave;
     const int64_t r0 = ((int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave) * R;
-    if (r0 >= n) return;  // whole waves, after the only barrier
-    float acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-    for (int64_t bb = lane; bb < nb; bb += (int64_t)kWave * BPL) {
-        Q40 blk[BPL][R];
+    // blocks bb, bb + 64, ... of rows r0 .. r0 + R - 1 (indices clamped into
+    // the matrix: waves past n and blocks past nb read valid bytes, unused)
+    auto request = [&](Q40 (&blk)[BPL][R], int64_t bb) {
 #pragma unroll
         for (int u = 0; u < BPL; ++u) {
             const int64_t b = min(bb + (int64_t)kWave * u, nb - 1);
@@ -337,6 +348,34 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ b
                 blk[u][r] = *reinterpret_cast<const Q40 *>(blocks + (row * nb + b) * 18);
             }
         }
+    };
+    // stage x: 16-byte pieces, piece p of block b at xs[36 b + 4 p]; the
+    // first kQ40XP pieces of each thread are requested before the blocks
+    const int64_t npc = LX ? 8 * nb : 0;
+    XPiece<XT> xp[kQ40XP];
+#pragma unroll
+    for (int j = 0; j < kQ40XP; ++j) {
+        const int64_t c = threadIdx.x + 256 * j;
+        if (c < npc) xp[j].load(x, c);
+    }
+    Q40 blk[BPL][R];
+    request(blk, lane);
+#pragma unroll
+    for (int j = 0; j < kQ40XP; ++j) {
+        const int64_t c = threadIdx.x + 256 * j;
+        if (c < npc) *reinterpret_cast<f32x4 *>(xs + kQ40Pitch * (c / 8) + 4 * (c % 8)) = xp[j].f32();
+    }
+    for (int64_t c = threadIdx.x + 256 * kQ40XP; c < npc; c += 256) {
+        XPiece<XT> q;
+        q.load(x, c);
+        *reinterpret_cast<f32x4 *>(xs + kQ40Pitch * (c / 8) + 4 * (c % 8)) = q.f32();
+    }
+    q40_lds_barrier();
+    if (r0 >= n) return;  // whole waves, after the only barrier
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    auto consume = [&](const Q40 (&blk)[BPL][R], int64_t bb) {
 #pragma unroll
         for (int u = 0; u < BPL; ++u) {
             const int64_t b = bb + (int64_t)kWave * u;
@@ -369,6 +408,12 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ b
                 acc[r] = fmaf(f16_bits_f32(blk[u][r].d), part, acc[r]);
             }
         }
+    };
+    consume(blk, lane);
+    for (int64_t bb = lane + (int64_t)kWave * BPL; bb < nb; bb += (int64_t)kWave * BPL) {
+        Q40 nxt[BPL][R];
+        request(nxt, bb);
+        consume(nxt, bb);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = group_sum_last<64>(acc[r]);
@@ -412,7 +457,10 @@ hipError_t run_affine(const qbn_tensor &w, const XT *x, float *y, hipStream_t s)
 
 template <typename XT>
 hipError_t run_q4_0(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
-    constexpr int R = 8, BPL = 2;
+    // two rows per wave: 11008 x 4096 in 8.7 us against 11.9 us with eight
+    // (1376 waves then hold too few requests each to cover the latency, and
+    // their arithmetic runs after the data arrives); four rows 8.9 us, one 9.0
+    constexpr int R = 2, BPL = 2;
     const int64_t waves = (w.n + R - 1) / R;
     const size_t lds = (size_t)(w.k / 32) * kQ40Pitch * sizeof(float);
     if (lds <= 64 * 1024)
