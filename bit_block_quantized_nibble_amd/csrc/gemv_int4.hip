@@ -435,17 +435,13 @@ hipError_t launch_affine(const qbn_tensor &w, const XT *x, float *y, hipStream_t
 
 template <int FMT, typename XT, bool VEC>
 hipError_t run_affine_spl(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
-    const int64_t gs = w.group / 8;  // steps per group; a round of SPL steps stays inside one
-    if (FMT == QBN_GPTQ4) {
-        // 512 threads with rounds of 4 steps measured 5% faster than 256 with
-        // rounds of 8 on the 11008 x 4096 layer (more waves over the same columns)
-        if (gs % 4 == 0) return launch_affine<FMT, XT, VEC, 512, 4>(w, x, y, s);
-        return launch_affine<FMT, XT, VEC, 512, 1>(w, x, y, s);
-    }
-    // AWQ: 512 threads (1024 would cap registers at 128 and spill)
-    if (gs % 8 == 0) return launch_affine<FMT, XT, VEC, 512, 8>(w, x, y, s);
-    if (gs % 4 == 0) return launch_affine<FMT, XT, VEC, 512, 4>(w, x, y, s);
-    return launch_affine<FMT, XT, VEC, 512, 1>(w, x, y, s);
+    // Rounds of one step (any group size), measured on the 11008 x 4096 layer
+    // against rounds of 2, 4 or 8: GPTQ with 512 threads 11.1 us (4-step
+    // rounds 11.5, 1024 threads 11.3, 256 threads 12.6); AWQ with 1024 threads
+    // 13.8 us (512 threads with 8-step rounds 14.6).
+    if constexpr (FMT == QBN_GPTQ4) return launch_affine<FMT, XT, VEC, 512, 1>(w, x, y, s);
+    else
+        return launch_affine<FMT, XT, VEC, 1024, 1>(w, x, y, s);
 }
 
 template <int FMT, typename XT>
