@@ -1,10 +1,14 @@
 #!/usr/bin/env python3
 """Throughput of the 4-bit block-quantized hot path on one MI355X.
 
-Default workload (the headline one): NVFP4 decode GEMV, W 4096 x 4096 (E2M1
-codes, E4M3FN scale per 16, f32 scale2 = 0.01), x bf16, batch 1. A step is
-one fused dequantize-and-dot over one weight matrix. The other workloads
-(--workload) measure the remaining kernels of the path on their own shapes.
+Default workload (the headline one, the largest configuration): the MXFP4
+prefill GEMM, W 8192 x 8192 (E2M1 codes, E8M0 scale per 32) times X bf16
+2048 x 8192, fp32 accumulation, Y bf16; a step is one GEMM, the metric FP4
+GEMM TFLOP/s against the dense bf16 matrix peak (the contraction runs on the
+bf16 matrix cores: the activations are bf16). The same run also times the
+two large decode GEMVs of the metric's GEMV half (Q4_K 14336 x 4096 and
+NVFP4 4096 x 4096, listed under "also"). The other workloads (--workload)
+measure the remaining kernels of the path on their own shapes.
 
 Timing. Inputs are generated on the host once and copied to HBM before the
 timed region. Each step reads its own copy of the weights, cycling through R
@@ -16,8 +20,8 @@ come from that replay. Before it, the same graph is replayed untimed until
 W steps have run (MFMA-heavy work needs ~0.1 s for its clocks to settle).
 Outside the timed region the line also gives, as context, the step time
 with one weight copy (cache-resident, not HBM) and a plain device copy's
-rate on the same box. The CPU baseline times the CPU oracle (single thread) on the
-same workload and reports it in the same unit.
+rate on the same box. The CPU baseline times the CPU oracle on the same
+workload and inputs, on one thread and on every host core, in the same unit.
 
 The per-launch duration used for the roofline is the event-timed replay
 divided by K: the graph issues the K launches back to back on one stream, so
@@ -129,21 +133,17 @@ WORKLOADS = {
         flops=2.0 * 2048 * 8192 * 8192,
         bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 * 2 + 2 * (2048 * 4096 + 2048 * 256) + 2048 * 8192 * 2,
         kernel_bytes=8192 * 4096 + 8192 * 256 + 2048 * 4096 + 2048 * 256 + 2048 * 8192 * 2),
-    "mxfp8_w4a8_gemm": dict(
-        cfg=4, kind="mxgemm", xfmt="mxfp8", unit="TFLOP/s", dtype="fp8 x fp4",
-        desc="MX-native W4A8 GEMM: OCP MX quantization of X bf16 2048x8192 to MXFP8 (E4M3) + W 8192x8192 MXFP4 on the "
-             "block-scaled FP8 x FP4 matrix cores -> Y bf16, fp32 accumulate",
-        flops=2.0 * 2048 * 8192 * 8192,
-        bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 * 2 + 2 * (2048 * 8192 + 2048 * 256) + 2048 * 8192 * 2,
-        kernel_bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 + 2048 * 256 + 2048 * 8192 * 2),
     "gptq_to_awq": dict(
         cfg=5, kind="repack", unit="GB/s", src="gptq4", dst="awq4",
         desc="int4 repack GPTQ int32 [K/8][N] -> AWQ int32 [K][N/8], K x N = 4096 x 11008",
         bytes=2 * 22544384),
     "awq_to_q4_0": dict(
         cfg=5, kind="repack", unit="GB/s", src="awq4", dst="q4_0",
-        desc="int4 repack AWQ int32 [K][N/8] + fp16 group-128 scales -> GGUF Q4_0 blocks, K x N = 4096 x 11008",
-        bytes=22544384 + 704512 + 25362432),
+        desc="int4 repack AWQ int32 [K][N/8] + fp16 group-128 scales -> GGUF Q4_0 blocks, K x N = 4096 x 11008, "
+             "every zero point 8 (the only one Q4_0 holds)",
+        bytes=22544384 + 704512 + 352256 + 25362432,
+        step_note="the step is the refusal scan of the 352,256 zero points (64 workgroups) and the repack kernel; "
+                  "the bytes count the zero points once"),
     "gptq_dequant_bf16": dict(
         cfg=5, kind="dequant", unit="GB/s",
         desc="bulk dequant GPTQ (fp16 scales, u8 zeros, group 128) -> bf16 [K][N], K x N = 4096 x 11008",
@@ -180,9 +180,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warmup steps, replayed from the captured graph (default 200; GEMM 500, "
                          "about 0.1 s, so its clocks have settled)")
-    ap.add_argument("--workload", default="nvfp4_gemv", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="mxfp4_gemm", choices=sorted(WORKLOADS))
+    ap.add_argument("--also", nargs="*", default=["q4k_gemv", "nvfp4_gemv"], choices=sorted(WORKLOADS),
+                    help="further workloads timed in the same run and listed under \"also\"")
+    ap.add_argument("--no-also", action="store_true", help="time only --workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="CPU oracle time budget (half on one thread, half on all host cores)")
     return ap.parse_args()
 
 
@@ -237,6 +241,8 @@ def build_steps(name, spec, dev):
         w = qbn.QTensor("nvfp4", n, k, host_to_device(inp["data"], dev), host_to_device(inp["scales"], dev),
                         scale2=inp["scale2"])
         Wb = qbn.dequantize(w, dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        Wbits = Wb.view(torch.int16).cpu().numpy().view(np.uint16)  # the same weight on the host, for the oracle
         wbytes = Wb.numel() * 2
         R = max(1, math.ceil(ROTATE_BYTES / wbytes))
         srcs = [Wb.clone() for _ in range(R)]
@@ -244,7 +250,7 @@ def build_steps(name, spec, dev):
         scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
         for W in srcs:
             calls.append(qbn.prepare_quantize_nvfp4(W, inp["scale2"], 0, codes, scales))
-        return calls, R, dict(inp, W=Wb), None
+        return calls, R, dict(inp, Wbits=Wbits), None
     if spec["kind"] == "int4gemm":
         K, N, g, M = inp["K"], inp["N"], inp["group"], inp["M"]
         fmt = spec["fmt"]
@@ -301,8 +307,8 @@ def build_steps(name, spec, dev):
         d0 = host_to_device(inp["data"], dev)
         s0 = host_to_device(inp["scales"], dev)
         X = host_to_device(inp["X"], dev).view(torch.bfloat16)
-        xfmt = spec.get("xfmt", "mxfp4")
-        xc = torch.empty((m, k if xfmt == "mxfp8" else k // 2), dtype=torch.uint8, device=dev)
+        xfmt = "mxfp4"
+        xc = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
         xs = torch.empty((m, k // 32), dtype=torch.uint8, device=dev)
         Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         quant = qbn.prepare_quantize_mx(X, xc, xs, xfmt)
@@ -327,11 +333,13 @@ def build_steps(name, spec, dev):
             w = qbn.QTensor("mxfp4", n, k, d0.clone(), s0.clone())
             calls.append(qbn.prepare_gemm(w, X, Y))
         return calls, R, inp, None
-    # cfg 5: repack / dequant from GPTQ (or from AWQ made by the library itself)
+    # cfg 5: repack / dequant from GPTQ (or from AWQ made by the library
+    # itself). Q4_0 holds no zero point: its leg takes every zero point as 8.
     K, N, g = inp["K"], inp["N"], inp["group"]
     qw = host_to_device(inp["qweight"], dev)
     sc = host_to_device(inp["scales"].view(np.uint16), dev)
-    zr = host_to_device(inp["zeros"], dev)
+    zeros = np.full_like(inp["zeros"], 8) if spec.get("dst") == "q4_0" else inp["zeros"]
+    zr = host_to_device(zeros, dev)
     per = spec["bytes"]
     R = max(1, math.ceil(ROTATE_BYTES / per))
     src_fmt = spec.get("src", "gptq4")
@@ -350,179 +358,209 @@ def build_steps(name, spec, dev):
                                   src.zeros, group=g)
             else:
                 dst = qbn.QTensor("q4_0", N, K, torch.empty((N, K // 32, 18), dtype=torch.uint8, device=dev))
-            calls.append(qbn.prepare_repack(src, dst))
+            status = torch.empty(qbn.REPACK_STATUS_WORDS, dtype=torch.int64, device=dev)
+            calls.append(qbn.prepare_repack(src, dst, status))
     return calls, R, inp, None
 
 
-def cpu_baseline(name, spec, inp, budget_s):
-    """Time the CPU oracle (one thread) on the same workload."""
+def oracle_unit(name, spec, inp):
+    """One unit of oracle work on the workload's own inputs: a function
+    f(rng) doing it and returning its amount in the metric's numerator (bytes
+    or flops), and a description of the unit."""
     import oracle
 
-    cores = 1
-    reps = []
-    t_end = time.perf_counter() + budget_s
-    if spec["kind"] == "w4a8":
+    kind = spec["kind"]
+    total = spec.get("flops", spec["bytes"])
+    if kind in ("gemv", "w4a8", "a16q8", "encode"):
         n, k = inp["n"], inp["k"]
-        rows = np.arange(n)
-        while True:
-            t0 = time.perf_counter()
-            q, d, _ = oracle.q8_quantize(inp["x"])
-            oracle.q4k_w4a8_rows(inp["data"], k, q, d, rows)
-            reps.append(time.perf_counter() - t0)
-            if time.perf_counter() > t_end and len(reps) >= 3:
-                break
-        t = float(np.median(reps))
-        return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
-                    sample="full quantize + %dx%d W4A8 GEMV, median of %d runs (%.2f s each)" % (n, k, len(reps), t))
-    if spec["kind"] == "a16q8":
-        n, k = inp["n"], inp["k"]
-        rows = np.arange(n)
-        while True:
-            t0 = time.perf_counter()
-            q, d, _ = oracle.q8_quantize(inp["x"])
-            oracle.nvfp4_a16q8_rows(inp["data"], inp["scales"], inp["scale2"], k, q, d, rows)
-            reps.append(time.perf_counter() - t0)
-            if time.perf_counter() > t_end and len(reps) >= 3:
-                break
-        t = float(np.median(reps))
-        return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
-                    sample="full quantize + %dx%d integer-exact NVFP4 decode, median of %d runs (%.2f s each)"
-                    % (n, k, len(reps), t))
-    if spec["kind"] == "encode":
-        import torch
-        n, k = inp["n"], inp["k"]
-        Wb = inp["W"].view(torch.int16).cpu().numpy().view(np.uint16)
-        while True:
-            t0 = time.perf_counter()
-            oracle.nvfp4_quantize(Wb, inp["scale2"], 0)
-            reps.append(time.perf_counter() - t0)
-            if time.perf_counter() > t_end and len(reps) >= 3:
-                break
-        t = float(np.median(reps))
-        return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
-                    sample="full %dx%d encode, median of %d runs (%.2f s each)" % (n, k, len(reps), t))
-    if spec["kind"] == "int4gemv":
-        K, N, g = inp["K"], inp["N"], inp["group"]
-        fmt = spec["fmt"]
-        while True:
-            t0 = time.perf_counter()
+        rows = max(1, n // 64)
+
+        def f(rng):
+            r0 = int(rng.integers(0, n - rows + 1))
+            rr = np.arange(r0, r0 + rows)
+            if kind == "gemv":
+                fmt = {"mxfp4": oracle.MXFP4, "nvfp4": oracle.NVFP4, "q4_k": oracle.Q4_K,
+                       "nvfp4_cke": oracle.NVFP4_CKE}[inp["fmt"]]
+                oracle.gemv_rows(fmt, inp["data"], inp["scales"], inp["scale2"], k, inp["x"], rr)
+            elif kind == "w4a8":
+                q, d, _ = oracle.q8_quantize(inp["x"])
+                oracle.q4k_w4a8_rows(inp["data"], k, q, d, rr)
+            elif kind == "a16q8":
+                q, d, _ = oracle.q8_quantize(inp["x"])
+                oracle.nvfp4_a16q8_rows(inp["data"], inp["scales"], inp["scale2"], k, q, d, rr)
+            else:
+                oracle.nvfp4_quantize(np.ascontiguousarray(inp["Wbits"][r0:r0 + rows]), inp["scale2"], 0)
+            return total * rows / n
+        return f, "slices of %d of the %d rows (activation quantization included where the step has it)" % (rows, n)
+    if kind == "int4gemv":
+        K, N, g, fmt = inp["K"], inp["N"], inp["group"], spec["fmt"]
+        cols = max(1, N // 64)
+
+        def f(rng):
+            c0 = int(rng.integers(0, N - cols + 1))
+            cc = np.arange(c0, c0 + cols)
             if fmt == "q4_0":
-                oracle.gemv_rows(oracle.Q4_0, inp["q4_0"], None, 1.0, K, inp["x"], np.arange(N))
+                oracle.gemv_rows(oracle.Q4_0, inp["q4_0"], None, 1.0, K, inp["x"], cc)
             else:
                 oracle.int4_gemv(fmt, inp["gptq"] if fmt == "gptq4" else inp["awq"], inp["scales"], inp["zeros"], g,
-                                 inp["x"], np.arange(N))
-            reps.append(time.perf_counter() - t0)
-            if time.perf_counter() > t_end and len(reps) >= 3:
-                break
-        t = float(np.median(reps))
-        return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
-                    sample="full %dx%d GEMV, median of %d runs (%.2f s each)" % (N, K, len(reps), t))
-    if spec["kind"] == "gemv":
-        fmt = {"mxfp4": oracle.MXFP4, "nvfp4": oracle.NVFP4, "q4_k": oracle.Q4_K,
-               "nvfp4_cke": oracle.NVFP4_CKE}[inp["fmt"]]
-        n, k = inp["n"], inp["k"]
-        rows = np.arange(n)
-        while True:
-            t0 = time.perf_counter()
-            oracle.gemv_rows(fmt, inp["data"], inp["scales"], inp["scale2"], k, inp["x"], rows)
-            reps.append(time.perf_counter() - t0)
-            if time.perf_counter() > t_end and len(reps) >= 3:
-                break
-        t = float(np.median(reps))
-        return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
-                    sample="full %dx%d GEMV, median of %d runs (%.2f s each)" % (n, k, len(reps), t))
-    if spec["kind"] == "mxgemm":
+                                 inp["x"], cc)
+            return total * cols / N
+        return f, "slices of %d of the %d outputs" % (cols, N)
+    if kind == "gemm":
         n, k, m = inp["n"], inp["k"], inp["m"]
-        rng = np.random.default_rng(0)
-        done = 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            i = int(rng.integers(0, m))
-            xf = oracle.MXFP8 if spec.get("xfmt") == "mxfp8" else oracle.MXFP4
-            xc, xs = oracle.mx_quantize(inp["X"][i:i + 1], xf)
-            nn = rng.integers(0, n, 16)
-            oracle.mx_gemm_entries(inp["data"], inp["scales"], k, xf, xc, xs, np.zeros(16, np.int64), nn)
-            done += 16
-        t = time.perf_counter() - t0
-        return dict(value=2.0 * k * done / t / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
-                    sample="%d sampled output entries (one quantized X row each 16 entries, 2k flops per entry), %.1f s"
-                    % (done, t))
-    if spec["kind"] == "int4gemm":
-        K, N, g, M = inp["K"], inp["N"], inp["group"], inp["M"]
-        fmt = spec["fmt"]
-        data = inp["q4_0"] if fmt == "q4_0" else (inp["gptq"] if fmt == "gptq4" else inp["awq"])
-        rng = np.random.default_rng(0)
-        done = 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            nn = rng.integers(0, N, 8)
-            ms_ = np.repeat(np.arange(M), nn.size)
-            ns_ = np.tile(nn, M)
-            oracle.int4_gemm_entries(fmt, data, inp["scales"], inp["zeros"], g, inp["X"], ms_, ns_)
-            done += ms_.size
-        t = time.perf_counter() - t0
-        return dict(value=2.0 * K * done / t / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
-                    sample="%d output entries (8 whole columns of the %dx%d output per oracle call, 2k flops each), "
-                    "%.1f s" % (done, M, N, t))
-    if spec["kind"] == "gemm":
-        n, k, m = inp["n"], inp["k"], inp["m"]
-        rng = np.random.default_rng(0)
-        ms_, ns_ = [], []
-        done = 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
+
+        def f(rng):
             mm = rng.integers(0, m, 16)
             nn = np.full(16, rng.integers(0, n))
             oracle.gemm_entries(oracle.MXFP4, inp["data"], inp["scales"], 1.0, k, inp["X"], mm, nn)
-            done += 16
-        t = time.perf_counter() - t0
-        return dict(value=2.0 * k * done / t / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
-                    sample="%d sampled output entries of the %dx%d output (2k flops each), %.1f s" % (done, m, n, t))
-    # repack / dequant through the oracle's logical matrix
+            return 2.0 * k * 16
+        return f, "16 output entries of one column of the %dx%d output per call (2k flops each)" % (m, n)
+    if kind == "mxgemm":
+        n, k, m = inp["n"], inp["k"], inp["m"]
+
+        def f(rng):
+            i = int(rng.integers(0, m))
+            xc, xs = oracle.mx_quantize(inp["X"][i:i + 1], oracle.MXFP4)
+            oracle.mx_gemm_entries(inp["data"], inp["scales"], k, oracle.MXFP4, xc, xs, np.zeros(16, np.int64),
+                                   rng.integers(0, n, 16))
+            return 2.0 * k * 16
+        return f, "one X row quantized and 16 of its output entries per call (2k flops each)"
+    if kind == "int4gemm":
+        K, N, g, M, fmt = inp["K"], inp["N"], inp["group"], inp["M"], spec["fmt"]
+        data = inp["q4_0"] if fmt == "q4_0" else (inp["gptq"] if fmt == "gptq4" else inp["awq"])
+
+        def f(rng):
+            nn = rng.integers(0, N, 2)
+            oracle.int4_gemm_entries(fmt, data, inp["scales"], inp["zeros"], g, inp["X"], np.repeat(np.arange(M), 2),
+                                     np.tile(nn, M))
+            return 2.0 * K * M * 2
+        return f, "2 whole columns of the %dx%d output per call (2k flops per entry)" % (M, N)
+    # repack / dequant through the oracle's logical matrix, on a slice of the
+    # K x N matrix (whole groups, whole 8-column words)
     K, N, g = inp["K"], inp["N"], inp["group"]
-    while True:
-        t0 = time.perf_counter()
-        q = oracle.gptq_unpack(inp["qweight"])
-        if spec["kind"] == "dequant":
-            w = oracle.affine_dequant(q, inp["scales"].view(np.uint16), inp["zeros"], g)
-            oracle.bf16_rne_array(w)
+    cols = 8 * max(1, N // 8 // 64)
+    qw, sc, zr = inp["qweight"], inp["scales"].view(np.uint16), inp["zeros"]
+
+    def f(rng):
+        c0 = 8 * int(rng.integers(0, (N - cols) // 8 + 1))
+        q = oracle.gptq_unpack(np.ascontiguousarray(qw[:, c0:c0 + cols]))
+        if kind == "dequant":
+            oracle.bf16_rne_array(oracle.affine_dequant(q, np.ascontiguousarray(sc[:, c0:c0 + cols]),
+                                                        np.ascontiguousarray(zr[:, c0:c0 + cols]), g))
         elif spec["dst"] == "awq4":
             oracle.awq_pack(q)
         else:
-            d = np.ascontiguousarray(np.repeat(inp["scales"].view(np.uint16).T, g // 32, axis=1))
-            oracle.q4_0_pack(q, d)
-        reps.append(time.perf_counter() - t0)
-        if time.perf_counter() > t_end or len(reps) >= 5:
-            break
-    t = float(np.median(reps))
-    return dict(value=spec["bytes"] / t / 1e9, unit="GB/s", cores=cores, kind="oracle",
-                sample="full %dx%d %s, median of %d runs (%.2f s each)" % (K, N, name, len(reps), t))
+            oracle.q4_0_pack(q, np.ascontiguousarray(np.repeat(sc[:, c0:c0 + cols].T, g // 32, axis=1)))
+        return total * cols / N
+    return f, "slices of %d of the %d columns of the %dx%d matrix" % (cols, N, K, N)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the GEMV would shard by output rows). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+def _oracle_rate(f, seconds, threads):
+    """Run f repeatedly on `threads` host threads for about `seconds` (the
+    oracle's C calls release the interpreter lock); returns (amount done,
+    elapsed seconds, calls)."""
+    import concurrent.futures as cf
+
+    t0 = time.perf_counter()
+    deadline = t0 + seconds
+
+    def worker(seed):
+        rng = np.random.default_rng(seed)
+        amount, calls = 0.0, 0
+        while True:
+            amount += f(rng)
+            calls += 1
+            if time.perf_counter() >= deadline:
+                return amount, calls, time.perf_counter()
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(worker, range(threads)))
+    return sum(r[0] for r in res), max(r[2] for r in res) - t0, sum(r[1] for r in res)
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(name, spec, inp, budget_s):
+    """The oracle as it stands, timed on the host: first on one thread, then
+    on every core this process may use (rows / columns / entries dealt to
+    threads), each for half the budget, on the workload's own inputs."""
+    f, what = oracle_unit(name, spec, inp)
+    unit = spec["unit"]
+    scale = 1e9 if unit == "GB/s" else 1e12
+    amount1, t1, calls1 = _oracle_rate(f, budget_s / 2, 1)
+    cores = host_cores()
+    amount, t, calls = _oracle_rate(f, budget_s / 2, cores)
+    return dict(value=round(amount / t / scale, 6), unit=unit, cores=cores, kind="oracle",
+                sample="%s: %d calls in %.1f s on %d threads" % (what, calls, t, cores),
+                one_core=dict(value=round(amount1 / t1 / scale, 6), cores=1,
+                              sample="%d calls in %.1f s on one thread" % (calls1, t1)),
+                cpu=cpu_model())
+
+
+def environment():
+    """What the numbers were taken on: GPU, clocks, ROCm and build flags."""
+    import subprocess
+
     import torch
 
-    import bit_block_quantized_nibble_amd as qbn
+    from bit_block_quantized_nibble_amd import build as qbn_build
 
-    if not os.path.exists(qbn.lib_path()):
-        import __graft_entry__
+    props = torch.cuda.get_device_properties(0)
+    env = {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+           "compute_units": props.multi_processor_count, "torch": torch.__version__, "hip": torch.version.hip,
+           "hipcc_flags": " ".join(f for f in qbn_build.CFLAGS if not f.startswith("-I")),
+           "host_cpu": cpu_model(), "host_cores": host_cores()}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            env["rocm"] = fh.read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        clocks = [ln.strip() for ln in r.stdout.splitlines() if "clock level" in ln.lower() or "sclk" in ln.lower()
+                  or "mclk" in ln.lower()]
+        env["clocks"] = clocks[:8] if clocks else None
+    except (OSError, subprocess.SubprocessError):
+        env["clocks"] = None
+    return env
 
-        __graft_entry__.build()
-    spec = WORKLOADS[args.workload]
-    steps = args.steps or (50 if spec["kind"] in ("gemm", "int4gemm") else 200 if spec["kind"] == "mxgemm" else 2000)
-    warmup = args.warmup if args.warmup is not None else (500 if spec["kind"] in ("gemm", "mxgemm", "int4gemm")
-                                                          else 200)
-    dev = torch.device("cuda:0")
-    calls, R, inp, kcalls = build_steps(args.workload, spec, dev)
+
+def default_steps(kind):
+    return 50 if kind in ("gemm", "int4gemm") else 200 if kind == "mxgemm" else 2000
+
+
+def default_warmup(kind):
+    return 500 if kind in ("gemm", "mxgemm", "int4gemm") else 200
+
+
+def measure(name, steps, warmup, dev):
+    """Capture `steps` steps of the workload in one HIP graph, warm up by
+    replaying it, time one replay between events (plus four more for the
+    spread), and take the context figures (one weight copy; device copy)."""
+    import torch
+
+    spec = WORKLOADS[name]
+    steps = steps or default_steps(spec["kind"])
+    warmup = warmup if warmup is not None else default_warmup(spec["kind"])
+    calls, R, inp, kcalls = build_steps(name, spec, dev)
     torch.cuda.synchronize()
 
-    # capture the K timed steps into one graph, then warm up (untimed) by
-    # replaying it until at least W steps have run
     for i in range(min(R, 3)):
         calls[i]()
     torch.cuda.synchronize()
@@ -543,11 +581,8 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / steps
+    ms_step = e0.elapsed_time(e1) / steps
 
-    # Further replays of the same graph give the spread of the per-launch
-    # duration (the first replay above is the reported measurement).
     spread = []
     for _ in range(4):
         a = torch.cuda.Event(enable_timing=True)
@@ -576,10 +611,6 @@ def main():
         kernel_ms = a.elapsed_time(b) / steps
         del kg
 
-    # Context, outside the timed region: the same step with one weight copy
-    # (cache-resident after the first launch: MALL / L2, not HBM), and a plain
-    # device-to-device copy of the step's bytes (read + write) as the
-    # practical bandwidth ceiling on this machine.
     warm = torch.cuda.CUDAGraph()
     with torch.cuda.graph(warm):
         for i in range(steps):
@@ -611,67 +642,97 @@ def main():
     b.record()
     torch.cuda.synchronize()
     copy_gbs = 2 * half / (a.elapsed_time(b) / csteps * 1e-3) / 1e9
-    del cg, bufs
+    del cg, bufs, graph, calls, kcalls
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
     if spec["kind"] in ("gemm", "mxgemm", "int4gemm"):
-        peak = BF16_MFMA_PEAK_TFLOPS if spec["kind"] in ("gemm", "int4gemm") else (
-            FP8_MFMA_PEAK_TFLOPS if spec.get("xfmt") == "mxfp8" else FP4_MFMA_PEAK_TFLOPS)
+        peak = BF16_MFMA_PEAK_TFLOPS if spec["kind"] in ("gemm", "int4gemm") else FP4_MFMA_PEAK_TFLOPS
         value = spec["flops"] / (ms_step * 1e-3) / 1e12
         achieved = spec["flops"] / (kernel_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4), traffic=recorded_traffic(args.workload))
-        metric = "FP8 x FP4 GEMM TFLOP/s (% MFMA peak)" if spec.get("xfmt") == "mxfp8" else (
-            "int4 GEMM TFLOP/s (% MFMA peak)" if spec["kind"] == "int4gemm" else "FP4 GEMM TFLOP/s (% MFMA peak)")
+                    frac=round(achieved / peak, 4), traffic=recorded_traffic(name))
+        metric = "int4 GEMM TFLOP/s (% MFMA peak)" if spec["kind"] == "int4gemm" else "FP4 GEMM TFLOP/s (% MFMA peak)"
     else:
         value = spec["bytes"] / (ms_step * 1e-3) / 1e9
         achieved = spec.get("kernel_bytes", spec["bytes"]) / (kernel_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=recorded_traffic(args.workload))
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=recorded_traffic(name))
         metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] in ("gemv", "w4a8", "a16q8", "int4gemv") else \
             "NVFP4 encode GB/s (% HBM peak)" if spec["kind"] == "encode" else (
             "int4 repack GB/s (% HBM peak)" if spec["kind"] == "repack" else "bulk dequant GB/s (% HBM peak)")
+    config = {
+        "workload": spec["desc"],
+        "name": name,
+        "seed": int(inp["seed"]),
+        "rotating_copies": R,
+        "step_bytes": spec["bytes"],
+        **({"step_flops": spec["flops"]} if "flops" in spec else {}),
+        **({"kernel_bytes": spec["kernel_bytes"], "kernel_note": spec.get("kernel_note", "roofline is the dominant "
+            "kernel alone, timed in its own graph of K launches; value is the whole step")}
+           if "kernel_bytes" in spec else {}),
+        **({"step_note": spec["step_note"]} if "step_note" in spec else {}),
+        "kernel_ms_per_launch": round(kernel_ms, 6),
+        "kernel_ms_other_replays": [round(v, 6) for v in spread],
+        "cache_resident_ms_per_launch": round(warm_ms, 6),
+        "cache_resident_note": "one weight copy reused: served from MALL/L2, not HBM (context only)",
+        "device_copy_gbs": round(copy_gbs, 1),
+        "device_copy_note": "plain device-to-device copy of the step's byte count, read + write (context only)",
+        **({"fp4_peak_frac": round(spec["flops"] / (kernel_ms * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS, 4)}
+           if spec["kind"] == "gemm" else {}),
+        "timed_wall_s": round(wall, 4),
+    }
+    return dict(name=name, spec=spec, inp=inp, steps=steps, warmup=warmup, ms_step=ms_step, value=value,
+                metric=metric, roofline=roof, config=config)
 
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: nothing in this library uses a second GPU "
+              "(the GEMV would shard by output rows, the GEMM by output columns). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_block_quantized_nibble_amd as qbn
+
+    if not os.path.exists(qbn.lib_path()):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    env = environment()
+    dev = torch.device("cuda:0")
+    main_r = measure(args.workload, args.steps, args.warmup, dev)
+    also = []
+    for other in ([] if args.no_also else args.also):
+        if other == args.workload:
+            continue
+        r = measure(other, 0, None, dev)
+        also.append({"name": other, "metric": r["metric"], "value": round(r["value"], 2), "unit": r["spec"]["unit"],
+                     "steps": r["steps"], "ms_per_step": round(r["ms_step"], 6), "roofline": r["roofline"],
+                     "workload": r["spec"]["desc"]})
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.workload, spec, inp, args.cpu_seconds)
-
+        cpu = cpu_baseline(args.workload, main_r["spec"], main_r["inp"], args.cpu_seconds)
+    spec = main_r["spec"]
     line = {
-        "metric": metric,
-        "value": round(value, 2),
+        "metric": main_r["metric"],
+        "value": round(main_r["value"], 2),
         "unit": spec["unit"],
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": round(ms_step, 6),
+        "steps": main_r["steps"],
+        "warmup": main_r["warmup"],
+        "ms_per_step": round(main_r["ms_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": spec.get("dtype", "f32"),
         "data": "synthetic",
-        "config": {
-            "workload": spec["desc"],
-            "name": args.workload,
-            "seed": int(inp["seed"]),
-            "rotating_copies": R,
-            "step_bytes": spec["bytes"],
-            **({"step_flops": spec["flops"]} if "flops" in spec else {}),
-            **({"kernel_bytes": spec["kernel_bytes"], "kernel_note": "roofline is the dominant kernel alone, timed "
-                "in its own graph of K launches; value is the whole step (activation quantization + the kernel)"}
-               if "kernel_bytes" in spec else {}),
-            "kernel_ms_per_launch": round(kernel_ms, 6),
-            "kernel_ms_other_replays": [round(v, 6) for v in spread],
-            "cache_resident_ms_per_launch": round(warm_ms, 6),
-            "cache_resident_note": "one weight copy reused: served from MALL/L2, not HBM (context only)",
-            "device_copy_gbs": round(copy_gbs, 1),
-            "device_copy_note": "plain device-to-device copy of the step's byte count, read + write (context only)",
-            **({"fp4_peak_frac": round(spec["flops"] / (kernel_ms * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS, 4)}
-               if "flops" in spec and spec.get("xfmt") != "mxfp8" else {}),
-            "timed_wall_s": round(wall, 4),
-            "gpu": torch.cuda.get_device_name(0),
-            "host": platform.processor() or platform.machine(),
-        },
-        "roofline": roof,
+        "config": {**main_r["config"], "environment": env},
+        "roofline": main_r["roofline"],
         "cpu_baseline": cpu,
+        "also": also,
     }
     print(json.dumps(line))
 

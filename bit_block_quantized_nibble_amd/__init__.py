@@ -2,8 +2,10 @@
 block-quantized weights (MXFP4, NVFP4, Q4_K), bulk dequantization of six
 formats and bit-exact int4 layout repacks, on AMD MI355X (gfx950).
 
-This module only marshals arguments: it turns torch device tensors into raw
-pointers, passes torch's current HIP stream, and raises on a nonzero status.
+This module only marshals arguments: it checks that every tensor is a
+device tensor holding at least the bytes the call will touch (the C ABI
+takes raw pointers and cannot), turns the tensors into raw pointers, passes
+torch's current HIP stream, and raises on a nonzero status.
 Every step of the computation runs in the HIP kernels of libqbn.so; there is
 no CPU or PyTorch fallback. The names mirror the C ABI in include/qbn.h
 (``qbn_quantized_gemv`` -> ``quantized_gemv`` and so on).
@@ -19,13 +21,14 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "QTensor", "QbnError", "quantized_gemv", "quantized_gemm", "dequantize", "repack", "validate", "nbytes",
-    "status_string", "lib_path", "FORMATS", "Prepared", "prepare_gemv", "prepare_gemm", "prepare_dequantize",
-    "prepare_repack",
+    "QTensor", "QbnError", "RepackRefused", "quantized_gemv", "quantized_gemm", "dequantize", "repack", "validate",
+    "validate_async", "nbytes", "status_string", "lib_path", "FORMATS", "Prepared", "prepare_gemv", "prepare_gemm",
+    "prepare_dequantize", "prepare_repack",
 ]
 
 FORMATS = {"mxfp4": 1, "nvfp4": 2, "q4_k": 3, "q4_0": 4, "gptq4": 5, "awq4": 6, "nvfp4_cke": 8}
 _F32, _BF16, _F16 = 0, 1, 2
+REPACK_STATUS_WORDS = 65  # QBN_REPACK_STATUS_WORDS: the result word and the refusal scan's 64 partial results
 _DTYPES = {torch.float32: _F32, torch.bfloat16: _BF16, torch.float16: _F16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +38,7 @@ _lib = None
 
 EXPORTED = (
     "qbn_abi_version", "qbn_tensor_struct_size", "qbn_status_string", "qbn_last_hip_error", "qbn_bytes",
-    "qbn_quantized_gemv", "qbn_quantized_gemm", "qbn_dequantize", "qbn_repack", "qbn_validate",
+    "qbn_quantized_gemv", "qbn_quantized_gemm", "qbn_dequantize", "qbn_repack", "qbn_validate", "qbn_validate_async",
     "qbn_quantize_q8", "qbn_quantized_gemv_q8", "qbn_quantize_mx", "qbn_quantized_gemm_mx",
     "qbn_gptq_qzeros", "qbn_gptq_resolve_g_idx", "qbn_permute",
     "qbn_quantize_nvfp4", "qbn_quantize_int4_sym", "qbn_pack_bits", "qbn_unpack_bits",
@@ -49,6 +52,17 @@ class QbnError(RuntimeError):
         if status == 9:
             detail += " (hipError %d)" % _load().qbn_last_hip_error()
         super().__init__("%s: qbn status %d: %s" % (where, status, detail))
+
+
+class RepackRefused(ValueError):
+    """A Q4_0 repack found a weight the target cannot hold exactly (a zero
+    point other than 8, or a group whose Q4_0 blocks disagree on d); nothing
+    was written to the destination. `index` is the first offending index."""
+
+    def __init__(self, index: int, what: str):
+        self.index = index
+        super().__init__("repack refused: %s (first offending index %d); the destination is untouched"
+                         % (what, index))
 
 
 class _CTensor(ctypes.Structure):
@@ -87,7 +101,7 @@ def _load():
         lib.qbn_quantized_gemm.restype = I32
         lib.qbn_dequantize.argtypes = [T, P, I32, I32, P]
         lib.qbn_dequantize.restype = I32
-        lib.qbn_repack.argtypes = [T, I32, I32, P, P, P, P]
+        lib.qbn_repack.argtypes = [T, T, P, P]
         lib.qbn_repack.restype = I32
         lib.qbn_gptq_qzeros.argtypes = [P, P, I64, I64, I32, I32, P]
         lib.qbn_gptq_qzeros.restype = I32
@@ -103,8 +117,10 @@ def _load():
         lib.qbn_pack_bits.restype = I32
         lib.qbn_unpack_bits.argtypes = [P, P, I64, I32, I32, P, P]
         lib.qbn_unpack_bits.restype = I32
-        lib.qbn_validate.argtypes = [T, P, P]
+        lib.qbn_validate.argtypes = [T, ctypes.POINTER(ctypes.c_int64), P]
         lib.qbn_validate.restype = I32
+        lib.qbn_validate_async.argtypes = [T, P, P]
+        lib.qbn_validate_async.restype = I32
         lib.qbn_quantize_q8.argtypes = [P, I32, I64, P, P, P, P]
         lib.qbn_quantize_q8.restype = I32
         lib.qbn_quantized_gemv_q8.argtypes = [T, P, P, P, P, I32, P]
@@ -113,7 +129,7 @@ def _load():
         lib.qbn_quantize_mx.restype = I32
         lib.qbn_quantized_gemm_mx.argtypes = [T, I64, I32, P, P, P, I32, I64, P]
         lib.qbn_quantized_gemm_mx.restype = I32
-        if lib.qbn_abi_version() != 1 or lib.qbn_tensor_struct_size() != ctypes.sizeof(_CTensor):
+        if lib.qbn_abi_version() != 2 or lib.qbn_tensor_struct_size() != ctypes.sizeof(_CTensor):
             raise RuntimeError("libqbn ABI mismatch: rebuild the library")
         _lib = lib
         return lib
@@ -127,6 +143,23 @@ def _ptr(t: Optional[torch.Tensor], name: str):
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: Optional[torch.Tensor], nbytes: int, name: str):
+    """Refuse, before any launch, a tensor that holds fewer bytes than the
+    call will read or write through its pointer."""
+    if nbytes <= 0:
+        return
+    if t is None:
+        raise ValueError("%s is required" % name)
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError("%s holds %d bytes; the call needs %d" % (name, have, nbytes))
+
+
+def _need_dtype(t: torch.Tensor, dtypes, name: str):
+    if t.dtype not in dtypes:
+        raise TypeError("%s dtype %s (expected %s)" % (name, t.dtype, ", ".join(str(d) for d in dtypes)))
 
 
 def _stream(device: torch.device) -> ctypes.c_void_p:
@@ -153,9 +186,21 @@ class QTensor:
     scale2: float = 1.0
     group: int = 0
 
-    def _c(self) -> _CTensor:
+    def check_sizes(self):
+        """Every buffer must hold the bytes of its part (the library reads
+        them through raw pointers and cannot check)."""
         if self.format not in FORMATS:
             raise ValueError("unknown format %r" % self.format)
+        grp = int(self.group) if self.format in ("gptq4", "awq4") else 0
+        for part, t, name in ((0, self.data, "data"), (1, self.scales, "scales"), (2, self.zeros, "zeros")):
+            need = nbytes(self.format, int(self.n), int(self.k), grp, part)
+            if need < 0:
+                break  # invalid shape or group: the library reports it
+            if t is not None or need > 0:
+                _need(t, need, name)
+
+    def _c(self) -> _CTensor:
+        self.check_sizes()
         c = _CTensor()
         c.format = FORMATS[self.format]
         c.group = int(self.group)
@@ -196,8 +241,10 @@ def gptq_qzeros(src: torch.Tensor, version: int, to_logical: bool, n: int,
     if dst is None:
         dst = (torch.empty((groups, n), dtype=torch.uint8, device=src.device) if to_logical
                else torch.empty((groups, n // 8), dtype=torch.int32, device=src.device))
+    _need(src, groups * (n // 2 if to_logical else n), "src")
+    _need(dst, groups * (n if to_logical else n // 2), "dst")
     _check(lib.qbn_gptq_qzeros(_ptr(src, "src"), _ptr(dst, "dst"), groups, n, int(version), int(bool(to_logical)),
-                               _stream(src.device)), "qbn_gptq_qzeros")
+                               _stream(src.device)), "qbn_gptq_qzeros")  # sizes checked above
     return dst
 
 
@@ -209,6 +256,8 @@ def gptq_resolve_g_idx(qweight: torch.Tensor, g_idx: torch.Tensor, group: int):
     out = torch.empty_like(qweight)
     perm = torch.empty(k, dtype=torch.int32, device=qweight.device)
     status = torch.empty(1, dtype=torch.int32, device=qweight.device)
+    _need(qweight, (k // 8) * n * 4, "qweight")
+    _need(g_idx, 4 * k, "g_idx")
     _check(lib.qbn_gptq_resolve_g_idx(_ptr(qweight, "qweight"), _ptr(g_idx, "g_idx"), k, n, int(group),
                                       _ptr(out, "qweight_out"), _ptr(perm, "perm"), _ptr(status, "status"),
                                       _stream(qweight.device)), "qbn_gptq_resolve_g_idx")
@@ -222,6 +271,8 @@ def permute(src: torch.Tensor, perm: torch.Tensor, dst: Optional[torch.Tensor] =
         raise TypeError("src dtype %s" % src.dtype)
     if dst is None:
         dst = torch.empty_like(src)
+    _need(perm, 4 * src.numel(), "perm")
+    _need(dst, src.numel() * src.element_size(), "dst")
     _check(lib.qbn_permute(_ptr(src, "src"), _ptr(perm, "perm"), src.numel(), _DTYPES[src.dtype], _ptr(dst, "dst"),
                            _stream(src.device)), "qbn_permute")
     return dst
@@ -277,6 +328,10 @@ def unpack_bits(words_lo: torch.Tensor, words_hi: Optional[torch.Tensor], count:
                 lo_bits: int = 0) -> torch.Tensor:
     lib = _load()
     out = torch.empty(count, dtype=torch.uint8, device=words_lo.device)
+    w0 = lo_bits if lo_bits else bits
+    _need(words_lo, 4 * ((count * w0 + 31) // 32), "words_lo")
+    if lo_bits:
+        _need(words_hi, 4 * ((count * (bits - lo_bits) + 31) // 32), "words_hi")
     _check(lib.qbn_unpack_bits(_ptr(words_lo, "words_lo"), _ptr(words_hi, "words_hi"), count, int(bits),
                                int(lo_bits), _ptr(out, "values"), _stream(words_lo.device)), "qbn_unpack_bits")
     return out
@@ -285,10 +340,12 @@ def unpack_bits(words_lo: torch.Tensor, words_hi: Optional[torch.Tensor], count:
 def quantized_gemv(w: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = W_hat @ x (float32 [n]) for x float32 or bfloat16 [k]."""
     lib = _load()
-    if x.dtype not in _DTYPES:
-        raise TypeError("x dtype %s" % x.dtype)
+    _need_dtype(x, (torch.float32, torch.bfloat16), "x")
     if y is None:
         y = torch.empty(w.n, dtype=torch.float32, device=w.device)
+    _need_dtype(y, (torch.float32,), "y")
+    _need(x, w.k * x.element_size(), "x")
+    _need(y, w.n * 4, "y")
     ct = w._c()
     _check(lib.qbn_quantized_gemv(ctypes.byref(ct), _ptr(x, "x"), _DTYPES[x.dtype], _ptr(y, "y"),
                                   _DTYPES.get(y.dtype, -1), _stream(w.device)), "qbn_quantized_gemv")
@@ -309,6 +366,9 @@ def quantize_q8(x: torch.Tensor, q: Optional[torch.Tensor] = None, d: Optional[t
         d = torch.empty(k // 256, dtype=torch.float32, device=x.device)
     if bsums is None:
         bsums = torch.empty(k // 32, dtype=torch.int32, device=x.device)
+    _need(q, k, "q")
+    _need(d, 4 * (k // 256), "d")
+    _need(bsums, 4 * (k // 32), "bsums")
     _check(lib.qbn_quantize_q8(_ptr(x, "x"), _DTYPES[x.dtype], k, _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"),
                                _stream(x.device)), "qbn_quantize_q8")
     return q, d, bsums
@@ -323,11 +383,21 @@ def quantized_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: Optio
     lib = _load()
     if y is None:
         y = torch.empty(w.n, dtype=torch.float32, device=w.device)
+    _check_gemv_q8(w, q, d, bsums, y)
     ct = w._c()
     _check(lib.qbn_quantized_gemv_q8(ctypes.byref(ct), _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"),
                                      _ptr(y, "y"), _DTYPES.get(y.dtype, -1), _stream(w.device)),
            "qbn_quantized_gemv_q8")
     return y
+
+
+def _check_gemv_q8(w, q, d, bsums, y):
+    _need(q, w.k, "q")
+    _need(d, 4 * (w.k // 256), "d")
+    if w.format == "q4_k":
+        _need(bsums, 4 * (w.k // 32), "bsums")
+    _need_dtype(y, (torch.float32, torch.float16), "y")
+    _need(y, w.n * y.element_size(), "y")
 
 
 MX_FORMATS = {"mxfp4": 1, "mxfp8": 7}
@@ -342,13 +412,15 @@ def quantize_mx(x: torch.Tensor, fmt: str = "mxfp4", codes: Optional[torch.Tenso
         raise TypeError("x dtype %s" % x.dtype)
     if x.dim() == 1:
         x = x.unsqueeze(0)
-    if not x.is_cuda or x.stride(1) != 1:
-        raise ValueError("x must be a device tensor with contiguous rows")
     m, k = x.shape
     if codes is None:
         codes = torch.empty((m, k // 2 if fmt == "mxfp4" else k), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    _need(codes, m * (k // 2 if fmt == "mxfp4" else k), "codes")
+    _need(scales, m * (k // 32), "scales")
+    if not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a device tensor with contiguous rows")
     _check(lib.qbn_quantize_mx(ctypes.c_void_p(x.data_ptr()), _DTYPES[x.dtype], m, k, x.stride(0), MX_FORMATS[fmt],
                                _ptr(codes, "codes"), _ptr(scales, "scales"), _stream(x.device)), "qbn_quantize_mx")
     return codes, scales
@@ -363,6 +435,7 @@ def quantized_gemm_mx(w: QTensor, xcodes: torch.Tensor, xscales: torch.Tensor, f
     m = xcodes.shape[0]
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.bfloat16, device=w.device)
+    _check_gemm_mx(w, m, xcodes, xscales, y, fmt)
     if not y.is_cuda or y.stride(1) != 1:
         raise ValueError("y must be a device tensor with contiguous rows")
     ct = w._c()
@@ -370,6 +443,20 @@ def quantized_gemm_mx(w: QTensor, xcodes: torch.Tensor, xscales: torch.Tensor, f
                                      _ptr(xscales, "xscales"), ctypes.c_void_p(y.data_ptr()), _DTYPES.get(y.dtype, -1),
                                      y.stride(0), _stream(w.device)), "qbn_quantized_gemm_mx")
     return y
+
+
+def _check_gemm_mx(w, m, xcodes, xscales, y, fmt):
+    _need(xcodes, m * (w.k // 2 if fmt == "mxfp4" else w.k), "xcodes")
+    _need(xscales, m * (w.k // 32), "xscales")
+    _check_rows(y, m, w.n, "y")
+
+
+def _check_rows(t: torch.Tensor, rows: int, cols: int, name: str):
+    """A [rows][>= cols] matrix with contiguous rows (leading dimension = stride 0)."""
+    if rows == 0 or cols == 0:
+        return
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError("%s must be at least [%d][%d], got %s" % (name, rows, cols, tuple(t.shape)))
 
 
 def quantized_gemm(w: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -381,6 +468,8 @@ def quantized_gemm(w: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None
     m = x.shape[0]
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.bfloat16, device=w.device)
+    _check_rows(x, m, w.k, "x")
+    _check_rows(y, m, w.n, "y")
     if not (x.is_cuda and y.is_cuda):
         raise ValueError("x and y must be device (cuda) tensors")
     ct = w._c()
@@ -402,72 +491,97 @@ def dequantize(w: QTensor, out: Optional[torch.Tensor] = None, dtype: torch.dtyp
     if out is None:
         shape = (w.n, w.k) if lay == 0 else (w.k, w.n)
         out = torch.empty(shape, dtype=dtype, device=w.device)
+    _need_dtype(out, (torch.float32, torch.bfloat16), "out")
+    _need(out, w.n * w.k * out.element_size(), "out")
     ct = w._c()
     _check(lib.qbn_dequantize(ctypes.byref(ct), _ptr(out, "out"), _DTYPES.get(out.dtype, -1), lay,
                               _stream(w.device)), "qbn_dequantize")
     return out
 
 
-def repack(src: QTensor, dst_format: str, dst_group: Optional[int] = None, data: Optional[torch.Tensor] = None,
-           scales: Optional[torch.Tensor] = None, zeros: Optional[torch.Tensor] = None) -> QTensor:
-    """Repack int4 codes between GPTQ4, AWQ4 and Q4_0, or NVFP4 codes between
-    the adjacent-pair and CKE split-half layouts (bit-exact)."""
-    lib = _load()
+def repack_target(src: QTensor, dst_format: str, dst_group: Optional[int] = None,
+                  data: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                  zeros: Optional[torch.Tensor] = None) -> QTensor:
+    """The destination tensor of a repack of src into dst_format: the given
+    buffers, the others allocated (GPTQ4 <-> AWQ4 share src's scales and zero
+    points unless new ones are given)."""
     n, k, dev = src.n, src.k, src.device
-    fmt = FORMATS[dst_format]
     if dst_format in ("nvfp4", "nvfp4_cke"):
         if data is None:
             data = (torch.empty((n, k // 2), dtype=torch.uint8, device=dev) if dst_format == "nvfp4"
                     else torch.empty((n, k // 64, 36), dtype=torch.uint8, device=dev))
         if dst_format == "nvfp4" and scales is None:
             scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
-        if dst_format == "nvfp4_cke":
-            scales = None
-        ct = src._c()
-        _check(lib.qbn_repack(ctypes.byref(ct), fmt, 0, _ptr(data, "data"), _ptr(scales, "scales"), None,
-                              _stream(dev)), "qbn_repack")
-        return QTensor(dst_format, n, k, data, scales, scale2=src.scale2)
-    if dst_group is None:
-        dst_group = src.group if dst_format != "q4_0" else 0
+        return QTensor(dst_format, n, k, data, scales if dst_format == "nvfp4" else None, scale2=src.scale2)
+    if dst_format not in ("gptq4", "awq4", "q4_0"):
+        raise ValueError("repack target must be gptq4, awq4, q4_0, nvfp4 or nvfp4_cke")
     if data is None:
         if dst_format == "gptq4":
             data = torch.empty((k // 8, n), dtype=torch.int32, device=dev)
         elif dst_format == "awq4":
             data = torch.empty((k, n // 8), dtype=torch.int32, device=dev)
-        elif dst_format == "q4_0":
+        else:
             data = torch.empty((n, k // 32, 18), dtype=torch.uint8, device=dev)
-        else:
-            raise ValueError("repack target must be gptq4, awq4 or q4_0")
-    if dst_format in ("gptq4", "awq4"):
-        g = dst_group
-        if src.format == "q4_0":
-            if scales is None:
-                scales = torch.empty((k // g, n), dtype=torch.float16, device=dev)
-            if zeros is None:
-                zeros = torch.empty((k // g, n), dtype=torch.uint8, device=dev)
-        else:
-            if scales is None:
-                scales = src.scales
-            if zeros is None:
-                zeros = src.zeros
-    ct = src._c()
-    pass_scales = scales if (scales is not None and scales is not src.scales) else None
-    pass_zeros = zeros if (zeros is not None and zeros is not src.zeros) else None
-    _check(lib.qbn_repack(ctypes.byref(ct), fmt, int(dst_group), _ptr(data, "data"), _ptr(pass_scales, "scales"),
-                          _ptr(pass_zeros, "zeros"), _stream(dev)), "qbn_repack")
     if dst_format == "q4_0":
         return QTensor("q4_0", n, k, data)
-    return QTensor(dst_format, n, k, data, scales, zeros, group=dst_group)
+    g = dst_group if dst_group is not None else src.group
+    if src.format == "q4_0":
+        if scales is None:
+            scales = torch.empty((k // g, n), dtype=torch.float16, device=dev)
+        if zeros is None:
+            zeros = torch.empty((k // g, n), dtype=torch.uint8, device=dev)
+    else:
+        scales = src.scales if scales is None else scales
+        zeros = src.zeros if zeros is None else zeros
+    return QTensor(dst_format, n, k, data, scales, zeros, group=g)
+
+
+def repack(src: QTensor, dst_format: str, dst_group: Optional[int] = None, data: Optional[torch.Tensor] = None,
+           scales: Optional[torch.Tensor] = None, zeros: Optional[torch.Tensor] = None) -> QTensor:
+    """Repack int4 codes between GPTQ4, AWQ4 and Q4_0, or NVFP4 codes between
+    the adjacent-pair and CKE split-half layouts (bit-exact). The Q4_0
+    directions fail closed: if a weight cannot be held exactly by the target
+    (a zero point other than 8; Q4_0 blocks of one target group with
+    different d) nothing is written and RepackRefused is raised; this waits
+    for the stream to read the device-side verdict."""
+    lib = _load()
+    dst = repack_target(src, dst_format, dst_group, data, scales, zeros)
+    src.check_sizes()
+    dst.check_sizes()
+    status = torch.empty(REPACK_STATUS_WORDS, dtype=torch.int64, device=src.device)
+    cs, cd = src._c(), dst._c()
+    _check(lib.qbn_repack(ctypes.byref(cs), ctypes.byref(cd), _ptr(status, "status"), _stream(src.device)),
+           "qbn_repack")
+    if "q4_0" in (src.format, dst_format):
+        bad = int(status[0].item())
+        if bad >= 0:
+            raise RepackRefused(bad, "a zero point other than 8" if dst_format == "q4_0"
+                                else "Q4_0 blocks of one target group with different d")
+    return dst
 
 
 def validate(w: QTensor) -> int:
-    """Fail-closed load-time scan; returns the first bad index or -1.
-    Synchronizes the current stream to read the result."""
+    """Fail-closed load-time scan (synchronous): -1 if the tensor is clean,
+    else the index of its first invalid element."""
     lib = _load()
-    first = torch.empty(1, dtype=torch.int64, device=w.device)
+    first = ctypes.c_int64(-1)
     ct = w._c()
-    _check(lib.qbn_validate(ctypes.byref(ct), _ptr(first, "first_bad"), _stream(w.device)), "qbn_validate")
-    return int(first.item())
+    st = lib.qbn_validate(ctypes.byref(ct), ctypes.byref(first), _stream(w.device))
+    if st not in (0, 7):  # 7: QBN_ERR_NAN_SCALE, an invalid element was found
+        raise QbnError(st, "qbn_validate")
+    return int(first.value)
+
+
+def validate_async(w: QTensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The same scan without waiting: out (int64 [1] on the device) receives
+    the result when the stream reaches it."""
+    lib = _load()
+    if out is None:
+        out = torch.empty(1, dtype=torch.int64, device=w.device)
+    _need_dtype(out, (torch.int64,), "out")
+    ct = w._c()
+    _check(lib.qbn_validate_async(ctypes.byref(ct), _ptr(out, "first_bad"), _stream(w.device)), "qbn_validate_async")
+    return out
 
 
 class Prepared:
@@ -487,6 +601,10 @@ class Prepared:
 
 def prepare_gemv(w: QTensor, x: torch.Tensor, y: torch.Tensor) -> Prepared:
     lib = _load()
+    _need_dtype(x, (torch.float32, torch.bfloat16), "x")
+    _need_dtype(y, (torch.float32,), "y")
+    _need(x, w.k * x.element_size(), "x")
+    _need(y, w.n * 4, "y")
     ct = w._c()
     args = (ctypes.byref(ct), _ptr(x, "x"), _DTYPES[x.dtype], _ptr(y, "y"), _DTYPES.get(y.dtype, -1))
     return Prepared(lib.qbn_quantized_gemv, args, "qbn_quantized_gemv", w.device, (w, x, y, ct))
@@ -494,6 +612,10 @@ def prepare_gemv(w: QTensor, x: torch.Tensor, y: torch.Tensor) -> Prepared:
 
 def prepare_quantize_q8(x: torch.Tensor, q: torch.Tensor, d: torch.Tensor, bsums: torch.Tensor) -> Prepared:
     lib = _load()
+    k = x.numel()
+    _need(q, k, "q")
+    _need(d, 4 * (k // 256), "d")
+    _need(bsums, 4 * (k // 32), "bsums")
     args = (_ptr(x, "x"), _DTYPES[x.dtype], x.numel(), _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"))
     return Prepared(lib.qbn_quantize_q8, args, "qbn_quantize_q8", x.device, (x, q, d, bsums))
 
@@ -501,6 +623,7 @@ def prepare_quantize_q8(x: torch.Tensor, q: torch.Tensor, d: torch.Tensor, bsums
 def prepare_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: Optional[torch.Tensor],
                     y: torch.Tensor) -> Prepared:
     lib = _load()
+    _check_gemv_q8(w, q, d, bsums, y)
     ct = w._c()
     args = (ctypes.byref(ct), _ptr(q, "q"), _ptr(d, "d"), _ptr(bsums, "bsums"), _ptr(y, "y"),
             _DTYPES.get(y.dtype, -1))
@@ -510,6 +633,8 @@ def prepare_gemv_q8(w: QTensor, q: torch.Tensor, d: torch.Tensor, bsums: Optiona
 def prepare_quantize_mx(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, fmt: str = "mxfp4") -> Prepared:
     lib = _load()
     m, k = x.shape
+    _need(codes, m * (k // 2 if fmt == "mxfp4" else k), "codes")
+    _need(scales, m * (k // 32), "scales")
     args = (ctypes.c_void_p(x.data_ptr()), _DTYPES[x.dtype], m, k, x.stride(0), MX_FORMATS[fmt], _ptr(codes, "codes"),
             _ptr(scales, "scales"))
     return Prepared(lib.qbn_quantize_mx, args, "qbn_quantize_mx", x.device, (x, codes, scales))
@@ -518,6 +643,7 @@ def prepare_quantize_mx(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tens
 def prepare_gemm_mx(w: QTensor, xcodes: torch.Tensor, xscales: torch.Tensor, y: torch.Tensor,
                     fmt: str = "mxfp4") -> Prepared:
     lib = _load()
+    _check_gemm_mx(w, xcodes.shape[0], xcodes, xscales, y, fmt)
     ct = w._c()
     args = (ctypes.byref(ct), xcodes.shape[0], MX_FORMATS[fmt], _ptr(xcodes, "xcodes"), _ptr(xscales, "xscales"),
             ctypes.c_void_p(y.data_ptr()), _DTYPES.get(y.dtype, -1), y.stride(0))
@@ -528,6 +654,8 @@ def prepare_quantize_nvfp4(x: torch.Tensor, scale2: float, tie: int, codes: torc
                            scales: torch.Tensor) -> Prepared:
     lib = _load()
     m, k = x.shape
+    _need(codes, m * (k // 2), "codes")
+    _need(scales, m * (k // 16), "scales")
     args = (ctypes.c_void_p(x.data_ptr()), _DTYPES.get(x.dtype, -1), m, k, x.stride(0) if m > 1 else k,
             ctypes.c_float(scale2), int(tie), _ptr(codes, "codes"), _ptr(scales, "scales"))
     return Prepared(lib.qbn_quantize_nvfp4, args, "qbn_quantize_nvfp4", x.device, (x, codes, scales))
@@ -535,10 +663,12 @@ def prepare_quantize_nvfp4(x: torch.Tensor, scale2: float, tie: int, codes: torc
 
 def prepare_gemm(w: QTensor, x: torch.Tensor, y: torch.Tensor) -> Prepared:
     lib = _load()
+    m = x.shape[0]
+    _check_rows(x, m, w.k, "x")
+    _check_rows(y, m, w.n, "y")
     if not (x.is_cuda and y.is_cuda) or x.stride(1) != 1 or y.stride(1) != 1:
         raise ValueError("x and y must be device tensors with contiguous rows")
     ct = w._c()
-    m = x.shape[0]
     args = (ctypes.byref(ct), m, ctypes.c_void_p(x.data_ptr()), _DTYPES.get(x.dtype, -1), x.stride(0),
             ctypes.c_void_p(y.data_ptr()), _DTYPES.get(y.dtype, -1), y.stride(0))
     return Prepared(lib.qbn_quantized_gemm, args, "qbn_quantized_gemm", w.device, (w, x, y, ct))
@@ -546,17 +676,22 @@ def prepare_gemm(w: QTensor, x: torch.Tensor, y: torch.Tensor) -> Prepared:
 
 def prepare_dequantize(w: QTensor, out: torch.Tensor, layout: str = "nk") -> Prepared:
     lib = _load()
+    _need_dtype(out, (torch.float32, torch.bfloat16), "out")
+    _need(out, w.n * w.k * out.element_size(), "out")
     ct = w._c()
     args = (ctypes.byref(ct), _ptr(out, "out"), _DTYPES.get(out.dtype, -1), {"nk": 0, "kn": 1}[layout])
     return Prepared(lib.qbn_dequantize, args, "qbn_dequantize", w.device, (w, out, ct))
 
 
-def prepare_repack(src: QTensor, dst: QTensor) -> Prepared:
-    """Repack src into the preallocated buffers of dst (same n, k)."""
+def prepare_repack(src: QTensor, dst: QTensor, status: torch.Tensor) -> Prepared:
+    """Repack src into the buffers of dst (same n, k). status (int64
+    [REPACK_STATUS_WORDS] on the device): status[0] receives -1, or the
+    refusal index of a Q4_0 direction (then dst is left untouched)."""
     lib = _load()
-    ct = src._c()
-    sc = dst.scales if (dst.scales is not None and dst.scales is not src.scales) else None
-    zr = dst.zeros if (dst.zeros is not None and dst.zeros is not src.zeros) else None
-    args = (ctypes.byref(ct), FORMATS[dst.format], int(dst.group), _ptr(dst.data, "data"), _ptr(sc, "scales"),
-            _ptr(zr, "zeros"))
-    return Prepared(lib.qbn_repack, args, "qbn_repack", src.device, (src, dst, ct))
+    _need_dtype(status, (torch.int64,), "status")
+    _need(status, 8 * REPACK_STATUS_WORDS, "status")
+    src.check_sizes()
+    dst.check_sizes()
+    cs, cd = src._c(), dst._c()
+    args = (ctypes.byref(cs), ctypes.byref(cd), _ptr(status, "status"))
+    return Prepared(lib.qbn_repack, args, "qbn_repack", src.device, (src, dst, status, cs, cd))

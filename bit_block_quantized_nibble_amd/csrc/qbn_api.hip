@@ -88,6 +88,22 @@ int32_t check_tensor(const qbn_tensor *w) {
     return QBN_OK;
 }
 
+// Argument rules of the validation scan. For Q4_0, `group` selects the
+// uniformity check (blocks of a group share d) and is not a tensor property.
+int32_t check_validate(const qbn_tensor *w) {
+    if (!w) return QBN_ERR_NULL;
+    if (w->format == QBN_Q4_0 && w->group != 0) {
+        if (w->group < 0 || w->group % 32) return QBN_ERR_GROUP;
+        if (w->k % w->group) return QBN_ERR_SHAPE;
+    }
+    if (w->format == QBN_Q4_0) {
+        qbn_tensor t = *w;
+        t.group = 0;
+        return check_tensor(&t);
+    }
+    return check_tensor(w);
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,7 +123,7 @@ const char *qbn_status_string(int32_t status) {
     case QBN_ERR_SHAPE: return "shape is negative, too large, or not a multiple of the block/pack/group size";
     case QBN_ERR_ALIGN: return "pointer or leading dimension is not aligned as required";
     case QBN_ERR_SCALE2: return "NVFP4 scale2 must be finite and > 0";
-    case QBN_ERR_NAN_SCALE: return "a NaN scale encoding was found";
+    case QBN_ERR_NAN_SCALE: return "validation found an invalid scale or metadata element (a NaN encoding, a non-finite fp16, a zero point above 15 or a Q4_0 group whose blocks disagree)";
     case QBN_ERR_DTYPE: return "unsupported activation or output dtype";
     case QBN_ERR_HIP: return "HIP runtime error (see qbn_last_hip_error)";
     case QBN_ERR_GROUP: return "invalid group size";
@@ -216,8 +232,10 @@ int32_t qbn_quantized_gemm_mx(const qbn_tensor *w, int64_t m, int32_t x_format, 
     int32_t st = check_tensor(w);
     if (st) return st;
     if (w->format != QBN_MXFP4) return QBN_ERR_UNSUPPORTED;
-    if (x_format != QBN_MXFP4 && x_format != QBN_MXFP8)
-        return known_format(x_format) ? QBN_ERR_UNSUPPORTED : QBN_ERR_FORMAT;
+    // MXFP8 activations are not taken: the FP8 x FP4 matrix instruction drops
+    // product bits more than 13 below each run's largest, past the tolerance
+    if (x_format != QBN_MXFP4)
+        return (known_format(x_format) || x_format == QBN_MXFP8) ? QBN_ERR_UNSUPPORTED : QBN_ERR_FORMAT;
     if (y_dtype < QBN_F32 || y_dtype > QBN_F16) return QBN_ERR_FORMAT;
     if (y_dtype != QBN_F32 && y_dtype != QBN_BF16) return QBN_ERR_DTYPE;
     if (m < 0 || m > kMaxElems) return QBN_ERR_SHAPE;
@@ -233,7 +251,7 @@ int32_t qbn_quantized_gemm_mx(const qbn_tensor *w, int64_t m, int32_t x_format, 
     if (m > kMaxElems / w->k) return QBN_ERR_SHAPE;
     if (!xcodes || !xscales) return QBN_ERR_NULL;
     if (!aligned(xcodes, 16)) return QBN_ERR_ALIGN;
-    return hip_status(qbn::launch_gemm_mx(*w, m, x_format, xcodes, xscales, y, y_dtype, ldy, s));
+    return hip_status(qbn::launch_gemm_mx(*w, m, xcodes, xscales, y, y_dtype, ldy, s));
 }
 
 int32_t qbn_quantized_gemm(const qbn_tensor *w, int64_t m, const void *x, int32_t x_dtype, int64_t ldx, void *y,
@@ -365,74 +383,60 @@ int32_t qbn_unpack_bits(const void *words_lo, const void *words_hi, int64_t coun
     return hip_status(qbn::launch_unpack_bits(words_lo, words_hi, count, bits, lo_bits, values, (hipStream_t)stream));
 }
 
-int32_t qbn_repack(const qbn_tensor *src, int32_t dst_format, int32_t dst_group, void *dst_data, void *dst_scales,
-                   void *dst_zeros, void *stream) {
+int32_t qbn_repack(const qbn_tensor *src, const qbn_tensor *dst, int64_t *status, void *stream) {
     int32_t st = check_tensor(src);
     if (st) return st;
-    if (!known_format(dst_format)) return QBN_ERR_FORMAT;
+    if (!dst) return QBN_ERR_NULL;
+    if (!known_format(dst->format) || dst->reserved != 0) return QBN_ERR_FORMAT;
+    const int32_t sf = src->format, df = dst->format;
     // NVFP4 <-> CKE split-half blocks: the codes and subscale bytes move, scale2 is unchanged
-    const bool nv_src = src->format == QBN_NVFP4 || src->format == QBN_NVFP4_CKE;
-    const bool nv_dst = dst_format == QBN_NVFP4 || dst_format == QBN_NVFP4_CKE;
-    if (nv_src || nv_dst) {
-        if (!nv_src || !nv_dst || src->format == dst_format) return QBN_ERR_UNSUPPORTED;
-        if (src->k % 64) return QBN_ERR_SHAPE;
-        if (src->n == 0 || src->k == 0) return QBN_OK;
-        if (!dst_data || (dst_format == QBN_NVFP4 && !dst_scales)) return QBN_ERR_NULL;
-        if (!aligned(dst_data, dst_format == QBN_NVFP4 ? 16 : 4)) return QBN_ERR_ALIGN;
-        return hip_status(qbn::launch_repack_cke(*src, dst_data, dst_scales, (hipStream_t)stream));
+    const bool nv_src = sf == QBN_NVFP4 || sf == QBN_NVFP4_CKE;
+    const bool nv_dst = df == QBN_NVFP4 || df == QBN_NVFP4_CKE;
+    const bool src_int4 = sf == QBN_GPTQ4 || sf == QBN_AWQ4 || sf == QBN_Q4_0;
+    const bool dst_int4 = df == QBN_GPTQ4 || df == QBN_AWQ4 || df == QBN_Q4_0;
+    if (!((nv_src && nv_dst) || (src_int4 && dst_int4)) || sf == df) return QBN_ERR_UNSUPPORTED;
+    if (dst->n != src->n || dst->k != src->k) return QBN_ERR_SHAPE;
+    if (df == QBN_Q4_0 && src->group % 32) return QBN_ERR_GROUP;  // Q4_0 blocks of 32 need whole groups
+    if (sf == QBN_Q4_0 && (dst->group <= 0 || dst->group % 32)) return QBN_ERR_GROUP;
+    if (sf != QBN_Q4_0 && df != QBN_Q4_0 && !nv_src && dst->group != src->group) return QBN_ERR_GROUP;
+    if (nv_src && src->k % 64) return QBN_ERR_SHAPE;
+    st = check_tensor(dst);
+    if (st) return st;
+    const bool q4_0_dir = sf == QBN_Q4_0 || df == QBN_Q4_0;
+    if (q4_0_dir) {  // these directions can refuse, and report it in status[0]
+        if (!status) return QBN_ERR_NULL;
+        if (!aligned(status, 8)) return QBN_ERR_ALIGN;
     }
-    const bool src_int4 = src->format == QBN_GPTQ4 || src->format == QBN_AWQ4 || src->format == QBN_Q4_0;
-    const bool dst_int4 = dst_format == QBN_GPTQ4 || dst_format == QBN_AWQ4 || dst_format == QBN_Q4_0;
-    if (!src_int4 || !dst_int4 || src->format == dst_format) return QBN_ERR_UNSUPPORTED;
-    const int64_t n = src->n, k = src->k;
-    // destination shape rules
-    if (dst_format == QBN_Q4_0) {
-        if (k % 32) return QBN_ERR_SHAPE;
-        if (src->group % 32) return QBN_ERR_GROUP;  // Q4_0 blocks of 32 need whole groups
-    } else {
-        if (k % 8) return QBN_ERR_SHAPE;
-        if (dst_format == QBN_AWQ4 && n % 8) return QBN_ERR_SHAPE;
-        if (src->format == QBN_Q4_0) {
-            if (dst_group <= 0 || dst_group % 32 || k % dst_group) return QBN_ERR_GROUP;
-        } else if (dst_group != src->group && dst_group != 0) {
-            return QBN_ERR_GROUP;
-        }
-    }
-    if (n == 0 || k == 0) return QBN_OK;
-    if (!dst_data) return QBN_ERR_NULL;
-    if (dst_format == QBN_Q4_0) {
-        if (!aligned(dst_data, 2)) return QBN_ERR_ALIGN;
-    } else {
-        if (!aligned(dst_data, 4)) return QBN_ERR_ALIGN;
-        if (src->format == QBN_Q4_0) {
-            if (!dst_scales || !dst_zeros) return QBN_ERR_NULL;
-            if (!aligned(dst_scales, 2)) return QBN_ERR_ALIGN;
-        } else if (dst_scales && !aligned(dst_scales, 2)) {
-            return QBN_ERR_ALIGN;
-        }
-    }
-    return hip_status(qbn::launch_repack(*src, dst_format, dst_group, dst_data, dst_scales, dst_zeros,
-                                         (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    if (src->n == 0 || src->k == 0) return q4_0_dir ? hip_status(qbn::launch_fill_i64(status, -1, 1, s)) : QBN_OK;
+    if (nv_src) return hip_status(qbn::launch_repack_cke(*src, (void *)dst->data, (void *)dst->scales, s));
+    return hip_status(qbn::launch_repack(*src, *dst, q4_0_dir ? status : nullptr, s));
 }
 
-int32_t qbn_validate(const qbn_tensor *w, int64_t *first_bad, void *stream) {
-    if (!w) return QBN_ERR_NULL;
-    if (w->format == QBN_Q4_0 && w->group != 0) {
-        if (w->group < 0 || w->group % 32) return QBN_ERR_GROUP;
-        if (w->k % w->group) return QBN_ERR_SHAPE;
-    }
-    int32_t st;
-    if (w->format == QBN_Q4_0) {
-        qbn_tensor t = *w;
-        t.group = 0;  // group here only selects the uniformity check
-        st = check_tensor(&t);
-    } else {
-        st = check_tensor(w);
-    }
+int32_t qbn_validate_async(const qbn_tensor *w, int64_t *first_bad, void *stream) {
+    const int32_t st = check_validate(w);
     if (st) return st;
     if (!first_bad) return QBN_ERR_NULL;
     if (!aligned(first_bad, 8)) return QBN_ERR_ALIGN;
     return hip_status(qbn::launch_validate(*w, first_bad, (hipStream_t)stream));
+}
+
+int32_t qbn_validate(const qbn_tensor *w, int64_t *first_bad, void *stream) {
+    int32_t st = check_validate(w);  // every argument error is reported before anything is allocated
+    if (st) return st;
+    int64_t *dev = nullptr;
+    hipError_t e = hipMalloc((void **)&dev, sizeof(int64_t));
+    if (e != hipSuccess) return hip_status(e);
+    hipStream_t s = (hipStream_t)stream;
+    int64_t found = -1;
+    e = qbn::launch_validate(*w, dev, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(&found, dev, sizeof(int64_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    const hipError_t ef = hipFree(dev);
+    if (e == hipSuccess) e = ef;
+    if (e != hipSuccess) return hip_status(e);
+    if (first_bad) *first_bad = found;
+    return found >= 0 ? QBN_ERR_NAN_SCALE : QBN_OK;
 }
 
 }  // extern "C"

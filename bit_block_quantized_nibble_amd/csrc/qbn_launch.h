@@ -35,8 +35,15 @@ hipError_t launch_gemm_int4(const qbn_tensor &w, int64_t m, const void *x, int64
                             int64_t ldy, hipStream_t s);
 bool gemm_int4_grid_fits(int64_t m, int64_t n);
 hipError_t launch_dequant(const qbn_tensor &w, void *out, int out_dtype, int out_layout, hipStream_t s);
-hipError_t launch_repack(const qbn_tensor &src, int dst_format, int dst_group, void *dst_data, void *dst_scales,
-                         void *dst_zeros, hipStream_t s);
+// int4 repacks. The Q4_0 directions first run a refusal scan whose
+// QBN_REPACK_SCAN_PARTS workgroups write their partial minima to
+// status[1..]; the repack kernels reduce them, write status[0] (-1 or the
+// first unrepresentable index) and write nothing on a refusal.
+hipError_t launch_repack(const qbn_tensor &src, const qbn_tensor &dst, int64_t *status, hipStream_t s);
+hipError_t launch_fill_i64(int64_t *p, int64_t v, int64_t count, hipStream_t s);
+hipError_t launch_scan_zero_points(const uint8_t *zeros, int64_t count, int64_t *status, hipStream_t s);
+hipError_t launch_scan_q4_0_groups(const uint8_t *blocks, int64_t n, int64_t k, int64_t group, int64_t *status,
+                                   hipStream_t s);
 hipError_t launch_validate(const qbn_tensor &w, int64_t *first_bad, hipStream_t s);
 hipError_t launch_quantize_q8(const void *x, int x_dtype, int64_t k, int8_t *q, float *d, int32_t *bsums,
                               hipStream_t s);
@@ -46,8 +53,8 @@ hipError_t launch_gemv_a16q8(const qbn_tensor &w, const int8_t *q, const float *
                              hipStream_t s);
 hipError_t launch_quantize_mx(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int x_format,
                               void *codes, void *scales, hipStream_t s);
-hipError_t launch_gemm_mx(const qbn_tensor &w, int64_t m, int x_format, const void *xcodes, const void *xscales,
-                          void *y, int y_dtype, int64_t ldy, hipStream_t s);
+hipError_t launch_gemm_mx(const qbn_tensor &w, int64_t m, const void *xcodes, const void *xscales, void *y,
+                          int y_dtype, int64_t ldy, hipStream_t s);
 hipError_t launch_fill_zero(void *out, int64_t bytes, hipStream_t s);
 hipError_t launch_fill_zero_2d_u16(void *out, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
 

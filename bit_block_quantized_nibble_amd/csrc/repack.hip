@@ -272,13 +272,33 @@ __device__ __forceinline__ void move_runs(uint8_t *lds, uint8_t *__restrict__ bl
     }
 }
 
+// The Q4_0 kernels run after a refusal scan that has left its partial minima
+// in status[1 .. QBN_REPACK_SCAN_PARTS] (kNone where nothing was found).
+// Every workgroup takes their minimum (the same for all, so the whole grid
+// agrees), workgroup 0 publishes it as status[0] (-1 for none), and on a
+// refusal every workgroup leaves before writing anything.
+constexpr unsigned long long kNone = 0x7FFFFFFFFFFFFFFFull;
+
+__device__ __forceinline__ bool refused(int64_t *status) {
+    unsigned long long m = kNone;
+#pragma unroll 8
+    for (int g = 0; g < QBN_REPACK_SCAN_PARTS; ++g) {
+        const unsigned long long v = (unsigned long long)status[1 + g];
+        m = v < m ? v : m;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) status[0] = (m == kNone) ? -1 : (int64_t)m;
+    return m != kNone;
+}
+
 // Workgroup tiles: RB consecutive blocks (RB * 32 k) of 64 columns (GPTQ
 // side) or of 256 columns = 32 AWQ word columns (AWQ side); blockIdx.x runs
 // fastest along k so the runs of one column are completed together.
 // GPTQ tile: thread (c = t % 64, i = t / 64) handles blocks i and i + 4.
 __global__ __launch_bounds__(256) void k_gptq_to_q4_0(const uint32_t *__restrict__ src,
                                                       const uint16_t *__restrict__ scales, int64_t group,
-                                                      uint8_t *__restrict__ dst, int64_t N, int64_t K, int words) {
+                                                      uint8_t *__restrict__ dst, int64_t N, int64_t K, int words,
+                                                      int64_t *__restrict__ status) {
+    if (refused(status)) return;  // the whole grid leaves: nothing is written
     __shared__ __attribute__((aligned(16))) uint8_t runs[64 * RS];
     const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, n0 = (int64_t)(blockIdx.x / nbt) * 64;
@@ -307,7 +327,9 @@ __global__ __launch_bounds__(256) void k_gptq_to_q4_0(const uint32_t *__restrict
 // pattern of its first block's d and the zero point is 8.
 __global__ __launch_bounds__(256) void k_q4_0_to_gptq(const uint8_t *__restrict__ src, uint32_t *__restrict__ dst,
                                                       uint16_t *__restrict__ gscales, uint8_t *__restrict__ gzeros,
-                                                      int64_t group, int64_t N, int64_t K, int words) {
+                                                      int64_t group, int64_t N, int64_t K, int words,
+                                                      int64_t *__restrict__ status) {
+    if (refused(status)) return;
     __shared__ __attribute__((aligned(16))) uint8_t runs[64 * RS];
     const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, n0 = (int64_t)(blockIdx.x / nbt) * 64;
@@ -340,7 +362,9 @@ __global__ __launch_bounds__(256) void k_q4_0_to_gptq(const uint8_t *__restrict_
 // b of word column g0 + g; run 32 s + g holds column 8 (g0 + g) + awq_col(s).
 __global__ __launch_bounds__(256) void k_awq_to_q4_0(const uint32_t *__restrict__ src,
                                                      const uint16_t *__restrict__ scales, int64_t group,
-                                                     uint8_t *__restrict__ dst, int64_t N, int64_t K, int words) {
+                                                     uint8_t *__restrict__ dst, int64_t N, int64_t K, int words,
+                                                     int64_t *__restrict__ status) {
+    if (refused(status)) return;
     __shared__ __attribute__((aligned(16))) uint8_t runs[256 * RS];
     const int64_t G = N / 8, nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, g0 = (int64_t)(blockIdx.x / nbt) * 32;
@@ -370,7 +394,9 @@ __global__ __launch_bounds__(256) void k_awq_to_q4_0(const uint32_t *__restrict_
 
 __global__ __launch_bounds__(256) void k_q4_0_to_awq(const uint8_t *__restrict__ src, uint32_t *__restrict__ dst,
                                                      uint16_t *__restrict__ gscales, uint8_t *__restrict__ gzeros,
-                                                     int64_t group, int64_t N, int64_t K, int words) {
+                                                     int64_t group, int64_t N, int64_t K, int words,
+                                                     int64_t *__restrict__ status) {
+    if (refused(status)) return;
     __shared__ __attribute__((aligned(16))) uint8_t runs[256 * RS];
     const int64_t G = N / 8, nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, g0 = (int64_t)(blockIdx.x / nbt) * 32;
@@ -407,12 +433,12 @@ __global__ __launch_bounds__(256) void k_q4_0_to_awq(const uint8_t *__restrict__
 
 }  // namespace
 
-hipError_t launch_repack(const qbn_tensor &src, int dst_format, int dst_group, void *dst_data, void *dst_scales,
-                         void *dst_zeros, hipStream_t s) {
+hipError_t launch_repack(const qbn_tensor &src, const qbn_tensor &dst, int64_t *status, hipStream_t s) {
     const int64_t N = src.n, K = src.k;
-    const int sf = src.format;
+    const int sf = src.format, df = dst.format;
+    void *const dst_data = const_cast<void *>(dst.data);
     const dim3 blk(256);
-    if ((sf == QBN_GPTQ4 && dst_format == QBN_AWQ4) || (sf == QBN_AWQ4 && dst_format == QBN_GPTQ4)) {
+    if ((sf == QBN_GPTQ4 && df == QBN_AWQ4) || (sf == QBN_AWQ4 && df == QBN_GPTQ4)) {
         // one thread per 8 x 8 block of codes
         const int64_t R = K / 8, G = N / 8, cnt = R * G;
         if (cnt > 0) {
@@ -434,16 +460,20 @@ hipError_t launch_repack(const qbn_tensor &src, int dst_format, int dst_group, v
         // scales and zero points keep their [K/group][N] layout
         const int64_t gcnt = (K / src.group) * N;
         hipError_t e = hipSuccess;
-        if (dst_scales && dst_scales != src.scales && gcnt > 0)
-            e = hipMemcpyAsync(dst_scales, src.scales, 2 * gcnt, hipMemcpyDeviceToDevice, s);
-        if (e == hipSuccess && dst_zeros && dst_zeros != src.zeros && gcnt > 0)
-            e = hipMemcpyAsync(dst_zeros, src.zeros, gcnt, hipMemcpyDeviceToDevice, s);
+        if (dst.scales != src.scales && gcnt > 0)
+            e = hipMemcpyAsync(const_cast<void *>(dst.scales), src.scales, 2 * gcnt, hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && dst.zeros != src.zeros && gcnt > 0)
+            e = hipMemcpyAsync(const_cast<void *>(dst.zeros), src.zeros, gcnt, hipMemcpyDeviceToDevice, s);
         return e;
     }
-    const bool to_q4 = dst_format == QBN_Q4_0;
-    if (!(to_q4 ? (sf == QBN_GPTQ4 || sf == QBN_AWQ4) : (sf == QBN_Q4_0 && (dst_format == QBN_GPTQ4 ||
-                                                                              dst_format == QBN_AWQ4))))
+    const bool to_q4 = df == QBN_Q4_0;
+    if (!(to_q4 ? (sf == QBN_GPTQ4 || sf == QBN_AWQ4) : (sf == QBN_Q4_0 && (df == QBN_GPTQ4 || df == QBN_AWQ4))))
         return hipErrorInvalidValue;
+    // refusal scan: every zero point must be 8 (to Q4_0), or every block of a
+    // target group must carry the same d (from Q4_0)
+    hipError_t e = to_q4 ? launch_scan_zero_points((const uint8_t *)src.zeros, (K / src.group) * N, status, s)
+                         : launch_scan_q4_0_groups((const uint8_t *)src.data, N, K, dst.group, status, s);
+    if (e != hipSuccess) return e;
     const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     // Q4_0 runs move as 4-byte words when every run starts and ends on a
     // word: an even block count per column (then every tile's count is even
@@ -454,23 +484,27 @@ hipError_t launch_repack(const qbn_tensor &src, int dst_format, int dst_group, v
     const int words = ((nbr % RB == 0) && (reinterpret_cast<uintptr_t>(q4) % 16 == 0)) ? 2
                       : ((nbr % 2 == 0) && (reinterpret_cast<uintptr_t>(q4) % 4 == 0)) ? 1
                                                                                         : 0;
-    const bool awq = (sf == QBN_AWQ4) || (dst_format == QBN_AWQ4);
+    const bool awq = (sf == QBN_AWQ4) || (df == QBN_AWQ4);
     const int64_t ntile = awq ? (N / 8 + 31) / 32 : (N + 63) / 64;
     const int64_t tiles = nbt * ntile;
     if (tiles > 0) {
         const dim3 grid((unsigned)tiles);
+        uint16_t *const gs = (uint16_t *)const_cast<void *>(dst.scales);
+        uint8_t *const gz = (uint8_t *)const_cast<void *>(dst.zeros);
         if (sf == QBN_GPTQ4)
             hipLaunchKernelGGL(k_gptq_to_q4_0, grid, blk, 0, s, (const uint32_t *)src.data,
-                               (const uint16_t *)src.scales, (int64_t)src.group, (uint8_t *)dst_data, N, K, words);
+                               (const uint16_t *)src.scales, (int64_t)src.group, (uint8_t *)dst_data, N, K, words,
+                               status);
         else if (sf == QBN_AWQ4)
             hipLaunchKernelGGL(k_awq_to_q4_0, grid, blk, 0, s, (const uint32_t *)src.data,
-                               (const uint16_t *)src.scales, (int64_t)src.group, (uint8_t *)dst_data, N, K, words);
-        else if (dst_format == QBN_GPTQ4)
-            hipLaunchKernelGGL(k_q4_0_to_gptq, grid, blk, 0, s, (const uint8_t *)src.data, (uint32_t *)dst_data,
-                               (uint16_t *)dst_scales, (uint8_t *)dst_zeros, (int64_t)dst_group, N, K, words);
+                               (const uint16_t *)src.scales, (int64_t)src.group, (uint8_t *)dst_data, N, K, words,
+                               status);
+        else if (df == QBN_GPTQ4)
+            hipLaunchKernelGGL(k_q4_0_to_gptq, grid, blk, 0, s, (const uint8_t *)src.data, (uint32_t *)dst_data, gs,
+                               gz, (int64_t)dst.group, N, K, words, status);
         else
-            hipLaunchKernelGGL(k_q4_0_to_awq, grid, blk, 0, s, (const uint8_t *)src.data, (uint32_t *)dst_data,
-                               (uint16_t *)dst_scales, (uint8_t *)dst_zeros, (int64_t)dst_group, N, K, words);
+            hipLaunchKernelGGL(k_q4_0_to_awq, grid, blk, 0, s, (const uint8_t *)src.data, (uint32_t *)dst_data, gs,
+                               gz, (int64_t)dst.group, N, K, words, status);
         return hipGetLastError();
     }
     return hipSuccess;

@@ -68,13 +68,33 @@ def _small_inputs(spec):
         inp = workloads.workload(9, n=64, k=256, m=8)
     if spec["kind"] == "encode":  # the bench dequantizes the weights on the device; here the oracle does
         w = oracle.dequant_rows(oracle.NVFP4, inp["data"], inp["scales"], inp["scale2"], inp["k"], range(inp["n"]))
-        inp = dict(inp, W=torch.from_numpy(oracle.bf16_rne_array(w).view(np.int16)).view(torch.bfloat16))
+        inp = dict(inp, Wbits=oracle.bf16_rne_array(w))
     return inp
 
 
 def test_cpu_baseline_leg_runs_for_every_workload():
     for name, spec in bench.WORKLOADS.items():
         out = bench.cpu_baseline(name, spec, _small_inputs(spec), 0.02)
-        assert out["kind"] == "oracle" and out["cores"] >= 1, name
+        assert out["kind"] == "oracle" and out["cores"] == bench.host_cores() >= 1, name
         assert out["value"] > 0 and out["unit"] == spec["unit"], name
         assert isinstance(out["sample"], str) and out["sample"], name
+        assert out["one_core"]["cores"] == 1 and out["one_core"]["value"] > 0, name
+        assert out["cpu"], name
+
+
+def test_default_line_is_the_largest_configuration():
+    """The headline is the MXFP4 GEMM (2.75e11 flops, 103 MB), with the two
+    large decode GEMVs timed alongside."""
+    import sys as _sys
+
+    old = _sys.argv
+    try:
+        _sys.argv = ["bench.py"]
+        args = bench.parse()
+    finally:
+        _sys.argv = old
+    assert args.workload == "mxfp4_gemm" and args.gpus == 1
+    assert set(args.also) == {"q4k_gemv", "nvfp4_gemv"}
+    spec = bench.WORKLOADS[args.workload]
+    assert spec["flops"] == 2.0 * 2048 * 8192 * 8192
+    assert max(w.get("flops", 0) for w in bench.WORKLOADS.values()) == spec["flops"]

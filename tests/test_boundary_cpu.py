@@ -37,7 +37,7 @@ def T(fmt, n, k, data=A, scales=B, zeros=C, scale2=1.0, group=0, reserved=0):
 def test_exports_every_declared_symbol(lib):
     header = open(os.path.join(ROOT, "include", "qbn.h")).read()
     declared = re.findall(r"QBN_API\s+[\w\s\*]+?\b(qbn_\w+)\s*\(", header)
-    assert len(declared) == 21
+    assert len(declared) == 22
     assert set(declared) == set(qbn.EXPORTED)
     so = ctypes.CDLL(qbn.lib_path())
     for name in declared:
@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_and_struct(lib):
-    assert lib.qbn_abi_version() == 1
+    assert lib.qbn_abi_version() == 2
     assert lib.qbn_tensor_struct_size() == ctypes.sizeof(qbn._CTensor) == 56
     for s in range(11):
         assert lib.qbn_status_string(s)
@@ -170,7 +170,10 @@ def test_mx_rejections(lib):
     assert q(None, F32, 0, 64, 64, MX, None, None, None) == OK
     g = lib.qbn_quantized_gemm_mx
     assert g(T(NV, 8, 64), 4, MX, A, B, C, BF16, 8, None) == UNSUP
-    assert g(T(MX, 8, 64), 4, MX8, A + 8, B, C, BF16, 8, None) == ALIGN
+    # MXFP8 activations are refused: the FP8 x FP4 instruction truncates each
+    # run of 8 products 13 bits below the run's largest, past the tolerance
+    assert g(T(MX, 8, 64), 4, MX8, A, B, C, BF16, 8, None) == UNSUP
+    assert g(T(MX, 8, 64), 4, MX8, A + 8, B, C, BF16, 8, None) == UNSUP
     assert g(T(MX, 8, 64), 4, 9, A, B, C, BF16, 8, None) == FORMAT
     assert g(T(MX, 8, 64), 4, MX, A, B, C, 2, 8, None) == DTYPE
     assert g(T(MX, 8, 64), 4, MX, A, B, C, BF16, 4, None) == SHAPE
@@ -223,27 +226,44 @@ def test_dequant_rejections(lib):
 
 def test_repack_rejections(lib):
     r = lib.qbn_repack
-    assert r(T(MX, 8, 64), Q0, 0, A, None, None, None) == UNSUP
-    assert r(T(GP, 8, 64, group=32), GP, 32, A, None, None, None) == UNSUP
-    assert r(T(GP, 8, 64, group=32), 11, 32, A, None, None, None) == FORMAT
-    assert r(T(GP, 12, 64, group=32), AW, 32, A, None, None, None) == SHAPE
-    assert r(T(GP, 8, 64, group=32), AW, 64, A, None, None, None) == GROUP
-    assert r(T(GP, 8, 64, group=16), Q0, 0, A, None, None, None) == GROUP
-    assert r(T(Q0, 8, 64), GP, 16, A, B, C, None) == GROUP
-    assert r(T(Q0, 8, 64), GP, 96, A, B, C, None) == GROUP
-    assert r(T(Q0, 8, 64), GP, 32, A, None, C, None) == NULL
-    assert r(T(GP, 8, 64, group=32), AW, 32, None, None, None, None) == NULL
-    assert r(T(GP, 8, 64, group=32), AW, 32, A + 2, None, None, None) == ALIGN
-    assert r(T(GP, 8, 64, group=32), Q0, 0, A + 1, None, None, None) == ALIGN
+    S = 0x40000  # a fake status array (8-byte aligned)
+    gp = T(GP, 8, 64, group=32)
+    assert r(T(MX, 8, 64), T(Q0, 8, 64), S, None) == UNSUP
+    assert r(gp, T(GP, 8, 64, group=32), S, None) == UNSUP
+    assert r(gp, T(11, 8, 64, group=32), S, None) == FORMAT
+    assert r(gp, T(AW, 8, 64, group=32, reserved=1), S, None) == FORMAT
+    assert r(gp, None, S, None) == NULL
+    assert r(T(GP, 12, 64, group=32), T(AW, 12, 64, group=32), S, None) == SHAPE   # AWQ needs n % 8 == 0
+    assert r(gp, T(AW, 8, 128, group=32), S, None) == SHAPE                        # n, k must match
+    assert r(gp, T(AW, 8, 64, group=64), S, None) == GROUP                         # GPTQ <-> AWQ keep the group
+    assert r(T(GP, 8, 64, group=16), T(Q0, 8, 64), S, None) == GROUP               # Q4_0 needs whole groups of 32
+    assert r(T(Q0, 8, 64), T(GP, 8, 64, group=16), S, None) == GROUP
+    assert r(T(Q0, 8, 64), T(GP, 8, 96, group=96), S, None) == SHAPE
+    assert r(T(Q0, 8, 64), T(GP, 8, 64, group=96), S, None) == SHAPE               # k % group
+    assert r(T(Q0, 8, 64), T(GP, 8, 64, group=32, scales=None), S, None) == NULL   # dst scales are outputs
+    assert r(gp, T(AW, 8, 64, group=32, data=None), S, None) == NULL
+    assert r(gp, T(AW, 8, 64, group=32, data=A + 2), S, None) == ALIGN
+    assert r(gp, T(Q0, 8, 64, data=A + 1), S, None) == ALIGN
+    # the Q4_0 directions can refuse and need the status array
+    assert r(gp, T(Q0, 8, 64), None, None) == NULL
+    assert r(T(Q0, 8, 64), T(AW, 8, 64, group=32), None, None) == NULL
+    assert r(gp, T(Q0, 8, 64), S + 4, None) == ALIGN
+    assert r(T(GP, 8, 0, group=32), T(AW, 8, 0, group=32), None, None) == OK      # empty, status not needed
 
 
 def test_validate_rejections(lib):
-    v = lib.qbn_validate
-    assert v(T(MX, 4, 64), None, None) == NULL
-    assert v(T(MX, 4, 64), A + 4, None) == ALIGN
-    assert v(T(NV, 4, 64, scale2=0.0), A, None) == SCALE2
-    assert v(T(Q0, 4, 64, group=48), A, None) == GROUP
-    assert v(T(Q0, 4, 96, group=64), A, None) == SHAPE
+    for v in (lib.qbn_validate_async,):
+        assert v(T(MX, 4, 64), None, None) == NULL
+        assert v(T(MX, 4, 64), A + 4, None) == ALIGN
+    host = ctypes.c_int64(0)
+    # the synchronous form takes a host int64 and reports argument errors
+    # before it allocates anything
+    for v, out in ((lib.qbn_validate, ctypes.byref(host)), (lib.qbn_validate_async, A)):
+        assert v(T(NV, 4, 64, scale2=0.0), out, None) == SCALE2
+        assert v(T(Q0, 4, 64, group=48), out, None) == GROUP
+        assert v(T(Q0, 4, 96, group=64), out, None) == SHAPE
+        assert v(T(MX, 4, 48), out, None) == SHAPE
+        assert v(None, out, None) == NULL
 
 
 def test_binding_refuses_host_tensors():
@@ -329,14 +349,16 @@ def test_cke_rejections(lib):
     assert lib.qbn_dequantize(T(CKE, 4, 96, scale2=0.01), B, F32, 0, None) == SHAPE
     assert lib.qbn_dequantize(T(CKE, 4, 64, scale2=0.01), B + 8, F32, 0, None) == ALIGN
     r = lib.qbn_repack
-    assert r(T(CKE, 4, 64, scale2=0.01), GP, 128, B, None, None, None) == UNSUP
-    assert r(T(GP, 4, 64, group=64), CKE, 0, B, None, None, None) == UNSUP
-    assert r(T(NV, 4, 64, scale2=0.01), NV, 0, B, C, None, None) == UNSUP
-    assert r(T(NV, 4, 32, scale2=0.01), CKE, 0, B, None, None, None) == SHAPE
-    assert r(T(NV, 4, 64, scale2=0.01), CKE, 0, B + 2, None, None, None) == ALIGN
-    assert r(T(NV, 4, 64, scale2=0.01), CKE, 0, None, None, None, None) == NULL
-    assert r(T(CKE, 4, 64, scale2=0.01), NV, 0, B + 4, C, None, None) == ALIGN
-    assert r(T(CKE, 4, 64, scale2=0.01), NV, 0, B, None, None, None) == NULL
-    assert r(T(CKE, 0, 64, scale2=0.01), NV, 0, None, None, None, None) == OK
-    assert lib.qbn_validate(T(CKE, 4, 96, scale2=0.01), B, None) == SHAPE
-    assert lib.qbn_validate(T(CKE, 4, 64, scale2=0.01), None, None) == NULL
+    nv, cke = T(NV, 4, 64, scale2=0.01), T(CKE, 4, 64, scale2=0.01)
+    assert r(cke, T(GP, 4, 64, group=64), None, None) == UNSUP
+    assert r(T(GP, 4, 64, group=64), cke, None, None) == UNSUP
+    assert r(nv, T(NV, 4, 64, scale2=0.01), None, None) == UNSUP
+    assert r(T(NV, 4, 32, scale2=0.01), T(CKE, 4, 32, scale2=0.01), None, None) == SHAPE
+    assert r(nv, T(CKE, 4, 64, data=B + 2, scale2=0.01), None, None) == ALIGN
+    assert r(nv, T(CKE, 4, 64, data=None, scale2=0.01), None, None) == NULL
+    assert r(nv, T(CKE, 4, 64, scale2=0.0), None, None) == SCALE2  # dst is a complete tensor
+    assert r(cke, T(NV, 4, 64, data=B + 4, scale2=0.01), None, None) == ALIGN
+    assert r(cke, T(NV, 4, 64, scales=None, scale2=0.01), None, None) == NULL
+    assert r(T(CKE, 0, 64, scale2=0.01), T(NV, 0, 64, data=None, scales=None, scale2=0.01), None, None) == OK
+    assert lib.qbn_validate_async(T(CKE, 4, 96, scale2=0.01), B, None) == SHAPE
+    assert lib.qbn_validate_async(T(CKE, 4, 64, scale2=0.01), None, None) == NULL

@@ -1,22 +1,20 @@
 """GPU parity of the MX path: qbn_quantize_mx must reproduce the oracle's
-OCP MX codes and E8M0 scales bit for bit; qbn_quantized_gemm_mx (MXFP4 or
-MXFP8 activations x MXFP4 weights on the block-scaled matrix cores) must
-match the oracle's exact sums within |y - y_ref| <= T (binary32 output), or
-inside the round-to-nearest band of that interval (bfloat16 output).
+OCP MX codes and E8M0 scales bit for bit (MXFP4 and MXFP8);
+qbn_quantized_gemm_mx (MXFP4 activations x MXFP4 weights on the
+block-scaled matrix cores) must match the oracle's exact sums within
+|y - y_ref| <= T = 1e-5 * sum|x_hat w_hat| + 1e-6 (binary32 output), or
+inside the round-to-nearest band of that interval (bfloat16 output), on
+every entry.
 
-MXFP4 activations: T = 1e-5 * sum|x_hat w_hat| + 1e-6.
-MXFP8 activations: T adds what the matrix core's group sums can drop.
-Measured on gfx950 (in-bounds probes, every lane active),
-v_mfma_scale_f32_32x32x64_f8f6f4 adds each run of 8 consecutive k aligned to
-the run's largest product, keeping 13 bits below its exponent and truncating
-the rest: 448 + 2^-5 comes out exact, 448 + 2^-6 as 448, 448 + 1.5 * 2^-5 as
-448 + 2^-5, while 448 - 2^-6 in another run is exact, and 448 plus 63 terms
-of 2^-6 loses just the 7 in the first run. E2M1 x E2M1 products (at most 4
-significant bits, within 2^8 of each other inside a block) never reach the
-cut, so the W4A4 sums are exact per run; E4M3 elements span 18 binades, so
-the W4A8 cut can exceed 1e-5 of sum|x_hat w_hat| at small k (see
-_step_loss_bound). At least 99% of the entries must still meet the plain
-bound."""
+MXFP8 activations (W4A8) are refused by the GEMM. Measured on gfx950
+(in-bounds probes, every lane active), v_mfma_scale_f32_32x32x64_f8f6f4 adds
+each run of 8 consecutive k aligned to the run's largest product, keeping 13
+bits below its exponent and truncating the rest (448 + 2^-5 comes out exact,
+448 + 2^-6 as 448). E2M1 x E2M1 products (at most 4 significant bits,
+within 2^8 of each other inside a block) never reach the cut, so the W4A4
+runs are exact; E4M3 x E2M1 products span 21 binades and do reach it, and
+on 37 x 70 x 96 four entries of 2590 missed T. The W4A8 parametrizations
+below are skipped for that reason."""
 import numpy as np
 import pytest
 import torch
@@ -84,42 +82,10 @@ def _bf16_value(bits):
 
 
 _OFMT = {"mxfp4": oracle.MXFP4, "mxfp8": oracle.MXFP8}
-
-
-def _x_values(xc, xs, fmt, k):
-    """Dequantized MX activations in binary64 (E4M3 decoded by torch)."""
-    if fmt == "mxfp4":
-        return oracle.dequant_rows(oracle.MXFP4, xc, xs, 1.0, k, range(xc.shape[0])).astype(np.float64)
-    f8 = torch.from_numpy(np.ascontiguousarray(xc)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
-    return f8 * np.repeat(2.0 ** (xs.astype(np.float64) - 127), 32, axis=1)
-
-
-def _step_loss_bound(Xh, W, ms, ns, k):
-    """Most the matrix core's group sums can drop for entries (ms[i], ns[i]).
-    Each run of 8 consecutive k (inside one 32-block, so under one pair of
-    scales) is added aligned to its largest product, keeping bits down to
-    2^(E - 13) with E = floor(log2 max|x_hat w_hat|); an E4M3 x E2M1 product
-    has at most 6 significant bits, so only products below 2^(E - 8) can lose
-    anything, and each loses less than min(|p|, 2^(E - 13))."""
-    H = np.zeros(len(ms))
-    for c0 in range(0, len(ms), 1024):
-        P = np.abs(Xh[ms[c0:c0 + 1024]] * W[ns[c0:c0 + 1024]]).reshape(-1, k // 8, 8)
-        with np.errstate(divide="ignore"):
-            E = np.floor(np.log2(P.max(axis=2, keepdims=True)))
-        lose = (P > 0) & (P < np.exp2(E - 8))
-        H[c0:c0 + 1024] = np.where(lose, np.minimum(P, np.exp2(E - 13)), 0.0).sum(axis=(1, 2))
-    return H
-
-
-def _tolerance(fmt, s_ref, wc, ws, xc, xs, ms, ns, k):
-    strict = 1e-5 * s_ref + 1e-6
-    if fmt == "mxfp4":
-        return strict, strict
-    ur, mi = np.unique(np.asarray(ms), return_inverse=True)
-    uc, ni = np.unique(np.asarray(ns), return_inverse=True)
-    W = oracle.dequant_rows(oracle.MXFP4, wc, ws, 1.0, k, uc).astype(np.float64)
-    Xh = _x_values(np.ascontiguousarray(xc[ur]), np.ascontiguousarray(xs[ur]), fmt, k)
-    return strict, strict + _step_loss_bound(Xh, W, mi, ni, k)
+W4A8_SKIP = pytest.mark.skip(reason="MXFP8 x MXFP4 is refused (QBN_ERR_UNSUPPORTED): the FP8 x FP4 matrix "
+                             "instruction truncates each run of 8 products 13 bits below the run's largest, "
+                             "which misses 1e-5 * sum|x_hat w_hat| + 1e-6 on some entries")
+FMTS = ["mxfp4", pytest.param("mxfp8", marks=W4A8_SKIP)]
 
 
 def _gemm(wc, ws, xc, xs, m, n, k, ydt, what, fmt="mxfp4"):
@@ -133,15 +99,9 @@ def _gemm(wc, ws, xc, xs, m, n, k, ydt, what, fmt="mxfp4"):
 
 def _check(wc, ws, xc, xs, m, n, k, ms, ns, what, fmt="mxfp4"):
     y_ref, s_ref = oracle.mx_gemm_entries(wc, ws, k, _OFMT[fmt], xc, xs, ms, ns)
-    strict, T = _tolerance(fmt, s_ref, wc, ws, xc, xs, ms, ns, k)
+    T = 1e-5 * s_ref + 1e-6
     y32 = _gemm(wc, ws, xc, xs, m, n, k, torch.float32, what, fmt).cpu().numpy()
-    if fmt == "mxfp4":
-        assert_within_tolerance(y32[ms, ns], y_ref, s_ref, "gemm_mx f32 " + what)
-    else:
-        err = np.abs(y32[ms, ns].astype(np.float64) - y_ref)
-        assert (err <= T).all(), "gemm_mx f32 %s: %d entries outside the step-loss bound" % (what, int((err > T).sum()))
-        assert (err <= strict).mean() >= 0.99, "gemm_mx f32 %s: %.4f within the plain bound" % (
-            what, (err <= strict).mean())
+    assert_within_tolerance(y32[ms, ns], y_ref, s_ref, "gemm_mx f32 " + what)
     yb = host_bits(_gemm(wc, ws, xc, xs, m, n, k, torch.bfloat16, what, fmt)).reshape(m, n)
     lo = _bf16_value(oracle.bf16_rne_array((y_ref - T).astype(np.float32)))
     hi = _bf16_value(oracle.bf16_rne_array((y_ref + T).astype(np.float32)))
@@ -158,13 +118,12 @@ def _inputs(rng, m, n, k, fmt="mxfp4"):
 
 
 # Shapes reach the small kernel (m or n below 256, or k not a multiple of the
-# tiled kernel's k-stage: 256 for MXFP4 activations, 128 for MXFP8; including
-# k % 64 == 32) and the 256 x 256 kernel with full and edge tiles, from one
-# k-stage to many.
+# tiled kernel's k-stage of 256, including k % 64 == 32) and the 256 x 256
+# kernel with full and edge tiles, from one k-stage to many.
 @pytest.mark.parametrize("m,n,k", [(1, 32, 32), (37, 70, 96), (130, 200, 1056), (64, 512, 2048), (256, 256, 256),
                                    (300, 520, 1024), (512, 256, 4096), (256, 384, 768), (512, 512, 8192),
                                    (256, 256, 128), (260, 512, 640), (384, 300, 1280), (256, 256, 352)])
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemm_mx_all_entries(m, n, k, fmt):
     rng = np.random.default_rng(m + 7 * n + k)
     xc, xs, wc, ws = _inputs(rng, m, n, k, fmt)
@@ -172,7 +131,7 @@ def test_gemm_mx_all_entries(m, n, k, fmt):
     _check(wc, ws, xc, xs, m, n, k, ms.ravel(), ns.ravel(), "%dx%dx%d" % (m, n, k), fmt)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemm_mx_exact_small_integers(fmt):
     """Activations and weights whose products and partial sums are all exact
     in binary32 must come out exactly."""
@@ -189,7 +148,7 @@ def test_gemm_mx_exact_small_integers(fmt):
     assert np.array_equal(y.ravel().astype(np.float64), y_ref)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemm_mx_workload_end_to_end_sampled(fmt):
     """The GEMM workload's shape (W 8192 x 8192 MXFP4, X 2048 x 8192 bf16):
     device quantizer checked row by row against the oracle on sampled rows,
@@ -211,7 +170,7 @@ def test_gemm_mx_workload_end_to_end_sampled(fmt):
     ms = np.concatenate([rng.integers(0, m, 1500), np.full(64, m - 1)])
     ns = np.concatenate([rng.integers(0, n, 1500), np.arange(n - 64, n)])
     y_ref, sa = oracle.mx_gemm_entries(inp["data"], inp["scales"], k, _OFMT[fmt], xc, xs, ms, ns)
-    _, T = _tolerance(fmt, sa, inp["data"], inp["scales"], xc, xs, ms, ns, k)
+    T = 1e-5 * sa + 1e-6
     lo = _bf16_value(oracle.bf16_rne_array((y_ref - T).astype(np.float32)))
     hi = _bf16_value(oracle.bf16_rne_array((y_ref + T).astype(np.float32)))
     got = _bf16_value(host_bits(Y).reshape(m, n)[ms, ns])
@@ -238,3 +197,21 @@ def test_gemm_mx_strided_output_and_empty():
     qbn.quantized_gemm_mx(w0, e, e, "mxfp4", y0)
     torch.cuda.synchronize()
     assert (y0.cpu() == 0).all()
+
+
+def test_gemm_mx_refuses_mxfp8_activations():
+    """W4A8 on the FP8 x FP4 instruction is refused before any launch, and
+    the output is left as it was."""
+    rng = np.random.default_rng(12)
+    m, n, k = 64, 64, 256
+    X = workloads.bf16_bits_from_f32(rng.standard_normal((m, k)).astype(np.float32))
+    xc, xs = oracle.mx_quantize(X, oracle.MXFP8)
+    wc, ws = workloads.mxfp4_weights(rng, n, k, -6, 2)
+    w = qbn.QTensor("mxfp4", n, k, dev(wc), dev(ws))
+    y = torch.full((m, n), 7.0, dtype=torch.float32, device=DEV)
+    say("gemm_mx mxfp8 refused")
+    with pytest.raises(qbn.QbnError) as e:
+        qbn.quantized_gemm_mx(w, dev(xc), dev(xs), "mxfp8", y)
+    assert e.value.status == 3  # QBN_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert (y.cpu() == 7.0).all()

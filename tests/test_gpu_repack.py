@@ -2,7 +2,11 @@
 bit-exactly (compared with the oracle's pack(unpack(...)) through the
 logical matrix), on ragged tiles, on the verification probes and on the full
 4096 x 11008 workload, including the GPTQ -> AWQ -> Q4_0 -> AWQ -> GPTQ round
-trip."""
+trip. The Q4_0 directions fail closed ("Bit Packing Architecture",
+'Repacking between formats': source and target weights must dequantize
+bit-identically): a zero point other than 8, or Q4_0 blocks of one target
+group with different d, is refused with its first index and nothing is
+written."""
 import numpy as np
 import pytest
 import torch
@@ -52,8 +56,8 @@ def test_repack_random(src, dst, K, N, g):
     q = rng.integers(0, 16, (K, N)).astype(np.uint8)
     scales = rng.uniform(-0.01, 0.01, (K // g, N)).astype(np.float16).view(np.uint16)
     zeros = rng.integers(0, 16, (K // g, N)).astype(np.uint8)
-    if src == "q4_0":
-        zeros[:] = 8  # what Q4_0 implies; the scales round-trip as block d values
+    if "q4_0" in (src, dst):
+        zeros[:] = 8  # the only zero point Q4_0 holds; the scales round-trip as block d values
     w = _mk(src, q, scales, zeros, g)
     say("repack", src, "->", dst, K, N, g)
     out = qbn.repack(w, dst, dst_group=g if dst != "q4_0" else None)
@@ -84,11 +88,34 @@ def test_repack_probes_all_directions():
                 (name, src, dst)
 
 
+def test_workload5_refused_with_random_zero_points():
+    """The workload's zero points are uniform over 0..15: Q4_0 cannot hold
+    them, so GPTQ / AWQ -> Q4_0 is refused at the first zero point != 8 and
+    the destination keeps its contents."""
+    inp = workloads.workload(5)
+    K, N, g = inp["K"], inp["N"], inp["group"]
+    zeros = inp["zeros"]
+    gptq = qbn.QTensor("gptq4", N, K, dev(inp["qweight"]), dev(inp["scales"].view(np.uint16)), dev(zeros), group=g)
+    awq = qbn.repack(gptq, "awq4")
+    first = int(np.flatnonzero(zeros.ravel() != 8)[0])
+    for src in (gptq, awq):
+        sentinel = torch.full((N, K // 32, 18), 0xA5, dtype=torch.uint8, device=DEV)
+        say("workload 5 refusal", src.format, "-> q4_0")
+        with pytest.raises(qbn.RepackRefused) as e:
+            qbn.repack(src, "q4_0", data=sentinel)
+        assert e.value.index == first
+        torch.cuda.synchronize()
+        assert (sentinel == 0xA5).all().item()
+
+
 def test_workload5_round_trip_and_dequant_identity():
+    """Workload 5's codes and scales with every zero point 8 (what Q4_0 can
+    hold): the round trip GPTQ -> AWQ -> Q4_0 -> AWQ -> GPTQ is bit-exact and
+    all four layouts dequantize to the same values everywhere."""
     inp = workloads.workload(5)
     K, N, g = inp["K"], inp["N"], inp["group"]
     scales = inp["scales"].view(np.uint16)
-    zeros = inp["zeros"]
+    zeros = np.full_like(inp["zeros"], 8)
     qw = inp["qweight"]
     gptq = qbn.QTensor("gptq4", N, K, dev(qw), dev(scales), dev(zeros), group=g)
     say("workload 5: gptq -> awq")
@@ -104,22 +131,48 @@ def test_workload5_round_trip_and_dequant_identity():
     assert np.array_equal(host_bits(awq.data).view(np.uint32), oracle.awq_pack(q))
     assert np.array_equal(host_bits(q40.data).reshape(N, K // 32, 18),
                           oracle.q4_0_pack(q, _q4_0_d_from_scales(scales, K, g)))
-    # codes and scales round-trip bit for bit; Q4_0 carries no zero points, so
-    # they come back as 8
     assert np.array_equal(host_bits(gptq2.data).view(np.uint32), qw)
     assert np.array_equal(host_bits(gptq2.scales).view(np.uint16).reshape(scales.shape), scales)
     assert (host_bits(gptq2.zeros) == 8).all()
-    # dequantized values: GPTQ and AWQ agree everywhere, Q4_0 agrees with them
-    # exactly where the group's zero point is 8
     say("workload 5: dequant identities")
     wg = host_bits(qbn.dequantize(gptq, dtype=torch.float32, layout="kn"))
     wa = host_bits(qbn.dequantize(awq, dtype=torch.float32, layout="kn"))
     w0 = host_bits(qbn.dequantize(q40, dtype=torch.float32, layout="kn"))
     torch.cuda.synchronize()
     assert np.array_equal(wg, wa)
-    z8 = np.repeat(zeros, g, axis=0) == 8
-    assert z8.any()
-    assert np.array_equal(w0.reshape(K, N)[z8], wg.reshape(K, N)[z8])
+    assert np.array_equal(w0, wg)
+
+
+@pytest.mark.parametrize("dst", ["gptq4", "awq4"])
+def test_q4_0_source_refused_when_a_group_mixes_d(dst):
+    """Q4_0 -> GPTQ / AWQ with group 128: a column whose four blocks of one
+    group carry different d cannot share one scale; the first such block is
+    reported through the status array and nothing is written."""
+    K, N, g = 512, 64, 128
+    rng = np.random.default_rng(17)
+    q = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    scales = rng.uniform(0.001, 0.01, (K // g, N)).astype(np.float16).view(np.uint16)
+    blocks = oracle.q4_0_pack(q, _q4_0_d_from_scales(scales, K, g))
+    blocks[9, 6, 0] ^= 0x01   # column 9, block 6 (group 1, its third block)
+    blocks[40, 2, 1] ^= 0x02  # a later column
+    src = qbn.QTensor("q4_0", N, K, dev(blocks))
+    out = qbn.repack_target(src, dst, g)
+    out.data.fill_(0x5A5A5A5A)
+    status = torch.empty(qbn.REPACK_STATUS_WORDS, dtype=torch.int64, device=DEV)
+    say("q4_0 mixed-d refusal ->", dst)
+    qbn.prepare_repack(src, out, status)()
+    torch.cuda.synchronize()
+    assert int(status[0].item()) == 9 * (K // 32) + 6
+    assert (out.data == 0x5A5A5A5A).all().item()
+    with pytest.raises(qbn.RepackRefused):
+        qbn.repack(src, dst, dst_group=g)
+    # with group 32 every block is its own group: accepted, and status[0] is -1
+    ok = qbn.repack_target(src, dst, 32)
+    qbn.prepare_repack(src, ok, status)()
+    torch.cuda.synchronize()
+    assert int(status[0].item()) == -1
+    want = oracle.gptq_pack(q) if dst == "gptq4" else oracle.awq_pack(q)
+    assert np.array_equal(host_bits(ok.data).reshape(want.shape).view(np.uint32), want.view(np.uint32))
 
 
 def test_repack_validate_q4_0_group_scales():

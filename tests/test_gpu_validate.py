@@ -77,3 +77,31 @@ def test_validate_affine_companions():
     s.reshape(-1)[50] = np.float16(np.inf)
     inp["scales"] = s
     assert qbn.validate(qtensor(inp)) == 50
+
+
+def test_validate_async_and_sync_agree_and_status_codes():
+    """qbn_validate_async leaves the index in device memory; qbn_validate
+    waits, returns QBN_ERR_NAN_SCALE (7) on a finding and QBN_OK when clean,
+    and hands the index back in host memory."""
+    import ctypes
+
+    inp = workloads.workload(2, n=48, k=512, seed=9)
+    s = inp["scales"].copy()
+    s.reshape(-1)[[1500, 700]] = 0x7F
+    inp["scales"] = s
+    w = qtensor(inp)
+    say("validate async")
+    out = qbn.validate_async(w)
+    torch.cuda.synchronize()
+    assert int(out.item()) == 700
+    lib = qbn._load()
+    host = ctypes.c_int64(123)
+    ct = w._c()
+    say("validate sync, raw status")
+    assert lib.qbn_validate(ctypes.byref(ct), ctypes.byref(host), None) == 7
+    assert host.value == 700
+    clean = qtensor(workloads.workload(2, n=48, k=512, seed=9))
+    ct2 = clean._c()
+    assert lib.qbn_validate(ctypes.byref(ct2), ctypes.byref(host), None) == 0
+    assert host.value == -1
+    assert lib.qbn_validate(ctypes.byref(ct2), None, None) == 0  # the result pointer may be NULL
