@@ -38,7 +38,8 @@ _lib = None
 
 EXPORTED = (
     "qbn_abi_version", "qbn_tensor_struct_size", "qbn_status_string", "qbn_last_hip_error", "qbn_bytes",
-    "qbn_quantized_gemv", "qbn_quantized_gemm", "qbn_dequantize", "qbn_repack", "qbn_validate", "qbn_validate_async",
+    "qbn_quantized_gemv", "qbn_quantized_gemm", "qbn_dequantize", "qbn_repack", "qbn_repack_noalloc", "qbn_validate",
+    "qbn_validate_async",
     "qbn_quantize_q8", "qbn_quantized_gemv_q8", "qbn_quantize_mx", "qbn_quantized_gemm_mx",
     "qbn_gptq_qzeros", "qbn_gptq_resolve_g_idx", "qbn_permute",
     "qbn_quantize_nvfp4", "qbn_quantize_int4_sym", "qbn_pack_bits", "qbn_unpack_bits",
@@ -103,6 +104,8 @@ def _load():
         lib.qbn_dequantize.restype = I32
         lib.qbn_repack.argtypes = [T, T, P, P]
         lib.qbn_repack.restype = I32
+        lib.qbn_repack_noalloc.argtypes = [T, T, P, P]
+        lib.qbn_repack_noalloc.restype = I32
         lib.qbn_gptq_qzeros.argtypes = [P, P, I64, I64, I32, I32, P]
         lib.qbn_gptq_qzeros.restype = I32
         lib.qbn_gptq_resolve_g_idx.argtypes = [P, P, I64, I64, I32, P, P, P, P]

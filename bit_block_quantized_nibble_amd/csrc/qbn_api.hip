@@ -104,6 +104,32 @@ int32_t check_validate(const qbn_tensor *w) {
     return check_tensor(w);
 }
 
+// Argument rules of a repack of src into the tensor dst (both complete
+// tensors of their formats, same n and k); *q4_0_dir tells whether the
+// direction can refuse (GPTQ4 / AWQ4 <-> Q4_0).
+int32_t check_repack(const qbn_tensor *src, const qbn_tensor *dst, bool *q4_0_dir) {
+    int32_t st = check_tensor(src);
+    if (st) return st;
+    if (!dst) return QBN_ERR_NULL;
+    if (!known_format(dst->format) || dst->reserved != 0) return QBN_ERR_FORMAT;
+    const int32_t sf = src->format, df = dst->format;
+    // NVFP4 <-> CKE split-half blocks: the codes and subscale bytes move, scale2 is unchanged
+    const bool nv_src = sf == QBN_NVFP4 || sf == QBN_NVFP4_CKE;
+    const bool nv_dst = df == QBN_NVFP4 || df == QBN_NVFP4_CKE;
+    const bool src_int4 = sf == QBN_GPTQ4 || sf == QBN_AWQ4 || sf == QBN_Q4_0;
+    const bool dst_int4 = df == QBN_GPTQ4 || df == QBN_AWQ4 || df == QBN_Q4_0;
+    if (!((nv_src && nv_dst) || (src_int4 && dst_int4)) || sf == df) return QBN_ERR_UNSUPPORTED;
+    if (dst->n != src->n || dst->k != src->k) return QBN_ERR_SHAPE;
+    if (df == QBN_Q4_0 && src->group % 32) return QBN_ERR_GROUP;  // Q4_0 blocks of 32 need whole groups
+    if (sf == QBN_Q4_0 && (dst->group <= 0 || dst->group % 32)) return QBN_ERR_GROUP;
+    if (sf != QBN_Q4_0 && df != QBN_Q4_0 && !nv_src && dst->group != src->group) return QBN_ERR_GROUP;
+    if (nv_src && src->k % 64) return QBN_ERR_SHAPE;
+    st = check_tensor(dst);
+    if (st) return st;
+    *q4_0_dir = sf == QBN_Q4_0 || df == QBN_Q4_0;
+    return QBN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,33 +410,38 @@ int32_t qbn_unpack_bits(const void *words_lo, const void *words_hi, int64_t coun
 }
 
 int32_t qbn_repack(const qbn_tensor *src, const qbn_tensor *dst, int64_t *status, void *stream) {
-    int32_t st = check_tensor(src);
+    bool q4_0_dir = false;
+    int32_t st = check_repack(src, dst, &q4_0_dir);
     if (st) return st;
-    if (!dst) return QBN_ERR_NULL;
-    if (!known_format(dst->format) || dst->reserved != 0) return QBN_ERR_FORMAT;
-    const int32_t sf = src->format, df = dst->format;
-    // NVFP4 <-> CKE split-half blocks: the codes and subscale bytes move, scale2 is unchanged
-    const bool nv_src = sf == QBN_NVFP4 || sf == QBN_NVFP4_CKE;
-    const bool nv_dst = df == QBN_NVFP4 || df == QBN_NVFP4_CKE;
-    const bool src_int4 = sf == QBN_GPTQ4 || sf == QBN_AWQ4 || sf == QBN_Q4_0;
-    const bool dst_int4 = df == QBN_GPTQ4 || df == QBN_AWQ4 || df == QBN_Q4_0;
-    if (!((nv_src && nv_dst) || (src_int4 && dst_int4)) || sf == df) return QBN_ERR_UNSUPPORTED;
-    if (dst->n != src->n || dst->k != src->k) return QBN_ERR_SHAPE;
-    if (df == QBN_Q4_0 && src->group % 32) return QBN_ERR_GROUP;  // Q4_0 blocks of 32 need whole groups
-    if (sf == QBN_Q4_0 && (dst->group <= 0 || dst->group % 32)) return QBN_ERR_GROUP;
-    if (sf != QBN_Q4_0 && df != QBN_Q4_0 && !nv_src && dst->group != src->group) return QBN_ERR_GROUP;
-    if (nv_src && src->k % 64) return QBN_ERR_SHAPE;
-    st = check_tensor(dst);
-    if (st) return st;
-    const bool q4_0_dir = sf == QBN_Q4_0 || df == QBN_Q4_0;
     if (q4_0_dir) {  // these directions can refuse, and report it in status[0]
         if (!status) return QBN_ERR_NULL;
         if (!aligned(status, 8)) return QBN_ERR_ALIGN;
     }
     hipStream_t s = (hipStream_t)stream;
     if (src->n == 0 || src->k == 0) return q4_0_dir ? hip_status(qbn::launch_fill_i64(status, -1, 1, s)) : QBN_OK;
-    if (nv_src) return hip_status(qbn::launch_repack_cke(*src, (void *)dst->data, (void *)dst->scales, s));
-    return hip_status(qbn::launch_repack(*src, *dst, q4_0_dir ? status : nullptr, s));
+    if (src->format == QBN_NVFP4 || src->format == QBN_NVFP4_CKE)
+        return hip_status(qbn::launch_repack_cke(*src, (void *)dst->data, (void *)dst->scales, s));
+    return hip_status(qbn::launch_repack(*src, *dst, q4_0_dir ? status + 1 : nullptr, q4_0_dir ? status : nullptr, s));
+}
+
+int32_t qbn_repack_noalloc(const qbn_tensor *src, const qbn_tensor *dst, int64_t *result, void *stream) {
+    bool q4_0_dir = false;
+    int32_t st = check_repack(src, dst, &q4_0_dir);
+    if (st) return st;
+    if (q4_0_dir) {
+        if (!result) return QBN_ERR_NULL;
+        if (!aligned(result, 8)) return QBN_ERR_ALIGN;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (src->n == 0 || src->k == 0) return q4_0_dir ? hip_status(qbn::launch_fill_i64(result, -1, 1, s)) : QBN_OK;
+    if (src->format == QBN_NVFP4 || src->format == QBN_NVFP4_CKE)
+        return hip_status(qbn::launch_repack_cke(*src, (void *)dst->data, (void *)dst->scales, s));
+    int64_t *parts = nullptr;
+    if (q4_0_dir) {
+        const hipError_t e = qbn::repack_scratch(&parts);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(qbn::launch_repack(*src, *dst, parts, q4_0_dir ? result : nullptr, s));
 }
 
 int32_t qbn_validate_async(const qbn_tensor *w, int64_t *first_bad, void *stream) {

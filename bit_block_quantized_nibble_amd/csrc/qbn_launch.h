@@ -36,13 +36,18 @@ hipError_t launch_gemm_int4(const qbn_tensor &w, int64_t m, const void *x, int64
 bool gemm_int4_grid_fits(int64_t m, int64_t n);
 hipError_t launch_dequant(const qbn_tensor &w, void *out, int out_dtype, int out_layout, hipStream_t s);
 // int4 repacks. The Q4_0 directions first run a refusal scan whose
-// QBN_REPACK_SCAN_PARTS workgroups write their partial minima to
-// status[1..]; the repack kernels reduce them, write status[0] (-1 or the
-// first unrepresentable index) and write nothing on a refusal.
-hipError_t launch_repack(const qbn_tensor &src, const qbn_tensor &dst, int64_t *status, hipStream_t s);
+// QBN_REPACK_SCAN_PARTS workgroups write their partial minima to parts[];
+// the repack kernels reduce them, write *result (-1 or the first
+// unrepresentable index) and write nothing on a refusal. parts and result
+// are unused (may be NULL) by the other directions.
+hipError_t launch_repack(const qbn_tensor &src, const qbn_tensor &dst, int64_t *parts, int64_t *result,
+                         hipStream_t s);
+// The device address of this GPU's file-scope scratch for parts[] (resolved
+// once per device).
+hipError_t repack_scratch(int64_t **parts);
 hipError_t launch_fill_i64(int64_t *p, int64_t v, int64_t count, hipStream_t s);
-hipError_t launch_scan_zero_points(const uint8_t *zeros, int64_t count, int64_t *status, hipStream_t s);
-hipError_t launch_scan_q4_0_groups(const uint8_t *blocks, int64_t n, int64_t k, int64_t group, int64_t *status,
+hipError_t launch_scan_zero_points(const uint8_t *zeros, int64_t count, int64_t *parts, hipStream_t s);
+hipError_t launch_scan_q4_0_groups(const uint8_t *blocks, int64_t n, int64_t k, int64_t group, int64_t *parts,
                                    hipStream_t s);
 hipError_t launch_validate(const qbn_tensor &w, int64_t *first_bad, hipStream_t s);
 hipError_t launch_quantize_q8(const void *x, int x_dtype, int64_t k, int8_t *q, float *d, int32_t *bsums,

@@ -28,6 +28,8 @@
 // makes the int32 negative round-trips). A Q4_0 block's d is the bit
 // pattern of the source group's fp16 scale; in the other direction the
 // group scale is the d of the group's first block and the zero point is 8.
+#include <mutex>
+
 #include "qbn_device.h"
 #include "qbn_launch.h"
 
@@ -273,20 +275,20 @@ __device__ __forceinline__ void move_runs(uint8_t *lds, uint8_t *__restrict__ bl
 }
 
 // The Q4_0 kernels run after a refusal scan that has left its partial minima
-// in status[1 .. QBN_REPACK_SCAN_PARTS] (kNone where nothing was found).
+// in parts[0 .. QBN_REPACK_SCAN_PARTS - 1] (kNone where nothing was found).
 // Every workgroup takes their minimum (the same for all, so the whole grid
-// agrees), workgroup 0 publishes it as status[0] (-1 for none), and on a
+// agrees), workgroup 0 publishes it as *result (-1 for none), and on a
 // refusal every workgroup leaves before writing anything.
 constexpr unsigned long long kNone = 0x7FFFFFFFFFFFFFFFull;
 
-__device__ __forceinline__ bool refused(int64_t *status) {
+__device__ __forceinline__ bool refused(const int64_t *parts, int64_t *result) {
     unsigned long long m = kNone;
 #pragma unroll 8
     for (int g = 0; g < QBN_REPACK_SCAN_PARTS; ++g) {
-        const unsigned long long v = (unsigned long long)status[1 + g];
+        const unsigned long long v = (unsigned long long)parts[g];
         m = v < m ? v : m;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) status[0] = (m == kNone) ? -1 : (int64_t)m;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *result = (m == kNone) ? -1 : (int64_t)m;
     return m != kNone;
 }
 
@@ -297,8 +299,8 @@ __device__ __forceinline__ bool refused(int64_t *status) {
 __global__ __launch_bounds__(256) void k_gptq_to_q4_0(const uint32_t *__restrict__ src,
                                                       const uint16_t *__restrict__ scales, int64_t group,
                                                       uint8_t *__restrict__ dst, int64_t N, int64_t K, int words,
-                                                      int64_t *__restrict__ status) {
-    if (refused(status)) return;  // the whole grid leaves: nothing is written
+                                                      const int64_t *__restrict__ parts, int64_t *__restrict__ result) {
+    if (refused(parts, result)) return;  // the whole grid leaves: nothing is written
     __shared__ __attribute__((aligned(16))) uint8_t runs[64 * RS];
     const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, n0 = (int64_t)(blockIdx.x / nbt) * 64;
@@ -328,8 +330,8 @@ __global__ __launch_bounds__(256) void k_gptq_to_q4_0(const uint32_t *__restrict
 __global__ __launch_bounds__(256) void k_q4_0_to_gptq(const uint8_t *__restrict__ src, uint32_t *__restrict__ dst,
                                                       uint16_t *__restrict__ gscales, uint8_t *__restrict__ gzeros,
                                                       int64_t group, int64_t N, int64_t K, int words,
-                                                      int64_t *__restrict__ status) {
-    if (refused(status)) return;
+                                                      const int64_t *__restrict__ parts, int64_t *__restrict__ result) {
+    if (refused(parts, result)) return;
     __shared__ __attribute__((aligned(16))) uint8_t runs[64 * RS];
     const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, n0 = (int64_t)(blockIdx.x / nbt) * 64;
@@ -363,8 +365,8 @@ __global__ __launch_bounds__(256) void k_q4_0_to_gptq(const uint8_t *__restrict_
 __global__ __launch_bounds__(256) void k_awq_to_q4_0(const uint32_t *__restrict__ src,
                                                      const uint16_t *__restrict__ scales, int64_t group,
                                                      uint8_t *__restrict__ dst, int64_t N, int64_t K, int words,
-                                                     int64_t *__restrict__ status) {
-    if (refused(status)) return;
+                                                     const int64_t *__restrict__ parts, int64_t *__restrict__ result) {
+    if (refused(parts, result)) return;
     __shared__ __attribute__((aligned(16))) uint8_t runs[256 * RS];
     const int64_t G = N / 8, nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, g0 = (int64_t)(blockIdx.x / nbt) * 32;
@@ -395,8 +397,8 @@ __global__ __launch_bounds__(256) void k_awq_to_q4_0(const uint32_t *__restrict_
 __global__ __launch_bounds__(256) void k_q4_0_to_awq(const uint8_t *__restrict__ src, uint32_t *__restrict__ dst,
                                                      uint16_t *__restrict__ gscales, uint8_t *__restrict__ gzeros,
                                                      int64_t group, int64_t N, int64_t K, int words,
-                                                     int64_t *__restrict__ status) {
-    if (refused(status)) return;
+                                                     const int64_t *__restrict__ parts, int64_t *__restrict__ result) {
+    if (refused(parts, result)) return;
     __shared__ __attribute__((aligned(16))) uint8_t runs[256 * RS];
     const int64_t G = N / 8, nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, g0 = (int64_t)(blockIdx.x / nbt) * 32;
@@ -433,7 +435,35 @@ __global__ __launch_bounds__(256) void k_q4_0_to_awq(const uint8_t *__restrict__
 
 }  // namespace
 
-hipError_t launch_repack(const qbn_tensor &src, const qbn_tensor &dst, int64_t *status, hipStream_t s) {
+// Scratch of the allocation-free repack (qbn_repack_noalloc): the partial
+// results of the refusal scan, one copy per GPU in file-scope device memory,
+// held until the process ends. The scan writes every word on every call, so
+// nothing in it has to be cleared; calls that overlap on one GPU race on it.
+static __device__ __align__(256) int64_t scratch[QBN_REPACK_SCAN_PARTS];
+
+hipError_t repack_scratch(int64_t **parts) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int64_t *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // the symbol's address on the current device; the host-side name
+        // `scratch` is never passed to a kernel
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<int64_t *>(p);
+    }
+    *parts = addr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_repack(const qbn_tensor &src, const qbn_tensor &dst, int64_t *parts, int64_t *result,
+                         hipStream_t s) {
     const int64_t N = src.n, K = src.k;
     const int sf = src.format, df = dst.format;
     void *const dst_data = const_cast<void *>(dst.data);
@@ -471,8 +501,8 @@ hipError_t launch_repack(const qbn_tensor &src, const qbn_tensor &dst, int64_t *
         return hipErrorInvalidValue;
     // refusal scan: every zero point must be 8 (to Q4_0), or every block of a
     // target group must carry the same d (from Q4_0)
-    hipError_t e = to_q4 ? launch_scan_zero_points((const uint8_t *)src.zeros, (K / src.group) * N, status, s)
-                         : launch_scan_q4_0_groups((const uint8_t *)src.data, N, K, dst.group, status, s);
+    hipError_t e = to_q4 ? launch_scan_zero_points((const uint8_t *)src.zeros, (K / src.group) * N, parts, s)
+                         : launch_scan_q4_0_groups((const uint8_t *)src.data, N, K, dst.group, parts, s);
     if (e != hipSuccess) return e;
     const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     // Q4_0 runs move as 4-byte words when every run starts and ends on a
@@ -494,17 +524,17 @@ hipError_t launch_repack(const qbn_tensor &src, const qbn_tensor &dst, int64_t *
         if (sf == QBN_GPTQ4)
             hipLaunchKernelGGL(k_gptq_to_q4_0, grid, blk, 0, s, (const uint32_t *)src.data,
                                (const uint16_t *)src.scales, (int64_t)src.group, (uint8_t *)dst_data, N, K, words,
-                               status);
+                               parts, result);
         else if (sf == QBN_AWQ4)
             hipLaunchKernelGGL(k_awq_to_q4_0, grid, blk, 0, s, (const uint32_t *)src.data,
                                (const uint16_t *)src.scales, (int64_t)src.group, (uint8_t *)dst_data, N, K, words,
-                               status);
+                               parts, result);
         else if (df == QBN_GPTQ4)
             hipLaunchKernelGGL(k_q4_0_to_gptq, grid, blk, 0, s, (const uint8_t *)src.data, (uint32_t *)dst_data, gs,
-                               gz, (int64_t)dst.group, N, K, words, status);
+                               gz, (int64_t)dst.group, N, K, words, parts, result);
         else
             hipLaunchKernelGGL(k_q4_0_to_awq, grid, blk, 0, s, (const uint8_t *)src.data, (uint32_t *)dst_data, gs,
-                               gz, (int64_t)dst.group, N, K, words, status);
+                               gz, (int64_t)dst.group, N, K, words, parts, result);
         return hipGetLastError();
     }
     return hipSuccess;

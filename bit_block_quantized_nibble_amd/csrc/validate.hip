@@ -78,10 +78,10 @@ __global__ __launch_bounds__(kBlock) void k_scan_q4_0(const uint8_t *__restrict_
 
 // Refusal scans of the Q4_0 repacks. Exactly QBN_REPACK_SCAN_PARTS
 // workgroups stride over the elements; workgroup g writes the smallest
-// offending index it saw (or kNone) to status[1 + g]. Every word is written
-// on every call, so nothing has to be cleared first; the repack kernel that
+// offending index it saw (or kNone) to parts[g]. Every word is written on
+// every call, so nothing has to be cleared first; the repack kernel that
 // follows takes the minimum of the parts.
-__device__ __forceinline__ void part_min_store(unsigned long long mine, unsigned long long *status) {
+__device__ __forceinline__ void part_min_store(unsigned long long mine, unsigned long long *parts) {
     __shared__ unsigned long long red[kBlock / 64];
     for (int off = 32; off > 0; off >>= 1) {
         const unsigned long long o = __shfl_xor(mine, off, 64);
@@ -92,24 +92,24 @@ __device__ __forceinline__ void part_min_store(unsigned long long mine, unsigned
     if (threadIdx.x == 0) {
         unsigned long long m = red[0];
         for (int w = 1; w < kBlock / 64; ++w) m = red[w] < m ? red[w] : m;
-        status[1 + blockIdx.x] = m;
+        parts[blockIdx.x] = m;
     }
 }
 
 // Zero points that Q4_0 cannot hold: every one must be 8.
 __global__ __launch_bounds__(kBlock) void k_part_zero8(const uint8_t *__restrict__ zeros, int64_t count,
-                                                        unsigned long long *status) {
+                                                        unsigned long long *parts) {
     unsigned long long mine = kNone;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
         if (zeros[i] != 8u && (unsigned long long)i < mine) mine = (unsigned long long)i;
-    part_min_store(mine, status);
+    part_min_store(mine, parts);
 }
 
 // Q4_0 blocks [n][k/32] whose d differs from the first block of their group
 // of bpg blocks along k.
 __global__ __launch_bounds__(kBlock) void k_part_q4_0_groups(const uint8_t *__restrict__ blocks, int64_t nblocks,
-                                                              int64_t bpr, int64_t bpg, unsigned long long *status) {
+                                                              int64_t bpr, int64_t bpg, unsigned long long *parts) {
     unsigned long long mine = kNone;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nblocks; i += stride) {
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kBlock) void k_part_q4_0_groups(const uint8_t *__re
         if (d != *reinterpret_cast<const uint16_t *>(blocks + 18 * lead) && (unsigned long long)i < mine)
             mine = (unsigned long long)i;
     }
-    part_min_store(mine, status);
+    part_min_store(mine, parts);
 }
 
 // GPTQ / AWQ companions: scale not finite or logical zero point above 15.
@@ -230,16 +230,16 @@ hipError_t launch_fill_i64(int64_t *p, int64_t v, int64_t count, hipStream_t s) 
     return hipGetLastError();
 }
 
-hipError_t launch_scan_zero_points(const uint8_t *zeros, int64_t count, int64_t *status, hipStream_t s) {
+hipError_t launch_scan_zero_points(const uint8_t *zeros, int64_t count, int64_t *parts, hipStream_t s) {
     hipLaunchKernelGGL(k_part_zero8, dim3(QBN_REPACK_SCAN_PARTS), dim3(kBlock), 0, s, zeros, count,
-                       reinterpret_cast<unsigned long long *>(status));
+                       reinterpret_cast<unsigned long long *>(parts));
     return hipGetLastError();
 }
 
-hipError_t launch_scan_q4_0_groups(const uint8_t *blocks, int64_t n, int64_t k, int64_t group, int64_t *status,
+hipError_t launch_scan_q4_0_groups(const uint8_t *blocks, int64_t n, int64_t k, int64_t group, int64_t *parts,
                                    hipStream_t s) {
     hipLaunchKernelGGL(k_part_q4_0_groups, dim3(QBN_REPACK_SCAN_PARTS), dim3(kBlock), 0, s, blocks, n * (k / 32),
-                       k / 32, group / 32, reinterpret_cast<unsigned long long *>(status));
+                       k / 32, group / 32, reinterpret_cast<unsigned long long *>(parts));
     return hipGetLastError();
 }
 

@@ -381,6 +381,19 @@ QBN_API int32_t qbn_unpack_bits(const void *words_lo, const void *words_hi, int6
  * the stream. No buffer of dst may overlap src's. */
 QBN_API int32_t qbn_repack(const qbn_tensor *src, const qbn_tensor *dst, int64_t *status, void *stream);
 
+/* qbn_repack for callers that cannot allocate device memory or a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same operation and argument rules, but the refusal scan's
+ * QBN_REPACK_SCAN_PARTS partial results live in the library's own scratch,
+ * a file-scope device array of QBN_REPACK_SCAN_PARTS int64 (512 bytes) that
+ * each GPU holds until the process ends, so the caller passes only *result
+ * (a DEVICE int64, 8-byte aligned; required for the Q4_0 directions, which
+ * write -1 or the first offending index to it, unused by the others). The
+ * scratch size does not depend on the tensor, so no size is refused for it.
+ * The call allocates nothing. Calls that overlap on one GPU (other streams,
+ * other threads) share that GPU's scratch and race on it: serialize them. */
+QBN_API int32_t qbn_repack_noalloc(const qbn_tensor *src, const qbn_tensor *dst, int64_t *result, void *stream);
+
 /* Load-time fail-closed scan ([NV] section 7.3: a NaN scale byte or an
  * inconsistent companion refuses the load; [FB] section 7). Synchronous: the
  * scan runs on `stream`, the call waits for it and returns QBN_OK if the

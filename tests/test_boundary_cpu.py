@@ -37,7 +37,7 @@ def T(fmt, n, k, data=A, scales=B, zeros=C, scale2=1.0, group=0, reserved=0):
 def test_exports_every_declared_symbol(lib):
     header = open(os.path.join(ROOT, "include", "qbn.h")).read()
     declared = re.findall(r"QBN_API\s+[\w\s\*]+?\b(qbn_\w+)\s*\(", header)
-    assert len(declared) == 22
+    assert len(declared) == 23
     assert set(declared) == set(qbn.EXPORTED)
     so = ctypes.CDLL(qbn.lib_path())
     for name in declared:
@@ -249,6 +249,13 @@ def test_repack_rejections(lib):
     assert r(T(Q0, 8, 64), T(AW, 8, 64, group=32), None, None) == NULL
     assert r(gp, T(Q0, 8, 64), S + 4, None) == ALIGN
     assert r(T(GP, 8, 0, group=32), T(AW, 8, 0, group=32), None, None) == OK      # empty, status not needed
+    # the allocation-free variant applies the same rules to its single result word
+    rn = lib.qbn_repack_noalloc
+    assert rn(gp, T(Q0, 8, 64), None, None) == NULL
+    assert rn(gp, T(Q0, 8, 64), S + 4, None) == ALIGN
+    assert rn(gp, T(AW, 8, 64, group=64), S, None) == GROUP
+    assert rn(T(MX, 8, 64), T(Q0, 8, 64), S, None) == UNSUP
+    assert rn(T(GP, 8, 0, group=32), T(AW, 8, 0, group=32), None, None) == OK
 
 
 def test_validate_rejections(lib):
