@@ -549,6 +549,16 @@ ORACLE_API int oracle_dequant_rows(int fmt, const uint8_t *data, const uint8_t *
 /* Dot products                                                        */
 /* ------------------------------------------------------------------ */
 
+/* The value of a Neumaier sum: the running sum plus its compensation. The
+ * compensation only exists for finite sums; once the running sum is an
+ * infinity or NaN (weights beyond binary32's range decode to +-inf), the
+ * IEEE sum itself is the value: +inf plus finite terms stays +inf, and
+ * infinities of both signs give NaN. */
+static double neumaier_value(double sum, double comp)
+{
+    return isfinite(sum) ? sum + comp : sum;
+}
+
 /* Neumaier-compensated binary64 sum of w[i]*x[i] (each product exact in
  * binary64 since both factors carry at most 24 significant bits), and the
  * plain binary64 sum of |w[i]*x[i]|. */
@@ -565,7 +575,7 @@ static void dot_f64(const float *w, const double *x, int64_t k, double *y, doubl
         sum = t;
         a += fabs(p);
     }
-    *y = sum + comp;
+    *y = neumaier_value(sum, comp);
     *sabs = a;
 }
 
@@ -617,7 +627,7 @@ ORACLE_API void oracle_gemv_kn(const float *W, int64_t K, int64_t N, const void 
             sum = t;
             a += fabs(p);
         }
-        y[i] = sum + comp;
+        y[i] = neumaier_value(sum, comp);
         sabs[i] = a;
     }
 }
@@ -754,7 +764,7 @@ ORACLE_API void oracle_q4k_w4a8_rows(const uint8_t *blocks, int64_t k, const int
                 }
             }
         }
-        y[ri] = sum + comp;
+        y[ri] = neumaier_value(sum, comp);
         sabs[ri] = sa;
     }
 }
@@ -985,7 +995,7 @@ ORACLE_API int oracle_mx_gemm_entries(const uint8_t *wcodes, const uint8_t *wsca
             sum = u;
             sa += fabs(p);
         }
-        y[t] = sum + comp;
+        y[t] = neumaier_value(sum, comp);
         sabs[t] = sa;
     }
     return 0;

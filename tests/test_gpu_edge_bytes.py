@@ -1,0 +1,266 @@
+"""GPU parity on the scale bytes at the ends of their ranges, inside the fused
+kernels themselves (the exhaustive decode sweeps of `dequantize` do not run
+the GEMV's or the GEMM's own scale decode).
+
+Every E8M0 byte 0..254 and every finite E4M3FN byte (both signs, the
+subnormals, the zero scales) reaches the GEMV's row kernel and its generic
+kernel ("Four Bits, Three Contracts" sections 3 and 4 define the two scale
+encodings; Muser, ch. 7 section 7.2, asks that what can be checked completely
+be checked completely). Each weight row holds one nonzero block, which carries
+the byte under test; the activations over that block are scaled by a power of
+two that brings the row's result near 1, so the 1e-5 relative tolerance is
+what decides, not the 1e-6 absolute floor. The GEMM gets the E8M0 bytes whose
+bf16 weights are subnormal (0, 1, 2) or near overflow (252..254) the same way,
+checked against the bf16 band.
+
+Weights that overflow binary32 (E8M0 254 with |E2M1| >= 2, 253 with
+|E2M1| >= 4, NVFP4 with a large scale2) decode to +-inf in the oracle. The
+kernels factor the block scale out of the block sum, so they agree with the
+oracle where every such product overflows by itself (activations >= 1 and one
+sign per row): those rows must come out +-inf with the oracle's sign."""
+import numpy as np
+import pytest
+import torch
+
+import bit_block_quantized_nibble_amd as qbn
+import oracle
+import workloads
+from gpu_util import DEV, assert_within_tolerance, dev, host_bits, say, x_dev
+
+pytestmark = pytest.mark.gpu
+
+E4M3FN_FINITE = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+def _e8m0_code_cap(byte):
+    """Largest E2M1 magnitude code (0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6)
+    whose weight stays finite in binary32 under this E8M0 byte."""
+    return 3 if byte == 254 else 5 if byte == 253 else 7
+
+
+def _nibbles(rng, size, cap):
+    mag = rng.integers(0, cap + 1, size)
+    return (mag | (rng.integers(0, 2, size) << 3)).astype(np.uint8)
+
+
+def _pack(nib):
+    """[n][k] nibbles -> [n][k/2] bytes, the even element in the low nibble."""
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _x_host(rng, k, shift, block, xdt):
+    """Activations u * 2^shift[k // block], |u| in [0.5, 2), random signs."""
+    u = rng.uniform(0.5, 2.0, k) * rng.choice([-1.0, 1.0], k)
+    x32 = (u * np.exp2(np.repeat(shift, block).astype(np.float64))).astype(np.float32)
+    assert np.isfinite(x32).all() and (np.abs(x32) >= np.float32(2.0 ** -126)).all()
+    return x32 if xdt == "f32" else workloads.bf16_bits_from_f32(x32)
+
+
+def _gemv(fmt, n, k, data, scales, scale2, x, what):
+    w = qbn.QTensor(fmt, n, k, dev(data), dev(scales), scale2=scale2)
+    say("gemv edge bytes", what, fmt, n, k, x.dtype)
+    y = qbn.quantized_gemv(w, x_dev(x))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _single_block_rows(rng, n, nb, block, row_byte, cap_of):
+    """Row r is zero except in block sigma[r], which has scale byte
+    row_byte[r] and random codes up to cap_of(byte); every other scale byte of
+    the row is drawn from the finite bytes."""
+    sigma = rng.permutation(nb)[:n] if n <= nb else np.arange(n) % nb
+    nib = np.zeros((n, nb * block), np.uint8)
+    for r in range(n):
+        j = sigma[r]
+        nib[r, block * j:block * (j + 1)] = _nibbles(rng, block, cap_of(row_byte[r]))
+    return sigma, _pack(nib)
+
+
+@pytest.mark.parametrize("k", [8192, 8160])  # 256 blocks: the row kernel; 255: the generic kernel
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_gemv_mxfp4_every_e8m0_byte(k, xdt):
+    rng = np.random.default_rng(k + (xdt == "bf16"))
+    nb = k // 32
+    n = nb
+    row_byte = (rng.permutation(n) % 255).astype(np.uint8)  # 0..254, each at least once
+    sigma, data = _single_block_rows(rng, n, nb, 32, row_byte, _e8m0_code_cap)
+    scales = rng.integers(0, 255, (n, nb)).astype(np.uint8)
+    scales[np.arange(n), sigma] = row_byte
+    shift = np.zeros(nb, np.int64)
+    shift[sigma] = np.clip(127 - row_byte.astype(np.int64), -100, 119)
+    x = _x_host(rng, k, shift, 32, xdt)
+    y = _gemv("mxfp4", n, k, data, scales, 1.0, x, "e8m0 sweep")
+    y_ref, s_ref = oracle.gemv_rows(oracle.MXFP4, data, scales, 1.0, k, x, range(n))
+    # every row's terms are large enough that the relative part of the bound decides
+    assert np.isfinite(y_ref).all() and (s_ref > 2.0 ** -10).all()
+    assert_within_tolerance(y, y_ref, s_ref, "mxfp4 every E8M0 byte, k=%d x=%s" % (k, xdt))
+
+
+def _e4m3fn_values(b):
+    return torch.from_numpy(np.asarray(b, np.uint8)).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("k", [4096, 4080])  # 256 blocks: the row kernel; 255: the generic kernel
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+@pytest.mark.parametrize("scale2", [1.0, 0.37])
+def test_gemv_nvfp4_every_finite_e4m3fn_byte(k, xdt, scale2):
+    rng = np.random.default_rng(k * 3 + (xdt == "bf16") + int(scale2 * 100))
+    nb = k // 16
+    n = nb
+    row_byte = E4M3FN_FINITE[rng.permutation(n) % E4M3FN_FINITE.size]
+    sigma, data = _single_block_rows(rng, n, nb, 16, row_byte, lambda b: 7)
+    scales = E4M3FN_FINITE[rng.integers(0, E4M3FN_FINITE.size, (n, nb))]
+    scales[np.arange(n), sigma] = row_byte
+    mag = np.abs(_e4m3fn_values(row_byte))
+    shift = np.zeros(nb, np.int64)
+    shift[sigma] = np.where(mag > 0, -np.floor(np.log2(np.where(mag > 0, mag, 1.0))), 0).astype(np.int64)
+    x = _x_host(rng, k, shift, 16, xdt)
+    s2 = float(np.float32(scale2))
+    y = _gemv("nvfp4", n, k, data, scales, s2, x, "e4m3fn sweep")
+    y_ref, s_ref = oracle.gemv_rows(oracle.NVFP4, data, scales, s2, k, x, range(n))
+    assert np.isfinite(y_ref).all()
+    zero_rows = mag == 0
+    assert zero_rows.sum() >= 2 and (y_ref[zero_rows] == 0).all()
+    assert (s_ref[~zero_rows] > 0.25).all()
+    assert_within_tolerance(y, y_ref, s_ref, "nvfp4 every finite E4M3FN byte, k=%d x=%s scale2=%g" % (k, xdt, s2))
+    # a zero scale gives a zero row, whatever its codes
+    assert (y[zero_rows] == 0).all()
+
+
+def _overflow_rows(rng, k, block, big_byte, small_byte):
+    """Four rows: 0 all blocks at big_byte with positive codes >= 2 (every
+    weight beyond binary32 when big_byte is), 1 its negation, 2 a finite
+    control row at small_byte, 3 the control row with one block of row 0."""
+    nb = k // block
+    nib = np.zeros((4, k), np.uint8)
+    nib[0] = rng.integers(4, 8, k)            # E2M1 2, 3, 4, 6
+    nib[1] = nib[0] | 8                        # the same, negative
+    nib[2] = _nibbles(rng, k, 7)
+    nib[3] = nib[2]
+    j = nb // 3
+    nib[3, block * j:block * (j + 1)] = nib[0, block * j:block * (j + 1)]
+    scales = np.full((4, nb), small_byte, np.uint8)
+    scales[0:2] = big_byte
+    scales[3, j] = big_byte
+    return _pack(nib), scales
+
+
+def _check_overflow_rows(y, y_ref, s_ref, what):
+    assert y_ref[0] == np.inf and y_ref[1] == -np.inf and y_ref[3] == np.inf, what
+    assert y[0] == np.inf and y[1] == -np.inf and y[3] == np.inf, "%s: got %r" % (what, y)
+    assert_within_tolerance(y[2:3], y_ref[2:3], s_ref[2:3], what + " control row")
+
+
+@pytest.mark.parametrize("k", [8192, 8160])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_gemv_mxfp4_overflowing_rows(k, xdt):
+    rng = np.random.default_rng(k + 5)
+    data, scales = _overflow_rows(rng, k, 32, 254, 120)
+    x = _x_host(rng, k, np.zeros(k // 32, np.int64), 32, xdt)
+    x = np.abs(x) if xdt == "f32" else (x & np.uint16(0x7FFF))  # positive, 0.5 .. 2
+    y = _gemv("mxfp4", 4, k, data, scales, 1.0, x, "overflow rows")
+    y_ref, s_ref = oracle.gemv_rows(oracle.MXFP4, data, scales, 1.0, k, x, range(4))
+    _check_overflow_rows(y, y_ref, s_ref, "mxfp4 overflow rows k=%d x=%s" % (k, xdt))
+
+
+@pytest.mark.parametrize("k", [4096, 4080])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_gemv_nvfp4_overflowing_rows(k, xdt):
+    rng = np.random.default_rng(k + 6)
+    # scale2 2^120: E4M3FN 448 (0x7E) times E2M1 >= 2 overflows; the control
+    # rows' scale 2^-9 (0x01, the smallest subnormal) keeps them finite
+    data, scales = _overflow_rows(rng, k, 16, 0x7E, 0x01)
+    x = _x_host(rng, k, np.zeros(k // 16, np.int64), 16, xdt)
+    x = np.abs(x) if xdt == "f32" else (x & np.uint16(0x7FFF))
+    s2 = 2.0 ** 120
+    y = _gemv("nvfp4", 4, k, data, scales, s2, x, "overflow rows")
+    y_ref, s_ref = oracle.gemv_rows(oracle.NVFP4, data, scales, s2, k, x, range(4))
+    _check_overflow_rows(y, y_ref, s_ref, "nvfp4 overflow rows k=%d x=%s" % (k, xdt))
+
+
+# ------------------------------------------------------------------ GEMM
+
+def _bf16_value(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _gemm(n, k, data, scales, X, what):
+    m = X.shape[0]
+    w = qbn.QTensor("mxfp4", n, k, dev(data), dev(scales))
+    say("gemm edge bytes", what, m, n, k)
+    Y = qbn.quantized_gemm(w, dev(X).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    return host_bits(Y).reshape(m, n)
+
+
+GEMM_EDGE_BYTES = np.array([0, 1, 2, 252, 253, 254, 127, 100], np.uint8)
+
+
+# the 256 x 256 kernel's chunked interior path; its per-k-tile interior path
+# with ragged edge tiles; the 128 x 128 kernel
+@pytest.mark.parametrize("m,n,k", [(256, 256, 2048), (300, 260, 1088), (96, 200, 1024)])
+def test_gemm_edge_e8m0_bytes(m, n, k):
+    """E8M0 0, 1, 2 put bf16-subnormal weights (down to 2^-128) into the
+    matrix cores; 252..254 weights up to 1.5 * 2^127. Each weight row has one
+    nonzero block; block column j carries byte GEMM_EDGE_BYTES[j % 8] in the
+    rows that use it, and X over column j is scaled to bring the products
+    near 1."""
+    rng = np.random.default_rng(m + n + k)
+    nb = k // 32
+    col_byte = GEMM_EDGE_BYTES[np.arange(nb) % GEMM_EDGE_BYTES.size]
+    active = rng.integers(0, nb, n)
+    nib = np.zeros((n, k), np.uint8)
+    for r in range(n):
+        j = active[r]
+        nib[r, 32 * j:32 * (j + 1)] = _nibbles(rng, 32, _e8m0_code_cap(col_byte[j]))
+    data = _pack(nib)
+    scales = rng.integers(0, 255, (n, nb)).astype(np.uint8)
+    scales[np.arange(n), active] = col_byte[active]
+    shift = np.clip(127 - col_byte.astype(np.int64), -100, 119)
+    u = rng.uniform(0.5, 2.0, (m, k)) * rng.choice([-1.0, 1.0], (m, k))
+    X = workloads.bf16_bits_from_f32((u * np.exp2(np.repeat(shift, 32))[None, :]).astype(np.float32))
+    Y = _gemm(n, k, data, scales, X, "edge e8m0")
+    ms, ns = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+    ms, ns = ms.ravel(), ns.ravel()
+    y_ref, s_ref = oracle.gemm_entries(oracle.MXFP4, data, scales, 1.0, k, X, ms, ns)
+    assert np.isfinite(y_ref).all()
+    sub = np.isin(col_byte[active[ns]], [0, 1, 2])
+    assert sub.sum() > 0 and (s_ref > 2.0 ** -8).all()
+    T = 1e-5 * s_ref + 1e-6
+    lo = _bf16_value(oracle.bf16_rne_array((y_ref - T).astype(np.float32)))
+    hi = _bf16_value(oracle.bf16_rne_array((y_ref + T).astype(np.float32)))
+    got = _bf16_value(Y[ms, ns])
+    bad = ~((lo <= got) & (got <= hi))
+    if bad.any():
+        i = int(np.argwhere(bad)[0][0])
+        raise AssertionError("gemm %dx%dx%d: %d of %d entries outside the band; first (m=%d, n=%d, byte %d): got %r, "
+                             "ref %r" % (m, n, k, int(bad.sum()), bad.size, ms[i], ns[i], col_byte[active[ns[i]]],
+                                         got[i], y_ref[i]))
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 256, 2048), (96, 200, 1024)])
+def test_gemm_overflowing_weight_rows(m, n, k):
+    """Weight rows 0 and 1 at E8M0 254 with codes >= 2 (every weight beyond
+    binary32 and bf16) against positive X: columns 0 and 1 of Y are +inf and
+    -inf; the other columns are ordinary and checked against the band."""
+    rng = np.random.default_rng(m * 7 + k)
+    nb = k // 32
+    nib = _nibbles(rng, (n, k), 7)
+    nib[0] = rng.integers(4, 8, k)
+    nib[1] = nib[0] | 8
+    data = _pack(nib)
+    scales = (120 + rng.integers(0, 8, (n, nb))).astype(np.uint8)
+    scales[0:2] = 254
+    X = workloads.bf16_bits_from_f32(rng.uniform(1.0, 2.0, (m, k)).astype(np.float32))
+    Y = _gemm(n, k, data, scales, X, "overflow rows")
+    assert (Y[:, 0] == 0x7F80).all() and (Y[:, 1] == 0xFF80).all()
+    ms, ns = np.meshgrid(np.arange(0, m, 5), np.arange(2, n, 3), indexing="ij")
+    ms, ns = ms.ravel(), ns.ravel()
+    y_ref, s_ref = oracle.gemm_entries(oracle.MXFP4, data, scales, 1.0, k, X, ms, ns)
+    T = 1e-5 * s_ref + 1e-6
+    lo = _bf16_value(oracle.bf16_rne_array((y_ref - T).astype(np.float32)))
+    hi = _bf16_value(oracle.bf16_rne_array((y_ref + T).astype(np.float32)))
+    got = _bf16_value(Y[ms, ns])
+    assert ((lo <= got) & (got <= hi)).all()
+    y0, _ = oracle.gemm_entries(oracle.MXFP4, data, scales, 1.0, k, X, [0, 0], [0, 1])
+    assert y0[0] == np.inf and y0[1] == -np.inf

@@ -4,6 +4,9 @@ RNE_bf16(y_ref - T) <= y <= RNE_bf16(y_ref + T), T = 1e-5 * sum|w x| + 1e-6:
 rounding to nearest is monotone, so any binary32 result within T of the exact
 value rounds into this band. Inputs whose partial sums are all exact must
 match bit for bit."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -37,8 +40,20 @@ def _run(inp, what):
     return host_bits(Y).reshape(m, n)
 
 
+def _oracle_entries(inp, ms, ns):
+    """The oracle's entries, split over the host's cores (each call releases
+    the interpreter lock while the C oracle runs)."""
+    ms, ns = np.asarray(ms), np.asarray(ns)
+    workers = max(1, min(16, os.cpu_count() or 1))
+    parts = [p for p in np.array_split(np.arange(ms.size), 4 * workers) if p.size]
+    with ThreadPoolExecutor(workers) as ex:
+        res = list(ex.map(lambda p: oracle.gemm_entries(oracle.MXFP4, inp["data"], inp["scales"], 1.0, inp["k"],
+                                                        inp["X"], ms[p], ns[p]), parts))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
 def _check_entries(inp, Ybits, ms, ns, what):
-    y_ref, s_ref = oracle.gemm_entries(oracle.MXFP4, inp["data"], inp["scales"], 1.0, inp["k"], inp["X"], ms, ns)
+    y_ref, s_ref = _oracle_entries(inp, ms, ns)
     got = _bf16_value(Ybits[ms, ns])
     lo, hi = _band(y_ref, s_ref)
     bad = ~((lo <= got) & (got <= hi))
@@ -84,6 +99,39 @@ def test_gemm_workload_full_size_sampled():
     ms = np.concatenate([rng.integers(0, m, 1500), np.full(64, m - 1), np.arange(64)])
     ns = np.concatenate([rng.integers(0, n, 1500), np.arange(n - 64, n), np.full(64, 0)])
     _check_entries(inp, Y, ms, ns, "workload 4 sampled")
+
+
+def test_gemm_workload_full_width_rows():
+    """64 full rows of the 2048 x 8192 x 8192 product: every column tile,
+    so every workgroup position of the XCD-banded order, 8 rows in each of
+    the 8 row tiles (first, last and inside)."""
+    inp = workloads.workload(4)
+    m, n = inp["m"], inp["n"]
+    Y = _run(inp, "full workload 4, 64 full rows")
+    rng = np.random.default_rng(64)
+    rows = np.concatenate([[256 * t, 256 * t + 255] + list(256 * t + rng.choice(np.arange(1, 255), 6, replace=False))
+                           for t in range(m // 256)])
+    assert rows.size == 64 and np.unique(rows).size == 64
+    ms, ns = np.meshgrid(rows, np.arange(n), indexing="ij")
+    _check_entries(inp, Y, ms.ravel(), ns.ravel(), "workload 4, 64 full rows")
+
+
+@pytest.mark.parametrize("k,x_binades", [(8192, 1), (8192, 13), (65536, 13)])
+def test_gemm_one_sign_long_k(k, x_binades):
+    """Positive weights and activations: nothing cancels, the accumulator
+    grows to the full sum, and every product is added far below it, which is
+    where the matrix core's alignment of the addends to the largest one drops
+    low bits. The band must still hold over 64 rows x 256 columns."""
+    rng = np.random.default_rng(k + x_binades)
+    m, n = 256, 256
+    nib = rng.integers(1, 8, (n, k)).astype(np.uint8)
+    data = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = rng.integers(112, 128, (n, k // 32)).astype(np.uint8)
+    x = rng.uniform(1.0, 2.0, (m, k)) * np.exp2(-rng.integers(0, x_binades, (m, k)))
+    inp = dict(n=n, k=k, m=m, data=data, scales=scales, X=workloads.bf16_bits_from_f32(x.astype(np.float32)))
+    Y = _run(inp, "one sign")
+    ms, ns = np.meshgrid(np.arange(0, m, 4), np.arange(n), indexing="ij")
+    _check_entries(inp, Y, ms.ravel(), ns.ravel(), "one-sign %d x %d x %d" % (m, n, k))
 
 
 def test_gemm_deterministic_and_strided():

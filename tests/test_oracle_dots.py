@@ -76,3 +76,30 @@ def test_compensated_sum_survives_cancellation():
     y, S = oracle.gemv_rows(oracle.MXFP4, codes, np.array([[126]], np.uint8), 1.0, 32, x, [0])
     assert y[0] == 1.0
     assert S[0] == 2.0 ** 61 + 1.0
+
+
+def test_rows_with_weights_beyond_binary32_follow_ieee_sums():
+    """MXFP4 scale byte 254 with E2M1 codes >= 2 decodes beyond binary32 to
+    +-inf (IEEE overflow, no saturation). The dot of such a row is then fixed
+    by IEEE addition alone: infinities of one sign with finite terms give that
+    infinity, infinities of both signs give NaN. A compensated sum must not
+    turn the first case into NaN through its inf - inf correction term."""
+    k = 64
+    x = np.linspace(0.5, 1.5, k).astype(np.float32)
+    nib = np.zeros((4, k), np.uint8)
+    nib[0, :] = 7                 # +6 everywhere: every weight +inf
+    nib[1, :] = 15                # -6 everywhere: every weight -inf
+    nib[2, :] = 2                 # +1: finite, 2^127 each
+    nib[3, :] = 2
+    nib[3, 5], nib[3, 40] = 7, 15  # one +inf and one -inf weight
+    nib[2, 33] = 7                # one +inf weight among finite ones
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.full((4, k // 32), 254, np.uint8)
+    W = oracle.dequant_rows(oracle.MXFP4, codes, scales, 1.0, k, range(4))
+    assert np.isposinf(W[0]).all() and np.isneginf(W[1]).all()
+    y, S = oracle.gemv_rows(oracle.MXFP4, codes, scales, 1.0, k, x, range(4))
+    assert y[0] == np.inf and y[1] == -np.inf and y[2] == np.inf and np.isnan(y[3])
+    assert np.isposinf(S).all()
+    Xb = workloads.bf16_bits_from_f32(np.tile(x, (2, 1)))
+    Y, _ = oracle.gemm_entries(oracle.MXFP4, codes, scales, 1.0, k, Xb, [0, 1, 1, 0], [0, 1, 2, 3])
+    assert Y[0] == np.inf and Y[1] == -np.inf and Y[2] == np.inf and np.isnan(Y[3])
