@@ -281,37 +281,35 @@ static void q4_0_row(const uint8_t *blocks, int64_t k, int64_t r, float *out)
 /* int4 layouts: GPTQ, AWQ, Q4_0 codes <-> logical u8 matrix q[K][N]   */
 /* ------------------------------------------------------------------ */
 
-/* Generic b-bit little-endian word stream: logical element i occupies bits
- * [i*b, (i+1)*b) of a stream of 32-bit words; an element may straddle two
- * words when b does not divide 32. [BP] "The packing arithmetic". */
+/* Generic b-bit little-endian word stream ([BP] "The packing arithmetic"):
+ * the stream is the concatenation of the words' bits, least significant bit
+ * of word 0 first, and element i owns stream bits i*b .. i*b + b - 1, its
+ * own least significant bit first. Written bit by bit from that definition,
+ * so an element that runs past a word boundary needs no special case.
+ * 1 <= bits <= 32. */
+static unsigned stream_bit(const uint32_t *words, int64_t s)
+{
+    return (unsigned)(words[s / 32] >> (s % 32)) & 1u;
+}
+
 ORACLE_API void oracle_pack_bits(const uint32_t *vals, int64_t count, int bits, uint32_t *words)
 {
-    int64_t nwords = (count * bits + 31) / 32;
-    for (int64_t w = 0; w < nwords; ++w)
+    int64_t total = count * bits;
+    for (int64_t w = 0; w < (total + 31) / 32; ++w)
         words[w] = 0;
-    uint64_t mask = (bits >= 32) ? 0xFFFFFFFFull : ((1ull << bits) - 1ull);
-    for (int64_t i = 0; i < count; ++i) {
-        uint64_t v = (uint64_t)vals[i] & mask;
-        int64_t pos = i * bits;
-        int64_t w = pos / 32;
-        int off = (int)(pos % 32);
-        words[w] |= (uint32_t)((v << off) & 0xFFFFFFFFull);
-        if (off + bits > 32)
-            words[w + 1] |= (uint32_t)(v >> (32 - off));
+    for (int64_t s = 0; s < total; ++s) {
+        unsigned bit = (unsigned)(vals[s / bits] >> (s % bits)) & 1u;
+        words[s / 32] |= (uint32_t)bit << (s % 32);
     }
 }
 
 ORACLE_API void oracle_unpack_bits(const uint32_t *words, int64_t count, int bits, uint32_t *vals)
 {
-    uint64_t mask = (bits >= 32) ? 0xFFFFFFFFull : ((1ull << bits) - 1ull);
     for (int64_t i = 0; i < count; ++i) {
-        int64_t pos = i * bits;
-        int64_t w = pos / 32;
-        int off = (int)(pos % 32);
-        uint64_t v = (uint64_t)words[w] >> off;
-        if (off + bits > 32)
-            v |= (uint64_t)words[w + 1] << (32 - off);
-        vals[i] = (uint32_t)(v & mask);
+        uint32_t v = 0;
+        for (int t = 0; t < bits; ++t)
+            v |= (uint32_t)stream_bit(words, i * bits + t) << t;
+        vals[i] = v;
     }
 }
 

@@ -129,10 +129,7 @@ def test_gptq_awq_random(K, N, g):
 
 def test_gptq_awq_probes():
     K, N, g = 256, 256, 128
-    pat = ((np.arange(K)[:, None] * 7 + np.arange(N)[None, :] * 3) % 16).astype(np.uint8)
-    full = np.full((K, N), 15, np.uint8)
-    rng = np.random.default_rng(0)
-    rand = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    pat, rand, full = workloads.layout_probes(K, N)
     scales = np.full((K // g, N), 1.0, np.float16)
     zeros = np.zeros((K // g, N), np.uint8)
     for name, probe in (("patterned", pat), ("random", rand), ("all-15", full)):

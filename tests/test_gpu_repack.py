@@ -72,10 +72,7 @@ def test_repack_random(src, dst, K, N, g):
 
 def test_repack_probes_all_directions():
     K, N, g = 256, 256, 128
-    pat = ((np.arange(K)[:, None] * 7 + np.arange(N)[None, :] * 3) % 16).astype(np.uint8)
-    rng = np.random.default_rng(0)
-    rand = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
-    full = np.full((K, N), 15, np.uint8)
+    pat, rand, full = workloads.layout_probes(K, N)
     scales = np.full((K // g, N), 0x3C00, np.uint16)
     zeros = np.full((K // g, N), 8, np.uint8)
     for name, probe in (("patterned", pat), ("random", rand), ("all-15", full)):

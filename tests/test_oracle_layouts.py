@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads
 from exact import round_f32, same_val, frac
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -117,18 +118,10 @@ def test_q4_0_byte_rule():
                 assert blk[2 + j] >> 4 == q[32 * b + j + 16, n]
 
 
-def _probes(K, N):
-    pat = ((np.arange(K)[:, None] * 7 + np.arange(N)[None, :] * 3) % 16).astype(np.uint8)
-    rng = np.random.default_rng(0)
-    rand = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
-    full = np.full((K, N), 15, np.uint8)
-    return [pat, rand, full]
-
-
 def test_verification_probes_round_trip():
     g = golden("int4_layouts.json")["probes"]
     K, N = g["K"], g["N"]
-    for probe in _probes(K, N):
+    for probe in workloads.layout_probes(K, N):
         assert np.array_equal(oracle.gptq_unpack(oracle.gptq_pack(probe)), probe)
         assert np.array_equal(oracle.awq_unpack(oracle.awq_pack(probe)), probe)
         d = np.arange(N * (K // 32), dtype=np.uint16).reshape(N, K // 32)
@@ -136,7 +129,7 @@ def test_verification_probes_round_trip():
         assert np.array_equal(q2, probe) and np.array_equal(d2, d)
     # all-15: the top slot's high bit is the int32 sign bit; unpacking a signed
     # view must still give 15 everywhere
-    full = _probes(K, N)[2]
+    full = workloads.layout_probes(K, N)[2]
     qw = oracle.gptq_pack(full).view(np.int32)
     assert (qw == -1).all()
     assert np.array_equal(oracle.gptq_unpack(qw), full)
@@ -147,7 +140,7 @@ def test_wrong_axis_or_order_is_visible():
     # Failure modes: reading GPTQ along N, or ignoring AWQ's interleave, must
     # scramble the patterned probe.
     K, N = 64, 64
-    pat = _probes(K, N)[0]
+    pat = workloads.layout_probes(K, N)[0]
     awq = oracle.awq_pack(pat)
     plain = np.stack([oracle.pack_bits(pat[kk].reshape(-1), 4) for kk in range(K)])
     assert not np.array_equal(awq, plain)

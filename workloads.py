@@ -114,6 +114,19 @@ def q4_0_weights(rng, n: int, k: int):
     return blocks.reshape(n, k // 32, 18)
 
 
+def layout_probes(K: int, N: int):
+    """Three K x N code matrices for checking a 4-bit layout both ways
+    ("Bit Packing Architecture", Verification): a pattern whose value changes
+    with the row and the column at different rates, so that reading the
+    wrong axis or the wrong slot order gives different codes; seeded random
+    codes; and every code 15, which sets the int32 sign bit of each word."""
+    kk = np.arange(K, dtype=np.int64)[:, None]
+    nn = np.arange(N, dtype=np.int64)[None, :]
+    pattern = ((5 * kk + 11 * nn + kk // 16) % 16).astype(np.uint8)
+    rand = _rng(4242).integers(0, 16, size=(K, N)).astype(np.uint8)
+    return [pattern, rand, np.full((K, N), 15, np.uint8)]
+
+
 def int4_affine(rng, K: int, N: int, group: int):
     qweight = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
     scales = rng.uniform(1e-3, 1e-2, size=(K // group, N)).astype(np.float16)
