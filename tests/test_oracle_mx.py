@@ -97,8 +97,12 @@ def test_mx_quantize_is_nearest_grid_point(xfmt):
     for i in range(m):
         for b in range(k // 32):
             blk = x[i, 32 * b: 32 * b + 32].astype(np.float64)
-            e = int(np.floor(np.log2(np.abs(blk).max()))) - emax
-            assert scales[i, b] == e + 127
+            # the OCP shared scale puts the block's largest magnitude into the
+            # element format's top binade [2^emax, 2^(emax+1)), checked in
+            # exact rationals from the stored byte alone
+            e = int(scales[i, b]) - 127
+            top = Fraction(float(np.abs(blk).max())) / Fraction(2) ** e
+            assert Fraction(2) ** emax <= top < Fraction(2) ** (emax + 1), (i, b, e)
             s = 2.0 ** e
             for j in range(32):
                 got = vals[q[i, 32 * b + j]] * s
@@ -126,3 +130,19 @@ def test_mx_gemm_entries_exact(xfmt):
         exact = sum(frac(Xh[i, e]) * frac(W[j, e]) for e in range(k))
         assert y[t] == float(exact)
         assert S[t] == float(sum(abs(frac(Xh[i, e]) * frac(W[j, e])) for e in range(k)))
+
+
+@pytest.mark.parametrize("xfmt,emax", [("mxfp4", 2), ("mxfp8", 8)])
+def test_mx_scale_at_the_ends_of_binary32(xfmt, emax):
+    """Blocks whose top binade would need a scale below 2^-127 take byte 0
+    (the clamp of the shared exponent); the largest binary32 block takes the
+    byte that puts 2^127 into the top binade; an all-zero block takes byte 0."""
+    fmt = oracle.MXFP4 if xfmt == "mxfp4" else oracle.MXFP8
+    x = np.zeros((1, 96), np.float32)
+    x[0, :32] = np.float32(2.0 ** -140) * np.arange(1, 33, dtype=np.float32) / 32   # binary32 subnormals
+    x[0, 32:64] = np.float32(3.0e38) * np.linspace(-1, 1, 32, dtype=np.float32)
+    codes, scales = oracle.mx_quantize(x, fmt)
+    assert scales[0, 0] == 0
+    top = Fraction(float(np.abs(x[0, 32:64]).max())) / Fraction(2) ** (int(scales[0, 1]) - 127)
+    assert Fraction(2) ** emax <= top < Fraction(2) ** (emax + 1)
+    assert scales[0, 2] == 0 and not codes[0, (64 if xfmt == "mxfp8" else 32):].any()
