@@ -281,13 +281,25 @@ __device__ __forceinline__ void move_runs(uint8_t *lds, uint8_t *__restrict__ bl
 // refusal every workgroup leaves before writing anything.
 constexpr unsigned long long kNone = 0x7FFFFFFFFFFFFFFFull;
 
-__device__ __forceinline__ bool refused(const int64_t *parts, int64_t *result) {
-    unsigned long long m = kNone;
-#pragma unroll 8
-    for (int g = 0; g < QBN_REPACK_SCAN_PARTS; ++g) {
-        const unsigned long long v = (unsigned long long)parts[g];
-        m = v < m ? v : m;
+// The scan's minimum: one part per lane (there are as many parts as lanes),
+// then a butterfly minimum across the wave, so every lane of every wave
+// holds it.
+static_assert(QBN_REPACK_SCAN_PARTS == kWave, "one refusal-scan part per lane");
+__device__ __forceinline__ unsigned long long refusal_min(const int64_t *parts) {
+    unsigned long long m = (unsigned long long)parts[threadIdx.x & (kWave - 1)];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(m, off, kWave);
+        m = o < m ? o : m;
     }
+    return m;
+}
+
+// Workgroup 0 publishes the scan's result; true means refused. The kernels
+// read the parts first and ask this just before their first global store,
+// so the parts' latency overlaps their own loads; nothing is stored on a
+// refusal.
+__device__ __forceinline__ bool refused(unsigned long long m, int64_t *result) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *result = (m == kNone) ? -1 : (int64_t)m;
     return m != kNone;
 }
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(256) void k_gptq_to_q4_0(const uint32_t *__restrict
                                                       const uint16_t *__restrict__ scales, int64_t group,
                                                       uint8_t *__restrict__ dst, int64_t N, int64_t K, int words,
                                                       const int64_t *__restrict__ parts, int64_t *__restrict__ result) {
-    if (refused(parts, result)) return;  // the whole grid leaves: nothing is written
+    const unsigned long long rm = refusal_min(parts);
     __shared__ __attribute__((aligned(16))) uint8_t runs[64 * RS];
     const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, n0 = (int64_t)(blockIdx.x / nbt) * 64;
@@ -320,6 +332,7 @@ __global__ __launch_bounds__(256) void k_gptq_to_q4_0(const uint32_t *__restrict
             put_block(runs + c * RS, b, scales[((32 * bg) / group) * N + n], D);
         }
     }
+    if (refused(rm, result)) return;  // the whole grid leaves: nothing is written
     __syncthreads();
     move_runs<false, 64>(runs, dst, [&](int r) { return n0 + r; }, N, nbr, b0, nb, words);
 }
@@ -331,7 +344,7 @@ __global__ __launch_bounds__(256) void k_q4_0_to_gptq(const uint8_t *__restrict_
                                                       uint16_t *__restrict__ gscales, uint8_t *__restrict__ gzeros,
                                                       int64_t group, int64_t N, int64_t K, int words,
                                                       const int64_t *__restrict__ parts, int64_t *__restrict__ result) {
-    if (refused(parts, result)) return;
+    const unsigned long long rm = refusal_min(parts);
     __shared__ __attribute__((aligned(16))) uint8_t runs[64 * RS];
     const int64_t nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, n0 = (int64_t)(blockIdx.x / nbt) * 64;
@@ -339,6 +352,7 @@ __global__ __launch_bounds__(256) void k_q4_0_to_gptq(const uint8_t *__restrict_
     move_runs<true, 64>(runs, const_cast<uint8_t *>(src), [&](int r) { return n0 + r; }, N, nbr, b0, nb,
                         words);
     __syncthreads();
+    if (refused(rm, result)) return;
     const int c = threadIdx.x % 64;
     const int64_t n = n0 + c;
     if (n >= N) return;
@@ -366,7 +380,7 @@ __global__ __launch_bounds__(256) void k_awq_to_q4_0(const uint32_t *__restrict_
                                                      const uint16_t *__restrict__ scales, int64_t group,
                                                      uint8_t *__restrict__ dst, int64_t N, int64_t K, int words,
                                                      const int64_t *__restrict__ parts, int64_t *__restrict__ result) {
-    if (refused(parts, result)) return;
+    const unsigned long long rm = refusal_min(parts);
     __shared__ __attribute__((aligned(16))) uint8_t runs[256 * RS];
     const int64_t G = N / 8, nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, g0 = (int64_t)(blockIdx.x / nbt) * 32;
@@ -389,6 +403,7 @@ __global__ __launch_bounds__(256) void k_awq_to_q4_0(const uint32_t *__restrict_
             put_block(runs + (32 * s2 + g) * RS, b, scales[((32 * bg) / group) * N + n], D);
         }
     }
+    if (refused(rm, result)) return;
     __syncthreads();
     move_runs<false, 256>(runs, dst, [&](int r) { return 8 * (g0 + r % 32) + awq_col(r / 32); }, N, nbr, b0, nb,
                           words);
@@ -398,7 +413,7 @@ __global__ __launch_bounds__(256) void k_q4_0_to_awq(const uint8_t *__restrict__
                                                      uint16_t *__restrict__ gscales, uint8_t *__restrict__ gzeros,
                                                      int64_t group, int64_t N, int64_t K, int words,
                                                      const int64_t *__restrict__ parts, int64_t *__restrict__ result) {
-    if (refused(parts, result)) return;
+    const unsigned long long rm = refusal_min(parts);
     __shared__ __attribute__((aligned(16))) uint8_t runs[256 * RS];
     const int64_t G = N / 8, nbr = K / 32, nbt = (nbr + RB - 1) / RB;
     const int64_t b0 = (int64_t)(blockIdx.x % nbt) * RB, g0 = (int64_t)(blockIdx.x / nbt) * 32;
@@ -406,6 +421,7 @@ __global__ __launch_bounds__(256) void k_q4_0_to_awq(const uint8_t *__restrict__
     move_runs<true, 256>(runs, const_cast<uint8_t *>(src),
                          [&](int r) { return 8 * (g0 + r % 32) + awq_col(r / 32); }, N, nbr, b0, nb, words);
     __syncthreads();
+    if (refused(rm, result)) return;
     const int g = threadIdx.x % 32, b = threadIdx.x / 32;
     if (g0 + g >= G || b >= nb) return;
     const int64_t bg = b0 + b;

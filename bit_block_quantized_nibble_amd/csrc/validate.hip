@@ -81,8 +81,15 @@ __global__ __launch_bounds__(kBlock) void k_scan_q4_0(const uint8_t *__restrict_
 // offending index it saw (or kNone) to parts[g]. Every word is written on
 // every call, so nothing has to be cleared first; the repack kernel that
 // follows takes the minimum of the parts.
+// The repack refusal scans: exactly QBN_REPACK_SCAN_PARTS workgroups of
+// kScanThreads, each writing the lowest offending index it saw (kNone if
+// none) to parts[blockIdx.x]; the repack kernels reduce the parts. Every
+// thread issues all of its loads before it compares anything, so a scan
+// costs about one memory round trip rather than one per loop trip.
+constexpr int kScanThreads = 1024;
+
 __device__ __forceinline__ void part_min_store(unsigned long long mine, unsigned long long *parts) {
-    __shared__ unsigned long long red[kBlock / 64];
+    __shared__ unsigned long long red[kScanThreads / 64];
     for (int off = 32; off > 0; off >>= 1) {
         const unsigned long long o = __shfl_xor(mine, off, 64);
         mine = o < mine ? o : mine;
@@ -91,32 +98,75 @@ __device__ __forceinline__ void part_min_store(unsigned long long mine, unsigned
     __syncthreads();
     if (threadIdx.x == 0) {
         unsigned long long m = red[0];
-        for (int w = 1; w < kBlock / 64; ++w) m = red[w] < m ? red[w] : m;
+        for (int w = 1; w < kScanThreads / 64; ++w) m = red[w] < m ? red[w] : m;
         parts[blockIdx.x] = m;
     }
 }
 
-// Zero points that Q4_0 cannot hold: every one must be 8.
-__global__ __launch_bounds__(kBlock) void k_part_zero8(const uint8_t *__restrict__ zeros, int64_t count,
-                                                        unsigned long long *parts) {
+__device__ __forceinline__ unsigned long long umin64(unsigned long long a, unsigned long long b) {
+    return b < a ? b : a;
+}
+
+// Zero points that Q4_0 cannot hold: every one must be 8. The bytes before
+// the first 16-byte boundary and after the last are checked one by one, the
+// rest 16 at a time, four pieces per thread in flight.
+__global__ __launch_bounds__(kScanThreads) void k_part_zero8(const uint8_t *__restrict__ zeros, int64_t count,
+                                                              unsigned long long *parts) {
     unsigned long long mine = kNone;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
-        if (zeros[i] != 8u && (unsigned long long)i < mine) mine = (unsigned long long)i;
+    const int64_t t = (int64_t)blockIdx.x * kScanThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kScanThreads;
+    int64_t head = (int64_t)((16u - (unsigned)(reinterpret_cast<uintptr_t>(zeros) & 15u)) & 15u);
+    if (head > count) head = count;
+    const int64_t pieces = (count - head) / 16;
+    if (t < head && zeros[t] != 8u) mine = (unsigned long long)t;
+    const u32x4 *al = reinterpret_cast<const u32x4 *>(zeros + head);
+    for (int64_t p0 = t; p0 < pieces; p0 += 4 * stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t p = p0 + j * stride;
+            v[j] = p < pieces ? al[p] : u32x4{0x08080808u, 0x08080808u, 0x08080808u, 0x08080808u};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t x = w[q] ^ 0x08080808u;  // nonzero bytes are zero points other than 8
+                if (x != 0u)
+                    mine = umin64(mine, (unsigned long long)(head + 16 * (p0 + j * stride) + 4 * q +
+                                                             (__builtin_ctz(x) >> 3)));
+            }
+        }
+    }
+    for (int64_t i = head + 16 * pieces + t; i < count; i += stride)
+        if (zeros[i] != 8u) mine = umin64(mine, (unsigned long long)i);
     part_min_store(mine, parts);
 }
 
 // Q4_0 blocks [n][k/32] whose d differs from the first block of their group
-// of bpg blocks along k.
-__global__ __launch_bounds__(kBlock) void k_part_q4_0_groups(const uint8_t *__restrict__ blocks, int64_t nblocks,
-                                                              int64_t bpr, int64_t bpg, unsigned long long *parts) {
+// of bpg blocks along k; eight blocks per thread in flight.
+__global__ __launch_bounds__(kScanThreads) void k_part_q4_0_groups(const uint8_t *__restrict__ blocks,
+                                                                    int64_t nblocks, int64_t bpr, int64_t bpg,
+                                                                    unsigned long long *parts) {
     unsigned long long mine = kNone;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nblocks; i += stride) {
-        const int64_t lead = i - ((i % bpr) % bpg);
-        const uint16_t d = *reinterpret_cast<const uint16_t *>(blocks + 18 * i);
-        if (d != *reinterpret_cast<const uint16_t *>(blocks + 18 * lead) && (unsigned long long)i < mine)
-            mine = (unsigned long long)i;
+    const int64_t t = (int64_t)blockIdx.x * kScanThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kScanThreads;
+    for (int64_t i0 = t; i0 < nblocks; i0 += 8 * stride) {
+        uint16_t d[8], lead_d[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t i = i0 + j * stride;
+            const int64_t ic = i < nblocks ? i : i0;
+            const int64_t lead = ic - ((ic % bpr) % bpg);
+            d[j] = *reinterpret_cast<const uint16_t *>(blocks + 18 * ic);
+            lead_d[j] = *reinterpret_cast<const uint16_t *>(blocks + 18 * lead);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t i = i0 + j * stride;
+            if (i < nblocks && d[j] != lead_d[j]) mine = umin64(mine, (unsigned long long)i);
+        }
     }
     part_min_store(mine, parts);
 }
@@ -231,14 +281,15 @@ hipError_t launch_fill_i64(int64_t *p, int64_t v, int64_t count, hipStream_t s) 
 }
 
 hipError_t launch_scan_zero_points(const uint8_t *zeros, int64_t count, int64_t *parts, hipStream_t s) {
-    hipLaunchKernelGGL(k_part_zero8, dim3(QBN_REPACK_SCAN_PARTS), dim3(kBlock), 0, s, zeros, count,
+    hipLaunchKernelGGL(k_part_zero8, dim3(QBN_REPACK_SCAN_PARTS), dim3(kScanThreads), 0, s, zeros, count,
                        reinterpret_cast<unsigned long long *>(parts));
     return hipGetLastError();
 }
 
 hipError_t launch_scan_q4_0_groups(const uint8_t *blocks, int64_t n, int64_t k, int64_t group, int64_t *parts,
                                    hipStream_t s) {
-    hipLaunchKernelGGL(k_part_q4_0_groups, dim3(QBN_REPACK_SCAN_PARTS), dim3(kBlock), 0, s, blocks, n * (k / 32),
+    hipLaunchKernelGGL(k_part_q4_0_groups, dim3(QBN_REPACK_SCAN_PARTS), dim3(kScanThreads), 0, s, blocks,
+                       n * (k / 32),
                        k / 32, group / 32, reinterpret_cast<unsigned long long *>(parts));
     return hipGetLastError();
 }

@@ -215,3 +215,35 @@ def test_repack_q4_0_run_modes(src, dst, offset):
         want = _expect("q4_0", q, scales, g)
         assert np.array_equal(q4.cpu().numpy().reshape(want.shape), want)
         assert (raw[:offset].cpu() == 0).all() and (raw[offset + nbytes:].cpu() == 0).all()
+
+
+@pytest.mark.parametrize("offset", list(range(16)))
+def test_zero_point_scan_finds_the_first_index_at_any_alignment(offset):
+    """The refusal scan reads zero points 16 bytes at a time between a head
+    and a tail checked byte by byte: the first zero point other than 8 is
+    found wherever it sits (head, a 16-byte piece, tail) for a buffer at
+    any byte offset, and a clean buffer is accepted."""
+    K, N, g = 256, 200, 128
+    rng = np.random.default_rng(offset)
+    q = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    scales = rng.integers(0x2000, 0x3C00, (K // g, N)).astype(np.uint16)
+    count = (K // g) * N
+    buf = torch.full((count + 32,), 8, dtype=torch.uint8, device=DEV)
+    zeros = buf[offset:offset + count].view(K // g, N)
+    src = qbn.QTensor("gptq4", N, K, dev(oracle.gptq_pack(q)), dev(scales), zeros, group=g)
+    head = (16 - offset) % 16
+    for first in sorted({0, max(head - 1, 0), head, head + 37, count - 17, count - 1}):
+        buf[offset:offset + count] = 8
+        buf[offset + first] = 3
+        buf[offset + count - 1] = 15  # a later offender too, except when first is the last one
+        say("zero-point scan", offset, first)
+        with pytest.raises(qbn.RepackRefused) as e:
+            qbn.repack(src, "q4_0")
+        assert e.value.index == first, (offset, first)
+    buf[offset:offset + count] = 8
+    buf[:offset] = 0        # bytes outside the view are not zero points
+    buf[offset + count:] = 0
+    out = qbn.repack(src, "q4_0")
+    torch.cuda.synchronize()
+    want = oracle.q4_0_pack(q, _q4_0_d_from_scales(scales, K, g))
+    assert np.array_equal(host_bits(out.data).reshape(want.shape).view(np.uint8), want.view(np.uint8))
