@@ -514,7 +514,8 @@ def cpu_baseline(name, spec, inp, budget_s):
 
 
 def environment():
-    """What the numbers were taken on: GPU, clocks, ROCm and build flags."""
+    """What the numbers were taken on: GPU, clocks (rocm-smi, read right after the
+    timed replays), ROCm and build flags."""
     import subprocess
 
     import torch
@@ -701,9 +702,9 @@ def main():
         import __graft_entry__
 
         __graft_entry__.build()
-    env = environment()
     dev = torch.device("cuda:0")
     main_r = measure(args.workload, args.steps, args.warmup, dev)
+    env = environment()  # after the timed replays, so the clock reading is that of a loaded GPU
     also = []
     for other in ([] if args.no_also else args.also):
         if other == args.workload:
