@@ -264,3 +264,98 @@ def test_gemm_overflowing_weight_rows(m, n, k):
     assert ((lo <= got) & (got <= hi)).all()
     y0, _ = oracle.gemm_entries(oracle.MXFP4, data, scales, 1.0, k, X, [0, 0], [0, 1])
     assert y0[0] == np.inf and y0[1] == -np.inf
+
+
+# ------------------------------------------------------------------ Q4_K
+
+# fp16 bit patterns for d across the binades: subnormals (2^-24 upward), the
+# smallest normal, ordinary values, the largest finite value, and negatives
+Q4K_D_BITS = [0x0001, 0x0155, 0x03FF, 0x0400, 0x1234, 0x2C00, 0x3555, 0x3C00, 0x4A00, 0x6400, 0x7BFF, 0xBC00,
+              0x8201]
+
+
+def _f16_value(bits):
+    return float(np.array([bits], np.uint16).view(np.float16)[0])
+
+
+def _q4k_edge_rows(rng, nb):
+    """nb rows, row r nonzero only in super-block r: d from Q4K_D_BITS (then
+    random), dmin = d times 2^U{-2..2} (same sign, clamped to the fp16 range),
+    6-bit sub-scales and mins with 0 and 63 forced in some sub-blocks, random
+    codes; every other super-block has d = dmin = 0."""
+    blocks = workloads.q4k_weights(rng, nb, 256 * nb)
+    blocks[:, :, 0:4] = 0
+    mags = np.zeros(nb)
+    for r in range(nb):
+        dbits = Q4K_D_BITS[r] if r < len(Q4K_D_BITS) else int(rng.integers(0x0001, 0x7C00))
+        d = _f16_value(dbits)
+        dmin = float(np.float16(np.clip(abs(d) * 2.0 ** int(rng.integers(-2, 3)), 2.0 ** -24, 65504.0)))
+        s = rng.integers(0, 64, 8)
+        m = rng.integers(0, 64, 8)
+        s[r % 8], m[(r + 3) % 8] = 63, 63
+        s[(r + 5) % 8], m[(r + 6) % 8] = 0, 0
+        blk = blocks[r, r]
+        blk[0:2] = np.array([dbits], np.uint16).view(np.uint8)
+        blk[2:4] = np.array([dmin], np.float16).view(np.uint8)
+        blk[4:16] = oracle.q4k_pack_scales(s, m)
+        mags[r] = max(abs(d) * 63 * 15, dmin * 63)
+    return blocks, mags
+
+
+@pytest.mark.parametrize("k", [4096, 3840])  # 16 super-blocks: the row-loop kernel; 15: the generic kernel
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_gemv_q4k_scale_edges(k, xdt):
+    """Q4_K super-block scales at the ends of fp16 (subnormal d and dmin,
+    the largest finite d, negative d) and 6-bit sub-scales and mins of 0 and
+    63 ("Four Bits, Three Contracts", sections 5 and 6), through the fused
+    GEMV; activations over each super-block scaled so its products are near 1."""
+    rng = np.random.default_rng(k + (xdt == "bf16"))
+    nb = k // 256
+    blocks, mags = _q4k_edge_rows(rng, nb)
+    shift = -np.floor(np.log2(mags)).astype(np.int64)
+    x = _x_host(rng, k, shift, 256, xdt)
+    inp = dict(fmt="q4_k", n=nb, k=k, data=blocks, scales=None, scale2=1.0)
+    w = qbn.QTensor("q4_k", nb, k, dev(blocks), None)
+    say("gemv q4_k scale edges", k, xdt)
+    y = qbn.quantized_gemv(w, x_dev(x))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    y_ref, s_ref = oracle.gemv_rows(oracle.Q4_K, blocks, None, 1.0, k, x, range(nb))
+    assert np.isfinite(y_ref).all() and (s_ref > 2.0 ** -6).all()
+    assert_within_tolerance(y, y_ref, s_ref, "q4_k scale edges k=%d x=%s" % (k, xdt))
+
+
+# ------------------------------------------------------------------ Q4_0
+
+@pytest.mark.parametrize("k", [4096, 16384])  # x staged in LDS; x read from global memory (k > 14560)
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_gemv_q4_0_d_edges(k, xdt):
+    """Q4_0 block scales d across fp16 ("Bit Packing Architecture", 'Real
+    layouts compared': w = d (q - 8)): every subnormal binade, the smallest
+    normal, the largest finite value, negative values and both zeros, one
+    nonzero block per row, the activations over it scaled so the products
+    are near 1; zero scales give zero rows."""
+    rng = np.random.default_rng(k * 7 + (xdt == "bf16"))
+    nb = k // 32
+    dvals = [2.0 ** e if e < -14 else float(np.float16(2.0 ** e * (1 + int(rng.integers(0, 1024)) / 1024.0)))
+             for e in range(-24, 16)] + [65504.0, -65504.0, -(2.0 ** -24), -0.375, 0.0, -0.0]
+    n = len(dvals)
+    blocks = workloads.q4_0_blocks(rng, n, k)
+    blocks[:, :, 0:2] = 0
+    sigma = rng.permutation(nb)[:n]
+    shift = np.zeros(nb, np.int64)
+    for r, dv in enumerate(dvals):
+        blocks[r, sigma[r], 0:2] = np.array([dv], np.float16).view(np.uint8)
+        if dv != 0.0:
+            shift[sigma[r]] = -int(np.floor(np.log2(abs(dv) * 8)))
+    x = _x_host(rng, k, shift, 32, xdt)
+    w = qbn.QTensor("q4_0", n, k, dev(blocks))
+    say("gemv q4_0 d edges", k, xdt)
+    y = qbn.quantized_gemv(w, x_dev(x))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    y_ref, s_ref = oracle.gemv_rows(oracle.Q4_0, blocks, None, 1.0, k, x, range(n))
+    nz = np.array([dv != 0.0 for dv in dvals])
+    assert np.isfinite(y_ref).all() and (y_ref[~nz] == 0).all() and (s_ref[nz] > 2.0 ** -6).all()
+    assert (y[~nz] == 0).all()
+    assert_within_tolerance(y, y_ref, s_ref, "q4_0 d edges k=%d x=%s" % (k, xdt))
