@@ -431,9 +431,11 @@ def quantize_mx(x: torch.Tensor, fmt: str = "mxfp4", codes: Optional[torch.Tenso
 
 def quantized_gemm_mx(w: QTensor, xcodes: torch.Tensor, xscales: torch.Tensor, fmt: str = "mxfp4",
                       y: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = X_hat @ W_hat^T for MX activations (from quantize_mx; "mxfp4" for
-    W4A4, "mxfp8" for W4A8) and an MXFP4 weight, on the block-scaled matrix
-    cores. Y bfloat16 (default) or float32 [m][n]."""
+    """Y = X_hat @ W_hat^T for MXFP4 activations (from quantize_mx) and an
+    MXFP4 weight (W4A4), on the block-scaled matrix cores. Y bfloat16 (default)
+    or float32 [m][n]. fmt "mxfp8" (W4A8) is refused by the library with
+    QBN_ERR_UNSUPPORTED: the FP8 x FP4 matrix instruction drops product bits
+    below a 13-bit window of each run of 8, so the tolerance would not hold."""
     lib = _load()
     m = xcodes.shape[0]
     if y is None:
