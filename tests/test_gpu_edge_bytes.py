@@ -359,3 +359,104 @@ def test_gemv_q4_0_d_edges(k, xdt):
     assert np.isfinite(y_ref).all() and (y_ref[~nz] == 0).all() and (s_ref[nz] > 2.0 ** -6).all()
     assert (y[~nz] == 0).all()
     assert_within_tolerance(y, y_ref, s_ref, "q4_0 d edges k=%d x=%s" % (k, xdt))
+
+
+# ------------------------------------------------------------------ NVFP4 in CKE's split-half blocks
+
+@pytest.mark.parametrize("k", [4096, 4160])  # 64 blocks: the row kernel; 65: the generic kernel
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_gemv_cke_every_finite_subscale_byte(k, xdt):
+    """Every finite E4M3FN byte as a subscale of CKE's 36-byte blocks ("Why
+    4-Bit Quantization Is King", section 5: four subscales, then the split-half
+    codes), through the fused GEMV: row r is nonzero only in block sigma[r],
+    whose four subscales take the next four bytes of the sweep; every other
+    block has zero subscales. The activations over each 16-element subblock
+    are scaled to bring its products near 1."""
+    rng = np.random.default_rng(k + 17 * (xdt == "bf16"))
+    nb = k // 64
+    n = nb
+    blocks = workloads.cke_blocks(rng, n, k)
+    blocks[:, :, 0:4] = 0
+    sigma = rng.permutation(nb)
+    sweep = E4M3FN_FINITE[rng.permutation(E4M3FN_FINITE.size)]
+    shift = np.zeros(4 * nb, np.int64)  # per 16-element subblock
+    for r in range(n):
+        sub = sweep[(4 * r + np.arange(4)) % sweep.size]
+        blocks[r, sigma[r], 0:4] = sub
+        mag = np.abs(_e4m3fn_values(sub))
+        shift[4 * sigma[r]:4 * sigma[r] + 4] = np.where(mag > 0, -np.floor(np.log2(np.where(mag > 0, mag, 1.0))), 0)
+    x = _x_host(rng, k, shift, 16, xdt)
+    s2 = float(np.float32(0.37))
+    w = qbn.QTensor("nvfp4_cke", n, k, dev(blocks), scale2=s2)
+    say("gemv cke subscale sweep", k, xdt)
+    y = qbn.quantized_gemv(w, x_dev(x))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    y_ref, s_ref = oracle.gemv_rows(oracle.NVFP4_CKE, blocks, None, s2, k, x, range(n))
+    assert np.isfinite(y_ref).all() and (s_ref > 0.25).all()
+    assert_within_tolerance(y, y_ref, s_ref, "cke every subscale byte k=%d x=%s" % (k, xdt))
+
+
+# ------------------------------------------------------------------ GPTQ / AWQ
+
+@pytest.mark.parametrize("fmt", ["gptq4", "awq4"])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_gemv_affine_scale_and_zero_edges(fmt, xdt):
+    """Group scales across fp16 (every subnormal binade up to 65504, negative
+    values) and zero points 0, 8 and 15 ("Bit Packing Architecture", 'Real
+    layouts compared': w = s (q - z), so q - z spans -15 .. 15), through the
+    fused GPTQ / AWQ GEMV: column n is nonzero only in group gamma[n], and the
+    activations over each group are scaled so its products are near 1."""
+    K, g = 4096, 32
+    ng = K // g
+    N = ng  # one group per column
+    rng = np.random.default_rng(31 + (fmt == "awq4") * 2 + (xdt == "bf16"))
+    svals = [2.0 ** e if e < -14 else float(np.float16(2.0 ** e * (1 + int(rng.integers(0, 1024)) / 1024.0)))
+             for e in range(-24, 16)] + [65504.0, -65504.0, -(2.0 ** -24), -0.375]
+    if fmt == "gptq4":
+        data = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
+    else:
+        data = rng.integers(0, 2**32, size=(K, N // 8), dtype=np.uint32)
+    s = np.zeros((ng, N), np.float16)
+    z = rng.integers(0, 16, size=(ng, N)).astype(np.uint8)
+    gamma = rng.permutation(ng)
+    shift = np.zeros(ng, np.int64)
+    for col in range(N):
+        sv = svals[col % len(svals)]
+        s[gamma[col], col] = sv
+        z[gamma[col], col] = (0, 15, 8, int(rng.integers(0, 16)))[col % 4]
+        shift[gamma[col]] = -int(np.floor(np.log2(abs(sv) * 15)))
+    x = _x_host(rng, K, shift, g, xdt)
+    w = qbn.QTensor(fmt, N, K, dev(data), dev(s.view(np.uint16)), dev(z), group=g)
+    say("gemv affine scale edges", fmt, xdt)
+    y = qbn.quantized_gemv(w, x_dev(x))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    y_ref, s_ref = oracle.int4_gemv(fmt, data, s, z, g, x, range(N))
+    assert np.isfinite(y_ref).all() and (s_ref > 2.0 ** -4).all()
+    assert_within_tolerance(y, y_ref, s_ref, "%s scale and zero edges x=%s" % (fmt, xdt))
+
+
+# ------------------------------------------------------------------ W4A8: Q4_K x int8
+
+@pytest.mark.parametrize("k", [4096, 3840])
+def test_gemv_q8_q4k_scale_edges(k):
+    """The W4A8 route ("Why 4-Bit Quantization Is King", section 7c: per
+    256-block d * sum s_j dot_j - dmin * sum m_j bsum_j) on the same
+    super-blocks as the Q4_K edge test: fp16 d and dmin from subnormal to
+    65504 and negative, sub-scales and mins 0 and 63. The activations are the
+    oracle's Q8_K quantization of x scaled per block so the products are near 1."""
+    rng = np.random.default_rng(k + 99)
+    nb = k // 256
+    blocks, mags = _q4k_edge_rows(rng, nb)
+    shift = -np.floor(np.log2(mags)).astype(np.int64)
+    x = _x_host(rng, k, shift, 256, "f32")
+    q, d, bs = oracle.q8_quantize(x)
+    w = qbn.QTensor("q4_k", nb, k, dev(blocks), None)
+    say("gemv_q8 q4_k scale edges", k)
+    y = qbn.quantized_gemv_q8(w, dev(q), dev(d), dev(bs))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    y_ref, s_ref = oracle.q4k_w4a8_rows(blocks, k, q, d, range(nb))
+    assert np.isfinite(y_ref).all() and (s_ref > 2.0 ** -6).all()
+    assert_within_tolerance(y, y_ref, s_ref, "gemv_q8 q4_k scale edges k=%d" % k)

@@ -215,3 +215,29 @@ def test_gemm_mx_refuses_mxfp8_activations():
     assert e.value.status == 3  # QBN_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert (y.cpu() == 7.0).all()
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 256, 8192), (64, 255, 8160)])  # tiled kernel; small kernel
+def test_gemm_mx_every_e8m0_byte_on_both_operands(m, n, k):
+    """Every E8M0 byte 0..254 as a weight block scale and as an activation
+    block scale, inside the block-scaled matrix core (both bytes go to the
+    instruction): weight row r is nonzero only in block column sigma[r], whose
+    weight byte b_r sweeps 0..254, and every activation row takes byte 254 - b_r
+    in that column, so the product scale is 2^0 and each entry is one block's
+    32 exact products. The f32 output within T and the bf16 output within the
+    band, for every entry."""
+    rng = np.random.default_rng(m + n + k)
+    nb = k // 32
+    sigma = rng.permutation(nb)[:n]
+    wbyte = (np.arange(n) % 255).astype(np.uint8)
+    wc = np.zeros((n, k // 2), np.uint8)
+    ws = rng.integers(0, 255, (n, nb)).astype(np.uint8)
+    for r in range(n):
+        wc[r, 16 * sigma[r]:16 * sigma[r] + 16] = rng.integers(0, 256, 16)
+        ws[r, sigma[r]] = wbyte[r]
+    xc = rng.integers(0, 256, (m, k // 2)).astype(np.uint8)
+    xs = rng.integers(100, 155, (m, nb)).astype(np.uint8)
+    for r in range(n):
+        xs[:, sigma[r]] = 254 - int(wbyte[r])
+    ms, ns = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+    _check(wc, ws, xc, xs, m, n, k, ms.ravel(), ns.ravel(), "every E8M0 byte %dx%dx%d" % (m, n, k))
