@@ -239,6 +239,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// The range check of a buffer load covers the lane's offset but not the
+// uniform one, which carries the k-tile and the group; so lanes whose
+// columns lie past n take the offsets of the last valid columns (their
+// outputs are never stored) rather than reading past the end of the codes,
+// zero points or scales on the last k-tile or group.
 template <int FMT>
 __device__ __forceinline__ BufOffsets buf_offsets(const Args &p, int64_t m0, int64_t n0) {
     const int t = threadIdx.x;
@@ -246,21 +251,22 @@ __device__ __forceinline__ BufOffsets buf_offsets(const Args &p, int64_t m0, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) o.x[i] = (uint32_t)(((m0 + t / 8 + 32 * i) * p.ldx + 8 * (t % 8)) * 2);
     if (FMT == QBN_GPTQ4) {
-        const int64_t n = n0 + 4 * (t / 8);
+        const int64_t n = min(n0 + 4 * (t / 8), p.N - 4);  // n % 8 == 0 on this path
         o.w = (uint32_t)(((t % 8) * p.N + n) * 4);
         o.z = (uint32_t)n;
     } else if (FMT == QBN_Q4_0) {
         // block (column n0 + t/2, t % 2) of the first k-tile; with k % 64 == 0 a
         // block starts 2 bytes past a dword boundary exactly when t is odd, so
         // the dword-aligned read starts at the block (t even) or 2 bytes before it
-        o.w = (uint32_t)(((n0 + t / 2) * (p.K / 32) + (t % 2)) * 18 - 2 * (t % 2));
+        const int64_t n = min(n0 + t / 2, p.N - 1);
+        o.w = (uint32_t)((n * (p.K / 32) + (t % 2)) * 18 - 2 * (t % 2));
         o.z = 0;
     } else {
-        const int64_t n = n0 + 8 * (t / 16);
+        const int64_t n = min(n0 + 8 * (t / 16), p.N - 8);
         o.w = (uint32_t)(((4 * (t % 16)) * (p.N / 8) + n / 8) * 4);
         o.z = (uint32_t)n;
     }
-    o.sc = (uint32_t)((n0 + t % 128) * 2);
+    o.sc = (uint32_t)(min(n0 + t % 128, p.N - 1) * 2);
     return o;
 }
 
@@ -586,6 +592,330 @@ bool buf_fits(const Args &a) {
            (int64_t)(a.N + BN) * 4 * 8 < L;
 }
 
+// ------------------------------------------------------------------ 256 x 128 kernel
+// Large-m variant for GPTQ4 with groups that are a multiple of 64 and
+// k % 64 == 0. Workgroup tile 256 x 128 of Y, eight waves in 4 x 2, each
+// 64 x 64 (2 x 2 MFMA tiles), one workgroup per compute unit. Each decoded
+// weight tile then serves 256 rows of X instead of 128, which halves the
+// decode work per MFMA.
+//  - X k-tiles are copied from global memory straight into LDS by buffer
+//    loads with an LDS destination (no registers, no LDS-write
+//    instructions), three k-tiles in flight in a ring. Rows past m lie beyond
+//    the descriptor's range and land as zeros.
+//  - The codes and zero points of k-tile kt + 1 are loaded into registers
+//    while tile kt is multiplied, then decoded to bf16 (q - z) and written
+//    to the other of two LDS weight buffers; one barrier per k-tile.
+//  - Each lane loads the scales of its two columns itself; at the end of a
+//    group the partial sums are scaled and added to the totals as above.
+// X and the decoded weights share one LDS layout: blocks of 8 rows, chunk c
+// (k = 8c .. 8c + 7) of row r at (r / 8) * 1152 + c * 128 + (r % 8) * 16, so
+// one 64-lane copy fills 8 rows x 128 bytes with lane i at 16 i, and the
+// fragment reads of 32 consecutive rows are conflict-free.
+namespace big {
+
+constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int WAVES = 8, THREADS = WAVES * kWave;
+constexpr int BLK = 1152;
+constexpr int A_STAGE = BM / 8 * BLK;
+constexpr int B_STAGE = BN / 8 * BLK;
+constexpr int XS = 3;
+constexpr int B_OFF = XS * A_STAGE;
+constexpr int SMEM = B_OFF + 2 * B_STAGE;
+constexpr int NX = BM / 8 / WAVES;  // X copies per wave per k-tile
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int frag(int r, int c) { return (r / 8) * BLK + c * 128 + (r % 8) * 16; }
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at base + 16 * lane.
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t *base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)base, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct WRegs {
+    uint32_t w[2];  // word rows r0 and r0 + 4 of the thread's column
+    uint32_t z;     // the column's zero-point byte for the k-tile's group
+};
+
+struct Frag {
+    bf16x8 a[2], b[2];
+};
+
+__device__ __forceinline__ void read_frag(Frag &f, const uint8_t *xs, const uint8_t *ws, int ks) {
+    f.a[0] = *reinterpret_cast<const bf16x8 *>(xs + 256 * ks);
+    f.a[1] = *reinterpret_cast<const bf16x8 *>(xs + 4 * BLK + 256 * ks);
+    f.b[0] = *reinterpret_cast<const bf16x8 *>(ws + 256 * ks);
+    f.b[1] = *reinterpret_cast<const bf16x8 *>(ws + 4 * BLK + 256 * ks);
+}
+
+template <bool FRESH>
+__device__ __forceinline__ void mma(const Frag &f, f32x16 (&part)[2][2]) {
+    const f32x16 zero = {};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], FRESH ? zero : part[i][j], 0, 0, 0);
+}
+
+__device__ __forceinline__ void scale_add(uint32_t s16, const f32x16 &part, f32x16 &tot) {
+    const float s = f16_to_f32(s16);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tot[v] = __builtin_fmaf(s, part[v], tot[v]);
+}
+
+// The last MFMA step of a group: each 32 x 32 tile's partial sums are scaled
+// into its totals right after the next tile's MFMA is issued, so that the
+// scaling overlaps the matrix core's work instead of waiting for all four.
+__device__ __forceinline__ void mma_last(const Frag &f, uint32_t s0, uint32_t s1, f32x16 (&part)[2][2],
+                                         f32x16 (&tot)[2][2]) {
+    part[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[0], f.b[0], part[0][0], 0, 0, 0);
+    part[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[0], f.b[1], part[0][1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    scale_add(s0, part[0][0], tot[0][0]);
+    part[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[1], f.b[0], part[1][0], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    scale_add(s1, part[0][1], tot[0][1]);
+    part[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[1], f.b[1], part[1][1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    scale_add(s0, part[1][0], tot[1][0]);
+    scale_add(s1, part[1][1], tot[1][1]);
+}
+
+// Pipeline of one k-tile kt (every wave issues the same loads in every
+// k-tile, tiles past the end clamped to the last one, so that the
+// compiler's wait counts for the register loads are static):
+//   issue: scales of k-tile kt + 1, codes and zero points of kt + 2 (into the
+//          register set kt % 2), X of kt + 2 (into ring slot (kt + 2) % 3);
+//   MFMA steps 0..2 of kt, each step's fragments read one step ahead;
+//   decode the codes of kt + 1 into LDS buffer (kt + 1) % 2;
+//   wait for X of kt + 1, barrier; read step 0 of kt + 1; MFMA step 3 of kt;
+//   at the end of a group, scale the partial sums into the totals.
+// The buffers written in k-tile kt were last read before the barrier of
+// k-tile kt - 1.
+// TPG: k-tiles per group when it is 1 or 2 (group 64 or 128; the group
+// boundaries then fall on fixed k-tile parities of the two-tile unrolled
+// loop), 0 for any other multiple of 64.
+template <bool YF32, int TPG>
+__global__ __launch_bounds__(THREADS) void k_gemm_gptq_big(Args p, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+    // tile order as in k_gemm_int4, with groups of GM row tiles
+    constexpr int GM = 4;
+    const int nblk = gridDim.x, q8 = nblk / 8, r8 = nblk % 8, xcd = blockIdx.x % 8;
+    const int lt = xcd * q8 + min(xcd, r8) + blockIdx.x / 8;
+    const int per_group = GM * tiles_n;
+    const int first_m = (lt / per_group) * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int64_t m0 = (int64_t)(first_m + (lt % per_group) % gm) * BM;
+    const int64_t n0 = (int64_t)((lt % per_group) / gm) * BN;
+
+    const int t = threadIdx.x;
+    const int lane = t % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int wm = wave / 2, wn = wave % 2;
+    const int lr = lane % 32, lh = lane / 32;
+    const int nk = (int)(p.K / BK);
+    const int tpg = TPG ? TPG : (int)(p.group / BK);
+    const int64_t N = p.N;
+
+    const __amdgpu_buffer_rsrc_t rx = rsrc(p.X, (uint32_t)(((p.M - 1) * p.ldx + p.K) * 2));
+    const __amdgpu_buffer_rsrc_t rw = rsrc(p.data, (uint32_t)(p.K * N / 2));
+    const __amdgpu_buffer_rsrc_t rz = rsrc(p.zeros, (uint32_t)((p.K / p.group) * N));
+    const __amdgpu_buffer_rsrc_t rs = rsrc(p.scales, (uint32_t)((p.K / p.group) * N * 2));
+
+    // X copy i of this wave: rows 8 q .. 8 q + 7 of the tile, q = wave + 8 i;
+    // lane: row 8 q + lane % 8, chunk lane / 8. The k-tile goes in the
+    // uniform offset; a row past m is past the descriptor's range.
+    uint32_t xo[NX];
+#pragma unroll
+    for (int i = 0; i < NX; ++i)
+        xo[i] = (uint32_t)(((m0 + 8 * (wave + WAVES * i) + lane % 8) * p.ldx + 8 * (lane / 8)) * 2);
+    auto copy_x = [&](int slot, int kt) {
+#pragma unroll
+        for (int i = 0; i < NX; ++i)
+            copy16(rx, xo[i], kt * BK * 2, smem + slot * A_STAGE + (wave + WAVES * i) * BLK);
+    };
+
+    // Decode role: column nl of the tile, word rows r0 and r0 + 4 (k = 8 r ..
+    // 8 r + 7 of the k-tile). A column past n reads column n - 1 instead.
+    const int nl = t % BN, r0 = t / BN;
+    const int64_t nw = min(n0 + nl, N - 1);
+    const uint32_t wo = (uint32_t)((r0 * N + nw) * 4);
+    auto load_w = [&](WRegs &R, int kt, int g) {
+        const uint32_t o = wo + (uint32_t)kt * (uint32_t)(32 * N);  // 8 word rows per k-tile
+        R.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, 0);
+        R.w[1] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + (uint32_t)(16 * N), 0, 0);
+        R.z = __builtin_amdgcn_raw_buffer_load_b8(rz, (uint32_t)(g * N + nw), 0, 0);
+    };
+    auto store_w = [&](const WRegs &R, int buf) {
+        const float z = (float)(R.z & 0xFFu);
+        const float zz[8] = {z, z, z, z, z, z, z, z};
+        uint8_t *wst = smem + B_OFF + buf * B_STAGE;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float v[8];
+            nibbles_minus(R.w[h], zz, v);
+            *reinterpret_cast<u32x4 *>(wst + frag(nl, r0 + 4 * h)) =
+                u32x4{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]), bf16_pair(v[4], v[5]), bf16_pair(v[6], v[7])};
+        }
+    };
+    // the scales of this lane's output columns (MFMA column lr of tiles j = 0, 1)
+    const uint32_t so0 = (uint32_t)(min(n0 + wn * 64 + lr, N - 1) * 2);
+    const uint32_t so1 = (uint32_t)(min(n0 + wn * 64 + 32 + lr, N - 1) * 2);
+    auto load_s = [&](uint32_t (&sv)[2], int g) {
+        const uint32_t go = (uint32_t)(g * N * 2);
+        sv[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, so0 + go, 0, 0);
+        sv[1] = __builtin_amdgcn_raw_buffer_load_b16(rs, so1 + go, 0, 0);
+    };
+
+    const int a_lane = frag(wm * 64 + lr, lh);
+    const int b_lane = B_OFF + frag(wn * 64 + lr, lh);
+    f32x16 part[2][2], tot[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            part[i][j] = f32x16{};
+            tot[i][j] = f32x16{};
+        }
+
+    WRegs R[2];
+    uint32_t sv[2][2];
+    const int last = nk - 1;
+    // group cursors: k-tile kt + 1 (scales) and kt + 2 (codes), clamped to
+    // the last k-tile like the loads themselves; (group, k-tile within it)
+    int gs = 0, ts = 0, gw = 0, tw = 0;
+    auto advance = [&](int &g, int &tl, int kt_next) {
+        if (kt_next > last) return;
+        if (++tl == tpg) {
+            tl = 0;
+            ++g;
+        }
+    };
+    load_w(R[0], 0, 0);
+    copy_x(0, 0);
+    load_s(sv[0], 0);
+    advance(gw, tw, 1);
+    load_w(R[1], min(1, last), gw);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_x(1, min(1, last));
+    store_w(R[0], 0);
+    // X of k-tile 0 has landed once at most k-tile 1's copies remain. (A
+    // count that also allowed the register loads issued after it would
+    // break wherever the compiler drops a load whose value is unused.)
+    __builtin_amdgcn_s_waitcnt(0xF70 | NX);
+    lds_barrier();
+    Frag f[2];
+    read_frag(f[0], smem + a_lane, smem + b_lane, 0);
+
+    int tig = 0;
+    int slot = 0;  // ring slot of k-tile kt
+    auto tile = [&](int kt, auto par) {
+        constexpr int P = decltype(par)::value;  // kt % 2
+        advance(gs, ts, kt + 1);
+        advance(gw, tw, kt + 2);
+        load_s(sv[P ^ 1], gs);
+        load_w(R[P], min(kt + 2, last), gw);
+        // the X copies are this tile's last memory issues (see the wait below)
+        __builtin_amdgcn_sched_barrier(0);
+        copy_x(slot == 0 ? 2 : slot - 1, min(kt + 2, last));
+        const uint8_t *xs = smem + slot * A_STAGE + a_lane;
+        const uint8_t *ws = smem + P * B_STAGE + b_lane;
+        read_frag(f[1], xs, ws, 1);
+        const bool first = TPG == 1 ? true : TPG == 2 ? P == 0 : tig == 0;
+        if (first)
+            mma<true>(f[0], part);
+        else
+            mma<false>(f[0], part);
+        read_frag(f[0], xs, ws, 2);
+        mma<false>(f[1], part);
+        read_frag(f[1], xs, ws, 3);
+        mma<false>(f[0], part);
+        store_w(R[P ^ 1], P ^ 1);
+        __builtin_amdgcn_s_waitcnt(0xF70 | NX);  // X of k-tile kt + 1: issued before this tile's copies
+        lds_barrier();
+        slot = slot == 2 ? 0 : slot + 1;
+        read_frag(f[0], smem + slot * A_STAGE + a_lane, smem + (P ^ 1) * B_STAGE + b_lane, 0);
+        bool end;
+        if (TPG == 0) {
+            end = ++tig == tpg;
+            if (end) tig = 0;
+        } else {
+            end = TPG == 1 || P == 1;
+        }
+        if (TPG != 0 && end) {
+            mma_last(f[1], sv[P][0], sv[P][1], part, tot);
+        } else {
+            // (other group sizes: the interleaved form costs a spill there)
+            mma<false>(f[1], part);
+            if (end) {
+                scale_add(sv[P][0], part[0][0], tot[0][0]);
+                scale_add(sv[P][1], part[0][1], tot[0][1]);
+                scale_add(sv[P][0], part[1][0], tot[1][0]);
+                scale_add(sv[P][1], part[1][1], tot[1][1]);
+            }
+        }
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        tile(kt + 1, std::integral_constant<int, 1>{});
+    }
+    if (kt < nk) tile(kt, std::integral_constant<int, 0>{});
+    // no copy into LDS may still be in flight when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0xF70);
+
+    // lane holds C[i][j] with j = lane % 32, i = 8(v/4) + 4(lane/32) + v%4
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t n = n0 + wn * 64 + 32 * j + lr;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t m = m0 + wm * 64 + 32 * i + 8 * (v / 4) + 4 * lh + (v % 4);
+                if (m < p.M && n < N) {
+                    if (YF32)
+                        ((float *)p.Y)[m * p.ldy + n] = tot[i][j][v];
+                    else
+                        ((uint16_t *)p.Y)[m * p.ldy + n] = bf16_bits_rne(tot[i][j][v]);
+                }
+            }
+        }
+}
+
+// k % 64 == 0, group % 64 == 0, n even, 4-byte aligned codes, and every
+// byte offset (X rows of the last tile included) within 31 bits.
+bool fits(const Args &a) {
+    constexpr int64_t L = (int64_t)1 << 31;
+    return a.K % BK == 0 && a.group % BK == 0 && a.N % 2 == 0 && a.M >= BM && a.N >= BN &&
+           ((a.M + BM) * a.ldx + a.K) * 2 < L && a.K * a.N / 2 < L && (a.K / a.group) * a.N * 2 < L;
+}
+
+template <bool YF32>
+void launch_gptq(const Args &a, int tm, int tn, hipStream_t s) {
+    const dim3 grid((unsigned)(tm * tn)), block(THREADS);
+    if (a.group == 64)
+        hipLaunchKernelGGL((k_gemm_gptq_big<YF32, 1>), grid, block, 0, s, a, tm, tn);
+    else if (a.group == 128)
+        hipLaunchKernelGGL((k_gemm_gptq_big<YF32, 2>), grid, block, 0, s, a, tm, tn);
+    else
+        hipLaunchKernelGGL((k_gemm_gptq_big<YF32, 0>), grid, block, 0, s, a, tm, tn);
+}
+
+hipError_t run_gptq(const Args &a, bool yf32, hipStream_t s) {
+    const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
+    if (yf32)
+        launch_gptq<true>(a, tm, tn, s);
+    else
+        launch_gptq<false>(a, tm, tn, s);
+    return hipGetLastError();
+}
+
+}  // namespace big
+
 template <int FMT>
 hipError_t run(const Args &a, bool yf32, hipStream_t s) {
     // X through its descriptor when k % 64 == 0: measured 4-6% faster for
@@ -597,6 +927,7 @@ hipError_t run(const Args &a, bool yf32, hipStream_t s) {
         if (qb) return run3<FMT, false, false, true, true>(a, yf32, s);
         return xb ? run3<FMT, false, false, false, true>(a, yf32, s) : run3<FMT, false, false>(a, yf32, s);
     } else {
+        if (FMT == QBN_GPTQ4 && big::fits(a) && (uintptr_t)a.data % 4 == 0) return big::run_gptq(a, yf32, s);
         const bool vec = a.N % 8 == 0 && (uintptr_t)a.data % 16 == 0 && (uintptr_t)a.zeros % 8 == 0;
         if (a.group % BK == 0) {
             if (vec && buf_fits(a)) return run3<FMT, true, true, true>(a, yf32, s);
