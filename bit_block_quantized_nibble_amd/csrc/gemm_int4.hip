@@ -593,24 +593,30 @@ bool buf_fits(const Args &a) {
 }
 
 // ------------------------------------------------------------------ 256 x 128 kernel
-// Large-m variant for GPTQ4 with groups that are a multiple of 64 and
-// k % 64 == 0. Workgroup tile 256 x 128 of Y, eight waves in 4 x 2, each
+// Large-m variant (k % 64 == 0; GPTQ4 / AWQ4 with groups that are a multiple
+// of 64, or Q4_0). Workgroup tile 256 x 128 of Y, eight waves in 4 x 2, each
 // 64 x 64 (2 x 2 MFMA tiles), one workgroup per compute unit. Each decoded
 // weight tile then serves 256 rows of X instead of 128, which halves the
 // decode work per MFMA.
 //  - X k-tiles are copied from global memory straight into LDS by buffer
 //    loads with an LDS destination (no registers, no LDS-write
-//    instructions), three k-tiles in flight in a ring. Rows past m lie beyond
-//    the descriptor's range and land as zeros.
-//  - The codes and zero points of k-tile kt + 1 are loaded into registers
-//    while tile kt is multiplied, then decoded to bf16 (q - z) and written
-//    to the other of two LDS weight buffers; one barrier per k-tile.
-//  - Each lane loads the scales of its two columns itself; at the end of a
-//    group the partial sums are scaled and added to the totals as above.
+//    instructions), three k-tiles in a ring. Rows past m lie beyond the
+//    descriptor's range and land as zeros.
+//  - The codes (and zero points) of k-tile kt + 2 are loaded into registers
+//    while tile kt is multiplied; those of kt + 1, loaded a tile earlier,
+//    are decoded to bf16 (q - z) and written to the other of two LDS weight
+//    buffers. One barrier per k-tile.
+//  - Each lane loads the scales of its two output columns itself; at the
+//    end of a group (GPTQ4 / AWQ4) or of each 32-k block (Q4_0) the partial
+//    sums are scaled and added to the totals as above.
 // X and the decoded weights share one LDS layout: blocks of 8 rows, chunk c
 // (k = 8c .. 8c + 7) of row r at (r / 8) * 1152 + c * 128 + (r % 8) * 16, so
 // one 64-lane copy fills 8 rows x 128 bytes with lane i at 16 i, and the
 // fragment reads of 32 consecutive rows are conflict-free.
+// The range check of a buffer load covers the lane's offset but not the
+// uniform one, so every offset that depends on k or the group is carried in
+// the lane's offset, and lanes whose columns lie past n read the last valid
+// column (their outputs are never stored).
 namespace big {
 
 constexpr int BM = 256, BN = 128, BK = 64;
@@ -620,7 +626,9 @@ constexpr int A_STAGE = BM / 8 * BLK;
 constexpr int B_STAGE = BN / 8 * BLK;
 constexpr int XS = 3;
 constexpr int B_OFF = XS * A_STAGE;
-constexpr int SMEM = B_OFF + 2 * B_STAGE;
+constexpr int D_STAGE = 4 * BN * 4;           // Q4_0: the d of the k-tile's two blocks per column, then unused slots
+constexpr int B_BUF = B_STAGE + D_STAGE;      // one weight buffer (decoded codes, then Q4_0 d)
+constexpr int SMEM = B_OFF + 2 * B_BUF;
 constexpr int NX = BM / 8 / WAVES;  // X copies per wave per k-tile
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -634,9 +642,153 @@ __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-struct WRegs {
-    uint32_t w[2];  // word rows r0 and r0 + 4 of the thread's column
-    uint32_t z;     // the column's zero-point byte for the k-tile's group
+__device__ __forceinline__ u32x4 bf16x8_of(const float (&v)[8]) {
+    return u32x4{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]), bf16_pair(v[4], v[5]), bf16_pair(v[6], v[7])};
+}
+
+// Decode roles: where a thread's codes come from and where their (q - z)
+// values go in the LDS weight buffer.
+template <int FMT>
+struct Role;
+
+// GPTQ4: column nl = t % 128 of the tile, word rows r0 = t / 128 and r0 + 4
+// (k = 8 r .. 8 r + 7 of the k-tile); one 16-byte chunk per word.
+template <>
+struct Role<QBN_GPTQ4> {
+    struct Regs {
+        uint32_t w[2];
+        uint32_t z;
+    };
+    int nl, r0;
+    uint32_t wo, zo, w4, step, nz;
+    __device__ __forceinline__ Role(const Args &p, int64_t n0, int t) {
+        nl = t % BN;
+        r0 = t / BN;
+        const int64_t nw = min(n0 + nl, p.N - 1);
+        wo = (uint32_t)((r0 * p.N + nw) * 4);
+        w4 = (uint32_t)(16 * p.N);
+        step = (uint32_t)(32 * p.N);  // 8 word rows per k-tile
+        zo = (uint32_t)nw;
+        nz = (uint32_t)p.N;
+    }
+    __device__ __forceinline__ void load(Regs &R, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rz, int kt,
+                                         int g) const {
+        const uint32_t o = wo + (uint32_t)kt * step;
+        R.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, 0);
+        R.w[1] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + w4, 0, 0);
+        R.z = __builtin_amdgcn_raw_buffer_load_b8(rz, (uint32_t)g * nz + zo, 0, 0);
+    }
+    __device__ __forceinline__ void store(const Regs &R, uint8_t *wst) const {
+        const float z = (float)(R.z & 0xFFu);
+        const float zz[8] = {z, z, z, z, z, z, z, z};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float v[8];
+            nibbles_minus(R.w[h], zz, v);
+            *reinterpret_cast<u32x4 *>(wst + frag(nl, r0 + 4 * h)) = bf16x8_of(v);
+        }
+    }
+};
+
+// AWQ4: word column c = (t / 4) % 16 (columns 8c .. 8c + 7; slot s of a
+// word holds column 0,2,4,6,1,3,5,7 [s]), word rows 8r .. 8r + 7 of the
+// k-tile with r = t / 64; lane q = t % 4 takes slots q and q + 4, i.e.
+// columns 8c + 2q and 8c + 2q + 1, and writes one 16-byte chunk for each.
+// (The four lanes of a word column read the same words; the 64 lanes of a
+// wave then write 16-byte chunks of eight different rows of each 8-row
+// block.)
+template <>
+struct Role<QBN_AWQ4> {
+    struct Regs {
+        uint32_t w[8];
+        uint32_t z;  // zero points of columns 8c + 2q and 8c + 2q + 1 (low two bytes)
+    };
+    int c, q, r;
+    uint32_t wo, row, step, zo, nz;
+    __device__ __forceinline__ Role(const Args &p, int64_t n0, int t) {
+        q = t % 4;
+        c = (t / 4) % 16;
+        r = t / 64;
+        const int64_t wc = min(n0 / 8 + c, p.N / 8 - 1);
+        row = (uint32_t)((p.N / 8) * 4);
+        wo = (uint32_t)((8 * r) * row + wc * 4);
+        step = (uint32_t)BK * row;
+        zo = (uint32_t)(wc * 8 + 2 * q);
+        nz = (uint32_t)p.N;
+    }
+    __device__ __forceinline__ void load(Regs &R, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rz, int kt,
+                                         int g) const {
+        const uint32_t o = wo + (uint32_t)kt * step;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) R.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + (uint32_t)i * row, 0, 0);
+        R.z = __builtin_amdgcn_raw_buffer_load_b16(rz, (uint32_t)g * nz + zo, 0, 0);
+    }
+    __device__ __forceinline__ void store(const Regs &R, uint8_t *wst) const {
+        const float z0 = (float)(R.z & 0xFFu), z1 = (float)((R.z >> 8) & 0xFFu);
+        // word i: nibble q (column 2q) and nibble q + 4 (column 2q + 1) read
+        // as the two halves of a binary16 pair of subnormals: q * 2^-24
+        float v0[8], v1[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f16x2 h = __builtin_bit_cast(f16x2, (R.w[i] >> (4 * q)) & 0x000F000Fu);
+            v0[i] = __builtin_fmaf((float)h.x, 0x1p24f, -z0);
+            v1[i] = __builtin_fmaf((float)h.y, 0x1p24f, -z1);
+        }
+        *reinterpret_cast<u32x4 *>(wst + frag(8 * c + 2 * q, r)) = bf16x8_of(v0);
+        *reinterpret_cast<u32x4 *>(wst + frag(8 * c + 2 * q + 1, r)) = bf16x8_of(v1);
+    }
+};
+
+// Q4_0: column nl = t / 4, quarter q = t % 4 of its two blocks in the k-tile:
+// block b = q / 2 (k = 32 b .. 32 b + 31), half hh = q % 2 of its 16 code
+// bytes. Byte j holds element j (low nibble) and element 16 + j (high
+// nibble), so bytes 8 hh .. 8 hh + 7 give chunks 4 b + hh and 4 b + 2 + hh.
+// With k % 64 == 0 a block starts on a dword boundary (b = 0) or 2 bytes
+// past one (b = 1), so the eight code bytes start 2 bytes past a dword
+// boundary (b = 0) or on one (b = 1); the lane reads the 12 dword-aligned
+// bytes that end at most 2 bytes past them (b = 0: into the k-tile's second
+// block), so the four lanes of a column cover its 36 bytes. The lanes with
+// hh = 0 hold their block's d (its first two bytes) and put it in LDS for
+// the scaling.
+template <>
+struct Role<QBN_Q4_0> {
+    struct Regs {
+        uint32_t w[3];
+    };
+    int nl, b, hh;
+    uint32_t wo, step;
+    __device__ __forceinline__ Role(const Args &p, int64_t n0, int t) {
+        nl = t / 4;
+        b = (t % 4) / 2;
+        hh = t % 2;
+        const int64_t n = min(n0 + nl, p.N - 1);
+        // codes of block b of k-tile 0 start at (n K/32 + b) 18 + 2 + 8 hh
+        wo = (uint32_t)((n * (p.K / 32) + b) * 18 + 2 + 8 * hh - (b ? 4 : 2));
+        step = 2 * 18;
+    }
+    __device__ __forceinline__ void load(Regs &R, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t, int kt,
+                                         int) const {
+        const uint32_t o = wo + (uint32_t)kt * step;
+        R.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, 0);
+        R.w[1] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + 4, 0, 0);
+        R.w[2] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + 8, 0, 0);
+    }
+    __device__ __forceinline__ void store(const Regs &R, uint8_t *wst) const {
+        const uint32_t c0 = b ? R.w[1] : __builtin_amdgcn_alignbyte(R.w[1], R.w[0], 2);
+        const uint32_t c1 = b ? R.w[2] : __builtin_amdgcn_alignbyte(R.w[2], R.w[1], 2);
+        const float z8[8] = {8.0f, 8.0f, 8.0f, 8.0f, 8.0f, 8.0f, 8.0f, 8.0f};
+        // nibbles_minus of dword d: v[2j] = element 8 hh + 4d + j, v[2j + 1] = 16 + the same
+        float v0[8], v1[8];
+        nibbles_minus(c0, z8, v0);
+        nibbles_minus(c1, z8, v1);
+        *reinterpret_cast<u32x4 *>(wst + frag(nl, 4 * b + hh)) =
+            u32x4{bf16_pair(v0[0], v0[2]), bf16_pair(v0[4], v0[6]), bf16_pair(v1[0], v1[2]), bf16_pair(v1[4], v1[6])};
+        *reinterpret_cast<u32x4 *>(wst + frag(nl, 4 * b + 2 + hh)) =
+            u32x4{bf16_pair(v0[1], v0[3]), bf16_pair(v0[5], v0[7]), bf16_pair(v1[1], v1[3]), bf16_pair(v1[5], v1[7])};
+        // d: bytes 0-1 of the window when b = 0, bytes 2-3 when b = 1 (for
+        // hh = 1 these bytes are codes, stored in a slot nobody reads)
+        *reinterpret_cast<uint32_t *>(wst + B_STAGE + 4 * (BN * (2 * hh + b) + nl)) = b ? R.w[0] >> 16 : R.w[0] & 0xFFFFu;
+    }
 };
 
 struct Frag {
@@ -688,7 +840,8 @@ __device__ __forceinline__ void mma_last(const Frag &f, uint32_t s0, uint32_t s1
 // k-tile, tiles past the end clamped to the last one, so that the
 // compiler's wait counts for the register loads are static):
 //   issue: scales of k-tile kt + 1, codes and zero points of kt + 2 (into the
-//          register set kt % 2), X of kt + 2 (into ring slot (kt + 2) % 3);
+//          register set kt % 2), then X of kt + 2 (into ring slot
+//          (kt + 2) % 3) as the tile's last memory issues;
 //   MFMA steps 0..2 of kt, each step's fragments read one step ahead;
 //   decode the codes of kt + 1 into LDS buffer (kt + 1) % 2;
 //   wait for X of kt + 1, barrier; read step 0 of kt + 1; MFMA step 3 of kt;
@@ -697,9 +850,11 @@ __device__ __forceinline__ void mma_last(const Frag &f, uint32_t s0, uint32_t s1
 // k-tile kt - 1.
 // TPG: k-tiles per group when it is 1 or 2 (group 64 or 128; the group
 // boundaries then fall on fixed k-tile parities of the two-tile unrolled
-// loop), 0 for any other multiple of 64.
-template <bool YF32, int TPG>
-__global__ __launch_bounds__(THREADS) void k_gemm_gptq_big(Args p, int tiles_m, int tiles_n) {
+// loop), 0 for any other multiple of 64; unused for Q4_0, whose 32-k blocks
+// are rescaled after steps 1 and 3 of every k-tile.
+template <int FMT, bool YF32, int TPG>
+__global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, int tiles_n) {
+    constexpr bool Q40 = FMT == QBN_Q4_0;
     __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
     // tile order as in k_gemm_int4, with groups of GM row tiles
     constexpr int GM = 4;
@@ -717,13 +872,20 @@ __global__ __launch_bounds__(THREADS) void k_gemm_gptq_big(Args p, int tiles_m, 
     const int wm = wave / 2, wn = wave % 2;
     const int lr = lane % 32, lh = lane / 32;
     const int nk = (int)(p.K / BK);
-    const int tpg = TPG ? TPG : (int)(p.group / BK);
+    const int tpg = Q40 ? 1 : TPG ? TPG : (int)(p.group / BK);
     const int64_t N = p.N;
 
     const __amdgpu_buffer_rsrc_t rx = rsrc(p.X, (uint32_t)(((p.M - 1) * p.ldx + p.K) * 2));
-    const __amdgpu_buffer_rsrc_t rw = rsrc(p.data, (uint32_t)(p.K * N / 2));
-    const __amdgpu_buffer_rsrc_t rz = rsrc(p.zeros, (uint32_t)((p.K / p.group) * N));
-    const __amdgpu_buffer_rsrc_t rs = rsrc(p.scales, (uint32_t)((p.K / p.group) * N * 2));
+    __amdgpu_buffer_rsrc_t rw, rz, rs;
+    if (Q40) {
+        rw = rsrc(p.data, (uint32_t)(N * (p.K / 32) * 18));
+        rz = rw;
+        rs = rw;
+    } else {
+        rw = rsrc(p.data, (uint32_t)(p.K * N / 2));
+        rz = rsrc(p.zeros, (uint32_t)((p.K / p.group) * N));
+        rs = rsrc(p.scales, (uint32_t)((p.K / p.group) * N * 2));
+    }
 
     // X copy i of this wave: rows 8 q .. 8 q + 7 of the tile, q = wave + 8 i;
     // lane: row 8 q + lane % 8, chunk lane / 8. The k-tile goes in the
@@ -738,36 +900,31 @@ __global__ __launch_bounds__(THREADS) void k_gemm_gptq_big(Args p, int tiles_m, 
             copy16(rx, xo[i], kt * BK * 2, smem + slot * A_STAGE + (wave + WAVES * i) * BLK);
     };
 
-    // Decode role: column nl of the tile, word rows r0 and r0 + 4 (k = 8 r ..
-    // 8 r + 7 of the k-tile). A column past n reads column n - 1 instead.
-    const int nl = t % BN, r0 = t / BN;
-    const int64_t nw = min(n0 + nl, N - 1);
-    const uint32_t wo = (uint32_t)((r0 * N + nw) * 4);
-    auto load_w = [&](WRegs &R, int kt, int g) {
-        const uint32_t o = wo + (uint32_t)kt * (uint32_t)(32 * N);  // 8 word rows per k-tile
-        R.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, 0);
-        R.w[1] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + (uint32_t)(16 * N), 0, 0);
-        R.z = __builtin_amdgcn_raw_buffer_load_b8(rz, (uint32_t)(g * N + nw), 0, 0);
+    const Role<FMT> role(p, n0, t);
+    using Regs = typename Role<FMT>::Regs;
+
+    // The scales of this lane's output columns (MFMA column lr of tiles j =
+    // 0, 1). GPTQ4 / AWQ4: the two fp16 scales of a group, loaded a k-tile
+    // ahead; Q4_0: the d of blocks b = 0, 1 of the k-tile, s[2 b + j], read
+    // from the LDS weight buffer.
+    const int64_t c0 = min(n0 + wn * 64 + lr, N - 1), c1 = min(n0 + wn * 64 + 32 + lr, N - 1);
+    const uint32_t so0 = (uint32_t)(c0 * 2), so1 = (uint32_t)(c1 * 2);
+    struct SRegs {
+        uint32_t s[Q40 ? 4 : 2];
     };
-    auto store_w = [&](const WRegs &R, int buf) {
-        const float z = (float)(R.z & 0xFFu);
-        const float zz[8] = {z, z, z, z, z, z, z, z};
-        uint8_t *wst = smem + B_OFF + buf * B_STAGE;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float v[8];
-            nibbles_minus(R.w[h], zz, v);
-            *reinterpret_cast<u32x4 *>(wst + frag(nl, r0 + 4 * h)) =
-                u32x4{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]), bf16_pair(v[4], v[5]), bf16_pair(v[6], v[7])};
+    auto load_s = [&](SRegs &S, int g) {
+        if (!Q40) {
+            const uint32_t go = (uint32_t)(g * N * 2);
+            S.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, so0 + go, 0, 0);
+            S.s[1] = __builtin_amdgcn_raw_buffer_load_b16(rs, so1 + go, 0, 0);
         }
     };
-    // the scales of this lane's output columns (MFMA column lr of tiles j = 0, 1)
-    const uint32_t so0 = (uint32_t)(min(n0 + wn * 64 + lr, N - 1) * 2);
-    const uint32_t so1 = (uint32_t)(min(n0 + wn * 64 + 32 + lr, N - 1) * 2);
-    auto load_s = [&](uint32_t (&sv)[2], int g) {
-        const uint32_t go = (uint32_t)(g * N * 2);
-        sv[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, so0 + go, 0, 0);
-        sv[1] = __builtin_amdgcn_raw_buffer_load_b16(rs, so1 + go, 0, 0);
+    const int d_lane = B_STAGE + 4 * (wn * 64 + lr);
+    auto read_d = [&](SRegs &S, const uint8_t *wbuf) {
+        S.s[0] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane);
+        S.s[1] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane + 128);
+        S.s[2] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane + 4 * BN);
+        S.s[3] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane + 4 * BN + 128);
     };
 
     const int a_lane = frag(wm * 64 + lr, lh);
@@ -781,11 +938,11 @@ __global__ __launch_bounds__(THREADS) void k_gemm_gptq_big(Args p, int tiles_m, 
             tot[i][j] = f32x16{};
         }
 
-    WRegs R[2];
-    uint32_t sv[2][2];
+    Regs R[2];
+    SRegs S[2];
     const int last = nk - 1;
-    // group cursors: k-tile kt + 1 (scales) and kt + 2 (codes), clamped to
-    // the last k-tile like the loads themselves; (group, k-tile within it)
+    // group cursors (GPTQ4 / AWQ4): k-tile kt + 1 (scales) and kt + 2 (codes),
+    // clamped to the last k-tile like the loads themselves
     int gs = 0, ts = 0, gw = 0, tw = 0;
     auto advance = [&](int &g, int &tl, int kt_next) {
         if (kt_next > last) return;
@@ -794,14 +951,14 @@ __global__ __launch_bounds__(THREADS) void k_gemm_gptq_big(Args p, int tiles_m, 
             ++g;
         }
     };
-    load_w(R[0], 0, 0);
+    role.load(R[0], rw, rz, 0, 0);
     copy_x(0, 0);
-    load_s(sv[0], 0);
+    load_s(S[0], 0);
     advance(gw, tw, 1);
-    load_w(R[1], min(1, last), gw);
+    role.load(R[1], rw, rz, min(1, last), gw);
     __builtin_amdgcn_sched_barrier(0);
     copy_x(1, min(1, last));
-    store_w(R[0], 0);
+    role.store(R[0], smem + B_OFF);
     // X of k-tile 0 has landed once at most k-tile 1's copies remain. (A
     // count that also allowed the register loads issued after it would
     // break wherever the compiler drops a load whose value is unused.)
@@ -816,45 +973,57 @@ __global__ __launch_bounds__(THREADS) void k_gemm_gptq_big(Args p, int tiles_m, 
         constexpr int P = decltype(par)::value;  // kt % 2
         advance(gs, ts, kt + 1);
         advance(gw, tw, kt + 2);
-        load_s(sv[P ^ 1], gs);
-        load_w(R[P], min(kt + 2, last), gw);
+        load_s(S[P ^ 1], gs);
+        role.load(R[P], rw, rz, min(kt + 2, last), gw);
         // the X copies are this tile's last memory issues (see the wait below)
         __builtin_amdgcn_sched_barrier(0);
         copy_x(slot == 0 ? 2 : slot - 1, min(kt + 2, last));
         const uint8_t *xs = smem + slot * A_STAGE + a_lane;
-        const uint8_t *ws = smem + P * B_STAGE + b_lane;
+        const uint8_t *ws = smem + P * B_BUF + b_lane;
         read_frag(f[1], xs, ws, 1);
-        const bool first = TPG == 1 ? true : TPG == 2 ? P == 0 : tig == 0;
-        if (first)
+        if (Q40) {
+            read_d(S[P], smem + B_OFF + P * B_BUF);
             mma<true>(f[0], part);
-        else
+            read_frag(f[0], xs, ws, 2);
+            mma_last(f[1], S[P].s[0], S[P].s[1], part, tot);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frag(f[1], xs, ws, 3);
+            mma<true>(f[0], part);
+        } else {
+            const bool first = TPG == 1 ? true : TPG == 2 ? P == 0 : tig == 0;
+            if (first)
+                mma<true>(f[0], part);
+            else
+                mma<false>(f[0], part);
+            read_frag(f[0], xs, ws, 2);
+            mma<false>(f[1], part);
+            read_frag(f[1], xs, ws, 3);
             mma<false>(f[0], part);
-        read_frag(f[0], xs, ws, 2);
-        mma<false>(f[1], part);
-        read_frag(f[1], xs, ws, 3);
-        mma<false>(f[0], part);
-        store_w(R[P ^ 1], P ^ 1);
+        }
+        role.store(R[P ^ 1], smem + B_OFF + (P ^ 1) * B_BUF);
         __builtin_amdgcn_s_waitcnt(0xF70 | NX);  // X of k-tile kt + 1: issued before this tile's copies
         lds_barrier();
         slot = slot == 2 ? 0 : slot + 1;
-        read_frag(f[0], smem + slot * A_STAGE + a_lane, smem + (P ^ 1) * B_STAGE + b_lane, 0);
-        bool end;
-        if (TPG == 0) {
+        read_frag(f[0], smem + slot * A_STAGE + a_lane, smem + (P ^ 1) * B_BUF + b_lane, 0);
+        bool end = true;
+        if (!Q40 && TPG == 0) {
             end = ++tig == tpg;
             if (end) tig = 0;
-        } else {
-            end = TPG == 1 || P == 1;
+        } else if (!Q40 && TPG == 2) {
+            end = P == 1;
         }
-        if (TPG != 0 && end) {
-            mma_last(f[1], sv[P][0], sv[P][1], part, tot);
+        if (Q40) {
+            mma_last(f[1], S[P].s[2], S[P].s[3], part, tot);
+        } else if (TPG != 0 && end) {
+            mma_last(f[1], S[P].s[0], S[P].s[1], part, tot);
         } else {
             // (other group sizes: the interleaved form costs a spill there)
             mma<false>(f[1], part);
             if (end) {
-                scale_add(sv[P][0], part[0][0], tot[0][0]);
-                scale_add(sv[P][1], part[0][1], tot[0][1]);
-                scale_add(sv[P][0], part[1][0], tot[1][0]);
-                scale_add(sv[P][1], part[1][1], tot[1][1]);
+                scale_add(S[P].s[0], part[0][0], tot[0][0]);
+                scale_add(S[P].s[1], part[0][1], tot[0][1]);
+                scale_add(S[P].s[0], part[1][0], tot[1][0]);
+                scale_add(S[P].s[1], part[1][1], tot[1][1]);
             }
         }
     };
@@ -886,31 +1055,42 @@ __global__ __launch_bounds__(THREADS) void k_gemm_gptq_big(Args p, int tiles_m, 
         }
 }
 
-// k % 64 == 0, group % 64 == 0, n even, 4-byte aligned codes, and every
-// byte offset (X rows of the last tile included) within 31 bits.
-bool fits(const Args &a) {
+// Shapes the 256 x 128 kernel takes: m >= 256, n >= 128, k % 64 == 0, every
+// byte offset (X rows of the last tile included) within 31 bits; GPTQ4 /
+// AWQ4 with groups that are a multiple of 64 (GPTQ4: n even, 4-byte aligned
+// codes; AWQ4: 4-byte aligned codes, 2-byte aligned zero points); Q4_0 with
+// dword-aligned blocks.
+bool fits(int fmt, const Args &a) {
     constexpr int64_t L = (int64_t)1 << 31;
-    return a.K % BK == 0 && a.group % BK == 0 && a.N % 2 == 0 && a.M >= BM && a.N >= BN &&
-           ((a.M + BM) * a.ldx + a.K) * 2 < L && a.K * a.N / 2 < L && (a.K / a.group) * a.N * 2 < L;
+    if (!(a.M >= BM && a.N >= BN && a.K % BK == 0 && ((a.M + BM) * a.ldx + a.K) * 2 < L)) return false;
+    if (fmt == QBN_Q4_0) return (uintptr_t)a.data % 4 == 0 && a.N * (a.K / 32) * 18 < L;
+    if (a.group % BK != 0 || a.K * a.N / 2 >= L || (a.K / a.group) * a.N * 2 >= L) return false;
+    if (fmt == QBN_GPTQ4) return a.N % 2 == 0 && (uintptr_t)a.data % 4 == 0;
+    return (uintptr_t)a.data % 4 == 0 && (uintptr_t)a.zeros % 2 == 0;
 }
 
-template <bool YF32>
-void launch_gptq(const Args &a, int tm, int tn, hipStream_t s) {
+template <int FMT, bool YF32>
+void launch(const Args &a, int tm, int tn, hipStream_t s) {
     const dim3 grid((unsigned)(tm * tn)), block(THREADS);
-    if (a.group == 64)
-        hipLaunchKernelGGL((k_gemm_gptq_big<YF32, 1>), grid, block, 0, s, a, tm, tn);
-    else if (a.group == 128)
-        hipLaunchKernelGGL((k_gemm_gptq_big<YF32, 2>), grid, block, 0, s, a, tm, tn);
-    else
-        hipLaunchKernelGGL((k_gemm_gptq_big<YF32, 0>), grid, block, 0, s, a, tm, tn);
+    if constexpr (FMT == QBN_Q4_0) {
+        hipLaunchKernelGGL((k_gemm_int4_big<FMT, YF32, 1>), grid, block, 0, s, a, tm, tn);
+    } else {
+        if (a.group == 64)
+            hipLaunchKernelGGL((k_gemm_int4_big<FMT, YF32, 1>), grid, block, 0, s, a, tm, tn);
+        else if (a.group == 128)
+            hipLaunchKernelGGL((k_gemm_int4_big<FMT, YF32, 2>), grid, block, 0, s, a, tm, tn);
+        else
+            hipLaunchKernelGGL((k_gemm_int4_big<FMT, YF32, 0>), grid, block, 0, s, a, tm, tn);
+    }
 }
 
-hipError_t run_gptq(const Args &a, bool yf32, hipStream_t s) {
+template <int FMT>
+hipError_t run(const Args &a, bool yf32, hipStream_t s) {
     const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
     if (yf32)
-        launch_gptq<true>(a, tm, tn, s);
+        launch<FMT, true>(a, tm, tn, s);
     else
-        launch_gptq<false>(a, tm, tn, s);
+        launch<FMT, false>(a, tm, tn, s);
     return hipGetLastError();
 }
 
@@ -918,6 +1098,7 @@ hipError_t run_gptq(const Args &a, bool yf32, hipStream_t s) {
 
 template <int FMT>
 hipError_t run(const Args &a, bool yf32, hipStream_t s) {
+    if (big::fits(FMT, a)) return big::run<FMT>(a, yf32, s);
     // X through its descriptor when k % 64 == 0: measured 4-6% faster for
     // Q4_0 and GPTQ; AWQ's general path spills more with it and is slower.
     const bool xb = FMT != QBN_AWQ4 && a.K % BK == 0 && x_buf_fits(a);
@@ -927,7 +1108,6 @@ hipError_t run(const Args &a, bool yf32, hipStream_t s) {
         if (qb) return run3<FMT, false, false, true, true>(a, yf32, s);
         return xb ? run3<FMT, false, false, false, true>(a, yf32, s) : run3<FMT, false, false>(a, yf32, s);
     } else {
-        if (FMT == QBN_GPTQ4 && big::fits(a) && (uintptr_t)a.data % 4 == 0) return big::run_gptq(a, yf32, s);
         const bool vec = a.N % 8 == 0 && (uintptr_t)a.data % 16 == 0 && (uintptr_t)a.zeros % 8 == 0;
         if (a.group % BK == 0) {
             if (vec && buf_fits(a)) return run3<FMT, true, true, true>(a, yf32, s);

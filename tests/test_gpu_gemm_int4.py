@@ -4,7 +4,7 @@ against the oracle's binary64 entries: a float32 output within
 |y - y_ref| <= 1e-5 * sum|w x| + 1e-6, a bf16 output inside
 [RNE(y_ref - T), RNE(y_ref + T)] (rounding to nearest is monotone). Shapes
 cover one and several 128 x 128 tiles, ragged m and n, k with a half k-tile
-tail, groups of 32 up to all of k, the 256 x 128 GPTQ kernel's cases, and
+tail, groups of 32 up to all of k, the 256 x 128 kernel's cases, and
 the 2048 x 11008 x 4096 layer."""
 import numpy as np
 import pytest
@@ -94,70 +94,79 @@ def test_int4_gemm_all_entries(fmt, M, N, K, g, ydt):
     _check(Y, y_ref, s_ref, ms, ns, "%s %dx%dx%d g=%d %s" % (fmt, M, N, K, g, ydt))
 
 
-# GPTQ with m >= 256, n >= 128, k % 64 == 0, a group that is a multiple of 64
-# and n even runs the 256 x 128 kernel: one k-tile (k = 64); an odd number of
-# k-tiles (the two-tile unrolled loop's tail) with one group per k-tile;
-# groups of two k-tiles; group sizes known only at run time (192, 256, all of
-# k); m just past one row tile; n even but not a multiple of 8 (its last
-# column tile reads column n - 1 in place of the missing ones).
+# m >= 256, n >= 128 and k % 64 == 0 (GPTQ / AWQ: a group that is a multiple
+# of 64; GPTQ: n even) run the 256 x 128 kernel: one k-tile (k = 64); an odd
+# number of k-tiles (the two-tile unrolled loop's tail) with one group per
+# k-tile; groups of two k-tiles; group sizes known only at run time (192,
+# 256, all of k); m just past one row tile; n even but not a multiple of 8
+# (the last column tile reads column n - 1 in place of the missing ones).
+# Q4_0 ignores the group size (its blocks are 32 long).
 SHAPES_256 = [(256, 128, 64, 64), (300, 264, 512, 128), (520, 200, 192, 64), (777, 130, 384, 192),
               (257, 1000, 1024, 256), (512, 136, 4096, 4096), (256, 136, 320, 64), (384, 250, 1152, 128)]
 
 
+@pytest.mark.parametrize("fmt", ["gptq4", "awq4", "q4_0"])
 @pytest.mark.parametrize("M,N,K,g", SHAPES_256)
 @pytest.mark.parametrize("ydt", ["bf16", "f32"])
-def test_gptq_gemm_256_row_tiles(M, N, K, g, ydt):
+def test_int4_gemm_256_row_tiles(fmt, M, N, K, g, ydt):
+    if fmt == "awq4" and N % 8:
+        pytest.skip("AWQ packs eight columns per word: n % 8 == 0")
     inp = _inputs(M * 5 + N * 3 + K + g, M, N, K, g)
-    w = _qt("gptq4", inp, K, N, g)
+    w = _qt(fmt, inp, K, N, g)
     X = dev(inp["X"]).view(torch.bfloat16)
     Y = torch.empty((M, N), dtype=torch.bfloat16 if ydt == "bf16" else torch.float32, device=DEV)
-    say("gptq gemm 256-row tiles", M, N, K, g, ydt)
+    say("int4 gemm 256-row tiles", fmt, M, N, K, g, ydt)
     qbn.quantized_gemm(w, X, Y)
     torch.cuda.synchronize()
     ms, ns = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     ms, ns = ms.ravel(), ns.ravel()
-    y_ref, s_ref = _ref("gptq4", inp, g, ms, ns)
-    _check(Y, y_ref, s_ref, ms, ns, "gptq4 %dx%dx%d g=%d %s" % (M, N, K, g, ydt))
+    y_ref, s_ref = _ref(fmt, inp, g, ms, ns)
+    _check(Y, y_ref, s_ref, ms, ns, "%s %dx%dx%d g=%d %s" % (fmt, M, N, K, g, ydt))
 
 
-def test_gptq_gemm_256_row_tiles_strided():
+@pytest.mark.parametrize("fmt", ["gptq4", "awq4", "q4_0"])
+def test_int4_gemm_256_row_tiles_strided(fmt):
     """The 256 x 128 kernel with ldx > k and ldy > n."""
     M, N, K, g = 300, 136, 256, 128
     inp = _inputs(41, M, N, K, g)
-    w = _qt("gptq4", inp, K, N, g)
+    w = _qt(fmt, inp, K, N, g)
     Xp = torch.zeros((M, K + 40), dtype=torch.bfloat16, device=DEV)
     Xp[:, :K] = dev(inp["X"]).view(torch.bfloat16)
     Yp = torch.full((M, N + 6), 7.0, dtype=torch.float32, device=DEV)
-    say("gptq gemm 256-row tiles strided")
+    say("int4 gemm 256-row tiles strided", fmt)
     qbn.quantized_gemm(w, Xp[:, :K], Yp[:, :N])
     torch.cuda.synchronize()
     ms, ns = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     ms, ns = ms.ravel(), ns.ravel()
-    y_ref, s_ref = _ref("gptq4", inp, g, ms, ns)
-    _check(Yp[:, :N], y_ref, s_ref, ms, ns, "gptq4 256-row strided")
+    y_ref, s_ref = _ref(fmt, inp, g, ms, ns)
+    _check(Yp[:, :N], y_ref, s_ref, ms, ns, fmt + " 256-row strided")
     assert (Yp[:, N:].cpu() == 7.0).all()
 
 
 @pytest.mark.parametrize("fmt", ["gptq4", "awq4"])
-def test_int4_gemm_misaligned_codes_and_zeros(fmt):
-    """Codes and zero points at odd offsets: the element-load path."""
-    M, N, K, g = 40, 136, 256, 64
-    inp = _inputs(17, M, N, K, g)
+@pytest.mark.parametrize("M,zofs", [(40, 1), (300, 1), (300, 2)])
+def test_int4_gemm_misaligned_codes_and_zeros(fmt, M, zofs):
+    """Codes 4 bytes past a 16-byte boundary and zero points 1 or 2 bytes past
+    an 8-byte one: the element-load path (m = 40), and the 256 x 128 kernel,
+    which takes dword-aligned codes and (AWQ) 2-byte aligned zero points
+    (m = 300; AWQ with zofs = 1 goes to the element-load path)."""
+    N, K, g = 136, 256, 64
+    inp = _inputs(17 + M + zofs, M, N, K, g)
     data = inp["gptq"] if fmt == "gptq4" else inp["awq"]
     dd = torch.zeros(data.size + 1, dtype=torch.int32, device=DEV)
     dd[1:] = dev(data).flatten()
-    zd = torch.zeros(inp["zeros"].size + 1, dtype=torch.uint8, device=DEV)
-    zd[1:] = dev(inp["zeros"]).flatten()
-    w = qbn.QTensor(fmt, N, K, dd[1:], dev(inp["scales"].view(np.uint16)), zd[1:], group=g)
+    zd = torch.zeros(inp["zeros"].size + zofs, dtype=torch.uint8, device=DEV)
+    zd[zofs:] = dev(inp["zeros"]).flatten()
+    w = qbn.QTensor(fmt, N, K, dd[1:], dev(inp["scales"].view(np.uint16)), zd[zofs:], group=g)
     X = dev(inp["X"]).view(torch.bfloat16)
-    say("int4 gemm misaligned", fmt)
+    say("int4 gemm misaligned", fmt, M, zofs)
     Y = torch.empty((M, N), dtype=torch.float32, device=DEV)
     qbn.quantized_gemm(w, X, Y)
     torch.cuda.synchronize()
     ms, ns = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     ms, ns = ms.ravel(), ns.ravel()
     y_ref, s_ref = _ref(fmt, inp, g, ms, ns)
-    _check(Y, y_ref, s_ref, ms, ns, fmt + " misaligned")
+    _check(Y, y_ref, s_ref, ms, ns, "%s misaligned m=%d zofs=%d" % (fmt, M, zofs))
 
 
 def test_int4_gemm_strided_activations_and_output():
