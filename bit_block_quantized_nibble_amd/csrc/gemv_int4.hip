@@ -257,6 +257,80 @@ __global__ __launch_bounds__(THREADS) void k_gemv_affine(const uint32_t *__restr
     }
 }
 
+// Balanced form (GPTQ4, VEC layout): the n / 8 column groups of 8 are dealt out
+// evenly, floor or ceil(groups / grid) consecutive groups per workgroup, with
+// grid = 256 (one workgroup per compute unit) unless that would need more
+// than 8 groups per workgroup. The 11008-column layer then runs 5 or 6
+// groups per compute unit instead of 1 or 2 blocks of 4 (which took as long
+// as 2 full rounds: 10.2 us against 6.6 us for 8192 columns). k is split
+// into 128 slices of SPL-step rounds (an 8-row step each); lane t of a
+// workgroup with CWB groups owns group t % CWB and slice t / CWB (whole
+// lines: consecutive lanes read consecutive 32-byte column groups of one
+// row). The slices' column sums go through LDS and are added in a fixed
+// order: 16 threads per column each add 8 consecutive slices, then a
+// butterfly over the 16.
+constexpr int kBalSlices = 128;
+constexpr int kBalMaxGroups = 8;
+constexpr int kBalCUs = 256;
+
+template <int FMT, typename XT, int SPL>
+__global__ __launch_bounds__(kBalMaxGroups * kBalSlices) void k_gemv_affine_bal(
+    const uint32_t *__restrict__ qw, const uint16_t *__restrict__ sc, const uint8_t *__restrict__ zp,
+    const XT *__restrict__ x, float *__restrict__ y, int64_t n, int64_t k, int64_t group) {
+    __shared__ float red[kBalSlices][kBalMaxGroups * 8];
+    const int t = threadIdx.x;
+    const int64_t groups = n / 8;
+    // XCD-aware order, as in k_gemv_affine: neighbouring column ranges (which
+    // share cache lines at their ends) go to one XCD
+    const int64_t nblk = gridDim.x, q8 = nblk / 8, r8 = nblk % 8, xcd = blockIdx.x % 8;
+    const int64_t blk = xcd * q8 + min(xcd, r8) + blockIdx.x / 8;
+    const int64_t g0 = blk * groups / nblk, g1 = (blk + 1) * groups / nblk;
+    const int cwb = (int)(g1 - g0);  // 1 .. kBalMaxGroups
+    const bool live = t < cwb * kBalSlices;
+    const int cw = live ? t % cwb : 0, sl = live ? t / cwb : 0;
+    const int64_t c0 = (g0 + cw) * 8;
+    const int64_t nsteps = k / 8;
+    int64_t cc[8];  // (element loads only; the VEC path reads 8 columns as vectors)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cc[i] = c0 + i;
+
+    float tot[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tot[i] = 0.0f;
+    for (int64_t jb = live ? (int64_t)sl * SPL : nsteps; jb < nsteps; jb += (int64_t)kBalSlices * SPL) {
+        AffRound<SPL, XT> rd;
+        aff_load<FMT, true, SPL>(rd, qw, sc, zp, x, n, group, c0, cc, jb);
+        aff_compute<FMT, true, SPL>(rd, tot);
+    }
+    if (live) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) red[sl][8 * cw + i] = tot[i];
+    }
+    __syncthreads();
+    // column j = t / 16 (of cwb * 8), part p = t % 16: slices 8p .. 8p + 7
+    const int j = t / 16, pp = t % 16;
+    float v = 0.0f;
+    if (j < cwb * 8) {
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) v += red[8 * pp + s8][j];
+    }
+    v += __shfl_xor(v, 1, 16);
+    v += __shfl_xor(v, 2, 16);
+    v += __shfl_xor(v, 4, 16);
+    v += __shfl_xor(v, 8, 16);
+    if (j < cwb * 8 && pp == 0) y[g0 * 8 + j] = v;
+}
+
+template <int FMT, typename XT, int SPL>
+hipError_t launch_affine_bal(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
+    const int64_t groups = w.n / 8;
+    const int64_t grid = max(min((int64_t)kBalCUs, groups), (groups + kBalMaxGroups - 1) / kBalMaxGroups);
+    hipLaunchKernelGGL((k_gemv_affine_bal<FMT, XT, SPL>), dim3((unsigned)grid), dim3(kBalMaxGroups * kBalSlices), 0, s,
+                       (const uint32_t *)w.data, (const uint16_t *)w.scales, (const uint8_t *)w.zeros, x, y, w.n, w.k,
+                       (int64_t)w.group);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ Q4_0
 // One wave per R rows; lanes stride over the rows' blocks and load each
 // block's activations once for all R rows.
@@ -448,6 +522,12 @@ template <int FMT, typename XT>
 hipError_t run_affine(const qbn_tensor &w, const XT *x, float *y, hipStream_t s) {
     const bool vec = (w.n % 8) == 0 && ((uintptr_t)w.data % 16) == 0 && ((uintptr_t)w.scales % 16) == 0 &&
                      ((uintptr_t)w.zeros % 8) == 0;
+    // GPTQ takes the balanced form, two 8-row steps per round when the group
+    // allows (11008 x 4096: 8.8 us; one step 9.3, four 9.0; the blocked form
+    // 10.2). AWQ measured slower in it (15.5-15.7 us against 11.4) and keeps
+    // the blocked form.
+    if (FMT == QBN_GPTQ4 && vec)
+        return (w.group % 16 == 0) ? launch_affine_bal<FMT, XT, 2>(w, x, y, s) : launch_affine_bal<FMT, XT, 1>(w, x, y, s);
     return vec ? run_affine_spl<FMT, XT, true>(w, x, y, s) : run_affine_spl<FMT, XT, false>(w, x, y, s);
 }
 

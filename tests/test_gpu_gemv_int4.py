@@ -58,6 +58,24 @@ def test_affine_gemv_shapes(fmt, K, N, g, xdt):
     assert_within_tolerance(y, y_ref, s_ref, "%s K=%d N=%d g=%d %s" % (fmt, K, N, g, xdt))
 
 
+# GPTQ in the vector layout deals its n / 8 column groups over up to 256
+# workgroups: 257 groups (one workgroup takes two), 513 (two or three each),
+# 2050 (more than 8 per workgroup would be needed: 257 workgroups of 7 or 8),
+# groups of 8 (rounds of one 8-row step) and k shorter than one round per
+# slice.
+@pytest.mark.parametrize("K,N,g", [(256, 2056, 64), (1024, 4104, 128), (512, 16400, 128), (64, 2064, 8),
+                                   (4096, 3000, 4096), (96, 2048, 32)])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_gptq_gemv_column_groups_per_workgroup(K, N, g, xdt):
+    rng = np.random.default_rng(K + 7 * N + g)
+    data, s, z = _affine(rng, "gptq4", K, N, g)
+    x32 = workloads.x_f32(rng, K)
+    x = x32 if xdt == "f32" else workloads.bf16_bits_from_f32(x32)
+    y = _run_affine("gptq4", data, s, z, K, N, g, x)
+    y_ref, s_ref = oracle.int4_gemv("gptq4", data, s, z, g, x, range(N))
+    assert_within_tolerance(y, y_ref, s_ref, "gptq4 K=%d N=%d g=%d %s" % (K, N, g, xdt))
+
+
 @pytest.mark.parametrize("fmt", ["gptq4", "awq4"])
 def test_affine_gemv_misaligned_buffers(fmt):
     rng = np.random.default_rng(5)
