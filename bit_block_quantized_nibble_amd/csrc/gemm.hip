@@ -159,15 +159,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4_bf16(const uint16_t *__
 }
 
 // ------------------------------------------------------------------ 256 x 256 kernel
-// Large-problem variant: workgroup tile 256 x 256, four waves in 2 x 2, each
-// owning a 128 x 128 block of Y (4 x 4 MFMA tiles, 256 accumulator
-// registers). X is staged in LDS as bf16 with an XOR swizzle of its
-// 16-byte chunks (chunk c of row r at position c ^ (r & 7)), so the 32 rows a
-// fragment read touches hit distinct LDS banks. W is staged as packed FP4
-// codes plus E8M0 bytes (a quarter of the bf16 bytes) and each wave expands
-// its B fragments to bf16 right after reading them, with the scale folded
-// into the conversion. The accumulation runs the full k in the MFMA
-// accumulators: at most k/16 binary32 roundings per output (512 at
+// Large-problem variant: workgroup tile 256 x 256, eight waves in 4 x 2, each
+// owning a 64 x 128 block of Y (2 x 4 MFMA tiles, 128 accumulator
+// registers). X is staged in LDS as bf16 in blocks of 8 rows (layout below),
+// so the 32 rows a fragment read touches hit distinct LDS banks. W is staged
+// as packed FP4 codes plus E8M0 bytes (a quarter of the bf16 bytes) and each
+// wave expands its B fragments to bf16 right after reading them, with the
+// scale folded into the conversion. The accumulation runs the full k in the
+// MFMA accumulators: at most k/16 binary32 roundings per output (512 at
 // k = 8192), each at most half an ulp of a partial sum.
 namespace big {
 
