@@ -108,7 +108,7 @@ WORKLOADS = {
              "scale2 = 0.01): read bf16, write codes and scale bytes",
         bytes=4096 * 4096 * 2 + 4096 * 2048 + 4096 * 256),
     "mxfp4_gemm": dict(
-        cfg=4, kind="gemm", unit="TFLOP/s",
+        cfg=4, kind="gemm", unit="TFLOP/s", dtype="bf16",
         desc="MXFP4 prefill GEMM: W 8192x8192 (E2M1, E8M0 per 32) x X bf16 2048x8192 -> Y bf16, fp32 accumulate",
         flops=2.0 * 2048 * 8192 * 8192, bytes=8192 * 4096 + 8192 * 256 + 2048 * 8192 * 2 * 2),
     "gptq_gemm": dict(
