@@ -594,7 +594,7 @@ bool buf_fits(const Args &a) {
 
 // ------------------------------------------------------------------ 256 x 128 kernel
 // Large-m variant (k % 64 == 0; GPTQ4 / AWQ4 with groups that are a multiple
-// of 64, or Q4_0). Workgroup tile 256 x 128 of Y, eight waves in 4 x 2, each
+// of 32, or Q4_0). Workgroup tile 256 x 128 of Y, eight waves in 4 x 2, each
 // 64 x 64 (2 x 2 MFMA tiles), one workgroup per compute unit. Each decoded
 // weight tile then serves 256 rows of X instead of 128, which halves the
 // decode work per MFMA.
@@ -607,8 +607,9 @@ bool buf_fits(const Args &a) {
 //    are decoded to bf16 (q - z) and written to the other of two LDS weight
 //    buffers. One barrier per k-tile.
 //  - Each lane loads the scales of its two output columns itself; at the
-//    end of a group (GPTQ4 / AWQ4) or of each 32-k block (Q4_0) the partial
-//    sums are scaled and added to the totals as above.
+//    end of a group (GPTQ4 / AWQ4 with groups that are a multiple of 64) or
+//    of each 32-k half of a k-tile (Q4_0, and odd multiples of 32) the
+//    partial sums are scaled and added to the totals as above.
 // X and the decoded weights share one LDS layout: blocks of 8 rows, chunk c
 // (k = 8c .. 8c + 7) of row r at (r / 8) * 1152 + c * 128 + (r % 8) * 16, so
 // one 64-lane copy fills 8 rows x 128 bytes with lane i at 16 i, and the
@@ -657,7 +658,7 @@ template <>
 struct Role<QBN_GPTQ4> {
     struct Regs {
         uint32_t w[2];
-        uint32_t z;
+        uint32_t z[2];  // zero-point bytes of the two words' groups
     };
     int nl, r0;
     uint32_t wo, zo, w4, step, nz;
@@ -671,18 +672,22 @@ struct Role<QBN_GPTQ4> {
         zo = (uint32_t)nw;
         nz = (uint32_t)p.N;
     }
+    // g0, g1: groups of the k-tile's two 32-k halves (equal unless HALF);
+    // word row r0 lies in the first half, r0 + 4 in the second
+    template <bool HALF>
     __device__ __forceinline__ void load(Regs &R, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rz, int kt,
-                                         int g) const {
+                                         int g0, int g1) const {
         const uint32_t o = wo + (uint32_t)kt * step;
         R.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, 0);
         R.w[1] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + w4, 0, 0);
-        R.z = __builtin_amdgcn_raw_buffer_load_b8(rz, (uint32_t)g * nz + zo, 0, 0);
+        R.z[0] = __builtin_amdgcn_raw_buffer_load_b8(rz, (uint32_t)g0 * nz + zo, 0, 0);
+        R.z[1] = HALF ? __builtin_amdgcn_raw_buffer_load_b8(rz, (uint32_t)g1 * nz + zo, 0, 0) : R.z[0];
     }
     __device__ __forceinline__ void store(const Regs &R, uint8_t *wst) const {
-        const float z = (float)(R.z & 0xFFu);
-        const float zz[8] = {z, z, z, z, z, z, z, z};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            const float z = (float)(R.z[h] & 0xFFu);
+            const float zz[8] = {z, z, z, z, z, z, z, z};
             float v[8];
             nibbles_minus(R.w[h], zz, v);
             *reinterpret_cast<u32x4 *>(wst + frag(nl, r0 + 4 * h)) = bf16x8_of(v);
@@ -716,11 +721,14 @@ struct Role<QBN_AWQ4> {
         zo = (uint32_t)(wc * 8 + 2 * q);
         nz = (uint32_t)p.N;
     }
+    // word rows 8r .. 8r + 7 lie in 32-k half r / 4 of the k-tile
+    template <bool HALF>
     __device__ __forceinline__ void load(Regs &R, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rz, int kt,
-                                         int g) const {
+                                         int g0, int g1) const {
         const uint32_t o = wo + (uint32_t)kt * step;
 #pragma unroll
         for (int i = 0; i < 8; ++i) R.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + (uint32_t)i * row, 0, 0);
+        const int g = (HALF && r >= 4) ? g1 : g0;
         R.z = __builtin_amdgcn_raw_buffer_load_b16(rz, (uint32_t)g * nz + zo, 0, 0);
     }
     __device__ __forceinline__ void store(const Regs &R, uint8_t *wst) const {
@@ -766,7 +774,8 @@ struct Role<QBN_Q4_0> {
         wo = (uint32_t)((n * (p.K / 32) + b) * 18 + 2 + 8 * hh - (b ? 4 : 2));
         step = 2 * 18;
     }
-    __device__ __forceinline__ void load(Regs &R, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t, int kt,
+    template <bool HALF>
+    __device__ __forceinline__ void load(Regs &R, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t, int kt, int,
                                          int) const {
         const uint32_t o = wo + (uint32_t)kt * step;
         R.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, 0);
@@ -850,11 +859,13 @@ __device__ __forceinline__ void mma_last(const Frag &f, uint32_t s0, uint32_t s1
 // k-tile kt - 1.
 // TPG: k-tiles per group when it is 1 or 2 (group 64 or 128; the group
 // boundaries then fall on fixed k-tile parities of the two-tile unrolled
-// loop), 0 for any other multiple of 64; unused for Q4_0, whose 32-k blocks
-// are rescaled after steps 1 and 3 of every k-tile.
+// loop), 0 for any other multiple of 64, -1 for odd multiples of 32 (32, 96,
+// ...). Q4_0 (32-k blocks) and TPG = -1 rescale after steps 1 and 3 of every
+// k-tile, each 32-k half with its own scale.
 template <int FMT, bool YF32, int TPG>
 __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, int tiles_n) {
     constexpr bool Q40 = FMT == QBN_Q4_0;
+    constexpr bool HALF = Q40 || TPG < 0;
     __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
     // tile order as in k_gemm_int4, with groups of GM row tiles
     constexpr int GM = 4;
@@ -872,7 +883,10 @@ __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, 
     const int wm = wave / 2, wn = wave % 2;
     const int lr = lane % 32, lh = lane / 32;
     const int nk = (int)(p.K / BK);
-    const int tpg = Q40 ? 1 : TPG ? TPG : (int)(p.group / BK);
+    const int tpg = HALF ? 1 : TPG ? TPG : (int)(p.group / BK);
+    const int group = (int)p.group;
+    // (HALF) group of 32-k half h of k-tile kt
+    auto grp = [&](int kt, int h) { return (BK * kt + 32 * h) / group; };
     const int64_t N = p.N;
 
     const __amdgpu_buffer_rsrc_t rx = rsrc(p.X, (uint32_t)(((p.M - 1) * p.ldx + p.K) * 2));
@@ -904,20 +918,36 @@ __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, 
     using Regs = typename Role<FMT>::Regs;
 
     // The scales of this lane's output columns (MFMA column lr of tiles j =
-    // 0, 1). GPTQ4 / AWQ4: the two fp16 scales of a group, loaded a k-tile
-    // ahead; Q4_0: the d of blocks b = 0, 1 of the k-tile, s[2 b + j], read
-    // from the LDS weight buffer.
+    // 0, 1), s[j]: GPTQ4 / AWQ4 the two fp16 scales of a group, loaded a
+    // k-tile ahead. HALF, s[2 h + j] for the k-tile's 32-k half h: Q4_0 the d
+    // of its two blocks, read from the LDS weight buffer; GPTQ4 / AWQ4 the
+    // scales of the halves' groups, loaded a k-tile ahead.
     const int64_t c0 = min(n0 + wn * 64 + lr, N - 1), c1 = min(n0 + wn * 64 + 32 + lr, N - 1);
     const uint32_t so0 = (uint32_t)(c0 * 2), so1 = (uint32_t)(c1 * 2);
     struct SRegs {
-        uint32_t s[Q40 ? 4 : 2];
+        uint32_t s[HALF ? 4 : 2];
     };
-    auto load_s = [&](SRegs &S, int g) {
-        if (!Q40) {
-            const uint32_t go = (uint32_t)(g * N * 2);
+    // u: the group (GPTQ4 / AWQ4) or, with HALF, the k-tile
+    auto load_s = [&](SRegs &S, int u) {
+        if (Q40) return;
+        if (HALF) {
+            const uint32_t g0 = (uint32_t)(grp(u, 0) * N * 2), g1 = (uint32_t)(grp(u, 1) * N * 2);
+            S.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, so0 + g0, 0, 0);
+            S.s[1] = __builtin_amdgcn_raw_buffer_load_b16(rs, so1 + g0, 0, 0);
+            S.s[2] = __builtin_amdgcn_raw_buffer_load_b16(rs, so0 + g1, 0, 0);
+            S.s[3] = __builtin_amdgcn_raw_buffer_load_b16(rs, so1 + g1, 0, 0);
+        } else {
+            const uint32_t go = (uint32_t)(u * N * 2);
             S.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, so0 + go, 0, 0);
             S.s[1] = __builtin_amdgcn_raw_buffer_load_b16(rs, so1 + go, 0, 0);
         }
+    };
+    // codes and zero points of k-tile kt (g: its group, without HALF)
+    auto load_w = [&](Regs &R, int kt, int g) {
+        if (HALF)
+            role.template load<true>(R, rw, rz, kt, grp(kt, 0), grp(kt, 1));
+        else
+            role.template load<false>(R, rw, rz, kt, g, g);
     };
     const int d_lane = B_STAGE + 4 * (wn * 64 + lr);
     auto read_d = [&](SRegs &S, const uint8_t *wbuf) {
@@ -951,11 +981,11 @@ __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, 
             ++g;
         }
     };
-    role.load(R[0], rw, rz, 0, 0);
+    load_w(R[0], 0, 0);
     copy_x(0, 0);
     load_s(S[0], 0);
     advance(gw, tw, 1);
-    role.load(R[1], rw, rz, min(1, last), gw);
+    load_w(R[1], min(1, last), gw);
     __builtin_amdgcn_sched_barrier(0);
     copy_x(1, min(1, last));
     role.store(R[0], smem + B_OFF);
@@ -973,16 +1003,16 @@ __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, 
         constexpr int P = decltype(par)::value;  // kt % 2
         advance(gs, ts, kt + 1);
         advance(gw, tw, kt + 2);
-        load_s(S[P ^ 1], gs);
-        role.load(R[P], rw, rz, min(kt + 2, last), gw);
+        load_s(S[P ^ 1], HALF ? min(kt + 1, last) : gs);
+        load_w(R[P], min(kt + 2, last), gw);
         // the X copies are this tile's last memory issues (see the wait below)
         __builtin_amdgcn_sched_barrier(0);
         copy_x(slot == 0 ? 2 : slot - 1, min(kt + 2, last));
         const uint8_t *xs = smem + slot * A_STAGE + a_lane;
         const uint8_t *ws = smem + P * B_BUF + b_lane;
         read_frag(f[1], xs, ws, 1);
-        if (Q40) {
-            read_d(S[P], smem + B_OFF + P * B_BUF);
+        if (HALF) {
+            if (Q40) read_d(S[P], smem + B_OFF + P * B_BUF);
             mma<true>(f[0], part);
             read_frag(f[0], xs, ws, 2);
             mma_last(f[1], S[P].s[0], S[P].s[1], part, tot);
@@ -1006,13 +1036,13 @@ __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, 
         slot = slot == 2 ? 0 : slot + 1;
         read_frag(f[0], smem + slot * A_STAGE + a_lane, smem + (P ^ 1) * B_BUF + b_lane, 0);
         bool end = true;
-        if (!Q40 && TPG == 0) {
+        if (!HALF && TPG == 0) {
             end = ++tig == tpg;
             if (end) tig = 0;
-        } else if (!Q40 && TPG == 2) {
+        } else if (!HALF && TPG == 2) {
             end = P == 1;
         }
-        if (Q40) {
+        if (HALF) {
             mma_last(f[1], S[P].s[2], S[P].s[3], part, tot);
         } else if (TPG != 0 && end) {
             mma_last(f[1], S[P].s[0], S[P].s[1], part, tot);
@@ -1057,14 +1087,14 @@ __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, 
 
 // Shapes the 256 x 128 kernel takes: m >= 256, n >= 128, k % 64 == 0, every
 // byte offset (X rows of the last tile included) within 31 bits; GPTQ4 /
-// AWQ4 with groups that are a multiple of 64 (GPTQ4: n even, 4-byte aligned
+// AWQ4 with groups that are a multiple of 32 (GPTQ4: n even, 4-byte aligned
 // codes; AWQ4: 4-byte aligned codes, 2-byte aligned zero points); Q4_0 with
 // dword-aligned blocks.
 bool fits(int fmt, const Args &a) {
     constexpr int64_t L = (int64_t)1 << 31;
     if (!(a.M >= BM && a.N >= BN && a.K % BK == 0 && ((a.M + BM) * a.ldx + a.K) * 2 < L)) return false;
     if (fmt == QBN_Q4_0) return (uintptr_t)a.data % 4 == 0 && a.N * (a.K / 32) * 18 < L;
-    if (a.group % BK != 0 || a.K * a.N / 2 >= L || (a.K / a.group) * a.N * 2 >= L) return false;
+    if (a.group % 32 != 0 || a.K * a.N / 2 >= L || (a.K / a.group) * a.N * 2 >= L) return false;
     if (fmt == QBN_GPTQ4) return a.N % 2 == 0 && (uintptr_t)a.data % 4 == 0;
     return (uintptr_t)a.data % 4 == 0 && (uintptr_t)a.zeros % 2 == 0;
 }
@@ -1079,8 +1109,10 @@ void launch(const Args &a, int tm, int tn, hipStream_t s) {
             hipLaunchKernelGGL((k_gemm_int4_big<FMT, YF32, 1>), grid, block, 0, s, a, tm, tn);
         else if (a.group == 128)
             hipLaunchKernelGGL((k_gemm_int4_big<FMT, YF32, 2>), grid, block, 0, s, a, tm, tn);
-        else
+        else if (a.group % BK == 0)
             hipLaunchKernelGGL((k_gemm_int4_big<FMT, YF32, 0>), grid, block, 0, s, a, tm, tn);
+        else
+            hipLaunchKernelGGL((k_gemm_int4_big<FMT, YF32, -1>), grid, block, 0, s, a, tm, tn);
     }
 }
 

@@ -99,10 +99,13 @@ def test_int4_gemm_all_entries(fmt, M, N, K, g, ydt):
 # number of k-tiles (the two-tile unrolled loop's tail) with one group per
 # k-tile; groups of two k-tiles; group sizes known only at run time (192,
 # 256, all of k); m just past one row tile; n even but not a multiple of 8
-# (the last column tile reads column n - 1 in place of the missing ones).
-# Q4_0 ignores the group size (its blocks are 32 long).
+# (the last column tile reads column n - 1 in place of the missing ones);
+# groups that are odd multiples of 32 (32, 96, 160: each 32-k half of a
+# k-tile scaled on its own, a k-tile spanning two groups). Q4_0 ignores the
+# group size (its blocks are 32 long).
 SHAPES_256 = [(256, 128, 64, 64), (300, 264, 512, 128), (520, 200, 192, 64), (777, 130, 384, 192),
-              (257, 1000, 1024, 256), (512, 136, 4096, 4096), (256, 136, 320, 64), (384, 250, 1152, 128)]
+              (257, 1000, 1024, 256), (512, 136, 4096, 4096), (256, 136, 320, 64), (384, 250, 1152, 128),
+              (300, 264, 512, 32), (520, 200, 384, 96), (256, 136, 640, 160), (777, 130, 192, 32)]
 
 
 @pytest.mark.parametrize("fmt", ["gptq4", "awq4", "q4_0"])
