@@ -615,9 +615,11 @@ bool buf_fits(const Args &a) {
 // one 64-lane copy fills 8 rows x 128 bytes with lane i at 16 i, and the
 // fragment reads of 32 consecutive rows are conflict-free.
 // The range check of a buffer load covers the lane's offset but not the
-// uniform one, so every offset that depends on k or the group is carried in
-// the lane's offset, and lanes whose columns lie past n read the last valid
-// column (their outputs are never stored).
+// uniform one. The weight-side loads therefore carry every offset that
+// depends on k or the group in the lane's offset, and lanes whose columns lie
+// past n read the last valid column (their outputs are never stored). The X
+// copies keep k in the uniform offset: a row past m is out of range by its
+// lane offset alone, and valid rows stay inside X for every k-tile.
 namespace big {
 
 constexpr int BM = 256, BN = 128, BK = 64;
