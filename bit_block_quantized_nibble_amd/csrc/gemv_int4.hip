@@ -259,10 +259,11 @@ __global__ __launch_bounds__(THREADS) void k_gemv_affine(const uint32_t *__restr
 
 // Balanced form (GPTQ4, VEC layout): the n / 8 column groups of 8 are dealt out
 // evenly, floor or ceil(groups / grid) consecutive groups per workgroup, with
-// grid = 256 (one workgroup per compute unit) unless that would need more
-// than 8 groups per workgroup. The 11008-column layer then runs 5 or 6
-// groups per compute unit instead of 1 or 2 blocks of 4 (which took as long
-// as 2 full rounds: 10.2 us against 6.6 us for 8192 columns). k is split
+// grid = 256 (one workgroup per compute unit; one per group when there are
+// fewer) unless that would need more than 8 groups per workgroup. The
+// 11008-column layer then runs 5 or 6 groups per compute unit instead of 1
+// or 2 blocks of 4 (with one cached weight copy the blocks took as long as 2
+// full rounds: 10.2 us against 6.6 us for 8192 columns). k is split
 // into 128 slices of SPL-step rounds (an 8-row step each); lane t of a
 // workgroup with CWB groups owns group t % CWB and slice t / CWB (whole
 // lines: consecutive lanes read consecutive 32-byte column groups of one
