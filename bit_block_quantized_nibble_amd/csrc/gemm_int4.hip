@@ -931,8 +931,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, 
     };
     // u: the group (GPTQ4 / AWQ4) or, with HALF, the k-tile
     auto load_s = [&](SRegs &S, int u) {
-        if (Q40) return;
-        if (HALF) {
+        if constexpr (Q40) return;
+        if constexpr (HALF) {
             const uint32_t g0 = (uint32_t)(grp(u, 0) * N * 2), g1 = (uint32_t)(grp(u, 1) * N * 2);
             S.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, so0 + g0, 0, 0);
             S.s[1] = __builtin_amdgcn_raw_buffer_load_b16(rs, so1 + g0, 0, 0);
@@ -946,17 +946,19 @@ __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, 
     };
     // codes and zero points of k-tile kt (g: its group, without HALF)
     auto load_w = [&](Regs &R, int kt, int g) {
-        if (HALF)
+        if constexpr (HALF)
             role.template load<true>(R, rw, rz, kt, grp(kt, 0), grp(kt, 1));
         else
             role.template load<false>(R, rw, rz, kt, g, g);
     };
     const int d_lane = B_STAGE + 4 * (wn * 64 + lr);
     auto read_d = [&](SRegs &S, const uint8_t *wbuf) {
-        S.s[0] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane);
-        S.s[1] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane + 128);
-        S.s[2] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane + 4 * BN);
-        S.s[3] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane + 4 * BN + 128);
+        if constexpr (Q40) {
+            S.s[0] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane);
+            S.s[1] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane + 128);
+            S.s[2] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane + 4 * BN);
+            S.s[3] = *reinterpret_cast<const uint32_t *>(wbuf + d_lane + 4 * BN + 128);
+        }
     };
 
     const int a_lane = frag(wm * 64 + lr, lh);
@@ -1013,8 +1015,8 @@ __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, 
         const uint8_t *xs = smem + slot * A_STAGE + a_lane;
         const uint8_t *ws = smem + P * B_BUF + b_lane;
         read_frag(f[1], xs, ws, 1);
-        if (HALF) {
-            if (Q40) read_d(S[P], smem + B_OFF + P * B_BUF);
+        if constexpr (HALF) {
+            if constexpr (Q40) read_d(S[P], smem + B_OFF + P * B_BUF);
             mma<true>(f[0], part);
             read_frag(f[0], xs, ws, 2);
             mma_last(f[1], S[P].s[0], S[P].s[1], part, tot);
@@ -1044,7 +1046,7 @@ __global__ __launch_bounds__(THREADS) void k_gemm_int4_big(Args p, int tiles_m, 
         } else if (!HALF && TPG == 2) {
             end = P == 1;
         }
-        if (HALF) {
+        if constexpr (HALF) {
             mma_last(f[1], S[P].s[2], S[P].s[3], part, tot);
         } else if (TPG != 0 && end) {
             mma_last(f[1], S[P].s[0], S[P].s[1], part, tot);
