@@ -1,0 +1,118 @@
+"""GPU parity over seeded random shapes: every GEMV format, both activation
+dtypes, row counts from 1 to a few hundred and reduction lengths that are
+arbitrary multiples of the format's block (so each launcher's shape switch,
+the generic kernels and the ragged tails all get drawn), compared element
+by element with the oracle within |y - y_ref| <= 1e-5 * sum|w x| + 1e-6.
+The shape list is fixed by the seed, so a failure names a reproducible case."""
+import numpy as np
+import pytest
+import torch
+
+import bit_block_quantized_nibble_amd as qbn
+import oracle
+import workloads
+from gpu_util import DEV, assert_within_tolerance, dev, say, x_dev
+
+pytestmark = pytest.mark.gpu
+
+# (format, k block, largest k multiple): k = block * U{1..kmax}
+FORMATS = {
+    "mxfp4": (32, 300),
+    "nvfp4": (16, 600),
+    "q4_k": (256, 40),
+    "q4_0": (32, 300),
+    "nvfp4_cke": (64, 150),
+    "gptq4": (None, None),
+    "awq4": (None, None),
+}
+
+
+def _cases(per_format=12, seed=31337):
+    rng = np.random.default_rng(seed)
+    out = []
+    for fmt, (blk, kmax) in FORMATS.items():
+        for i in range(per_format):
+            xdt = "bf16" if i % 2 else "f32"
+            if fmt in ("gptq4", "awq4"):
+                g = int(rng.choice([32, 64, 128]))
+                k = g * int(rng.integers(1, 33))
+                n = 8 * int(rng.integers(1, 97)) if fmt == "awq4" or i % 3 else int(rng.integers(1, 700))
+                out.append((fmt, n, k, g, xdt))
+            else:
+                k = blk * int(rng.integers(1, kmax + 1))
+                n = int(rng.integers(1, 700))
+                out.append((fmt, n, k, 0, xdt))
+    return out
+
+
+def _x(rng, k, xdt):
+    x32 = rng.standard_normal(k).astype(np.float32)
+    return x32 if xdt == "f32" else workloads.bf16_bits_from_f32(x32)
+
+
+@pytest.mark.parametrize("fmt,n,k,g,xdt", _cases())
+def test_gemv_random_shapes(fmt, n, k, g, xdt):
+    rng = np.random.default_rng(n * 7919 + k * 31 + g)
+    x = _x(rng, k, xdt)
+    if fmt in ("gptq4", "awq4"):
+        qweight, scales, zeros = workloads.int4_affine(rng, k, n, g)
+        data = qweight if fmt == "gptq4" else rng.integers(0, 2**32, size=(k, n // 8), dtype=np.uint32)
+        w = qbn.QTensor(fmt, n, k, dev(data), dev(scales.view(np.uint16)), dev(zeros), group=g)
+        y_ref, s_ref = oracle.int4_gemv(fmt, data, scales, zeros, g, x, range(n))
+    else:
+        if fmt == "q4_0":
+            data, scales, scale2, ofmt = workloads.q4_0_blocks(rng, n, k), None, 1.0, oracle.Q4_0
+        elif fmt == "nvfp4_cke":
+            data, scales, scale2, ofmt = workloads.cke_blocks(rng, n, k), None, 0.01, oracle.NVFP4_CKE
+        else:
+            inp = workloads.workload({"mxfp4": 1, "nvfp4": 2, "q4_k": 3}[fmt], n=n, k=k, seed=int(rng.integers(1 << 30)))
+            data, scales, scale2 = inp["data"], inp["scales"], inp["scale2"]
+            ofmt = {"mxfp4": oracle.MXFP4, "nvfp4": oracle.NVFP4, "q4_k": oracle.Q4_K}[fmt]
+        w = qbn.QTensor(fmt, n, k, dev(data), None if scales is None else dev(scales), scale2=scale2)
+        y_ref, s_ref = oracle.gemv_rows(ofmt, data, scales, scale2, k, x, range(n))
+    say("gemv sweep", fmt, n, k, g, xdt)
+    y = qbn.quantized_gemv(w, x_dev(x))
+    torch.cuda.synchronize()
+    assert_within_tolerance(y.cpu().numpy(), y_ref, s_ref, "gemv %s n=%d k=%d g=%d x=%s" % (fmt, n, k, g, xdt))
+
+
+# ------------------------------------------------------------------ GEMMs
+# Random (m, n, k) for the MXFP4 bf16 GEMM and the three int4 layouts; about
+# half the draws reach the 256-row workgroup tiles (m >= 256). Every entry
+# is checked: bf16 outputs inside [RNE(y_ref - T), RNE(y_ref + T)].
+def _gemm_cases(count=12, seed=4711):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        m = int(rng.integers(256, 520)) if i % 2 else int(rng.integers(1, 256))
+        n = int(rng.integers(1, 520))
+        k = 32 * int(rng.integers(1, 33))
+        out.append(("mxfp4", m, n, k, 0))
+    for fmt in ("gptq4", "awq4", "q4_0"):
+        for i in range(count):
+            g = int(rng.choice([32, 64, 128]))
+            k = g * int(rng.integers(1, 1024 // g + 1))
+            m = int(rng.integers(256, 520)) if i % 2 else int(rng.integers(1, 256))
+            n = int(rng.integers(1, 66)) * 8 if fmt == "awq4" else int(rng.integers(1, 520))
+            out.append((fmt, m, n, k, g if fmt != "q4_0" else 32))
+    return out
+
+
+@pytest.mark.parametrize("fmt,m,n,k,g", _gemm_cases())
+def test_gemm_random_shapes(fmt, m, n, k, g):
+    ms, ns = np.divmod(np.arange(m * n), n)
+    if fmt == "mxfp4":
+        from test_gpu_gemm import _check_entries, _run
+        inp = workloads.workload(4, n=n, k=k, m=m, seed=m * 131 + n * 7 + k)
+        Ybits = _run(inp, "sweep")
+        _check_entries(inp, Ybits, ms, ns, "gemm mxfp4 m=%d n=%d k=%d" % (m, n, k))
+        return
+    from test_gpu_gemm_int4 import _check, _inputs, _qt, _ref
+    inp = _inputs(m * 131 + n * 7 + k + g, m, n, k, g)
+    w = _qt(fmt, inp, k, n, g)
+    X = dev(inp["X"]).view(torch.bfloat16)
+    say("gemm sweep", fmt, m, n, k, g)
+    Y = qbn.quantized_gemm(w, X)
+    torch.cuda.synchronize()
+    y_ref, s_ref = _ref(fmt, inp, g, ms, ns)
+    _check(Y, y_ref, s_ref, ms, ns, "gemm %s m=%d n=%d k=%d g=%d" % (fmt, m, n, k, g))
