@@ -11,7 +11,7 @@ import torch
 import bit_block_quantized_nibble_amd as qbn
 import oracle
 import workloads
-from gpu_util import DEV, assert_within_tolerance, dev, say, x_dev
+from gpu_util import DEV, assert_within_tolerance, dev, host_bits, say, x_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -116,3 +116,80 @@ def test_gemm_random_shapes(fmt, m, n, k, g):
     torch.cuda.synchronize()
     y_ref, s_ref = _ref(fmt, inp, g, ms, ns)
     _check(Y, y_ref, s_ref, ms, ns, "gemm %s m=%d n=%d k=%d g=%d" % (fmt, m, n, k, g))
+
+
+# ------------------------------------------------------------------ dequant and repack
+def _dequant_cases(per_format=5, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for fmt, (blk, kmax) in FORMATS.items():
+        for _ in range(per_format):
+            if fmt in ("gptq4", "awq4"):
+                g = int(rng.choice([8, 32, 64, 128])) if fmt == "gptq4" else int(rng.choice([32, 64, 128]))
+                k = g * int(rng.integers(1, 512 // g + 1))
+                n = 8 * int(rng.integers(1, 80)) if fmt == "awq4" else int(rng.integers(1, 600))
+                out.append((fmt, n, k, g))
+            else:
+                out.append((fmt, int(rng.integers(1, 300)), blk * int(rng.integers(1, min(kmax, 4096 // blk) + 1)), 0))
+    return out
+
+
+@pytest.mark.parametrize("fmt,n,k,g", _dequant_cases())
+def test_dequant_random_shapes(fmt, n, k, g):
+    """Bit-exact dequantization, every output dtype and layout."""
+    from test_gpu_dequant import _check_all
+    rng = np.random.default_rng(n * 131 + k + g)
+    if fmt in ("gptq4", "awq4"):
+        q = rng.integers(0, 16, (k, n)).astype(np.uint8)
+        scales = rng.uniform(-0.02, 0.02, (k // g, n)).astype(np.float16)
+        zeros = rng.integers(0, 16, (k // g, n)).astype(np.uint8)
+        data = oracle.gptq_pack(q) if fmt == "gptq4" else oracle.awq_pack(q)
+        w = qbn.QTensor(fmt, n, k, dev(data), dev(scales.view(np.uint16)), dev(zeros), group=g)
+        ref = np.ascontiguousarray(oracle.affine_dequant(q, scales.view(np.uint16), zeros, g).T)
+    else:
+        if fmt == "q4_0":
+            data, scales, scale2, ofmt = workloads.q4_0_blocks(rng, n, k), None, 1.0, oracle.Q4_0
+        elif fmt == "nvfp4_cke":
+            data, scales, scale2, ofmt = workloads.cke_blocks(rng, n, k), None, 0.01, oracle.NVFP4_CKE
+        else:
+            inp = workloads.workload({"mxfp4": 1, "nvfp4": 2, "q4_k": 3}[fmt], n=n, k=k, seed=int(rng.integers(1 << 30)))
+            data, scales, scale2 = inp["data"], inp["scales"], inp["scale2"]
+            ofmt = {"mxfp4": oracle.MXFP4, "nvfp4": oracle.NVFP4, "q4_k": oracle.Q4_K}[fmt]
+        w = qbn.QTensor(fmt, n, k, dev(data), None if scales is None else dev(scales), scale2=scale2)
+        ref = oracle.dequant_rows(ofmt, data, scales, scale2, k, range(n))
+    _check_all(w, ref, "sweep %s %dx%d g%d" % (fmt, n, k, g))
+
+
+def _repack_cases(count=4, seed=99):
+    from test_gpu_repack import DIRS
+    rng = np.random.default_rng(seed)
+    out = []
+    for src, dst in DIRS:
+        for _ in range(count):
+            g = int(rng.choice([32, 64, 128, 256]))
+            K = g * int(rng.integers(1, 2048 // g + 1))
+            N = 8 * int(rng.integers(1, 100)) if "awq4" in (src, dst) else int(rng.integers(1, 600))
+            out.append((src, dst, K, N, g))
+    return out
+
+
+@pytest.mark.parametrize("src,dst,K,N,g", _repack_cases())
+def test_repack_random_shapes(src, dst, K, N, g):
+    """Bit-exact repacks in all six directions; the Q4_0 directions with
+    every zero point 8 (the only one Q4_0 holds), so none is refused."""
+    from test_gpu_repack import _expect, _mk
+    rng = np.random.default_rng(K * 7 + N + g)
+    q = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    scales = rng.uniform(-0.01, 0.01, (K // g, N)).astype(np.float16).view(np.uint16)
+    zeros = rng.integers(0, 16, (K // g, N)).astype(np.uint8)
+    if "q4_0" in (src, dst):
+        zeros[:] = 8
+    w = _mk(src, q, scales, zeros, g)
+    say("repack sweep", src, "->", dst, K, N, g)
+    out = qbn.repack(w, dst, dst_group=g if dst != "q4_0" else None)
+    torch.cuda.synchronize()
+    want = _expect(dst, q, scales, g)
+    assert np.array_equal(host_bits(out.data).reshape(want.shape).view(np.uint8), want.view(np.uint8))
+    if dst != "q4_0":
+        assert np.array_equal(host_bits(out.scales).view(np.uint16).reshape(scales.shape), scales)
+        assert np.array_equal(host_bits(out.zeros).reshape(zeros.shape), zeros)
