@@ -193,3 +193,70 @@ def test_repack_random_shapes(src, dst, K, N, g):
     if dst != "q4_0":
         assert np.array_equal(host_bits(out.scales).view(np.uint16).reshape(scales.shape), scales)
         assert np.array_equal(host_bits(out.zeros).reshape(zeros.shape), zeros)
+
+
+# ------------------------------------------------------------------ quantizers and the W4A4 / W4A8 routes
+def _mx_cases(count=10, seed=777):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        m = int(rng.integers(256, 520)) if i % 2 else int(rng.integers(1, 256))
+        n = int(rng.integers(1, 520)) if i % 3 else int(rng.integers(256, 520))
+        k = 32 * int(rng.integers(1, 65))
+        out.append((m, n, k))
+    return out
+
+
+@pytest.mark.parametrize("m,n,k", _mx_cases())
+def test_gemm_mx_random_shapes(m, n, k):
+    """MXFP4 x MXFP4 on the block-scaled matrix cores, every entry, float32
+    and bf16 outputs."""
+    from test_gpu_mx import _check, _inputs
+    rng = np.random.default_rng(m * 17 + n * 3 + k)
+    xc, xs, wc, ws = _inputs(rng, m, n, k)
+    ms, ns = np.divmod(np.arange(m * n), n)
+    _check(wc, ws, xc, xs, m, n, k, ms, ns, "sweep %dx%dx%d" % (m, n, k))
+
+
+def _q8_cases(count=8, seed=555):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 400)), 256 * int(rng.integers(1, 57)), "bf16" if i % 2 else "f32")
+            for i in range(count)]
+
+
+@pytest.mark.parametrize("n,k,xdt", _q8_cases())
+def test_quantize_q8_and_w4a8_gemv_random_shapes(n, k, xdt):
+    """Q8_K activation quantization bit for bit, then the Q4_K x Q8_K GEMV
+    within tolerance of the oracle on the oracle's own codes."""
+    from test_gpu_w4a8 import _check_quantize
+    rng = np.random.default_rng(n * 13 + k)
+    x = _x(rng, k, xdt)
+    q, d, bs = _check_quantize(x, "sweep k=%d %s" % (k, xdt))
+    inp = workloads.workload(3, n=n, k=k, seed=int(rng.integers(1 << 30)))
+    w = qbn.QTensor("q4_k", n, k, dev(inp["data"]), None)
+    say("gemv_q8 sweep", n, k, xdt)
+    y = qbn.quantized_gemv_q8(w, dev(q), dev(d), dev(bs))
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.q4k_w4a8_rows(inp["data"], k, q, d, range(n))
+    assert_within_tolerance(y.cpu().numpy(), y_ref, s_ref, "w4a8 sweep n=%d k=%d" % (n, k))
+
+
+def _encode_cases(count=8, seed=333):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 300)), 16 * int(rng.integers(1, 300)), "bf16" if i % 2 else "f32", i % 2,
+             float(np.float32(rng.choice([1.0, 0.01, 2.0 ** -10])))) for i in range(count)]
+
+
+@pytest.mark.parametrize("m,k,xdt,tie,scale2", _encode_cases())
+def test_quantize_nvfp4_random_shapes(m, k, xdt, tie, scale2):
+    """NVFP4 encode bit for bit (codes and E4M3FN scale bytes), both tie rules."""
+    from test_gpu_encode import _x as enc_x
+    rng = np.random.default_rng(m * 5 + k + tie)
+    X32 = enc_x(rng, m, k)
+    X = X32 if xdt == "f32" else workloads.bf16_bits_from_f32(X32)
+    say("quantize_nvfp4 sweep", m, k, xdt, tie, scale2)
+    codes, scales = qbn.quantize_nvfp4(x_dev(X), scale2, tie)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.nvfp4_quantize(X, scale2, tie)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
