@@ -148,6 +148,21 @@ WORKLOADS = {
         cfg=5, kind="dequant", unit="GB/s",
         desc="bulk dequant GPTQ (fp16 scales, u8 zeros, group 128) -> bf16 [K][N], K x N = 4096 x 11008",
         bytes=22544384 + 704512 + 352256 + 90177536),
+    "int4_sym_encode": dict(
+        cfg=10, kind="int4sym", unit="GB/s", dtype="f32",
+        desc="signed INT4 symmetric encode of a bf16 11008x4096 weight, group 128 (s = amax / 7, q = clip(RNE(w/s), "
+             "-8, 7)): read bf16, write two's-complement nibbles and binary32 scales",
+        bytes=11008 * 4096 * 2 + 11008 * 2048 + 11008 * 32 * 4),
+    "pack3_encode": dict(
+        cfg=11, kind="pack", unit="GB/s", dtype="u8",
+        desc="3-bit packing of 33,554,432 values (u8 in, one little-endian stream of 32-bit words out, fields "
+             "straddling words)",
+        bytes=33554432 + 33554432 * 3 // 8),
+    "gptq_act_order": dict(
+        cfg=12, kind="actorder", unit="GB/s", dtype="i32",
+        desc="GPTQ act-order resolution, K x N = 4096 x 11008, group 128: rows ordered by group from g_idx, "
+             "the packed int32 qweight permuted alike (two kernels: placement, then the row permute)",
+        bytes=2 * 22544384 + 4096 * 4 + 4096 * 4 + 4),
 }
 
 
@@ -333,6 +348,45 @@ def build_steps(name, spec, dev):
             w = qbn.QTensor("mxfp4", n, k, d0.clone(), s0.clone())
             calls.append(qbn.prepare_gemm(w, X, Y))
         return calls, R, inp, None
+    if spec["kind"] in ("int4sym", "pack", "actorder"):
+        lib = qbn._load()
+        if spec["kind"] == "int4sym":
+            m, k, g = inp["m"], inp["k"], inp["group"]
+            W0 = host_to_device(inp["W"], dev).view(torch.bfloat16)
+            R = max(1, math.ceil(ROTATE_BYTES / (m * k * 2)))
+            codes = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+            scales = torch.empty((m, k // g), dtype=torch.float32, device=dev)
+            for _ in range(R):
+                W = W0.clone()
+                calls.append(qbn.Prepared(lib.qbn_quantize_int4_sym,
+                                          (qbn._ptr(W, "w"), qbn._DTYPES[torch.bfloat16], m, k, k, g,
+                                           qbn._ptr(codes, "codes"), qbn._ptr(scales, "scales")),
+                                          "qbn_quantize_int4_sym", dev, (W, codes, scales)))
+        elif spec["kind"] == "pack":
+            count, bits = inp["count"], inp["bits"]
+            V0 = host_to_device(inp["values"], dev)
+            R = max(1, math.ceil(ROTATE_BYTES / count))
+            words = torch.empty((count * bits + 31) // 32, dtype=torch.int32, device=dev)
+            for _ in range(R):
+                V = V0.clone()
+                calls.append(qbn.Prepared(lib.qbn_pack_bits,
+                                          (qbn._ptr(V, "values"), count, bits, 0, qbn._ptr(words, "words"), None),
+                                          "qbn_pack_bits", dev, (V, words)))
+        else:
+            K, N, g = inp["K"], inp["N"], inp["group"]
+            Q0 = host_to_device(inp["qweight"], dev)
+            gi = host_to_device(inp["g_idx"], dev)
+            R = max(1, math.ceil(ROTATE_BYTES / (2 * Q0.numel() * 4)))
+            out = torch.empty_like(Q0)
+            perm = torch.empty(K, dtype=torch.int32, device=dev)
+            status = torch.empty(1, dtype=torch.int32, device=dev)
+            for _ in range(R):
+                Q = Q0.clone()
+                calls.append(qbn.Prepared(lib.qbn_gptq_resolve_g_idx,
+                                          (qbn._ptr(Q, "qweight"), qbn._ptr(gi, "g_idx"), K, N, g, qbn._ptr(out, "out"),
+                                           qbn._ptr(perm, "perm"), qbn._ptr(status, "status")),
+                                          "qbn_gptq_resolve_g_idx", dev, (Q, gi, out, perm, status)))
+        return calls, R, inp, None
     # cfg 5: repack / dequant from GPTQ (or from AWQ made by the library
     # itself). Q4_0 holds no zero point: its leg takes every zero point as 8.
     K, N, g = inp["K"], inp["N"], inp["group"]
@@ -435,6 +489,35 @@ def oracle_unit(name, spec, inp):
                                      np.tile(nn, M))
             return 2.0 * K * M * 2
         return f, "2 whole columns of the %dx%d output per call (2k flops per entry)" % (M, N)
+    if kind == "int4sym":
+        m, g = inp["m"], inp["group"]
+        rows = max(1, m // 64)
+
+        def f(rng):
+            r0 = int(rng.integers(0, m - rows + 1))
+            oracle.int4_sym_quantize(np.ascontiguousarray(inp["W"][r0:r0 + rows]), g)
+            return total * rows / m
+        return f, "slices of %d of the %d rows" % (rows, m)
+    if kind == "pack":
+        count, bits = inp["count"], inp["bits"]
+        span = count // 64
+
+        def f(rng):
+            i0 = 32 * int(rng.integers(0, (count - span) // 32 + 1))
+            oracle.pack_bits(inp["values"][i0:i0 + span], bits)
+            return total * span / count
+        return f, "slices of %d of the %d values" % (span, count)
+    if kind == "actorder":
+        K, N, g = inp["K"], inp["N"], inp["group"]
+        cols = max(1, N // 64)
+
+        def f(rng):
+            c0 = int(rng.integers(0, N - cols + 1))
+            _, perm = oracle.resolve_g_idx(inp["g_idx"], g)
+            q = oracle.gptq_unpack(np.ascontiguousarray(inp["qweight"][:, c0:c0 + cols]))
+            oracle.gptq_pack(np.ascontiguousarray(q[perm]))
+            return total * cols / N
+        return f, "the row order for all of K and the permuted rows of a slice of %d of the %d columns" % (cols, N)
     # repack / dequant through the oracle's logical matrix, on a slice of the
     # K x N matrix (whole groups, whole 8-column words)
     K, N, g = inp["K"], inp["N"], inp["group"]
@@ -660,7 +743,10 @@ def measure(name, steps, warmup, dev):
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=recorded_traffic(name))
         metric = "quantized GEMV GB/s (% HBM peak)" if spec["kind"] in ("gemv", "w4a8", "a16q8", "int4gemv") else \
-            "NVFP4 encode GB/s (% HBM peak)" if spec["kind"] == "encode" else (
+            "NVFP4 encode GB/s (% HBM peak)" if spec["kind"] == "encode" else \
+            "INT4 encode GB/s (% HBM peak)" if spec["kind"] == "int4sym" else \
+            "b-bit packing GB/s (% HBM peak)" if spec["kind"] == "pack" else \
+            "act-order resolution GB/s (% HBM peak)" if spec["kind"] == "actorder" else (
             "int4 repack GB/s (% HBM peak)" if spec["kind"] == "repack" else "bulk dequant GB/s (% HBM peak)")
     config = {
         "workload": spec["desc"],

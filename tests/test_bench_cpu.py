@@ -64,6 +64,12 @@ def _small_inputs(spec):
         inp = workloads.workload(5, n=64, k=256)
     elif cfg == 7:
         inp = workloads.workload(7, n=64, k=256)
+    elif cfg == 10:
+        inp = workloads.workload(10, n=64, k=256)
+    elif cfg == 11:
+        inp = workloads.workload(11, n=4096)
+    elif cfg == 12:
+        inp = workloads.workload(12, n=64, k=256)
     else:
         inp = workloads.workload(9, n=64, k=256, m=8)
     if spec["kind"] == "encode":  # the bench dequantizes the weights on the device; here the oracle does

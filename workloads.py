@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the nine workloads (host numpy arrays).
+"""Seeded synthetic inputs for the twelve workloads (host numpy arrays).
 
 This module holds no decoding, dot-product or repacking arithmetic: it only
 draws random bytes and numbers with the distributions below and lays them
@@ -46,6 +46,12 @@ Workloads (n = output rows, k = reduction length):
      weights drawn exactly as workload 7 (GPTQ, AWQ, scales, zero points,
      Q4_0 blocks, in that order, then workload 7's x, unused), then X bf16
      N(0,1) [M][K].
+ 10  INT4 symmetric encode, W bf16 N(0,1) [m][k] = [11008][4096], group 128.
+ 11  3-bit packing: values U{0..7} u8 [33554432].
+ 12  GPTQ act-order resolution, K x N = 4096 x 11008, group 128: qweight
+     uniform u32 [K/8][N]; g_idx int32 [K] = (a uniform permutation of
+     0..K-1) // 128, so every group holds exactly 128 rows, scattered as
+     desc_act orders them.
 """
 from __future__ import annotations
 
@@ -63,6 +69,9 @@ SHAPES = {
     7: dict(fmt="int4", K=4096, N=11008, group=128),
     8: dict(fmt="nvfp4_cke", n=4096, k=4096),
     9: dict(fmt="int4", K=4096, N=11008, group=128, M=2048),
+    10: dict(fmt="int4_sym", m=11008, k=4096, group=128),
+    11: dict(fmt="pack", count=33554432, bits=3),
+    12: dict(fmt="gptq4", K=4096, N=11008, group=128),
 }
 
 
@@ -162,7 +171,7 @@ def x_bf16(rng, k: int):
 
 def workload(c: int, seed: int | None = None, n: int | None = None, k: int | None = None,
              m: int | None = None) -> dict:
-    """Inputs of workload c (1..9). n / k / m override the shape (same
+    """Inputs of workload c (1..12). n / k / m override the shape (same
     distributions) so that tests can run the same recipe at small sizes."""
     seed = 1000 + c if seed is None else seed
     rng = _rng(seed)
@@ -219,4 +228,20 @@ def workload(c: int, seed: int | None = None, n: int | None = None, k: int | Non
         blocks = cke_blocks(rng, n, k)
         return dict(fmt="nvfp4_cke", n=n, k=k, data=blocks, scales=None, scale2=float(SCALE2_NVFP4),
                     x=x_bf16(rng, k), seed=seed)
-    raise ValueError("workload must be 1..9")
+    if c == 10:
+        m = n or sh["m"]
+        k = k or sh["k"]
+        W = bf16_bits_from_f32(rng.standard_normal((m, k)).astype(np.float32))
+        return dict(fmt="int4_sym", m=m, k=k, group=sh["group"], W=W, seed=seed)
+    if c == 11:
+        count = n or sh["count"]
+        values = rng.integers(0, 1 << sh["bits"], size=count).astype(np.uint8)
+        return dict(fmt="pack", count=count, bits=sh["bits"], values=values, seed=seed)
+    if c == 12:
+        K = k or sh["K"]
+        N = n or sh["N"]
+        g = sh["group"]
+        qweight = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
+        g_idx = (rng.permutation(K) // g).astype(np.int32)
+        return dict(fmt="gptq4", K=K, N=N, group=g, qweight=qweight, g_idx=g_idx, seed=seed)
+    raise ValueError("workload must be 1..12")
