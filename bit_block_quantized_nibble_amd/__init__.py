@@ -148,6 +148,17 @@ def _ptr(t: Optional[torch.Tensor], name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _ptr_rows(t: torch.Tensor, name: str):
+    """Pointer to a 2-D matrix whose rows are contiguous but may sit inside a
+    wider one (row stride >= columns, passed to the library as its leading
+    dimension)."""
+    if not t.is_cuda:
+        raise ValueError("%s must be a device (cuda) tensor" % name)
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1) or (t.shape[0] > 1 and t.stride(0) < t.shape[1]):
+        raise ValueError("%s must be 2-D with contiguous rows" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def _need(t: Optional[torch.Tensor], nbytes: int, name: str):
     """Refuse, before any launch, a tensor that holds fewer bytes than the
     call will read or write through its pointer."""
@@ -285,13 +296,12 @@ def quantize_nvfp4(x: torch.Tensor, scale2: float, tie: int = 0):
     """NVFP4 encode of x [m][k] (float32 or bfloat16): (codes uint8 [m][k/2],
     E4M3FN scale bytes uint8 [m][k/16]); tie 0 ties-to-even, 1 lowest code."""
     lib = _load()
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be 2-D with contiguous rows")
-    m, k = x.shape
+    m, k = x.shape if x.dim() == 2 else (0, 0)
+    xp = _ptr_rows(x, "x")
     codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((m, k // 16), dtype=torch.uint8, device=x.device)
     ldx = x.stride(0) if m > 1 else k
-    _check(lib.qbn_quantize_nvfp4(_ptr(x, "x"), _DTYPES.get(x.dtype, -1), m, k, ldx, float(scale2), int(tie),
+    _check(lib.qbn_quantize_nvfp4(xp, _DTYPES.get(x.dtype, -1), m, k, ldx, float(scale2), int(tie),
                                   _ptr(codes, "codes"), _ptr(scales, "scales"), _stream(x.device)),
            "qbn_quantize_nvfp4")
     return codes, scales
@@ -301,13 +311,12 @@ def quantize_int4_sym(w: torch.Tensor, group: int):
     """Signed INT4 symmetric encode of w [m][k]: (codes uint8 [m][k/2],
     scales float32 [m][k/group])."""
     lib = _load()
-    if w.dim() != 2 or w.stride(1) != 1:
-        raise ValueError("w must be 2-D with contiguous rows")
-    m, k = w.shape
+    m, k = w.shape if w.dim() == 2 else (0, 0)
+    wp = _ptr_rows(w, "w")
     codes = torch.empty((m, k // 2), dtype=torch.uint8, device=w.device)
     scales = torch.empty((m, k // group), dtype=torch.float32, device=w.device)
     ldw = w.stride(0) if m > 1 else k
-    _check(lib.qbn_quantize_int4_sym(_ptr(w, "w"), _DTYPES.get(w.dtype, -1), m, k, ldw, int(group),
+    _check(lib.qbn_quantize_int4_sym(wp, _DTYPES.get(w.dtype, -1), m, k, ldw, int(group),
                                      _ptr(codes, "codes"), _ptr(scales, "scales"), _stream(w.device)),
            "qbn_quantize_int4_sym")
     return codes, scales

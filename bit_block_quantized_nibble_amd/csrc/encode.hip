@@ -111,22 +111,98 @@ __global__ __launch_bounds__(256) void k_quantize_int4_sym(const XT *__restrict_
     }
 }
 
-// One thread per output word: the bits [32 w, 32 w + 32) of the stream of
-// `width`-bit fields ((src[i] >> shift) & mask at bits i * width).
-__global__ __launch_bounds__(256) void k_pack_bits(const uint8_t *__restrict__ src, int64_t count, int shift,
-                                                   int width, uint32_t *__restrict__ words, int64_t nwords) {
-    const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (w >= nwords) return;
-    const uint32_t mask = (1u << width) - 1u;
-    const int64_t b0 = 32 * w;
-    const int64_t i0 = b0 / width, i1 = min(count - 1, (b0 + 31) / width);
-    uint32_t acc = 0;
-    for (int64_t i = i0; i <= i1; ++i) {
-        const uint32_t v = ((uint32_t)src[i] >> shift) & mask;
-        const int64_t pos = i * width - b0;  // may be negative: the field started in the previous word
-        acc |= pos >= 0 ? (v << pos) : (v >> (-pos));
+// L = group / 8 consecutive lanes per group (L a power of two <= 64, so a
+// group never straddles a wave), eight consecutive elements per lane: the
+// lanes load 16- or 32-byte pieces of the row side by side, take the group's
+// amax with xor shuffles inside the L-lane segment (max is exact, so the
+// order does not matter), and each stores the 32-bit word of its eight
+// nibbles. Same arithmetic per element as the one-thread-per-group kernel.
+template <typename XT, int L>
+__global__ __launch_bounds__(256) void k_quantize_int4_sym_lanes(const XT *__restrict__ w, int64_t m, int64_t k,
+                                                                 int64_t ldw, uint8_t *__restrict__ codes,
+                                                                 float *__restrict__ scales) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_row = k / 8;
+    if (t >= m * per_row) return;  // whole groups leave together: m * per_row is a multiple of L
+    const int64_t row = t / per_row, c = t - row * per_row;
+    const XT *p = w + row * ldw + 8 * c;
+    float v[8];
+    if constexpr (sizeof(XT) == 2) {
+        const u32x4 q = ld16(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __builtin_bit_cast(float, q[j] << 16);
+            v[2 * j + 1] = __builtin_bit_cast(float, q[j] & 0xFFFF0000u);
+        }
+    } else {
+        const u32x4 a = ld16(p), b = ld16(p + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // through plain words: a bit cast taken of a vector element
+            // itself reads element 0 whatever the index
+            const uint32_t wa = a[j], wb = b[j];
+            v[j] = __builtin_bit_cast(float, wa);
+            v[4 + j] = __builtin_bit_cast(float, wb);
+        }
     }
-    words[w] = acc;
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+#pragma unroll
+    for (int o = 1; o < L; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float s = amax / 7.0f;
+    if ((c & (L - 1)) == 0) scales[t / L] = s;  // group index = row * (k / group) + c / L = t / L
+    uint32_t word = 0;
+    if (s != 0.0f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float r = __builtin_rintf(v[j] / s);
+            word |= ((uint32_t)(int)__builtin_fminf(__builtin_fmaxf(r, -8.0f), 7.0f) & 15u) << (4 * j);
+        }
+    }
+    *reinterpret_cast<uint32_t *>(codes + row * (k / 2) + 4 * c) = word;
+}
+
+// One thread per 32 values, whose W-bit fields (shift..shift + W - 1 of each
+// byte; shift + W <= 8) fill exactly the W whole words W t .. W t + W - 1 of
+// the stream, so threads share no word. Values past `count` count as 0 (the
+// unused high bits of the last word). VEC: the 32 bytes are read as two
+// 16-byte loads (base 16-byte aligned, all 32 in range).
+template <int W, bool VEC>
+__global__ __launch_bounds__(256) void k_pack_bits(const uint8_t *__restrict__ src, int64_t count, int shift,
+                                                   uint32_t *__restrict__ words, int64_t nwords) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i0 = 32 * t;
+    if (i0 >= count) return;
+    uint32_t b[8];
+    if (VEC && i0 + 32 <= count) {
+        const u32x4 lo = ld16(src + i0), hi = ld16(src + i0 + 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            b[j] = lo[j];
+            b[4 + j] = hi[j];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = 0u;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            if (i0 + i < count) b[i / 4] |= (uint32_t)src[i0 + i] << (8 * (i % 4));
+    }
+    constexpr uint32_t mask = (1u << W) - 1u;
+    uint32_t out[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) out[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const uint32_t v = (b[i / 4] >> (8 * (i % 4) + shift)) & mask;
+        const int pos = i * W, wd = pos / 32, off = pos % 32;
+        out[wd] |= v << off;
+        if (off + W > 32) out[wd + 1] |= v >> (32 - off);
+    }
+#pragma unroll
+    for (int j = 0; j < W; ++j)
+        if (W * t + j < nwords) words[W * t + j] = out[j];
 }
 
 // One thread per element: the lo-bit field of stream a and, when hi_width >
@@ -147,6 +223,50 @@ __global__ __launch_bounds__(256) void k_unpack_bits(const uint32_t *__restrict_
     uint32_t v = field(a, i, lo_width);
     if (hi_width > 0) v |= field(b, i, hi_width) << lo_width;
     dst[i] = (uint8_t)v;
+}
+
+template <typename XT>
+hipError_t launch_int4_sym_lanes(int64_t lanes, dim3 g, hipStream_t s, const XT *w, int64_t m, int64_t k,
+                                 int64_t ldw, uint8_t *codes, float *scales) {
+#define QBN_I4L(L) hipLaunchKernelGGL((k_quantize_int4_sym_lanes<XT, L>), g, dim3(256), 0, s, w, m, k, ldw, codes, scales)
+    switch (lanes) {
+        case 1: QBN_I4L(1); break;
+        case 2: QBN_I4L(2); break;
+        case 4: QBN_I4L(4); break;
+        case 8: QBN_I4L(8); break;
+        case 16: QBN_I4L(16); break;
+        case 32: QBN_I4L(32); break;
+        default: QBN_I4L(64); break;
+    }
+#undef QBN_I4L
+    return hipGetLastError();
+}
+
+template <bool VEC>
+void launch_pack_width(int width, dim3 g, hipStream_t s, const uint8_t *src, int64_t count, int shift,
+                       uint32_t *words, int64_t nwords) {
+#define QBN_PK(W) hipLaunchKernelGGL((k_pack_bits<W, VEC>), g, dim3(256), 0, s, src, count, shift, words, nwords)
+    switch (width) {
+        case 1: QBN_PK(1); break;
+        case 2: QBN_PK(2); break;
+        case 3: QBN_PK(3); break;
+        case 4: QBN_PK(4); break;
+        case 5: QBN_PK(5); break;
+        case 6: QBN_PK(6); break;
+        case 7: QBN_PK(7); break;
+        default: QBN_PK(8); break;
+    }
+#undef QBN_PK
+}
+
+hipError_t pack_stream(const uint8_t *src, int64_t count, int shift, int width, uint32_t *words, hipStream_t s) {
+    const int64_t nwords = (count * width + 31) / 32;
+    const dim3 g((unsigned)(((count + 31) / 32 + 255) / 256));
+    if (reinterpret_cast<uintptr_t>(src) % 16 == 0)
+        launch_pack_width<true>(width, g, s, src, count, shift, words, nwords);
+    else
+        launch_pack_width<false>(width, g, s, src, count, shift, words, nwords);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -177,6 +297,17 @@ hipError_t launch_quantize_nvfp4(const void *x, int x_dtype, int64_t m, int64_t 
 hipError_t launch_quantize_int4_sym(const void *w, int w_dtype, int64_t m, int64_t k, int64_t ldw, int64_t group,
                                     void *codes, float *scales, hipStream_t s) {
     const int64_t groups = m * (k / group);
+    const int64_t lanes = group / 8;
+    const int eb = w_dtype == QBN_BF16 ? 2 : 4;
+    // the lane kernel: group = 8 L with L a power of two <= 64, 16-byte rows
+    // and base (vector loads), 4-byte code rows (k % 8 == 0 follows)
+    if (group % 8 == 0 && lanes <= 64 && (lanes & (lanes - 1)) == 0 && (ldw * eb) % 16 == 0 &&
+        reinterpret_cast<uintptr_t>(w) % 16 == 0 && reinterpret_cast<uintptr_t>(codes) % 4 == 0) {
+        const dim3 g((unsigned)((m * (k / 8) + 255) / 256));
+        if (w_dtype == QBN_BF16)
+            return launch_int4_sym_lanes<__bf16>(lanes, g, s, (const __bf16 *)w, m, k, ldw, (uint8_t *)codes, scales);
+        return launch_int4_sym_lanes<float>(lanes, g, s, (const float *)w, m, k, ldw, (uint8_t *)codes, scales);
+    }
     const dim3 grid((unsigned)((groups + 255) / 256));
     if (w_dtype == QBN_BF16)
         hipLaunchKernelGGL(k_quantize_int4_sym<__bf16>, grid, dim3(256), 0, s, (const __bf16 *)w, m, k, ldw, group,
@@ -189,16 +320,10 @@ hipError_t launch_quantize_int4_sym(const void *w, int w_dtype, int64_t m, int64
 
 hipError_t launch_pack_bits(const void *values, int64_t count, int bits, int lo, void *words_lo, void *words_hi,
                             hipStream_t s) {
-    const int w0 = lo > 0 ? lo : bits;
-    const int64_t n0 = (count * w0 + 31) / 32;
-    hipLaunchKernelGGL(k_pack_bits, dim3((unsigned)((n0 + 255) / 256)), dim3(256), 0, s, (const uint8_t *)values,
-                       count, 0, w0, (uint32_t *)words_lo, n0);
-    hipError_t e = hipGetLastError();
+    const uint8_t *v = (const uint8_t *)values;
+    hipError_t e = pack_stream(v, count, 0, lo > 0 ? lo : bits, (uint32_t *)words_lo, s);
     if (e != hipSuccess || lo == 0) return e;
-    const int64_t n1 = (count * (bits - lo) + 31) / 32;
-    hipLaunchKernelGGL(k_pack_bits, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, (const uint8_t *)values,
-                       count, lo, bits - lo, (uint32_t *)words_hi, n1);
-    return hipGetLastError();
+    return pack_stream(v, count, lo, bits - lo, (uint32_t *)words_hi, s);
 }
 
 hipError_t launch_unpack_bits(const void *words_lo, const void *words_hi, int64_t count, int bits, int lo,

@@ -43,26 +43,54 @@ __global__ __launch_bounds__(256) void k_qzeros(const void *__restrict__ src, vo
     }
 }
 
-// One workgroup. Counts the rows of each group (LDS), checks every group
-// holds exactly `group` rows, then places rows chunk by chunk: a row's slot
-// is its group's base, plus the rows of that group in earlier chunks, plus
-// those before it in its chunk. On a bad g_idx it writes the identity (so
-// that the row permutation that follows stays in bounds) and status -1 (a
-// value outside 0..G-1) or -2 (a group of the wrong size); else status 0.
-constexpr int kMaxGroups = 8192;
+// Lanes of one wave whose group index equals this lane's: one ballot per bit
+// of the index (nbits covers 0..G-1), starting from the lanes in range.
+__device__ __forceinline__ uint64_t same_group_lanes(bool in, int g, int nbits) {
+    uint64_t same = __ballot(in);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (g >> b) & 1;
+        const uint64_t v = __ballot(bit);
+        same &= bit ? v : ~v;
+    }
+    return same;
+}
 
-__global__ __launch_bounds__(256) void k_resolve_g_idx(const int32_t *__restrict__ g_idx, int64_t K, int64_t group,
-                                                       int32_t *__restrict__ perm, int32_t *__restrict__ status) {
-    __shared__ int cnt[kMaxGroups];
-    __shared__ int gbuf[256];
+// One workgroup of 1024 threads (16 waves). Counts the rows of each group
+// (LDS), checks every group holds exactly `group` rows, then gives each row
+// its slot: its group's base, plus the rows of its group before it. Each
+// wave owns one contiguous share of the rows (`span`, a multiple of 64) and
+// walks it 64 rows at a time; the lanes holding the same group index find
+// each other with ballots (same_group_lanes), so the rank inside a 64-row
+// piece is a popcount. With G * 16 counters in LDS (G <= kPrefixGroups) the
+// waves count their shares, an exclusive prefix over the waves gives each
+// wave its starting offset per group, and the waves then place their rows
+// independently, reading g_idx from an LDS copy made while counting when K
+// <= kStageRows. Beyond that the waves take turns, one 64-row piece each per
+// turn, on one shared counter per group. Either way each group keeps the
+// original row order. On a bad g_idx it writes the identity (so that the
+// row permutation that follows stays in bounds) and status -1 (a value
+// outside 0..G-1) or -2 (a group of the wrong size); else status 0.
+constexpr int kMaxGroups = 8192;
+constexpr int kPrefixGroups = 512;
+constexpr int kResolveThreads = 1024;
+constexpr int kResolveWaves = kResolveThreads / 64;
+constexpr int kStageRows = 16384;  // g_idx kept in LDS for the placement passes up to this K
+
+__global__ __launch_bounds__(kResolveThreads) void k_resolve_g_idx(const int32_t *__restrict__ g_idx, int64_t K,
+                                                                   int64_t group, int32_t *__restrict__ perm,
+                                                                   int32_t *__restrict__ status) {
+    __shared__ int cnt[kMaxGroups];  // also kResolveWaves x kPrefixGroups per-wave counters
+    __shared__ int staged[kStageRows];
     __shared__ int bad;
     const int t = threadIdx.x;
     const int64_t G = K / group;
-    for (int64_t g = t; g < G; g += 256) cnt[g] = 0;
+    const bool stage = K <= kStageRows;
+    for (int64_t g = t; g < G; g += kResolveThreads) cnt[g] = 0;
     if (t == 0) bad = 0;
     __syncthreads();
-    for (int64_t k = t; k < K; k += 256) {
+    for (int64_t k = t; k < K; k += kResolveThreads) {
         const int g = g_idx[k];
+        if (stage) staged[k] = g;
         if (g < 0 || g >= G)
             atomicOr(&bad, 1);
         else
@@ -70,47 +98,110 @@ __global__ __launch_bounds__(256) void k_resolve_g_idx(const int32_t *__restrict
     }
     __syncthreads();
     if (bad == 0)
-        for (int64_t g = t; g < G; g += 256)
+        for (int64_t g = t; g < G; g += kResolveThreads)
             if (cnt[g] != group) atomicOr(&bad, 2);
     __syncthreads();
     if (bad) {
-        for (int64_t k = t; k < K; k += 256) perm[k] = (int32_t)k;
+        for (int64_t k = t; k < K; k += kResolveThreads) perm[k] = (int32_t)k;
         if (t == 0) status[0] = (bad & 1) ? -1 : -2;
         return;
     }
-    for (int64_t g = t; g < G; g += 256) cnt[g] = 0;
-    __syncthreads();
-    for (int64_t c = 0; c < K; c += 256) {
-        const int64_t k = c + t;
-        const int g = k < K ? g_idx[k] : -1;
-        gbuf[t] = g;
+    const int lane = t & 63, wave = t >> 6;
+    const int nbits = G > 1 ? 32 - __builtin_clz((unsigned)(G - 1)) : 0;
+    const uint64_t below = (1ull << lane) - 1ull, above = ~(below | (1ull << lane));
+    if (G <= kPrefixGroups) {
+        int *cw = cnt + wave * kPrefixGroups;  // this wave's counters
+        const int32_t *gsrc = stage ? staged : g_idx;
+        const int64_t span = ((K + kResolveThreads - 1) / kResolveThreads) * 64;
+        const int64_t k0 = wave * span, k1 = min(K, k0 + span);
         __syncthreads();
-        if (k < K) {
-            int rank = 0;
-            for (int u = 0; u < t; ++u) rank += gbuf[u] == g;
-            perm[(int64_t)g * group + cnt[g] + rank] = (int32_t)k;
+        for (int64_t g = lane; g < G; g += 64) cw[g] = 0;
+        for (int64_t c = k0; c < k1; c += 64) {
+            const int64_t k = c + lane;
+            const bool in = k < k1;
+            const int g = in ? gsrc[k] : 0;
+            const uint64_t same = same_group_lanes(in, g, nbits);
+            if (in && (same & above) == 0) cw[g] += __popcll(same);  // the last lane of its set
         }
         __syncthreads();
-        if (k < K) atomicAdd(&cnt[g], 1);
+        for (int64_t g = t; g < G; g += kResolveThreads) {
+            int run = (int)(g * group);
+            for (int w = 0; w < kResolveWaves; ++w) {
+                const int c = cnt[w * kPrefixGroups + g];
+                cnt[w * kPrefixGroups + g] = run;
+                run += c;
+            }
+        }
         __syncthreads();
+        for (int64_t c = k0; c < k1; c += 64) {
+            const int64_t k = c + lane;
+            const bool in = k < k1;
+            const int g = in ? gsrc[k] : 0;
+            const uint64_t same = same_group_lanes(in, g, nbits);
+            if (in) {
+                const int base = cw[g];
+                perm[base + __popcll(same & below)] = (int32_t)k;
+                if ((same & above) == 0) cw[g] = base + __popcll(same);
+            }
+        }
+    } else {
+        for (int64_t g = t; g < G; g += kResolveThreads) cnt[g] = 0;
+        __syncthreads();
+        for (int64_t c = 0; c < K; c += kResolveThreads) {
+            const int64_t k = c + t;
+            const bool in = k < K;
+            const int g = in ? g_idx[k] : 0;
+            const uint64_t same = same_group_lanes(in, g, nbits);
+            for (int w = 0; w < kResolveWaves; ++w) {
+                if (wave == w && in) {
+                    const int base = cnt[g];
+                    perm[(int64_t)g * group + base + __popcll(same & below)] = (int32_t)k;
+                    if ((same & above) == 0) cnt[g] = base + __popcll(same);
+                }
+                __syncthreads();
+            }
+        }
     }
     if (t == 0) status[0] = 0;
 }
 
-// One thread per output word (r, n): row 8r + j of the result is source row
-// perm[8r + j], whose nibble sits at bits 4 (p % 8) of source word (p / 8, n).
+// One thread per output word (r, n), or per four neighbouring words (r, 4n ..
+// 4n + 3) with 16-byte accesses when V4: row 8r + j of the result is source
+// row p = perm[8r + j], whose nibble sits at bits 4 (p % 8) of source word
+// (p / 8, n). A workgroup covers 256 (or 1024) neighbouring columns of one
+// row r, so the eight source rows it gathers are read in runs of 1 (or 4)
+// KB.
+template <bool V4>
 __global__ __launch_bounds__(256) void k_permute_gptq(const uint32_t *__restrict__ qw, const int32_t *__restrict__ perm,
                                                       int64_t K, int64_t N, uint32_t *__restrict__ out) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= (K / 8) * N) return;
-    const int64_t r = t / N, n = t - r * N;
-    uint32_t w = 0;
+    // tiles of 256 threads: (row r, column tile c), taken column-tile-major
+    // and dealt in contiguous shares to the 8 XCDs (workgroup b runs on XCD
+    // b % 8), so one XCD gathers from one column slab while it lasts in L2
+    constexpr int64_t cols = V4 ? 1024 : 256;
+    const int64_t rows = K / 8, ctiles = (N + cols - 1) / cols, B = rows * ctiles, b = blockIdx.x;
+    const int64_t xcd = b % 8, idx = xcd * (B / 8) + (xcd < B % 8 ? xcd : B % 8) + b / 8;
+    const int64_t r = idx % rows, n = (idx / rows) * cols + (int64_t)threadIdx.x * (V4 ? 4 : 1);
+    if (n >= N) return;
+    if constexpr (V4) {
+        u32x4 w = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int64_t p = perm[8 * r + j];
-        w |= ((qw[(p / 8) * N + n] >> (4 * (p % 8))) & 15u) << (4 * j);
+        for (int j = 0; j < 8; ++j) {
+            const int64_t p = perm[8 * r + j];
+            const u32x4 src = ld16(qw + (p / 8) * N + n);
+            const uint32_t sh = 4 * (uint32_t)(p % 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] |= ((src[i] >> sh) & 15u) << (4 * j);
+        }
+        *reinterpret_cast<u32x4 *>(out + r * N + n) = w;
+    } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t p = perm[8 * r + j];
+            w |= ((qw[(p / 8) * N + n] >> (4 * (p % 8))) & 15u) << (4 * j);
+        }
+        out[r * N + n] = w;
     }
-    out[t] = w;
 }
 
 template <typename T>
@@ -132,12 +223,19 @@ hipError_t launch_gptq_qzeros(const void *src, void *dst, int64_t groups, int64_
 
 hipError_t launch_gptq_resolve_g_idx(const void *qweight, const int32_t *g_idx, int64_t k, int64_t n, int64_t group,
                                      void *qweight_out, int32_t *perm, int32_t *status, hipStream_t s) {
-    hipLaunchKernelGGL(k_resolve_g_idx, dim3(1), dim3(256), 0, s, g_idx, k, group, perm, status);
+    hipLaunchKernelGGL(k_resolve_g_idx, dim3(1), dim3(kResolveThreads), 0, s, g_idx, k, group, perm, status);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || n == 0) return e;
-    const int64_t words = (k / 8) * n;
-    hipLaunchKernelGGL(k_permute_gptq, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
-                       (const uint32_t *)qweight, perm, k, n, (uint32_t *)qweight_out);
+    if (e != hipSuccess || n == 0 || k == 0) return e;
+    const bool v4 = n % 4 == 0 && reinterpret_cast<uintptr_t>(qweight) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(qweight_out) % 16 == 0;
+    const int64_t cols = v4 ? 1024 : 256;
+    const dim3 grid((unsigned)((k / 8) * ((n + cols - 1) / cols)));
+    if (v4)
+        hipLaunchKernelGGL(k_permute_gptq<true>, grid, dim3(256), 0, s, (const uint32_t *)qweight, perm, k, n,
+                           (uint32_t *)qweight_out);
+    else
+        hipLaunchKernelGGL(k_permute_gptq<false>, grid, dim3(256), 0, s, (const uint32_t *)qweight, perm, k, n,
+                           (uint32_t *)qweight_out);
     return hipGetLastError();
 }
 

@@ -107,3 +107,61 @@ def test_pack_bits_planes(bits, lo_bits):
     back = qbn.unpack_bits(lo, hi, count, bits, lo_bits)
     torch.cuda.synchronize()
     assert np.array_equal(back.cpu().numpy(), v)
+
+
+@pytest.mark.parametrize("g", [8, 16, 64, 256, 512, 1024, 24])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_quantize_int4_sym_group_sizes(g, xdt):
+    """Group sizes 8 L for L = 1 .. 64 lanes per group (the lane kernel), and
+    1024 and 24 (one thread per group), each with a zero group."""
+    m, k = 9, 3072
+    rng = np.random.default_rng(g * 5 + len(xdt))
+    W32 = (rng.standard_normal((m, k)) * 10.0 ** rng.uniform(-3, 3, (m, 1))).astype(np.float32)
+    W32[4, g:2 * g] = 0.0
+    W = W32 if xdt == "f32" else workloads.bf16_bits_from_f32(W32)
+    say("quantize_int4_sym group", g, xdt)
+    codes, scales = qbn.quantize_int4_sym(x_dev(W), g)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.int4_sym_quantize(W, g)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(host_bits(scales).reshape(s_ref.shape), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("pad,off", [(8, 0), (3, 0), (8, 1)])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_quantize_int4_sym_strided_rows(pad, off, xdt):
+    """Rows inside a wider matrix: a 16-byte row stride and base (pad 8, no
+    offset) keep the lane kernel; an odd stride or a base one element in
+    takes the one-thread-per-group kernel. Both bit-exact."""
+    m, k, g = 6, 512, 32
+    rng = np.random.default_rng(pad * 3 + off + len(xdt))
+    W32 = rng.standard_normal((m, k + pad)).astype(np.float32)
+    W = W32 if xdt == "f32" else workloads.bf16_bits_from_f32(W32)
+    Wd = x_dev(W)[:, off:off + k]
+    say("quantize_int4_sym strided", pad, off, xdt)
+    codes, scales = qbn.quantize_int4_sym(Wd, g)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.int4_sym_quantize(np.ascontiguousarray(W[:, off:off + k]), g)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(host_bits(scales).reshape(s_ref.shape), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits,lo_bits", [(3, 0), (5, 0), (8, 0), (6, 4)])
+@pytest.mark.parametrize("count", [33, 1000, 100003])
+def test_pack_bits_unaligned_values(bits, lo_bits, count):
+    """Values starting one byte past a 16-byte boundary (byte loads) against
+    the same values aligned (16-byte loads): both equal the oracle."""
+    rng = np.random.default_rng(bits * 13 + count + lo_bits)
+    v = rng.integers(0, 1 << bits, count).astype(np.uint8)
+    buf = torch.zeros(count + 1, dtype=torch.uint8, device=DEV)
+    buf[1:] = dev(v)
+    say("pack_bits unaligned", bits, lo_bits, count)
+    lo, hi = qbn.pack_bits(buf[1:], bits, lo_bits)
+    lo_a, hi_a = qbn.pack_bits(dev(v), bits, lo_bits)
+    torch.cuda.synchronize()
+    if lo_bits:
+        lo_ref, hi_ref = oracle.pack_planes(v.astype(np.uint32), bits, lo_bits)
+        assert np.array_equal(host_bits(hi), hi_ref) and np.array_equal(host_bits(hi_a), hi_ref)
+    else:
+        lo_ref = oracle.pack_bits(v.astype(np.uint32), bits)
+    assert np.array_equal(host_bits(lo), lo_ref) and np.array_equal(host_bits(lo_a), lo_ref)

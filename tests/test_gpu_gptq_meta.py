@@ -35,12 +35,34 @@ def _act_order(rng, K, g):
     return rng.permutation(np.arange(K) // g).astype(np.int32)
 
 
-@pytest.mark.parametrize("K,N,g", [(256, 64, 32), (4096, 11008, 128), (1024, 40, 8), (128, 8, 128)])
+@pytest.mark.parametrize("K,N,g", [(256, 64, 32), (4096, 11008, 128), (1024, 40, 8), (128, 8, 128),
+                                   (1160, 300, 8), (65536, 8, 8), (2048, 256, 2048), (28672, 520, 128),
+                                   (512, 42, 64), (1024, 1001, 128), (8192, 64, 8)])
 def test_resolve_g_idx_bit_exact(K, N, g):
     rng = np.random.default_rng(K + N + g)
     qw = rng.integers(0, 2**32, (K // 8, N), dtype=np.uint32)
     g_idx = _act_order(rng, K, g)
     say("resolve g_idx", K, N, g)
+    out, perm, status = qbn.gptq_resolve_g_idx(dev(qw), dev(g_idx), g)
+    torch.cuda.synchronize()
+    rc, perm_ref = oracle.resolve_g_idx(g_idx, g)
+    assert int(status.cpu()[0]) == rc == 0
+    assert np.array_equal(perm.cpu().numpy(), perm_ref)
+    want = oracle.gptq_pack(oracle.gptq_unpack(qw)[perm_ref])
+    assert np.array_equal(host_bits(out).reshape(want.shape), want)
+
+
+@pytest.mark.parametrize("order", ["sorted", "reversed", "interleaved"])
+def test_resolve_g_idx_structured_orders(order):
+    """g_idx already in group order (the identity), groups in reverse order,
+    and rows dealt to groups in turn (every wave sees every group)."""
+    K, N, g = 3072, 264, 64
+    G = K // g
+    base = np.arange(K) // g
+    g_idx = {"sorted": base, "reversed": G - 1 - base, "interleaved": np.arange(K) % G}[order].astype(np.int32)
+    rng = np.random.default_rng(len(order))
+    qw = rng.integers(0, 2**32, (K // 8, N), dtype=np.uint32)
+    say("resolve g_idx", order)
     out, perm, status = qbn.gptq_resolve_g_idx(dev(qw), dev(g_idx), g)
     torch.cuda.synchronize()
     rc, perm_ref = oracle.resolve_g_idx(g_idx, g)
