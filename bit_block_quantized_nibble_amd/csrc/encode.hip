@@ -15,6 +15,8 @@
 //     each its own stream, as GGUF's Q6_K keeps 4 + 2).
 // Every output is bit-exact with the definitions (IEEE binary32 division,
 // correctly rounded).
+#include <algorithm>
+
 #include "qbn_device.h"
 #include "qbn_launch.h"
 
@@ -32,6 +34,42 @@ __device__ __forceinline__ float load_elem<__bf16>(const __bf16 *p) {
     return __builtin_bit_cast(float, (uint32_t)*reinterpret_cast<const uint16_t *>(p) << 16);
 }
 
+// Division-free codes for the lane kernels. A code that depends on q =
+// fl(v / d) through a non-decreasing map C (round half even then clip for
+// INT4, the E2M1 code for NVFP4) is taken from x = fl(v * fl(1 / d)), which
+// lies within 3 ulp of q: when C(fl(x * kBelow)) == C(fl(x * kAbove)), the
+// two ends bracket q (the margin of 2^-20 relative is 16 ulp) and C(q) is
+// that common value. Otherwise (INT4: that element; NVFP4: that pair), or
+// for every element when 1 / d overflows, the code comes from the correctly
+// rounded quotient. Exact ties (a quotient on a rounding boundary) always
+// take that path; with bf16 weights they are common (a group whose amax has
+// a mantissa divisible by 7 puts many weights on half-integers).
+constexpr float kBelow = 1.0f - 0x1p-20f, kAbove = 1.0f + 0x1p-20f;
+
+// Eight consecutive elements as binary32 from one (bf16) or two (f32) 16-byte
+// loads; p must be 16-byte aligned.
+template <typename XT>
+__device__ __forceinline__ void load8(const XT *p, float v[8]) {
+    if constexpr (sizeof(XT) == 2) {
+        const u32x4 q = ld16(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __builtin_bit_cast(float, q[j] << 16);
+            v[2 * j + 1] = __builtin_bit_cast(float, q[j] & 0xFFFF0000u);
+        }
+    } else {
+        const u32x4 a = ld16(p), b = ld16(p + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // through plain words: a bit cast taken of a vector element
+            // itself reads element 0 whatever the index
+            const uint32_t wa = a[j], wb = b[j];
+            v[j] = __builtin_bit_cast(float, wa);
+            v[4 + j] = __builtin_bit_cast(float, wb);
+        }
+    }
+}
+
 // E2M1 code of v: magnitude saturated at 6, then the number of grid
 // midpoints (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) below it; an exact
 // midpoint between codes c and c + 1 goes up when TIE_EVEN and c + 1 is
@@ -44,6 +82,29 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
 #pragma unroll
     for (int i = 0; i < 7; ++i) c += (a > mid[i] || (TIE_EVEN && (i & 1) && a == mid[i])) ? 1u : 0u;
     return c | (__builtin_signbit(v) ? 8u : 0u);
+}
+
+// The 32-bit word of the E2M1 codes of q[0..7], element j at bits 4j. Ties
+// to even through the hardware conversion (scale 1: nearest, ties to the
+// even code, magnitudes past 6 saturate, the sign kept, also on a zero: the
+// code e2m1_code<true> gives; byte b takes elements 2b and 2b + 1, low
+// nibble first), else e2m1_code<false> per element.
+template <bool TIE_EVEN>
+__device__ __forceinline__ uint32_t e2m1_word(const float q[8]) {
+    uint32_t w = 0;
+    if constexpr (TIE_EVEN) {
+        float c[8];  // magnitudes clipped at 6 first (same code), so an infinite quotient saturates too
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = __builtin_copysignf(__builtin_fminf(__builtin_fabsf(q[j]), 6.0f), q[j]);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[0], c[1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[2], c[3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[4], c[5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[6], c[7], 1.0f, 3);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w |= e2m1_code<false>(q[j]) << (4 * j);
+    }
+    return w;
 }
 
 // E4M3FN byte of q >= 0 (finite): nearest, ties to even, saturating at 448.
@@ -83,6 +144,65 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4(const XT *__restrict__ x
     *reinterpret_cast<u32x2 *>(codes + row * (k / 2) + 8 * b) = u32x2{w[0], w[1]};
 }
 
+// Two lanes per 16-element block, eight elements per lane from 16-byte
+// loads: the block amax is one xor shuffle away, the even lane stores the
+// scale byte and each lane the 32-bit word of its eight codes. Same
+// arithmetic per block as the one-thread-per-block kernel.
+template <typename XT, bool TIE_EVEN, bool DENSE>
+__global__ __launch_bounds__(256) void k_quantize_nvfp4_lanes(const XT *__restrict__ x, int64_t m, int64_t k,
+                                                              int64_t ldx, float scale2, uint8_t *__restrict__ codes,
+                                                              uint8_t *__restrict__ scales) {
+    const int64_t per_row = k / 8, total = m * per_row, stride = (int64_t)gridDim.x * 256;
+    // t counts 8-element pieces: code word at byte 4t, block t / 2 (both
+    // lanes of a block iterate together: the stride is even)
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += stride) {
+        float v[8];
+        if (DENSE) {
+            load8(x + 8 * t, v);
+        } else {
+            const int64_t row = t / per_row;
+            load8(x + row * ldx + 8 * (t - row * per_row), v);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));
+        const float den = 6.0f * scale2;
+        const uint32_t sb = e4m3fn_byte(amax / den);
+        if ((t & 1) == 0) scales[t / 2] = (uint8_t)sb;
+        const float tt = e4m3fn_f32(sb) * scale2;
+        uint32_t word = 0;
+        if (tt != 0.0f) {
+            const float inv = 1.0f / tt;
+            const bool all_exact = !(inv < __builtin_huge_valf());  // uniform over the block
+            float lo[8], hi[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float q = v[j] * inv;
+                lo[j] = q * kBelow;
+                hi[j] = q * kAbove;
+            }
+            word = e2m1_word<TIE_EVEN>(lo);
+            const uint32_t diff = all_exact ? ~0u : word ^ e2m1_word<TIE_EVEN>(hi);
+            if (diff != 0u) {  // some pair next to a code boundary: those pairs from the exact quotients
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    if ((diff >> (8 * b)) & 0xFFu) {
+                        float q[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) q[j] = 0.0f;
+                        q[2 * b] = v[2 * b] / tt;
+                        q[2 * b + 1] = v[2 * b + 1] / tt;
+                        const uint32_t e = e2m1_word<TIE_EVEN>(q);
+                        word = (word & ~(0xFFu << (8 * b))) | (e & (0xFFu << (8 * b)));
+                    }
+                }
+            }
+        }
+        reinterpret_cast<uint32_t *>(codes)[t] = word;
+    }
+}
+
 // One thread per group.
 template <typename XT>
 __global__ __launch_bounds__(256) void k_quantize_int4_sym(const XT *__restrict__ w, int64_t m, int64_t k,
@@ -117,50 +237,43 @@ __global__ __launch_bounds__(256) void k_quantize_int4_sym(const XT *__restrict_
 // amax with xor shuffles inside the L-lane segment (max is exact, so the
 // order does not matter), and each stores the 32-bit word of its eight
 // nibbles. Same arithmetic per element as the one-thread-per-group kernel.
-template <typename XT, int L>
+template <typename XT, int L, bool DENSE>
 __global__ __launch_bounds__(256) void k_quantize_int4_sym_lanes(const XT *__restrict__ w, int64_t m, int64_t k,
                                                                  int64_t ldw, uint8_t *__restrict__ codes,
                                                                  float *__restrict__ scales) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t per_row = k / 8;
-    if (t >= m * per_row) return;  // whole groups leave together: m * per_row is a multiple of L
-    const int64_t row = t / per_row, c = t - row * per_row;
-    const XT *p = w + row * ldw + 8 * c;
-    float v[8];
-    if constexpr (sizeof(XT) == 2) {
-        const u32x4 q = ld16(p);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[2 * j] = __builtin_bit_cast(float, q[j] << 16);
-            v[2 * j + 1] = __builtin_bit_cast(float, q[j] & 0xFFFF0000u);
+    const int64_t per_row = k / 8, total = m * per_row, stride = (int64_t)gridDim.x * 256;
+    // t counts 8-element pieces; the code word of piece t sits at byte 4t and
+    // its group is t / L (per_row is a multiple of L). The stride is a
+    // multiple of L, so the L lanes of a group always iterate together.
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += stride) {
+        float v[8];
+        if (DENSE) {
+            load8(w + 8 * t, v);
+        } else {
+            const int64_t row = t / per_row;
+            load8(w + row * ldw + 8 * (t - row * per_row), v);
         }
-    } else {
-        const u32x4 a = ld16(p), b = ld16(p + 4);
+        float amax = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // through plain words: a bit cast taken of a vector element
-            // itself reads element 0 whatever the index
-            const uint32_t wa = a[j], wb = b[j];
-            v[j] = __builtin_bit_cast(float, wa);
-            v[4 + j] = __builtin_bit_cast(float, wb);
+        for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+#pragma unroll
+        for (int o = 1; o < L; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, 64));
+        const float s = amax / 7.0f;
+        if ((t & (L - 1)) == 0) scales[t / L] = s;
+        uint32_t word = 0;
+        if (s != 0.0f) {
+            const float inv = 1.0f / s;
+            const bool all_exact = !(inv < __builtin_huge_valf());  // uniform over the group
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = v[j] * inv;
+                float r = __builtin_rintf(x * kBelow);
+                if (all_exact || r != __builtin_rintf(x * kAbove)) r = __builtin_rintf(v[j] / s);
+                word |= ((uint32_t)(int)__builtin_fminf(__builtin_fmaxf(r, -8.0f), 7.0f) & 15u) << (4 * j);
+            }
         }
+        reinterpret_cast<uint32_t *>(codes)[t] = word;
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
-#pragma unroll
-    for (int o = 1; o < L; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, 64));
-    const float s = amax / 7.0f;
-    if ((c & (L - 1)) == 0) scales[t / L] = s;  // group index = row * (k / group) + c / L = t / L
-    uint32_t word = 0;
-    if (s != 0.0f) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float r = __builtin_rintf(v[j] / s);
-            word |= ((uint32_t)(int)__builtin_fminf(__builtin_fmaxf(r, -8.0f), 7.0f) & 15u) << (4 * j);
-        }
-    }
-    *reinterpret_cast<uint32_t *>(codes + row * (k / 2) + 4 * c) = word;
 }
 
 // One thread per 32 values, whose W-bit fields (shift..shift + W - 1 of each
@@ -225,10 +338,16 @@ __global__ __launch_bounds__(256) void k_unpack_bits(const uint32_t *__restrict_
     dst[i] = (uint8_t)v;
 }
 
-template <typename XT>
-hipError_t launch_int4_sym_lanes(int64_t lanes, dim3 g, hipStream_t s, const XT *w, int64_t m, int64_t k,
-                                 int64_t ldw, uint8_t *codes, float *scales) {
-#define QBN_I4L(L) hipLaunchKernelGGL((k_quantize_int4_sym_lanes<XT, L>), g, dim3(256), 0, s, w, m, k, ldw, codes, scales)
+// Grid of the grid-stride lane kernels: enough 256-thread workgroups to fill
+// every CU at full occupancy (8 per CU), fewer for a small input.
+dim3 lane_grid(int64_t pieces) { return dim3((unsigned)std::min<int64_t>((pieces + 255) / 256, 256 * 8)); }
+
+template <typename XT, bool DENSE>
+void launch_int4_sym_lanes_d(int64_t lanes, hipStream_t s, const XT *w, int64_t m, int64_t k, int64_t ldw,
+                             uint8_t *codes, float *scales) {
+    const dim3 g = lane_grid(m * (k / 8));
+#define QBN_I4L(L) \
+    hipLaunchKernelGGL((k_quantize_int4_sym_lanes<XT, L, DENSE>), g, dim3(256), 0, s, w, m, k, ldw, codes, scales)
     switch (lanes) {
         case 1: QBN_I4L(1); break;
         case 2: QBN_I4L(2); break;
@@ -239,7 +358,29 @@ hipError_t launch_int4_sym_lanes(int64_t lanes, dim3 g, hipStream_t s, const XT 
         default: QBN_I4L(64); break;
     }
 #undef QBN_I4L
+}
+
+template <typename XT>
+hipError_t launch_int4_sym_lanes(int64_t lanes, hipStream_t s, const XT *w, int64_t m, int64_t k, int64_t ldw,
+                                 uint8_t *codes, float *scales) {
+    if (ldw == k || m == 1)
+        launch_int4_sym_lanes_d<XT, true>(lanes, s, w, m, k, ldw, codes, scales);
+    else
+        launch_int4_sym_lanes_d<XT, false>(lanes, s, w, m, k, ldw, codes, scales);
     return hipGetLastError();
+}
+
+template <typename XT>
+void launch_nvfp4_lanes(bool dense, bool tie_even, hipStream_t s, const XT *x, int64_t m, int64_t k, int64_t ldx,
+                        float scale2, uint8_t *c, uint8_t *sc) {
+    const dim3 g = lane_grid(m * (k / 8));
+#define QBN_NVL(T, D) hipLaunchKernelGGL((k_quantize_nvfp4_lanes<XT, T, D>), g, dim3(256), 0, s, x, m, k, ldx, scale2, c, sc)
+    if (dense) {
+        if (tie_even) QBN_NVL(true, true); else QBN_NVL(false, true);
+    } else {
+        if (tie_even) QBN_NVL(true, false); else QBN_NVL(false, false);
+    }
+#undef QBN_NVL
 }
 
 template <bool VEC>
@@ -274,8 +415,17 @@ hipError_t pack_stream(const uint8_t *src, int64_t count, int shift, int width, 
 hipError_t launch_quantize_nvfp4(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, float scale2, int tie,
                                  void *codes, void *scales, hipStream_t s) {
     const int64_t blocks = m * (k / 16);
-    const dim3 grid((unsigned)((blocks + 255) / 256));
     uint8_t *c = (uint8_t *)codes, *sc = (uint8_t *)scales;
+    const int eb = x_dtype == QBN_BF16 ? 2 : 4;
+    if ((ldx * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0) {  // 16-byte rows and base
+        const bool dense = ldx == k || m == 1;
+        if (x_dtype == QBN_BF16)
+            launch_nvfp4_lanes<__bf16>(dense, tie == 0, s, (const __bf16 *)x, m, k, ldx, scale2, c, sc);
+        else
+            launch_nvfp4_lanes<float>(dense, tie == 0, s, (const float *)x, m, k, ldx, scale2, c, sc);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((blocks + 255) / 256));
     if (x_dtype == QBN_BF16) {
         if (tie == 0)
             hipLaunchKernelGGL((k_quantize_nvfp4<__bf16, true>), grid, dim3(256), 0, s, (const __bf16 *)x, m, k, ldx,
@@ -303,10 +453,9 @@ hipError_t launch_quantize_int4_sym(const void *w, int w_dtype, int64_t m, int64
     // and base (vector loads), 4-byte code rows (k % 8 == 0 follows)
     if (group % 8 == 0 && lanes <= 64 && (lanes & (lanes - 1)) == 0 && (ldw * eb) % 16 == 0 &&
         reinterpret_cast<uintptr_t>(w) % 16 == 0 && reinterpret_cast<uintptr_t>(codes) % 4 == 0) {
-        const dim3 g((unsigned)((m * (k / 8) + 255) / 256));
         if (w_dtype == QBN_BF16)
-            return launch_int4_sym_lanes<__bf16>(lanes, g, s, (const __bf16 *)w, m, k, ldw, (uint8_t *)codes, scales);
-        return launch_int4_sym_lanes<float>(lanes, g, s, (const float *)w, m, k, ldw, (uint8_t *)codes, scales);
+            return launch_int4_sym_lanes<__bf16>(lanes, s, (const __bf16 *)w, m, k, ldw, (uint8_t *)codes, scales);
+        return launch_int4_sym_lanes<float>(lanes, s, (const float *)w, m, k, ldw, (uint8_t *)codes, scales);
     }
     const dim3 grid((unsigned)((groups + 255) / 256));
     if (w_dtype == QBN_BF16)

@@ -165,3 +165,44 @@ def test_pack_bits_unaligned_values(bits, lo_bits, count):
     else:
         lo_ref = oracle.pack_bits(v.astype(np.uint32), bits)
     assert np.array_equal(host_bits(lo), lo_ref) and np.array_equal(host_bits(lo_a), lo_ref)
+
+
+@pytest.mark.parametrize("pad,off", [(16, 0), (3, 0), (16, 1)])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+@pytest.mark.parametrize("tie", [0, 1])
+def test_quantize_nvfp4_strided_rows(pad, off, xdt, tie):
+    """Rows inside a wider matrix: a 16-byte row stride and base keep the
+    two-lanes-per-block kernel; an odd stride or a base one element in take
+    the one-thread-per-block kernel. Both bit-exact."""
+    m, k, scale2 = 7, 1024, 0.01
+    rng = np.random.default_rng(pad * 5 + off + tie + len(xdt))
+    X32 = _x(rng, m, k + 16)[:, :k + pad] if pad <= 16 else None
+    X = X32 if xdt == "f32" else workloads.bf16_bits_from_f32(X32)
+    X = np.ascontiguousarray(X)
+    Xd = x_dev(X)[:, off:off + k]
+    say("quantize_nvfp4 strided", pad, off, xdt, tie)
+    codes, scales = qbn.quantize_nvfp4(Xd, float(np.float32(scale2)), tie)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.nvfp4_quantize(np.ascontiguousarray(X[:, off:off + k]), float(np.float32(scale2)), tie)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+
+
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+@pytest.mark.parametrize("tie", [0, 1])
+def test_quantize_nvfp4_quotient_overflow(xdt, tie):
+    """A tiny per-tensor scale under large weights: the block scale saturates
+    at 448 and x / t overflows binary32 to infinity, whose code still
+    saturates at magnitude 6 (sign kept); zeros and a negative zero too."""
+    rng = np.random.default_rng(77 + tie)
+    X32 = (rng.standard_normal((4, 64)) * 1e12).astype(np.float32)
+    X32[0, :16] = 0.0
+    X32[1, 0] = -0.0
+    X = X32 if xdt == "f32" else workloads.bf16_bits_from_f32(X32)
+    scale2 = float(np.float32(1e-30))
+    say("quantize_nvfp4 overflow", xdt, tie)
+    codes, scales = qbn.quantize_nvfp4(x_dev(X), scale2, tie)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.nvfp4_quantize(X, scale2, tie)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
