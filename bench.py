@@ -193,8 +193,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0, help="timed steps (default depends on the workload)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warmup steps, replayed from the captured graph (default 200; GEMM 500, "
-                         "about 0.1 s, so its clocks have settled)")
+                    help="untimed warmup steps, replayed from the captured graph (default 200; GEMMs 1500, "
+                         "about 0.3 s, so their clocks have settled)")
     ap.add_argument("--workload", default="mxfp4_gemm", choices=sorted(WORKLOADS))
     ap.add_argument("--also", nargs="*", default=["q4k_gemv", "nvfp4_gemv"], choices=sorted(WORKLOADS),
                     help="further workloads timed in the same run and listed under \"also\"")
@@ -630,7 +630,7 @@ def default_steps(kind):
 
 
 def default_warmup(kind):
-    return 500 if kind in ("gemm", "mxgemm", "int4gemm") else 200
+    return 1500 if kind in ("gemm", "mxgemm", "int4gemm") else 200
 
 
 def measure(name, steps, warmup, dev):

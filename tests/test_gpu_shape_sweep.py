@@ -260,3 +260,93 @@ def test_quantize_nvfp4_random_shapes(m, k, xdt, tie, scale2):
     c_ref, s_ref = oracle.nvfp4_quantize(X, scale2, tie)
     assert np.array_equal(scales.cpu().numpy(), s_ref)
     assert np.array_equal(codes.cpu().numpy(), c_ref)
+
+
+def _int4_cases(count=12, seed=4242):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        g = int(rng.choice([8, 16, 32, 64, 128, 256, 512])) if i % 3 else 2 * int(rng.integers(1, 40))
+        k = g * int(rng.integers(1, max(2, 8192 // g)))
+        out.append((int(rng.integers(1, 200)), k, g, "bf16" if i % 2 else "f32", int(rng.choice([0, 8, 3])),
+                    bool(i % 4 == 1)))
+    return out
+
+
+@pytest.mark.parametrize("m,k,g,xdt,pad,ties", _int4_cases())
+def test_quantize_int4_sym_random_shapes(m, k, g, xdt, pad, ties):
+    """INT4 symmetric encode bit for bit on random shapes, groups and row
+    strides (the lane kernel and the one-thread-per-group kernel). `ties`
+    draws half-integer multiples of a power of two, so most quotients sit
+    exactly on a rounding boundary or an integer."""
+    rng = np.random.default_rng(m + 3 * k + g)
+    if ties:
+        W32 = (rng.integers(-14, 15, (m, k + pad)) * 0.5 * 2.0 ** rng.integers(-3, 4, (m, 1))).astype(np.float32)
+    else:
+        W32 = (rng.standard_normal((m, k + pad)) * 10.0 ** rng.uniform(-3, 3, (m, 1))).astype(np.float32)
+    W = W32 if xdt == "f32" else workloads.bf16_bits_from_f32(W32)
+    say("quantize_int4_sym sweep", m, k, g, xdt, pad, ties)
+    codes, scales = qbn.quantize_int4_sym(x_dev(W)[:, :k], g)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.int4_sym_quantize(np.ascontiguousarray(W[:, :k]), g)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(host_bits(scales).reshape(s_ref.shape), s_ref.view(np.uint32))
+
+
+def _pack_cases(count=12, seed=8080):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        bits = int(rng.integers(1, 9))
+        lo = int(rng.integers(1, bits)) if bits > 1 and i % 3 == 2 else 0
+        out.append((int(rng.integers(1, 200000)), bits, lo, int(i % 2)))
+    return out
+
+
+@pytest.mark.parametrize("count,bits,lo,off", _pack_cases())
+def test_pack_bits_random_shapes(count, bits, lo, off):
+    """b-bit packing (one stream or two planes) bit for bit on random counts,
+    from 16-byte-aligned and unaligned values, and the unpack back."""
+    rng = np.random.default_rng(count + bits + lo)
+    v = rng.integers(0, 1 << bits, count).astype(np.uint8)
+    buf = torch.zeros(count + off, dtype=torch.uint8, device=DEV)
+    buf[off:] = dev(v)
+    say("pack_bits sweep", count, bits, lo, off)
+    w_lo, w_hi = qbn.pack_bits(buf[off:], bits, lo)
+    torch.cuda.synchronize()
+    if lo:
+        lo_ref, hi_ref = oracle.pack_planes(v.astype(np.uint32), bits, lo)
+        assert np.array_equal(host_bits(w_hi), hi_ref)
+    else:
+        lo_ref = oracle.pack_bits(v.astype(np.uint32), bits)
+    assert np.array_equal(host_bits(w_lo), lo_ref)
+    back = qbn.unpack_bits(w_lo, w_hi, count, bits, lo)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().numpy(), v)
+
+
+def _act_order_cases(count=8, seed=1212):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        g = int(rng.choice([8, 16, 32, 64, 128]))
+        K = g * int(rng.integers(1, 1 + min(1100, 16384 // g)))
+        out.append((K, int(rng.integers(1, 700)), g))
+    return out
+
+
+@pytest.mark.parametrize("K,N,g", _act_order_cases())
+def test_resolve_g_idx_random_shapes(K, N, g):
+    """Act-order resolution bit for bit on random K, N and group sizes (both
+    placement paths: up to 512 groups and beyond)."""
+    rng = np.random.default_rng(K + N + g)
+    qw = rng.integers(0, 2**32, (K // 8, N), dtype=np.uint32)
+    g_idx = rng.permutation(np.arange(K) // g).astype(np.int32)
+    say("resolve g_idx sweep", K, N, g)
+    out, perm, status = qbn.gptq_resolve_g_idx(dev(qw), dev(g_idx), g)
+    torch.cuda.synchronize()
+    rc, perm_ref = oracle.resolve_g_idx(g_idx, g)
+    assert int(status.cpu()[0]) == rc == 0
+    assert np.array_equal(perm.cpu().numpy(), perm_ref)
+    want = oracle.gptq_pack(oracle.gptq_unpack(qw)[perm_ref])
+    assert np.array_equal(host_bits(out).reshape(want.shape), want)
