@@ -62,8 +62,9 @@ __device__ __forceinline__ uint64_t same_group_lanes(bool in, int g, int nbits) 
 // walks it 64 rows at a time; the lanes holding the same group index find
 // each other with ballots (same_group_lanes), so the rank inside a 64-row
 // piece is a popcount. With G * 16 counters in LDS (G <= kPrefixGroups) the
-// waves count their shares, an exclusive prefix over the waves gives each
-// wave its starting offset per group, and the waves then place their rows
+// waves count their shares, an exclusive prefix over the waves (a shuffle
+// scan across 16 lanes per group) gives each wave its starting offset per
+// group, and the waves then place their rows
 // independently, reading g_idx from an LDS copy made while counting when K
 // <= kStageRows. Beyond that the waves take turns, one 64-row piece each per
 // turn, on one shared counter per group. Either way each group keeps the
@@ -88,13 +89,34 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve_g_idx(const int32_t
     for (int64_t g = t; g < G; g += kResolveThreads) cnt[g] = 0;
     if (t == 0) bad = 0;
     __syncthreads();
-    for (int64_t k = t; k < K; k += kResolveThreads) {
-        const int g = g_idx[k];
-        if (stage) staged[k] = g;
-        if (g < 0 || g >= G)
-            atomicOr(&bad, 1);
-        else
-            atomicAdd(&cnt[g], 1);
+    if (stage) {
+        // all of a thread's (at most 16) loads in flight before the first use
+        int gv[kStageRows / kResolveThreads];
+#pragma unroll
+        for (int i = 0; i < kStageRows / kResolveThreads; ++i) {
+            const int64_t k = t + (int64_t)i * kResolveThreads;
+            gv[i] = k < K ? g_idx[k] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < kStageRows / kResolveThreads; ++i) {
+            const int64_t k = t + (int64_t)i * kResolveThreads;
+            if (k < K) {
+                const int g = gv[i];
+                staged[k] = g;
+                if (g < 0 || g >= G)
+                    atomicOr(&bad, 1);
+                else
+                    atomicAdd(&cnt[g], 1);
+            }
+        }
+    } else {
+        for (int64_t k = t; k < K; k += kResolveThreads) {
+            const int g = g_idx[k];
+            if (g < 0 || g >= G)
+                atomicOr(&bad, 1);
+            else
+                atomicAdd(&cnt[g], 1);
+        }
     }
     __syncthreads();
     if (bad == 0)
@@ -124,13 +146,20 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve_g_idx(const int32_t
             if (in && (same & above) == 0) cw[g] += __popcll(same);  // the last lane of its set
         }
         __syncthreads();
-        for (int64_t g = t; g < G; g += kResolveThreads) {
-            int run = (int)(g * group);
-            for (int w = 0; w < kResolveWaves; ++w) {
-                const int c = cnt[w * kPrefixGroups + g];
-                cnt[w * kPrefixGroups + g] = run;
-                run += c;
+        // exclusive prefix over the 16 waves, per group: 16 neighbouring lanes
+        // hold one group's 16 counts and scan them with shuffles; 64 groups
+        // per pass (each count is read and written by its own thread)
+        for (int64_t g0 = 0; g0 < G; g0 += kResolveThreads / kResolveWaves) {
+            const int64_t g = g0 + t / kResolveWaves;
+            const int w = t % kResolveWaves;
+            const int c = g < G ? cnt[w * kPrefixGroups + g] : 0;
+            int incl = c;
+#pragma unroll
+            for (int o = 1; o < kResolveWaves; o <<= 1) {
+                const int n = __shfl_up(incl, o, kResolveWaves);
+                if (w >= o) incl += n;
             }
+            if (g < G) cnt[w * kPrefixGroups + g] = (int)(g * group) + incl - c;
         }
         __syncthreads();
         for (int64_t c = k0; c < k1; c += 64) {
