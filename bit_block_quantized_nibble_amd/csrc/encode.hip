@@ -14,7 +14,8 @@
 //     or split into two planes (the low `lo` bits and the high b - lo bits,
 //     each its own stream, as GGUF's Q6_K keeps 4 + 2).
 // Every output is bit-exact with the definitions (IEEE binary32 division,
-// correctly rounded).
+// correctly rounded); the lane kernels reach the same codes with a division
+// only next to a rounding boundary (the bracket below).
 #include <algorithm>
 
 #include "qbn_device.h"
@@ -146,8 +147,8 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4(const XT *__restrict__ x
 
 // Two lanes per 16-element block, eight elements per lane from 16-byte
 // loads: the block amax is one xor shuffle away, the even lane stores the
-// scale byte and each lane the 32-bit word of its eight codes. Same
-// arithmetic per block as the one-thread-per-block kernel.
+// scale byte and each lane the 32-bit word of its eight codes. The same
+// scale bytes and codes as the one-thread-per-block kernel.
 template <typename XT, bool TIE_EVEN, bool DENSE>
 __global__ __launch_bounds__(256) void k_quantize_nvfp4_lanes(const XT *__restrict__ x, int64_t m, int64_t k,
                                                               int64_t ldx, float scale2, uint8_t *__restrict__ codes,
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256) void k_quantize_int4_sym(const XT *__restrict_
 // lanes load 16- or 32-byte pieces of the row side by side, take the group's
 // amax with xor shuffles inside the L-lane segment (max is exact, so the
 // order does not matter), and each stores the 32-bit word of its eight
-// nibbles. Same arithmetic per element as the one-thread-per-group kernel.
+// nibbles. The same scales and codes as the one-thread-per-group kernel.
 template <typename XT, int L, bool DENSE>
 __global__ __launch_bounds__(256) void k_quantize_int4_sym_lanes(const XT *__restrict__ w, int64_t m, int64_t k,
                                                                  int64_t ldw, uint8_t *__restrict__ codes,

@@ -192,3 +192,53 @@ def test_graph_dequantize(layout):
     src = _gptq_src(512, 1024, 128, False, 7700)
     out = torch.empty((1024, 512) if layout == "nk" else (512, 1024), dtype=torch.bfloat16, device=DEV)
     _replays_match(qbn.prepare_dequantize(src, out, layout=layout), [out], "dequantize gptq4 %s" % layout)
+
+
+def _prepared(fn, args, what, keep):
+    return qbn.Prepared(fn, args, what, torch.device(DEV), keep)
+
+
+@pytest.mark.parametrize("g", [128, 24])
+def test_graph_quantize_int4_sym(g):
+    # group 128: the grid-stride lane kernel; 24: one thread per group
+    rng = np.random.default_rng(7800 + g)
+    m, k = 96, 1536
+    W = x_dev(workloads.bf16_bits_from_f32(rng.standard_normal((m, k)).astype(np.float32)))
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((m, k // g), dtype=torch.float32, device=DEV)
+    lib = qbn._load()
+    step = _prepared(lib.qbn_quantize_int4_sym, (qbn._ptr(W, "w"), qbn._DTYPES[torch.bfloat16], m, k, k, g,
+                                                 qbn._ptr(codes, "codes"), qbn._ptr(scales, "scales")),
+                     "qbn_quantize_int4_sym", (W, codes, scales))
+    _replays_match(step, [codes, scales], "quantize_int4_sym %dx%d group %d" % (m, k, g))
+
+
+def test_graph_pack_bits_planes():
+    rng = np.random.default_rng(7900)
+    count, bits, lo = 100003, 6, 4
+    v = dev(rng.integers(0, 1 << bits, count).astype(np.uint8))
+    w_lo = torch.empty((count * lo + 31) // 32, dtype=torch.int32, device=DEV)
+    w_hi = torch.empty((count * (bits - lo) + 31) // 32, dtype=torch.int32, device=DEV)
+    lib = qbn._load()
+    step = _prepared(lib.qbn_pack_bits, (qbn._ptr(v, "values"), count, bits, lo, qbn._ptr(w_lo, "lo"),
+                                         qbn._ptr(w_hi, "hi")), "qbn_pack_bits", (v, w_lo, w_hi))
+    _replays_match(step, [w_lo, w_hi], "pack_bits %d values, 6 bits as 4 + 2" % count)
+
+
+@pytest.mark.parametrize("K,g", [(4096, 128), (8192, 8)])
+def test_graph_resolve_g_idx(K, g):
+    # 32 groups (per-wave prefix) and 1024 groups (waves taking turns)
+    rng = np.random.default_rng(8000 + K)
+    N = 264
+    qw = dev(rng.integers(0, 2**32, (K // 8, N), dtype=np.uint32))
+    gi = dev(rng.permutation(np.arange(K) // g).astype(np.int32))
+    out = torch.empty_like(qw)
+    perm = torch.empty(K, dtype=torch.int32, device=DEV)
+    status = torch.empty(1, dtype=torch.int32, device=DEV)
+    lib = qbn._load()
+    step = _prepared(lib.qbn_gptq_resolve_g_idx, (qbn._ptr(qw, "q"), qbn._ptr(gi, "g_idx"), K, N, g,
+                                                  qbn._ptr(out, "out"), qbn._ptr(perm, "perm"),
+                                                  qbn._ptr(status, "status")),
+                     "qbn_gptq_resolve_g_idx", (qw, gi, out, perm, status))
+    _replays_match(step, [out, perm, status], "resolve g_idx K=%d group %d" % (K, g))
+    assert int(status[0].item()) == 0
