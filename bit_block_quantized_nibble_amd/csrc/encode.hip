@@ -87,16 +87,18 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
 
 // The 32-bit word of the E2M1 codes of q[0..7], element j at bits 4j. Ties
 // to even through the hardware conversion (scale 1: nearest, ties to the
-// even code, magnitudes past 6 saturate, the sign kept, also on a zero: the
-// code e2m1_code<true> gives; byte b takes elements 2b and 2b + 1, low
-// nibble first), else e2m1_code<false> per element.
-template <bool TIE_EVEN>
+// even code, finite magnitudes past 6 saturate, the sign kept, also on a
+// zero: the code e2m1_code<true> gives; byte b takes elements 2b and 2b + 1,
+// low nibble first), else e2m1_code<false> per element.
+template <bool TIE_EVEN, bool CLIP = true>
 __device__ __forceinline__ uint32_t e2m1_word(const float q[8]) {
     uint32_t w = 0;
     if constexpr (TIE_EVEN) {
-        float c[8];  // magnitudes clipped at 6 first (same code), so an infinite quotient saturates too
+        // CLIP: magnitudes clipped at 6 first (the same code), so that an
+        // infinite quotient saturates too; without it q must be finite
+        float c[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[j] = __builtin_copysignf(__builtin_fminf(__builtin_fabsf(q[j]), 6.0f), q[j]);
+        for (int j = 0; j < 8; ++j) c[j] = CLIP ? __builtin_copysignf(__builtin_fminf(__builtin_fabsf(q[j]), 6.0f), q[j]) : q[j];
         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[0], c[1], 1.0f, 0);
         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[2], c[3], 1.0f, 1);
         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[4], c[5], 1.0f, 2);
@@ -175,7 +177,9 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4_lanes(const XT *__restri
         uint32_t word = 0;
         if (tt != 0.0f) {
             const float inv = 1.0f / tt;
-            const bool all_exact = !(inv < __builtin_huge_valf());  // uniform over the block
+            // uniform over the block: 1 / t overflows, or some bracket end
+            // v * (1 / t) * (1 + 2^-20) would not be finite (|v| <= amax)
+            const bool all_exact = !(amax * inv * kAbove < __builtin_huge_valf());
             float lo[8], hi[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -183,8 +187,8 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4_lanes(const XT *__restri
                 lo[j] = q * kBelow;
                 hi[j] = q * kAbove;
             }
-            word = e2m1_word<TIE_EVEN>(lo);
-            const uint32_t diff = all_exact ? ~0u : word ^ e2m1_word<TIE_EVEN>(hi);
+            word = e2m1_word<TIE_EVEN, false>(lo);
+            const uint32_t diff = all_exact ? ~0u : word ^ e2m1_word<TIE_EVEN, false>(hi);
             if (diff != 0u) {  // some pair next to a code boundary: those pairs from the exact quotients
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
