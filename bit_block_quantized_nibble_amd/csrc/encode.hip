@@ -47,6 +47,21 @@ __device__ __forceinline__ float load_elem<__bf16>(const __bf16 *p) {
 // a mantissa divisible by 7 puts many weights on half-integers).
 constexpr float kBelow = 1.0f - 0x1p-20f, kAbove = 1.0f + 0x1p-20f;
 
+// Maximum over groups of L consecutive lanes (L a power of two <= 64), in
+// every lane of the group: DPP moves inside a row of 16 (quad swaps, then
+// the half-row and row mirrors), shuffles across rows. Max is exact, so the
+// order does not matter. The lanes of a group are active together.
+template <int L>
+__device__ __forceinline__ float group_max(float a) {
+    if (L >= 2) a = __builtin_fmaxf(a, dpp_f32<0xB1>(a));   // quad_perm [1,0,3,2]
+    if (L >= 4) a = __builtin_fmaxf(a, dpp_f32<0x4E>(a));   // quad_perm [2,3,0,1]
+    if (L >= 8) a = __builtin_fmaxf(a, dpp_f32<0x141>(a));  // row_half_mirror
+    if (L >= 16) a = __builtin_fmaxf(a, dpp_f32<0x140>(a)); // row_mirror
+    if (L >= 32) a = __builtin_fmaxf(a, __shfl_xor(a, 16, 64));
+    if (L >= 64) a = __builtin_fmaxf(a, __shfl_xor(a, 32, 64));
+    return a;
+}
+
 // Eight consecutive elements as binary32 from one (bf16) or two (f32) 16-byte
 // loads; p must be 16-byte aligned.
 template <typename XT>
@@ -148,7 +163,7 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4(const XT *__restrict__ x
 }
 
 // Two lanes per 16-element block, eight elements per lane from 16-byte
-// loads: the block amax is one xor shuffle away, the even lane stores the
+// loads: the block amax is one DPP swap away, the even lane stores the
 // scale byte and each lane the 32-bit word of its eight codes. The same
 // scale bytes and codes as the one-thread-per-block kernel.
 template <typename XT, bool TIE_EVEN, bool DENSE>
@@ -169,7 +184,7 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4_lanes(const XT *__restri
         float amax = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = group_max<2>(amax);
         const float den = 6.0f * scale2;
         const uint32_t sb = e4m3fn_byte(amax / den);
         if ((t & 1) == 0) scales[t / 2] = (uint8_t)sb;
@@ -239,9 +254,8 @@ __global__ __launch_bounds__(256) void k_quantize_int4_sym(const XT *__restrict_
 // L = group / 8 consecutive lanes per group (L a power of two <= 64, so a
 // group never straddles a wave), eight consecutive elements per lane: the
 // lanes load 16- or 32-byte pieces of the row side by side, take the group's
-// amax with xor shuffles inside the L-lane segment (max is exact, so the
-// order does not matter), and each stores the 32-bit word of its eight
-// nibbles. The same scales and codes as the one-thread-per-group kernel.
+// amax across the L-lane segment (group_max), and each stores the 32-bit
+// word of its eight nibbles. The same scales and codes as the one-thread-per-group kernel.
 template <typename XT, int L, bool DENSE>
 __global__ __launch_bounds__(256) void k_quantize_int4_sym_lanes(const XT *__restrict__ w, int64_t m, int64_t k,
                                                                  int64_t ldw, uint8_t *__restrict__ codes,
@@ -261,8 +275,7 @@ __global__ __launch_bounds__(256) void k_quantize_int4_sym_lanes(const XT *__res
         float amax = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
-#pragma unroll
-        for (int o = 1; o < L; o <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, 64));
+        amax = group_max<L>(amax);
         const float s = amax / 7.0f;
         if ((t & (L - 1)) == 0) scales[t / L] = s;
         uint32_t word = 0;
