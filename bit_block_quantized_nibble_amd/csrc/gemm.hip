@@ -601,6 +601,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const uint16_t *__restr
         }
     }
 
+    // Y is written once and read by no later step of this kernel: non-temporal
+    // stores (all 256 workgroups write their tiles at about the same time)
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -609,7 +611,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const uint16_t *__restr
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t m = m0 + wm * (32 * TM) + 32 * i + 8 * (v / 4) + 4 * lh + (v % 4);
-                if (m < M && n < N) Y[m * ldy + n] = bf16_bits_rne(acc[i][j][v]);
+                if (m < M && n < N) __builtin_nontemporal_store(bf16_bits_rne(acc[i][j][v]), Y + m * ldy + n);
             }
         }
 }
