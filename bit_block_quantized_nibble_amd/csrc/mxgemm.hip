@@ -465,7 +465,9 @@ __global__ __launch_bounds__(256) void k_mxgemm(const uint8_t *__restrict__ xc, 
             const int64_t m = rm0 + 32 * i + r, n = cn0 + c;
             YT *const dst = Y + m * ldy + n;
             if (vec && m < M && n + O::E <= N) {
-                *reinterpret_cast<u32x4 *>(dst) = v;
+                // Y is written once: non-temporal (about 1% faster on the
+                // 2048 x 8192 x 8192 step)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
             } else if (m < M) {
                 const YT *e = reinterpret_cast<const YT *>(&v);
 #pragma unroll
