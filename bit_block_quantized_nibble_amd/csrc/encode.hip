@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4_lanes(const XT *__restri
                 }
             }
         }
-        reinterpret_cast<uint32_t *>(codes)[t] = word;
+        __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(codes) + t);  // one contiguous run per wave
     }
 }
 
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void k_quantize_int4_sym_lanes(const XT *__res
                 word |= ((uint32_t)(int)__builtin_fminf(__builtin_fmaxf(r, -8.0f), 7.0f) & 15u) << (4 * j);
             }
         }
-        reinterpret_cast<uint32_t *>(codes)[t] = word;
+        __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(codes) + t);  // one contiguous run per wave
     }
 }
 

@@ -93,7 +93,9 @@ __global__ __launch_bounds__(256) void k_gptq_to_awq(const uint32_t *__restrict_
     for (int s2 = 0; s2 < 8; ++s2) x[s2] = a[awq_col(s2)];
     nib_transpose8(x);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dst[(8 * r + j) * G + g] = x[j];
+    // non-temporal: lanes hold neighbouring words, so each store is one
+    // contiguous run (11.1 -> 9.7 us for 4096 x 11008)
+    for (int j = 0; j < 8; ++j) __builtin_nontemporal_store(x[j], dst + (8 * r + j) * G + g);
 }
 
 template <bool VEC>
