@@ -217,7 +217,9 @@ __device__ __forceinline__ void move_runs(uint8_t *lds, uint8_t *__restrict__ bl
                     q.v[0] = v[it].x, q.v[1] = v[it].y, q.v[2] = v[it].z, q.v[3] = v[it].w;
                     *reinterpret_cast<Piece16 *>(lds + r * RS + 16 * pc) = q;
                 } else {
-                    reinterpret_cast<u32x4 *>(blocks + (col(r) * nbr + b0) * 18)[pc] = v[it];
+                    // non-temporal: the 144-byte runs are written once (AWQ -> Q4_0
+                    // 21.9 -> 21.4 us a step)
+                    __builtin_nontemporal_store(v[it], reinterpret_cast<u32x4 *>(blocks + (col(r) * nbr + b0) * 18) + pc);
                 }
             }
         }
@@ -244,7 +246,7 @@ __device__ __forceinline__ void move_runs(uint8_t *lds, uint8_t *__restrict__ bl
                 uint32_t *lp = reinterpret_cast<uint32_t *>(lds + (r0 + 4 * i) * RS) + lane;
                 if (ok[i]) {
                     if (TO_LDS) *lp = v[i];
-                    else *gp[i] = v[i];
+                    else __builtin_nontemporal_store(v[i], gp[i]);
                 }
             }
         } else {
@@ -268,7 +270,7 @@ __device__ __forceinline__ void move_runs(uint8_t *lds, uint8_t *__restrict__ bl
                     uint16_t *lp = reinterpret_cast<uint16_t *>(lds + (r0 + 4 * i) * RS) + u;
                     if (ok[i]) {
                         if (TO_LDS) *lp = v[i];
-                        else *gp[i] = v[i];
+                        else __builtin_nontemporal_store(v[i], gp[i]);
                     }
                 }
             }
