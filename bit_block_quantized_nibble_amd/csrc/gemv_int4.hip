@@ -420,7 +420,14 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(const uint8_t *__restrict__ b
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int64_t row = min(r0 + r, n - 1);
-                blk[u][r] = *reinterpret_cast<const Q40 *>(blocks + (row * nb + b) * 18);
+                {
+                    // blocks are read once: non-temporal loads, one per field
+                    // (8.73 -> 8.45 us on 11008 x 4096)
+                    const Q40 *q = reinterpret_cast<const Q40 *>(blocks + (row * nb + b) * 18);
+                    blk[u][r].d = __builtin_nontemporal_load(&q->d);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) blk[u][r].c[e] = __builtin_nontemporal_load(&q->c[e]);
+                }
             }
         }
     };
