@@ -18,6 +18,8 @@
 // the run's largest and drops bits more than 13 below it, which E4M3 x E2M1
 // products (up to 6 significant bits over a 21-binade range) exceed, so the
 // error bound of the sum would not hold. E2M1 x E2M1 runs never reach it.
+#include <algorithm>
+
 #include "qbn_device.h"
 #include "qbn_launch.h"
 
@@ -50,44 +52,46 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
 
 // Eight lanes per 32-element block, four consecutive elements per lane.
 // E8 = true: E4M3FN elements (codes [m][k]); false: E2M1 (codes [m][k/2]).
-template <typename XT, bool E8>
+template <typename XT, bool E8, bool DENSE>
 __global__ __launch_bounds__(256) void k_quantize_mx(const XT *__restrict__ x, int64_t ldx, uint8_t *__restrict__ codes,
                                                      uint8_t *__restrict__ scales, int64_t m, int64_t k) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t quads = k / 4;
-    const int64_t row = t / quads;
-    if (row >= m) return;  // whole 8-lane groups leave together (k / 4 is a multiple of 8)
-    const int64_t c4 = 4 * (t % quads);
-    const f32x4 v = XLoad4<XT>::at(x + row * ldx + c4);
-    // block maximum over the 8 lanes (bit patterns of magnitudes order like the values)
-    uint32_t a = max(max(__float_as_uint(v.x) & 0x7FFFFFFFu, __float_as_uint(v.y) & 0x7FFFFFFFu),
-                     max(__float_as_uint(v.z) & 0x7FFFFFFFu, __float_as_uint(v.w) & 0x7FFFFFFFu));
-    a = max(a, dpp_u32<0xB1>(a));   // quad_perm [1,0,3,2]
-    a = max(a, dpp_u32<0x4E>(a));   // quad_perm [2,3,0,1]
-    a = max(a, dpp_u32<0x141>(a));  // row_half_mirror: all 8 lanes of the block
-    // floor(log2 amax) is the exponent field - 127 for normal amax; zero or
-    // subnormal amax gives <= -127 - emax, which clamps to -127 anyway
-    constexpr int EMAX = E8 ? 8 : 2;
-    int e = (int)(a >> 23) - 127 - EMAX;
-    e = e < -127 ? -127 : (e > 127 ? 127 : e);
-    const float s0 = __builtin_amdgcn_ldexpf(v.x, -e), s1 = __builtin_amdgcn_ldexpf(v.y, -e);
-    const float s2 = __builtin_amdgcn_ldexpf(v.z, -e), s3 = __builtin_amdgcn_ldexpf(v.w, -e);
-    if (E8) {
-        typedef short v2s __attribute__((ext_vector_type(2)));
-        const float lim = 448.0f;
-        v2s lo = {0, 0}, hi = {0, 0};
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, __builtin_fminf(__builtin_fmaxf(s0, -lim), lim),
-                                                      __builtin_fminf(__builtin_fmaxf(s1, -lim), lim), 1.0f, false);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, __builtin_fminf(__builtin_fmaxf(s2, -lim), lim),
-                                                      __builtin_fminf(__builtin_fmaxf(s3, -lim), lim), 1.0f, false);
-        const uint32_t w = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)hi[0] << 16);
-        *reinterpret_cast<uint32_t *>(codes + row * k + c4) = w;
-    } else {
-        uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s0, s1, 1.0f, 0);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, s2, s3, 1.0f, 1);
-        *reinterpret_cast<uint16_t *>(codes + row * (k / 2) + c4 / 2) = (uint16_t)w;
+    const int64_t quads = k / 4, total = m * quads, stride = (int64_t)gridDim.x * 256;
+    // grid-stride; whole 8-lane groups iterate together (k / 4 and the stride
+    // are multiples of 8). Dense rows (ldx == k) skip the row division.
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += stride) {
+        const int64_t row = DENSE ? 0 : t / quads;
+        const int64_t c4 = DENSE ? 4 * t : 4 * (t - row * quads);
+        const f32x4 v = XLoad4<XT>::at(x + row * ldx + c4);
+        // block maximum over the 8 lanes (bit patterns of magnitudes order like the values)
+        uint32_t a = max(max(__float_as_uint(v.x) & 0x7FFFFFFFu, __float_as_uint(v.y) & 0x7FFFFFFFu),
+                         max(__float_as_uint(v.z) & 0x7FFFFFFFu, __float_as_uint(v.w) & 0x7FFFFFFFu));
+        a = max(a, dpp_u32<0xB1>(a));   // quad_perm [1,0,3,2]
+        a = max(a, dpp_u32<0x4E>(a));   // quad_perm [2,3,0,1]
+        a = max(a, dpp_u32<0x141>(a));  // row_half_mirror: all 8 lanes of the block
+        // floor(log2 amax) is the exponent field - 127 for normal amax; zero or
+        // subnormal amax gives <= -127 - emax, which clamps to -127 anyway
+        constexpr int EMAX = E8 ? 8 : 2;
+        int e = (int)(a >> 23) - 127 - EMAX;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        const float s0 = __builtin_amdgcn_ldexpf(v.x, -e), s1 = __builtin_amdgcn_ldexpf(v.y, -e);
+        const float s2 = __builtin_amdgcn_ldexpf(v.z, -e), s3 = __builtin_amdgcn_ldexpf(v.w, -e);
+        if (E8) {
+            typedef short v2s __attribute__((ext_vector_type(2)));
+            const float lim = 448.0f;
+            v2s lo = {0, 0}, hi = {0, 0};
+            lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, __builtin_fminf(__builtin_fmaxf(s0, -lim), lim),
+                                                          __builtin_fminf(__builtin_fmaxf(s1, -lim), lim), 1.0f, false);
+            hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, __builtin_fminf(__builtin_fmaxf(s2, -lim), lim),
+                                                          __builtin_fminf(__builtin_fmaxf(s3, -lim), lim), 1.0f, false);
+            const uint32_t w = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)hi[0] << 16);
+            *reinterpret_cast<uint32_t *>(codes + row * k + c4) = w;
+        } else {
+            uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s0, s1, 1.0f, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, s2, s3, 1.0f, 1);
+            *reinterpret_cast<uint16_t *>(codes + row * (k / 2) + c4 / 2) = (uint16_t)w;
+        }
+        if ((threadIdx.x & 7) == 0) scales[row * (k / 32) + c4 / 32] = (uint8_t)(e + 127);
     }
-    if ((threadIdx.x & 7) == 0) scales[row * (k / 32) + c4 / 32] = (uint8_t)(e + 127);
 }
 
 // ------------------------------------------------------------------ GEMM, 256 x 256 tiles
@@ -540,23 +544,19 @@ hipError_t run_mxgemm(const qbn_tensor &w, int64_t m, const void *xc, const void
 hipError_t launch_quantize_mx(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int x_format,
                               void *codes, void *scales, hipStream_t s) {
     const int64_t threads = m * (k / 4);
-    const unsigned grid = (unsigned)((threads + 255) / 256);
-    const bool e8 = x_format == QBN_MXFP8;
+    const unsigned grid = (unsigned)std::min<int64_t>((threads + 255) / 256, 256 * 8);
+    const bool e8 = x_format == QBN_MXFP8, dense = ldx == k || m == 1;
+#define QBN_QMX(XT, E8, D) \
+    hipLaunchKernelGGL((k_quantize_mx<XT, E8, D>), dim3(grid), dim3(256), 0, s, (const XT *)x, ldx, (uint8_t *)codes, \
+                       (uint8_t *)scales, m, k)
     if (x_dtype == QBN_BF16) {
-        if (e8)
-            hipLaunchKernelGGL((k_quantize_mx<__bf16, true>), dim3(grid), dim3(256), 0, s, (const __bf16 *)x, ldx,
-                               (uint8_t *)codes, (uint8_t *)scales, m, k);
-        else
-            hipLaunchKernelGGL((k_quantize_mx<__bf16, false>), dim3(grid), dim3(256), 0, s, (const __bf16 *)x, ldx,
-                               (uint8_t *)codes, (uint8_t *)scales, m, k);
+        if (e8) { if (dense) QBN_QMX(__bf16, true, true); else QBN_QMX(__bf16, true, false); }
+        else { if (dense) QBN_QMX(__bf16, false, true); else QBN_QMX(__bf16, false, false); }
     } else {
-        if (e8)
-            hipLaunchKernelGGL((k_quantize_mx<float, true>), dim3(grid), dim3(256), 0, s, (const float *)x, ldx,
-                               (uint8_t *)codes, (uint8_t *)scales, m, k);
-        else
-            hipLaunchKernelGGL((k_quantize_mx<float, false>), dim3(grid), dim3(256), 0, s, (const float *)x, ldx,
-                               (uint8_t *)codes, (uint8_t *)scales, m, k);
+        if (e8) { if (dense) QBN_QMX(float, true, true); else QBN_QMX(float, true, false); }
+        else { if (dense) QBN_QMX(float, false, true); else QBN_QMX(float, false, false); }
     }
+#undef QBN_QMX
     return hipGetLastError();
 }
 
