@@ -370,15 +370,16 @@ __device__ __forceinline__ void q4k_load(Q4KFrag<BPL> &f, const uint8_t *__restr
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
         const uint8_t *blk = blocks + row * row_bytes + 144 * (int64_t)(bs + NBR * j);
-        // codes are read once: non-temporal (about 1% faster on 14336 x 4096);
-        // the headers below are shared by a quad's lanes and stay ordinary
+        // codes and headers are read once (a quad's four lanes share a header
+        // within one load instruction): non-temporal loads, about 1% and 1.7%
+        // faster on 14336 x 4096
         f.q[j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(blk + 16 + 16 * c))
                     : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
         const uint8_t *blk = blocks + row * row_bytes + 144 * (int64_t)(bs + NBR * j);
-        f.h[j] = ok ? ld16(blk) : u32x4{0u, 0u, 0u, 0u};
+        f.h[j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(blk)) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
