@@ -62,7 +62,10 @@ __device__ __forceinline__ void load_afrag(AFrag &f, const uint8_t *__restrict__
     // the codes are read once: non-temporal (kernel 4.28 -> 4.09 us on 4096 x 4096)
     f.w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cp));
     f.w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cp + 16));
-    __builtin_memcpy(&f.sc, scales + (uint64_t)row * (uint64_t)(k / 16) + 16 * b + 4 * c, 4);
+    // the four scale bytes too (kernel 4.09 -> 3.98 us; an unaligned address
+    // is a legal load here)
+    f.sc = __builtin_nontemporal_load(
+        reinterpret_cast<const uint32_t *>(scales + (uint64_t)row * (uint64_t)(k / 16) + 16 * b + 4 * c));
 }
 
 // Exact sum over 16 elements (two code words) of e2m1 * q.
